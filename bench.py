@@ -1,0 +1,250 @@
+"""Benchmark: one flow-match Euler denoising step of the 36 x 4096 DiT stack at
+4096 tokens on one MI355X (timestep embedding + dit_stack_step + Euler update,
+all on the device through libdit.so).
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu] [--gpus 1]
+
+Prints one JSON line: s/denoise-step, the roofline of the dominant kernel
+(the SwiGLU up-GEMM, timed with HIP events on the launch stream), per-kernel
+MFMA / HBM utilisation, and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from diffusion_transformer_dit_amd import inputs as I  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+METRIC = "s/denoise-step (36x4096 DiT, 4096 tok) + bf16 MFMA util % of peak"
+
+
+def block_flops(cfg) -> dict:
+    """Algorithmic flops of one block (2 per multiply-add; attention 4 S^2 hd H B)."""
+    N, D, F = cfg.tokens, cfg.hidden, cfg.ffn
+    return {
+        "gemm_qkv": 2.0 * N * D * cfg.qkv_dim,
+        "flash_attention": 4.0 * cfg.batch * cfg.seq ** 2 * cfg.head_dim * cfg.heads,
+        "gemm_out_proj": 2.0 * N * D * cfg.heads * cfg.head_dim,
+        "gemm_swiglu": 2.0 * N * D * 2 * F,
+        "gemm_down": 2.0 * N * F * D,
+    }
+
+
+def step_flops(cfg) -> float:
+    edges = 2.0 * cfg.tokens * cfg.latent_dim * cfg.hidden * 2
+    return cfg.layers * sum(block_flops(cfg).values()) + edges
+
+
+def build_full_stack(cfg=I.C4, device="cuda"):
+    """The full stack resident in HBM, weights N(0, 0.02) bf16 drawn on the device
+    from seeded generators; one AdaLN linear shared by all blocks."""
+    import torch
+    from diffusion_transformer_dit_amd import runtime as R
+    D, F, Dc, C, hd = cfg.hidden, cfg.ffn, cfg.cond_dim, cfg.latent_dim, cfg.head_dim
+    nb = lambda shape, blk, name: I.torch_normal_bf16(shape, 0.02, I.torch_seed(cfg.cfg_id, blk, name), device)
+    shared = {"w_ada": nb((6 * D, Dc), 999, "w_ada"), "b_ada": nb((6 * D,), 999, "b_ada").float()}
+    ones = torch.ones(hd, dtype=torch.float32, device=device)
+    zeros = torch.zeros(hd, dtype=torch.float32, device=device)
+    blocks = []
+    for l in range(cfg.layers):
+        t = dict(shared)
+        t.update({"w_qkv": nb((cfg.qkv_dim, D), l, "w_qkv"), "w_o": nb((D, cfg.heads * hd), l, "w_o"),
+                  "w_gate_up": nb((2 * F, D), l, "w_gate_up"), "w_down": nb((D, F), l, "w_down"),
+                  "q_g": ones, "q_b": zeros, "k_g": ones, "k_b": zeros})
+        blocks.append(R.DeviceBlock(None, tensors=t))
+    edges = {"w_in": nb((D, C), 1000, "w_in"), "b_in": nb((D,), 1000, "b_in").float(),
+             "w_fmod": nb((2 * D, Dc), 1000, "w_fmod"), "b_fmod": nb((2 * D,), 1000, "b_fmod").float(),
+             "w_out": nb((C, D), 1000, "w_out"), "b_out": nb((C,), 1000, "b_out").float()}
+    stack = R.DeviceStack(cfg, blocks, edges)
+    cos, sin = R.rope_tables(cfg)
+    return stack, cos, sin
+
+
+def time_kernels(cfg, stack, reps=20):
+    """Average device time of each block kernel at the stack's shapes, launched
+    through the stage entry points (same kernels and launch configuration as
+    inside dit_stack_step) on torch's current stream, timed with HIP events."""
+    import torch
+    from diffusion_transformer_dit_amd import native as N
+    from diffusion_transformer_dit_amd import runtime as R
+    dev = "cuda"
+    Nt, D, F, Dc, hd = cfg.tokens, cfg.hidden, cfg.ffn, cfg.cond_dim, cfg.head_dim
+    H, Hk, S, B = cfg.heads, cfg.kv_heads, cfg.seq, cfg.batch
+    blk = stack.blocks[0].t
+    desc = R.desc_of(cfg, "f32")
+    bf = torch.bfloat16
+    g = torch.Generator(device=dev).manual_seed(7)
+    x = torch.randn((Nt, D), generator=g, device=dev)
+    h = torch.randn((Nt, D), generator=g, device=dev).to(bf)
+    c = torch.randn((Dc,), generator=g, device=dev)
+    m = torch.empty(6 * D, device=dev)
+    q = torch.empty((B, H, S, hd), dtype=bf, device=dev)
+    k = torch.empty((B, Hk, S, hd), dtype=bf, device=dev)
+    vt = torch.empty((B, Hk, hd, N.dit_seq_pad(S)), dtype=bf, device=dev)
+    att = torch.empty((Nt, H * hd), dtype=bf, device=dev)
+    x1 = torch.empty((Nt, D), device=dev)
+    u = torch.empty((Nt, F), dtype=bf, device=dev)
+    cos, sin = R.rope_tables(cfg)
+    launches = {
+        "adaln_gemv": (lambda: N.dit_adaln_modulation(blk["w_ada"], blk["b_ada"], c, 6 * D, Dc, 1, m),
+                       "hbm", 6 * D * Dc * 2 + Dc * 4 + 6 * D * 4 * 2),
+        "ln_modulate": (lambda: N.dit_ln_modulate(x, N.DIT_F32, Nt, D, m, m[D:], 0, cfg.eps, h),
+                        "hbm", Nt * D * 4 + Nt * D * 2),
+        "gemm_qkv": (lambda: N.dit_qkv_rope(desc, h, blk["w_qkv"], blk["q_g"], blk["q_b"], blk["k_g"], blk["k_b"],
+                                            cos, sin, q, k, vt), "mfma", None),
+        "flash_attention": (lambda: N.dit_flash_attention(desc, q, k, vt, att), "mfma", None),
+        "gemm_out_proj": (lambda: N.dit_gemm_gated_residual(att, blk["w_o"], Nt, D, H * hd, x, N.DIT_F32, m[2 * D:],
+                                                            None, x1, N.DIT_F32), "mfma", None),
+        "gemm_swiglu": (lambda: N.dit_gemm_swiglu(h, blk["w_gate_up"], Nt, F, D, u), "mfma", None),
+        "gemm_down": (lambda: N.dit_gemm_gated_residual(u, blk["w_down"], Nt, D, F, x1, N.DIT_F32, m[5 * D:], None,
+                                                        x, N.DIT_F32), "mfma", None),
+    }
+    fl = block_flops(cfg)
+    out = {}
+    for name, (fn, bound, nbytes) in launches.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1000.0 / reps
+        if bound == "mfma":
+            tf = fl[name] / (us * 1e-6) / 1e12
+            out[name] = {"us": round(us, 2), "bound": "mfma", "achieved": round(tf, 1), "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "work": fl[name]}
+        else:
+            gbs = nbytes / (us * 1e-6) / 1e9
+            out[name] = {"us": round(us, 2), "bound": "hbm", "achieved": round(gbs, 1), "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "work": nbytes}
+    return out
+
+
+def cpu_baseline(cfg=I.C4):
+    """The float64 CPU oracle on a bounded sample of one step: one block of the
+    stack plus the stack edges, scaled by the block count to s/denoise-step."""
+    from oracle import dit as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("internal_api") == "openblas"]
+                      or [os.cpu_count() or 1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    w = I.block_weights(cfg, 0)
+    shared = I.shared_ada(cfg)
+    w["w_ada"], w["b_ada"] = shared["w_ada"], shared["b_ada"]
+    edges = I.stack_edges(cfg)
+    lat, pos = I.latent(cfg), I.positions(cfg)
+    sigma = 1.0
+    t0 = time.perf_counter()
+    c = O.timestep_embedding(1000.0 * sigma, cfg.cond_dim)
+    x = O.linear(lat, edges["w_in"], edges["b_in"])
+    x = O.block_forward(x, c, w, cfg, pos)
+    t_block_end = time.perf_counter()
+    v = O.final_layer(x, c, edges, cfg)
+    _ = O.euler_update(lat, v, 1.0, 0.9)
+    t1 = time.perf_counter()
+    block_s = t_block_end - t0          # includes the (tiny) patch embedding
+    edge_s = t1 - t_block_end
+    step_s = block_s * cfg.layers + edge_s
+    return {"value": round(step_s, 2), "unit": "s/denoise-step", "cores": int(threads), "kind": "oracle",
+            "sample": f"1 of {cfg.layers} blocks (4096 tok, hidden 4096, float64 NumPy) + patch-embed + final layer "
+                      f"+ Euler, timed once ({t1 - t0:.1f} s), block time x {cfg.layers}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=8)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--kernels-only", action="store_true", help="time the block kernels only")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the hot path is one DiT denoising step on one MI355X; "
+              "multi-GPU runs are not part of this benchmark (see DESIGN.md, sharding).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from diffusion_transformer_dit_amd import native as N
+    from diffusion_transformer_dit_amd import runtime as R
+    R.require_gpu()
+    cfg = I.C4
+    print(f"[bench] building {cfg.layers}-block stack (hidden {cfg.hidden}, {cfg.tokens} tokens)", file=sys.stderr,
+          flush=True)
+    stack, cos, sin = build_full_stack(cfg)
+    kern = time_kernels(cfg, stack)
+    print(f"[bench] kernels: {json.dumps({k: v['us'] for k, v in kern.items()})}", file=sys.stderr, flush=True)
+
+    lat = R.to_dev_f32(I.latent(cfg))
+    cond = torch.empty(cfg.cond_dim, dtype=torch.float32, device="cuda")
+    vel = torch.empty_like(lat)
+    sig = N.dit_flowmatch_sigmas(I.STACK_STEPS, I.STACK_SHIFT)
+
+    def one_step(i):
+        j = i % I.STACK_STEPS
+        N.dit_timestep_embedding(1000.0 * float(sig[j]), cfg.cond_dim, cond)
+        stack.step(lat, cond, cos, sin, vel)
+        N.euler_flowmatch_update(lat, vel, lat.numel(), float(sig[j]), float(sig[j + 1]))
+
+    for i in range(args.warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+    per = []
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(args.steps):
+        one_step(args.warmup + i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    ms = wall * 1000.0 / args.steps
+    assert torch.isfinite(lat).all().item(), "non-finite latent"
+
+    flops = step_flops(cfg)
+    util = flops / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
+    dom = kern["gemm_swiglu"]
+    roof = {"bound": "mfma", "kernel": "gemm_swiglu (SwiGLU up-GEMM, 4096 x 24576 x 4096)", "achieved": dom["achieved"],
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": dom["frac"], "traffic": None,
+            "avg_us": dom["us"]}
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] CPU oracle baseline (one block sample)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cfg)
+    line = {
+        "metric": METRIC, "value": round(ms / 1000.0, 6), "unit": "s/denoise-step", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "36-block DiT stack, hidden 4096, 32x128 heads, SwiGLU 12288, 4096 tokens (64x64 "
+                               "latent, 128 channels), one flow-match Euler step of 8 (shift 4)",
+                   "layers": cfg.layers, "hidden": cfg.hidden, "tokens": cfg.tokens, "heads": cfg.heads,
+                   "head_dim": cfg.head_dim, "ffn": cfg.ffn, "steps_per_loop": I.STACK_STEPS},
+        "mfma_util_pct": round(100.0 * util, 2),
+        "step_tflop": round(flops / 1e12, 3),
+        "step_ms_events": {"median": round(float(np.median(per)), 3), "min": round(min(per), 3),
+                           "max": round(max(per), 3)},
+        "roofline": roof,
+        "kernels": kern,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

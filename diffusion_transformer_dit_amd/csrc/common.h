@@ -1,0 +1,88 @@
+// Shared device types and helpers of the gfx950 kernels (internal header).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf2f(bf16 v) { return (float)v; }
+__device__ __forceinline__ bf16 f2bf(float v) { return (bf16)v; }   // v_cvt_pk_bf16_f32, round-to-nearest-even
+
+template <typename T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<bf16>(bf16 v) { return (float)v; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
+
+// butterfly sum over groups of `W` consecutive lanes (W a power of two <= 64)
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int m = 1; m < W; m <<= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+template <int W>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+    for (int m = 1; m < W; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+    return v;
+}
+
+__device__ __forceinline__ float silu_f(float z) {
+    // z * sigmoid(z); expf of a large positive -z gives inf and z/inf -> -0
+    return z / (1.0f + __expf(-z));
+}
+
+}  // namespace dit
+
+// ---------------------------------------------------------------------------
+// launchers (host side), implemented in the .hip files of this directory
+// ---------------------------------------------------------------------------
+namespace dit {
+
+struct QkvEpiArgs {
+    int batch, seq, seq_pad, heads, kv_heads, head_dim;
+    int qk_norm, rope_half;
+    float eps;
+    const float *q_g, *q_b, *k_g, *k_b;
+    const float *cos_t, *sin_t;
+    bf16 *q, *k, *vt;
+};
+
+hipError_t launch_gemm_residual(const bf16 *a, const bf16 *w, int64_t M, int N, int K,
+                                const void *resid, int resid_f32, const float *gate,
+                                const float *bias, void *out, int out_f32, hipStream_t s);
+hipError_t launch_gemm_swiglu(const bf16 *a, const bf16 *w, int64_t M, int F, int K,
+                              bf16 *u, hipStream_t s);
+hipError_t launch_gemm_qkv(const bf16 *h, const bf16 *w, int64_t M, int N, int K,
+                           const QkvEpiArgs &e, hipStream_t s);
+
+hipError_t launch_flash_attention(const bf16 *q, const bf16 *k, const bf16 *vt, bf16 *out,
+                                  int batch, int seq, int seq_pad, int heads, int kv_heads,
+                                  int head_dim, hipStream_t s);
+
+hipError_t launch_adaln_gemv(const bf16 *w, const float *b, const float *c, int out_dim,
+                             int in_dim, int silu_input, float *m, hipStream_t s);
+hipError_t launch_ln_modulate(const void *x, int x_f32, int64_t rows, int dim,
+                              const float *shift, const float *scale, int mode, float eps,
+                              bf16 *h, hipStream_t s);
+hipError_t launch_euler(float *latent, const float *v, int64_t n, float dsigma, hipStream_t s);
+hipError_t launch_timestep_embedding(float t, int dim, float *out, hipStream_t s);
+hipError_t launch_f32_to_bf16(const float *x, bf16 *y, int64_t n, hipStream_t s);
+hipError_t launch_vt_pad_zero(bf16 *vt, int rows, int seq, int seq_pad, hipStream_t s);
+
+}  // namespace dit

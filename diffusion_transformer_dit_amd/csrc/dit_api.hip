@@ -1,0 +1,497 @@
+// C ABI of libdit.so: argument validation, workspace layout and the
+// composition of the block / stack / loop entry points out of the kernels.
+#include "dit.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+
+#include "common.h"
+
+using namespace dit;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok() {
+    g_err.clear();
+    return DIT_OK;
+}
+
+#define DIT_TRY_HIP(expr)                                                                  \
+    do {                                                                                   \
+        hipError_t e_ = (expr);                                                            \
+        if (e_ != hipSuccess) return fail(DIT_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+    } while (0)
+
+#define DIT_TRY(expr)             \
+    do {                          \
+        int rc_ = (expr);         \
+        if (rc_ != DIT_OK) return rc_; \
+    } while (0)
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+bool aligned4(const void *p) { return ((uintptr_t)p & 3) == 0; }
+
+int device_check() {
+    static int status = 1;
+    static std::once_flag once;
+    std::call_once(once, [] {
+        int n = 0;
+        status = (hipGetDeviceCount(&n) == hipSuccess && n > 0) ? DIT_OK : DIT_ERR_NO_DEVICE;
+    });
+    if (status != DIT_OK) return fail(DIT_ERR_NO_DEVICE, "no HIP device is visible to this process");
+    return DIT_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int32_t seq_pad_of(int32_t s) { return (s + 63) / 64 * 64; }
+
+// Workspace of one block evaluation.
+struct BlockWs {
+    size_t m, h, q, k, vt, att, x1, u, total;
+};
+
+BlockWs block_ws(const dit_block_desc &d) {
+    const size_t N = (size_t)d.batch * d.seq, D = d.hidden, B = d.batch;
+    const size_t hd = d.head_dim, H = d.heads, Hk = d.kv_heads, F = d.ffn;
+    BlockWs L{};
+    size_t off = 0;
+    L.m = off;   off += align256(6 * D * 4);
+    L.h = off;   off += align256(N * D * 2);
+    L.q = off;   off += align256(B * H * d.seq * hd * 2);
+    L.k = off;   off += align256(B * Hk * d.seq * hd * 2);
+    L.vt = off;  off += align256(B * Hk * hd * (size_t)seq_pad_of(d.seq) * 2);
+    L.att = off; off += align256(N * H * hd * 2);
+    L.x1 = off;  off += align256(N * D * 4);
+    L.u = off;   off += align256(N * F * 2);
+    L.total = off;
+    return L;
+}
+
+int check_desc(const dit_block_desc *d) {
+    if (!d) return fail(DIT_ERR_INVALID_ARG, "desc is NULL");
+    if (d->batch <= 0 || d->seq <= 0 || d->hidden <= 0 || d->heads <= 0 || d->kv_heads <= 0 ||
+        d->head_dim <= 0 || d->ffn <= 0 || d->cond_dim < 0)
+        return fail(DIT_ERR_INVALID_ARG, "dimensions must be positive (cond_dim >= 0)");
+    if (d->heads * d->head_dim != d->hidden)
+        return fail(DIT_ERR_INVALID_ARG, "heads * head_dim (%d) != hidden (%d)", d->heads * d->head_dim, d->hidden);
+    if (d->heads % d->kv_heads != 0)
+        return fail(DIT_ERR_INVALID_ARG, "heads (%d) not a multiple of kv_heads (%d)", d->heads, d->kv_heads);
+    if (!(d->eps > 0.f) || !isfinite(d->eps)) return fail(DIT_ERR_INVALID_ARG, "eps must be positive and finite");
+    if (d->x_dtype != DIT_F32 && d->x_dtype != DIT_BF16) return fail(DIT_ERR_INVALID_ARG, "bad x_dtype");
+    if (d->rope != DIT_ROPE_INTERLEAVED && d->rope != DIT_ROPE_HALF) return fail(DIT_ERR_INVALID_ARG, "bad rope layout");
+    if (d->norm != DIT_LAYERNORM && d->norm != DIT_RMSNORM) return fail(DIT_ERR_INVALID_ARG, "bad norm kind");
+    if (d->norm != DIT_LAYERNORM) return fail(DIT_ERR_UNSUPPORTED, "only DIT_LAYERNORM is built");
+    if (d->w_dtype != DIT_BF16) return fail(DIT_ERR_UNSUPPORTED, "weights must be bf16");
+    if (d->head_dim != 64 && d->head_dim != 128) return fail(DIT_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+    if (d->hidden % 256) return fail(DIT_ERR_UNSUPPORTED, "hidden must be a multiple of 256");
+    if (d->hidden > 8192) return fail(DIT_ERR_UNSUPPORTED, "hidden must be <= 8192");
+    if (d->ffn % 128) return fail(DIT_ERR_UNSUPPORTED, "ffn must be a multiple of 128");
+    if (((d->heads + 2 * d->kv_heads) * d->head_dim) % 256)
+        return fail(DIT_ERR_UNSUPPORTED, "(heads + 2 kv_heads) * head_dim must be a multiple of 256");
+    if (d->cond_dim % 8) return fail(DIT_ERR_UNSUPPORTED, "cond_dim must be a multiple of 8");
+    const double n = (double)d->batch * d->seq;
+    if (n * d->ffn >= 2147483648.0 || n * d->hidden >= 2147483648.0 || (double)d->ffn * 2 * d->hidden >= 2147483648.0)
+        return fail(DIT_ERR_UNSUPPORTED, "a GEMM operand exceeds 2^31 elements");
+    return DIT_OK;
+}
+
+int check_weights(const dit_block_desc &d, const dit_block_weights *w) {
+    if (!w) return fail(DIT_ERR_INVALID_ARG, "weights is NULL");
+    if (!w->w_qkv || !w->w_o || !w->w_gate_up || !w->w_down)
+        return fail(DIT_ERR_INVALID_ARG, "w_qkv, w_o, w_gate_up and w_down are required");
+    if (!aligned16(w->w_qkv) || !aligned16(w->w_o) || !aligned16(w->w_gate_up) || !aligned16(w->w_down))
+        return fail(DIT_ERR_ALIGNMENT, "weight matrices must be 16-byte aligned");
+    if (d.cond_dim > 0) {
+        if (!w->w_ada || !w->b_ada) return fail(DIT_ERR_INVALID_ARG, "AdaLN mode needs w_ada and b_ada");
+        if (!aligned16(w->w_ada) || !aligned16(w->b_ada)) return fail(DIT_ERR_ALIGNMENT, "w_ada/b_ada must be 16-byte aligned");
+        if (w->ln1_g || w->ln1_b || w->ln2_g || w->ln2_b)
+            return fail(DIT_ERR_UNSUPPORTED, "LayerNorm affine is not used in AdaLN mode; pass NULL");
+    } else {
+        const float *v[4] = {w->ln1_g, w->ln1_b, w->ln2_g, w->ln2_b};
+        for (const float *p : v)
+            if (p && !aligned16(p)) return fail(DIT_ERR_ALIGNMENT, "LayerNorm gamma/beta must be 16-byte aligned");
+    }
+    if (d.qk_norm) {
+        if (!w->q_g || !w->q_b || !w->k_g || !w->k_b) return fail(DIT_ERR_INVALID_ARG, "qk_norm needs q_g, q_b, k_g, k_b");
+        if (!aligned4(w->q_g) || !aligned4(w->q_b) || !aligned4(w->k_g) || !aligned4(w->k_b))
+            return fail(DIT_ERR_ALIGNMENT, "qk-norm vectors must be 4-byte aligned");
+    }
+    return DIT_OK;
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+hipStream_t as_stream(void *s) { return (hipStream_t)s; }
+
+// The block body after the modulation vector m (or NULL without AdaLN) is ready.
+int block_body(const dit_block_desc &d, const dit_block_weights &w, const void *x, int x_f32, const float *m,
+               const float *cosT, const float *sinT, void *out, int out_f32, uint8_t *ws, const BlockWs &L,
+               hipStream_t s) {
+    const int64_t N = (int64_t)d.batch * d.seq;
+    const int D = d.hidden, hd = d.head_dim, F = d.ffn;
+    const int qkv_dim = (d.heads + 2 * d.kv_heads) * hd;
+    const int spad = seq_pad_of(d.seq);
+    bf16 *h = (bf16 *)(ws + L.h);
+    bf16 *q = (bf16 *)(ws + L.q), *k = (bf16 *)(ws + L.k), *vt = (bf16 *)(ws + L.vt);
+    bf16 *att = (bf16 *)(ws + L.att);
+    float *x1 = (float *)(ws + L.x1);
+    bf16 *u = (bf16 *)(ws + L.u);
+    const int mode = m ? 0 : 1;
+
+    DIT_TRY_HIP(launch_ln_modulate(x, x_f32, N, D, m ? m : w.ln1_b, m ? m + D : w.ln1_g, mode, d.eps, h, s));
+    DIT_TRY_HIP(launch_vt_pad_zero(vt, d.batch * d.kv_heads * hd, d.seq, spad, s));
+    QkvEpiArgs e{d.batch, d.seq, spad, d.heads, d.kv_heads, hd, d.qk_norm, d.rope == DIT_ROPE_HALF, d.eps,
+                 w.q_g, w.q_b, w.k_g, w.k_b, cosT, sinT, q, k, vt};
+    DIT_TRY_HIP(launch_gemm_qkv(h, (const bf16 *)w.w_qkv, N, qkv_dim, D, e, s));
+    DIT_TRY_HIP(launch_flash_attention(q, k, vt, att, d.batch, d.seq, spad, d.heads, d.kv_heads, hd, s));
+    DIT_TRY_HIP(launch_gemm_residual(att, (const bf16 *)w.w_o, N, D, d.heads * hd, x, x_f32, m ? m + 2 * D : nullptr,
+                                     nullptr, x1, 1, s));
+    DIT_TRY_HIP(launch_ln_modulate(x1, 1, N, D, m ? m + 3 * D : w.ln2_b, m ? m + 4 * D : w.ln2_g, mode, d.eps, h, s));
+    DIT_TRY_HIP(launch_gemm_swiglu(h, (const bf16 *)w.w_gate_up, N, F, D, u, s));
+    DIT_TRY_HIP(launch_gemm_residual(u, (const bf16 *)w.w_down, N, D, F, x1, 1, m ? m + 5 * D : nullptr, nullptr,
+                                     out, out_f32, s));
+    return DIT_OK;
+}
+
+// Stack workspace: the block workspace followed by the fp32 residual stream,
+// the final modulation and the bf16 copy of the latent.
+struct StackWs {
+    BlockWs blk;
+    size_t x, fm, lat, total;
+};
+
+StackWs stack_ws(const dit_model &mdl) {
+    StackWs L{};
+    L.blk = block_ws(mdl.blk);
+    const size_t N = (size_t)mdl.blk.batch * mdl.blk.seq, D = mdl.blk.hidden;
+    size_t off = L.blk.total;
+    L.x = off;   off += align256(N * D * 4);
+    L.fm = off;  off += align256(2 * D * 4);
+    L.lat = off; off += align256(N * (size_t)mdl.latent_dim * 2);
+    L.total = off;
+    return L;
+}
+
+int check_model(const dit_model *mdl) {
+    if (!mdl) return fail(DIT_ERR_INVALID_ARG, "model is NULL");
+    DIT_TRY(check_desc(&mdl->blk));
+    if (mdl->layers <= 0 || !mdl->blocks) return fail(DIT_ERR_INVALID_ARG, "layers must be > 0 and blocks non-NULL");
+    if (mdl->blk.cond_dim <= 0) return fail(DIT_ERR_INVALID_ARG, "the stack needs a conditioning vector (cond_dim > 0)");
+    if (mdl->blk.x_dtype != DIT_F32) return fail(DIT_ERR_UNSUPPORTED, "the stack keeps an fp32 residual stream (x_dtype F32)");
+    if (mdl->latent_dim <= 0 || mdl->latent_dim % 128) return fail(DIT_ERR_UNSUPPORTED, "latent_dim must be a multiple of 128");
+    if (!mdl->w_in || !mdl->b_in || !mdl->w_fmod || !mdl->b_fmod || !mdl->w_out || !mdl->b_out)
+        return fail(DIT_ERR_INVALID_ARG, "stack edge weights are required");
+    if (!aligned16(mdl->w_in) || !aligned16(mdl->w_fmod) || !aligned16(mdl->w_out) || !aligned16(mdl->b_in) ||
+        !aligned16(mdl->b_fmod) || !aligned16(mdl->b_out))
+        return fail(DIT_ERR_ALIGNMENT, "stack edge weights must be 16-byte aligned");
+    for (int l = 0; l < mdl->layers; ++l) DIT_TRY(check_weights(mdl->blk, &mdl->blocks[l]));
+    return DIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dit_version(void) { return "dit-gfx950 0.1"; }
+
+const char *dit_last_error(void) { return g_err.c_str(); }
+
+const char *dit_status_string(int st) {
+    switch (st) {
+        case DIT_OK: return "ok";
+        case DIT_ERR_INVALID_ARG: return "invalid argument";
+        case DIT_ERR_UNSUPPORTED: return "unsupported shape or option";
+        case DIT_ERR_WORKSPACE: return "workspace too small";
+        case DIT_ERR_ALIGNMENT: return "misaligned pointer";
+        case DIT_ERR_NO_DEVICE: return "no HIP device";
+        case DIT_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int32_t dit_seq_pad(int32_t seq) { return seq_pad_of(seq); }
+
+int dit_block_workspace_size(const dit_block_desc *desc, size_t *bytes) {
+    DIT_TRY(check_desc(desc));
+    if (!bytes) return fail(DIT_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = block_ws(*desc).total;
+    return ok();
+}
+
+int dit_block_forward(const dit_block_desc *desc, const dit_block_weights *w, const void *x, const float *cond,
+                      const float *rope_cos, const float *rope_sin, void *out, void *ws, size_t ws_bytes,
+                      void *stream) {
+    DIT_TRY(check_desc(desc));
+    const dit_block_desc &d = *desc;
+    DIT_TRY(check_weights(d, w));
+    if (!x || !out || !rope_cos || !rope_sin || !ws) return fail(DIT_ERR_INVALID_ARG, "x, out, rope tables and ws are required");
+    if ((d.cond_dim > 0) != (cond != nullptr)) return fail(DIT_ERR_INVALID_ARG, "cond must be given iff cond_dim > 0");
+    if (!aligned16(x) || !aligned16(out) || !aligned16(ws) || !aligned4(rope_cos) || !aligned4(rope_sin) ||
+        (cond && !aligned16(cond)))
+        return fail(DIT_ERR_ALIGNMENT, "x, out, ws, cond must be 16-byte aligned (rope tables 4-byte)");
+    const BlockWs L = block_ws(d);
+    if (ws_bytes < L.total) return fail(DIT_ERR_WORKSPACE, "workspace %zu < required %zu bytes", ws_bytes, L.total);
+    const size_t xbytes = (size_t)d.batch * d.seq * d.hidden * (d.x_dtype == DIT_F32 ? 4 : 2);
+    if (out != x && overlaps(out, xbytes, x, xbytes)) return fail(DIT_ERR_INVALID_ARG, "out overlaps x without being equal to it");
+    if (overlaps(ws, L.total, x, xbytes) || overlaps(ws, L.total, out, xbytes))
+        return fail(DIT_ERR_INVALID_ARG, "workspace overlaps x or out");
+    DIT_TRY(device_check());
+    hipStream_t s = as_stream(stream);
+    uint8_t *wsb = (uint8_t *)ws;
+    float *m = nullptr;
+    if (d.cond_dim > 0) {
+        m = (float *)(wsb + L.m);
+        DIT_TRY_HIP(launch_adaln_gemv((const bf16 *)w->w_ada, w->b_ada, cond, 6 * d.hidden, d.cond_dim, 1, m, s));
+    }
+    const int xf = d.x_dtype == DIT_F32;
+    DIT_TRY(block_body(d, *w, x, xf, m, rope_cos, rope_sin, out, xf, wsb, L, s));
+    return ok();
+}
+
+int dit_stack_workspace_size(const dit_model *model, size_t *bytes) {
+    DIT_TRY(check_model(model));
+    if (!bytes) return fail(DIT_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = stack_ws(*model).total;
+    return ok();
+}
+
+int dit_stack_step(const dit_model *model, const float *latent, const float *cond, const float *rope_cos,
+                   const float *rope_sin, float *velocity, void *ws, size_t ws_bytes, void *stream) {
+    DIT_TRY(check_model(model));
+    const dit_model &M = *model;
+    const dit_block_desc &d = M.blk;
+    if (!latent || !cond || !rope_cos || !rope_sin || !velocity || !ws)
+        return fail(DIT_ERR_INVALID_ARG, "latent, cond, rope tables, velocity and ws are required");
+    if (!aligned16(latent) || !aligned16(cond) || !aligned16(velocity) || !aligned16(ws) || !aligned4(rope_cos) ||
+        !aligned4(rope_sin))
+        return fail(DIT_ERR_ALIGNMENT, "latent, cond, velocity, ws must be 16-byte aligned");
+    const StackWs L = stack_ws(M);
+    if (ws_bytes < L.total) return fail(DIT_ERR_WORKSPACE, "workspace %zu < required %zu bytes", ws_bytes, L.total);
+    const int64_t N = (int64_t)d.batch * d.seq;
+    const size_t lbytes = (size_t)N * M.latent_dim * 4;
+    if (overlaps(ws, L.total, latent, lbytes) || overlaps(ws, L.total, velocity, lbytes))
+        return fail(DIT_ERR_INVALID_ARG, "workspace overlaps latent or velocity");
+    DIT_TRY(device_check());
+    hipStream_t s = as_stream(stream);
+    uint8_t *wsb = (uint8_t *)ws;
+    float *x = (float *)(wsb + L.x);
+    float *fm = (float *)(wsb + L.fm);
+    bf16 *lat = (bf16 *)(wsb + L.lat);
+    float *m = (float *)(wsb + L.blk.m);
+    const int D = d.hidden;
+
+    // patch embedding: x = bf16(latent) W_in^T + b_in (fp32 residual stream)
+    DIT_TRY_HIP(launch_f32_to_bf16(latent, lat, N * M.latent_dim, s));
+    DIT_TRY_HIP(launch_gemm_residual(lat, (const bf16 *)M.w_in, N, D, M.latent_dim, nullptr, 1, nullptr, M.b_in, x, 1, s));
+
+    bool shared = true;
+    for (int l = 1; l < M.layers; ++l)
+        shared = shared && M.blocks[l].w_ada == M.blocks[0].w_ada && M.blocks[l].b_ada == M.blocks[0].b_ada;
+    for (int l = 0; l < M.layers; ++l) {
+        const dit_block_weights &w = M.blocks[l];
+        if (l == 0 || !shared)
+            DIT_TRY_HIP(launch_adaln_gemv((const bf16 *)w.w_ada, w.b_ada, cond, 6 * D, d.cond_dim, 1, m, s));
+        DIT_TRY(block_body(d, w, x, 1, m, rope_cos, rope_sin, x, 1, wsb, L.blk, s));
+    }
+
+    // final AdaLN-continuous norm: [scale | shift] = W_f c + b_f (no SiLU), then projection
+    DIT_TRY_HIP(launch_adaln_gemv((const bf16 *)M.w_fmod, M.b_fmod, cond, 2 * D, d.cond_dim, 0, fm, s));
+    bf16 *h = (bf16 *)(wsb + L.blk.h);
+    DIT_TRY_HIP(launch_ln_modulate(x, 1, N, D, fm + D, fm, 0, d.eps, h, s));
+    DIT_TRY_HIP(launch_gemm_residual(h, (const bf16 *)M.w_out, N, M.latent_dim, D, nullptr, 1, nullptr, M.b_out,
+                                     velocity, 1, s));
+    return ok();
+}
+
+int euler_flowmatch_update(float *latent, const float *velocity, int64_t n, float sigma, float sigma_next,
+                           void *stream) {
+    if (!latent || !velocity) return fail(DIT_ERR_INVALID_ARG, "latent and velocity are required");
+    if (n < 0) return fail(DIT_ERR_INVALID_ARG, "n must be >= 0");
+    if (!aligned16(latent) || !aligned16(velocity)) return fail(DIT_ERR_ALIGNMENT, "latent/velocity must be 16-byte aligned");
+    if (latent != velocity && overlaps(latent, n * 4, velocity, n * 4))
+        return fail(DIT_ERR_INVALID_ARG, "latent and velocity overlap");
+    if (!isfinite(sigma) || !isfinite(sigma_next)) return fail(DIT_ERR_INVALID_ARG, "sigmas must be finite");
+    DIT_TRY(device_check());
+    if (n == 0) return ok();
+    DIT_TRY_HIP(launch_euler(latent, velocity, n, sigma_next - sigma, as_stream(stream)));
+    return ok();
+}
+
+int dit_timestep_embedding(float t, int32_t dim, float *cond_out, void *stream) {
+    if (!cond_out) return fail(DIT_ERR_INVALID_ARG, "cond_out is NULL");
+    if (dim <= 0 || dim % 2) return fail(DIT_ERR_INVALID_ARG, "dim must be positive and even");
+    if (!isfinite(t)) return fail(DIT_ERR_INVALID_ARG, "t must be finite");
+    DIT_TRY(device_check());
+    DIT_TRY_HIP(launch_timestep_embedding(t, dim, cond_out, as_stream(stream)));
+    return ok();
+}
+
+int dit_flowmatch_sigmas(int32_t steps, float shift, float *out) {
+    if (!out) return fail(DIT_ERR_INVALID_ARG, "sigmas_out is NULL");
+    if (steps <= 0) return fail(DIT_ERR_INVALID_ARG, "steps must be positive");
+    if (!(shift > 0.f) || !isfinite(shift)) return fail(DIT_ERR_INVALID_ARG, "shift must be positive");
+    for (int i = 0; i <= steps; ++i) {
+        const double s = 1.0 - (double)i / steps;
+        out[i] = (float)(shift * s / (1.0 + (shift - 1.0) * s));
+    }
+    return ok();
+}
+
+int dit_rope_tables(const int32_t *pos, int32_t seq, int32_t rope, const int32_t *axes, int32_t n_axes, float theta,
+                    int32_t head_dim, float *cos_out, float *sin_out) {
+    if (!pos || !axes || !cos_out || !sin_out) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+    if (seq <= 0 || head_dim <= 0 || head_dim % 2) return fail(DIT_ERR_INVALID_ARG, "bad seq/head_dim");
+    if (!(theta > 0.f)) return fail(DIT_ERR_INVALID_ARG, "theta must be positive");
+    int first_col;
+    if (rope == DIT_ROPE_INTERLEAVED) {
+        if (n_axes != 3) return fail(DIT_ERR_INVALID_ARG, "interleaved 3D RoPE takes 3 axes (t, h, w)");
+        first_col = 0;
+    } else if (rope == DIT_ROPE_HALF) {
+        if (n_axes != 2) return fail(DIT_ERR_INVALID_ARG, "rotate-half 2D RoPE takes 2 axes (h, w)");
+        first_col = 1;
+    } else {
+        return fail(DIT_ERR_INVALID_ARG, "bad rope layout");
+    }
+    int sum = 0;
+    for (int a = 0; a < n_axes; ++a) {
+        if (axes[a] <= 0 || axes[a] % 2) return fail(DIT_ERR_INVALID_ARG, "axis widths must be positive and even");
+        sum += axes[a];
+    }
+    if (sum != head_dim) return fail(DIT_ERR_INVALID_ARG, "axis widths sum to %d, head_dim is %d", sum, head_dim);
+    const int half = head_dim / 2;
+    for (int s = 0; s < seq; ++s) {
+        int m = 0;
+        for (int a = 0; a < n_axes; ++a) {
+            const double p = pos[s * 3 + first_col + a];
+            for (int j = 0; j < axes[a] / 2; ++j, ++m) {
+                const double ang = p * pow((double)theta, -2.0 * j / axes[a]);
+                cos_out[(size_t)s * half + m] = (float)cos(ang);
+                sin_out[(size_t)s * half + m] = (float)sin(ang);
+            }
+        }
+    }
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+// stage entry points
+// ---------------------------------------------------------------------------
+int dit_adaln_modulation(const void *w, const float *b, const float *c, int32_t out_dim, int32_t in_dim,
+                         int32_t silu_input, float *m, void *stream) {
+    if (!w || !c || !m) return fail(DIT_ERR_INVALID_ARG, "w, c and m are required");
+    if (out_dim <= 0 || in_dim <= 0) return fail(DIT_ERR_INVALID_ARG, "dims must be positive");
+    if (in_dim % 8) return fail(DIT_ERR_UNSUPPORTED, "in_dim must be a multiple of 8");
+    if (!aligned16(w) || !aligned16(c) || !aligned4(m) || (b && !aligned4(b)))
+        return fail(DIT_ERR_ALIGNMENT, "w and c must be 16-byte aligned");
+    DIT_TRY(device_check());
+    DIT_TRY_HIP(launch_adaln_gemv((const bf16 *)w, b, c, out_dim, in_dim, silu_input, m, as_stream(stream)));
+    return ok();
+}
+
+int dit_ln_modulate(const void *x, int32_t x_dtype, int64_t rows, int32_t dim, const float *shift, const float *scale,
+                    int32_t mode, float eps, void *h, void *stream) {
+    if (!x || !h) return fail(DIT_ERR_INVALID_ARG, "x and h are required");
+    if (rows <= 0 || dim <= 0) return fail(DIT_ERR_INVALID_ARG, "rows and dim must be positive");
+    if (x_dtype != DIT_F32 && x_dtype != DIT_BF16) return fail(DIT_ERR_INVALID_ARG, "bad x_dtype");
+    if (mode != 0 && mode != 1) return fail(DIT_ERR_INVALID_ARG, "mode must be 0 or 1");
+    if (mode == 0 && (!shift || !scale)) return fail(DIT_ERR_INVALID_ARG, "mode 0 needs shift and scale");
+    if (!(eps > 0.f)) return fail(DIT_ERR_INVALID_ARG, "eps must be positive");
+    if (dim % 256 || dim > 8192) return fail(DIT_ERR_UNSUPPORTED, "dim must be a multiple of 256 and <= 8192");
+    if (!aligned16(x) || !aligned16(h) || (shift && !aligned16(shift)) || (scale && !aligned16(scale)))
+        return fail(DIT_ERR_ALIGNMENT, "x, h, shift, scale must be 16-byte aligned");
+    DIT_TRY(device_check());
+    DIT_TRY_HIP(launch_ln_modulate(x, x_dtype == DIT_F32, rows, dim, shift, scale, mode, eps, (bf16 *)h,
+                                   as_stream(stream)));
+    return ok();
+}
+
+int dit_qkv_rope(const dit_block_desc *desc, const void *h, const void *w_qkv, const float *q_g, const float *q_b,
+                 const float *k_g, const float *k_b, const float *rope_cos, const float *rope_sin, void *q, void *k,
+                 void *vt, void *stream) {
+    DIT_TRY(check_desc(desc));
+    const dit_block_desc &d = *desc;
+    if (!h || !w_qkv || !rope_cos || !rope_sin || !q || !k || !vt) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+    if (d.qk_norm && (!q_g || !q_b || !k_g || !k_b)) return fail(DIT_ERR_INVALID_ARG, "qk_norm needs gamma/beta");
+    if (!aligned16(h) || !aligned16(w_qkv) || !aligned16(q) || !aligned16(k) || !aligned16(vt))
+        return fail(DIT_ERR_ALIGNMENT, "h, w_qkv, q, k, vt must be 16-byte aligned");
+    DIT_TRY(device_check());
+    hipStream_t s = as_stream(stream);
+    const int spad = seq_pad_of(d.seq);
+    DIT_TRY_HIP(launch_vt_pad_zero((bf16 *)vt, d.batch * d.kv_heads * d.head_dim, d.seq, spad, s));
+    QkvEpiArgs e{d.batch, d.seq, spad, d.heads, d.kv_heads, d.head_dim, d.qk_norm, d.rope == DIT_ROPE_HALF, d.eps,
+                 q_g, q_b, k_g, k_b, rope_cos, rope_sin, (bf16 *)q, (bf16 *)k, (bf16 *)vt};
+    DIT_TRY_HIP(launch_gemm_qkv((const bf16 *)h, (const bf16 *)w_qkv, (int64_t)d.batch * d.seq,
+                                (d.heads + 2 * d.kv_heads) * d.head_dim, d.hidden, e, s));
+    return ok();
+}
+
+int dit_flash_attention(const dit_block_desc *desc, const void *q, const void *k, const void *vt, void *out,
+                        void *stream) {
+    DIT_TRY(check_desc(desc));
+    const dit_block_desc &d = *desc;
+    if (!q || !k || !vt || !out) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(out))
+        return fail(DIT_ERR_ALIGNMENT, "q, k, vt, out must be 16-byte aligned");
+    DIT_TRY(device_check());
+    DIT_TRY_HIP(launch_flash_attention((const bf16 *)q, (const bf16 *)k, (const bf16 *)vt, (bf16 *)out, d.batch, d.seq,
+                                       seq_pad_of(d.seq), d.heads, d.kv_heads, d.head_dim, as_stream(stream)));
+    return ok();
+}
+
+int dit_gemm_gated_residual(const void *a, const void *w, int64_t M, int32_t N, int32_t K, const void *resid,
+                            int32_t resid_dtype, const float *gate, const float *bias, void *out, int32_t out_dtype,
+                            void *stream) {
+    if (!a || !w || !out) return fail(DIT_ERR_INVALID_ARG, "a, w and out are required");
+    if (M <= 0 || N <= 0 || K <= 0) return fail(DIT_ERR_INVALID_ARG, "dims must be positive");
+    if ((resid && resid_dtype != DIT_F32 && resid_dtype != DIT_BF16) || (out_dtype != DIT_F32 && out_dtype != DIT_BF16))
+        return fail(DIT_ERR_INVALID_ARG, "bad dtype");
+    if (N % 128 || K % 64) return fail(DIT_ERR_UNSUPPORTED, "N must be a multiple of 128 and K of 64");
+    if ((double)M * K >= 2147483648.0 || (double)N * K >= 2147483648.0)
+        return fail(DIT_ERR_UNSUPPORTED, "operand exceeds 2^31 elements");
+    if (!aligned16(a) || !aligned16(w) || !aligned16(out) || (resid && !aligned16(resid)) || (gate && !aligned4(gate)) ||
+        (bias && !aligned4(bias)))
+        return fail(DIT_ERR_ALIGNMENT, "a, w, out, resid must be 16-byte aligned");
+    const size_t ob = (size_t)M * N * (out_dtype == DIT_F32 ? 4 : 2);
+    const size_t rb = (size_t)M * N * (resid_dtype == DIT_F32 ? 4 : 2);
+    if (resid && resid != out && overlaps(resid, rb, out, ob)) return fail(DIT_ERR_INVALID_ARG, "resid overlaps out");
+    if (resid == out && resid && resid_dtype != out_dtype) return fail(DIT_ERR_INVALID_ARG, "in-place needs equal dtypes");
+    DIT_TRY(device_check());
+    DIT_TRY_HIP(launch_gemm_residual((const bf16 *)a, (const bf16 *)w, M, N, K, resid, resid_dtype == DIT_F32, gate, bias,
+                                     out, out_dtype == DIT_F32, as_stream(stream)));
+    return ok();
+}
+
+int dit_gemm_swiglu(const void *a, const void *w_gate_up, int64_t M, int32_t F, int32_t K, void *u, void *stream) {
+    if (!a || !w_gate_up || !u) return fail(DIT_ERR_INVALID_ARG, "a, w_gate_up and u are required");
+    if (M <= 0 || F <= 0 || K <= 0) return fail(DIT_ERR_INVALID_ARG, "dims must be positive");
+    if (F % 128 || K % 64) return fail(DIT_ERR_UNSUPPORTED, "F must be a multiple of 128 and K of 64");
+    if ((double)M * K >= 2147483648.0 || 2.0 * F * K >= 2147483648.0 || (double)M * F >= 2147483648.0)
+        return fail(DIT_ERR_UNSUPPORTED, "operand exceeds 2^31 elements");
+    if (!aligned16(a) || !aligned16(w_gate_up) || !aligned16(u)) return fail(DIT_ERR_ALIGNMENT, "16-byte alignment required");
+    DIT_TRY(device_check());
+    DIT_TRY_HIP(launch_gemm_swiglu((const bf16 *)a, (const bf16 *)w_gate_up, M, F, K, (bf16 *)u, as_stream(stream)));
+    return ok();
+}
+
+}  // extern "C"

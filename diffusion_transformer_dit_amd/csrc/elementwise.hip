@@ -1,0 +1,234 @@
+// Memory-bound kernels of the block and the loop (gfx950):
+//   adaln_gemv     m = W act(c) + b            (ERNIE page §IV: 6-way AdaLN modulation;
+//                                               §V Bug 4: final modulation, no SiLU)
+//   ln_modulate    h = LN(x) * mul + add       (ERNIE page §V Bug 4 modulation form;
+//                                               makepad log: affine LN of the ViT)
+//   euler          latent += dsigma * v        (zml-flow-rs page §IV "Euler sign +1")
+//   timestep_emb   [cos(t w) | sin(t w)]       (zml-flow-rs page §IV flip_sin_to_cos)
+//   f32_to_bf16, vt_pad_zero                   (layout helpers of the path)
+#include <algorithm>
+
+#include "common.h"
+
+namespace dit {
+
+// ---------------------------------------------------------------------------
+// AdaLN GEMV: one wave per 4 output rows; each lane streams 16-byte chunks of
+// the 4 weight rows (8 bf16 each) against act(c) of the same 8 inputs, so a
+// lane keeps 8 independent 16-byte loads in flight per unrolled step.
+// ---------------------------------------------------------------------------
+constexpr int kGemvRows = 4;
+
+__global__ __launch_bounds__(256)
+void adaln_gemv_kernel(const bf16 *__restrict__ W, const float *__restrict__ b, const float *__restrict__ c,
+                       int out_dim, int in_dim, int silu_input, float *__restrict__ m) {
+    const int lane = threadIdx.x & 63;
+    const int o0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kGemvRows;
+    if (o0 >= out_dim) return;
+    const int nch = in_dim >> 3;   // 8-element chunks per row
+    float acc[kGemvRows] = {0.f, 0.f, 0.f, 0.f};
+    const bf16 *wr[kGemvRows];
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r) wr[r] = W + (size_t)min(o0 + r, out_dim - 1) * in_dim;
+
+    for (int ch0 = lane; ch0 < nch; ch0 += 128) {
+        bf16x8 wv[2][kGemvRows];
+        floatx4 c0[2], c1[2];
+        bool ok[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int ch = ch0 + u * 64;
+            ok[u] = ch < nch;
+            const int chs = ok[u] ? ch : ch0;
+#pragma unroll
+            for (int r = 0; r < kGemvRows; ++r) wv[u][r] = *(const bf16x8 *)(wr[r] + chs * 8);
+            c0[u] = *(const floatx4 *)(c + chs * 8);
+            c1[u] = *(const floatx4 *)(c + chs * 8 + 4);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            if (!ok[u]) continue;
+            float a[8] = {c0[u][0], c0[u][1], c0[u][2], c0[u][3], c1[u][0], c1[u][1], c1[u][2], c1[u][3]};
+            if (silu_input) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) a[k] = silu_f(a[k]);
+            }
+#pragma unroll
+            for (int r = 0; r < kGemvRows; ++r)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) acc[r] += (float)wv[u][r][k] * a[k];
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r) {
+        const float s = group_sum<64>(acc[r]);
+        if (lane == 0 && o0 + r < out_dim) m[o0 + r] = s + (b ? b[o0 + r] : 0.f);
+    }
+}
+
+hipError_t launch_adaln_gemv(const bf16 *w, const float *b, const float *c, int out_dim, int in_dim,
+                             int silu_input, float *m, hipStream_t s) {
+    const int waves = (out_dim + kGemvRows - 1) / kGemvRows;
+    hipLaunchKernelGGL(adaln_gemv_kernel, dim3((waves + 3) / 4), dim3(256), 0, s, w, b, c, out_dim, in_dim,
+                       silu_input, m);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// LayerNorm + modulation, one wave per row.  The row stays in registers
+// (dim/256 float4 per lane) between the mean pass, the centred variance pass
+// and the output pass, so x is read from HBM exactly once.
+//   mode 0: h = n * (1 + scale) + shift      mode 1: h = n * scale + shift
+// ---------------------------------------------------------------------------
+constexpr int kLnMaxIt = 32;   // dim <= 32 * 256
+
+template <typename TX>
+__global__ __launch_bounds__(256)
+void ln_modulate_kernel(const TX *__restrict__ x, int64_t rows, int dim, const float *__restrict__ shift,
+                        const float *__restrict__ scale, int mode, float eps, bf16 *__restrict__ h) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const int iters = dim >> 8;
+    const TX *xr = x + row * dim;
+    floatx4 v[kLnMaxIt];
+    float s = 0.f;
+#pragma unroll
+    for (int it = 0; it < kLnMaxIt; ++it) {
+        if (it < iters) {
+            const int i = it * 256 + lane * 4;
+            if constexpr (sizeof(TX) == 4) {
+                v[it] = *(const floatx4 *)(xr + i);
+            } else {
+                const bf16x4 t = *(const bf16x4 *)(xr + i);
+                v[it] = floatx4{(float)t[0], (float)t[1], (float)t[2], (float)t[3]};
+            }
+            s += (v[it][0] + v[it][1]) + (v[it][2] + v[it][3]);
+        }
+    }
+    const float mean = group_sum<64>(s) / (float)dim;
+    float ss = 0.f;
+#pragma unroll
+    for (int it = 0; it < kLnMaxIt; ++it) {
+        if (it < iters) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float d = v[it][k] - mean;
+                v[it][k] = d;
+                ss += d * d;
+            }
+        }
+    }
+    const float rstd = rsqrtf(group_sum<64>(ss) / (float)dim + eps);
+    bf16 *hr = h + row * dim;
+#pragma unroll
+    for (int it = 0; it < kLnMaxIt; ++it) {
+        if (it < iters) {
+            const int i = it * 256 + lane * 4;
+            floatx4 mul = {1.f, 1.f, 1.f, 1.f}, add = {0.f, 0.f, 0.f, 0.f};
+            if (scale) mul = *(const floatx4 *)(scale + i);
+            if (mode == 0) mul += 1.0f;
+            if (shift) add = *(const floatx4 *)(shift + i);
+            bf16x4 o;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) o[k] = f2bf(v[it][k] * rstd * mul[k] + add[k]);
+            *(bf16x4 *)(hr + i) = o;
+        }
+    }
+}
+
+hipError_t launch_ln_modulate(const void *x, int x_f32, int64_t rows, int dim, const float *shift,
+                              const float *scale, int mode, float eps, bf16 *h, hipStream_t s) {
+    const dim3 grid((unsigned)((rows + 3) / 4));
+    if (x_f32)
+        hipLaunchKernelGGL(ln_modulate_kernel<float>, grid, dim3(256), 0, s, (const float *)x, rows, dim, shift,
+                           scale, mode, eps, h);
+    else
+        hipLaunchKernelGGL(ln_modulate_kernel<bf16>, grid, dim3(256), 0, s, (const bf16 *)x, rows, dim, shift,
+                           scale, mode, eps, h);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Euler step: latent += dsigma * v  (float4 body, scalar tail)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256)
+void euler_kernel(float *__restrict__ lat, const float *__restrict__ v, int64_t n, float dsigma) {
+    const int64_t n4 = n >> 2;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+        floatx4 a = ((floatx4 *)lat)[i];
+        const floatx4 b = ((const floatx4 *)v)[i];
+        a += dsigma * b;
+        ((floatx4 *)lat)[i] = a;
+    }
+    if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
+        const int64_t i = n4 * 4 + threadIdx.x;
+        lat[i] += dsigma * v[i];
+    }
+}
+
+hipError_t launch_euler(float *latent, const float *v, int64_t n, float dsigma, hipStream_t s) {
+    const int64_t n4 = (n >> 2) + 1;
+    const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 4096);
+    hipLaunchKernelGGL(euler_kernel, dim3(blocks), dim3(256), 0, s, latent, v, n, dsigma);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// timestep embedding [cos(t w_j) | sin(t w_j)], w_j = exp(-ln(1e4) j / half)
+// ---------------------------------------------------------------------------
+__global__ void timestep_embedding_kernel(float t, int half, float *__restrict__ out) {
+    const int j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= half) return;
+    const float w = expf(-9.210340371976184f * (float)j / (float)half);   // ln(10000)
+    const float a = t * w;
+    out[j] = cosf(a);
+    out[half + j] = sinf(a);
+}
+
+hipError_t launch_timestep_embedding(float t, int dim, float *out, hipStream_t s) {
+    const int half = dim / 2;
+    hipLaunchKernelGGL(timestep_embedding_kernel, dim3((half + 255) / 256), dim3(256), 0, s, t, half, out);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// fp32 -> bf16 (round to nearest even)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256)
+void f32_to_bf16_kernel(const float *__restrict__ x, bf16 *__restrict__ y, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) y[i] = f2bf(x[i]);
+}
+
+hipError_t launch_f32_to_bf16(const float *x, bf16 *y, int64_t n, hipStream_t s) {
+    const int blocks = (int)std::min<int64_t>((n + 255) / 256, 8192);
+    hipLaunchKernelGGL(f32_to_bf16_kernel, dim3(blocks), dim3(256), 0, s, x, y, n);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// zero the padded key positions [seq, seq_pad) of every row of transposed V
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256)
+void vt_pad_zero_kernel(bf16 *__restrict__ vt, int rows, int seq, int seq_pad) {
+    const int pad = seq_pad - seq;
+    const int64_t n = (int64_t)rows * pad;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+        const int64_t r = i / pad;
+        const int c = (int)(i - r * pad);
+        vt[r * seq_pad + seq + c] = f2bf(0.f);
+    }
+}
+
+hipError_t launch_vt_pad_zero(bf16 *vt, int rows, int seq, int seq_pad, hipStream_t s) {
+    const int64_t n = (int64_t)rows * (seq_pad - seq);
+    if (n <= 0) return hipSuccess;
+    const int blocks = (int)std::min<int64_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(vt_pad_zero_kernel, dim3(blocks), dim3(256), 0, s, vt, rows, seq, seq_pad);
+    return hipGetLastError();
+}
+
+}  // namespace dit

@@ -1,0 +1,266 @@
+/*
+ * dit.h -- C ABI of libdit.so: the forward pass of a pre-norm AdaLN
+ * diffusion-transformer block, the block stack of one flow-match denoising
+ * step, and the Euler update, as hand-written HIP kernels for gfx950 (MI355X).
+ *
+ * Sources for what each call computes (the pages the method comes from):
+ *   [ERNIE]   "Porting ERNIE-Image-Turbo to Zig and Metal: An 8B Diffusion
+ *             Transformer From Scratch on Apple Silicon"
+ *   [ZML]     "From Python + CUDA to Pure Rust + Metal 4: How zml-flow-rs
+ *             Stops Us Writing a Kernel Per Model"
+ *   [MAKEPAD] makepad commit log (libs/ai/metal/shaders/ggml): the resident
+ *             pre-norm ViT backbone.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named as device memory are device memory owned by the caller;
+ *     the library never frees, keeps or reallocates them, and allocates no
+ *     device memory of its own: scratch space comes in through `ws`.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
+ *     enqueued asynchronously; no call synchronises the host.  A fault inside
+ *     a kernel is reported by the caller's next hipStreamSynchronize.
+ *   - Every call validates its arguments before launching anything and
+ *     returns a dit_status; it never aborts.  dit_last_error() then gives a
+ *     thread-local message.  Without a usable GPU the compute calls return
+ *     DIT_ERR_NO_DEVICE (after argument validation).
+ *   - Device pointers must be 16-byte aligned (DIT_ERR_ALIGNMENT otherwise).
+ *   - GEMM weights are [out_features, in_features] row-major (y = x W^T),
+ *     bf16.  Accumulation is fp32 everywhere.
+ *   - Repeated calls with the same inputs are bitwise identical (no atomics).
+ *   - Calls on different streams are thread-safe when their workspaces and
+ *     outputs are distinct.
+ */
+#ifndef DIT_H
+#define DIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DIT_OK = 0,
+    DIT_ERR_INVALID_ARG = -1,   /* null pointer, bad dimension, illegal aliasing   */
+    DIT_ERR_UNSUPPORTED = -2,   /* valid request the kernels are not built for      */
+    DIT_ERR_WORKSPACE = -3,     /* ws_bytes smaller than the *_workspace_size value */
+    DIT_ERR_ALIGNMENT = -4,     /* a device pointer is not 16-byte aligned          */
+    DIT_ERR_NO_DEVICE = -5,     /* no HIP device visible                            */
+    DIT_ERR_HIP = -6            /* a HIP runtime call or kernel launch failed       */
+} dit_status;
+
+typedef enum { DIT_F32 = 0, DIT_BF16 = 1 } dit_dtype;
+typedef enum { DIT_LAYERNORM = 0, DIT_RMSNORM = 1 } dit_norm;
+/* RoPE pair layout: (2m, 2m+1) interleaved, or rotate-half (m, m + hd/2). */
+typedef enum { DIT_ROPE_INTERLEAVED = 0, DIT_ROPE_HALF = 1 } dit_rope;
+
+/* Shape and semantic switches of one block.
+ *   tokens N = batch * seq; attention runs within each sequence.
+ *   heads * head_dim must equal hidden; heads % kv_heads == 0 (grouped KV:
+ *   query head h reads KV head h / (heads / kv_heads)).
+ *   cond_dim > 0: AdaLN mode ([ERNIE] §IV): modulation from the conditioning
+ *     vector, LayerNorm without affine, gated residuals.
+ *   cond_dim == 0: plain pre-norm block ([MAKEPAD] ViT): affine LayerNorm
+ *     (ln*_g / ln*_b), gates fixed at 1.
+ *   qk_norm: per-(token, head) LayerNorm of q and k over head_dim with the
+ *     [head_dim] gamma/beta, applied before RoPE ([ZML] §VI "QKV + norm + RoPE").
+ *   norm: only DIT_LAYERNORM is built (DIT_RMSNORM returns UNSUPPORTED).
+ *   eps: epsilon of every norm of the block.
+ *   x_dtype: dtype of x and out (residual arithmetic is fp32 either way).
+ *   w_dtype: must be DIT_BF16.
+ * Built shapes: head_dim in {64, 128}; hidden % 256 == 0; ffn % 128 == 0;
+ * (heads + 2 kv_heads) * head_dim % 256 == 0; cond_dim % 8 == 0; any seq >= 1
+ * (ragged tails handled in every kernel). */
+typedef struct {
+    int32_t batch, seq, hidden, heads, kv_heads, head_dim, ffn, cond_dim;
+    int32_t qk_norm;
+    int32_t norm;      /* dit_norm  */
+    int32_t rope;      /* dit_rope  */
+    float eps;
+    int32_t x_dtype;   /* dit_dtype */
+    int32_t w_dtype;   /* dit_dtype */
+} dit_block_desc;
+
+/* Device pointers to one block's parameters (NULL where marked optional).
+ *   w_ada  [6*hidden, cond_dim] bf16, b_ada [6*hidden] fp32: AdaLN linear whose
+ *          output splits into (shift1, scale1, gate1, shift2, scale2, gate2)
+ *          ([ERNIE] §IV).  Required iff cond_dim > 0.
+ *   ln1_g, ln1_b, ln2_g, ln2_b [hidden] fp32: affine of the pre-norms; used
+ *          only when cond_dim == 0 (NULL = gamma 1 / beta 0); must be NULL in
+ *          AdaLN mode.
+ *   w_qkv  [(heads + 2 kv_heads) * head_dim, hidden] bf16: rows are the q heads,
+ *          then the k heads, then the v heads.
+ *   q_g, q_b, k_g, k_b [head_dim] fp32: qk-norm affine; required iff qk_norm.
+ *   w_o    [hidden, heads * head_dim] bf16.
+ *   w_gate_up [2 * ffn, hidden] bf16: the ffn gate rows first, then the ffn up
+ *          rows (SwiGLU: SiLU(gate) * up).
+ *   w_down [hidden, ffn] bf16. */
+typedef struct {
+    const void *w_ada;
+    const float *b_ada;
+    const float *ln1_g, *ln1_b, *ln2_g, *ln2_b;
+    const void *w_qkv;
+    const float *q_g, *q_b, *k_g, *k_b;
+    const void *w_o, *w_gate_up, *w_down;
+} dit_block_weights;
+
+/* ------------------------------------------------------------------------ */
+/* Block                                                                     */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of device workspace dit_block_forward needs for `desc`. */
+int dit_block_workspace_size(const dit_block_desc *desc, size_t *bytes);
+
+/* out = block(x, cond) ([ERNIE] §IV per-layer compute graph, with the SwiGLU
+ * feed-forward and the gated fp32 residual of §VII Decision 1):
+ *   m   = W_ada SiLU(cond) + b_ada        -> shift1 scale1 gate1 shift2 scale2 gate2
+ *   h   = LN(x) (1 + scale1) + shift1     (bf16)
+ *   q,k,v = h W_qkv^T; q,k <- RoPE(qkLN(q,k))          (bf16)
+ *   x1  = x + gate1 * (softmax(q k^T / sqrt(hd)) v  W_o^T)   (fp32)
+ *   h2  = LN(x1) (1 + scale2) + shift2    (bf16)
+ *   out = x1 + gate2 * ((SiLU(h2 Wg^T) * (h2 Wu^T)) W_down^T)
+ * x, out: device [batch*seq, hidden] of desc->x_dtype; out may equal x
+ *   (in-place residual, [MAKEPAD]); any other overlap is INVALID_ARG.
+ * cond: device fp32 [cond_dim] (NULL iff cond_dim == 0).
+ * rope_cos, rope_sin: device fp32 [seq, head_dim/2]: cos/sin of the rotation
+ *   angle of pair slot m for sequence position s (see dit_rope_tables); pair
+ *   slot m rotates dims (2m, 2m+1) (INTERLEAVED) or (m, m + hd/2) (HALF).
+ * ws: device workspace of at least dit_block_workspace_size bytes. */
+int dit_block_forward(const dit_block_desc *desc, const dit_block_weights *w,
+                      const void *x, const float *cond,
+                      const float *rope_cos, const float *rope_sin,
+                      void *out, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Stack step and denoising loop                                             */
+/* ------------------------------------------------------------------------ */
+
+/* A stack of `layers` blocks of one shape plus the stack edges
+ * ([ERNIE] §IV and §V Bug 4).  `blocks` is a HOST array of `layers` weight
+ * sets (device pointers inside).  Blocks may share one AdaLN linear: when
+ * every block's (w_ada, b_ada) equals block 0's, the modulation is computed
+ * once per step.  blk.x_dtype must be DIT_F32 (fp32 residual stream).
+ *   w_in  [hidden, latent_dim] bf16, b_in [hidden] fp32: patch embedding.
+ *   w_fmod [2*hidden, cond_dim] bf16, b_fmod [2*hidden] fp32: final
+ *         modulation, chunks (scale, shift) -- the reverse of the per-layer
+ *         order ([ERNIE] §V Bug 4); applied to cond without SiLU.
+ *   w_out [latent_dim, hidden] bf16, b_out [latent_dim] fp32. */
+typedef struct {
+    dit_block_desc blk;
+    int32_t layers, latent_dim;
+    const dit_block_weights *blocks;
+    const void *w_in;
+    const float *b_in;
+    const void *w_fmod;
+    const float *b_fmod;
+    const void *w_out;
+    const float *b_out;
+} dit_model;
+
+int dit_stack_workspace_size(const dit_model *model, size_t *bytes);
+
+/* velocity = final(block_{L-1}(... block_0(latent W_in^T + b_in, cond) ...), cond)
+ * with final(x, c) = (LN(x)(1 + scale_f) + shift_f) W_out^T + b_out.
+ * latent (read-only), velocity: device fp32 [batch*seq, latent_dim].
+ * cond: device fp32 [cond_dim] (e.g. from dit_timestep_embedding).
+ * The latent is rounded to bf16 before the patch-embedding GEMM. */
+int dit_stack_step(const dit_model *model, const float *latent, const float *cond,
+                   const float *rope_cos, const float *rope_sin, float *velocity,
+                   void *ws, size_t ws_bytes, void *stream);
+
+/* latent[i] += (sigma_next - sigma) * velocity[i] for i < n, fp32, in place
+ * (flow-match Euler step; [ZML] §IV "Euler sign +1"). */
+int euler_flowmatch_update(float *latent, const float *velocity, int64_t n,
+                           float sigma, float sigma_next, void *stream);
+
+/* cond_out[j] = cos(t w_j), cond_out[dim/2 + j] = sin(t w_j),
+ * w_j = exp(-ln(10000) j / (dim/2)): the flip_sin_to_cos sinusoidal timestep
+ * features ([ZML] §IV).  dim even, > 0; cond_out device fp32 [dim]. */
+int dit_timestep_embedding(float t, int32_t dim, float *cond_out, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Host helpers (no device work)                                             */
+/* ------------------------------------------------------------------------ */
+
+/* sigmas_out[i] = shift * s / (1 + (shift - 1) s), s = 1 - i/steps, i = 0..steps
+ * (FlowMatchEulerDiscreteScheduler grid with the time shift, [ERNIE] §I).
+ * sigmas_out: host fp32 [steps + 1]. */
+int dit_flowmatch_sigmas(int32_t steps, float shift, float *sigmas_out);
+
+/* RoPE cos/sin tables for `seq` positions.  pos: host int32 [seq, 3] (t, h, w).
+ * The head dim is split into contiguous per-axis chunks of widths axes[0..n_axes)
+ * (sum = head_dim); pair slot j of the chunk of axis a rotates by
+ * pos_a * theta^(-2j / axes[a]).  rope == INTERLEAVED uses axes (t, h, w)
+ * (n_axes 3, [ERNIE] §I axes [32,48,48] theta 256); rope == HALF uses (h, w)
+ * (n_axes 2, the ViT of [MAKEPAD]).  cos_out, sin_out: host fp32 [seq, head_dim/2]. */
+int dit_rope_tables(const int32_t *pos, int32_t seq, int32_t rope, const int32_t *axes,
+                    int32_t n_axes, float theta, int32_t head_dim,
+                    float *cos_out, float *sin_out);
+
+/* ------------------------------------------------------------------------ */
+/* Stage entry points: each stage of dit_block_forward on its own, with the  */
+/* same kernels, for per-stage parity checks and timing.                     */
+/* ------------------------------------------------------------------------ */
+
+/* m[o] = sum_k W[o,k] act(c[k]) + b[o], act = SiLU if silu_input else identity.
+ * W device bf16 [out_dim, in_dim]; b device fp32 [out_dim] or NULL; c device
+ * fp32 [in_dim]; m device fp32 [out_dim].  in_dim % 8 == 0.
+ * ([ERNIE] §IV AdaLN modulation; §V Bug 4 final modulation without SiLU.) */
+int dit_adaln_modulation(const void *w, const float *b, const float *c, int32_t out_dim,
+                         int32_t in_dim, int32_t silu_input, float *m, void *stream);
+
+/* Row LayerNorm + modulation to bf16: h = LN(x) * mul + add, where
+ * mode 0: mul = 1 + scale, add = shift (AdaLN; scale/shift fp32 [dim], required);
+ * mode 1: mul = scale, add = shift (affine LN; either may be NULL = 1 / 0).
+ * x device [rows, dim] of x_dtype; h device bf16 [rows, dim]; dim % 256 == 0,
+ * dim <= 8192. */
+int dit_ln_modulate(const void *x, int32_t x_dtype, int64_t rows, int32_t dim,
+                    const float *shift, const float *scale, int32_t mode, float eps,
+                    void *h, void *stream);
+
+/* QKV GEMM with the qk-LayerNorm and RoPE epilogue.
+ * h device bf16 [batch*seq, hidden]; outputs (device bf16):
+ *   q  [batch, heads, seq, head_dim]
+ *   k  [batch, kv_heads, seq, head_dim]
+ *   vt [batch, kv_heads, head_dim, seq_pad], seq_pad = dit_seq_pad(seq):
+ *      V transposed; positions [seq, seq_pad) are written with zeros. */
+int dit_qkv_rope(const dit_block_desc *desc, const void *h, const void *w_qkv,
+                 const float *q_g, const float *q_b, const float *k_g, const float *k_b,
+                 const float *rope_cos, const float *rope_sin,
+                 void *q, void *k, void *vt, void *stream);
+
+/* Padded key count of the transposed V layout: seq rounded up to 64. */
+int32_t dit_seq_pad(int32_t seq);
+
+/* Mask-free flash attention: out[b*seq + s, h*hd + d] =
+ * sum_j softmax_j(q[b,h,s,:] . k[b,g,j,:] / sqrt(hd)) v[b,g,j,d], g = h/(H/Hkv)
+ * ([ERNIE] §VII Decision 2 and §IX "Flash SDPA").  q, k, vt in the layouts of
+ * dit_qkv_rope; out device bf16 [batch*seq, heads*head_dim]. */
+int dit_flash_attention(const dit_block_desc *desc, const void *q, const void *k,
+                        const void *vt, void *out, void *stream);
+
+/* out = resid + gate * (a W^T) + bias over an [M, N] output:
+ * a device bf16 [M, K]; W device bf16 [N, K]; resid device [M, N] of
+ * resid_dtype or NULL; gate, bias device fp32 [N] or NULL (gate NULL = 1,
+ * bias NULL = 0); out device [M, N] of out_dtype (may equal resid).
+ * N % 128 == 0, K % 64 == 0.  ([ERNIE] §VII Decision 1: gated residual with
+ * fp32 accumulation; out-projection and down-projection epilogue.) */
+int dit_gemm_gated_residual(const void *a, const void *w, int64_t M, int32_t N, int32_t K,
+                            const void *resid, int32_t resid_dtype, const float *gate,
+                            const float *bias, void *out, int32_t out_dtype, void *stream);
+
+/* u = SiLU(a Wg^T) * (a Wu^T) with W = [Wg; Wu] device bf16 [2F, K];
+ * a device bf16 [M, K]; u device bf16 [M, F].  F % 128 == 0, K % 64 == 0. */
+int dit_gemm_swiglu(const void *a, const void *w_gate_up, int64_t M, int32_t F, int32_t K,
+                    void *u, void *stream);
+
+/* ------------------------------------------------------------------------ */
+const char *dit_status_string(int status);
+const char *dit_last_error(void);
+/* Library version string. */
+const char *dit_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DIT_H */

@@ -77,6 +77,26 @@ def modulate(n, shift, scale):
     return n * (1.0 + scale) + shift
 
 
+def linear(x, w, b=None, dtype=F64):
+    """y = x W^T (+ b) for W stored [out, in]."""
+    y = np.asarray(x, dtype) @ np.asarray(w, dtype).T
+    return y if b is None else y + np.asarray(b, dtype)
+
+
+def gated_residual(r, gate, y):
+    """r + gate * y, with the residual kept in full precision ([ERNIE] §VII
+    Decision 1 prints this gated residual)."""
+    return r + gate * y
+
+
+def swiglu(h, w_gate_up, dtype=F64):
+    """SiLU(h Wg^T) * (h Wu^T) with W = [Wg; Wu] stacked gate rows first
+    ([ZML] §VI: Glu step with gate_first; SwiGLU names the SiLU gate)."""
+    w = np.asarray(w_gate_up, dtype)
+    F = w.shape[0] // 2
+    return silu(linear(h, w[:F], dtype=dtype)) * linear(h, w[F:], dtype=dtype)
+
+
 # ---------------------------------------------------------------------------
 # conditioning
 # ---------------------------------------------------------------------------
@@ -200,7 +220,7 @@ def block_qkv(h, w, spec, pos, dtype=F64):
     order taken here.  Returns q [N,H,hd], k/v [N,Hkv,hd]."""
     H, Hk, hd = spec.heads, spec.kv_heads, spec.head_dim
     N = h.shape[0]
-    qkv = h @ np.asarray(w["w_qkv"], dtype).T
+    qkv = linear(h, w["w_qkv"], dtype=dtype)
     q = qkv[:, : H * hd].reshape(N, H, hd)
     k = qkv[:, H * hd: (H + Hk) * hd].reshape(N, Hk, hd)
     v = qkv[:, (H + Hk) * hd:].reshape(N, Hk, hd)
@@ -244,14 +264,10 @@ def block_forward(x, c, w, spec, pos, dtype=F64, rows=None, keep=None):
             continue
         sl = slice(b * S, (b + 1) * S)
         att[sel] = attention(q[sl], k[sl], v[sl], spec.heads, spec.kv_heads, rows[sel] - b * S)
-    x1 = x[rows] + gate1 * (att @ np.asarray(w["w_o"], dtype).T)
+    x1 = gated_residual(x[rows], gate1, linear(att, w["w_o"], dtype=dtype))
     h2 = _prenorm(x1, w, "ln2", shift2, scale2, spec, dtype)
-    wgu = np.asarray(w["w_gate_up"], dtype)
-    F = wgu.shape[0] // 2
-    g = h2 @ wgu[:F].T
-    u = h2 @ wgu[F:].T
-    ff = silu(g) * u
-    out = x1 + gate2 * (ff @ np.asarray(w["w_down"], dtype).T)
+    ff = swiglu(h2, w["w_gate_up"], dtype)
+    out = gated_residual(x1, gate2, linear(ff, w["w_down"], dtype=dtype))
     if keep is not None:
         keep.update(dict(mods=(shift1, scale1, gate1, shift2, scale2, gate2), h=h, q=q, k=k, v=v,
                          att=att, x1=x1, h2=h2, ff=ff, out=out))

@@ -1,0 +1,50 @@
+"""Shared helpers of the GPU parity tests (metrics, uploads, configs)."""
+import sys
+
+import numpy as np
+
+from diffusion_transformer_dit_amd import inputs as I
+
+# The parity bar on block outputs (bf16 path): max relative error
+# max|g - o| / max|o| <= 2e-2 and cosine similarity >= 0.9995.
+MAX_REL = 2e-2
+MIN_COS = 0.9995
+
+
+def metrics(got, ref):
+    g = np.asarray(got, np.float64).ravel()
+    o = np.asarray(ref, np.float64).ravel()
+    d = g - o
+    return {
+        "max_rel": float(np.abs(d).max() / max(np.abs(o).max(), 1e-300)),
+        "cos": float(g @ o / max(np.linalg.norm(g) * np.linalg.norm(o), 1e-300)),
+        "rel_rms": float(np.linalg.norm(d) / max(np.linalg.norm(o), 1e-300)),
+    }
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def assert_parity(got, ref, max_rel=MAX_REL, min_cos=MIN_COS, what=""):
+    m = metrics(got, ref)
+    say(f"  parity {what}: max_rel={m['max_rel']:.3e} cos={m['cos']:.8f} rel_rms={m['rel_rms']:.3e}")
+    assert np.isfinite(np.asarray(got)).all(), f"{what}: non-finite output"
+    assert m["max_rel"] <= max_rel, (what, m)
+    assert m["cos"] >= min_cos, (what, m)
+    return m
+
+
+# small block shapes for GPU parity: several tiles and ragged tails
+SMALL = {
+    "c1_tiny": I.C1,
+    "c1_ragged200": I.C1.replace(name="c1_ragged200", seq_override=200),
+    "hd128_ragged400": I.DiTConfig("hd128_ragged400", 11, 1, (1, 20, 20), 512, 4, 4, 128, 1024, 256, True,
+                                   "interleaved3d", (32, 48, 48), 256.0, x_dtype="bf16"),
+    "gqa3_b2_ragged300": I.DiTConfig("gqa3_b2_ragged300", 12, 2, (1, 15, 20), 768, 6, 2, 128, 1536, 512, True,
+                                     "interleaved3d", (32, 48, 48), 256.0, x_dtype="bf16"),
+    "vit_b2_f32": I.DiTConfig("vit_b2_f32", 13, 2, (1, 16, 16), 512, 8, 8, 64, 1024, 0, False,
+                              "half2d", (32, 32), 100.0, x_dtype="f32"),
+    "c1_f32x_t3": I.C1.replace(name="c1_f32x_t3", cfg_id=14, x_dtype="f32", grid=(3, 8, 12)),
+}

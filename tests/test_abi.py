@@ -1,0 +1,193 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/dit.h declares, validates arguments before touching a device, and its
+host helpers agree with the oracle."""
+import ctypes as C
+import os
+import re
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from diffusion_transformer_dit_amd import inputs as I
+from diffusion_transformer_dit_amd import native as N
+from oracle import dit as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dit.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(N.LIB_PATH), reason="libdit.so not built")
+
+FAKE = 1 << 20          # a 16-byte aligned address that is never dereferenced
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_function():
+    names = header_functions()
+    assert len(names) >= 18
+    L = N.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(N.EXPORTED)
+    assert N.dit_version().startswith("dit-gfx950")
+
+
+def test_status_strings():
+    for st in range(0, -7, -1):
+        assert N.dit_status_string(st) != "unknown status"
+    assert N.dit_status_string(5) == "unknown status"
+
+
+def _desc(**kw):
+    cfg = I.C1
+    d = dict(batch=1, seq=256, hidden=256, heads=4, kv_heads=4, head_dim=64, ffn=768, cond_dim=256)
+    d.update(kw)
+    return N.make_desc(**d)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hidden=320, heads=5, kv_heads=5), N.DIT_ERR_UNSUPPORTED),   # hidden % 256
+    (dict(heads=3), N.DIT_ERR_INVALID_ARG),                   # heads*hd != hidden
+    (dict(kv_heads=3), N.DIT_ERR_INVALID_ARG),                # heads % kv_heads
+    (dict(head_dim=32, heads=8), N.DIT_ERR_UNSUPPORTED),      # head_dim not built
+    (dict(ffn=100), N.DIT_ERR_UNSUPPORTED),
+    (dict(seq=0), N.DIT_ERR_INVALID_ARG),
+    (dict(cond_dim=12), N.DIT_ERR_UNSUPPORTED),
+    (dict(eps=0.0), N.DIT_ERR_INVALID_ARG),
+    (dict(norm=N.DIT_RMSNORM), N.DIT_ERR_UNSUPPORTED),
+    (dict(w_dtype=N.DIT_F32), N.DIT_ERR_UNSUPPORTED),
+])
+def test_desc_validation(kw, status):
+    with pytest.raises(N.DitError) as e:
+        N.dit_block_workspace_size(_desc(**kw))
+    assert e.value.status == status
+    assert N.dit_last_error()
+
+
+def test_workspace_size_accounts_for_buffers():
+    d = _desc()
+    n = N.dit_block_workspace_size(d)
+    N_, D, F = 256, 256, 768
+    # h, q, k, vt, att bf16 + x1 fp32 + u bf16 + modulation
+    assert n >= N_ * D * 2 * 5 + N_ * D * 4 + N_ * F * 2 + 6 * D * 4
+    assert N.dit_seq_pad(200) == 256 and N.dit_seq_pad(256) == 256 and N.dit_seq_pad(257) == 320
+
+
+def _weights(**over):
+    names = dict(w_ada=FAKE, b_ada=FAKE, w_qkv=FAKE, q_g=FAKE, q_b=FAKE, k_g=FAKE, k_b=FAKE, w_o=FAKE,
+                 w_gate_up=FAKE, w_down=FAKE)
+    names.update(over)
+    return N.make_weights(names)
+
+
+def test_block_forward_validation_before_device():
+    d = _desc()
+    ws_need = N.dit_block_workspace_size(d)
+    ws = 1 << 40
+    good = dict(x=FAKE, cond=FAKE, rope_cos=FAKE, rope_sin=FAKE, out=FAKE, ws=ws)
+
+    def call(w=None, ws_bytes=ws_need, **kw):
+        a = dict(good)
+        a.update(kw)
+        N.dit_block_forward(d, w or _weights(), a["x"], a["cond"], a["rope_cos"], a["rope_sin"], a["out"], a["ws"],
+                            stream=0, ws_bytes=ws_bytes)
+
+    cases = [
+        (dict(w=_weights(w_qkv=None)), N.DIT_ERR_INVALID_ARG),
+        (dict(w=_weights(w_o=FAKE + 8)), N.DIT_ERR_ALIGNMENT),
+        (dict(w=_weights(w_ada=None)), N.DIT_ERR_INVALID_ARG),
+        (dict(w=_weights(q_g=None)), N.DIT_ERR_INVALID_ARG),
+        (dict(w=_weights(ln1_g=FAKE)), N.DIT_ERR_UNSUPPORTED),
+        (dict(cond=None), N.DIT_ERR_INVALID_ARG),
+        (dict(x=FAKE + 4), N.DIT_ERR_ALIGNMENT),
+        (dict(ws_bytes=ws_need - 1), N.DIT_ERR_WORKSPACE),
+        (dict(out=FAKE + 256), N.DIT_ERR_INVALID_ARG),       # partial overlap with x
+        (dict(ws=FAKE), N.DIT_ERR_INVALID_ARG),              # workspace overlaps x
+    ]
+    for kw, st in cases:
+        with pytest.raises(N.DitError) as e:
+            call(**kw)
+        assert e.value.status == st, (kw, e.value)
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd") and os.access("/dev/kfd", os.R_OK), reason="a GPU may be present")
+def test_valid_calls_report_no_device():
+    d = _desc()
+    ws_need = N.dit_block_workspace_size(d)
+    with pytest.raises(N.DitError) as e:
+        N.dit_block_forward(d, _weights(), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, stream=0, ws_bytes=ws_need)
+    assert e.value.status == N.DIT_ERR_NO_DEVICE
+    with pytest.raises(N.DitError) as e:
+        N.euler_flowmatch_update(FAKE, FAKE + 4096, 16, 1.0, 0.5, stream=0)
+    assert e.value.status == N.DIT_ERR_NO_DEVICE
+    with pytest.raises(N.DitError) as e:
+        N.dit_timestep_embedding(3.0, 16, FAKE, stream=0)
+    assert e.value.status == N.DIT_ERR_NO_DEVICE
+
+
+def test_stage_entry_validation():
+    with pytest.raises(N.DitError) as e:
+        N.dit_gemm_gated_residual(FAKE, FAKE, 100, 100, 64, None, 0, None, None, FAKE + (1 << 24), 0, stream=0)
+    assert e.value.status == N.DIT_ERR_UNSUPPORTED
+    with pytest.raises(N.DitError) as e:
+        N.dit_gemm_swiglu(FAKE, FAKE, 100, 128, 60, FAKE, stream=0)
+    assert e.value.status == N.DIT_ERR_UNSUPPORTED
+    with pytest.raises(N.DitError) as e:
+        N.dit_ln_modulate(FAKE, 0, 10, 300, FAKE, FAKE, 0, 1e-6, FAKE + (1 << 24), stream=0)
+    assert e.value.status == N.DIT_ERR_UNSUPPORTED
+    with pytest.raises(N.DitError) as e:
+        N.dit_ln_modulate(FAKE, 0, 10, 256, None, FAKE, 0, 1e-6, FAKE + (1 << 24), stream=0)
+    assert e.value.status == N.DIT_ERR_INVALID_ARG
+    with pytest.raises(N.DitError) as e:
+        N.euler_flowmatch_update(FAKE, FAKE + 8, 64, 1.0, 0.5, stream=0)
+    assert e.value.status in (N.DIT_ERR_ALIGNMENT, N.DIT_ERR_INVALID_ARG)
+
+
+def test_stack_validation():
+    d = _desc(x_dtype=N.DIT_BF16)
+    e = dict(w_in=FAKE, b_in=FAKE, w_fmod=FAKE, b_fmod=FAKE, w_out=FAKE, b_out=FAKE)
+    m = N.make_model(d, [_weights()] * 2, 128, e)
+    with pytest.raises(N.DitError) as err:
+        N.dit_stack_workspace_size(m)
+    assert err.value.status == N.DIT_ERR_UNSUPPORTED           # stack needs an fp32 residual stream
+    m = N.make_model(_desc(x_dtype=N.DIT_F32), [_weights()] * 2, 100, e)
+    with pytest.raises(N.DitError) as err:
+        N.dit_stack_workspace_size(m)
+    assert err.value.status == N.DIT_ERR_UNSUPPORTED           # latent_dim % 128
+    m = N.make_model(_desc(x_dtype=N.DIT_F32), [_weights()] * 2, 128, e)
+    assert N.dit_stack_workspace_size(m) > N.dit_block_workspace_size(_desc(x_dtype=N.DIT_F32))
+
+
+# ---------------------------------------------------------------------------
+# host helpers against the oracle
+# ---------------------------------------------------------------------------
+def test_sigmas_match_oracle_and_golden():
+    got = N.dit_flowmatch_sigmas(8, 4.0)
+    ref = O.flowmatch_sigmas(8, 4.0)
+    np.testing.assert_allclose(got, ref, rtol=1e-7, atol=1e-8)
+    assert got[0] == 1.0 and got[-1] == 0.0
+
+
+@pytest.mark.parametrize("cfg", [I.C1, I.C2, I.C3], ids=lambda c: c.name)
+def test_rope_tables_match_oracle(cfg):
+    pos = I.positions(cfg) + np.array([2, 0, 0])    # nonzero t so the t-axis slots rotate
+    rope = N.DIT_ROPE_INTERLEAVED if cfg.rope == "interleaved3d" else N.DIT_ROPE_HALF
+    cos, sin = N.dit_rope_tables(pos, rope, cfg.rope_axes, cfg.rope_theta, cfg.head_dim)
+    ang = O.rope_angles(pos, cfg)
+    np.testing.assert_allclose(cos, np.cos(ang), atol=2e-7)
+    np.testing.assert_allclose(sin, np.sin(ang), atol=2e-7)
+    # position 0 is the identity rotation, exactly
+    c0, s0 = N.dit_rope_tables(np.zeros((3, 3), np.int32), rope, cfg.rope_axes, cfg.rope_theta, cfg.head_dim)
+    assert (c0 == 1).all() and (s0 == 0).all()
+
+
+def test_rope_tables_validation():
+    with pytest.raises(N.DitError):
+        N.dit_rope_tables(np.zeros((4, 3)), N.DIT_ROPE_INTERLEAVED, (16, 24, 20), 256.0, 64)   # widths sum != hd
+    with pytest.raises(N.DitError):
+        N.dit_rope_tables(np.zeros((4, 3)), N.DIT_ROPE_HALF, (16, 24, 24), 256.0, 64)          # half takes 2 axes
