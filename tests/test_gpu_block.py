@@ -6,7 +6,12 @@ block at 4x1024 tokens): sampled token rows, which the oracle computes one by
 one (all keys are still projected; attention, out-projection and FFN run only
 for the sampled rows).  The gate is on `out` (max-rel <= 2e-2, cosine >=
 0.9995); the branch delta = out - x is checked as well, since x dominates out
-at N(0, 0.02) weights."""
+at N(0, 0.02) weights on the small shapes.
+
+When out is stored in bf16 and |delta| << |x|, one bf16 rounding of out
+already moves delta by ~2^-9 |x|, i.e. tens of percent of a small delta; that
+floor is computed from the oracle (|| bf16(ref) - ref || / || ref - x ||) and
+only the error in excess of it (in quadrature) is held to DELTA_EXCESS."""
 import numpy as np
 import pytest
 
@@ -19,11 +24,10 @@ from gpu_helpers import SMALL, assert_parity, metrics, say
 
 pytestmark = pytest.mark.gpu
 
-# delta = out - x carries every rounding of the path (bf16 h, q, k, v, P,
-# attention output, SwiGLU output; bf16 out for bf16 x) on a quantity that is
-# ~10x smaller than out, so its relative bar is 10x looser than out's.
-DELTA_MAX_REL = 0.2
-DELTA_MIN_COS = 0.999
+# Relative RMS error of delta beyond the output-rounding floor: the seven bf16
+# rounding points inside the block (h, q, k, v, P, attention output, SwiGLU
+# output) each add ~1e-3 relative noise to the branch.
+DELTA_EXCESS = 2e-2
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -51,9 +55,14 @@ def _check(cfg, got, ref, x):
     x = np.asarray(x, np.float64)
     assert_parity(got, ref, what=f"{cfg.name} out")
     dm = metrics(got - x, ref - x)
+    dref = np.linalg.norm(ref - x)
+    floor = 0.0
+    if cfg.x_dtype == "bf16":
+        floor = np.linalg.norm(I.bf16_round(np.asarray(ref, np.float32)) - ref) / dref
+    excess = np.sqrt(max(dm["rel_rms"] ** 2 - floor ** 2, 0.0))
     say(f"  delta {cfg.name}: max_rel={dm['max_rel']:.3e} cos={dm['cos']:.6f} rel_rms={dm['rel_rms']:.3e} "
-        f"|delta|/|x|={np.linalg.norm(ref - x) / np.linalg.norm(x):.3e}")
-    assert dm["max_rel"] <= DELTA_MAX_REL and dm["cos"] >= DELTA_MIN_COS, dm
+        f"out-rounding floor={floor:.3e} excess={excess:.3e} |delta|/|x|={dref / np.linalg.norm(x):.3e}")
+    assert excess <= DELTA_EXCESS, (dm, floor)
 
 
 @pytest.mark.parametrize("name", list(SMALL))
