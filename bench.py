@@ -152,18 +152,24 @@ def cpu_baseline(cfg=I.C4):
     sigma = 1.0
     t0 = time.perf_counter()
     c = O.timestep_embedding(1000.0 * sigma, cfg.cond_dim)
-    x = O.linear(lat, edges["w_in"], edges["b_in"])
-    x = O.block_forward(x, c, w, cfg, pos)
-    t_block_end = time.perf_counter()
+    x0 = O.linear(lat, edges["w_in"], edges["b_in"])
+    t_embed = time.perf_counter()
+    runs = []
+    for _ in range(3):                  # the block: median of 3
+        tb = time.perf_counter()
+        x = O.block_forward(x0, c, w, cfg, pos)
+        runs.append(time.perf_counter() - tb)
+    t_blocks = time.perf_counter()
     v = O.final_layer(x, c, edges, cfg)
     _ = O.euler_update(lat, v, 1.0, 0.9)
     t1 = time.perf_counter()
-    block_s = t_block_end - t0          # includes the (tiny) patch embedding
-    edge_s = t1 - t_block_end
+    block_s = float(np.median(runs))
+    edge_s = (t_embed - t0) + (t1 - t_blocks)
     step_s = block_s * cfg.layers + edge_s
     return {"value": round(step_s, 2), "unit": "s/denoise-step", "cores": int(threads), "kind": "oracle",
-            "sample": f"1 of {cfg.layers} blocks (4096 tok, hidden 4096, float64 NumPy) + patch-embed + final layer "
-                      f"+ Euler, timed once ({t1 - t0:.1f} s), block time x {cfg.layers}"}
+            "sample": f"1 of {cfg.layers} blocks (4096 tok, hidden 4096, float64 NumPy; median of 3 runs "
+                      f"{block_s:.2f} s) x {cfg.layers} + patch-embed + final layer + Euler ({edge_s:.2f} s); "
+                      f"{t1 - t0:.1f} s of CPU work"}
 
 
 def main():
@@ -172,7 +178,8 @@ def main():
     ap.add_argument("--steps", type=int, default=8)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--kernels-only", action="store_true", help="time the block kernels only")
+    ap.add_argument("--counters", action="store_true",
+                    help="one block's weights; each block kernel a few times plus a 512 MiB copy (for rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the hot path is one DiT denoising step on one MI355X; "
@@ -184,6 +191,17 @@ def main():
     from diffusion_transformer_dit_amd import runtime as R
     R.require_gpu()
     cfg = I.C4
+    if args.counters:
+        stack, cos, sin = build_full_stack(cfg.replace(layers=1))
+        kern = time_kernels(cfg, stack, reps=2)
+        src = torch.ones(128 * 1024 * 1024, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)                  # calibration: 512 MiB read + 512 MiB written
+        torch.cuda.synchronize()
+        print(json.dumps({"counters_run": True, "copy_bytes_each_way": src.numel() * 4,
+                          "kernels_us": {k: v["us"] for k, v in kern.items()}}), flush=True)
+        return
     print(f"[bench] building {cfg.layers}-block stack (hidden {cfg.hidden}, {cfg.tokens} tokens)", file=sys.stderr,
           flush=True)
     stack, cos, sin = build_full_stack(cfg)

@@ -21,25 +21,34 @@
 
 namespace dit {
 
-constexpr int kBK = 64;   // K step per LDS stage (one 128-byte row segment)
-
-template <int BM_, int BN_, int WM_, int WN_>
+// Tile shape: BM x BN outputs per workgroup of WM x WN waves, K consumed BK at
+// a time through NS LDS stages.
+template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64, int NS_ = 2>
 struct Tile {
-    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-    static constexpr int kThreads = WM * WN * kWave;
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_;
+    static constexpr int kWaves = WM * WN;
+    static constexpr int kThreads = kWaves * kWave;
     static constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
     static constexpr int TM = kWaveM / 32, TN = kWaveN / 32;
-    static constexpr int kAChunks = BM * 8 / kThreads;   // 16-byte chunks per thread per stage
-    static constexpr int kBChunks = BN * 8 / kThreads;
-    static constexpr int kStageBytes = (BM + BN) * 128;
-    static_assert(BM * 8 % kThreads == 0 && BN * 8 % kThreads == 0, "tile/threads");
-    static_assert(kWaveM % 32 == 0 && kWaveN % 32 == 0, "wave tile");
+    static constexpr int kRowBytes = BK * 2;                    // one tile row (BK bf16) in LDS
+    static constexpr int kChunks = kRowBytes / 16;              // 16-byte chunks per row
+    static constexpr int kRowsPerLine = 256 / kRowBytes;        // rows sharing one 64-bank line
+    static constexpr int kRowsPerLoad = 1024 / kRowBytes;       // rows one wave-wide 1 KiB load fills
+    static constexpr int kALoads = BM / kRowsPerLoad / kWaves;  // buffer->LDS loads per wave per stage
+    static constexpr int kBLoads = BN / kRowsPerLoad / kWaves;
+    static constexpr int kLoads = kALoads + kBLoads;
+    static constexpr int kStageBytes = (BM + BN) * kRowBytes;
+    static_assert(BM % (kRowsPerLoad * kWaves) == 0 && BN % (kRowsPerLoad * kWaves) == 0, "tile vs loads");
+    static_assert(kWaveM % 32 == 0 && kWaveN % 32 == 0 && BK % 16 == 0, "wave tile");
+    static_assert((NS - 2) * kLoads <= 63, "vmcnt range");
+    // Chunk c of tile row r lives at slot c ^ swz(r).  gfx950 LDS has 64 banks
+    // (256 B per cycle) and a ds_read_b128 serves 16 lanes per cycle; the
+    // fragment reads of those 16 lanes are 16 consecutive rows at one logical
+    // chunk.  kRowsPerLine rows share a bank line, so rotating the chunk by the
+    // line index spreads the 16 rows over all 64 banks.
+    static __device__ __forceinline__ int swz(int r) { return (r / kRowsPerLine) & (kChunks - 1); }
+    static __device__ __forceinline__ uint32_t off(int r, int c) { return r * kRowBytes + ((c ^ swz(r)) << 4); }
 };
-
-// Row-major LDS tile of 64 bf16 (128 B) per row, eight 16-byte chunks per row;
-// chunk c of row r lives at chunk slot c ^ (r & 7) so that the 8 lanes of a
-// ds_read_b128 phase (rows r..r+7, same logical chunk) hit 8 distinct slots.
-__device__ __forceinline__ uint32_t lds_off(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
 
 // Maps the launch index to a (row-tile, col-tile).  Workgroups are dispatched
 // round-robin over the 8 XCDs, so index p runs on XCD p % 8; remap so that
@@ -78,12 +87,31 @@ struct RowsSwiglu {
     }
 };
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
+// [6:4], lgkmcnt [11:8]); LGKM = 0 also drains this wave's LDS reads.
+template <int N, int LGKM = 15>
+__device__ __forceinline__ void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (LGKM << 8));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(): that fence
+// would wait for every outstanding buffer->LDS load, including the stages
+// still meant to be in flight.  Ordering is provided by the explicit waits.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
 template <class T, class RowMap, class Epi>
 __global__ __launch_bounds__(T::kThreads, 1)
-void gemm_kernel(const bf16 *__restrict__ A, const bf16 *__restrict__ W, int M, int K,
+void gemm_kernel(const bf16 *__restrict__ A, const bf16 *__restrict__ W, int M, int K, int w_rows,
                  int tiles_m, int tiles_n, RowMap rowmap, Epi epi) {
-    constexpr int kLds = Epi::template lds_bytes<T>() > 2 * T::kStageBytes ? Epi::template lds_bytes<T>()
-                                                                              : 2 * T::kStageBytes;
+#if defined(__HIP_DEVICE_COMPILE__)   // buffer resources exist only in the device pass
+    constexpr int kMain = T::NS * T::kStageBytes;
+    constexpr int kLds = Epi::template lds_bytes<T>() > kMain ? Epi::template lds_bytes<T>() : kMain;
     __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
 
     int tm, tn;
@@ -95,34 +123,35 @@ void gemm_kernel(const bf16 *__restrict__ A, const bf16 *__restrict__ W, int M, 
     const int wm = wave / T::WN, wn = wave % T::WN;
     const int lrow = lane & 31, lhalf = lane >> 5;
 
-    // global source offsets (elements) and LDS destinations of this thread's chunks
-    uint32_t a_src[T::kAChunks], a_dst[T::kAChunks];
-    uint32_t b_src[T::kBChunks], b_dst[T::kBChunks];
+    // Global -> LDS without registers: buffer_load_dwordx4 ... lds moves 64 x 16
+    // bytes of one wave into a contiguous 1 KiB of LDS (lane l at +16 l).  Load
+    // q of wave w fills tile rows kRowsPerLoad (q waves + w) ..; lane l brings
+    // row + l / kChunks into physical slot l % kChunks, i.e. the logical chunk
+    // (l % kChunks) ^ swz(row).
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)M * (uint32_t)K * 2u);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(W, (uint32_t)w_rows * (uint32_t)K * 2u);
+    const int lr = lane / T::kChunks, ls = lane % T::kChunks;
+    uint32_t a_off[T::kALoads], b_off[T::kBLoads];
 #pragma unroll
-    for (int q = 0; q < T::kAChunks; ++q) {
-        const int id = q * T::kThreads + tid, r = id >> 3, c = id & 7;
+    for (int q = 0; q < T::kALoads; ++q) {
+        const int r = (q * T::kWaves + wave) * T::kRowsPerLoad + lr;
         const int grow = min(m0 + r, M - 1);              // ragged M: clamp reads, mask stores
-        a_src[q] = (uint32_t)grow * (uint32_t)K + c * 8;
-        a_dst[q] = lds_off(r, c);
+        a_off[q] = ((uint32_t)grow * (uint32_t)K + (ls ^ T::swz(r)) * 8) * 2u;
     }
 #pragma unroll
-    for (int q = 0; q < T::kBChunks; ++q) {
-        const int id = q * T::kThreads + tid, r = id >> 3, c = id & 7;
-        b_src[q] = (uint32_t)rowmap(tn, r) * (uint32_t)K + c * 8;
-        b_dst[q] = T::BM * 128 + lds_off(r, c);
+    for (int q = 0; q < T::kBLoads; ++q) {
+        const int r = (q * T::kWaves + wave) * T::kRowsPerLoad + lr;
+        b_off[q] = ((uint32_t)rowmap(tn, r) * (uint32_t)K + (ls ^ T::swz(r)) * 8) * 2u;
     }
-
-    uint4 ra[T::kAChunks], rb[T::kBChunks];
-#define DIT_GEMM_GLOAD(k0)                                                                      \
-    do {                                                                                        \
-        _Pragma("unroll") for (int q = 0; q < T::kAChunks; ++q) ra[q] = *(const uint4 *)(A + a_src[q] + (k0)); \
-        _Pragma("unroll") for (int q = 0; q < T::kBChunks; ++q) rb[q] = *(const uint4 *)(W + b_src[q] + (k0)); \
-    } while (0)
-#define DIT_GEMM_LSTORE(stage)                                                                  \
-    do {                                                                                        \
-        uint8_t *base_ = smem + (stage) * T::kStageBytes;                                       \
-        _Pragma("unroll") for (int q = 0; q < T::kAChunks; ++q) *(uint4 *)(base_ + a_dst[q]) = ra[q]; \
-        _Pragma("unroll") for (int q = 0; q < T::kBChunks; ++q) *(uint4 *)(base_ + b_dst[q]) = rb[q]; \
+#define DIT_ISSUE(stage, k0)                                                                             \
+    do {                                                                                                 \
+        uint8_t *base_ = smem + (stage) * T::kStageBytes;                                                \
+        const uint32_t kb_ = (uint32_t)(k0) * 2u;                                                        \
+        _Pragma("unroll") for (int q = 0; q < T::kALoads; ++q) __builtin_amdgcn_raw_ptr_buffer_load_lds( \
+            ra, (lds_void *)(base_ + (q * T::kWaves + wave) * 1024), 16, a_off[q], kb_, 0, 0);           \
+        _Pragma("unroll") for (int q = 0; q < T::kBLoads; ++q) __builtin_amdgcn_raw_ptr_buffer_load_lds( \
+            rw, (lds_void *)(base_ + T::BM * T::kRowBytes + (q * T::kWaves + wave) * 1024), 16, b_off[q], \
+            kb_, 0, 0);                                                                                  \
     } while (0)
 
     floatx16 acc[T::TM][T::TN];
@@ -133,41 +162,66 @@ void gemm_kernel(const bf16 *__restrict__ A, const bf16 *__restrict__ W, int M, 
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    const int KT = K / kBK;
-    DIT_GEMM_GLOAD(0);
-    DIT_GEMM_LSTORE(0);
-    __syncthreads();
+    // NS-stage ring: stage s holds K tile kt with kt % NS == s.  Tiles past the
+    // end re-load the last tile (never read) so that every iteration issues the
+    // same number of loads and the vmcnt bookkeeping stays uniform.
+    const int KT = K / T::BK;
+#pragma unroll
+    for (int s0 = 0; s0 < T::NS - 1; ++s0) DIT_ISSUE(s0, min(s0, KT - 1) * T::BK);
+
+    bf16x8 af[2][T::TM], bfr[2][T::TN];
+#define DIT_LOAD_FRAGS(buf, sa_, sb_, kk)                                                           \
+    do {                                                                                          \
+        const int c_ = (kk) * 2 + lhalf;                                                          \
+        _Pragma("unroll") for (int i = 0; i < T::TM; ++i)                                        \
+            af[buf][i] = *(const bf16x8 *)((sa_) + T::off(wm * T::kWaveM + i * 32 + lrow, c_));   \
+        _Pragma("unroll") for (int j = 0; j < T::TN; ++j)                                        \
+            bfr[buf][j] = *(const bf16x8 *)((sb_) + T::off(wn * T::kWaveN + j * 32 + lrow, c_));  \
+    } while (0)
 
     for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        // the last iteration re-reads the final K tile into the idle stage: no branch
-        // around the prefetch, so the staging registers stay registers
-        DIT_GEMM_GLOAD(min(kt + 1, KT - 1) * kBK);
-        const uint8_t *sa = smem + cur * T::kStageBytes;
-        const uint8_t *sb = sa + T::BM * 128;
+        // tile kt has landed once at most NS-2 later stages are still in flight;
+        // the barrier extends that to every wave and also certifies that all
+        // waves are done with the stage consumed in the previous iteration
+        wait_vmcnt<(T::NS - 2) * T::kLoads, 0>();
+        barrier_only();
+        DIT_ISSUE((kt + T::NS - 1) % T::NS, min(kt + T::NS - 1, KT - 1) * T::BK);
+        const uint8_t *sa = smem + (kt % T::NS) * T::kStageBytes;
+        const uint8_t *sb = sa + T::BM * T::kRowBytes;
+        DIT_LOAD_FRAGS(0, sa, sb, 0);
 #pragma unroll
-        for (int kk = 0; kk < kBK / 16; ++kk) {
-            const int c = kk * 2 + lhalf;
-            bf16x8 af[T::TM], bfr[T::TN];
-#pragma unroll
-            for (int i = 0; i < T::TM; ++i)
-                af[i] = *(const bf16x8 *)(sa + lds_off(wm * T::kWaveM + i * 32 + lrow, c));
-#pragma unroll
-            for (int j = 0; j < T::TN; ++j)
-                bfr[j] = *(const bf16x8 *)(sb + lds_off(wn * T::kWaveN + j * 32 + lrow, c));
+        for (int kk = 0; kk < T::BK / 16; ++kk) {
+            // fetch k-step kk+1 while the MFMAs of k-step kk run
+            if (kk + 1 < T::BK / 16) DIT_LOAD_FRAGS((kk + 1) & 1, sa, sb, kk + 1);
 #pragma unroll
             for (int i = 0; i < T::TM; ++i)
 #pragma unroll
                 for (int j = 0; j < T::TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][i], bfr[kk & 1][j], acc[i][j],
+                                                                        0, 0, 0);
         }
-        DIT_GEMM_LSTORE(cur ^ 1);   // stage cur^1 was released by the barrier of iteration kt-1
-        __syncthreads();
+        // instruction order hint: the buffer->LDS loads first, the fragment reads
+        // of k-step 0, then each later k-step's reads spread between the MFMAs of
+        // the k-step before it
+        __builtin_amdgcn_sched_group_barrier(0x020, T::kLoads, 0);          // VMEM
+        __builtin_amdgcn_sched_group_barrier(0x100, T::TM + T::TN, 0);      // DS read
+#pragma unroll
+        for (int kk = 0; kk < T::BK / 16 - 1; ++kk) {
+#pragma unroll
+            for (int r = 0; r < T::TM + T::TN; ++r) {
+                __builtin_amdgcn_sched_group_barrier(0x008, (T::TM * T::TN) / (T::TM + T::TN), 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                   // DS read
+            }
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, T::TM * T::TN, 0);
     }
-#undef DIT_GEMM_GLOAD
-#undef DIT_GEMM_LSTORE
+#undef DIT_LOAD_FRAGS
+#undef DIT_ISSUE
+    wait_vmcnt<0>();      // retire the trailing (never read) loads before LDS is reused
+    __syncthreads();
 
     epi.template apply<T>(acc, m0 + wm * T::kWaveM, tn, wn, lane, M, smem);
+#endif
 }
 
 // Accumulator element (i, j, e) of a wave sits at wave-tile row
@@ -371,8 +425,12 @@ struct EpiQkv {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-using TileBig = Tile<256, 256, 2, 2>;    // 128x128 per wave
-using TileNarrow = Tile<256, 128, 2, 2>; // 128x64 per wave (N = 128 outputs)
+// 8 waves (2 per SIMD, 128x64 each) for the plain epilogues: two waves per SIMD
+// let one wave's LDS waits overlap the other's MFMAs.  The qk-norm epilogue
+// needs whole heads per wave, so the QKV GEMM keeps 4 waves of 128x128.
+using Tile8w = Tile<256, 256, 2, 4>;
+using TileBig = Tile<256, 256, 2, 2>;
+using TileNarrow = Tile<256, 128, 2, 2>;   // N = 128 outputs (the projection to latent channels)
 
 template <class T, class RowMap, class Epi>
 static hipError_t run(const bf16 *a, const bf16 *w, int64_t M, int N_tile_cols, int K, RowMap rm, Epi epi,
@@ -382,7 +440,7 @@ static hipError_t run(const bf16 *a, const bf16 *w, int64_t M, int N_tile_cols, 
     const int grid = tiles_m * tiles_n;
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL((gemm_kernel<T, RowMap, Epi>), dim3(grid), dim3(T::kThreads), 0, s, a, w, (int)M, K,
-                       tiles_m, tiles_n, rm, epi);
+                       N_tile_cols, tiles_m, tiles_n, rm, epi);
     return hipGetLastError();
 }
 
@@ -390,7 +448,7 @@ template <typename TR, typename TO>
 static hipError_t residual_typed(const bf16 *a, const bf16 *w, int64_t M, int N, int K, const void *resid,
                                  const float *gate, const float *bias, void *out, hipStream_t s) {
     EpiResidual<TR, TO> epi{(const TR *)resid, gate, bias, (TO *)out, N};
-    if (N % 256 == 0) return run<TileBig>(a, w, M, N, K, RowsIdentity{256}, epi, s);
+    if (N % 256 == 0) return run<Tile8w>(a, w, M, N, K, RowsIdentity{256}, epi, s);
     return run<TileNarrow>(a, w, M, N, K, RowsIdentity{128}, epi, s);
 }
 
@@ -406,7 +464,7 @@ hipError_t launch_gemm_residual(const bf16 *a, const bf16 *w, int64_t M, int N, 
 }
 
 hipError_t launch_gemm_swiglu(const bf16 *a, const bf16 *w, int64_t M, int F, int K, bf16 *u, hipStream_t s) {
-    using T = TileBig;
+    using T = Tile8w;
     return run<T>(a, w, M, 2 * F, K, RowsSwiglu{T::BN, T::kWaveN, F}, EpiSwiglu{u, F}, s);
 }
 
