@@ -134,6 +134,21 @@ def time_kernels(cfg, stack, reps=20):
     return out
 
 
+def measured_traffic():
+    """HBM bytes per launch of the SwiGLU GEMM from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, or None when gemm.hip changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gemm_swiglu_stack_8b_hbm_counters.md")
+    try:
+        kv = dict(l.strip().split(": ", 1) for l in open(path) if l.startswith("    ") and ": " in l)
+        src = open(os.path.join(ROOT, kv["source"]), "rb").read()
+        if hashlib.sha256(src).hexdigest()[:16] != kv["source_sha256_16"]:
+            return None
+        return int(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(cfg=I.C4):
     """The float64 CPU oracle on a bounded sample of one step: one block of the
     stack plus the stack edges, scaled by the block count to s/denoise-step."""
@@ -239,7 +254,7 @@ def main():
     util = flops / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
     dom = kern["gemm_swiglu"]
     roof = {"bound": "mfma", "kernel": "gemm_swiglu (SwiGLU up-GEMM, 4096 x 24576 x 4096)", "achieved": dom["achieved"],
-            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": dom["frac"], "traffic": None,
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": dom["frac"], "traffic": measured_traffic(),
             "avg_us": dom["us"]}
     cpu = None
     if not args.no_cpu:
