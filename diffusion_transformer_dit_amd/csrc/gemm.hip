@@ -293,128 +293,166 @@ struct EpiSwiglu {
 
 // ---------------------------------------------------------------------------
 // epilogue: qk-LayerNorm + RoPE, scatter to q [B,H,S,hd], k [B,Hk,S,hd],
-// vt [B,Hk,hd,Spad].  The accumulators go through LDS (free once the K loop
-// has drained) in two passes of 64 rows per wave, so that afterwards one lane
-// holds one token row of a head: the LayerNorm statistics and the RoPE pairs
-// are then in-lane, q/k rows leave as 16-byte stores, and for v one lane
-// holds one head-dim column and writes it contiguously along the tokens.
+// vt [B,Hk,hd,Spad], for the 8-wave 256 x 256 tile (wave tile 128 x 64).
+// A head spans several waves' columns, so the accumulators go through LDS
+// (free once the K loop has drained): each 4-wave cluster (128 rows) stages
+// 64 of its rows x 256 columns at a time, both clusters in parallel.  Then
+// each lane takes one unit of work of one head of the tile:
+//   q/k head: one token row (64 values per lane; a 128-wide head row is
+//             split over a lane pair that combines its LayerNorm statistics
+//             with one exchange) -- RoPE pairs in-lane (rotate-half at
+//             hd = 128 swaps halves with the partner lane); 16-byte stores;
+//   v head:   one head-dim column over the 64 staged tokens, written
+//             contiguously along the key axis of v^T.
 // ---------------------------------------------------------------------------
-constexpr int kQkvStride = 132;   // floats per staged row: 128 + 4 (row-per-lane reads hit distinct banks)
+constexpr int kQkvStride = 260;   // floats per staged row: 256 + 4, so 16 row-per-lane reads hit distinct banks
 
 template <int HD>
 struct EpiQkv {
     QkvEpiArgs e;
-    template <class T> static constexpr int lds_bytes() { return T::WM * T::WN * 64 * kQkvStride * 4; }
+    template <class T> static constexpr int lds_bytes() { return 2 * 64 * kQkvStride * 4; }
 
     template <class T>
     __device__ __forceinline__ void apply(floatx16 (&acc)[T::TM][T::TN], int row0, int tn, int wn, int lane, int M,
                                           uint8_t *smem) const {
-        static_assert(T::kWaveN == 128 && T::kWaveM == 128, "staging assumes 128x128 wave tiles");
-        constexpr int HPW = 128 / HD;                  // heads per wave
+        static_assert(T::BN == 256 && T::WM == 2 && T::WN == 4 && T::kWaveM == 128 && T::kWaveN == 64,
+                      "staging assumes the 8-wave 256x256 tile");
         const int lrow = lane & 31, lhalf = lane >> 5;
         const int wave = threadIdx.x >> 6;
-        float *red = (float *)smem + wave * 64 * kQkvStride;
-        const int col0 = tn * T::BN + wn * 128;
+        const int cl = wave >> 2;                          // cluster = wm: rows cl*128 .. +128 of the tile
+        const int lc = (wave & 3) * 64 + lane;             // lane within the cluster, 0..255
+        float *red = (float *)smem + cl * 64 * kQkvStride;
+        const int hl = lc / HD, within = lc % HD;          // head of the tile, unit within that head
+        const int hc0 = tn * T::BN + hl * HD;              // global first column of that head
         const int qcols = e.heads * HD, kcols = e.kv_heads * HD;
+        const int sect = hc0 < qcols ? 0 : (hc0 < qcols + kcols ? 1 : 2);   // uniform per wave
+        const int head = sect == 0 ? hc0 / HD : (sect == 1 ? (hc0 - qcols) / HD : (hc0 - qcols - kcols) / HD);
         const int S = e.seq;
 #pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
-            __syncthreads();   // previous users of the LDS (K loop or pass 0) are done
+        for (int sp = 0; sp < 2; ++sp) {
+            __syncthreads();   // the K loop (or the previous sub-pass) is done with the LDS
 #pragma unroll
             for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
                 for (int j = 0; j < T::TN; ++j)
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
-                        red[(ii * 32 + ((r >> 2) << 3) + (lhalf << 2) + (r & 3)) * kQkvStride + j * 32 + lrow] =
-                            acc[pass * 2 + ii][j][r];
+                        red[(ii * 32 + ((r >> 2) << 3) + (lhalf << 2) + (r & 3)) * kQkvStride + wn * 64 + j * 32 +
+                            lrow] = acc[sp * 2 + ii][j][r];
             __syncthreads();
-            const int rbase = row0 + pass * 64;        // token of staged row 0
+            const int rbase = row0 + sp * 64;             // token of staged row 0
+            if (sect < 2) {
+                // one token row per lane pair (hd = 128: 64 values per lane,
+                // `part` = which half of the head) or per lane (hd = 64)
+                constexpr int PARTS = HD / 64;
+                const int rl = within / PARTS, part = within % PARTS;
+                const int row = rbase + rl;
+                float y[64];
+                const float *src = red + rl * kQkvStride + hl * HD + part * 64;
 #pragma unroll
-            for (int hw = 0; hw < HPW; ++hw) {
-                const int hc0 = col0 + hw * HD;
-                const int sect = hc0 < qcols ? 0 : (hc0 < qcols + kcols ? 1 : 2);
-                const int head = sect == 0 ? hc0 / HD : (sect == 1 ? (hc0 - qcols) / HD : (hc0 - qcols - kcols) / HD);
-                if (sect < 2) {
-                    // one token row per lane
-                    const int row = rbase + lane;
-                    float y[HD];
-                    const float *src = red + lane * kQkvStride + hw * HD;
+                for (int c = 0; c < 64; c += 4) {
+                    const floatx4 v = *(const floatx4 *)(src + c);
+                    y[c] = v[0]; y[c + 1] = v[1]; y[c + 2] = v[2]; y[c + 3] = v[3];
+                }
+                if (e.qk_norm) {
+                    const float *g = (sect == 0 ? e.q_g : e.k_g) + part * 64;
+                    const float *bb = (sect == 0 ? e.q_b : e.k_b) + part * 64;
+                    float sum = 0.f;
 #pragma unroll
-                    for (int c = 0; c < HD; c += 4) {
-                        const floatx4 v = *(const floatx4 *)(src + c);
-                        y[c] = v[0]; y[c + 1] = v[1]; y[c + 2] = v[2]; y[c + 3] = v[3];
+                    for (int c = 0; c < 64; ++c) sum += y[c];
+                    if (PARTS == 2) sum += __shfl_xor(sum, 1, 64);
+                    const float mean = sum * (1.0f / HD);
+                    float ss = 0.f;
+#pragma unroll
+                    for (int c = 0; c < 64; ++c) { y[c] -= mean; ss += y[c] * y[c]; }
+                    if (PARTS == 2) ss += __shfl_xor(ss, 1, 64);
+                    const float rstd = rsqrtf(ss * (1.0f / HD) + e.eps);
+#pragma unroll
+                    for (int c = 0; c < 64; c += 4) {
+                        const floatx4 g4 = *(const floatx4 *)(g + c), b4 = *(const floatx4 *)(bb + c);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) y[c + u] = y[c + u] * rstd * g4[u] + b4[u];
                     }
-                    if (e.qk_norm) {
-                        const float *g = sect == 0 ? e.q_g : e.k_g;
-                        const float *bb = sect == 0 ? e.q_b : e.k_b;
-                        float sum = 0.f;
+                }
+                const int trow = min(row, M - 1);
+                const int bidx = trow / S, sp_ = trow - bidx * S;
+                const float *ct = e.cos_t + (size_t)sp_ * (HD / 2);
+                const float *st = e.sin_t + (size_t)sp_ * (HD / 2);
+                if (!e.rope_half) {
+                    // interleaved pairs (2m, 2m+1) lie inside this lane's 64 values
 #pragma unroll
-                        for (int c = 0; c < HD; ++c) sum += y[c];
-                        const float mean = sum * (1.0f / HD);
-                        float ss = 0.f;
+                    for (int m4 = 0; m4 < 32; m4 += 4) {
+                        const floatx4 c4 = *(const floatx4 *)(ct + part * 32 + m4);
+                        const floatx4 s4 = *(const floatx4 *)(st + part * 32 + m4);
 #pragma unroll
-                        for (int c = 0; c < HD; ++c) { y[c] -= mean; ss += y[c] * y[c]; }
-                        const float rstd = rsqrtf(ss * (1.0f / HD) + e.eps);
-#pragma unroll
-                        for (int c = 0; c < HD; ++c) y[c] = y[c] * rstd * g[c] + bb[c];
+                        for (int u = 0; u < 4; ++u) {
+                            const int m = m4 + u;
+                            const float a = y[2 * m], bq = y[2 * m + 1];
+                            y[2 * m] = a * c4[u] - bq * s4[u];
+                            y[2 * m + 1] = a * s4[u] + bq * c4[u];
+                        }
                     }
-                    const int trow = min(row, M - 1);
-                    const int bidx = trow / S, sp = trow - bidx * S;
-                    const float *ct = e.cos_t + (size_t)sp * (HD / 2);
-                    const float *st = e.sin_t + (size_t)sp * (HD / 2);
-                    // rotate in place, 4 pair slots (one float4 of each table) at a time
+                } else if (PARTS == 1) {
+                    // rotate-half, hd = 64: pairs (m, m + 32) inside the lane
 #pragma unroll
-                    for (int m4 = 0; m4 < HD / 2; m4 += 4) {
+                    for (int m4 = 0; m4 < 32; m4 += 4) {
                         const floatx4 c4 = *(const floatx4 *)(ct + m4), s4 = *(const floatx4 *)(st + m4);
 #pragma unroll
                         for (int u = 0; u < 4; ++u) {
                             const int m = m4 + u;
-                            const int ia = e.rope_half ? m : 2 * m;
-                            const int ib = e.rope_half ? m + HD / 2 : 2 * m + 1;
-                            const float a = y[ia], bq = y[ib];
-                            y[ia] = a * c4[u] - bq * s4[u];
-                            y[ib] = a * s4[u] + bq * c4[u];
-                        }
-                    }
-                    if (row < M) {
-                        bf16 *dst = (sect == 0 ? e.q : e.k) +
-                                    (((size_t)bidx * (sect == 0 ? e.heads : e.kv_heads) + head) * S + sp) * HD;
-#pragma unroll
-                        for (int c = 0; c < HD; c += 8) {
-                            bf16x8 v;
-#pragma unroll
-                            for (int u = 0; u < 8; ++u) v[u] = f2bf(y[c + u]);
-                            *(bf16x8 *)(dst + c) = v;
+                            const float a = y[m], bq = y[m + 32];
+                            y[m] = a * c4[u] - bq * s4[u];
+                            y[m + 32] = a * s4[u] + bq * c4[u];
                         }
                     }
                 } else {
-                    // v: one head-dim column per lane, 64 tokens along the row of vt
-                    const int b0 = min(rbase, M - 1) / S;
-                    const int s0 = rbase - b0 * S;
-                    const bool fast = (rbase + 63 < M) && (s0 + 63 < S) && ((s0 & 7) == 0);
+                    // rotate-half, hd = 128: pair (m, m + 64) spans the lane pair
 #pragma unroll
-                    for (int dc = 0; dc < HD; dc += 64) {
-                        const int d = dc + lane;
-                        const float *src = red + hw * HD + d;
-                        if (fast) {
-                            bf16 *dst = e.vt + (((size_t)b0 * e.kv_heads + head) * HD + d) * e.seq_pad + s0;
+                    for (int m4 = 0; m4 < 64; m4 += 4) {
+                        const floatx4 c4 = *(const floatx4 *)(ct + m4), s4 = *(const floatx4 *)(st + m4);
 #pragma unroll
-                            for (int r8 = 0; r8 < 64; r8 += 8) {
-                                bf16x8 v;
-#pragma unroll
-                                for (int u = 0; u < 8; ++u) v[u] = f2bf(src[(r8 + u) * kQkvStride]);
-                                *(bf16x8 *)(dst + r8) = v;
-                            }
-                        } else {
-                            for (int r = 0; r < 64; ++r) {
-                                const int row = rbase + r;
-                                if (row >= M) break;
-                                const int bidx = row / S, sp = row - bidx * S;
-                                e.vt[(((size_t)bidx * e.kv_heads + head) * HD + d) * e.seq_pad + sp] =
-                                    f2bf(src[r * kQkvStride]);
-                            }
+                        for (int u = 0; u < 4; ++u) {
+                            const int m = m4 + u;
+                            const float other = __shfl_xor(y[m], 1, 64);
+                            y[m] = part == 0 ? y[m] * c4[u] - other * s4[u] : other * s4[u] + y[m] * c4[u];
                         }
+                    }
+                }
+                if (row < M) {
+                    bf16 *dst = (sect == 0 ? e.q : e.k) +
+                                (((size_t)bidx * (sect == 0 ? e.heads : e.kv_heads) + head) * S + sp_) * HD +
+                                part * 64;
+#pragma unroll
+                    for (int c = 0; c < 64; c += 8) {
+                        bf16x8 v;
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) v[u] = f2bf(y[c + u]);
+                        *(bf16x8 *)(dst + c) = v;
+                    }
+                }
+            } else {
+                // v: head-dim column `within` over the 64 staged tokens
+                const int d = within;
+                const float *src = red + hl * HD + d;
+                const int b0 = min(rbase, M - 1) / S;
+                const int s0 = rbase - b0 * S;
+                const bool fast = (rbase + 63 < M) && (s0 + 63 < S) && ((s0 & 7) == 0);
+                if (fast) {
+                    bf16 *dst = e.vt + (((size_t)b0 * e.kv_heads + head) * HD + d) * e.seq_pad + s0;
+#pragma unroll
+                    for (int r8 = 0; r8 < 64; r8 += 8) {
+                        bf16x8 v;
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) v[u] = f2bf(src[(r8 + u) * kQkvStride]);
+                        *(bf16x8 *)(dst + r8) = v;
+                    }
+                } else {
+                    for (int r = 0; r < 64; ++r) {
+                        const int row = rbase + r;
+                        if (row >= M) break;
+                        const int bidx = row / S, sp_ = row - bidx * S;
+                        e.vt[(((size_t)bidx * e.kv_heads + head) * HD + d) * e.seq_pad + sp_] =
+                            f2bf(src[r * kQkvStride]);
                     }
                 }
             }
@@ -425,11 +463,9 @@ struct EpiQkv {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-// 8 waves (2 per SIMD, 128x64 each) for the plain epilogues: two waves per SIMD
-// let one wave's LDS waits overlap the other's MFMAs.  The qk-norm epilogue
-// needs whole heads per wave, so the QKV GEMM keeps 4 waves of 128x128.
+// 8 waves (2 per SIMD, 128x64 each): two waves per SIMD let one wave's LDS
+// waits overlap the other's MFMAs.
 using Tile8w = Tile<256, 256, 2, 4>;
-using TileBig = Tile<256, 256, 2, 2>;
 using TileNarrow = Tile<256, 128, 2, 2>;   // N = 128 outputs (the projection to latent channels)
 
 template <class T, class RowMap, class Epi>
@@ -470,7 +506,7 @@ hipError_t launch_gemm_swiglu(const bf16 *a, const bf16 *w, int64_t M, int F, in
 
 hipError_t launch_gemm_qkv(const bf16 *h, const bf16 *w, int64_t M, int N, int K, const QkvEpiArgs &e,
                            hipStream_t s) {
-    using T = TileBig;
+    using T = Tile8w;
     if (e.head_dim == 128) return run<T>(h, w, M, N, K, RowsIdentity{T::BN}, EpiQkv<128>{e}, s);
     return run<T>(h, w, M, N, K, RowsIdentity{T::BN}, EpiQkv<64>{e}, s);
 }
