@@ -5,19 +5,25 @@
 // grouped KV heads as in the zml-flow-rs page §VI attention signature).
 //
 // Work split: one workgroup = 8 waves = 256 queries of one (batch, head); each
-// wave owns 32 queries, two waves share a SIMD so that one wave's softmax
-// (VALU, transcendental exp2) overlaps the other wave's MFMAs.  Keys stream
-// through LDS in tiles of 64 (the K tile and the transposed V tile,
-// double-buffered; the next tile is prefetched into registers while the
-// current one is consumed).
+// wave owns 32 queries, two waves share a SIMD.  Keys stream through LDS in
+// tiles of 64 (the K tile and the transposed V tile) over a 4-stage ring that
+// is filled by register-free buffer->LDS loads, two tiles ahead of use.
 //
 // The scores are computed transposed, S^T = K Q^T (MFMA A = K rows, B = Q rows),
 // so an accumulator lane owns one query column and 16 keys: the running row
 // max and row sum are in-lane reductions plus one exchange with lane ^ 32.
-// P^T is then already in the B-operand layout of O^T += V^T P^T, up to a fixed
-// permutation of the 16 keys of each MFMA k-step ({0-3, 8-11} in lanes 0-31,
-// {4-7, 12-15} in lanes 32-63); the V^T tile is stored in LDS with its keys in
-// that order, so every V^T fragment is one 16-byte read.
+// P^T is then already the B operand of O^T += V^T P^T provided the 16 keys a
+// lane holds per MFMA k-step are the 8 consecutive keys its half of the wave
+// feeds to that k-step.  The accumulator puts rows {0-3, 8-11} of each
+// 16-row group in lanes 0-31 and {4-7, 12-15} in lanes 32-63, so the K tile is
+// loaded with rows 4-7 and 8-11 of every 16-row group swapped: LDS row r holds
+// key r with bits 2 and 3 exchanged.  V^T then stays in natural key order and
+// every V^T fragment is one 16-byte LDS read.
+//
+// Software pipeline per wave and key tile t: the QK^T MFMAs of tile t + 1 are
+// issued interleaved with the exponentials of tile t (VALU and the matrix
+// pipe overlap within the wave), then the PV MFMAs of tile t interleaved with
+// the row max of tile t + 1.
 #include "common.h"
 
 namespace dit {
@@ -25,36 +31,41 @@ namespace dit {
 template <int HD>
 __global__ __launch_bounds__(512, 1)
 void flash_attn_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ Vt,
-                       bf16 *__restrict__ O, int S, int S_pad, int H, int Hkv, float scale_log2) {
+                       bf16 *__restrict__ O, int S, int S_pad, int H, int Hkv, int n_qt, float scale_log2) {
+#if defined(__HIP_DEVICE_COMPILE__)   // buffer resources exist only in the device pass
     constexpr int NW = 8;                    // waves per workgroup
     constexpr int QW = 32;                   // queries per wave
     constexpr int BQ = NW * QW;              // queries per workgroup
     constexpr int BKV = 64;                  // keys per tile
-    constexpr int NT = NW * kWave;           // threads
-    constexpr int KCH = HD / 8;              // 16-byte chunks per K row
-    constexpr int KT_BYTES = BKV * HD * 2;   // K tile  [64 keys][HD]
+    constexpr int NS = 4;                    // LDS ring stages
+    constexpr int KROW = HD * 2;             // bytes per K row
+    constexpr int KT_BYTES = BKV * KROW;     // K tile  [64 keys][HD]
     constexpr int VT_BYTES = HD * BKV * 2;   // V^T tile [HD][64 keys]
     constexpr int STAGE = KT_BYTES + VT_BYTES;
-    constexpr int KLD = BKV * KCH / NT;      // K chunks per thread
-    constexpr int VLD = HD * 8 / NT;         // V^T chunks per thread
+    constexpr int KL = KT_BYTES / (1024 * NW);   // 1 KiB K loads per wave per tile
+    constexpr int VL = VT_BYTES / (1024 * NW);   // 1 KiB V^T loads per wave per tile
+    constexpr int LOADS = KL + VL;
     constexpr int KK = HD / 16;              // MFMA k-steps over head_dim
     constexpr int DS = HD / 32;              // 32-row blocks of O^T
-    static_assert(KLD >= 1 && VLD >= 1, "tile vs threads");
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+    static_assert(KL >= 1 && VL >= 1 && KT_BYTES % (1024 * NW) == 0, "tile vs waves");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[NS * STAGE];
 
     // LDS layouts (gfx950: 64 banks, 256 B per cycle; a ds_read_b128 serves 16
-    // lanes per cycle, a ds_write_b64 32 lanes).
-    // K tile: row r (key) of HD*2 bytes; 16-byte chunk c at slot c ^ kswz(r):
+    // lanes per cycle).
+    // K tile: row r of HD*2 bytes; 16-byte chunk c at slot c ^ kswz(r):
     //   HD = 128: 256-byte rows, kswz = r & 15 (16 rows hit 16 distinct slots);
     //   HD = 64: 128-byte rows, two per bank line, kswz = (r >> 1) & 7.
-    // V^T tile: row d of 128 bytes.  Keys 4q..4q+3 of 16-key group g sit in
-    //   8-byte slot 4g + perm(q), perm = {0, 2, 1, 3}, so 16-byte slot 2g+h
-    //   holds exactly the 8 keys lane half h feeds to the MFMA; 16-byte slot s
-    //   is stored at s ^ ((d >> 1) & 7).
+    // V^T tile: row d of 128 bytes (64 keys); chunk c at slot c ^ ((d >> 1) & 7).
     auto kswz = [](int r) { return HD == 128 ? (r & 15) : ((r >> 1) & 7); };
-    auto vslot = [](int d, int s16) { return (s16 ^ ((d >> 1) & 7)) << 4; };
+    auto vswz = [](int d) { return (d >> 1) & 7; };
 
-    const int h = blockIdx.y, b = blockIdx.z;
+    // Task order: with a multiple of 8 workgroups, XCD x (workgroups x, x + 8,
+    // ...) runs the contiguous task range [x n/8, (x+1) n/8), so the q tiles of
+    // one head share that XCD's L2 for K and V.
+    int task = blockIdx.x;
+    if ((gridDim.x & 7) == 0) task = (task & 7) * (gridDim.x >> 3) + (task >> 3);
+    const int qt = task % n_qt, bh = task / n_qt;
+    const int h = bh % H, b = bh / H;
     const int g = h / (H / Hkv);
     const bf16 *Qh = Q + (size_t)(b * H + h) * S * HD;
     const bf16 *Kh = K + (size_t)(b * Hkv + g) * S * HD;
@@ -62,7 +73,7 @@ void flash_attn_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K, c
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lrow = lane & 31, lhalf = lane >> 5;
-    const int q_base = blockIdx.x * BQ + wave * QW;
+    const int q_base = qt * BQ + wave * QW;
 
     // Q as the B operand: lane -> query q_base + lrow, dims kk*16 + lhalf*8 .. +8
     bf16x8 qf[KK];
@@ -72,34 +83,65 @@ void flash_attn_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K, c
         for (int kk = 0; kk < KK; ++kk) qf[kk] = *(const bf16x8 *)(Qh + (size_t)qr * HD + kk * 16 + lhalf * 8);
     }
 
-    uint4 rk[KLD], rv[VLD];
-#define DIT_ATT_GLOAD(kv0)                                                                          \
-    do {                                                                                            \
-        _Pragma("unroll") for (int q = 0; q < KLD; ++q) {                                          \
-            const int id = q * NT + tid, r = id / KCH, c = id % KCH;                                \
-            const int key = min((kv0) + r, S - 1);   /* tail keys: any valid row, masked below */   \
-            rk[q] = *(const uint4 *)(Kh + (size_t)key * HD + c * 8);                                \
-        }                                                                                           \
-        _Pragma("unroll") for (int q = 0; q < VLD; ++q) {                                          \
-            const int id = q * NT + tid, d = id >> 3, c = id & 7;                                   \
-            rv[q] = *(const uint4 *)(Vh + (size_t)d * S_pad + (kv0) + c * 8); /* [S,S_pad) zero */  \
-        }                                                                                           \
+    // Load q of this wave fills 1 KiB at (q * NW + wave) KiB of the K (V^T) tile;
+    // lane l lands at +16 l, i.e. in row lin / rowbytes, slot (lin % rowbytes) / 16.
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh, (uint32_t)S * (uint32_t)KROW);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh, (uint32_t)HD * (uint32_t)S_pad * 2u);
+    int k_key[KL];            // key within the tile (bits 2 and 3 of the row swapped)
+    uint32_t k_col[KL];       // byte offset of the logical chunk within the row
+    uint32_t v_off[VL];
+#pragma unroll
+    for (int q = 0; q < KL; ++q) {
+        const int lin = (q * NW + wave) * 1024 + lane * 16;
+        const int r = lin / KROW, slot = (lin % KROW) >> 4;
+        k_key[q] = (r & ~15) | (((r >> 2) & 1) << 3) | (((r >> 3) & 1) << 2) | (r & 3);
+        k_col[q] = (uint32_t)((slot ^ kswz(r)) << 4);
+    }
+#pragma unroll
+    for (int q = 0; q < VL; ++q) {
+        const int lin = (q * NW + wave) * 1024 + lane * 16;
+        const int d = lin >> 7, slot = (lin & 127) >> 4;
+        v_off[q] = (uint32_t)d * (uint32_t)S_pad * 2u + (uint32_t)((slot ^ vswz(d)) << 4);
+    }
+    const int nt = (S + BKV - 1) / BKV;
+    // tail keys of K read a valid row (masked below); V^T keys in [S, S_pad) are zero
+#define DIT_ATT_ISSUE(tile, st)                                                                        \
+    do {                                                                                               \
+        const int kv0_ = (tile) * BKV;                                                                 \
+        uint8_t *base_ = smem + (st) * STAGE;                                                          \
+        _Pragma("unroll") for (int q = 0; q < KL; ++q) __builtin_amdgcn_raw_ptr_buffer_load_lds(      \
+            rk, (lds_void *)(base_ + (q * NW + wave) * 1024), 16,                                      \
+            (uint32_t)min(kv0_ + k_key[q], S - 1) * (uint32_t)KROW + k_col[q], 0, 0, 0);               \
+        _Pragma("unroll") for (int q = 0; q < VL; ++q) __builtin_amdgcn_raw_ptr_buffer_load_lds(      \
+            rv, (lds_void *)(base_ + KT_BYTES + (q * NW + wave) * 1024), 16, v_off[q],                 \
+            (uint32_t)kv0_ * 2u, 0, 0);                                                                \
     } while (0)
-#define DIT_ATT_LSTORE(st)                                                                          \
-    do {                                                                                            \
-        uint8_t *base_ = smem + (st) * STAGE;                                                       \
-        _Pragma("unroll") for (int q = 0; q < KLD; ++q) {                                          \
-            const int id = q * NT + tid, r = id / KCH, c = id % KCH;                                \
-            *(uint4 *)(base_ + r * (HD * 2) + ((c ^ kswz(r)) << 4)) = rk[q];                        \
-        }                                                                                           \
-        _Pragma("unroll") for (int q = 0; q < VLD; ++q) {                                          \
-            const int id = q * NT + tid, d = id >> 3, c = id & 7;                                   \
-            /* keys 8c..8c+3 -> 8-byte slot 4(c/2) + (c&1); keys 8c+4.. -> 4(c/2) + 2 + (c&1) */    \
-            const int lo = ((c >> 1) << 2) + (c & 1), hi = lo + 2;                                  \
-            uint8_t *row = base_ + KT_BYTES + d * 128;                                              \
-            *(uint2 *)(row + vslot(d, lo >> 1) + ((lo & 1) << 3)) = make_uint2(rv[q].x, rv[q].y);  \
-            *(uint2 *)(row + vslot(d, hi >> 1) + ((hi & 1) << 3)) = make_uint2(rv[q].z, rv[q].w);  \
-        }                                                                                           \
+    // S^T[key, q] of the tile in stage st (64 keys x 32 queries)
+#define DIT_ATT_QK(st, acc)                                                                            \
+    do {                                                                                               \
+        const uint8_t *sk_ = smem + (st) * STAGE;                                                      \
+        _Pragma("unroll") for (int ks = 0; ks < 2; ++ks)                                               \
+            _Pragma("unroll") for (int e = 0; e < 16; ++e) acc[ks][e] = 0.f;                           \
+        _Pragma("unroll") for (int kk = 0; kk < KK; ++kk) {                                            \
+            const int c_ = kk * 2 + lhalf;                                                             \
+            _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                         \
+                const bf16x8 kf_ =                                                                     \
+                    *(const bf16x8 *)(sk_ + (ks * 32 + lrow) * KROW + ((c_ ^ kswz(lrow)) << 4));       \
+                acc[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf_, qf[kk], acc[ks], 0, 0, 0);      \
+            }                                                                                          \
+        }                                                                                              \
+    } while (0)
+    // keys >= S (tail tile, or the never-used tile past the end) -> -inf; element
+    // e of acc[ks] in lane half h is key kv0 + 32 ks + 16 (e / 8) + 8 h + e % 8
+#define DIT_ATT_MASK(kv0, acc)                                                                         \
+    do {                                                                                               \
+        if ((kv0) + BKV > S) {                                                                         \
+            _Pragma("unroll") for (int ks = 0; ks < 2; ++ks)                                           \
+                _Pragma("unroll") for (int e = 0; e < 16; ++e) {                                       \
+                    const int key_ = (kv0) + ks * 32 + ((e >> 3) << 4) + (lhalf << 3) + (e & 7);       \
+                    if (key_ >= S) acc[ks][e] = -INFINITY;                                             \
+                }                                                                                      \
+        }                                                                                              \
     } while (0)
 
     floatx16 oacc[DS];
@@ -107,94 +149,126 @@ void flash_attn_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K, c
     for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[ds][e] = 0.f;
-    float mraw = -INFINITY;     // running max of the raw (unscaled) scores of this lane's query
+
+    // prologue: tiles 0 .. NS-2 in flight, wait for tiles 0 and 1
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j) DIT_ATT_ISSUE(min(j, nt - 1), j);
+    wait_vmcnt<(NS - 3) * LOADS>();
+    barrier_only();
+
+    floatx16 sa[2];             // scores of the tile being exponentiated
+    DIT_ATT_QK(0, sa);
+    DIT_ATT_MASK(0, sa);
+    // running max of the raw (unscaled) scores of this lane's query; scale > 0
+    // commutes with max
+    float mraw;
+    {
+        float mx = sa[0][0];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sa[ks][e]);
+        mraw = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    }
+    float alpha = 1.f;          // factor taking O and l from the previous max to mraw
     float lsum = 0.f;           // this lane's partial row sum (the other 16 keys live in lane ^ 32)
 
-    const int ntiles = (S + BKV - 1) / BKV;
-    DIT_ATT_GLOAD(0);
-    DIT_ATT_LSTORE(0);
-    __syncthreads();
-
-    for (int t = 0; t < ntiles; ++t) {
-        const int cur = t & 1;
-        const int kv0 = t * BKV;
-        if (t + 1 < ntiles) DIT_ATT_GLOAD(kv0 + BKV);
-        const uint8_t *sk = smem + cur * STAGE;
-        const uint8_t *sv = sk + KT_BYTES;
-
-        // S^T[key, q] for 64 keys x 32 queries
-        floatx16 sacc[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) sacc[ks][e] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            const int c = kk * 2 + lhalf;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 kf = *(const bf16x8 *)(sk + (ks * 32 + lrow) * (HD * 2) + ((c ^ kswz(lrow)) << 4));
-                sacc[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[ks], 0, 0, 0);
-            }
-        }
-
-        // online softmax on raw scores (scale > 0 commutes with max); keys >= S
-        // are masked in the last tile
-        if (kv0 + BKV > S) {
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int key = kv0 + ks * 32 + ((e >> 2) << 3) + (lhalf << 2) + (e & 3);
-                    if (key >= S) sacc[ks][e] = -INFINITY;
-                }
-        }
-        float mx = sacc[0][0];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[ks][e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        // rescale only when some lane's running max grew (wave-uniform branch;
-        // lanes whose max did not move get factor 1)
-        if (__any(mx > mraw)) {
-            const float mnew = fmaxf(mraw, mx);
-            const float alpha = __builtin_amdgcn_exp2f((mraw - mnew) * scale_log2);
-            mraw = mnew;
-            lsum *= alpha;
-#pragma unroll
-            for (int ds = 0; ds < DS; ++ds)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) oacc[ds][e] *= alpha;
-        }
-        const float neg = -mraw * scale_log2;
-        bf16x8 pf[4];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(sacc[ks][e], scale_log2, neg));
-                lsum += p;
-                pf[ks * 2 + (e >> 3)][e & 7] = f2bf(p);
-            }
-
-        // O^T[d, q] += V^T[d, keys] P^T[keys, q]
-#pragma unroll
-        for (int k2 = 0; k2 < 4; ++k2) {
-#pragma unroll
-            for (int ds = 0; ds < DS; ++ds) {
-                const int d = ds * 32 + lrow;
-                const bf16x8 vf = *(const bf16x8 *)(sv + d * 128 + vslot(d, k2 * 2 + lhalf));
-                oacc[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[k2], oacc[ds], 0, 0, 0);
-            }
-        }
-
-        // stage cur ^ 1 (tile t - 1) was released by the barrier closing iteration t - 1
-        if (t + 1 < ntiles) DIT_ATT_LSTORE(cur ^ 1);
-        __syncthreads();
+    // one key tile; MASKED = 0 for the steady state (tile t + 1 holds 64 valid
+    // keys), 1 for the last two tiles
+#define DIT_ATT_STEP(MASKED, T, SC, SN)                                                                       \
+    do {                                                                                                      \
+        /* stage (t-1) % NS was released by the barrier that closed iteration t - 1 */                        \
+        DIT_ATT_ISSUE(min((T) + NS - 1, nt - 1), ((T) + NS - 1) % NS);                                        \
+        /* rescale only when some lane's running max grew (wave-uniform branch) */                            \
+        if (__any(alpha < 1.f)) {                                                                             \
+_Pragma("unroll")                                                                                             \
+            for (int ds = 0; ds < DS; ++ds)                                                                   \
+_Pragma("unroll")                                                                                             \
+                for (int e = 0; e < 16; ++e) oacc[ds][e] *= alpha;                                            \
+        }                                                                                                     \
+        lsum *= alpha;                                                                                        \
+                                                                                                              \
+        /* QK^T of tile t + 1 || exponentials of tile t */                                                    \
+        DIT_ATT_QK(((T) + 1) % NS, SN);                                                                       \
+        const float neg = -mraw * scale_log2;                                                                 \
+        bf16x8 pf[4];                                                                                         \
+_Pragma("unroll")                                                                                             \
+        for (int ks = 0; ks < 2; ++ks)                                                                        \
+_Pragma("unroll")                                                                                             \
+            for (int e = 0; e < 16; ++e) {                                                                    \
+                const float p = __builtin_amdgcn_exp2f(fmaf(SC[ks][e], scale_log2, neg));                     \
+                lsum += p;                                                                                    \
+                pf[ks * 2 + (e >> 3)][e & 7] = f2bf(p);                                                       \
+            }                                                                                                 \
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                                    \
+_Pragma("unroll")                                                                                             \
+        for (int i = 0; i < 2 * KK - 2; ++i) {                                                                \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                \
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                                \
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);                                                \
+        }                                                                                                     \
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                                    \
+                                                                                                              \
+        if (MASKED) DIT_ATT_MASK(((T) + 1) * BKV, SN);                                                        \
+                                                                                                              \
+        /* O^T[d, q] += V^T[d, keys] P^T[keys, q] of tile t || row max of tile t + 1 */                       \
+        {                                                                                                     \
+            const uint8_t *sv = smem + ((T) % NS) * STAGE + KT_BYTES;                                         \
+_Pragma("unroll")                                                                                             \
+            for (int k2 = 0; k2 < 4; ++k2) {                                                                  \
+_Pragma("unroll")                                                                                             \
+                for (int ds = 0; ds < DS; ++ds) {                                                             \
+                    const int d = ds * 32 + lrow;                                                             \
+                    const bf16x8 vf = *(const bf16x8 *)(sv + d * 128 + (((k2 * 2 + lhalf) ^ vswz(d)) << 4));  \
+                    oacc[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[k2], oacc[ds], 0, 0, 0);        \
+                }                                                                                             \
+            }                                                                                                 \
+            float mx = SN[0][0];                                                                              \
+_Pragma("unroll")                                                                                             \
+            for (int ks = 0; ks < 2; ++ks)                                                                    \
+_Pragma("unroll")                                                                                             \
+                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, SN[ks][e]);                                       \
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));                                                           \
+            const float mnew = fmaxf(mraw, mx);                                                               \
+            alpha = __builtin_amdgcn_exp2f((mraw - mnew) * scale_log2);                                       \
+            mraw = mnew;                                                                                      \
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                                \
+_Pragma("unroll")                                                                                             \
+            for (int i = 0; i < 4 * DS - 2; ++i) {                                                            \
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                            \
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                            \
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);                                            \
+            }                                                                                                 \
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                                \
+        }                                                                                                     \
+                                                                                                              \
+        /* tile t + 2 landed (tiles t+3 .. t+NS-1 may still be in flight) */                                  \
+        wait_vmcnt<(NS - 3) * LOADS>();                                                                       \
+        barrier_only();                                                                                       \
+                                                                                                              \
+    } while (0)
+    floatx16 sb[2];
+    int t = 0;
+    for (; t + 1 < nt - 2; t += 2) {
+        DIT_ATT_STEP(0, t, sa, sb);
+        DIT_ATT_STEP(0, t + 1, sb, sa);
     }
-#undef DIT_ATT_GLOAD
-#undef DIT_ATT_LSTORE
+    if (t < nt - 2) {
+        DIT_ATT_STEP(0, t, sa, sb);
+        ++t;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) sa[ks] = sb[ks];
+    }
+    for (; t < nt; ++t) {
+        DIT_ATT_STEP(1, t, sa, sb);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) sa[ks] = sb[ks];
+    }
+#undef DIT_ATT_STEP
+    wait_vmcnt<0>();      // retire the trailing (never read) loads before the workgroup's LDS is released
+#undef DIT_ATT_ISSUE
+#undef DIT_ATT_QK
+#undef DIT_ATT_MASK
 
     // normalise and store O[b*S + q, h*HD + d] (4 consecutive d per 8-byte store)
     const float l = lsum + __shfl_xor(lsum, 32, 64);
@@ -212,18 +286,20 @@ void flash_attn_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K, c
                 *(bf16x4 *)(orow + ds * 32 + e4 * 8 + lhalf * 4) = v;
             }
     }
+#endif
 }
 
 hipError_t launch_flash_attention(const bf16 *q, const bf16 *k, const bf16 *vt, bf16 *out, int batch, int seq,
                                   int seq_pad, int heads, int kv_heads, int head_dim, hipStream_t s) {
-    const dim3 grid((seq + 255) / 256, heads, batch);
+    const int n_qt = (seq + 255) / 256;
+    const dim3 grid((unsigned)(n_qt * heads * batch));
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)head_dim);
     if (head_dim == 128)
         hipLaunchKernelGGL(flash_attn_kernel<128>, grid, dim3(512), 0, s, q, k, vt, out, seq, seq_pad, heads,
-                           kv_heads, scale_log2);
+                           kv_heads, n_qt, scale_log2);
     else
         hipLaunchKernelGGL(flash_attn_kernel<64>, grid, dim3(512), 0, s, q, k, vt, out, seq, seq_pad, heads,
-                           kv_heads, scale_log2);
+                           kv_heads, n_qt, scale_log2);
     return hipGetLastError();
 }
 

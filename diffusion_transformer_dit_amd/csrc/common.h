@@ -42,6 +42,27 @@ __device__ __forceinline__ float group_max(float v) {
     return v;
 }
 
+// Register-free global -> LDS loads (buffer_load_dwordx4 ... lds): one
+// instruction moves 64 lanes x 16 bytes into 1 KiB of LDS at the wave-uniform
+// LDS address (lane l at +16 l).
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
+// [6:4], lgkmcnt [11:8]); LGKM = 0 also drains this wave's LDS reads.
+template <int N, int LGKM = 15>
+__device__ __forceinline__ void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (LGKM << 8));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(): that fence
+// would wait for every outstanding buffer->LDS load, including the stages
+// still meant to be in flight.  Ordering is provided by the explicit waits.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
 __device__ __forceinline__ float silu_f(float z) {
     // z * sigmoid(z); expf of a large positive -z gives inf and z/inf -> -0
     return z / (1.0f + __expf(-z));

@@ -87,24 +87,6 @@ struct RowsSwiglu {
     }
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
-// [6:4], lgkmcnt [11:8]); LGKM = 0 also drains this wave's LDS reads.
-template <int N, int LGKM = 15>
-__device__ __forceinline__ void wait_vmcnt() {
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (LGKM << 8));
-}
-
-// Workgroup barrier without the memory fence of __syncthreads(): that fence
-// would wait for every outstanding buffer->LDS load, including the stages
-// still meant to be in flight.  Ordering is provided by the explicit waits.
-__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
-
 template <class T, class RowMap, class Epi>
 __global__ __launch_bounds__(T::kThreads, 1)
 void gemm_kernel(const bf16 *__restrict__ A, const bf16 *__restrict__ W, int M, int K, int w_rows,
