@@ -225,23 +225,53 @@ struct EpiResidual {
                                           uint8_t *) const {
         const int lrow = lane & 31, lhalf = lane >> 5;
         const int col0 = tn * T::BN + wn * T::kWaveN;
+        float g[T::TN], bb[T::TN];
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) {
             const int col = col0 + j * 32 + lrow;
-            const float g = gate ? gate[col] : 1.0f;
-            const float bb = bias ? bias[col] : 0.0f;
+            g[j] = gate ? gate[col] : 1.0f;
+            bb[j] = bias ? bias[col] : 0.0f;
+        }
+        // out may alias resid (in-place update), but every element is read and
+        // written by this lane only, so a batch of residual loads may precede the
+        // batch of stores; without the batching the compiler has to wait for each
+        // store before the next load.  Rows past M load row M - 1 and store nothing.
 #pragma unroll
-            for (int i = 0; i < T::TM; ++i)
+        for (int i = 0; i < T::TM; ++i) {
+            float r[T::TN][16];
+            if (resid) {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int row = row0 + acc_row(i, e, lhalf);
-                    if (row < M) {
-                        const size_t o = (size_t)row * N + col;
-                        float v = acc[i][j][e] * g + bb;
-                        if (resid) v += to_f32<TR>(resid[o]);
-                        out[o] = from_f32<TO>(v);
+                for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int row = min(row0 + acc_row(i, e, lhalf), M - 1);
+                        r[j][e] = to_f32<TR>(resid[(size_t)row * N + col0 + j * 32 + lrow]);
                     }
-                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) r[j][e] = 0.0f;
+            }
+            // wave-uniform: all 32 rows of block i in range -> straight-line stores
+            if (row0 + i * 32 + 32 <= M) {
+#pragma unroll
+                for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        out[(size_t)(row0 + acc_row(i, e, lhalf)) * N + col0 + j * 32 + lrow] =
+                            from_f32<TO>(fmaf(acc[i][j][e], g[j], bb[j]) + r[j][e]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int row = row0 + acc_row(i, e, lhalf);
+                        if (row < M)
+                            out[(size_t)row * N + col0 + j * 32 + lrow] =
+                                from_f32<TO>(fmaf(acc[i][j][e], g[j], bb[j]) + r[j][e]);
+                    }
+            }
         }
     }
 };
