@@ -76,58 +76,67 @@ hipError_t launch_adaln_gemv(const bf16 *w, const float *b, const float *c, int 
 
 // ---------------------------------------------------------------------------
 // LayerNorm + modulation, one wave per row.  The row stays in registers
-// (dim/256 float4 per lane) between the mean pass, the centred variance pass
-// and the output pass, so x is read from HBM exactly once.
+// (IT = dim/256 float4 per lane) between the mean pass, the centred variance
+// pass and the output pass, so x is read from HBM exactly once.  IT is a
+// template parameter so that all IT loads of a lane are issued back to back
+// (a runtime trip count puts each load behind its own branch and the wave
+// then waits for every load before issuing the next).
 //   mode 0: h = n * (1 + scale) + shift      mode 1: h = n * scale + shift
 // ---------------------------------------------------------------------------
-constexpr int kLnMaxIt = 32;   // dim <= 32 * 256
-
-template <typename TX>
+template <typename TX, int IT>
 __global__ __launch_bounds__(256)
-void ln_modulate_kernel(const TX *__restrict__ x, int64_t rows, int dim, const float *__restrict__ shift,
+void ln_modulate_kernel(const TX *__restrict__ x, int64_t rows, const float *__restrict__ shift,
                         const float *__restrict__ scale, int mode, float eps, bf16 *__restrict__ h) {
+    constexpr int dim = IT * 256;
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
-    const int iters = dim >> 8;
     const TX *xr = x + row * dim;
-    floatx4 v[kLnMaxIt];
+    floatx4 v[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int i = it * 256 + lane * 4;
+        if constexpr (sizeof(TX) == 4) {
+            v[it] = *(const floatx4 *)(xr + i);
+        } else {
+            const bf16x4 t = *(const bf16x4 *)(xr + i);
+            v[it] = floatx4{(float)t[0], (float)t[1], (float)t[2], (float)t[3]};
+        }
+    }
     float s = 0.f;
 #pragma unroll
-    for (int it = 0; it < kLnMaxIt; ++it) {
-        if (it < iters) {
-            const int i = it * 256 + lane * 4;
-            if constexpr (sizeof(TX) == 4) {
-                v[it] = *(const floatx4 *)(xr + i);
-            } else {
-                const bf16x4 t = *(const bf16x4 *)(xr + i);
-                v[it] = floatx4{(float)t[0], (float)t[1], (float)t[2], (float)t[3]};
-            }
-            s += (v[it][0] + v[it][1]) + (v[it][2] + v[it][3]);
-        }
-    }
-    const float mean = group_sum<64>(s) / (float)dim;
+    for (int it = 0; it < IT; ++it) s += (v[it][0] + v[it][1]) + (v[it][2] + v[it][3]);
+    const float mean = group_sum<64>(s) * (1.0f / dim);
     float ss = 0.f;
 #pragma unroll
-    for (int it = 0; it < kLnMaxIt; ++it) {
-        if (it < iters) {
+    for (int it = 0; it < IT; ++it)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float d = v[it][k] - mean;
-                v[it][k] = d;
-                ss += d * d;
-            }
+        for (int k = 0; k < 4; ++k) {
+            const float d = v[it][k] - mean;
+            v[it][k] = d;
+            ss += d * d;
         }
-    }
-    const float rstd = rsqrtf(group_sum<64>(ss) / (float)dim + eps);
+    const float rstd = rsqrtf(group_sum<64>(ss) * (1.0f / dim) + eps);
+    const float one = mode == 0 ? 1.0f : 0.0f;
     bf16 *hr = h + row * dim;
+    if (scale && shift) {
 #pragma unroll
-    for (int it = 0; it < kLnMaxIt; ++it) {
-        if (it < iters) {
+        for (int it = 0; it < IT; ++it) {
+            const int i = it * 256 + lane * 4;
+            const floatx4 mul = *(const floatx4 *)(scale + i);
+            const floatx4 add = *(const floatx4 *)(shift + i);
+            bf16x4 o;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) o[k] = f2bf(v[it][k] * rstd * (mul[k] + one) + add[k]);
+            *(bf16x4 *)(hr + i) = o;
+        }
+    } else {
+        // mode 1 with a null scale (taken as 1) and/or a null shift (taken as 0)
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
             const int i = it * 256 + lane * 4;
             floatx4 mul = {1.f, 1.f, 1.f, 1.f}, add = {0.f, 0.f, 0.f, 0.f};
-            if (scale) mul = *(const floatx4 *)(scale + i);
-            if (mode == 0) mul += 1.0f;
+            if (scale) mul = *(const floatx4 *)(scale + i) + one;
             if (shift) add = *(const floatx4 *)(shift + i);
             bf16x4 o;
 #pragma unroll
@@ -137,16 +146,34 @@ void ln_modulate_kernel(const TX *__restrict__ x, int64_t rows, int dim, const f
     }
 }
 
+template <typename TX>
+static hipError_t ln_modulate_typed(const TX *x, int64_t rows, int dim, const float *shift, const float *scale,
+                                    int mode, float eps, bf16 *h, hipStream_t s) {
+    const dim3 grid((unsigned)((rows + 3) / 4));
+    switch (dim >> 8) {
+#define DIT_LN_CASE(n)                                                                                 \
+    case n:                                                                                            \
+        hipLaunchKernelGGL((ln_modulate_kernel<TX, n>), grid, dim3(256), 0, s, x, rows, shift, scale, \
+                           mode, eps, h);                                                              \
+        break;
+        DIT_LN_CASE(1) DIT_LN_CASE(2) DIT_LN_CASE(3) DIT_LN_CASE(4) DIT_LN_CASE(5) DIT_LN_CASE(6)
+        DIT_LN_CASE(7) DIT_LN_CASE(8) DIT_LN_CASE(9) DIT_LN_CASE(10) DIT_LN_CASE(11) DIT_LN_CASE(12)
+        DIT_LN_CASE(13) DIT_LN_CASE(14) DIT_LN_CASE(15) DIT_LN_CASE(16) DIT_LN_CASE(17) DIT_LN_CASE(18)
+        DIT_LN_CASE(19) DIT_LN_CASE(20) DIT_LN_CASE(21) DIT_LN_CASE(22) DIT_LN_CASE(23) DIT_LN_CASE(24)
+        DIT_LN_CASE(25) DIT_LN_CASE(26) DIT_LN_CASE(27) DIT_LN_CASE(28) DIT_LN_CASE(29) DIT_LN_CASE(30)
+        DIT_LN_CASE(31) DIT_LN_CASE(32)
+#undef DIT_LN_CASE
+        default:
+            return hipErrorInvalidValue;   // dim must be a multiple of 256 in [256, 8192]
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_ln_modulate(const void *x, int x_f32, int64_t rows, int dim, const float *shift,
                               const float *scale, int mode, float eps, bf16 *h, hipStream_t s) {
-    const dim3 grid((unsigned)((rows + 3) / 4));
-    if (x_f32)
-        hipLaunchKernelGGL(ln_modulate_kernel<float>, grid, dim3(256), 0, s, (const float *)x, rows, dim, shift,
-                           scale, mode, eps, h);
-    else
-        hipLaunchKernelGGL(ln_modulate_kernel<bf16>, grid, dim3(256), 0, s, (const bf16 *)x, rows, dim, shift,
-                           scale, mode, eps, h);
-    return hipGetLastError();
+    if (dim % 256 != 0) return hipErrorInvalidValue;
+    if (x_f32) return ln_modulate_typed<float>((const float *)x, rows, dim, shift, scale, mode, eps, h, s);
+    return ln_modulate_typed<bf16>((const bf16 *)x, rows, dim, shift, scale, mode, eps, h, s);
 }
 
 // ---------------------------------------------------------------------------
