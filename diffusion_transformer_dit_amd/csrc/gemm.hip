@@ -307,42 +307,82 @@ struct EpiSwiglu {
 // epilogue: qk-LayerNorm + RoPE, scatter to q [B,H,S,hd], k [B,Hk,S,hd],
 // vt [B,Hk,hd,Spad], for the 8-wave 256 x 256 tile (wave tile 128 x 64).
 // A head spans several waves' columns, so the accumulators go through LDS
-// (free once the K loop has drained): each 4-wave cluster (128 rows) stages
-// 64 of its rows x 256 columns at a time, both clusters in parallel.  Then
-// each lane takes one unit of work of one head of the tile:
-//   q/k head: one token row (64 values per lane; a 128-wide head row is
-//             split over a lane pair that combines its LayerNorm statistics
-//             with one exchange) -- RoPE pairs in-lane (rotate-half at
-//             hd = 128 swaps halves with the partner lane); 16-byte stores;
-//   v head:   one head-dim column over the 64 staged tokens, written
-//             contiguously along the key axis of v^T.
+// (free once the K loop has drained): each 4-wave cluster (128 rows) handles
+// 64 of its rows x 256 columns at a time (two sub-passes), both clusters in
+// parallel.  Per sub-pass:
+//   1. the cluster's fp32 accumulators are staged in LDS;
+//   2. each lane computes one unit of one head of the tile into registers:
+//      q/k head: one token row, 64 values per lane (a 128-wide head row is
+//                split over a lane pair that combines its LayerNorm
+//                statistics with one exchange); the split keeps every RoPE
+//                pair in one lane: interleaved pairs (2m, 2m+1) -> lane half
+//                p holds columns [64p, 64p+64); rotate-half pairs (m, m+hd/2)
+//                -> it holds [32p, 32p+32) and [hd/2+32p, hd/2+32p+32);
+//      v head:   one head-dim column over the 64 staged tokens;
+//   3. the bf16 results replace the staged values in LDS, laid out as they
+//      are in memory (a q/k head: 64 rows x hd; a v head: hd rows x 64
+//      tokens of v^T), and the cluster copies them out with lane-contiguous
+//      16-byte stores (a q/k head of 64 tokens is one contiguous block, a v^T
+//      row one 128-byte line).
+// The LayerNorm gamma/beta of q and k sit in LDS behind the staging area
+// (copied once per tile), and a lane's cos/sin row is loaded before the
+// staging barrier, which waits for LDS traffic only, so those global loads
+// overlap the staging.
 // ---------------------------------------------------------------------------
 constexpr int kQkvStride = 260;   // floats per staged row: 256 + 4, so 16 row-per-lane reads hit distinct banks
 
 template <int HD>
 struct EpiQkv {
     QkvEpiArgs e;
-    template <class T> static constexpr int lds_bytes() { return 2 * 64 * kQkvStride * 4; }
+    static constexpr int kStageBytes = 2 * 64 * kQkvStride * 4;
+    static constexpr int kHeadBlock = 64 * HD * 2;        // bf16 bytes of one head x 64 tokens
+    static constexpr int kRowChunks = HD / 8;             // 16-byte chunks per q/k output row
+    template <class T> static constexpr int lds_bytes() { return kStageBytes + 4 * HD * 4; }
+
+    // LDS slot of 16-byte chunk c of q/k output row r / of v^T row d
+    static __device__ __forceinline__ int qk_slot(int r, int c) { return r * (HD * 2) + ((c ^ (r & (kRowChunks - 1))) << 4); }
+    static __device__ __forceinline__ int v_slot(int d, int c) { return d * 128 + ((c ^ ((d >> 1) & 7)) << 4); }
 
     template <class T>
     __device__ __forceinline__ void apply(floatx16 (&acc)[T::TM][T::TN], int row0, int tn, int wn, int lane, int M,
                                           uint8_t *smem) const {
         static_assert(T::BN == 256 && T::WM == 2 && T::WN == 4 && T::kWaveM == 128 && T::kWaveN == 64,
                       "staging assumes the 8-wave 256x256 tile");
+        static_assert(2 * 64 * kQkvStride * 4 / 2 >= (256 / HD) * kHeadBlock, "output block fits the staging area");
         const int lrow = lane & 31, lhalf = lane >> 5;
         const int wave = threadIdx.x >> 6;
         const int cl = wave >> 2;                          // cluster = wm: rows cl*128 .. +128 of the tile
         const int lc = (wave & 3) * 64 + lane;             // lane within the cluster, 0..255
         float *red = (float *)smem + cl * 64 * kQkvStride;
-        const int hl = lc / HD, within = lc % HD;          // head of the tile, unit within that head
-        const int hc0 = tn * T::BN + hl * HD;              // global first column of that head
+        uint8_t *ob = (uint8_t *)red;                      // bf16 output blocks (same bytes, after the reads)
         const int qcols = e.heads * HD, kcols = e.kv_heads * HD;
-        const int sect = hc0 < qcols ? 0 : (hc0 < qcols + kcols ? 1 : 2);   // uniform per wave
-        const int head = sect == 0 ? hc0 / HD : (sect == 1 ? (hc0 - qcols) / HD : (hc0 - qcols - kcols) / HD);
+        // section (0 q, 1 k, 2 v) and head index of head slot hs of this tile
+        auto head_of = [&](int hs, int &sect, int &head) {
+            const int c0 = tn * T::BN + hs * HD;
+            sect = c0 < qcols ? 0 : (c0 < qcols + kcols ? 1 : 2);
+            head = (c0 - (sect == 0 ? 0 : (sect == 1 ? qcols : qcols + kcols))) / HD;
+        };
+        const int hl = lc / HD, within = lc % HD;          // head slot of this lane, unit within that head
+        int sect, head;
+        head_of(hl, sect, head);                           // uniform per wave
         const int S = e.seq;
+        // q_g, q_b, k_g, k_b (HD floats each); visible after the first staging barrier
+        float *gb = (float *)(smem + kStageBytes);
+        if (e.qk_norm) {
+            for (int i = threadIdx.x; i < 4 * HD; i += T::kThreads) {
+                const int which = i / HD, c = i - which * HD;
+                const float *src = which == 0 ? e.q_g : (which == 1 ? e.q_b : (which == 2 ? e.k_g : e.k_b));
+                gb[i] = src[c];
+            }
+        }
+        constexpr int PARTS = HD / 64;                     // lanes per q/k head row
+        const int rl = within / PARTS, part = within % PARTS;
+        // the 32 RoPE pairs of this lane: frequencies pair0 .. pair0 + 31
+        const int pair0 = part * 32;
 #pragma unroll
         for (int sp = 0; sp < 2; ++sp) {
-            __syncthreads();   // the K loop (or the previous sub-pass) is done with the LDS
+            // the K loop, or the previous sub-pass's copy-out, is done with the LDS
+            if (sp > 0) { wait_vmcnt<63, 0>(); barrier_only(); }
 #pragma unroll
             for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
@@ -351,120 +391,154 @@ struct EpiQkv {
                     for (int r = 0; r < 16; ++r)
                         red[(ii * 32 + ((r >> 2) << 3) + (lhalf << 2) + (r & 3)) * kQkvStride + wn * 64 + j * 32 +
                             lrow] = acc[sp * 2 + ii][j][r];
-            __syncthreads();
             const int rbase = row0 + sp * 64;             // token of staged row 0
+            const int trow = min(rbase + rl, M - 1);
+            const int sp_ = trow - (trow / S) * S;
+            const float *ct = e.cos_t + (size_t)sp_ * (HD / 2);
+            const float *st = e.sin_t + (size_t)sp_ * (HD / 2);
+            floatx4 cpre[8], spre[8];    // cos/sin of this lane's 32 pairs, loaded before the barrier
             if (sect < 2) {
-                // one token row per lane pair (hd = 128: 64 values per lane,
-                // `part` = which half of the head) or per lane (hd = 64)
-                constexpr int PARTS = HD / 64;
-                const int rl = within / PARTS, part = within % PARTS;
-                const int row = rbase + rl;
-                float y[64];
-                const float *src = red + rl * kQkvStride + hl * HD + part * 64;
 #pragma unroll
-                for (int c = 0; c < 64; c += 4) {
-                    const floatx4 v = *(const floatx4 *)(src + c);
-                    y[c] = v[0]; y[c + 1] = v[1]; y[c + 2] = v[2]; y[c + 3] = v[3];
+                for (int m4 = 0; m4 < 8; ++m4) {
+                    cpre[m4] = *(const floatx4 *)(ct + pair0 + m4 * 4);
+                    spre[m4] = *(const floatx4 *)(st + pair0 + m4 * 4);
                 }
+            }
+            wait_vmcnt<63, 0>();   // this wave's LDS writes done; global loads stay in flight
+            barrier_only();
+
+            bf16x8 o[8];           // this lane's 64 bf16 results, 8 at a time
+            // column (within the head) of this lane's 8-value chunk q, q = 0..7
+            auto qcol = [&](int q) {
+                return e.rope_half ? (q < 4 ? pair0 + q * 8 : HD / 2 + pair0 + (q - 4) * 8) : part * 64 + q * 8;
+            };
+            if (sect < 2) {
+                // the row is read from LDS once per pass (mean, centred variance,
+                // output) instead of being held in registers
+                const float *src = red + rl * kQkvStride + hl * HD;
+                float mean = 0.f, rstd = 1.f;
                 if (e.qk_norm) {
-                    const float *g = (sect == 0 ? e.q_g : e.k_g) + part * 64;
-                    const float *bb = (sect == 0 ? e.q_b : e.k_b) + part * 64;
                     float sum = 0.f;
 #pragma unroll
-                    for (int c = 0; c < 64; ++c) sum += y[c];
+                    for (int q = 0; q < 8; ++q) {
+                        const floatx4 v0 = *(const floatx4 *)(src + qcol(q)), v1 = *(const floatx4 *)(src + qcol(q) + 4);
+                        sum += ((v0[0] + v0[1]) + (v0[2] + v0[3])) + ((v1[0] + v1[1]) + (v1[2] + v1[3]));
+                    }
                     if (PARTS == 2) sum += __shfl_xor(sum, 1, 64);
-                    const float mean = sum * (1.0f / HD);
+                    mean = sum * (1.0f / HD);
                     float ss = 0.f;
 #pragma unroll
-                    for (int c = 0; c < 64; ++c) { y[c] -= mean; ss += y[c] * y[c]; }
-                    if (PARTS == 2) ss += __shfl_xor(ss, 1, 64);
-                    const float rstd = rsqrtf(ss * (1.0f / HD) + e.eps);
+                    for (int q = 0; q < 8; ++q) {
+                        const floatx4 v0 = *(const floatx4 *)(src + qcol(q)), v1 = *(const floatx4 *)(src + qcol(q) + 4);
 #pragma unroll
-                    for (int c = 0; c < 64; c += 4) {
-                        const floatx4 g4 = *(const floatx4 *)(g + c), b4 = *(const floatx4 *)(bb + c);
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) y[c + u] = y[c + u] * rstd * g4[u] + b4[u];
+                        for (int u = 0; u < 4; ++u) ss += (v0[u] - mean) * (v0[u] - mean) + (v1[u] - mean) * (v1[u] - mean);
                     }
+                    if (PARTS == 2) ss += __shfl_xor(ss, 1, 64);
+                    rstd = rsqrtf(ss * (1.0f / HD) + e.eps);
                 }
-                const int trow = min(row, M - 1);
-                const int bidx = trow / S, sp_ = trow - bidx * S;
-                const float *ct = e.cos_t + (size_t)sp_ * (HD / 2);
-                const float *st = e.sin_t + (size_t)sp_ * (HD / 2);
-                if (!e.rope_half) {
-                    // interleaved pairs (2m, 2m+1) lie inside this lane's 64 values
+                const float *g = gb + (sect == 0 ? 0 : 2 * HD);
+                const float *bb = g + HD;
+                // the 8 values of chunk q, normalised
+                auto chunk = [&](int q, float (&y)[8]) {
+                    const int c = qcol(q);
+                    const floatx4 v0 = *(const floatx4 *)(src + c), v1 = *(const floatx4 *)(src + c + 4);
 #pragma unroll
-                    for (int m4 = 0; m4 < 32; m4 += 4) {
-                        const floatx4 c4 = *(const floatx4 *)(ct + part * 32 + m4);
-                        const floatx4 s4 = *(const floatx4 *)(st + part * 32 + m4);
+                    for (int u = 0; u < 4; ++u) { y[u] = v0[u]; y[u + 4] = v1[u]; }
+                    if (e.qk_norm) {
+                        const floatx4 g0 = *(const floatx4 *)(g + c), g1 = *(const floatx4 *)(g + c + 4);
+                        const floatx4 b0 = *(const floatx4 *)(bb + c), b1 = *(const floatx4 *)(bb + c + 4);
 #pragma unroll
                         for (int u = 0; u < 4; ++u) {
-                            const int m = m4 + u;
-                            const float a = y[2 * m], bq = y[2 * m + 1];
-                            y[2 * m] = a * c4[u] - bq * s4[u];
-                            y[2 * m + 1] = a * s4[u] + bq * c4[u];
+                            y[u] = (y[u] - mean) * rstd * g0[u] + b0[u];
+                            y[u + 4] = (y[u + 4] - mean) * rstd * g1[u] + b1[u];
                         }
                     }
-                } else if (PARTS == 1) {
-                    // rotate-half, hd = 64: pairs (m, m + 32) inside the lane
+                };
+                if (!e.rope_half) {
+                    // interleaved: chunk q holds pairs 4q .. 4q + 3 of this lane
 #pragma unroll
-                    for (int m4 = 0; m4 < 32; m4 += 4) {
-                        const floatx4 c4 = *(const floatx4 *)(ct + m4), s4 = *(const floatx4 *)(st + m4);
+                    for (int q = 0; q < 8; ++q) {
+                        float y[8];
+                        chunk(q, y);
 #pragma unroll
                         for (int u = 0; u < 4; ++u) {
-                            const int m = m4 + u;
-                            const float a = y[m], bq = y[m + 32];
-                            y[m] = a * c4[u] - bq * s4[u];
-                            y[m + 32] = a * s4[u] + bq * c4[u];
+                            const int m = q * 4 + u;
+                            const float cs = cpre[m >> 2][m & 3], sn = spre[m >> 2][m & 3];
+                            o[q][2 * u] = f2bf(y[2 * u] * cs - y[2 * u + 1] * sn);
+                            o[q][2 * u + 1] = f2bf(y[2 * u] * sn + y[2 * u + 1] * cs);
                         }
                     }
                 } else {
-                    // rotate-half, hd = 128: pair (m, m + 64) spans the lane pair
+                    // rotate-half: chunk q (first half) pairs with chunk q + 4
 #pragma unroll
-                    for (int m4 = 0; m4 < 64; m4 += 4) {
-                        const floatx4 c4 = *(const floatx4 *)(ct + m4), s4 = *(const floatx4 *)(st + m4);
+                    for (int q = 0; q < 4; ++q) {
+                        float ya[8], yb[8];
+                        chunk(q, ya);
+                        chunk(q + 4, yb);
 #pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            const int m = m4 + u;
-                            const float other = __shfl_xor(y[m], 1, 64);
-                            y[m] = part == 0 ? y[m] * c4[u] - other * s4[u] : other * s4[u] + y[m] * c4[u];
+                        for (int u = 0; u < 8; ++u) {
+                            const int m = q * 8 + u;
+                            const float cs = cpre[m >> 2][m & 3], sn = spre[m >> 2][m & 3];
+                            o[q][u] = f2bf(ya[u] * cs - yb[u] * sn);
+                            o[q + 4][u] = f2bf(ya[u] * sn + yb[u] * cs);
                         }
-                    }
-                }
-                if (row < M) {
-                    bf16 *dst = (sect == 0 ? e.q : e.k) +
-                                (((size_t)bidx * (sect == 0 ? e.heads : e.kv_heads) + head) * S + sp_) * HD +
-                                part * 64;
-#pragma unroll
-                    for (int c = 0; c < 64; c += 8) {
-                        bf16x8 v;
-#pragma unroll
-                        for (int u = 0; u < 8; ++u) v[u] = f2bf(y[c + u]);
-                        *(bf16x8 *)(dst + c) = v;
                     }
                 }
             } else {
                 // v: head-dim column `within` over the 64 staged tokens
-                const int d = within;
-                const float *src = red + hl * HD + d;
-                const int b0 = min(rbase, M - 1) / S;
-                const int s0 = rbase - b0 * S;
-                const bool fast = (rbase + 63 < M) && (s0 + 63 < S) && ((s0 & 7) == 0);
-                if (fast) {
-                    bf16 *dst = e.vt + (((size_t)b0 * e.kv_heads + head) * HD + d) * e.seq_pad + s0;
+                const float *src = red + hl * HD + within;
 #pragma unroll
-                    for (int r8 = 0; r8 < 64; r8 += 8) {
-                        bf16x8 v;
+                for (int r8 = 0; r8 < 8; ++r8)
 #pragma unroll
-                        for (int u = 0; u < 8; ++u) v[u] = f2bf(src[(r8 + u) * kQkvStride]);
-                        *(bf16x8 *)(dst + r8) = v;
+                    for (int u = 0; u < 8; ++u) o[r8][u] = f2bf(src[(r8 * 8 + u) * kQkvStride]);
+            }
+
+            // 3. results into LDS in output order (after every lane's fp32 reads)
+            wait_vmcnt<63, 0>();
+            barrier_only();
+            if (sect < 2) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) *(bf16x8 *)(ob + hl * kHeadBlock + qk_slot(rl, qcol(q) >> 3)) = o[q];
+            } else {
+#pragma unroll
+                for (int r8 = 0; r8 < 8; ++r8) *(bf16x8 *)(ob + hl * kHeadBlock + v_slot(within, r8)) = o[r8];
+            }
+            wait_vmcnt<63, 0>();
+            barrier_only();
+
+            // copy-out: 16-byte piece pc of the cluster's (256 / HD) head blocks;
+            // one wave's 64 pieces always lie in one head block
+            const int b0 = min(rbase, M - 1) / S, s0 = min(rbase, M - 1) - b0 * S;
+            const bool v_fast = (rbase + 63 < M) && (s0 + 63 < S) && ((s0 & 7) == 0);
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                const int pc = it * 256 + lc;
+                const int hs = pc / (kHeadBlock / 16), pw = pc - hs * (kHeadBlock / 16);
+                int psect, phead;
+                head_of(hs, psect, phead);
+                if (psect < 2) {
+                    const int r = pw / kRowChunks, c = pw - r * kRowChunks;
+                    const int row = rbase + r;
+                    if (row < M) {
+                        const int bi = row / S, si = row - bi * S;
+                        bf16 *dst = (psect == 0 ? e.q : e.k) +
+                                    (((size_t)bi * (psect == 0 ? e.heads : e.kv_heads) + phead) * S + si) * HD + c * 8;
+                        *(bf16x8 *)dst = *(const bf16x8 *)(ob + hs * kHeadBlock + qk_slot(r, c));
                     }
                 } else {
-                    for (int r = 0; r < 64; ++r) {
-                        const int row = rbase + r;
-                        if (row >= M) break;
-                        const int bidx = row / S, sp_ = row - bidx * S;
-                        e.vt[(((size_t)bidx * e.kv_heads + head) * HD + d) * e.seq_pad + sp_] =
-                            f2bf(src[r * kQkvStride]);
+                    const int d = pw >> 3, c = pw & 7;
+                    const bf16x8 v = *(const bf16x8 *)(ob + hs * kHeadBlock + v_slot(d, c));
+                    if (v_fast) {
+                        *(bf16x8 *)(e.vt + (((size_t)b0 * e.kv_heads + phead) * HD + d) * e.seq_pad + s0 + c * 8) = v;
+                    } else {
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) {
+                            const int row = rbase + c * 8 + u;
+                            if (row < M) {
+                                const int bi = row / S, si = row - bi * S;
+                                e.vt[(((size_t)bi * e.kv_heads + phead) * HD + d) * e.seq_pad + si] = v[u];
+                            }
+                        }
                     }
                 }
             }
