@@ -101,7 +101,9 @@ void gemm_kernel(const bf16 *__restrict__ A, const bf16 *__restrict__ W, int M, 
     const int m0 = tm * T::BM;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    // wave index as a scalar: the LDS destinations of the buffer->LDS loads (M0)
+    // are then computed on the scalar unit
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / T::WN, wn = wave % T::WN;
     const int lrow = lane & 31, lhalf = lane >> 5;
 
@@ -148,55 +150,82 @@ void gemm_kernel(const bf16 *__restrict__ A, const bf16 *__restrict__ W, int M, 
     // end re-load the last tile (never read) so that every iteration issues the
     // same number of loads and the vmcnt bookkeeping stays uniform.
     const int KT = K / T::BK;
+    constexpr int KS = T::BK / 16;   // MFMA k-steps per stage (even: k-step 0 always uses buffer 0)
+    static_assert(KS % 2 == 0, "fragment double buffer");
 #pragma unroll
-    for (int s0 = 0; s0 < T::NS - 1; ++s0) DIT_ISSUE(s0, min(s0, KT - 1) * T::BK);
+    for (int s0 = 0; s0 < T::NS; ++s0) DIT_ISSUE(s0, min(s0, KT - 1) * T::BK);
 
     bf16x8 af[2][T::TM], bfr[2][T::TN];
+    // fragment reads in the order the MFMAs consume them: A0, B0 .. B(TN-1), A1 .. A(TM-1)
 #define DIT_LOAD_FRAGS(buf, sa_, sb_, kk)                                                           \
     do {                                                                                          \
         const int c_ = (kk) * 2 + lhalf;                                                          \
-        _Pragma("unroll") for (int i = 0; i < T::TM; ++i)                                        \
-            af[buf][i] = *(const bf16x8 *)((sa_) + T::off(wm * T::kWaveM + i * 32 + lrow, c_));   \
+        af[buf][0] = *(const bf16x8 *)((sa_) + T::off(wm * T::kWaveM + lrow, c_));                \
         _Pragma("unroll") for (int j = 0; j < T::TN; ++j)                                        \
             bfr[buf][j] = *(const bf16x8 *)((sb_) + T::off(wn * T::kWaveN + j * 32 + lrow, c_));  \
+        _Pragma("unroll") for (int i = 1; i < T::TM; ++i)                                        \
+            af[buf][i] = *(const bf16x8 *)((sa_) + T::off(wm * T::kWaveM + i * 32 + lrow, c_));   \
+    } while (0)
+#define DIT_MFMAS(buf)                                                                             \
+    do {                                                                                          \
+        _Pragma("unroll") for (int i = 0; i < T::TM; ++i)                                        \
+            _Pragma("unroll") for (int j = 0; j < T::TN; ++j)                                    \
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bfr[buf][j], acc[i][j], 0, 0, 0); \
     } while (0)
 
+    wait_vmcnt<(T::NS - 1) * T::kLoads>();   // tile 0 landed
+    barrier_only();
+    DIT_LOAD_FRAGS(0, smem, smem + T::BM * T::kRowBytes, 0);
+
+    // The workgroup barrier sits inside the MFMA stream: the last k-step's
+    // MFMAs run after it, from fragments already in registers, and cover the
+    // barrier, the loads of a later tile and the first fragment reads of the
+    // next stage, so the matrix pipe does not drain at every K tile.
     for (int kt = 0; kt < KT; ++kt) {
-        // tile kt has landed once at most NS-2 later stages are still in flight;
-        // the barrier extends that to every wave and also certifies that all
-        // waves are done with the stage consumed in the previous iteration
-        wait_vmcnt<(T::NS - 2) * T::kLoads, 0>();
-        barrier_only();
-        DIT_ISSUE((kt + T::NS - 1) % T::NS, min(kt + T::NS - 1, KT - 1) * T::BK);
         const uint8_t *sa = smem + (kt % T::NS) * T::kStageBytes;
         const uint8_t *sb = sa + T::BM * T::kRowBytes;
-        DIT_LOAD_FRAGS(0, sa, sb, 0);
 #pragma unroll
-        for (int kk = 0; kk < T::BK / 16; ++kk) {
-            // fetch k-step kk+1 while the MFMAs of k-step kk run
-            if (kk + 1 < T::BK / 16) DIT_LOAD_FRAGS((kk + 1) & 1, sa, sb, kk + 1);
-#pragma unroll
-            for (int i = 0; i < T::TM; ++i)
-#pragma unroll
-                for (int j = 0; j < T::TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][i], bfr[kk & 1][j], acc[i][j],
-                                                                        0, 0, 0);
+        for (int kk = 0; kk < KS - 1; ++kk) {
+            DIT_LOAD_FRAGS((kk + 1) & 1, sa, sb, kk + 1);   // fetch k-step kk+1 while kk runs
+            DIT_MFMAS(kk & 1);
         }
-        // instruction order hint: the buffer->LDS loads first, the fragment reads
-        // of k-step 0, then each later k-step's reads spread between the MFMAs of
-        // the k-step before it
-        __builtin_amdgcn_sched_group_barrier(0x020, T::kLoads, 0);          // VMEM
-        __builtin_amdgcn_sched_group_barrier(0x100, T::TM + T::TN, 0);      // DS read
+        // the next k-step's reads go out early in each k-step (two per MFMA), so
+        // they land long before the MFMAs that need them
 #pragma unroll
-        for (int kk = 0; kk < T::BK / 16 - 1; ++kk) {
+        for (int kk = 0; kk < KS - 1; ++kk) {
 #pragma unroll
-            for (int r = 0; r < T::TM + T::TN; ++r) {
-                __builtin_amdgcn_sched_group_barrier(0x008, (T::TM * T::TN) / (T::TM + T::TN), 0);   // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                   // DS read
+            for (int r = 0; r < (T::TM + T::TN + 1) / 2; ++r) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
             }
+            __builtin_amdgcn_sched_group_barrier(0x008, T::TM * T::TN - (T::TM + T::TN + 1) / 2, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, T::TM * T::TN, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        // tile kt+1 has landed once at most NS-2 later tiles are in flight, and this
+        // wave's reads of stage kt are done; after the barrier that holds for every
+        // wave, so stage kt may be refilled with tile kt + NS
+        wait_vmcnt<(T::NS - 2) * T::kLoads, 0>();
+        barrier_only();
+        {
+            // next stage's first fragments (before the loads: LDS reads are not
+            // reordered across the LDS-writing loads)
+            const uint8_t *na = smem + ((kt + 1) % T::NS) * T::kStageBytes;
+            DIT_LOAD_FRAGS(0, na, na + T::BM * T::kRowBytes, 0);
+        }
+        DIT_ISSUE(kt % T::NS, min(kt + T::NS, KT - 1) * T::BK);
+        DIT_MFMAS((KS - 1) & 1);
+        // after the barrier: fragment reads, then the tile loads spread between
+        // the MFMAs of the last k-step
+        constexpr int kPer = (T::kLoads + T::TM * T::TN - 1) / (T::TM * T::TN);
+        __builtin_amdgcn_sched_group_barrier(0x100, T::TM + T::TN, 0);       // DS read
+#pragma unroll
+        for (int r = 0; r < T::TM * T::TN; ++r) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x020, kPer, 0);            // VMEM
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
+#undef DIT_MFMAS
 #undef DIT_LOAD_FRAGS
 #undef DIT_ISSUE
     wait_vmcnt<0>();      // retire the trailing (never read) loads before LDS is reused
