@@ -95,6 +95,8 @@ def time_kernels(cfg, stack, reps=20):
     att = torch.empty((Nt, H * hd), dtype=bf, device=dev)
     x1 = torch.empty((Nt, D), device=dev)
     u = torch.empty((Nt, F), dtype=bf, device=dev)
+    lat = torch.randn((Nt, cfg.latent_dim), generator=g, device=dev)
+    vel = torch.randn((Nt, cfg.latent_dim), generator=g, device=dev)
     cos, sin = R.rope_tables(cfg)
     launches = {
         "adaln_gemv": (lambda: N.dit_adaln_modulation(blk["w_ada"], blk["b_ada"], c, 6 * D, Dc, 1, m),
@@ -109,6 +111,9 @@ def time_kernels(cfg, stack, reps=20):
         "gemm_swiglu": (lambda: N.dit_gemm_swiglu(h, blk["w_gate_up"], Nt, F, D, u), "mfma", None),
         "gemm_down": (lambda: N.dit_gemm_gated_residual(u, blk["w_down"], Nt, D, F, x1, N.DIT_F32, m[5 * D:], None,
                                                         x, N.DIT_F32), "mfma", None),
+        # latent and velocity read, latent written (fp32)
+        "euler_update": (lambda: N.euler_flowmatch_update(lat, vel, lat.numel(), 1.0, 0.999), "hbm",
+                         3 * lat.numel() * 4),
     }
     fl = block_flops(cfg)
     out = {}
@@ -132,6 +137,43 @@ def time_kernels(cfg, stack, reps=20):
             out[name] = {"us": round(us, 2), "bound": "hbm", "achieved": round(gbs, 1), "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "work": nbytes}
     return out
+
+
+def canary_tflops(reps=10):
+    """bf16 4096^3 torch.matmul (a vendor library, only a clock / contention
+    canary around the timed region, never part of the measured path)."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(11)
+    a = torch.randn((4096, 4096), generator=g, device="cuda").to(torch.bfloat16)
+    b = (torch.randn((4096, 4096), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    for _ in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    return round(2 * 4096 ** 3 / (e0.elapsed_time(e1) * 1e-3 / reps) / 1e12, 1)
+
+
+def host_info():
+    model = "unknown"
+    try:
+        for l in open("/proc/cpuinfo"):
+            if l.startswith("model name"):
+                model = l.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [f"{p.get('internal_api')} {p.get('version')}" for p in threadpool_info() if p.get("user_api") == "blas"]
+    except Exception:
+        pass
+    return {"cpu": model, "nproc": os.cpu_count(), "blas": blas}
 
 
 def measured_traffic():
@@ -182,6 +224,7 @@ def cpu_baseline(cfg=I.C4):
     edge_s = (t_embed - t0) + (t1 - t_blocks)
     step_s = block_s * cfg.layers + edge_s
     return {"value": round(step_s, 2), "unit": "s/denoise-step", "cores": int(threads), "kind": "oracle",
+            "host": host_info(),
             "sample": f"1 of {cfg.layers} blocks (4096 tok, hidden 4096, float64 NumPy; median of 3 runs "
                       f"{block_s:.2f} s) x {cfg.layers} + patch-embed + final layer + Euler ({edge_s:.2f} s); "
                       f"{t1 - t0:.1f} s of CPU work"}
@@ -234,6 +277,7 @@ def main():
         stack.step(lat, cond, cos, sin, vel)
         N.euler_flowmatch_update(lat, vel, lat.numel(), float(sig[j]), float(sig[j + 1]))
 
+    canary_before = canary_tflops()
     for i in range(args.warmup):
         one_step(i)
     torch.cuda.synchronize()
@@ -249,6 +293,7 @@ def main():
     per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
     ms = wall * 1000.0 / args.steps
     assert torch.isfinite(lat).all().item(), "non-finite latent"
+    canary_after = canary_tflops()
 
     flops = step_flops(cfg)
     util = flops / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
@@ -274,6 +319,10 @@ def main():
                            "max": round(max(per), 3)},
         "roofline": roof,
         "kernels": kern,
+        # hipBLASLt bf16 4096^3 before / after the timed steps: a drift of more than 7 %
+        # marks a clock or contention change during the run
+        "canary_tflops": {"before": canary_before, "after": canary_after,
+                          "drift_ok": abs(canary_after - canary_before) <= 0.07 * canary_before},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
