@@ -293,6 +293,24 @@ def main():
     per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
     ms = wall * 1000.0 / args.steps
     assert torch.isfinite(lat).all().item(), "non-finite latent"
+
+    # the same steps replayed from the library's per-step HIP graphs (dit_loop_*)
+    loop = R.DeviceLoop(stack, lat, cos, sin, I.STACK_STEPS, I.STACK_SHIFT)
+    for i in range(args.warmup):
+        loop.step(i % I.STACK_STEPS)
+    torch.cuda.synchronize()
+    gev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    gev[0].record()
+    for i in range(args.steps):
+        loop.step((args.warmup + i) % I.STACK_STEPS)
+        gev[i + 1].record()
+    torch.cuda.synchronize()
+    gwall = time.perf_counter() - t0
+    gper = [gev[i].elapsed_time(gev[i + 1]) for i in range(args.steps)]
+    gms = gwall * 1000.0 / args.steps
+    assert torch.isfinite(lat).all().item(), "non-finite latent (graph replay)"
+    loop.close()
     canary_after = canary_tflops()
 
     flops = step_flops(cfg)
@@ -317,6 +335,10 @@ def main():
         "step_tflop": round(flops / 1e12, 3),
         "step_ms_events": {"median": round(float(np.median(per)), 3), "min": round(min(per), 3),
                            "max": round(max(per), 3)},
+        # the loop executor: each step replayed as one HIP graph (timestep embedding + 36 blocks + Euler)
+        "graph_ms_per_step": round(gms, 3),
+        "graph_step_ms_events": {"median": round(float(np.median(gper)), 3), "min": round(min(gper), 3),
+                                 "max": round(max(gper), 3)},
         "roofline": roof,
         "kernels": kern,
         # hipBLASLt bf16 4096^3 before / after the timed steps: a drift of more than 7 %

@@ -9,6 +9,7 @@
 
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "common.h"
 
@@ -491,6 +492,117 @@ int dit_gemm_swiglu(const void *a, const void *w_gate_up, int64_t M, int32_t F, 
     if (!aligned16(a) || !aligned16(w_gate_up) || !aligned16(u)) return fail(DIT_ERR_ALIGNMENT, "16-byte alignment required");
     DIT_TRY(device_check());
     DIT_TRY_HIP(launch_gemm_swiglu((const bf16 *)a, (const bf16 *)w_gate_up, M, F, K, (bf16 *)u, as_stream(stream)));
+    return ok();
+}
+
+
+// ---------------------------------------------------------------------------
+// whole denoising loop as HIP graphs
+// ---------------------------------------------------------------------------
+struct dit_loop {
+    std::vector<hipGraphExec_t> steps;
+};
+
+namespace {
+struct LoopWs {
+    size_t stack, cond, vel, total;
+};
+LoopWs loop_ws(const dit_model &M) {
+    LoopWs L;
+    L.stack = 0;
+    L.cond = align256(stack_ws(M).total);
+    L.vel = L.cond + align256((size_t)M.blk.cond_dim * 4);
+    L.total = L.vel + align256((size_t)M.blk.batch * M.blk.seq * M.latent_dim * 4);
+    return L;
+}
+void free_loop(dit_loop *lp) {
+    for (hipGraphExec_t e : lp->steps)
+        if (e) (void)hipGraphExecDestroy(e);
+    delete lp;
+}
+}  // namespace
+
+int dit_loop_workspace_size(const dit_model *model, size_t *bytes) {
+    DIT_TRY(check_model(model));
+    if (!bytes) return fail(DIT_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = loop_ws(*model).total;
+    return ok();
+}
+
+int dit_loop_create(const dit_model *model, float *latent, const float *rope_cos, const float *rope_sin,
+                    int32_t steps, float shift, void *ws, size_t ws_bytes, dit_loop **loop) {
+    if (!loop) return fail(DIT_ERR_INVALID_ARG, "loop is NULL");
+    *loop = nullptr;
+    DIT_TRY(check_model(model));
+    const dit_model &M = *model;
+    if (!latent || !rope_cos || !rope_sin || !ws) return fail(DIT_ERR_INVALID_ARG, "latent, rope tables and ws are required");
+    if (steps < 1 || steps > 1000) return fail(DIT_ERR_INVALID_ARG, "steps must be in [1, 1000]");
+    if (!(shift > 0.f) || !isfinite(shift)) return fail(DIT_ERR_INVALID_ARG, "shift must be positive");
+    if (!aligned16(latent) || !aligned16(ws)) return fail(DIT_ERR_ALIGNMENT, "latent and ws must be 16-byte aligned");
+    const LoopWs L = loop_ws(M);
+    if (ws_bytes < L.total) return fail(DIT_ERR_WORKSPACE, "workspace %zu < required %zu bytes", ws_bytes, L.total);
+    const int64_t n = (int64_t)M.blk.batch * M.blk.seq * M.latent_dim;
+    if (overlaps(ws, L.total, latent, (size_t)n * 4)) return fail(DIT_ERR_INVALID_ARG, "workspace overlaps latent");
+    DIT_TRY(device_check());
+    std::vector<float> sig(steps + 1);
+    DIT_TRY(dit_flowmatch_sigmas(steps, shift, sig.data()));
+    uint8_t *wsb = (uint8_t *)ws;
+    float *cond = (float *)(wsb + L.cond), *vel = (float *)(wsb + L.vel);
+
+    // private capture stream (default priority); nothing is launched while capturing
+    hipStream_t cs;
+    DIT_TRY_HIP(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
+    dit_loop *lp = new dit_loop();
+    lp->steps.assign(steps, nullptr);
+    int rc = DIT_OK;
+    for (int i = 0; i < steps && rc == DIT_OK; ++i) {
+        hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+        if (e != hipSuccess) {
+            rc = fail(DIT_ERR_HIP, "hipStreamBeginCapture: %s", hipGetErrorString(e));
+            break;
+        }
+        rc = dit_timestep_embedding(1000.0f * sig[i], M.blk.cond_dim, cond, cs);
+        if (rc == DIT_OK) rc = dit_stack_step(model, latent, cond, rope_cos, rope_sin, vel, wsb + L.stack, L.cond, cs);
+        if (rc == DIT_OK) rc = euler_flowmatch_update(latent, vel, n, sig[i], sig[i + 1], cs);
+        const std::string err = g_err;              // keep the first error across the clean-up calls
+        hipGraph_t g = nullptr;
+        e = hipStreamEndCapture(cs, &g);
+        if (rc == DIT_OK && e != hipSuccess) rc = fail(DIT_ERR_HIP, "hipStreamEndCapture: %s", hipGetErrorString(e));
+        if (rc == DIT_OK) {
+            e = hipGraphInstantiate(&lp->steps[i], g, nullptr, nullptr, 0);
+            if (e != hipSuccess) rc = fail(DIT_ERR_HIP, "hipGraphInstantiate: %s", hipGetErrorString(e));
+        } else {
+            g_err = err;
+        }
+        if (g) (void)hipGraphDestroy(g);
+    }
+    (void)hipStreamDestroy(cs);
+    if (rc != DIT_OK) {
+        const std::string err = g_err;
+        free_loop(lp);
+        g_err = err;
+        return rc;
+    }
+    *loop = lp;
+    return ok();
+}
+
+int dit_loop_launch_step(dit_loop *loop, int32_t step, void *stream) {
+    if (!loop) return fail(DIT_ERR_INVALID_ARG, "loop is NULL");
+    if (step < 0 || step >= (int32_t)loop->steps.size())
+        return fail(DIT_ERR_INVALID_ARG, "step %d outside [0, %zu)", step, loop->steps.size());
+    DIT_TRY_HIP(hipGraphLaunch(loop->steps[step], as_stream(stream)));
+    return ok();
+}
+
+int dit_loop_launch(dit_loop *loop, void *stream) {
+    if (!loop) return fail(DIT_ERR_INVALID_ARG, "loop is NULL");
+    for (size_t i = 0; i < loop->steps.size(); ++i) DIT_TRY_HIP(hipGraphLaunch(loop->steps[i], as_stream(stream)));
+    return ok();
+}
+
+int dit_loop_destroy(dit_loop *loop) {
+    if (loop) free_loop(loop);
     return ok();
 }
 

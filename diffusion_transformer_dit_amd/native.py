@@ -24,6 +24,7 @@ EXPORTED = (
     "euler_flowmatch_update", "dit_timestep_embedding", "dit_flowmatch_sigmas", "dit_rope_tables",
     "dit_adaln_modulation", "dit_ln_modulate", "dit_qkv_rope", "dit_seq_pad", "dit_flash_attention",
     "dit_gemm_gated_residual", "dit_gemm_swiglu", "dit_status_string", "dit_last_error", "dit_version",
+    "dit_loop_workspace_size", "dit_loop_create", "dit_loop_launch_step", "dit_loop_launch", "dit_loop_destroy",
 )
 
 
@@ -85,6 +86,11 @@ def lib():
             "dit_status_string": (C.c_char_p, [C.c_int]),
             "dit_last_error": (C.c_char_p, []),
             "dit_version": (C.c_char_p, []),
+            "dit_loop_workspace_size": (C.c_int, [pm, C.POINTER(sz)]),
+            "dit_loop_create": (C.c_int, [pm, vp, vp, vp, i32, f32, vp, sz, C.POINTER(vp)]),
+            "dit_loop_launch_step": (C.c_int, [vp, i32, vp]),
+            "dit_loop_launch": (C.c_int, [vp, vp]),
+            "dit_loop_destroy": (C.c_int, [vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -175,6 +181,33 @@ def dit_stack_step(model, latent, cond, rope_cos, rope_sin, velocity, ws, stream
     nb = _nbytes(ws) if ws_bytes is None else ws_bytes
     _check(lib().dit_stack_step(C.byref(model), _p(latent), _p(cond), _p(rope_cos), _p(rope_sin), _p(velocity),
                                 _p(ws), nb, _stream(stream)))
+
+
+def dit_loop_workspace_size(model: dit_model) -> int:
+    n = C.c_size_t(0)
+    _check(lib().dit_loop_workspace_size(C.byref(model), C.byref(n)))
+    return n.value
+
+
+def dit_loop_create(model, latent, rope_cos, rope_sin, steps, shift, ws, ws_bytes=None) -> int:
+    """Returns the loop handle (an opaque address)."""
+    h = C.c_void_p(None)
+    nb = _nbytes(ws) if ws_bytes is None else ws_bytes
+    _check(lib().dit_loop_create(C.byref(model), _p(latent), _p(rope_cos), _p(rope_sin), int(steps), float(shift),
+                                 _p(ws), nb, C.byref(h)))
+    return h.value
+
+
+def dit_loop_launch_step(loop, step, stream=None):
+    _check(lib().dit_loop_launch_step(loop, int(step), _stream(stream)))
+
+
+def dit_loop_launch(loop, stream=None):
+    _check(lib().dit_loop_launch(loop, _stream(stream)))
+
+
+def dit_loop_destroy(loop):
+    _check(lib().dit_loop_destroy(loop))
 
 
 def euler_flowmatch_update(latent, velocity, n, sigma, sigma_next, stream=None):

@@ -124,3 +124,37 @@ def denoise(stack: DeviceStack, latent, cos, sin, steps: int, shift: float, star
         stack.step(latent, cond, cos, sin, vel, stream)
         N.euler_flowmatch_update(latent, vel, latent.numel(), float(sig[i]), float(sig[i + 1]), stream)
     return latent
+
+
+class DeviceLoop:
+    """The whole flow-match loop recorded by the library as one HIP graph per
+    step (dit_loop_create); each replay updates `latent` in place.  The
+    latent, rope tables and the stack's weights must stay alive and in place
+    while the loop exists."""
+
+    def __init__(self, stack: DeviceStack, latent, cos, sin, steps: int, shift: float):
+        self.stack, self.latent, self.cos, self.sin = stack, latent, cos, sin
+        self.steps = steps
+        self.ws = alloc_ws(N.dit_loop_workspace_size(stack.model))
+        self.handle = N.dit_loop_create(stack.model, latent, cos, sin, steps, shift, self.ws)
+
+    def step(self, i: int, stream=None):
+        N.dit_loop_launch_step(self.handle, i, stream)
+
+    def run(self, start: int = 0, stream=None):
+        for i in range(start, self.steps):
+            self.step(i, stream)
+        return self.latent
+
+    def close(self):
+        if self.handle:
+            _torch().cuda.synchronize()
+            N.dit_loop_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+

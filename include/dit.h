@@ -179,6 +179,45 @@ int euler_flowmatch_update(float *latent, const float *velocity, int64_t n,
 int dit_timestep_embedding(float t, int32_t dim, float *cond_out, void *stream);
 
 /* ------------------------------------------------------------------------ */
+/* Whole denoising loop, recorded once as HIP graphs                         */
+/* ------------------------------------------------------------------------ */
+
+/* The flow-match Euler loop of [ERNIE] §I (8 steps, shift 4.0, sigma grid of
+ * dit_flowmatch_sigmas) with each step = dit_timestep_embedding(1000 sigma_i)
+ * -> dit_stack_step -> euler_flowmatch_update(sigma_i, sigma_{i+1}), recorded
+ * into one HIP graph per step so that replaying a step costs one launch
+ * instead of ~300 ([ZML] §XI: host round trips dominate small steps).
+ *
+ * Workspace: dit_loop_workspace_size bytes = the stack workspace followed by
+ * the conditioning vector [cond_dim] and the velocity [batch*seq, latent_dim]
+ * (fp32).  The loop keeps the pointers it was created with: model weights,
+ * rope tables, latent and ws must stay allocated and at the same addresses
+ * until dit_loop_destroy; the model struct itself may be freed after create.
+ * The latent (device fp32 [batch*seq, latent_dim]) is updated in place by
+ * every replayed step; refill it to start a new loop.
+ * The loop object owns host-side graph resources only (no device buffers). */
+typedef struct dit_loop dit_loop;
+
+int dit_loop_workspace_size(const dit_model *model, size_t *bytes);
+
+/* Validates like dit_stack_step, then records steps graphs on a private
+ * stream (nothing runs yet).  steps in [1, 1000], shift > 0.
+ * On success *loop receives the handle; on error *loop is left NULL. */
+int dit_loop_create(const dit_model *model, float *latent, const float *rope_cos,
+                    const float *rope_sin, int32_t steps, float shift, void *ws,
+                    size_t ws_bytes, dit_loop **loop);
+
+/* Replays step `step` (0-based, < steps) on `stream`, asynchronously. */
+int dit_loop_launch_step(dit_loop *loop, int32_t step, void *stream);
+
+/* Replays all steps in order on `stream`, asynchronously. */
+int dit_loop_launch(dit_loop *loop, void *stream);
+
+/* Frees the graphs.  NULL is accepted.  The caller must not destroy a loop
+ * whose replays are still running (synchronise the stream first). */
+int dit_loop_destroy(dit_loop *loop);
+
+/* ------------------------------------------------------------------------ */
 /* Host helpers (no device work)                                             */
 /* ------------------------------------------------------------------------ */
 

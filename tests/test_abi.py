@@ -163,6 +163,42 @@ def test_stack_validation():
     assert N.dit_stack_workspace_size(m) > N.dit_block_workspace_size(_desc(x_dtype=N.DIT_F32))
 
 
+def test_loop_validation_before_device():
+    """dit_loop_*: every argument is checked before any HIP call."""
+    e = dict(w_in=FAKE, b_in=FAKE, w_fmod=FAKE, b_fmod=FAKE, w_out=FAKE, b_out=FAKE)
+    m = N.make_model(_desc(x_dtype=N.DIT_F32), [_weights()] * 2, 128, e)
+    need = N.dit_loop_workspace_size(m)
+    assert need > N.dit_stack_workspace_size(m)
+    big = 1 << 40
+    cases = [
+        (dict(steps=0), N.DIT_ERR_INVALID_ARG),
+        (dict(steps=1001), N.DIT_ERR_INVALID_ARG),
+        (dict(shift=0.0), N.DIT_ERR_INVALID_ARG),
+        (dict(shift=float("nan")), N.DIT_ERR_INVALID_ARG),
+        (dict(latent=None), N.DIT_ERR_INVALID_ARG),
+        (dict(latent=FAKE + 4), N.DIT_ERR_ALIGNMENT),
+        (dict(ws_bytes=need - 1), N.DIT_ERR_WORKSPACE),
+        (dict(latent=big + 4096), N.DIT_ERR_INVALID_ARG),      # latent inside the workspace
+    ]
+    for kw, st in cases:
+        args = dict(latent=FAKE, steps=8, shift=4.0, ws_bytes=need)
+        args.update(kw)
+        with pytest.raises(N.DitError) as err:
+            N.dit_loop_create(m, args["latent"], FAKE, FAKE, args["steps"], args["shift"], big, ws_bytes=args["ws_bytes"])
+        assert err.value.status == st, (kw, err.value)
+    with pytest.raises(N.DitError) as err:
+        N.dit_loop_launch_step(None, 0, stream=0)
+    assert err.value.status == N.DIT_ERR_INVALID_ARG
+    with pytest.raises(N.DitError) as err:
+        N.dit_loop_launch(None, stream=0)
+    assert err.value.status == N.DIT_ERR_INVALID_ARG
+    N.dit_loop_destroy(None)                                      # NULL is accepted
+    if not (os.path.exists("/dev/kfd") and os.access("/dev/kfd", os.R_OK)):
+        with pytest.raises(N.DitError) as err:
+            N.dit_loop_create(m, FAKE, FAKE, FAKE, 8, 4.0, big, ws_bytes=need)
+        assert err.value.status == N.DIT_ERR_NO_DEVICE
+
+
 # ---------------------------------------------------------------------------
 # host helpers against the oracle
 # ---------------------------------------------------------------------------

@@ -93,6 +93,46 @@ def test_denoise_loop_vs_oracle_and_resume():
     np.testing.assert_array_equal(R.to_host_f32(resumed), got)
 
 
+def test_loop_graph_replays_match_eager_loop():
+    """dit_loop_*: the whole loop recorded as HIP graphs reproduces the eager
+    loop bit for bit, on every replay, with eager work and synchronisations
+    between the replays; single-step replays resume like the eager loop."""
+    import torch
+    cfg = STK
+    blocks, edges, stack = _small_stack()
+    pos = I.positions(cfg)
+    lat0 = I.latent(cfg)
+    cos, sin = R.rope_tables(cfg, pos)
+    steps = 4
+    eager = R.to_host_f32(R.denoise(stack, R.to_dev_f32(lat0), cos, sin, steps, 4.0))
+    lat = R.to_dev_f32(lat0)
+    loop = R.DeviceLoop(stack, lat, cos, sin, steps, 4.0)
+    try:
+        other = R.to_dev_f32(lat0)
+        for rep in range(3):
+            lat.copy_(R.to_dev_f32(lat0))
+            loop.run()
+            _sync()
+            got = R.to_host_f32(lat)
+            say(f"  replay {rep}: max |graph - eager| = {np.abs(got - eager).max():.3e}")
+            np.testing.assert_array_equal(got, eager)
+            R.denoise(stack, other, cos, sin, 1, 4.0)         # eager work between replays
+            _sync()
+        # steps 0-1 by graph, 2-3 eagerly: same as the uninterrupted loop
+        lat.copy_(R.to_dev_f32(lat0))
+        loop.step(0)
+        loop.step(1)
+        _sync()
+        resumed = R.denoise(stack, R.to_dev_f32(R.to_host_f32(lat)), cos, sin, steps, 4.0, start=2)
+        _sync()
+        np.testing.assert_array_equal(R.to_host_f32(resumed), eager)
+        with pytest.raises(N.DitError) as err:
+            loop.step(steps)
+        assert err.value.status == N.DIT_ERR_INVALID_ARG
+    finally:
+        loop.close()
+
+
 def test_full_stack_step_properties():
     """The 36-block, 4096-wide stack at 4096 tokens: one denoising step is
     finite and bitwise reproducible (weights drawn on the device)."""
