@@ -139,6 +139,36 @@ def time_kernels(cfg, stack, reps=20):
     return out
 
 
+def time_block(cfg, blk, reps=10):
+    """One block (dit_block_forward: AdaLN GEMV + the seven block kernels) at
+    cfg's shapes with the given device weights, HIP events on torch's current
+    stream; returns us per block and the algorithmic TFLOP/s."""
+    import torch
+    from diffusion_transformer_dit_amd import native as N
+    from diffusion_transformer_dit_amd import runtime as R
+    g = torch.Generator(device="cuda").manual_seed(13)
+    x = torch.randn((cfg.tokens, cfg.hidden), generator=g, device="cuda")
+    c = torch.randn((cfg.cond_dim,), generator=g, device="cuda")
+    cos, sin = R.rope_tables(cfg)
+    desc = R.desc_of(cfg)
+    out = torch.empty_like(x)
+    ws = R.alloc_ws(N.dit_block_workspace_size(desc))
+    for _ in range(2):
+        N.dit_block_forward(desc, blk.c, x, c, cos, sin, out, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        N.dit_block_forward(desc, blk.c, x, c, cos, sin, out, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item()
+    us = e0.elapsed_time(e1) * 1000.0 / reps
+    tf = sum(block_flops(cfg).values()) / (us * 1e-6) / 1e12
+    return {"tokens": cfg.seq, "us": round(us, 1), "achieved": round(tf, 1), "unit": "TFLOP/s",
+            "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
 def canary_tflops(reps=10):
     """bf16 4096^3 torch.matmul (a vendor library, only a clock / contention
     canary around the timed region, never part of the measured path)."""
@@ -265,6 +295,10 @@ def main():
     stack, cos, sin = build_full_stack(cfg)
     kern = time_kernels(cfg, stack)
     print(f"[bench] kernels: {json.dumps({k: v['us'] for k, v in kern.items()})}", file=sys.stderr, flush=True)
+    # one block of the stack on the 4096-token latent and on the joint 4096 + 74 text sequence
+    blocks = {"latent_4096": time_block(cfg, stack.blocks[0]),
+              "joint_4170": time_block(I.C3_JOINT.replace(x_dtype="f32"), stack.blocks[0])}
+    print(f"[bench] blocks: {json.dumps(blocks)}", file=sys.stderr, flush=True)
 
     lat = R.to_dev_f32(I.latent(cfg))
     cond = torch.empty(cfg.cond_dim, dtype=torch.float32, device="cuda")
@@ -341,6 +375,8 @@ def main():
                                  "max": round(max(gper), 3)},
         "roofline": roof,
         "kernels": kern,
+        # dit_block_forward at 4096 tokens and on the joint text + image sequence (4096 + 74 tokens)
+        "block": blocks,
         # hipBLASLt bf16 4096^3 before / after the timed steps: a drift of more than 7 %
         # marks a clock or contention change during the run
         "canary_tflops": {"before": canary_before, "after": canary_after,

@@ -57,12 +57,18 @@ class DiTConfig:
     layers: int = 1
     latent_dim: int = 0              # stack only: latent channels (patch-embed input)
     seq_override: int = 0            # ragged sequence: use the first `seq` grid positions
+    text_len: int = 0                # joint sequence: text tokens packed with the spatial ones
+    text_first: bool = False         # joint order: text rows before the spatial rows
 
     @property
-    def seq(self) -> int:
+    def spatial(self) -> int:
         if self.seq_override:
             return self.seq_override
         return self.grid[0] * self.grid[1] * self.grid[2]
+
+    @property
+    def seq(self) -> int:
+        return self.spatial + self.text_len
 
     @property
     def tokens(self) -> int:
@@ -87,8 +93,14 @@ C4 = C3.replace(name="stack_8b", cfg_id=4, x_dtype="f32", layers=36, latent_dim=
 C5_4096 = DiTConfig("gqa_wide_4096", 5, 1, (1, 64, 64), 6144, 48, 8, 128, 16384, 6144, True,
                     "interleaved3d", (32, 48, 48), 256.0, x_dtype="bf16", layers=28)
 C5_1024 = C5_4096.replace(name="gqa_wide_1024", grid=(1, 32, 32))
+# joint text + image sequences (ERNIE page, "Token Layout"): 4096 spatial + 74
+# text tokens = 4170, spatial rows first; the text-first order is the variant
+# the zml-flow-rs page (§IV semantics table) found for another model
+C3_JOINT = C3.replace(name="block_8b_joint", cfg_id=6, text_len=74)
+C1_JOINT = C1.replace(name="tiny_joint", cfg_id=7, text_len=7)
+C1_JOINT_TF = C1_JOINT.replace(name="tiny_joint_text_first", text_first=True)
 
-CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5_4096, C5_1024)}
+CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5_4096, C5_1024, C3_JOINT, C1_JOINT, C1_JOINT_TF)}
 
 STACK_STEPS = 8
 STACK_SHIFT = 4.0
@@ -127,11 +139,20 @@ def positions(cfg: DiTConfig) -> np.ndarray:
     Spatial token i of a frames x rows x cols grid sits at
     (i // (rows*cols), (i // cols) % rows, i % cols); the latent grid is
     walked row-major (ERNIE page, §VII Decision 3, spatial positions).
+    In a joint sequence (text_len > 0) the spatial tokens' t is offset by
+    text_len and text token j sits at (j, 0, 0) (ERNIE page, "Token Layout"
+    and §VII Decision 3); the spatial rows come first unless text_first.
     """
     f, hh, ww = cfg.grid
     i = np.arange(f * hh * ww, dtype=np.int64)
-    pos = np.stack([i // (hh * ww), (i // ww) % hh, i % ww], axis=1)
-    return pos[: cfg.seq].copy()
+    pos = np.stack([i // (hh * ww), (i // ww) % hh, i % ww], axis=1)[: cfg.spatial]
+    if cfg.text_len == 0:
+        return pos.copy()
+    pos = pos.copy()
+    pos[:, 0] += cfg.text_len
+    text = np.zeros((cfg.text_len, 3), np.int64)
+    text[:, 0] = np.arange(cfg.text_len)
+    return np.concatenate([text, pos] if cfg.text_first else [pos, text], axis=0)
 
 
 def block_weights(cfg: DiTConfig, block: int = 0, affine_random: bool = False,

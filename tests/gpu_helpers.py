@@ -47,4 +47,7 @@ SMALL = {
     "vit_b2_f32": I.DiTConfig("vit_b2_f32", 13, 2, (1, 16, 16), 512, 8, 8, 64, 1024, 0, False,
                               "half2d", (32, 32), 100.0, x_dtype="f32"),
     "c1_f32x_t3": I.C1.replace(name="c1_f32x_t3", cfg_id=14, x_dtype="f32", grid=(3, 8, 12)),
+    # joint text + image sequences: 256 spatial + 7 text tokens, both orders
+    "tiny_joint": I.C1_JOINT,
+    "tiny_joint_text_first": I.C1_JOINT_TF,
 }

@@ -97,6 +97,20 @@ def test_block_in_place_and_deterministic():
     np.testing.assert_array_equal(a, ip)
 
 
+def test_block_joint_text_first_is_a_row_permutation():
+    """On the GPU too, moving the text rows (with their positions) to the front
+    permutes the output rows (up to rounding: the row tiles differ)."""
+    cfg, cft = I.C1_JOINT, I.C1_JOINT_TF
+    w = I.block_weights(cfg, 0)
+    x, c = I.block_x(cfg), I.cond(cfg)
+    perm = np.r_[np.arange(cfg.spatial, cfg.seq), np.arange(cfg.spatial)]
+    a = _run_block(cfg, w, x, c, I.positions(cfg))
+    b = _run_block(cft, w, x[perm], c, I.positions(cft))
+    m = metrics(b - x[perm], a[perm] - x[perm])
+    say(f"  text-first vs permuted spatial-first: {m}")
+    assert m["cos"] > 0.9999
+
+
 def test_block_rope_position_offset_invariance():
     """Shifting every position by one constant leaves the output unchanged up
     to rounding (relative-position property of RoPE), on the GPU path too."""
@@ -119,7 +133,7 @@ def _sample_rows(n, seed=0, k=24):
     return np.unique(np.clip(np.r_[fixed, r], 0, n - 1))
 
 
-@pytest.mark.parametrize("cfg", [I.C3, I.C5_1024, I.C2], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [I.C3, I.C5_1024, I.C2, I.C3_JOINT], ids=lambda c: c.name)
 def test_block_full_size_sampled(cfg):
     say(f"full-size block {cfg.name}: N={cfg.tokens} D={cfg.hidden}")
     w = I.block_weights(cfg, 0)
@@ -127,5 +141,7 @@ def test_block_full_size_sampled(cfg):
     got = _run_block(cfg, w, x, c, pos)
     assert np.isfinite(got).all()
     rows = _sample_rows(cfg.tokens)
+    if cfg.text_len:
+        rows = np.unique(np.r_[rows, cfg.spatial - 1, cfg.spatial])   # last spatial, first text row
     ref = O.block_forward(x, c, w, cfg, pos, dtype=np.float32, rows=rows)
     _check(cfg, got[rows], ref, x[rows])

@@ -418,3 +418,55 @@ def test_workload_dims_match_ernie_page():
         assert c.seq == g["latent_tokens"] and list(c.grid[1:]) == g["latent_grid"]
     assert I.C4.layers == g["layers"] and I.C4.latent_dim == g["latent_channels"]
     assert I.STACK_STEPS == g["euler_steps"] and I.STACK_SHIFT == g["scheduler_shift"]
+
+
+# ---------------------------------------------------------------------------
+# joint text + image sequence (ERNIE page, "Token Layout" and §VII Decision 3)
+# ---------------------------------------------------------------------------
+def test_joint_positions_follow_the_token_layout():
+    g = json.load(open(os.path.join(GOLDEN, "ernie_dims.json")))
+    cfg = I.C3_JOINT
+    assert cfg.text_len == g["joint_text_tokens"] and cfg.seq == g["joint_tokens"]
+    assert g["joint_order"] == "spatial_first" and not cfg.text_first
+    pos = I.positions(cfg)
+    n_sp = g["latent_tokens"]
+    assert pos.shape == (g["joint_tokens"], 3)
+    sp, tx = pos[:n_sp], pos[n_sp:]
+    assert (sp[:, 0] == g["joint_text_tokens"]).all()                   # spatial t = text_len
+    hh, ww = g["latent_grid"]
+    np.testing.assert_array_equal(sp[:, 1], np.arange(n_sp) // ww)     # row-major h, w
+    np.testing.assert_array_equal(sp[:, 2], np.arange(n_sp) % ww)
+    np.testing.assert_array_equal(tx[:, 0], np.arange(g["joint_text_tokens"]))   # text (j, 0, 0)
+    assert (tx[:, 1:] == 0).all()
+    # text-first order: the same ids, text rows moved to the front
+    tf = I.positions(cfg.replace(text_first=True))
+    np.testing.assert_array_equal(tf, np.concatenate([tx, sp]))
+
+
+def test_joint_text_tokens_rotate_only_along_t():
+    """Text tokens sit at h = w = 0: their rotation on the h and w chunks of
+    the head dim is the identity, and on the t chunk it is position j."""
+    cfg = I.C1_JOINT
+    pos = I.positions(cfg)
+    ang = O.rope_angles(pos, cfg)
+    t_pairs = cfg.rope_axes[0] // 2
+    text = ang[cfg.spatial:]
+    assert np.all(text[:, t_pairs:] == 0.0)
+    j = np.arange(cfg.text_len, dtype=np.float64)
+    np.testing.assert_allclose(text[:, 0], j)                             # pair 0 of t: angle = position
+    assert np.all(ang[: cfg.spatial, 0] == cfg.text_len)                  # spatial t offset by text_len
+
+
+def test_joint_text_first_is_a_row_permutation():
+    """Moving the text rows to the front (with their positions) permutes the
+    block's output rows and changes nothing else."""
+    cfg = I.C1_JOINT
+    cft = I.C1_JOINT_TF
+    w, c = I.block_weights(cfg), I.cond(cfg)
+    x = I.block_x(cfg)
+    n = cfg.spatial
+    perm = np.r_[np.arange(n, cfg.seq), np.arange(n)]      # text-first row order
+    a = O.block_forward(x, c, w, cfg, I.positions(cfg))
+    b = O.block_forward(x[perm], c, w, cft, I.positions(cft))
+    np.testing.assert_allclose(b, a[perm], rtol=1e-10, atol=1e-12)
+
