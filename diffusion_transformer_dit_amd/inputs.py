@@ -59,6 +59,12 @@ class DiTConfig:
     seq_override: int = 0            # ragged sequence: use the first `seq` grid positions
     text_len: int = 0                # joint sequence: text tokens packed with the spatial ones
     text_first: bool = False         # joint order: text rows before the spatial rows
+    # semantics switches the pages disagree on (defaults = the readings of the main path)
+    norm: str = "layernorm"          # "layernorm" | "rmsnorm" (block norms and qk-norm)
+    act: str = "silu"                # FFN GLU activation: "silu" | "gelu_tanh" (clamped)
+    gate: str = "identity"           # gate function: "identity" | "tanh" | "sigmoid"
+    mod: str = "shift_scale_gate"    # AdaLN chunks: "shift_scale_gate" (6D) | "scale_gate" (4D, no shift)
+    qk_order: str = "norm_rope"      # "norm_rope" | "rope_norm"
 
     @property
     def spatial(self) -> int:
@@ -69,6 +75,11 @@ class DiTConfig:
     @property
     def seq(self) -> int:
         return self.spatial + self.text_len
+
+    @property
+    def ada_rows(self) -> int:
+        """Rows of the AdaLN linear: 6 or 4 chunks of hidden."""
+        return (4 if self.mod == "scale_gate" else 6) * self.hidden
 
     @property
     def tokens(self) -> int:
@@ -168,8 +179,8 @@ def block_weights(cfg: DiTConfig, block: int = 0, affine_random: bool = False,
     w: Dict[str, Optional[np.ndarray]] = {}
     if Dc > 0:
         if draw_ada:
-            w["w_ada"] = _normal(cid, block, "w_ada", (6 * D, Dc), 0.02)
-            w["b_ada"] = _normal(cid, block, "b_ada", (6 * D,), 0.02)
+            w["w_ada"] = _normal(cid, block, "w_ada", (cfg.ada_rows, Dc), 0.02)
+            w["b_ada"] = _normal(cid, block, "b_ada", (cfg.ada_rows,), 0.02)
         else:
             w["w_ada"] = w["b_ada"] = None
         if zero_ada and draw_ada:
@@ -242,8 +253,8 @@ def stack_block_weights(cfg: DiTConfig, block: int, shared_ada: Dict[str, np.nda
 
 def shared_ada(cfg: DiTConfig) -> Dict[str, np.ndarray]:
     D, Dc, cid = cfg.hidden, cfg.cond_dim, cfg.cfg_id
-    return {"w_ada": _normal(cid, 999, "w_ada", (6 * D, Dc), 0.02),
-            "b_ada": _normal(cid, 999, "b_ada", (6 * D,), 0.02)}
+    return {"w_ada": _normal(cid, 999, "w_ada", (cfg.ada_rows, Dc), 0.02),
+            "b_ada": _normal(cid, 999, "b_ada", (cfg.ada_rows,), 0.02)}
 
 
 # ---------------------------------------------------------------------------

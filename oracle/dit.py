@@ -25,7 +25,10 @@ shift*s/(1+(shift-1)s); final layer chunks (scale, shift) with no SiLU.
 
 `spec` arguments are any object with the attributes: batch, seq, heads,
 kv_heads, head_dim, cond_dim, qk_norm, rope ("interleaved3d" | "half2d"),
-rope_axes, rope_theta, eps.
+rope_axes, rope_theta, eps, and optionally the semantics switches the pages
+disagree on (defaults in brackets): norm ["layernorm"] | "rmsnorm"; act
+["silu"] | "gelu_tanh"; gate ["identity"] | "tanh" | "sigmoid"; mod
+["shift_scale_gate"] | "scale_gate"; qk_order ["norm_rope"] | "rope_norm".
 
 Parity status: every function here is pinned by a closed form, an invariant,
 a special case or a brute-force loop in tests/test_oracle.py, except the
@@ -71,6 +74,40 @@ def rms_norm(x, eps, gamma=None):
     return y if gamma is None else y * gamma
 
 
+def gelu_tanh(z):
+    """GELU in its tanh approximation, 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))),
+    with the tanh argument clamped to [-20, 20] and the result to the fp16
+    range +-65504 ([ERNIE] §V Bug 1: the FFN activation, and the clamps that
+    keep a large gate projection from producing inf - inf)."""
+    with np.errstate(over="ignore", invalid="ignore"):      # z^3 may overflow; the clamp absorbs it
+        a = np.sqrt(2.0 / np.pi) * (z + 0.044715 * z * z * z)
+        return np.clip(0.5 * z * (1.0 + np.tanh(np.clip(a, -20.0, 20.0))), -65504.0, 65504.0)
+
+
+def gate_fn(g, kind="identity"):
+    """The function applied to a modulation gate before the gated residual:
+    identity ([ERNIE] §VII Decision 1 prints r + g y), tanh or sigmoid (the
+    alternatives [ZML] §IV's semantics search chooses between)."""
+    if kind == "identity":
+        return g
+    if kind == "tanh":
+        return np.tanh(g)
+    if kind == "sigmoid":
+        return 1.0 / (1.0 + np.exp(-g))
+    raise ValueError(kind)
+
+
+def norm(x, spec, gamma=None, beta=None):
+    """The block's norm kind: LayerNorm, or RMSNorm ([ERNIE] §IV draws RMSNorm
+    for the AdaLN norm and the qk-norm), then the optional affine."""
+    if getattr(spec, "norm", "layernorm") == "rmsnorm":
+        y = rms_norm(x, spec.eps)
+        if gamma is not None:
+            y = y * gamma
+        return y if beta is None else y + beta
+    return layer_norm(x, spec.eps, gamma, beta)
+
+
 def modulate(n, shift, scale):
     """AdaLN modulation n * (1 + scale) + shift ([ERNIE] §V Bug 4 prints the
     form; [ZML] §IV calls the `1 + scale` variant plus_one)."""
@@ -89,24 +126,33 @@ def gated_residual(r, gate, y):
     return r + gate * y
 
 
-def swiglu(h, w_gate_up, dtype=F64):
-    """SiLU(h Wg^T) * (h Wu^T) with W = [Wg; Wu] stacked gate rows first
-    ([ZML] §VI: Glu step with gate_first; SwiGLU names the SiLU gate)."""
+def swiglu(h, w_gate_up, dtype=F64, act="silu"):
+    """act(h Wg^T) * (h Wu^T) with W = [Wg; Wu] stacked gate rows first
+    ([ZML] §VI: Glu step with gate_first; SwiGLU names the SiLU gate; [ERNIE]
+    §IV / §V Bug 1: GELU(gate) x up with the clamped tanh GELU)."""
     w = np.asarray(w_gate_up, dtype)
     F = w.shape[0] // 2
-    return silu(linear(h, w[:F], dtype=dtype)) * linear(h, w[F:], dtype=dtype)
+    f = silu if act == "silu" else gelu_tanh
+    return f(linear(h, w[:F], dtype=dtype)) * linear(h, w[F:], dtype=dtype)
 
 
 # ---------------------------------------------------------------------------
 # conditioning
 # ---------------------------------------------------------------------------
-def adaln_modulation(w_ada, b_ada, c, dtype=F64):
-    """6-way AdaLN modulation m = W_ada . SiLU(c) + b_ada, split in six [D]
-    chunks in the order (shift1, scale1, gate1, shift2, scale2, gate2)
-    ([ERNIE] §IV, last paragraph of the per-layer graph)."""
+def adaln_modulation(w_ada, b_ada, c, dtype=F64, mod="shift_scale_gate"):
+    """AdaLN modulation m = W_ada . SiLU(c) + b_ada, returned as (shift1,
+    scale1, gate1, shift2, scale2, gate2): six [D] chunks in that order
+    ([ERNIE] §IV, last paragraph of the per-layer graph), or for mod =
+    "scale_gate" four chunks (scale1, gate1, scale2, gate2) with no shift
+    ([ZML] §IV table: modulation "[scale, gate], 1 + scale, no shift"; the
+    order of the four chunks is a reading: [scale, gate] per branch)."""
     w = np.asarray(w_ada, dtype)
     m = w @ silu(np.asarray(c, dtype)) + np.asarray(b_ada, dtype)
-    return np.split(m, 6)
+    if mod == "scale_gate":
+        scale1, gate1, scale2, gate2 = np.split(m, 4)
+        z = np.zeros_like(scale1)
+        return z, scale1, gate1, z, scale2, gate2
+    return tuple(np.split(m, 6))
 
 
 def timestep_embedding(t, dim, dtype=F64):
@@ -196,41 +242,51 @@ def attention(q, k, v, heads, kv_heads, q_rows=None):
 # the block
 # ---------------------------------------------------------------------------
 def _mods(w, c, spec, dtype):
+    """(shift1, scale1, gate1, shift2, scale2, gate2); the gates already
+    passed through the gate function."""
     D = w["w_qkv"].shape[1]
     if spec.cond_dim > 0:
-        return adaln_modulation(w["w_ada"], w["b_ada"], c, dtype)
+        sh1, sc1, g1, sh2, sc2, g2 = adaln_modulation(w["w_ada"], w["b_ada"], c, dtype,
+                                                      getattr(spec, "mod", "shift_scale_gate"))
+        kind = getattr(spec, "gate", "identity")
+        return sh1, sc1, gate_fn(g1, kind), sh2, sc2, gate_fn(g2, kind)
     z, one = np.zeros(D, dtype), np.ones(D, dtype)
     return z, z, one, z, z, one
 
 
 def _prenorm(x, w, which, shift, scale, spec, dtype):
     if spec.cond_dim > 0:
-        return modulate(layer_norm(x, spec.eps), shift, scale)
+        return modulate(norm(x, spec), shift, scale)
     g, b = w[which + "_g"], w[which + "_b"]
-    return layer_norm(x, spec.eps,
-                      None if g is None else np.asarray(g, dtype),
-                      None if b is None else np.asarray(b, dtype))
+    return norm(x, spec, None if g is None else np.asarray(g, dtype), None if b is None else np.asarray(b, dtype))
 
 
 def block_qkv(h, w, spec, pos, dtype=F64):
-    """QKV projection, per-head qk-LayerNorm, then RoPE on q and k.
+    """QKV projection, per-head qk-norm and RoPE on q and k.
 
-    [ERNIE] §IV per-layer graph: QKV projection, 3D RoPE, qk_layernorm;
-    [ZML] §I/§VI fuse "QKV + norm + RoPE" with the norm first, which is the
-    order taken here.  Returns q [N,H,hd], k/v [N,Hkv,hd]."""
+    [ZML] §I/§VI fuse "QKV + norm + RoPE" with the norm first (the default,
+    qk_order "norm_rope"); [ERNIE] §IV's per-layer graph draws 3D RoPE before
+    qk_layernorm (qk_order "rope_norm").  Returns q [N,H,hd], k/v [N,Hkv,hd]."""
     H, Hk, hd = spec.heads, spec.kv_heads, spec.head_dim
     N = h.shape[0]
     qkv = linear(h, w["w_qkv"], dtype=dtype)
     q = qkv[:, : H * hd].reshape(N, H, hd)
     k = qkv[:, H * hd: (H + Hk) * hd].reshape(N, Hk, hd)
     v = qkv[:, (H + Hk) * hd:].reshape(N, Hk, hd)
-    if spec.qk_norm:
-        q = layer_norm(q, spec.eps, np.asarray(w["q_g"], dtype), np.asarray(w["q_b"], dtype))
-        k = layer_norm(k, spec.eps, np.asarray(w["k_g"], dtype), np.asarray(w["k_b"], dtype))
     ang = rope_angles(pos, spec, dtype)                       # [S, hd/2]
     ang = np.tile(ang, (spec.batch, 1))                       # every sequence uses the same positions
-    q = apply_rope(q, ang, spec.rope)
-    k = apply_rope(k, ang, spec.rope)
+
+    def qknorm(q, k):
+        if not spec.qk_norm:
+            return q, k
+        return (norm(q, spec, np.asarray(w["q_g"], dtype), np.asarray(w["q_b"], dtype)),
+                norm(k, spec, np.asarray(w["k_g"], dtype), np.asarray(w["k_b"], dtype)))
+
+    if getattr(spec, "qk_order", "norm_rope") == "rope_norm":
+        q, k = qknorm(apply_rope(q, ang, spec.rope), apply_rope(k, ang, spec.rope))
+    else:
+        q, k = qknorm(q, k)
+        q, k = apply_rope(q, ang, spec.rope), apply_rope(k, ang, spec.rope)
     return q, k, v
 
 
@@ -266,7 +322,7 @@ def block_forward(x, c, w, spec, pos, dtype=F64, rows=None, keep=None):
         att[sel] = attention(q[sl], k[sl], v[sl], spec.heads, spec.kv_heads, rows[sel] - b * S)
     x1 = gated_residual(x[rows], gate1, linear(att, w["w_o"], dtype=dtype))
     h2 = _prenorm(x1, w, "ln2", shift2, scale2, spec, dtype)
-    ff = swiglu(h2, w["w_gate_up"], dtype)
+    ff = swiglu(h2, w["w_gate_up"], dtype, getattr(spec, "act", "silu"))
     out = gated_residual(x1, gate2, linear(ff, w["w_down"], dtype=dtype))
     if keep is not None:
         keep.update(dict(mods=(shift1, scale1, gate1, shift2, scale2, gate2), h=h, q=q, k=k, v=v,
@@ -298,7 +354,7 @@ def final_layer(x, c, edges, spec, dtype=F64):
     v = (LN(x)(1 + scale) + shift) W_out^T + b_out."""
     m = np.asarray(edges["w_fmod"], dtype) @ np.asarray(c, dtype) + np.asarray(edges["b_fmod"], dtype)
     scale, shift = np.split(m, 2)
-    h = modulate(layer_norm(x, spec.eps), shift, scale)
+    h = modulate(norm(x, spec), shift, scale)
     return h @ np.asarray(edges["w_out"], dtype).T + np.asarray(edges["b_out"], dtype)
 
 

@@ -470,3 +470,100 @@ def test_joint_text_first_is_a_row_permutation():
     b = O.block_forward(x[perm], c, w, cft, I.positions(cft))
     np.testing.assert_allclose(b, a[perm], rtol=1e-10, atol=1e-12)
 
+
+
+# ---------------------------------------------------------------------------
+# semantics switches: norm kind, GLU activation, gate function, modulation
+# chunks, qk-norm / RoPE order
+# ---------------------------------------------------------------------------
+def test_gelu_tanh_against_erf_gelu_and_its_clamps():
+    """ERNIE page §V Bug 1: GELU in its tanh approximation with the argument
+    clamped to +-20 and the result to +-65504."""
+    import scipy.special as sp
+    x = np.linspace(-10.0, 10.0, 20001)
+    exact = 0.5 * x * (1.0 + sp.erf(x / np.sqrt(2.0)))      # GELU's definition, x Phi(x)
+    assert np.abs(O.gelu_tanh(x) - exact).max() < 5e-4         # the tanh approximation's deviation
+    # odd part: f(x) - f(-x) = x, since tanh is odd (holds through the argument clamp)
+    x = np.linspace(-50.0, 50.0, 10001)
+    np.testing.assert_allclose(O.gelu_tanh(x) - O.gelu_tanh(-x), x, rtol=0, atol=1e-12)
+    # the clamps: large gate projections stay finite and saturate
+    g = O.gelu_tanh(np.array([30.0, -30.0, 1e6, -1e6]))
+    assert g[0] == 30.0 and abs(g[1]) < 1e-12 and g[2] == 65504.0 and abs(g[3]) < 1e-6
+    g32 = O.gelu_tanh(np.array([1e30], np.float32))           # z^3 overflows fp32: still finite
+    assert np.isfinite(g32).all() and g32[0] == 65504.0
+
+
+def _zero_ada_weights(cfg, b_gate=None):
+    w = I.block_weights(cfg)
+    w["w_ada"] = np.zeros_like(w["w_ada"])
+    return w
+
+
+def test_gate_function_tanh_and_sigmoid():
+    """With W_ada = 0 the modulation is b_ada, so a tanh / sigmoid gate equals
+    the identity gate with those functions applied to b_ada's gate chunks; a
+    zero tanh gate kills both branches."""
+    base = I.C1.replace(name="t_gate")
+    D = base.hidden
+    x, c, pos = I.block_x(base), I.cond(base), I.positions(base)
+    w = _zero_ada_weights(base)
+    for kind, f in (("tanh", np.tanh), ("sigmoid", lambda g: 1.0 / (1.0 + np.exp(-g)))):
+        got = O.block_forward(x, c, w, base.replace(gate=kind), pos)
+        w2 = dict(w)
+        b = np.array(w["b_ada"], np.float64)
+        for chunk in (2, 5):                                    # gate1, gate2
+            b[chunk * D:(chunk + 1) * D] = f(b[chunk * D:(chunk + 1) * D])
+        w2["b_ada"] = b
+        ref = O.block_forward(x, c, w2, base, pos)
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    w0 = dict(w)
+    w0["b_ada"] = np.zeros_like(w["b_ada"])
+    np.testing.assert_array_equal(O.block_forward(x, c, w0, base.replace(gate="tanh"), pos), x)
+
+
+def test_scale_gate_modulation_is_the_six_way_one_with_zero_shift():
+    """mod = "scale_gate" (chunks scale1, gate1, scale2, gate2; no shift) equals
+    the six-way modulation whose shift rows are zero."""
+    cfg = I.C1.replace(name="t_sg", mod="scale_gate")
+    D = cfg.hidden
+    w4 = I.block_weights(cfg)
+    assert w4["w_ada"].shape[0] == 4 * D
+    x, c, pos = I.block_x(cfg), I.cond(cfg), I.positions(cfg)
+    got = O.block_forward(x, c, w4, cfg, pos)
+    w6 = dict(w4)
+    wz, bz = np.zeros((D, cfg.cond_dim)), np.zeros(D)
+    W, B = w4["w_ada"], w4["b_ada"]
+    w6["w_ada"] = np.concatenate([wz, W[:D], W[D:2 * D], wz, W[2 * D:3 * D], W[3 * D:]])
+    w6["b_ada"] = np.concatenate([bz, B[:D], B[D:2 * D], bz, B[2 * D:3 * D], B[3 * D:]])
+    ref = O.block_forward(x, c, w6, cfg.replace(mod="shift_scale_gate"), pos)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_rmsnorm_of_centred_rows_is_layernorm():
+    x = np.random.default_rng(31).standard_normal((7, 96))
+    xc = x - x.mean(axis=-1, keepdims=True)
+    np.testing.assert_allclose(O.rms_norm(xc, 1e-6), O.layer_norm(x, 1e-6), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(O.rms_norm(5.0 * xc, 0.0), O.rms_norm(xc, 0.0), rtol=1e-12)
+    spec = I.C1.replace(norm="rmsnorm")
+    g, b = np.full(96, 2.0), np.full(96, 0.5)
+    np.testing.assert_allclose(O.norm(x, spec, g, b), O.rms_norm(x, spec.eps) * 2.0 + 0.5, rtol=1e-12)
+
+
+def test_qk_order_rope_then_norm():
+    """RoPE is a rotation of pairs: it preserves the RMS, so with RMSNorm
+    (gamma 1, beta 0) both orders agree; at position 0 (identity rotation) they
+    agree for LayerNorm too; in general LayerNorm does not commute with RoPE."""
+    cfg = I.C1.replace(name="t_order")
+    w = I.block_weights(cfg)
+    x, c, pos = I.block_x(cfg), I.cond(cfg), I.positions(cfg)
+    w1 = dict(w, q_g=np.ones(cfg.head_dim), k_g=np.ones(cfg.head_dim),
+              q_b=np.zeros(cfg.head_dim), k_b=np.zeros(cfg.head_dim))
+    rms = cfg.replace(norm="rmsnorm")
+    np.testing.assert_allclose(O.block_forward(x, c, w1, rms.replace(qk_order="rope_norm"), pos),
+                               O.block_forward(x, c, w1, rms, pos), rtol=1e-9, atol=1e-10)
+    z = np.zeros_like(pos)
+    np.testing.assert_allclose(O.block_forward(x, c, w, cfg.replace(qk_order="rope_norm"), z),
+                               O.block_forward(x, c, w, cfg, z), rtol=1e-10, atol=1e-12)
+    a = O.block_forward(x, c, w, cfg.replace(qk_order="rope_norm"), pos)
+    b = O.block_forward(x, c, w, cfg, pos)
+    assert np.abs((a - x) - (b - x)).max() > 1e-3 * np.abs(b - x).max()
