@@ -63,6 +63,23 @@ __device__ __forceinline__ void wait_vmcnt() {
 // still meant to be in flight.  Ordering is provided by the explicit waits.
 __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
+// clamped GELU in its tanh approximation: 0.5 z (1 + tanh(a)), a = sqrt(2/pi)(z + 0.044715 z^3)
+// clamped to [-20, 20], result clamped to +-65504 (ERNIE page §V Bug 1).  tanh(a) is
+// 1 - 2 / (e^{2a} + 1), finite for |a| <= 20.
+__device__ __forceinline__ float gelu_tanh_f(float z) {
+    float a = 0.7978845608028654f * (z + 0.044715f * z * z * z);
+    a = fminf(fmaxf(a, -20.0f), 20.0f);   // an overflowing z^3 gives +-inf: clamped like any large value
+    const float t = 1.0f - 2.0f / (__expf(2.0f * a) + 1.0f);
+    return fminf(fmaxf(0.5f * z * (1.0f + t), -65504.0f), 65504.0f);
+}
+
+// gate function before the gated residual: 0 identity, 1 tanh, 2 sigmoid
+__device__ __forceinline__ float gate_f(float g, int fn) {
+    if (fn == 1) return tanhf(g);
+    if (fn == 2) return 1.0f / (1.0f + expf(-g));
+    return g;
+}
+
 __device__ __forceinline__ float silu_f(float z) {
     // z * sigmoid(z); expf of a large positive -z gives inf and z/inf -> -0
     return z / (1.0f + __expf(-z));
@@ -78,16 +95,19 @@ namespace dit {
 struct QkvEpiArgs {
     int batch, seq, seq_pad, heads, kv_heads, head_dim;
     int qk_norm, rope_half;
+    int rms;          // qk-norm kind: 0 LayerNorm, 1 RMSNorm
+    int rope_first;   // 0: qk-norm then RoPE, 1: RoPE then qk-norm
     float eps;
     const float *q_g, *q_b, *k_g, *k_b;
     const float *cos_t, *sin_t;
     bf16 *q, *k, *vt;
 };
 
+// gate_fn: 0 identity, 1 tanh, 2 sigmoid (applied to gate[n]); act: 0 SiLU, 1 clamped GELU-tanh
 hipError_t launch_gemm_residual(const bf16 *a, const bf16 *w, int64_t M, int N, int K,
-                                const void *resid, int resid_f32, const float *gate,
+                                const void *resid, int resid_f32, const float *gate, int gate_fn,
                                 const float *bias, void *out, int out_f32, hipStream_t s);
-hipError_t launch_gemm_swiglu(const bf16 *a, const bf16 *w, int64_t M, int F, int K,
+hipError_t launch_gemm_swiglu(const bf16 *a, const bf16 *w, int64_t M, int F, int K, int act,
                               bf16 *u, hipStream_t s);
 hipError_t launch_gemm_qkv(const bf16 *h, const bf16 *w, int64_t M, int N, int K,
                            const QkvEpiArgs &e, hipStream_t s);
@@ -98,7 +118,7 @@ hipError_t launch_flash_attention(const bf16 *q, const bf16 *k, const bf16 *vt, 
 
 hipError_t launch_adaln_gemv(const bf16 *w, const float *b, const float *c, int out_dim,
                              int in_dim, int silu_input, float *m, hipStream_t s);
-hipError_t launch_ln_modulate(const void *x, int x_f32, int64_t rows, int dim,
+hipError_t launch_ln_modulate(const void *x, int x_f32, int64_t rows, int dim, int rms,
                               const float *shift, const float *scale, int mode, float eps,
                               bf16 *h, hipStream_t s);
 hipError_t launch_euler(float *latent, const float *v, int64_t n, float dsigma, hipStream_t s);

@@ -99,7 +99,10 @@ int check_desc(const dit_block_desc *d) {
     if (d->x_dtype != DIT_F32 && d->x_dtype != DIT_BF16) return fail(DIT_ERR_INVALID_ARG, "bad x_dtype");
     if (d->rope != DIT_ROPE_INTERLEAVED && d->rope != DIT_ROPE_HALF) return fail(DIT_ERR_INVALID_ARG, "bad rope layout");
     if (d->norm != DIT_LAYERNORM && d->norm != DIT_RMSNORM) return fail(DIT_ERR_INVALID_ARG, "bad norm kind");
-    if (d->norm != DIT_LAYERNORM) return fail(DIT_ERR_UNSUPPORTED, "only DIT_LAYERNORM is built");
+    if (d->act != DIT_ACT_SILU && d->act != DIT_ACT_GELU_TANH) return fail(DIT_ERR_INVALID_ARG, "bad act");
+    if (d->gate < DIT_GATE_IDENTITY || d->gate > DIT_GATE_SIGMOID) return fail(DIT_ERR_INVALID_ARG, "bad gate function");
+    if (d->mod != DIT_MOD_SHIFT_SCALE_GATE && d->mod != DIT_MOD_SCALE_GATE) return fail(DIT_ERR_INVALID_ARG, "bad mod");
+    if (d->qk_order != DIT_QK_NORM_ROPE && d->qk_order != DIT_QK_ROPE_NORM) return fail(DIT_ERR_INVALID_ARG, "bad qk_order");
     if (d->w_dtype != DIT_BF16) return fail(DIT_ERR_UNSUPPORTED, "weights must be bf16");
     if (d->head_dim != 64 && d->head_dim != 128) return fail(DIT_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
     if (d->hidden % 256) return fail(DIT_ERR_UNSUPPORTED, "hidden must be a multiple of 256");
@@ -145,6 +148,9 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 
 hipStream_t as_stream(void *s) { return (hipStream_t)s; }
 
+// Rows of the AdaLN linear: 6 or 4 chunks of hidden.
+int ada_rows(const dit_block_desc &d) { return (d.mod == DIT_MOD_SCALE_GATE ? 4 : 6) * d.hidden; }
+
 // The block body after the modulation vector m (or NULL without AdaLN) is ready.
 int block_body(const dit_block_desc &d, const dit_block_weights &w, const void *x, int x_f32, const float *m,
                const float *cosT, const float *sinT, void *out, int out_f32, uint8_t *ws, const BlockWs &L,
@@ -159,18 +165,29 @@ int block_body(const dit_block_desc &d, const dit_block_weights &w, const void *
     float *x1 = (float *)(ws + L.x1);
     bf16 *u = (bf16 *)(ws + L.u);
     const int mode = m ? 0 : 1;
+    const int rms = d.norm == DIT_RMSNORM;
+    // modulation chunks: (shift1, scale1, gate1, shift2, scale2, gate2) or, without
+    // shift, (scale1, gate1, scale2, gate2); without AdaLN the affine LN parameters
+    const float *shift1, *scale1, *gate1, *shift2, *scale2, *gate2;
+    if (!m) {
+        shift1 = w.ln1_b; scale1 = w.ln1_g; shift2 = w.ln2_b; scale2 = w.ln2_g; gate1 = gate2 = nullptr;
+    } else if (d.mod == DIT_MOD_SCALE_GATE) {
+        shift1 = shift2 = nullptr; scale1 = m; gate1 = m + D; scale2 = m + 2 * D; gate2 = m + 3 * D;
+    } else {
+        shift1 = m; scale1 = m + D; gate1 = m + 2 * D; shift2 = m + 3 * D; scale2 = m + 4 * D; gate2 = m + 5 * D;
+    }
 
-    DIT_TRY_HIP(launch_ln_modulate(x, x_f32, N, D, m ? m : w.ln1_b, m ? m + D : w.ln1_g, mode, d.eps, h, s));
+    DIT_TRY_HIP(launch_ln_modulate(x, x_f32, N, D, rms, shift1, scale1, mode, d.eps, h, s));
     DIT_TRY_HIP(launch_vt_pad_zero(vt, d.batch * d.kv_heads * hd, d.seq, spad, s));
-    QkvEpiArgs e{d.batch, d.seq, spad, d.heads, d.kv_heads, hd, d.qk_norm, d.rope == DIT_ROPE_HALF, d.eps,
-                 w.q_g, w.q_b, w.k_g, w.k_b, cosT, sinT, q, k, vt};
+    QkvEpiArgs e{d.batch, d.seq, spad, d.heads, d.kv_heads, hd, d.qk_norm, d.rope == DIT_ROPE_HALF, rms,
+                 d.qk_order == DIT_QK_ROPE_NORM, d.eps, w.q_g, w.q_b, w.k_g, w.k_b, cosT, sinT, q, k, vt};
     DIT_TRY_HIP(launch_gemm_qkv(h, (const bf16 *)w.w_qkv, N, qkv_dim, D, e, s));
     DIT_TRY_HIP(launch_flash_attention(q, k, vt, att, d.batch, d.seq, spad, d.heads, d.kv_heads, hd, s));
-    DIT_TRY_HIP(launch_gemm_residual(att, (const bf16 *)w.w_o, N, D, d.heads * hd, x, x_f32, m ? m + 2 * D : nullptr,
+    DIT_TRY_HIP(launch_gemm_residual(att, (const bf16 *)w.w_o, N, D, d.heads * hd, x, x_f32, gate1, d.gate,
                                      nullptr, x1, 1, s));
-    DIT_TRY_HIP(launch_ln_modulate(x1, 1, N, D, m ? m + 3 * D : w.ln2_b, m ? m + 4 * D : w.ln2_g, mode, d.eps, h, s));
-    DIT_TRY_HIP(launch_gemm_swiglu(h, (const bf16 *)w.w_gate_up, N, F, D, u, s));
-    DIT_TRY_HIP(launch_gemm_residual(u, (const bf16 *)w.w_down, N, D, F, x1, 1, m ? m + 5 * D : nullptr, nullptr,
+    DIT_TRY_HIP(launch_ln_modulate(x1, 1, N, D, rms, shift2, scale2, mode, d.eps, h, s));
+    DIT_TRY_HIP(launch_gemm_swiglu(h, (const bf16 *)w.w_gate_up, N, F, D, d.act, u, s));
+    DIT_TRY_HIP(launch_gemm_residual(u, (const bf16 *)w.w_down, N, D, F, x1, 1, gate2, d.gate, nullptr,
                                      out, out_f32, s));
     return DIT_OK;
 }
@@ -263,7 +280,7 @@ int dit_block_forward(const dit_block_desc *desc, const dit_block_weights *w, co
     float *m = nullptr;
     if (d.cond_dim > 0) {
         m = (float *)(wsb + L.m);
-        DIT_TRY_HIP(launch_adaln_gemv((const bf16 *)w->w_ada, w->b_ada, cond, 6 * d.hidden, d.cond_dim, 1, m, s));
+        DIT_TRY_HIP(launch_adaln_gemv((const bf16 *)w->w_ada, w->b_ada, cond, ada_rows(d), d.cond_dim, 1, m, s));
     }
     const int xf = d.x_dtype == DIT_F32;
     DIT_TRY(block_body(d, *w, x, xf, m, rope_cos, rope_sin, out, xf, wsb, L, s));
@@ -304,7 +321,7 @@ int dit_stack_step(const dit_model *model, const float *latent, const float *con
 
     // patch embedding: x = bf16(latent) W_in^T + b_in (fp32 residual stream)
     DIT_TRY_HIP(launch_f32_to_bf16(latent, lat, N * M.latent_dim, s));
-    DIT_TRY_HIP(launch_gemm_residual(lat, (const bf16 *)M.w_in, N, D, M.latent_dim, nullptr, 1, nullptr, M.b_in, x, 1, s));
+    DIT_TRY_HIP(launch_gemm_residual(lat, (const bf16 *)M.w_in, N, D, M.latent_dim, nullptr, 1, nullptr, 0, M.b_in, x, 1, s));
 
     bool shared = true;
     for (int l = 1; l < M.layers; ++l)
@@ -312,15 +329,15 @@ int dit_stack_step(const dit_model *model, const float *latent, const float *con
     for (int l = 0; l < M.layers; ++l) {
         const dit_block_weights &w = M.blocks[l];
         if (l == 0 || !shared)
-            DIT_TRY_HIP(launch_adaln_gemv((const bf16 *)w.w_ada, w.b_ada, cond, 6 * D, d.cond_dim, 1, m, s));
+            DIT_TRY_HIP(launch_adaln_gemv((const bf16 *)w.w_ada, w.b_ada, cond, ada_rows(d), d.cond_dim, 1, m, s));
         DIT_TRY(block_body(d, w, x, 1, m, rope_cos, rope_sin, x, 1, wsb, L.blk, s));
     }
 
     // final AdaLN-continuous norm: [scale | shift] = W_f c + b_f (no SiLU), then projection
     DIT_TRY_HIP(launch_adaln_gemv((const bf16 *)M.w_fmod, M.b_fmod, cond, 2 * D, d.cond_dim, 0, fm, s));
     bf16 *h = (bf16 *)(wsb + L.blk.h);
-    DIT_TRY_HIP(launch_ln_modulate(x, 1, N, D, fm + D, fm, 0, d.eps, h, s));
-    DIT_TRY_HIP(launch_gemm_residual(h, (const bf16 *)M.w_out, N, M.latent_dim, D, nullptr, 1, nullptr, M.b_out,
+    DIT_TRY_HIP(launch_ln_modulate(x, 1, N, D, d.norm == DIT_RMSNORM, fm + D, fm, 0, d.eps, h, s));
+    DIT_TRY_HIP(launch_gemm_residual(h, (const bf16 *)M.w_out, N, M.latent_dim, D, nullptr, 1, nullptr, 0, M.b_out,
                                      velocity, 1, s));
     return ok();
 }
@@ -410,20 +427,21 @@ int dit_adaln_modulation(const void *w, const float *b, const float *c, int32_t 
     return ok();
 }
 
-int dit_ln_modulate(const void *x, int32_t x_dtype, int64_t rows, int32_t dim, const float *shift, const float *scale,
-                    int32_t mode, float eps, void *h, void *stream) {
+int dit_ln_modulate(const void *x, int32_t x_dtype, int64_t rows, int32_t dim, int32_t norm, const float *shift,
+                    const float *scale, int32_t mode, float eps, void *h, void *stream) {
     if (!x || !h) return fail(DIT_ERR_INVALID_ARG, "x and h are required");
     if (rows <= 0 || dim <= 0) return fail(DIT_ERR_INVALID_ARG, "rows and dim must be positive");
     if (x_dtype != DIT_F32 && x_dtype != DIT_BF16) return fail(DIT_ERR_INVALID_ARG, "bad x_dtype");
     if (mode != 0 && mode != 1) return fail(DIT_ERR_INVALID_ARG, "mode must be 0 or 1");
-    if (mode == 0 && (!shift || !scale)) return fail(DIT_ERR_INVALID_ARG, "mode 0 needs shift and scale");
+    if (mode == 0 && !scale) return fail(DIT_ERR_INVALID_ARG, "mode 0 needs scale");
+    if (norm != DIT_LAYERNORM && norm != DIT_RMSNORM) return fail(DIT_ERR_INVALID_ARG, "bad norm kind");
     if (!(eps > 0.f)) return fail(DIT_ERR_INVALID_ARG, "eps must be positive");
     if (dim % 256 || dim > 8192) return fail(DIT_ERR_UNSUPPORTED, "dim must be a multiple of 256 and <= 8192");
     if (!aligned16(x) || !aligned16(h) || (shift && !aligned16(shift)) || (scale && !aligned16(scale)))
         return fail(DIT_ERR_ALIGNMENT, "x, h, shift, scale must be 16-byte aligned");
     DIT_TRY(device_check());
-    DIT_TRY_HIP(launch_ln_modulate(x, x_dtype == DIT_F32, rows, dim, shift, scale, mode, eps, (bf16 *)h,
-                                   as_stream(stream)));
+    DIT_TRY_HIP(launch_ln_modulate(x, x_dtype == DIT_F32, rows, dim, norm == DIT_RMSNORM, shift, scale, mode, eps,
+                                   (bf16 *)h, as_stream(stream)));
     return ok();
 }
 
@@ -440,8 +458,9 @@ int dit_qkv_rope(const dit_block_desc *desc, const void *h, const void *w_qkv, c
     hipStream_t s = as_stream(stream);
     const int spad = seq_pad_of(d.seq);
     DIT_TRY_HIP(launch_vt_pad_zero((bf16 *)vt, d.batch * d.kv_heads * d.head_dim, d.seq, spad, s));
-    QkvEpiArgs e{d.batch, d.seq, spad, d.heads, d.kv_heads, d.head_dim, d.qk_norm, d.rope == DIT_ROPE_HALF, d.eps,
-                 q_g, q_b, k_g, k_b, rope_cos, rope_sin, (bf16 *)q, (bf16 *)k, (bf16 *)vt};
+    QkvEpiArgs e{d.batch, d.seq, spad, d.heads, d.kv_heads, d.head_dim, d.qk_norm, d.rope == DIT_ROPE_HALF,
+                 d.norm == DIT_RMSNORM, d.qk_order == DIT_QK_ROPE_NORM, d.eps, q_g, q_b, k_g, k_b, rope_cos, rope_sin,
+                 (bf16 *)q, (bf16 *)k, (bf16 *)vt};
     DIT_TRY_HIP(launch_gemm_qkv((const bf16 *)h, (const bf16 *)w_qkv, (int64_t)d.batch * d.seq,
                                 (d.heads + 2 * d.kv_heads) * d.head_dim, d.hidden, e, s));
     return ok();
@@ -461,12 +480,13 @@ int dit_flash_attention(const dit_block_desc *desc, const void *q, const void *k
 }
 
 int dit_gemm_gated_residual(const void *a, const void *w, int64_t M, int32_t N, int32_t K, const void *resid,
-                            int32_t resid_dtype, const float *gate, const float *bias, void *out, int32_t out_dtype,
-                            void *stream) {
+                            int32_t resid_dtype, const float *gate, int32_t gate_fn, const float *bias, void *out,
+                            int32_t out_dtype, void *stream) {
     if (!a || !w || !out) return fail(DIT_ERR_INVALID_ARG, "a, w and out are required");
     if (M <= 0 || N <= 0 || K <= 0) return fail(DIT_ERR_INVALID_ARG, "dims must be positive");
     if ((resid && resid_dtype != DIT_F32 && resid_dtype != DIT_BF16) || (out_dtype != DIT_F32 && out_dtype != DIT_BF16))
         return fail(DIT_ERR_INVALID_ARG, "bad dtype");
+    if (gate_fn < DIT_GATE_IDENTITY || gate_fn > DIT_GATE_SIGMOID) return fail(DIT_ERR_INVALID_ARG, "bad gate function");
     if (N % 128 || K % 64) return fail(DIT_ERR_UNSUPPORTED, "N must be a multiple of 128 and K of 64");
     if ((double)M * K >= 2147483648.0 || (double)N * K >= 2147483648.0)
         return fail(DIT_ERR_UNSUPPORTED, "operand exceeds 2^31 elements");
@@ -478,20 +498,22 @@ int dit_gemm_gated_residual(const void *a, const void *w, int64_t M, int32_t N, 
     if (resid && resid != out && overlaps(resid, rb, out, ob)) return fail(DIT_ERR_INVALID_ARG, "resid overlaps out");
     if (resid == out && resid && resid_dtype != out_dtype) return fail(DIT_ERR_INVALID_ARG, "in-place needs equal dtypes");
     DIT_TRY(device_check());
-    DIT_TRY_HIP(launch_gemm_residual((const bf16 *)a, (const bf16 *)w, M, N, K, resid, resid_dtype == DIT_F32, gate, bias,
-                                     out, out_dtype == DIT_F32, as_stream(stream)));
+    DIT_TRY_HIP(launch_gemm_residual((const bf16 *)a, (const bf16 *)w, M, N, K, resid, resid_dtype == DIT_F32, gate,
+                                     gate_fn, bias, out, out_dtype == DIT_F32, as_stream(stream)));
     return ok();
 }
 
-int dit_gemm_swiglu(const void *a, const void *w_gate_up, int64_t M, int32_t F, int32_t K, void *u, void *stream) {
+int dit_gemm_swiglu(const void *a, const void *w_gate_up, int64_t M, int32_t F, int32_t K, int32_t act, void *u,
+                    void *stream) {
     if (!a || !w_gate_up || !u) return fail(DIT_ERR_INVALID_ARG, "a, w_gate_up and u are required");
+    if (act != DIT_ACT_SILU && act != DIT_ACT_GELU_TANH) return fail(DIT_ERR_INVALID_ARG, "bad act");
     if (M <= 0 || F <= 0 || K <= 0) return fail(DIT_ERR_INVALID_ARG, "dims must be positive");
     if (F % 128 || K % 64) return fail(DIT_ERR_UNSUPPORTED, "F must be a multiple of 128 and K of 64");
     if ((double)M * K >= 2147483648.0 || 2.0 * F * K >= 2147483648.0 || (double)M * F >= 2147483648.0)
         return fail(DIT_ERR_UNSUPPORTED, "operand exceeds 2^31 elements");
     if (!aligned16(a) || !aligned16(w_gate_up) || !aligned16(u)) return fail(DIT_ERR_ALIGNMENT, "16-byte alignment required");
     DIT_TRY(device_check());
-    DIT_TRY_HIP(launch_gemm_swiglu((const bf16 *)a, (const bf16 *)w_gate_up, M, F, K, (bf16 *)u, as_stream(stream)));
+    DIT_TRY_HIP(launch_gemm_swiglu((const bf16 *)a, (const bf16 *)w_gate_up, M, F, K, act, (bf16 *)u, as_stream(stream)));
     return ok();
 }
 

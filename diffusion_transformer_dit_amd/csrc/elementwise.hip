@@ -75,15 +75,17 @@ hipError_t launch_adaln_gemv(const bf16 *w, const float *b, const float *c, int 
 }
 
 // ---------------------------------------------------------------------------
-// LayerNorm + modulation, one wave per row.  The row stays in registers
+// LayerNorm (or RMSNorm) + modulation, one wave per row.  The row stays in registers
 // (IT = dim/256 float4 per lane) between the mean pass, the centred variance
 // pass and the output pass, so x is read from HBM exactly once.  IT is a
 // template parameter so that all IT loads of a lane are issued back to back
 // (a runtime trip count puts each load behind its own branch and the wave
 // then waits for every load before issuing the next).
 //   mode 0: h = n * (1 + scale) + shift      mode 1: h = n * scale + shift
+// n = (x - mean) / sqrt(var + eps) (LayerNorm) or x / sqrt(mean(x^2) + eps)
+// (RMSNorm, RMS = true: no centring).
 // ---------------------------------------------------------------------------
-template <typename TX, int IT>
+template <typename TX, int IT, bool RMS>
 __global__ __launch_bounds__(256)
 void ln_modulate_kernel(const TX *__restrict__ x, int64_t rows, const float *__restrict__ shift,
                         const float *__restrict__ scale, int mode, float eps, bf16 *__restrict__ h) {
@@ -103,10 +105,13 @@ void ln_modulate_kernel(const TX *__restrict__ x, int64_t rows, const float *__r
             v[it] = floatx4{(float)t[0], (float)t[1], (float)t[2], (float)t[3]};
         }
     }
-    float s = 0.f;
+    float mean = 0.f;
+    if (!RMS) {
+        float s = 0.f;
 #pragma unroll
-    for (int it = 0; it < IT; ++it) s += (v[it][0] + v[it][1]) + (v[it][2] + v[it][3]);
-    const float mean = group_sum<64>(s) * (1.0f / dim);
+        for (int it = 0; it < IT; ++it) s += (v[it][0] + v[it][1]) + (v[it][2] + v[it][3]);
+        mean = group_sum<64>(s) * (1.0f / dim);
+    }
     float ss = 0.f;
 #pragma unroll
     for (int it = 0; it < IT; ++it)
@@ -146,14 +151,14 @@ void ln_modulate_kernel(const TX *__restrict__ x, int64_t rows, const float *__r
     }
 }
 
-template <typename TX>
+template <typename TX, bool RMS>
 static hipError_t ln_modulate_typed(const TX *x, int64_t rows, int dim, const float *shift, const float *scale,
                                     int mode, float eps, bf16 *h, hipStream_t s) {
     const dim3 grid((unsigned)((rows + 3) / 4));
     switch (dim >> 8) {
 #define DIT_LN_CASE(n)                                                                                 \
     case n:                                                                                            \
-        hipLaunchKernelGGL((ln_modulate_kernel<TX, n>), grid, dim3(256), 0, s, x, rows, shift, scale, \
+        hipLaunchKernelGGL((ln_modulate_kernel<TX, n, RMS>), grid, dim3(256), 0, s, x, rows, shift, scale, \
                            mode, eps, h);                                                              \
         break;
         DIT_LN_CASE(1) DIT_LN_CASE(2) DIT_LN_CASE(3) DIT_LN_CASE(4) DIT_LN_CASE(5) DIT_LN_CASE(6)
@@ -169,11 +174,14 @@ static hipError_t ln_modulate_typed(const TX *x, int64_t rows, int dim, const fl
     return hipGetLastError();
 }
 
-hipError_t launch_ln_modulate(const void *x, int x_f32, int64_t rows, int dim, const float *shift,
+hipError_t launch_ln_modulate(const void *x, int x_f32, int64_t rows, int dim, int rms, const float *shift,
                               const float *scale, int mode, float eps, bf16 *h, hipStream_t s) {
     if (dim % 256 != 0) return hipErrorInvalidValue;
-    if (x_f32) return ln_modulate_typed<float>((const float *)x, rows, dim, shift, scale, mode, eps, h, s);
-    return ln_modulate_typed<bf16>((const bf16 *)x, rows, dim, shift, scale, mode, eps, h, s);
+    if (x_f32)
+        return rms ? ln_modulate_typed<float, true>((const float *)x, rows, dim, shift, scale, mode, eps, h, s)
+                   : ln_modulate_typed<float, false>((const float *)x, rows, dim, shift, scale, mode, eps, h, s);
+    return rms ? ln_modulate_typed<bf16, true>((const bf16 *)x, rows, dim, shift, scale, mode, eps, h, s)
+               : ln_modulate_typed<bf16, false>((const bf16 *)x, rows, dim, shift, scale, mode, eps, h, s);
 }
 
 // ---------------------------------------------------------------------------

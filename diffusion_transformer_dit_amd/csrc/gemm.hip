@@ -12,11 +12,12 @@
 // Epilogues (run on the fp32 accumulators, no extra pass over memory):
 //   * residual : out = resid + gate[n] * acc + bias[n]   (gated residual, ERNIE
 //                page §VII Decision 1; out-projection / down-projection)
-//   * swiglu   : u = SiLU(acc_gate) * acc_up             (the tile's W rows
+//   * swiglu   : u = act(acc_gate) * acc_up              (the tile's W rows
 //                interleave gate rows and the matching up rows)
-//   * qkv      : per-(token, head) LayerNorm over head_dim with gamma/beta,
-//                RoPE rotation from cos/sin tables, scatter to head-major
-//                q/k and transposed v (zml-flow-rs page §VI, "QKV + norm + RoPE")
+//   * qkv      : per-(token, head) LayerNorm or RMSNorm over head_dim with
+//                gamma/beta and the RoPE rotation from cos/sin tables, in either
+//                order, scatter to head-major q/k and transposed v (zml-flow-rs
+//                page §VI "QKV + norm + RoPE"; ERNIE page §IV draws RoPE first)
 #include "common.h"
 
 namespace dit {
@@ -248,6 +249,7 @@ struct EpiResidual {
     const float *gate, *bias;
     TO *out;
     int N;
+    int gate_fn;      // 0 identity, 1 tanh, 2 sigmoid, applied to gate[n]
     template <class T> static constexpr int lds_bytes() { return 0; }
     template <class T>
     __device__ __forceinline__ void apply(floatx16 (&acc)[T::TM][T::TN], int row0, int tn, int wn, int lane, int M,
@@ -258,7 +260,7 @@ struct EpiResidual {
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) {
             const int col = col0 + j * 32 + lrow;
-            g[j] = gate ? gate[col] : 1.0f;
+            g[j] = gate ? gate_f(gate[col], gate_fn) : 1.0f;
             bb[j] = bias ? bias[col] : 0.0f;
         }
         // out may alias resid (in-place update), but every element is read and
@@ -306,8 +308,9 @@ struct EpiResidual {
 };
 
 // ---------------------------------------------------------------------------
-// epilogue: u = SiLU(gate) * up
+// epilogue: u = act(gate) * up, act = SiLU or the clamped GELU-tanh
 // ---------------------------------------------------------------------------
+template <int ACT>     // 0: SiLU (SwiGLU), 1: clamped GELU-tanh
 struct EpiSwiglu {
     bf16 *u;
     int F;
@@ -326,7 +329,10 @@ struct EpiSwiglu {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int row = row0 + acc_row(i, e, lhalf);
-                    if (row < M) u[(size_t)row * F + f] = f2bf(silu_f(acc[i][j][e]) * acc[i][j + HJ][e]);
+                    if (row < M) {
+                        const float g = ACT == 1 ? gelu_tanh_f(acc[i][j][e]) : silu_f(acc[i][j][e]);
+                        u[(size_t)row * F + f] = f2bf(g * acc[i][j + HJ][e]);
+                    }
                 }
         }
     }
@@ -360,7 +366,7 @@ struct EpiSwiglu {
 // ---------------------------------------------------------------------------
 constexpr int kQkvStride = 260;   // floats per staged row: 256 + 4, so 16 row-per-lane reads hit distinct banks
 
-template <int HD>
+template <int HD, bool RMS, bool RF>   // qk-norm kind RMSNorm; RoPE before the qk-norm
 struct EpiQkv {
     QkvEpiArgs e;
     static constexpr int kStageBytes = 2 * 64 * kQkvStride * 4;
@@ -442,38 +448,78 @@ struct EpiQkv {
                 return e.rope_half ? (q < 4 ? pair0 + q * 8 : HD / 2 + pair0 + (q - 4) * 8) : part * 64 + q * 8;
             };
             if (sect < 2) {
-                // the row is read from LDS once per pass (mean, centred variance,
-                // output) instead of being held in registers
+                // The row is read from LDS once per pass (mean, centred variance,
+                // output) instead of being held in registers.  A pair unit is one
+                // 8-value chunk (interleaved pairs) or chunks q and q + 4
+                // (rotate-half pairs); with rope_first the statistics and the
+                // output see the rotated values.
                 const float *src = red + rl * kQkvStride + hl * HD;
+                constexpr bool rf = RF;
+                auto raw = [&](int q, float (&y)[8]) {
+                    const floatx4 v0 = *(const floatx4 *)(src + qcol(q)), v1 = *(const floatx4 *)(src + qcol(q) + 4);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) { y[u] = v0[u]; y[u + 4] = v1[u]; }
+                };
+                auto rot_il = [&](int q, float (&y)[8]) {          // pairs 4q .. 4q + 3 of this lane
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int m = q * 4 + u;
+                        const float cs = cpre[m >> 2][m & 3], sn = spre[m >> 2][m & 3];
+                        const float a0 = y[2 * u], a1 = y[2 * u + 1];
+                        y[2 * u] = a0 * cs - a1 * sn;
+                        y[2 * u + 1] = a0 * sn + a1 * cs;
+                    }
+                };
+                auto rot_half = [&](int q, float (&ya)[8], float (&yb)[8]) {   // pairs 8q .. 8q + 7
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const int m = q * 8 + u;
+                        const float cs = cpre[m >> 2][m & 3], sn = spre[m >> 2][m & 3];
+                        const float a0 = ya[u], a1 = yb[u];
+                        ya[u] = a0 * cs - a1 * sn;
+                        yb[u] = a0 * sn + a1 * cs;
+                    }
+                };
                 float mean = 0.f, rstd = 1.f;
                 if (e.qk_norm) {
-                    float sum = 0.f;
+                    // pass 0: sum (LayerNorm only); pass 1: centred sum of squares
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        const floatx4 v0 = *(const floatx4 *)(src + qcol(q)), v1 = *(const floatx4 *)(src + qcol(q) + 4);
-                        sum += ((v0[0] + v0[1]) + (v0[2] + v0[3])) + ((v1[0] + v1[1]) + (v1[2] + v1[3]));
+                    for (int pass = 0; pass < 2; ++pass) {
+                        if (pass == 0 && RMS) continue;
+                        float acc_ = 0.f;
+                        auto add = [&](const float (&y)[8]) {
+#pragma unroll
+                            for (int u = 0; u < 8; ++u) acc_ += pass == 0 ? y[u] : (y[u] - mean) * (y[u] - mean);
+                        };
+                        if (!e.rope_half) {
+#pragma unroll
+                            for (int q = 0; q < 8; ++q) {
+                                float y[8];
+                                raw(q, y);
+                                if (rf) rot_il(q, y);
+                                add(y);
+                            }
+                        } else {
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                float ya[8], yb[8];
+                                raw(q, ya);
+                                raw(q + 4, yb);
+                                if (rf) rot_half(q, ya, yb);
+                                add(ya);
+                                add(yb);
+                            }
+                        }
+                        if (PARTS == 2) acc_ += __shfl_xor(acc_, 1, 64);
+                        if (pass == 0) mean = acc_ * (1.0f / HD);
+                        else rstd = rsqrtf(acc_ * (1.0f / HD) + e.eps);
                     }
-                    if (PARTS == 2) sum += __shfl_xor(sum, 1, 64);
-                    mean = sum * (1.0f / HD);
-                    float ss = 0.f;
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        const floatx4 v0 = *(const floatx4 *)(src + qcol(q)), v1 = *(const floatx4 *)(src + qcol(q) + 4);
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) ss += (v0[u] - mean) * (v0[u] - mean) + (v1[u] - mean) * (v1[u] - mean);
-                    }
-                    if (PARTS == 2) ss += __shfl_xor(ss, 1, 64);
-                    rstd = rsqrtf(ss * (1.0f / HD) + e.eps);
                 }
                 const float *g = gb + (sect == 0 ? 0 : 2 * HD);
                 const float *bb = g + HD;
-                // the 8 values of chunk q, normalised
-                auto chunk = [&](int q, float (&y)[8]) {
-                    const int c = qcol(q);
-                    const floatx4 v0 = *(const floatx4 *)(src + c), v1 = *(const floatx4 *)(src + c + 4);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) { y[u] = v0[u]; y[u + 4] = v1[u]; }
+                auto nrm = [&](int q, float (&y)[8]) {              // (y - mean) rstd gamma + beta
                     if (e.qk_norm) {
+                        const int c = qcol(q);
                         const floatx4 g0 = *(const floatx4 *)(g + c), g1 = *(const floatx4 *)(g + c + 4);
                         const floatx4 b0 = *(const floatx4 *)(bb + c), b1 = *(const floatx4 *)(bb + c + 4);
 #pragma unroll
@@ -484,33 +530,31 @@ struct EpiQkv {
                     }
                 };
                 if (!e.rope_half) {
-                    // interleaved: chunk q holds pairs 4q .. 4q + 3 of this lane
 #pragma unroll
                     for (int q = 0; q < 8; ++q) {
                         float y[8];
-                        chunk(q, y);
+                        raw(q, y);
+                        if (rf) { rot_il(q, y); nrm(q, y); } else { nrm(q, y); rot_il(q, y); }
 #pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            const int m = q * 4 + u;
-                            const float cs = cpre[m >> 2][m & 3], sn = spre[m >> 2][m & 3];
-                            o[q][2 * u] = f2bf(y[2 * u] * cs - y[2 * u + 1] * sn);
-                            o[q][2 * u + 1] = f2bf(y[2 * u] * sn + y[2 * u + 1] * cs);
-                        }
+                        for (int u = 0; u < 8; ++u) o[q][u] = f2bf(y[u]);
                     }
                 } else {
-                    // rotate-half: chunk q (first half) pairs with chunk q + 4
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         float ya[8], yb[8];
-                        chunk(q, ya);
-                        chunk(q + 4, yb);
-#pragma unroll
-                        for (int u = 0; u < 8; ++u) {
-                            const int m = q * 8 + u;
-                            const float cs = cpre[m >> 2][m & 3], sn = spre[m >> 2][m & 3];
-                            o[q][u] = f2bf(ya[u] * cs - yb[u] * sn);
-                            o[q + 4][u] = f2bf(ya[u] * sn + yb[u] * cs);
+                        raw(q, ya);
+                        raw(q + 4, yb);
+                        if (rf) {
+                            rot_half(q, ya, yb);
+                            nrm(q, ya);
+                            nrm(q + 4, yb);
+                        } else {
+                            nrm(q, ya);
+                            nrm(q + 4, yb);
+                            rot_half(q, ya, yb);
                         }
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) { o[q][u] = f2bf(ya[u]); o[q + 4][u] = f2bf(yb[u]); }
                     }
                 }
             } else {
@@ -597,33 +641,41 @@ static hipError_t run(const bf16 *a, const bf16 *w, int64_t M, int N_tile_cols, 
 
 template <typename TR, typename TO>
 static hipError_t residual_typed(const bf16 *a, const bf16 *w, int64_t M, int N, int K, const void *resid,
-                                 const float *gate, const float *bias, void *out, hipStream_t s) {
-    EpiResidual<TR, TO> epi{(const TR *)resid, gate, bias, (TO *)out, N};
+                                 const float *gate, int gate_fn, const float *bias, void *out, hipStream_t s) {
+    EpiResidual<TR, TO> epi{(const TR *)resid, gate, bias, (TO *)out, N, gate_fn};
     if (N % 256 == 0) return run<Tile8w>(a, w, M, N, K, RowsIdentity{256}, epi, s);
     return run<TileNarrow>(a, w, M, N, K, RowsIdentity{128}, epi, s);
 }
 
 hipError_t launch_gemm_residual(const bf16 *a, const bf16 *w, int64_t M, int N, int K, const void *resid,
-                                int resid_f32, const float *gate, const float *bias, void *out, int out_f32,
-                                hipStream_t s) {
+                                int resid_f32, const float *gate, int gate_fn, const float *bias, void *out,
+                                int out_f32, hipStream_t s) {
     if (resid_f32) {
-        return out_f32 ? residual_typed<float, float>(a, w, M, N, K, resid, gate, bias, out, s)
-                       : residual_typed<float, bf16>(a, w, M, N, K, resid, gate, bias, out, s);
+        return out_f32 ? residual_typed<float, float>(a, w, M, N, K, resid, gate, gate_fn, bias, out, s)
+                       : residual_typed<float, bf16>(a, w, M, N, K, resid, gate, gate_fn, bias, out, s);
     }
-    return out_f32 ? residual_typed<bf16, float>(a, w, M, N, K, resid, gate, bias, out, s)
-                   : residual_typed<bf16, bf16>(a, w, M, N, K, resid, gate, bias, out, s);
+    return out_f32 ? residual_typed<bf16, float>(a, w, M, N, K, resid, gate, gate_fn, bias, out, s)
+                   : residual_typed<bf16, bf16>(a, w, M, N, K, resid, gate, gate_fn, bias, out, s);
 }
 
-hipError_t launch_gemm_swiglu(const bf16 *a, const bf16 *w, int64_t M, int F, int K, bf16 *u, hipStream_t s) {
+hipError_t launch_gemm_swiglu(const bf16 *a, const bf16 *w, int64_t M, int F, int K, int act, bf16 *u,
+                              hipStream_t s) {
     using T = Tile8w;
-    return run<T>(a, w, M, 2 * F, K, RowsSwiglu{T::BN, T::kWaveN, F}, EpiSwiglu{u, F}, s);
+    if (act == 1) return run<T>(a, w, M, 2 * F, K, RowsSwiglu{T::BN, T::kWaveN, F}, EpiSwiglu<1>{u, F}, s);
+    return run<T>(a, w, M, 2 * F, K, RowsSwiglu{T::BN, T::kWaveN, F}, EpiSwiglu<0>{u, F}, s);
 }
 
 hipError_t launch_gemm_qkv(const bf16 *h, const bf16 *w, int64_t M, int N, int K, const QkvEpiArgs &e,
                            hipStream_t s) {
     using T = Tile8w;
-    if (e.head_dim == 128) return run<T>(h, w, M, N, K, RowsIdentity{T::BN}, EpiQkv<128>{e}, s);
-    return run<T>(h, w, M, N, K, RowsIdentity{T::BN}, EpiQkv<64>{e}, s);
+#define DIT_QKV(HD_, RMS_, RF_) run<T>(h, w, M, N, K, RowsIdentity{T::BN}, EpiQkv<HD_, RMS_, RF_>{e}, s)
+    if (e.head_dim == 128) {
+        if (e.rms) return e.rope_first ? DIT_QKV(128, true, true) : DIT_QKV(128, true, false);
+        return e.rope_first ? DIT_QKV(128, false, true) : DIT_QKV(128, false, false);
+    }
+    if (e.rms) return e.rope_first ? DIT_QKV(64, true, true) : DIT_QKV(64, true, false);
+    return e.rope_first ? DIT_QKV(64, false, true) : DIT_QKV(64, false, false);
+#undef DIT_QKV
 }
 
 }  // namespace dit

@@ -18,6 +18,10 @@ DIT_ERR_ALIGNMENT, DIT_ERR_NO_DEVICE, DIT_ERR_HIP = -4, -5, -6
 DIT_F32, DIT_BF16 = 0, 1
 DIT_LAYERNORM, DIT_RMSNORM = 0, 1
 DIT_ROPE_INTERLEAVED, DIT_ROPE_HALF = 0, 1
+DIT_ACT_SILU, DIT_ACT_GELU_TANH = 0, 1
+DIT_GATE_IDENTITY, DIT_GATE_TANH, DIT_GATE_SIGMOID = 0, 1, 2
+DIT_MOD_SHIFT_SCALE_GATE, DIT_MOD_SCALE_GATE = 0, 1
+DIT_QK_NORM_ROPE, DIT_QK_ROPE_NORM = 0, 1
 
 EXPORTED = (
     "dit_block_workspace_size", "dit_block_forward", "dit_stack_workspace_size", "dit_stack_step",
@@ -37,7 +41,8 @@ class DitError(RuntimeError):
 class dit_block_desc(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("batch", "seq", "hidden", "heads", "kv_heads", "head_dim", "ffn",
                                          "cond_dim", "qk_norm", "norm", "rope")] + \
-               [("eps", C.c_float), ("x_dtype", C.c_int32), ("w_dtype", C.c_int32)]
+               [("eps", C.c_float), ("x_dtype", C.c_int32), ("w_dtype", C.c_int32)] + \
+               [(n, C.c_int32) for n in ("act", "gate", "mod", "qk_order")]
 
 
 WEIGHT_FIELDS = ("w_ada", "b_ada", "ln1_g", "ln1_b", "ln2_g", "ln2_b", "w_qkv", "q_g", "q_b", "k_g", "k_b",
@@ -77,12 +82,12 @@ def lib():
             "dit_flowmatch_sigmas": (C.c_int, [i32, f32, vp]),
             "dit_rope_tables": (C.c_int, [vp, i32, i32, vp, i32, f32, i32, vp, vp]),
             "dit_adaln_modulation": (C.c_int, [vp, vp, vp, i32, i32, i32, vp, vp]),
-            "dit_ln_modulate": (C.c_int, [vp, i32, i64, i32, vp, vp, i32, f32, vp, vp]),
+            "dit_ln_modulate": (C.c_int, [vp, i32, i64, i32, i32, vp, vp, i32, f32, vp, vp]),
             "dit_qkv_rope": (C.c_int, [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
             "dit_seq_pad": (i32, [i32]),
             "dit_flash_attention": (C.c_int, [pd, vp, vp, vp, vp, vp]),
-            "dit_gemm_gated_residual": (C.c_int, [vp, vp, i64, i32, i32, vp, i32, vp, vp, vp, i32, vp]),
-            "dit_gemm_swiglu": (C.c_int, [vp, vp, i64, i32, i32, vp, vp]),
+            "dit_gemm_gated_residual": (C.c_int, [vp, vp, i64, i32, i32, vp, i32, vp, i32, vp, vp, i32, vp]),
+            "dit_gemm_swiglu": (C.c_int, [vp, vp, i64, i32, i32, i32, vp, vp]),
             "dit_status_string": (C.c_char_p, [C.c_int]),
             "dit_last_error": (C.c_char_p, []),
             "dit_version": (C.c_char_p, []),
@@ -136,9 +141,10 @@ def _check(rc: int):
 
 
 def make_desc(batch, seq, hidden, heads, kv_heads, head_dim, ffn, cond_dim, qk_norm=True, rope=DIT_ROPE_INTERLEAVED,
-              eps=1e-6, x_dtype=DIT_BF16, norm=DIT_LAYERNORM, w_dtype=DIT_BF16) -> dit_block_desc:
+              eps=1e-6, x_dtype=DIT_BF16, norm=DIT_LAYERNORM, w_dtype=DIT_BF16, act=DIT_ACT_SILU,
+              gate=DIT_GATE_IDENTITY, mod=DIT_MOD_SHIFT_SCALE_GATE, qk_order=DIT_QK_NORM_ROPE) -> dit_block_desc:
     return dit_block_desc(batch, seq, hidden, heads, kv_heads, head_dim, ffn, cond_dim, int(bool(qk_norm)), norm,
-                          rope, eps, x_dtype, w_dtype)
+                          rope, eps, x_dtype, w_dtype, act, gate, mod, qk_order)
 
 
 def make_weights(tensors: Dict[str, Any]) -> dit_block_weights:
@@ -244,8 +250,8 @@ def dit_adaln_modulation(w, b, c, out_dim, in_dim, silu_input, m, stream=None):
                                       _stream(stream)))
 
 
-def dit_ln_modulate(x, x_dtype, rows, dim, shift, scale, mode, eps, h, stream=None):
-    _check(lib().dit_ln_modulate(_p(x), int(x_dtype), int(rows), int(dim), _p(shift), _p(scale), int(mode),
+def dit_ln_modulate(x, x_dtype, rows, dim, shift, scale, mode, eps, h, stream=None, norm=DIT_LAYERNORM):
+    _check(lib().dit_ln_modulate(_p(x), int(x_dtype), int(rows), int(dim), int(norm), _p(shift), _p(scale), int(mode),
                                  float(eps), _p(h), _stream(stream)))
 
 
@@ -262,13 +268,14 @@ def dit_flash_attention(desc, q, k, vt, out, stream=None):
     _check(lib().dit_flash_attention(C.byref(desc), _p(q), _p(k), _p(vt), _p(out), _stream(stream)))
 
 
-def dit_gemm_gated_residual(a, w, M, N, K, resid, resid_dtype, gate, bias, out, out_dtype, stream=None):
+def dit_gemm_gated_residual(a, w, M, N, K, resid, resid_dtype, gate, bias, out, out_dtype, stream=None,
+                            gate_fn=DIT_GATE_IDENTITY):
     _check(lib().dit_gemm_gated_residual(_p(a), _p(w), int(M), int(N), int(K), _p(resid), int(resid_dtype), _p(gate),
-                                         _p(bias), _p(out), int(out_dtype), _stream(stream)))
+                                         int(gate_fn), _p(bias), _p(out), int(out_dtype), _stream(stream)))
 
 
-def dit_gemm_swiglu(a, w_gate_up, M, F, K, u, stream=None):
-    _check(lib().dit_gemm_swiglu(_p(a), _p(w_gate_up), int(M), int(F), int(K), _p(u), _stream(stream)))
+def dit_gemm_swiglu(a, w_gate_up, M, F, K, u, stream=None, act=DIT_ACT_SILU):
+    _check(lib().dit_gemm_swiglu(_p(a), _p(w_gate_up), int(M), int(F), int(K), int(act), _p(u), _stream(stream)))
 
 
 def dit_status_string(status: int) -> str:

@@ -45,7 +45,13 @@ def desc_of(cfg: I.DiTConfig, x_dtype: Optional[str] = None) -> N.dit_block_desc
     return N.make_desc(cfg.batch, cfg.seq, cfg.hidden, cfg.heads, cfg.kv_heads, cfg.head_dim, cfg.ffn, cfg.cond_dim,
                        qk_norm=cfg.qk_norm,
                        rope=N.DIT_ROPE_INTERLEAVED if cfg.rope == "interleaved3d" else N.DIT_ROPE_HALF,
-                       eps=cfg.eps, x_dtype=N.DIT_F32 if xd == "f32" else N.DIT_BF16)
+                       eps=cfg.eps, x_dtype=N.DIT_F32 if xd == "f32" else N.DIT_BF16,
+                       norm=N.DIT_RMSNORM if cfg.norm == "rmsnorm" else N.DIT_LAYERNORM,
+                       act=N.DIT_ACT_GELU_TANH if cfg.act == "gelu_tanh" else N.DIT_ACT_SILU,
+                       gate={"identity": N.DIT_GATE_IDENTITY, "tanh": N.DIT_GATE_TANH,
+                             "sigmoid": N.DIT_GATE_SIGMOID}[cfg.gate],
+                       mod=N.DIT_MOD_SCALE_GATE if cfg.mod == "scale_gate" else N.DIT_MOD_SHIFT_SCALE_GATE,
+                       qk_order=N.DIT_QK_ROPE_NORM if cfg.qk_order == "rope_norm" else N.DIT_QK_NORM_ROPE)
 
 
 def rope_tables(cfg: I.DiTConfig, pos: Optional[np.ndarray] = None, device="cuda"):

@@ -53,6 +53,21 @@ typedef enum { DIT_F32 = 0, DIT_BF16 = 1 } dit_dtype;
 typedef enum { DIT_LAYERNORM = 0, DIT_RMSNORM = 1 } dit_norm;
 /* RoPE pair layout: (2m, 2m+1) interleaved, or rotate-half (m, m + hd/2). */
 typedef enum { DIT_ROPE_INTERLEAVED = 0, DIT_ROPE_HALF = 1 } dit_rope;
+/* Feed-forward GLU activation on the gate half: SiLU (SwiGLU), or GELU in its
+ * tanh approximation with the argument clamped to +-20 and the result to
+ * +-65504 ([ERNIE] §IV "GELU(gate) x up, tanh approx, clamped", §V Bug 1). */
+typedef enum { DIT_ACT_SILU = 0, DIT_ACT_GELU_TANH = 1 } dit_act;
+/* Function applied to gate1 / gate2 before the gated residual r + f(g) y:
+ * identity ([ERNIE] §VII Decision 1), tanh or sigmoid ([ZML] §IV: the
+ * semantics search chooses between them per model). */
+typedef enum { DIT_GATE_IDENTITY = 0, DIT_GATE_TANH = 1, DIT_GATE_SIGMOID = 2 } dit_gate;
+/* AdaLN chunks: six (shift1, scale1, gate1, shift2, scale2, gate2) ([ERNIE]
+ * §IV), or four (scale1, gate1, scale2, gate2) with no shift ([ZML] §IV table:
+ * "[scale, gate], 1 + scale, no shift"). */
+typedef enum { DIT_MOD_SHIFT_SCALE_GATE = 0, DIT_MOD_SCALE_GATE = 1 } dit_mod;
+/* qk-norm before RoPE ([ZML] §VI "QKV + norm + RoPE"), or RoPE before the
+ * qk-norm ([ERNIE] §IV per-layer graph draws 3D RoPE, then qk_layernorm). */
+typedef enum { DIT_QK_NORM_ROPE = 0, DIT_QK_ROPE_NORM = 1 } dit_qk_order;
 
 /* Shape and semantic switches of one block.
  *   tokens N = batch * seq; attention runs within each sequence.
@@ -62,12 +77,17 @@ typedef enum { DIT_ROPE_INTERLEAVED = 0, DIT_ROPE_HALF = 1 } dit_rope;
  *     vector, LayerNorm without affine, gated residuals.
  *   cond_dim == 0: plain pre-norm block ([MAKEPAD] ViT): affine LayerNorm
  *     (ln*_g / ln*_b), gates fixed at 1.
- *   qk_norm: per-(token, head) LayerNorm of q and k over head_dim with the
- *     [head_dim] gamma/beta, applied before RoPE ([ZML] §VI "QKV + norm + RoPE").
- *   norm: only DIT_LAYERNORM is built (DIT_RMSNORM returns UNSUPPORTED).
+ *   qk_norm: per-(token, head) norm of q and k over head_dim with the
+ *     [head_dim] gamma/beta (order against RoPE: qk_order).
+ *   norm: kind of every norm of the block (the two pre-norms, the qk-norm and,
+ *     in a stack, the final norm): LayerNorm (x - mean) / sqrt(var + eps), or
+ *     RMSNorm x / sqrt(mean(x^2) + eps) ([ERNIE] §IV draws RMSNorm); the
+ *     optional gamma/beta are applied after either.
  *   eps: epsilon of every norm of the block.
  *   x_dtype: dtype of x and out (residual arithmetic is fp32 either way).
  *   w_dtype: must be DIT_BF16.
+ *   act, gate, mod, qk_order: the semantics switches above; 0 everywhere is
+ *     SwiGLU, identity gate, six chunks, norm before RoPE.
  * Built shapes: head_dim in {64, 128}; hidden % 256 == 0; ffn % 128 == 0;
  * (heads + 2 kv_heads) * head_dim % 256 == 0; cond_dim % 8 == 0; any seq >= 1
  * (ragged tails handled in every kernel). */
@@ -79,12 +99,17 @@ typedef struct {
     float eps;
     int32_t x_dtype;   /* dit_dtype */
     int32_t w_dtype;   /* dit_dtype */
+    int32_t act;       /* dit_act */
+    int32_t gate;      /* dit_gate */
+    int32_t mod;       /* dit_mod */
+    int32_t qk_order;  /* dit_qk_order */
 } dit_block_desc;
 
 /* Device pointers to one block's parameters (NULL where marked optional).
  *   w_ada  [6*hidden, cond_dim] bf16, b_ada [6*hidden] fp32: AdaLN linear whose
  *          output splits into (shift1, scale1, gate1, shift2, scale2, gate2)
- *          ([ERNIE] §IV).  Required iff cond_dim > 0.
+ *          ([ERNIE] §IV); [4*hidden, ...] split (scale1, gate1, scale2, gate2)
+ *          when mod is DIT_MOD_SCALE_GATE.  Required iff cond_dim > 0.
  *   ln1_g, ln1_b, ln2_g, ln2_b [hidden] fp32: affine of the pre-norms; used
  *          only when cond_dim == 0 (NULL = gamma 1 / beta 0); must be NULL in
  *          AdaLN mode.
@@ -114,11 +139,14 @@ int dit_block_workspace_size(const dit_block_desc *desc, size_t *bytes);
 /* out = block(x, cond) ([ERNIE] §IV per-layer compute graph, with the SwiGLU
  * feed-forward and the gated fp32 residual of §VII Decision 1):
  *   m   = W_ada SiLU(cond) + b_ada        -> shift1 scale1 gate1 shift2 scale2 gate2
- *   h   = LN(x) (1 + scale1) + shift1     (bf16)
- *   q,k,v = h W_qkv^T; q,k <- RoPE(qkLN(q,k))          (bf16)
- *   x1  = x + gate1 * (softmax(q k^T / sqrt(hd)) v  W_o^T)   (fp32)
- *   h2  = LN(x1) (1 + scale2) + shift2    (bf16)
- *   out = x1 + gate2 * ((SiLU(h2 Wg^T) * (h2 Wu^T)) W_down^T)
+ *   h   = N(x) (1 + scale1) + shift1      (bf16)
+ *   q,k,v = h W_qkv^T; q,k <- RoPE(qkN(q,k))           (bf16)
+ *   x1  = x + f(gate1) * (softmax(q k^T / sqrt(hd)) v  W_o^T)   (fp32)
+ *   h2  = N(x1) (1 + scale2) + shift2     (bf16)
+ *   out = x1 + f(gate2) * ((act(h2 Wg^T) * (h2 Wu^T)) W_down^T)
+ * with the defaults N = LayerNorm, qkN before RoPE, f = identity, act = SiLU,
+ * and the desc switches norm / qk_order / gate / act / mod (no shift chunks
+ * with DIT_MOD_SCALE_GATE).
  * x, out: device [batch*seq, hidden] of desc->x_dtype; out may equal x
  *   (in-place residual, [MAKEPAD]); any other overlap is INVALID_ARG.
  * cond: device fp32 [cond_dim] (NULL iff cond_dim == 0).
@@ -248,12 +276,14 @@ int dit_rope_tables(const int32_t *pos, int32_t seq, int32_t rope, const int32_t
 int dit_adaln_modulation(const void *w, const float *b, const float *c, int32_t out_dim,
                          int32_t in_dim, int32_t silu_input, float *m, void *stream);
 
-/* Row LayerNorm + modulation to bf16: h = LN(x) * mul + add, where
- * mode 0: mul = 1 + scale, add = shift (AdaLN; scale/shift fp32 [dim], required);
- * mode 1: mul = scale, add = shift (affine LN; either may be NULL = 1 / 0).
+/* Row norm + modulation to bf16: h = norm(x) * mul + add, norm = LayerNorm or
+ * RMSNorm (dit_norm), where
+ * mode 0: mul = 1 + scale, add = shift (AdaLN; scale fp32 [dim] required,
+ *         shift fp32 [dim] or NULL = 0 for the no-shift modulation);
+ * mode 1: mul = scale, add = shift (affine norm; either may be NULL = 1 / 0).
  * x device [rows, dim] of x_dtype; h device bf16 [rows, dim]; dim % 256 == 0,
  * dim <= 8192. */
-int dit_ln_modulate(const void *x, int32_t x_dtype, int64_t rows, int32_t dim,
+int dit_ln_modulate(const void *x, int32_t x_dtype, int64_t rows, int32_t dim, int32_t norm,
                     const float *shift, const float *scale, int32_t mode, float eps,
                     void *h, void *stream);
 
@@ -278,20 +308,24 @@ int32_t dit_seq_pad(int32_t seq);
 int dit_flash_attention(const dit_block_desc *desc, const void *q, const void *k,
                         const void *vt, void *out, void *stream);
 
-/* out = resid + gate * (a W^T) + bias over an [M, N] output:
+/* out = resid + f(gate) * (a W^T) + bias over an [M, N] output, f = the gate
+ * function gate_fn (dit_gate):
  * a device bf16 [M, K]; W device bf16 [N, K]; resid device [M, N] of
- * resid_dtype or NULL; gate, bias device fp32 [N] or NULL (gate NULL = 1,
- * bias NULL = 0); out device [M, N] of out_dtype (may equal resid).
+ * resid_dtype or NULL; gate, bias device fp32 [N] or NULL (gate NULL = 1
+ * whatever gate_fn, bias NULL = 0); out device [M, N] of out_dtype (may equal
+ * resid).
  * N % 128 == 0, K % 64 == 0.  ([ERNIE] §VII Decision 1: gated residual with
  * fp32 accumulation; out-projection and down-projection epilogue.) */
 int dit_gemm_gated_residual(const void *a, const void *w, int64_t M, int32_t N, int32_t K,
                             const void *resid, int32_t resid_dtype, const float *gate,
-                            const float *bias, void *out, int32_t out_dtype, void *stream);
+                            int32_t gate_fn, const float *bias, void *out, int32_t out_dtype,
+                            void *stream);
 
-/* u = SiLU(a Wg^T) * (a Wu^T) with W = [Wg; Wu] device bf16 [2F, K];
- * a device bf16 [M, K]; u device bf16 [M, F].  F % 128 == 0, K % 64 == 0. */
+/* u = act(a Wg^T) * (a Wu^T) with W = [Wg; Wu] device bf16 [2F, K], act =
+ * SiLU or the clamped GELU-tanh (dit_act); a device bf16 [M, K]; u device
+ * bf16 [M, F].  F % 128 == 0, K % 64 == 0. */
 int dit_gemm_swiglu(const void *a, const void *w_gate_up, int64_t M, int32_t F, int32_t K,
-                    void *u, void *stream);
+                    int32_t act, void *u, void *stream);
 
 /* ------------------------------------------------------------------------ */
 const char *dit_status_string(int status);

@@ -50,4 +50,17 @@ SMALL = {
     # joint text + image sequences: 256 spatial + 7 text tokens, both orders
     "tiny_joint": I.C1_JOINT,
     "tiny_joint_text_first": I.C1_JOINT_TF,
+    # semantics switches, one at a time and in combination
+    "c1_rms": I.C1.replace(name="c1_rms", cfg_id=15, norm="rmsnorm"),
+    "c1_gelu": I.C1.replace(name="c1_gelu", cfg_id=16, act="gelu_tanh"),
+    "c1_gate_tanh": I.C1.replace(name="c1_gate_tanh", cfg_id=17, gate="tanh"),
+    "c1_gate_sigmoid": I.C1.replace(name="c1_gate_sigmoid", cfg_id=18, gate="sigmoid"),
+    "c1_scale_gate": I.C1.replace(name="c1_scale_gate", cfg_id=19, mod="scale_gate"),
+    "c1_rope_first": I.C1.replace(name="c1_rope_first", cfg_id=21, qk_order="rope_norm"),
+    "hd128_ernie_diagram": I.DiTConfig("hd128_ernie_diagram", 22, 1, (1, 20, 20), 512, 4, 4, 128, 1024, 256, True,
+                                       "interleaved3d", (32, 48, 48), 256.0, x_dtype="f32", norm="rmsnorm",
+                                       act="gelu_tanh", qk_order="rope_norm"),
+    "half_hd128_rope_first": I.DiTConfig("half_hd128_rope_first", 23, 2, (1, 12, 16), 512, 4, 2, 128, 1024, 256, True,
+                                         "half2d", (64, 64), 100.0, x_dtype="bf16", qk_order="rope_norm"),
+    "qwen_like": I.C1.replace(name="qwen_like", cfg_id=24, gate="tanh", mod="scale_gate", x_dtype="f32"),
 }

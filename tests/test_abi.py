@@ -50,6 +50,12 @@ def _desc(**kw):
     return N.make_desc(**d)
 
 
+def test_desc_accepts_every_semantics_switch():
+    for kw in (dict(norm=N.DIT_RMSNORM), dict(act=N.DIT_ACT_GELU_TANH), dict(gate=N.DIT_GATE_TANH),
+               dict(gate=N.DIT_GATE_SIGMOID), dict(mod=N.DIT_MOD_SCALE_GATE), dict(qk_order=N.DIT_QK_ROPE_NORM)):
+        assert N.dit_block_workspace_size(_desc(**kw)) > 0
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(hidden=320, heads=5, kv_heads=5), N.DIT_ERR_UNSUPPORTED),   # hidden % 256
     (dict(heads=3), N.DIT_ERR_INVALID_ARG),                   # heads*hd != hidden
@@ -59,7 +65,12 @@ def _desc(**kw):
     (dict(seq=0), N.DIT_ERR_INVALID_ARG),
     (dict(cond_dim=12), N.DIT_ERR_UNSUPPORTED),
     (dict(eps=0.0), N.DIT_ERR_INVALID_ARG),
-    (dict(norm=N.DIT_RMSNORM), N.DIT_ERR_UNSUPPORTED),
+    (dict(norm=2), N.DIT_ERR_INVALID_ARG),
+    (dict(act=2), N.DIT_ERR_INVALID_ARG),
+    (dict(gate=3), N.DIT_ERR_INVALID_ARG),
+    (dict(gate=-1), N.DIT_ERR_INVALID_ARG),
+    (dict(mod=2), N.DIT_ERR_INVALID_ARG),
+    (dict(qk_order=2), N.DIT_ERR_INVALID_ARG),
     (dict(w_dtype=N.DIT_F32), N.DIT_ERR_UNSUPPORTED),
 ])
 def test_desc_validation(kw, status):
@@ -141,7 +152,17 @@ def test_stage_entry_validation():
         N.dit_ln_modulate(FAKE, 0, 10, 300, FAKE, FAKE, 0, 1e-6, FAKE + (1 << 24), stream=0)
     assert e.value.status == N.DIT_ERR_UNSUPPORTED
     with pytest.raises(N.DitError) as e:
-        N.dit_ln_modulate(FAKE, 0, 10, 256, None, FAKE, 0, 1e-6, FAKE + (1 << 24), stream=0)
+        N.dit_ln_modulate(FAKE, 0, 10, 256, FAKE, None, 0, 1e-6, FAKE + (1 << 24), stream=0)   # mode 0 needs scale
+    assert e.value.status == N.DIT_ERR_INVALID_ARG
+    with pytest.raises(N.DitError) as e:
+        N.dit_ln_modulate(FAKE, 0, 10, 256, FAKE, FAKE, 0, 1e-6, FAKE + (1 << 24), stream=0, norm=7)
+    assert e.value.status == N.DIT_ERR_INVALID_ARG
+    with pytest.raises(N.DitError) as e:
+        N.dit_gemm_gated_residual(FAKE, FAKE, 256, 256, 64, None, 0, FAKE, None, FAKE + (1 << 24), 0, stream=0,
+                                  gate_fn=3)
+    assert e.value.status == N.DIT_ERR_INVALID_ARG
+    with pytest.raises(N.DitError) as e:
+        N.dit_gemm_swiglu(FAKE, FAKE, 256, 128, 64, FAKE + (1 << 24), stream=0, act=2)
     assert e.value.status == N.DIT_ERR_INVALID_ARG
     with pytest.raises(N.DitError) as e:
         N.euler_flowmatch_update(FAKE, FAKE + 8, 64, 1.0, 0.5, stream=0)

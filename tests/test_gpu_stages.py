@@ -68,6 +68,31 @@ def test_ln_modulate(rows, dim, xdt, mode):
     assert_parity(got, ref, max_rel=4e-3, min_cos=0.99999, what="ln_modulate")
 
 
+@pytest.mark.parametrize("rows,dim,xdt,mode,shift", [(300, 256, "f32", 0, True), (257, 4096, "bf16", 0, False),
+                                                     (64, 1024, "f32", 1, True)])
+def test_ln_modulate_rmsnorm(rows, dim, xdt, mode, shift):
+    """RMSNorm rows (no centring) and the no-shift modulation (shift NULL)."""
+    import torch
+    say(f"ln_modulate RMSNorm rows={rows} dim={dim} x={xdt} mode={mode} shift={shift}")
+    r = _rng(12)
+    x = (r.standard_normal((rows, dim), dtype=np.float32) * 3 + 0.5).astype(np.float32)
+    if xdt == "bf16":
+        x = I.bf16_round(x)
+    sh = (r.standard_normal(dim) * 0.5).astype(np.float32) if shift else None
+    sc = (r.standard_normal(dim) * 0.5).astype(np.float32)
+    xd = R.to_dev_f32(x) if xdt == "f32" else R.to_dev_bf16(x)
+    h = torch.empty((rows, dim), dtype=torch.bfloat16, device="cuda")
+    N.dit_ln_modulate(xd, N.DIT_F32 if xdt == "f32" else N.DIT_BF16, rows, dim, R.to_dev_f32(sh), R.to_dev_f32(sc),
+                      mode, 1e-6, h, norm=N.DIT_RMSNORM)
+    _sync()
+    n = O.rms_norm(x.astype(np.float64), 1e-6)
+    add = 0.0 if sh is None else sh
+    ref = O.modulate(n, add, sc) if mode == 0 else n * sc + add
+    got = R.to_host_f32(h)
+    assert (np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5).all()
+    assert_parity(got, ref, max_rel=4e-3, min_cos=0.99999, what="ln_modulate rms")
+
+
 # ---------------------------------------------------------------------------
 def _qkv_case(cfg, seed=3):
     """Random bf16 h and block weights with a non-trivial qk-norm affine."""
@@ -77,7 +102,8 @@ def _qkv_case(cfg, seed=3):
     return h, w
 
 
-@pytest.mark.parametrize("name", ["c1_tiny", "c1_ragged200", "hd128_ragged400", "gqa3_b2_ragged300", "vit_b2_f32",
+@pytest.mark.parametrize("name", ["c1_rms", "c1_rope_first", "hd128_ernie_diagram", "half_hd128_rope_first",
+                                  "c1_tiny", "c1_ragged200", "hd128_ragged400", "gqa3_b2_ragged300", "vit_b2_f32",
                                   "c1_f32x_t3"])
 def test_qkv_rope(name):
     import torch
@@ -185,6 +211,23 @@ def test_gemm_gated_residual(M, Nn, K, rdt, odt, gate, bias):
     assert_parity(R.to_host_f32(out), ref, max_rel=tol, min_cos=0.99999, what="gemm_residual")
 
 
+@pytest.mark.parametrize("gate_fn,kind", [(N.DIT_GATE_TANH, "tanh"), (N.DIT_GATE_SIGMOID, "sigmoid")])
+def test_gemm_gated_residual_gate_functions(gate_fn, kind):
+    import torch
+    M, Nn, K = 300, 512, 320
+    r = _rng(13)
+    a = I.bf16_round(r.standard_normal((M, K), dtype=np.float32))
+    w = I.bf16_round(r.standard_normal((Nn, K), dtype=np.float32) * 0.05)
+    res = r.standard_normal((M, Nn), dtype=np.float32)
+    g = (r.standard_normal(Nn, dtype=np.float32) * 3).astype(np.float32)
+    out = torch.empty((M, Nn), dtype=torch.float32, device="cuda")
+    N.dit_gemm_gated_residual(R.to_dev_bf16(a), R.to_dev_bf16(w), M, Nn, K, R.to_dev_f32(res), N.DIT_F32,
+                              R.to_dev_f32(g), None, out, N.DIT_F32, gate_fn=gate_fn)
+    _sync()
+    ref = O.gated_residual(res, O.gate_fn(g.astype(np.float64), kind), O.linear(a, w))
+    assert_parity(R.to_host_f32(out), ref, max_rel=1e-5, min_cos=0.99999, what=f"gated residual {kind}")
+
+
 def test_gemm_residual_in_place_and_identity():
     """W = I gives y = a exactly; resid == out (in place) is legal."""
     import torch
@@ -210,6 +253,27 @@ def test_gemm_swiglu(M, F, K):
     N.dit_gemm_swiglu(R.to_dev_bf16(a), R.to_dev_bf16(w), M, F, K, u)
     _sync()
     assert_parity(R.to_host_f32(u), O.swiglu(a, w), max_rel=8e-3, min_cos=0.99999, what="swiglu")
+
+
+def test_gemm_glu_gelu_tanh_with_clamps():
+    """The clamped GELU-tanh GLU; one block of rows is scaled so that gate
+    projections reach the tanh-argument clamp and the +-65504 output clamp."""
+    import torch
+    M, F, K = 300, 384, 256
+    r = _rng(14)
+    a = r.standard_normal((M, K), dtype=np.float32)
+    a[:32] *= 3e3                     # |gate| ~ 1e5 on these rows: both clamps engage
+    a[32:64] *= 8.0                   # |gate| ~ 20: the tanh argument clamp
+    a = I.bf16_round(a)
+    w = I.bf16_round(r.standard_normal((2 * F, K), dtype=np.float32) * 0.08)
+    u = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    N.dit_gemm_swiglu(R.to_dev_bf16(a), R.to_dev_bf16(w), M, F, K, u, act=N.DIT_ACT_GELU_TANH)
+    _sync()
+    got = R.to_host_f32(u)
+    ref = O.swiglu(a, w, act="gelu_tanh")
+    assert np.isfinite(got).all()
+    for sl, what in ((slice(0, 32), "clamped rows"), (slice(32, 64), "large rows"), (slice(64, M), "normal rows")):
+        assert_parity(got[sl], ref[sl], max_rel=8e-3, min_cos=0.99999, what=f"gelu glu {what}")
 
 
 # ---------------------------------------------------------------------------
