@@ -625,7 +625,32 @@ struct EpiQkv {
 // 8 waves (2 per SIMD, 128x64 each): two waves per SIMD let one wave's LDS
 // waits overlap the other's MFMAs.
 using Tile8w = Tile<256, 256, 2, 4>;
+using Tile8wTall = Tile<320, 256, 2, 4>;   // 160 x 64 per wave: ragged row counts just above a multiple of 256
 using TileNarrow = Tile<256, 128, 2, 2>;   // N = 128 outputs (the projection to latent channels)
+
+// Compute units of the current device (one 256 x 256 tile runs per CU at a time).
+static int cu_count() {
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            n = v;
+        else
+            n = 256;
+    }
+    return n;
+}
+
+// Tile height for an M x N output of 256-wide column tiles: the 320-row tile
+// when it needs fewer rounds of workgroups over the CUs than the 256-row one
+// costs extra time per tile (e.g. 4170 rows x 4096 columns: 224 tiles in one
+// round instead of 272 in two).
+static bool prefer_tall(int64_t M, int N) {
+    const int64_t cus = cu_count(), tn = N / 256;
+    const int64_t r256 = ((M + 255) / 256 * tn + cus - 1) / cus;
+    const int64_t r320 = ((M + 319) / 320 * tn + cus - 1) / cus;
+    return r320 * 320 < r256 * 256;
+}
 
 template <class T, class RowMap, class Epi>
 static hipError_t run(const bf16 *a, const bf16 *w, int64_t M, int N_tile_cols, int K, RowMap rm, Epi epi,
@@ -643,6 +668,7 @@ template <typename TR, typename TO>
 static hipError_t residual_typed(const bf16 *a, const bf16 *w, int64_t M, int N, int K, const void *resid,
                                  const float *gate, int gate_fn, const float *bias, void *out, hipStream_t s) {
     EpiResidual<TR, TO> epi{(const TR *)resid, gate, bias, (TO *)out, N, gate_fn};
+    if (N % 256 == 0 && prefer_tall(M, N)) return run<Tile8wTall>(a, w, M, N, K, RowsIdentity{256}, epi, s);
     if (N % 256 == 0) return run<Tile8w>(a, w, M, N, K, RowsIdentity{256}, epi, s);
     return run<TileNarrow>(a, w, M, N, K, RowsIdentity{128}, epi, s);
 }

@@ -186,6 +186,7 @@ def test_flash_attention_closed_forms():
     (513, 256, 768, "f32", "bf16", False, False),
     (100, 128, 256, None, "f32", False, True),        # narrow N tile, no residual
     (4096, 384, 128, None, "f32", False, True),       # patch-embed-like K = 128
+    (4170, 4096, 256, "f32", "f32", True, True),      # ragged rows: the 320-row tile (one round of tiles)
 ])
 def test_gemm_gated_residual(M, Nn, K, rdt, odt, gate, bias):
     import torch
