@@ -65,6 +65,9 @@ class DiTConfig:
     gate: str = "identity"           # gate function: "identity" | "tanh" | "sigmoid"
     mod: str = "shift_scale_gate"    # AdaLN chunks: "shift_scale_gate" (6D) | "scale_gate" (4D, no shift)
     qk_order: str = "norm_rope"      # "norm_rope" | "rope_norm"
+    # format of the four block projections: "bf16", or "w8a8_h256" (int8 codes
+    # of both operands after a 256-point Hadamard rotation, one scale per row)
+    fmt: str = "bf16"
 
     @property
     def spatial(self) -> int:
@@ -111,7 +114,13 @@ C3_JOINT = C3.replace(name="block_8b_joint", cfg_id=6, text_len=74)
 C1_JOINT = C1.replace(name="tiny_joint", cfg_id=7, text_len=7)
 C1_JOINT_TF = C1_JOINT.replace(name="tiny_joint_text_first", text_first=True)
 
-CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5_4096, C5_1024, C3_JOINT, C1_JOINT, C1_JOINT_TF)}
+# the W8A8 H256 format of the zml-flow-rs page (§VII) on the same shapes (same data)
+C1_W8A8 = C1.replace(name="tiny_block_w8a8", fmt="w8a8_h256")
+C3_W8A8 = C3.replace(name="block_8b_w8a8", fmt="w8a8_h256")
+C4_W8A8 = C4.replace(name="stack_8b_w8a8", fmt="w8a8_h256")
+
+CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5_4096, C5_1024, C3_JOINT, C1_JOINT, C1_JOINT_TF,
+                               C1_W8A8, C3_W8A8, C4_W8A8)}
 
 STACK_STEPS = 8
 STACK_SHIFT = 4.0

@@ -28,7 +28,9 @@ kv_heads, head_dim, cond_dim, qk_norm, rope ("interleaved3d" | "half2d"),
 rope_axes, rope_theta, eps, and optionally the semantics switches the pages
 disagree on (defaults in brackets): norm ["layernorm"] | "rmsnorm"; act
 ["silu"] | "gelu_tanh"; gate ["identity"] | "tanh" | "sigmoid"; mod
-["shift_scale_gate"] | "scale_gate"; qk_order ["norm_rope"] | "rope_norm".
+["shift_scale_gate"] | "scale_gate"; qk_order ["norm_rope"] | "rope_norm";
+fmt ["bf16"] | "w8a8_h256" (the four block projections in int8 with a
+256-point Hadamard rotation on both operands, per-row scales).
 
 Parity status: every function here is pinned by a closed form, an invariant,
 a special case or a brute-force loop in tests/test_oracle.py, except the
@@ -134,6 +136,93 @@ def swiglu(h, w_gate_up, dtype=F64, act="silu"):
     F = w.shape[0] // 2
     f = silu if act == "silu" else gelu_tanh
     return f(linear(h, w[:F], dtype=dtype)) * linear(h, w[F:], dtype=dtype)
+
+
+# ---------------------------------------------------------------------------
+# W8A8 with a 256-point Hadamard rotation on both operands ([ZML] §VII
+# "Precision Formats Derived, Not Picked": the I8 per-row format with H256 on
+# both sides, legal by rotation invariance (x H)(W H)^T = x W^T for orthogonal H)
+# ---------------------------------------------------------------------------
+ROT_BLOCK = 256
+QMAX = 127
+
+
+def hadamard(n):
+    """Normalised Sylvester-Hadamard matrix of order n (a power of two), built
+    by doubling [[H, H], [H, -H]]; entry (a, b) is (-1)^popcount(a & b) / sqrt(n).
+    Orthogonal and symmetric."""
+    h = np.ones((1, 1), F64)
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h / np.sqrt(n)
+
+
+def rotate_h256(x):
+    """x [..., K] times blockdiag(H256, ..., H256) along the last axis (K a
+    multiple of 256): every consecutive run of 256 inputs is rotated on its own
+    (a reading: the page names H256 but not its placement along K)."""
+    x = np.asarray(x, F64)
+    K = x.shape[-1]
+    assert K % ROT_BLOCK == 0, "reduction length must be a multiple of 256"
+    blocks = x.reshape(x.shape[:-1] + (K // ROT_BLOCK, ROT_BLOCK))
+    return (blocks @ hadamard(ROT_BLOCK)).reshape(x.shape)
+
+
+def quantize_rows(v):
+    """Symmetric per-row int8 codes ("I8 per-row"): amax = max |v| over the
+    row, scale = amax / 127, code = v * (127 / amax) rounded half to even and
+    clamped to [-127, 127]; a zero row has codes 0 and scale 0.
+
+    The code is an integer decided by floating point, so it is decided in
+    float32, the precision the device kernels use: v is rounded to float32,
+    and 127 / amax, the product and amax / 127 are each rounded to float32.
+    Returns (codes int8 [..., K], scale float32 [...])."""
+    v32 = np.asarray(v, np.float32)
+    amax = np.abs(v32).max(axis=-1, keepdims=True)
+    safe = np.where(amax > 0, amax, np.float32(1))
+    inv = np.where(amax > 0, np.float32(QMAX) / safe, np.float32(0)).astype(np.float32)
+    q = np.clip(np.rint((v32 * inv).astype(np.float32)), -QMAX, QMAX).astype(np.int8)
+    scale = (amax[..., 0] / np.float32(QMAX)).astype(np.float32)
+    return q, scale
+
+
+def quantize_h256(x):
+    """Rotate then quantize per row: the form both the weights [out, in] (one
+    scale per output channel, prepared once) and the activations [tokens, in]
+    (one scale per token) take."""
+    return quantize_rows(rotate_h256(x))
+
+
+def w8a8_matmul(qx, sx, qw, sw):
+    """y[m, n] = sx[m] sw[n] sum_k qx[m, k] qw[n, k]: the integer products are
+    summed exactly (int64), then scaled in float64."""
+    acc = np.asarray(qx, np.int64) @ np.asarray(qw, np.int64).T
+    return acc.astype(F64) * np.asarray(sx, F64)[:, None] * np.asarray(sw, F64)[None, :]
+
+
+def w8a8_linear(x, w):
+    """y ~ x W^T in the W8A8 H256 format: both x [M, K] and W [N, K] rotated
+    and quantized per row.  `w` is the weight matrix or its prepared
+    (codes, scales) pair."""
+    qw, sw = w if isinstance(w, tuple) else quantize_h256(w)
+    qx, sx = quantize_h256(x)
+    return w8a8_matmul(qx, sx, qw, sw)
+
+
+def block_linear(x, w, name, spec, dtype=F64):
+    """One of the block's four projections (w_qkv, w_o, w_gate_up, w_down) in
+    the block's format: spec.fmt "bf16" (default; plain x W^T) or "w8a8_h256".
+    In the W8A8 format `w` may hold the prepared pair under name + "_q8"."""
+    if getattr(spec, "fmt", "bf16") == "w8a8_h256":
+        return np.asarray(w8a8_linear(x, w.get(name + "_q8") or w[name]), dtype)
+    return linear(x, w[name], dtype=dtype)
+
+
+def glu(gu, act="silu"):
+    """act(gate) * up for gu = [gate | up] along the last axis (gate first)."""
+    F = gu.shape[-1] // 2
+    f = silu if act == "silu" else gelu_tanh
+    return f(gu[..., :F]) * gu[..., F:]
 
 
 # ---------------------------------------------------------------------------
@@ -269,7 +358,7 @@ def block_qkv(h, w, spec, pos, dtype=F64):
     qk_layernorm (qk_order "rope_norm").  Returns q [N,H,hd], k/v [N,Hkv,hd]."""
     H, Hk, hd = spec.heads, spec.kv_heads, spec.head_dim
     N = h.shape[0]
-    qkv = linear(h, w["w_qkv"], dtype=dtype)
+    qkv = block_linear(h, w, "w_qkv", spec, dtype)
     q = qkv[:, : H * hd].reshape(N, H, hd)
     k = qkv[:, H * hd: (H + Hk) * hd].reshape(N, Hk, hd)
     v = qkv[:, (H + Hk) * hd:].reshape(N, Hk, hd)
@@ -320,10 +409,10 @@ def block_forward(x, c, w, spec, pos, dtype=F64, rows=None, keep=None):
             continue
         sl = slice(b * S, (b + 1) * S)
         att[sel] = attention(q[sl], k[sl], v[sl], spec.heads, spec.kv_heads, rows[sel] - b * S)
-    x1 = gated_residual(x[rows], gate1, linear(att, w["w_o"], dtype=dtype))
+    x1 = gated_residual(x[rows], gate1, block_linear(att, w, "w_o", spec, dtype))
     h2 = _prenorm(x1, w, "ln2", shift2, scale2, spec, dtype)
-    ff = swiglu(h2, w["w_gate_up"], dtype, getattr(spec, "act", "silu"))
-    out = gated_residual(x1, gate2, linear(ff, w["w_down"], dtype=dtype))
+    ff = glu(block_linear(h2, w, "w_gate_up", spec, dtype), getattr(spec, "act", "silu"))
+    out = gated_residual(x1, gate2, block_linear(ff, w, "w_down", spec, dtype))
     if keep is not None:
         keep.update(dict(mods=(shift1, scale1, gate1, shift2, scale2, gate2), h=h, q=q, k=k, v=v,
                          att=att, x1=x1, h2=h2, ff=ff, out=out))

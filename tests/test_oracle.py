@@ -567,3 +567,128 @@ def test_qk_order_rope_then_norm():
     a = O.block_forward(x, c, w, cfg.replace(qk_order="rope_norm"), pos)
     b = O.block_forward(x, c, w, cfg, pos)
     assert np.abs((a - x) - (b - x)).max() > 1e-3 * np.abs(b - x).max()
+
+
+# ---------------------------------------------------------------------------
+# W8A8 with the 256-point Hadamard rotation (zml-flow-rs page §VII)
+# ---------------------------------------------------------------------------
+def test_hadamard_is_the_library_sylvester_matrix():
+    from scipy.linalg import hadamard as sylvester
+    H = O.hadamard(256)
+    np.testing.assert_array_equal(H * 16.0, sylvester(256).astype(np.float64))
+    np.testing.assert_array_equal(H, H.T)
+    np.testing.assert_array_equal(H @ H.T, np.eye(256))   # entries +-1/16: every product and sum is exact
+
+
+def test_rotation_is_blockwise_and_orthogonal():
+    r = np.random.default_rng(41)
+    x, w = r.standard_normal((5, 768)), r.standard_normal((7, 768))
+    # rotation invariance (x H)(W H)^T = x W^T, the identity the format rests on
+    np.testing.assert_allclose(O.rotate_h256(x) @ O.rotate_h256(w).T, x @ w.T, rtol=1e-12, atol=1e-11)
+    # each run of 256 inputs is rotated on its own: a unit input at offset 5 of
+    # the second run becomes row 5 of H256 in that run only, by the sign formula
+    e = np.zeros(768)
+    e[256 + 5] = 1.0
+    got = O.rotate_h256(e)
+    assert not got[:256].any() and not got[512:].any()
+    expect = np.array([(-1.0) ** bin(5 & j).count("1") / 16.0 for j in range(256)])
+    np.testing.assert_array_equal(got[256:512], expect)
+    # a constant run maps to (16 c, 0, ..., 0)
+    c = np.full(256, 0.75)
+    np.testing.assert_array_equal(O.rotate_h256(c), np.r_[16 * 0.75, np.zeros(255)])
+
+
+def test_quantize_rows_closed_form():
+    v = np.zeros((3, 8), np.float32)
+    v[0, :4] = [1.0, -0.5, 0.25, 0.125]   # amax 1: 127, -63.5 -> -64 (half to even), 31.75 -> 32, 15.875 -> 16
+    v[1, :3] = [-2.0, 1.0, 0.0]           # amax 2 at a negative value: -127, 63.5 -> 64 (half to even), 0
+    q, s = O.quantize_rows(v)
+    assert q.dtype == np.int8 and s.dtype == np.float32
+    np.testing.assert_array_equal(q[0, :4], [127, -64, 32, 16])
+    np.testing.assert_array_equal(q[1, :3], [-127, 64, 0])
+    assert not q[2].any() and s[2] == 0.0                      # a zero row
+    assert s[0] == np.float32(1.0) / np.float32(127.0) and s[1] == np.float32(2.0) / np.float32(127.0)
+
+
+def test_quantize_rows_range_and_half_step_error():
+    r = np.random.default_rng(43)
+    v = r.standard_normal((64, 512)) * np.exp(2.0 * r.standard_normal((64, 1)))
+    q, s = O.quantize_rows(v)
+    assert np.abs(q.astype(int)).max() == 127
+    i = np.abs(v.astype(np.float32)).argmax(axis=1)
+    np.testing.assert_array_equal(np.abs(q[np.arange(64), i].astype(int)), 127)   # the row max maps to +-127
+    assert (np.sign(q) * np.sign(v) >= 0).all()                                    # no sign flips
+    err = np.abs(q * s[:, None].astype(np.float64) - v)
+    assert (err <= s[:, None] * (0.5 + 1e-4)).all()                                 # within half a step
+
+
+def _bf_rot(row):
+    out = []
+    for b0 in range(0, len(row), 256):
+        for j in range(256):
+            acc = 0.0
+            for a in range(256):
+                acc += row[b0 + a] if bin(a & j).count("1") % 2 == 0 else -row[b0 + a]
+            out.append(acc / 16.0)
+    return out
+
+
+def _bf_quant(row):
+    v = [np.float32(t) for t in row]
+    amax = max(abs(t) for t in v)
+    inv = np.float32(127.0) / amax
+    codes = [max(-127, min(127, round(float(np.float32(t * inv))))) for t in v]   # round(): half to even
+    return codes, float(amax / np.float32(127.0))
+
+
+def test_w8a8_linear_brute_force():
+    """The W8A8 H256 product from scalar loops: rotation from the sign formula,
+    codes from per-element float32 steps, integer dot products in Python ints."""
+    r = np.random.default_rng(47)
+    x = r.standard_normal((3, 512))
+    w = r.standard_normal((2, 512)) * 0.02
+    qx = [_bf_quant(_bf_rot(list(row))) for row in x]
+    qw = [_bf_quant(_bf_rot(list(row))) for row in w]
+    ref = np.array([[sx * sw * sum(a * b for a, b in zip(cx, cw)) for (cw, sw) in qw] for (cx, sx) in qx])
+    np.testing.assert_allclose(O.w8a8_linear(x, w), ref, rtol=1e-12, atol=0)
+    # the prepared-weight form is the same product
+    np.testing.assert_array_equal(O.w8a8_linear(x, O.quantize_h256(w)), O.w8a8_linear(x, w))
+
+
+def test_w8a8_error_within_the_quantisation_bound():
+    """With xr = x H = sx (qx + dx), wr = W H = sw (qw + dw), |d| <= 1/2:
+    |x W^T - y8| <= sum_k |xr_k| sw / 2 + |wr_k| sx / 2 + sx sw / 4."""
+    r = np.random.default_rng(53)
+    K = 1024
+    x = r.standard_normal((16, K))
+    w = r.standard_normal((24, K)) * 0.02
+    y = O.w8a8_linear(x, w)
+    exact = x @ w.T
+    xr, wr = O.rotate_h256(x), O.rotate_h256(w)
+    _, sx = O.quantize_rows(xr)
+    _, sw = O.quantize_rows(wr)
+    sx, sw = sx.astype(np.float64)[:, None], sw.astype(np.float64)[None, :]
+    half = 0.5 + 1e-4
+    bound = (np.abs(xr).sum(1)[:, None] * sw * half + np.abs(wr).sum(1)[None, :] * sx * half + K * sx * sw * half ** 2)
+    err = np.abs(y - exact)
+    assert (err <= bound).all()
+    assert err.max() > 0 and err.max() < 0.05 * np.abs(exact).max()
+
+
+def test_w8a8_block_zero_adaln_is_identity_and_close_to_fp64():
+    """In the W8A8 format too, zero AdaLN weights give zero gates and out == x
+    exactly; with the drawn weights the block stays near the float64 block
+    (a synthetic numerics gate: the pages gate on image quality from trained
+    weights, which random weights cannot give)."""
+    cfg = I.C1_W8A8
+    w = I.block_weights(cfg)
+    x, c, pos = I.block_x(cfg), I.cond(cfg), I.positions(cfg)
+    wz = dict(w, w_ada=np.zeros_like(w["w_ada"]), b_ada=np.zeros_like(w["b_ada"]))
+    np.testing.assert_array_equal(O.block_forward(x, c, wz, cfg, pos), np.asarray(x, np.float64))
+    q8 = O.block_forward(x, c, w, cfg, pos) - x
+    ref = O.block_forward(x, c, w, I.C1, pos) - x
+    rel_rms = np.sqrt(((q8 - ref) ** 2).mean() / (ref ** 2).mean())
+    assert 1e-4 < rel_rms < 3e-2, rel_rms
+    # prepared weights (codes and scales made once) give the same block
+    wp = dict(w, **{k + "_q8": O.quantize_h256(w[k]) for k in ("w_qkv", "w_o", "w_gate_up", "w_down")})
+    np.testing.assert_array_equal(O.block_forward(x, c, wp, cfg, pos) - x, q8)
