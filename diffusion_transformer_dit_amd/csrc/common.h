@@ -13,6 +13,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef int intx4 __attribute__((ext_vector_type(4)));
+typedef int intx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kWave = 64;
 
@@ -111,6 +113,22 @@ hipError_t launch_gemm_swiglu(const bf16 *a, const bf16 *w, int64_t M, int F, in
                               bf16 *u, hipStream_t s);
 hipError_t launch_gemm_qkv(const bf16 *h, const bf16 *w, int64_t M, int N, int K,
                            const QkvEpiArgs &e, hipStream_t s);
+
+// W8A8 H256 projections: a / w int8 codes [M, K] / [rows, K] with fp32 row scales
+// a_scale [M] and w_scale [rows of w]; the products are dequantized before the
+// same epilogues
+hipError_t launch_gemm_residual_q8(const int8_t *a, const float *a_scale, const int8_t *w, const float *w_scale,
+                                   int64_t M, int N, int K, const void *resid, int resid_f32, const float *gate,
+                                   int gate_fn, const float *bias, void *out, int out_f32, hipStream_t s);
+hipError_t launch_gemm_swiglu_q8(const int8_t *a, const float *a_scale, const int8_t *w, const float *w_scale,
+                                 int64_t M, int F, int K, int act, bf16 *u, hipStream_t s);
+hipError_t launch_gemm_qkv_q8(const int8_t *h, const float *h_scale, const int8_t *w, const float *w_scale,
+                              int64_t M, int N, int K, const QkvEpiArgs &e, hipStream_t s);
+bool quantize_h256_supported(int cols);
+hipError_t launch_quantize_h256(const void *x, int x_f32, int64_t rows, int cols, int8_t *q, float *scale,
+                                hipStream_t s);
+hipError_t launch_ln_modulate_q8(const void *x, int x_f32, int64_t rows, int dim, int rms, const float *shift,
+                                 const float *scale, int mode, float eps, int8_t *q, float *qscale, hipStream_t s);
 
 hipError_t launch_flash_attention(const bf16 *q, const bf16 *k, const bf16 *vt, bf16 *out,
                                   int batch, int seq, int seq_pad, int heads, int kv_heads,

@@ -64,9 +64,11 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int32_t seq_pad_of(int32_t s) { return (s + 63) / 64 * 64; }
 
-// Workspace of one block evaluation.
+// Workspace of one block evaluation.  In the W8A8 format h holds the int8
+// codes of the normed rows (hs their scales), and the attention output and the
+// GLU output get int8 copies (aq/as, uq/us) for the projections that read them.
 struct BlockWs {
-    size_t m, h, q, k, vt, att, x1, u, total;
+    size_t m, h, q, k, vt, att, x1, u, hs, aq, as, uq, us, total;
 };
 
 BlockWs block_ws(const dit_block_desc &d) {
@@ -82,6 +84,13 @@ BlockWs block_ws(const dit_block_desc &d) {
     L.att = off; off += align256(N * H * hd * 2);
     L.x1 = off;  off += align256(N * D * 4);
     L.u = off;   off += align256(N * F * 2);
+    if (d.fmt == DIT_FMT_W8A8_H256) {
+        L.hs = off; off += align256(N * 4);
+        L.aq = off; off += align256(N * H * hd);
+        L.as = off; off += align256(N * 4);
+        L.uq = off; off += align256(N * F);
+        L.us = off; off += align256(N * 4);
+    }
     L.total = off;
     return L;
 }
@@ -103,6 +112,7 @@ int check_desc(const dit_block_desc *d) {
     if (d->gate < DIT_GATE_IDENTITY || d->gate > DIT_GATE_SIGMOID) return fail(DIT_ERR_INVALID_ARG, "bad gate function");
     if (d->mod != DIT_MOD_SHIFT_SCALE_GATE && d->mod != DIT_MOD_SCALE_GATE) return fail(DIT_ERR_INVALID_ARG, "bad mod");
     if (d->qk_order != DIT_QK_NORM_ROPE && d->qk_order != DIT_QK_ROPE_NORM) return fail(DIT_ERR_INVALID_ARG, "bad qk_order");
+    if (d->fmt != DIT_FMT_BF16 && d->fmt != DIT_FMT_W8A8_H256) return fail(DIT_ERR_INVALID_ARG, "bad fmt");
     if (d->w_dtype != DIT_BF16) return fail(DIT_ERR_UNSUPPORTED, "weights must be bf16");
     if (d->head_dim != 64 && d->head_dim != 128) return fail(DIT_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
     if (d->hidden % 256) return fail(DIT_ERR_UNSUPPORTED, "hidden must be a multiple of 256");
@@ -111,6 +121,8 @@ int check_desc(const dit_block_desc *d) {
     if (((d->heads + 2 * d->kv_heads) * d->head_dim) % 256)
         return fail(DIT_ERR_UNSUPPORTED, "(heads + 2 kv_heads) * head_dim must be a multiple of 256");
     if (d->cond_dim % 8) return fail(DIT_ERR_UNSUPPORTED, "cond_dim must be a multiple of 8");
+    if (d->fmt == DIT_FMT_W8A8_H256 && (d->ffn % 256 || !quantize_h256_supported(d->ffn)))
+        return fail(DIT_ERR_UNSUPPORTED, "W8A8 H256 needs ffn a multiple of 256 with ceil(ffn / 1024) <= 7 or a multiple of 4 up to 32");
     const double n = (double)d->batch * d->seq;
     if (n * d->ffn >= 2147483648.0 || n * d->hidden >= 2147483648.0 || (double)d->ffn * 2 * d->hidden >= 2147483648.0)
         return fail(DIT_ERR_UNSUPPORTED, "a GEMM operand exceeds 2^31 elements");
@@ -132,6 +144,12 @@ int check_weights(const dit_block_desc &d, const dit_block_weights *w) {
         const float *v[4] = {w->ln1_g, w->ln1_b, w->ln2_g, w->ln2_b};
         for (const float *p : v)
             if (p && !aligned16(p)) return fail(DIT_ERR_ALIGNMENT, "LayerNorm gamma/beta must be 16-byte aligned");
+    }
+    if (d.fmt == DIT_FMT_W8A8_H256) {
+        if (!w->s_qkv || !w->s_o || !w->s_gate_up || !w->s_down)
+            return fail(DIT_ERR_INVALID_ARG, "the W8A8 format needs the weight scales s_qkv, s_o, s_gate_up, s_down");
+        if (!aligned16(w->s_qkv) || !aligned16(w->s_o) || !aligned16(w->s_gate_up) || !aligned16(w->s_down))
+            return fail(DIT_ERR_ALIGNMENT, "weight scales must be 16-byte aligned");
     }
     if (d.qk_norm) {
         if (!w->q_g || !w->q_b || !w->k_g || !w->k_b) return fail(DIT_ERR_INVALID_ARG, "qk_norm needs q_g, q_b, k_g, k_b");
@@ -177,10 +195,29 @@ int block_body(const dit_block_desc &d, const dit_block_weights &w, const void *
         shift1 = m; scale1 = m + D; gate1 = m + 2 * D; shift2 = m + 3 * D; scale2 = m + 4 * D; gate2 = m + 5 * D;
     }
 
-    DIT_TRY_HIP(launch_ln_modulate(x, x_f32, N, D, rms, shift1, scale1, mode, d.eps, h, s));
-    DIT_TRY_HIP(launch_vt_pad_zero(vt, d.batch * d.kv_heads * hd, d.seq, spad, s));
     QkvEpiArgs e{d.batch, d.seq, spad, d.heads, d.kv_heads, hd, d.qk_norm, d.rope == DIT_ROPE_HALF, rms,
                  d.qk_order == DIT_QK_ROPE_NORM, d.eps, w.q_g, w.q_b, w.k_g, w.k_b, cosT, sinT, q, k, vt};
+    if (d.fmt == DIT_FMT_W8A8_H256) {
+        // the four projections in int8 (zml-flow-rs page §VII W8A8 with H256 on
+        // both sides); norms, attention and the residual stream as in bf16
+        int8_t *hq = (int8_t *)(ws + L.h), *aq = (int8_t *)(ws + L.aq), *uq = (int8_t *)(ws + L.uq);
+        float *hs = (float *)(ws + L.hs), *as = (float *)(ws + L.as), *us = (float *)(ws + L.us);
+        DIT_TRY_HIP(launch_ln_modulate_q8(x, x_f32, N, D, rms, shift1, scale1, mode, d.eps, hq, hs, s));
+        DIT_TRY_HIP(launch_vt_pad_zero(vt, d.batch * d.kv_heads * hd, d.seq, spad, s));
+        DIT_TRY_HIP(launch_gemm_qkv_q8(hq, hs, (const int8_t *)w.w_qkv, w.s_qkv, N, qkv_dim, D, e, s));
+        DIT_TRY_HIP(launch_flash_attention(q, k, vt, att, d.batch, d.seq, spad, d.heads, d.kv_heads, hd, s));
+        DIT_TRY_HIP(launch_quantize_h256(att, 0, N, d.heads * hd, aq, as, s));
+        DIT_TRY_HIP(launch_gemm_residual_q8(aq, as, (const int8_t *)w.w_o, w.s_o, N, D, d.heads * hd, x, x_f32, gate1,
+                                            d.gate, nullptr, x1, 1, s));
+        DIT_TRY_HIP(launch_ln_modulate_q8(x1, 1, N, D, rms, shift2, scale2, mode, d.eps, hq, hs, s));
+        DIT_TRY_HIP(launch_gemm_swiglu_q8(hq, hs, (const int8_t *)w.w_gate_up, w.s_gate_up, N, F, D, d.act, u, s));
+        DIT_TRY_HIP(launch_quantize_h256(u, 0, N, F, uq, us, s));
+        DIT_TRY_HIP(launch_gemm_residual_q8(uq, us, (const int8_t *)w.w_down, w.s_down, N, D, F, x1, 1, gate2, d.gate,
+                                            nullptr, out, out_f32, s));
+        return DIT_OK;
+    }
+    DIT_TRY_HIP(launch_ln_modulate(x, x_f32, N, D, rms, shift1, scale1, mode, d.eps, h, s));
+    DIT_TRY_HIP(launch_vt_pad_zero(vt, d.batch * d.kv_heads * hd, d.seq, spad, s));
     DIT_TRY_HIP(launch_gemm_qkv(h, (const bf16 *)w.w_qkv, N, qkv_dim, D, e, s));
     DIT_TRY_HIP(launch_flash_attention(q, k, vt, att, d.batch, d.seq, spad, d.heads, d.kv_heads, hd, s));
     DIT_TRY_HIP(launch_gemm_residual(att, (const bf16 *)w.w_o, N, D, d.heads * hd, x, x_f32, gate1, d.gate,
@@ -514,6 +551,121 @@ int dit_gemm_swiglu(const void *a, const void *w_gate_up, int64_t M, int32_t F, 
     if (!aligned16(a) || !aligned16(w_gate_up) || !aligned16(u)) return fail(DIT_ERR_ALIGNMENT, "16-byte alignment required");
     DIT_TRY(device_check());
     DIT_TRY_HIP(launch_gemm_swiglu((const bf16 *)a, (const bf16 *)w_gate_up, M, F, K, act, (bf16 *)u, as_stream(stream)));
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+// W8A8 H256 stage entry points
+// ---------------------------------------------------------------------------
+int dit_quantize_h256(const void *x, int32_t x_dtype, int64_t rows, int32_t cols, void *q, float *scale,
+                      void *stream) {
+    if (!x || !q || !scale) return fail(DIT_ERR_INVALID_ARG, "x, q and scale are required");
+    if (rows <= 0 || cols <= 0) return fail(DIT_ERR_INVALID_ARG, "rows and cols must be positive");
+    if (x_dtype != DIT_F32 && x_dtype != DIT_BF16) return fail(DIT_ERR_INVALID_ARG, "bad x_dtype");
+    if (!quantize_h256_supported(cols))
+        return fail(DIT_ERR_UNSUPPORTED, "cols must be a multiple of 256 with ceil(cols / 1024) <= 7 or a multiple of 4 up to 32");
+    if ((double)rows * cols >= 2147483648.0) return fail(DIT_ERR_UNSUPPORTED, "x exceeds 2^31 elements");
+    if (!aligned16(x) || !aligned16(q) || !aligned4(scale)) return fail(DIT_ERR_ALIGNMENT, "x and q must be 16-byte aligned");
+    const size_t xb = (size_t)rows * cols * (x_dtype == DIT_F32 ? 4 : 2);
+    if (overlaps(x, xb, q, (size_t)rows * cols) || overlaps(x, xb, scale, (size_t)rows * 4) ||
+        overlaps(q, (size_t)rows * cols, scale, (size_t)rows * 4))
+        return fail(DIT_ERR_INVALID_ARG, "x, q and scale must not overlap");
+    DIT_TRY(device_check());
+    DIT_TRY_HIP(launch_quantize_h256(x, x_dtype == DIT_F32, rows, cols, (int8_t *)q, scale, as_stream(stream)));
+    return ok();
+}
+
+int dit_ln_modulate_h256q(const void *x, int32_t x_dtype, int64_t rows, int32_t dim, int32_t norm,
+                          const float *shift, const float *scale, int32_t mode, float eps, void *q, float *qscale,
+                          void *stream) {
+    if (!x || !q || !qscale) return fail(DIT_ERR_INVALID_ARG, "x, q and qscale are required");
+    if (rows <= 0 || dim <= 0) return fail(DIT_ERR_INVALID_ARG, "rows and dim must be positive");
+    if (x_dtype != DIT_F32 && x_dtype != DIT_BF16) return fail(DIT_ERR_INVALID_ARG, "bad x_dtype");
+    if (mode != 0 && mode != 1) return fail(DIT_ERR_INVALID_ARG, "mode must be 0 or 1");
+    if (mode == 0 && !scale) return fail(DIT_ERR_INVALID_ARG, "mode 0 needs scale");
+    if (norm != DIT_LAYERNORM && norm != DIT_RMSNORM) return fail(DIT_ERR_INVALID_ARG, "bad norm kind");
+    if (!(eps > 0.f)) return fail(DIT_ERR_INVALID_ARG, "eps must be positive");
+    if (dim % 256 || dim > 8192) return fail(DIT_ERR_UNSUPPORTED, "dim must be a multiple of 256 and <= 8192");
+    if (!aligned16(x) || !aligned16(q) || !aligned4(qscale) || (shift && !aligned16(shift)) ||
+        (scale && !aligned16(scale)))
+        return fail(DIT_ERR_ALIGNMENT, "x, q, shift, scale must be 16-byte aligned");
+    DIT_TRY(device_check());
+    DIT_TRY_HIP(launch_ln_modulate_q8(x, x_dtype == DIT_F32, rows, dim, norm == DIT_RMSNORM, shift, scale, mode, eps,
+                                      (int8_t *)q, qscale, as_stream(stream)));
+    return ok();
+}
+
+namespace {
+int check_q8_operands(const void *a, const float *as, const void *w, const float *ws, int64_t M, int64_t wrows,
+                      int32_t K) {
+    if (!a || !as || !w || !ws) return fail(DIT_ERR_INVALID_ARG, "a, a_scale, w and w_scale are required");
+    if (K % 128) return fail(DIT_ERR_UNSUPPORTED, "K must be a multiple of 128");
+    if ((double)M * K >= 2147483648.0 || (double)wrows * K >= 2147483648.0)
+        return fail(DIT_ERR_UNSUPPORTED, "operand exceeds 2^31 elements");
+    if (!aligned16(a) || !aligned16(w) || !aligned16(as) || !aligned16(ws))
+        return fail(DIT_ERR_ALIGNMENT, "codes and scales must be 16-byte aligned");
+    return DIT_OK;
+}
+}  // namespace
+
+int dit_gemm_w8a8_gated_residual(const void *a, const float *a_scale, const void *w, const float *w_scale, int64_t M,
+                                 int32_t N, int32_t K, const void *resid, int32_t resid_dtype, const float *gate,
+                                 int32_t gate_fn, const float *bias, void *out, int32_t out_dtype, void *stream) {
+    if (!out) return fail(DIT_ERR_INVALID_ARG, "out is required");
+    if (M <= 0 || N <= 0 || K <= 0) return fail(DIT_ERR_INVALID_ARG, "dims must be positive");
+    if ((resid && resid_dtype != DIT_F32 && resid_dtype != DIT_BF16) || (out_dtype != DIT_F32 && out_dtype != DIT_BF16))
+        return fail(DIT_ERR_INVALID_ARG, "bad dtype");
+    if (gate_fn < DIT_GATE_IDENTITY || gate_fn > DIT_GATE_SIGMOID) return fail(DIT_ERR_INVALID_ARG, "bad gate function");
+    if (N % 128) return fail(DIT_ERR_UNSUPPORTED, "N must be a multiple of 128");
+    DIT_TRY(check_q8_operands(a, a_scale, w, w_scale, M, N, K));
+    if (!aligned16(out) || (resid && !aligned16(resid)) || (gate && !aligned4(gate)) || (bias && !aligned4(bias)))
+        return fail(DIT_ERR_ALIGNMENT, "out and resid must be 16-byte aligned");
+    const size_t ob = (size_t)M * N * (out_dtype == DIT_F32 ? 4 : 2);
+    const size_t rb = (size_t)M * N * (resid_dtype == DIT_F32 ? 4 : 2);
+    if (resid && resid != out && overlaps(resid, rb, out, ob)) return fail(DIT_ERR_INVALID_ARG, "resid overlaps out");
+    if (resid == out && resid && resid_dtype != out_dtype) return fail(DIT_ERR_INVALID_ARG, "in-place needs equal dtypes");
+    DIT_TRY(device_check());
+    DIT_TRY_HIP(launch_gemm_residual_q8((const int8_t *)a, a_scale, (const int8_t *)w, w_scale, M, N, K, resid,
+                                        resid_dtype == DIT_F32, gate, gate_fn, bias, out, out_dtype == DIT_F32,
+                                        as_stream(stream)));
+    return ok();
+}
+
+int dit_gemm_w8a8_swiglu(const void *a, const float *a_scale, const void *w_gate_up, const float *w_scale, int64_t M,
+                         int32_t F, int32_t K, int32_t act, void *u, void *stream) {
+    if (!u) return fail(DIT_ERR_INVALID_ARG, "u is required");
+    if (act != DIT_ACT_SILU && act != DIT_ACT_GELU_TANH) return fail(DIT_ERR_INVALID_ARG, "bad act");
+    if (M <= 0 || F <= 0 || K <= 0) return fail(DIT_ERR_INVALID_ARG, "dims must be positive");
+    if (F % 128) return fail(DIT_ERR_UNSUPPORTED, "F must be a multiple of 128");
+    DIT_TRY(check_q8_operands(a, a_scale, w_gate_up, w_scale, M, 2 * (int64_t)F, K));
+    if ((double)M * F >= 2147483648.0) return fail(DIT_ERR_UNSUPPORTED, "operand exceeds 2^31 elements");
+    if (!aligned16(u)) return fail(DIT_ERR_ALIGNMENT, "u must be 16-byte aligned");
+    DIT_TRY(device_check());
+    DIT_TRY_HIP(launch_gemm_swiglu_q8((const int8_t *)a, a_scale, (const int8_t *)w_gate_up, w_scale, M, F, K, act,
+                                      (bf16 *)u, as_stream(stream)));
+    return ok();
+}
+
+int dit_qkv_rope_w8a8(const dit_block_desc *desc, const void *h, const float *h_scale, const void *w_qkv,
+                      const float *w_scale, const float *q_g, const float *q_b, const float *k_g, const float *k_b,
+                      const float *rope_cos, const float *rope_sin, void *q, void *k, void *vt, void *stream) {
+    DIT_TRY(check_desc(desc));
+    const dit_block_desc &d = *desc;
+    if (!rope_cos || !rope_sin || !q || !k || !vt) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+    if (d.qk_norm && (!q_g || !q_b || !k_g || !k_b)) return fail(DIT_ERR_INVALID_ARG, "qk_norm needs gamma/beta");
+    const int64_t N = (int64_t)d.batch * d.seq;
+    const int qkv_dim = (d.heads + 2 * d.kv_heads) * d.head_dim;
+    DIT_TRY(check_q8_operands(h, h_scale, w_qkv, w_scale, N, qkv_dim, d.hidden));
+    if (!aligned16(q) || !aligned16(k) || !aligned16(vt)) return fail(DIT_ERR_ALIGNMENT, "q, k, vt must be 16-byte aligned");
+    DIT_TRY(device_check());
+    hipStream_t s = as_stream(stream);
+    const int spad = seq_pad_of(d.seq);
+    DIT_TRY_HIP(launch_vt_pad_zero((bf16 *)vt, d.batch * d.kv_heads * d.head_dim, d.seq, spad, s));
+    QkvEpiArgs e{d.batch, d.seq, spad, d.heads, d.kv_heads, d.head_dim, d.qk_norm, d.rope == DIT_ROPE_HALF,
+                 d.norm == DIT_RMSNORM, d.qk_order == DIT_QK_ROPE_NORM, d.eps, q_g, q_b, k_g, k_b, rope_cos, rope_sin,
+                 (bf16 *)q, (bf16 *)k, (bf16 *)vt};
+    DIT_TRY_HIP(launch_gemm_qkv_q8((const int8_t *)h, h_scale, (const int8_t *)w_qkv, w_scale, N, qkv_dim, d.hidden,
+                                   e, s));
     return ok();
 }
 

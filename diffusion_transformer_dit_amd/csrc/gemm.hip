@@ -1,13 +1,16 @@
-// bf16 MFMA GEMM for gfx950 with the block's fused epilogues.
+// bf16 and int8 MFMA GEMM for gfx950 with the block's fused epilogues.
 //
 // C[m, n] = sum_k A[m, k] * W[n, k]: A is [M, K] row-major (activations), W is
 // [N, K] row-major (weights as [out, in]), both K-contiguous, so both operand
 // tiles are copied to LDS row by row and read back as MFMA fragments without a
 // transpose.  One workgroup computes a BM x BN tile with WM x WN waves; each
 // wave owns a (BM/WM) x (BN/WN) sub-tile built from 32x32 MFMA blocks
-// (v_mfma_f32_32x32x16_bf16, fp32 accumulators).  K advances in steps of 64
-// through two LDS stages: while one stage feeds the MFMAs, the next tile is
-// already in flight from global memory into registers.
+// (v_mfma_f32_32x32x16_bf16 with fp32 accumulators, or for the W8A8 H256
+// format of the zml-flow-rs page §VII v_mfma_i32_32x32x32_i8 with exact int32
+// accumulators, dequantized by the row scales of A and W before the
+// epilogue).  K advances 128 bytes of each operand row at a time (64 bf16 or
+// 128 int8) through two LDS stages: while one stage feeds the MFMAs, the next
+// tile is already in flight from global memory.
 //
 // Epilogues (run on the fp32 accumulators, no extra pass over memory):
 //   * residual : out = resid + gate[n] * acc + bias[n]   (gated residual, ERNIE
@@ -18,20 +21,22 @@
 //                gamma/beta and the RoPE rotation from cos/sin tables, in either
 //                order, scatter to head-major q/k and transposed v (zml-flow-rs
 //                page §VI "QKV + norm + RoPE"; ERNIE page §IV draws RoPE first)
+#include <type_traits>
+
 #include "common.h"
 
 namespace dit {
 
-// Tile shape: BM x BN outputs per workgroup of WM x WN waves, K consumed BK at
-// a time through NS LDS stages.
-template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64, int NS_ = 2>
+// Tile shape: BM x BN outputs per workgroup of WM x WN waves, K consumed BK
+// elements of ES bytes (2: bf16, 1: int8) at a time through NS LDS stages.
+template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64, int NS_ = 2, int ES_ = 2>
 struct Tile {
-    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_;
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_, ES = ES_;
     static constexpr int kWaves = WM * WN;
     static constexpr int kThreads = kWaves * kWave;
     static constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
     static constexpr int TM = kWaveM / 32, TN = kWaveN / 32;
-    static constexpr int kRowBytes = BK * 2;                    // one tile row (BK bf16) in LDS
+    static constexpr int kRowBytes = BK * ES;                   // one tile row (BK elements) in LDS
     static constexpr int kChunks = kRowBytes / 16;              // 16-byte chunks per row
     static constexpr int kRowsPerLine = 256 / kRowBytes;        // rows sharing one 64-bank line
     static constexpr int kRowsPerLoad = 1024 / kRowBytes;       // rows one wave-wide 1 KiB load fills
@@ -40,7 +45,7 @@ struct Tile {
     static constexpr int kLoads = kALoads + kBLoads;
     static constexpr int kStageBytes = (BM + BN) * kRowBytes;
     static_assert(BM % (kRowsPerLoad * kWaves) == 0 && BN % (kRowsPerLoad * kWaves) == 0, "tile vs loads");
-    static_assert(kWaveM % 32 == 0 && kWaveN % 32 == 0 && BK % 16 == 0, "wave tile");
+    static_assert(kWaveM % 32 == 0 && kWaveN % 32 == 0 && kRowBytes % 64 == 0, "wave tile");
     static_assert((NS - 2) * kLoads <= 63, "vmcnt range");
     // Chunk c of tile row r lives at slot c ^ swz(r).  gfx950 LDS has 64 banks
     // (256 B per cycle) and a ds_read_b128 serves 16 lanes per cycle; the
@@ -88,10 +93,25 @@ struct RowsSwiglu {
     }
 };
 
+// one 32x32 MFMA block, k = 32 bytes of each operand row (16 bf16 or 32 int8).
+// The int8 form keeps its int32 accumulators in the same float registers (bit
+// patterns; 0.0f is int 0), so the dequantization below converts them in place.
+__device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx16 mfma32(intx4 a, intx4 b, floatx16 c) {
+    return __builtin_bit_cast(floatx16,
+                              __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, __builtin_bit_cast(intx16, c), 0, 0, 0));
+}
+
+__device__ __forceinline__ int acc_row(int i, int e, int lhalf);
+
+// a_scale [M] / w_scale [w_rows]: the int8 operands' row scales (ES == 1 only)
 template <class T, class RowMap, class Epi>
 __global__ __launch_bounds__(T::kThreads, 1)
-void gemm_kernel(const bf16 *__restrict__ A, const bf16 *__restrict__ W, int M, int K, int w_rows,
-                 int tiles_m, int tiles_n, RowMap rowmap, Epi epi) {
+void gemm_kernel(const void *__restrict__ A, const void *__restrict__ W, int M, int K, int w_rows,
+                 int tiles_m, int tiles_n, RowMap rowmap, Epi epi, const float *__restrict__ a_scale,
+                 const float *__restrict__ w_scale) {
 #if defined(__HIP_DEVICE_COMPILE__)   // buffer resources exist only in the device pass
     constexpr int kMain = T::NS * T::kStageBytes;
     constexpr int kLds = Epi::template lds_bytes<T>() > kMain ? Epi::template lds_bytes<T>() : kMain;
@@ -113,25 +133,26 @@ void gemm_kernel(const bf16 *__restrict__ A, const bf16 *__restrict__ W, int M, 
     // q of wave w fills tile rows kRowsPerLoad (q waves + w) ..; lane l brings
     // row + l / kChunks into physical slot l % kChunks, i.e. the logical chunk
     // (l % kChunks) ^ swz(row).
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)M * (uint32_t)K * 2u);
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(W, (uint32_t)w_rows * (uint32_t)K * 2u);
+    using Frag = typename std::conditional<T::ES == 2, bf16x8, intx4>::type;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)M * (uint32_t)K * (uint32_t)T::ES);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(W, (uint32_t)w_rows * (uint32_t)K * (uint32_t)T::ES);
     const int lr = lane / T::kChunks, ls = lane % T::kChunks;
     uint32_t a_off[T::kALoads], b_off[T::kBLoads];
 #pragma unroll
     for (int q = 0; q < T::kALoads; ++q) {
         const int r = (q * T::kWaves + wave) * T::kRowsPerLoad + lr;
         const int grow = min(m0 + r, M - 1);              // ragged M: clamp reads, mask stores
-        a_off[q] = ((uint32_t)grow * (uint32_t)K + (ls ^ T::swz(r)) * 8) * 2u;
+        a_off[q] = (uint32_t)grow * (uint32_t)K * (uint32_t)T::ES + (uint32_t)((ls ^ T::swz(r)) << 4);
     }
 #pragma unroll
     for (int q = 0; q < T::kBLoads; ++q) {
         const int r = (q * T::kWaves + wave) * T::kRowsPerLoad + lr;
-        b_off[q] = ((uint32_t)rowmap(tn, r) * (uint32_t)K + (ls ^ T::swz(r)) * 8) * 2u;
+        b_off[q] = (uint32_t)rowmap(tn, r) * (uint32_t)K * (uint32_t)T::ES + (uint32_t)((ls ^ T::swz(r)) << 4);
     }
 #define DIT_ISSUE(stage, k0)                                                                             \
     do {                                                                                                 \
         uint8_t *base_ = smem + (stage) * T::kStageBytes;                                                \
-        const uint32_t kb_ = (uint32_t)(k0) * 2u;                                                        \
+        const uint32_t kb_ = (uint32_t)(k0) * (uint32_t)T::ES;                                           \
         _Pragma("unroll") for (int q = 0; q < T::kALoads; ++q) __builtin_amdgcn_raw_ptr_buffer_load_lds( \
             ra, (lds_void *)(base_ + (q * T::kWaves + wave) * 1024), 16, a_off[q], kb_, 0, 0);           \
         _Pragma("unroll") for (int q = 0; q < T::kBLoads; ++q) __builtin_amdgcn_raw_ptr_buffer_load_lds( \
@@ -151,27 +172,27 @@ void gemm_kernel(const bf16 *__restrict__ A, const bf16 *__restrict__ W, int M, 
     // end re-load the last tile (never read) so that every iteration issues the
     // same number of loads and the vmcnt bookkeeping stays uniform.
     const int KT = K / T::BK;
-    constexpr int KS = T::BK / 16;   // MFMA k-steps per stage (even: k-step 0 always uses buffer 0)
+    constexpr int KS = T::kRowBytes / 32;   // MFMA k-steps per stage (even: k-step 0 always uses buffer 0)
     static_assert(KS % 2 == 0, "fragment double buffer");
 #pragma unroll
     for (int s0 = 0; s0 < T::NS; ++s0) DIT_ISSUE(s0, min(s0, KT - 1) * T::BK);
 
-    bf16x8 af[2][T::TM], bfr[2][T::TN];
+    Frag af[2][T::TM], bfr[2][T::TN];
     // fragment reads in the order the MFMAs consume them: A0, B0 .. B(TN-1), A1 .. A(TM-1)
 #define DIT_LOAD_FRAGS(buf, sa_, sb_, kk)                                                           \
     do {                                                                                          \
         const int c_ = (kk) * 2 + lhalf;                                                          \
-        af[buf][0] = *(const bf16x8 *)((sa_) + T::off(wm * T::kWaveM + lrow, c_));                \
+        af[buf][0] = *(const Frag *)((sa_) + T::off(wm * T::kWaveM + lrow, c_));                  \
         _Pragma("unroll") for (int j = 0; j < T::TN; ++j)                                        \
-            bfr[buf][j] = *(const bf16x8 *)((sb_) + T::off(wn * T::kWaveN + j * 32 + lrow, c_));  \
+            bfr[buf][j] = *(const Frag *)((sb_) + T::off(wn * T::kWaveN + j * 32 + lrow, c_));    \
         _Pragma("unroll") for (int i = 1; i < T::TM; ++i)                                        \
-            af[buf][i] = *(const bf16x8 *)((sa_) + T::off(wm * T::kWaveM + i * 32 + lrow, c_));   \
+            af[buf][i] = *(const Frag *)((sa_) + T::off(wm * T::kWaveM + i * 32 + lrow, c_));     \
     } while (0)
 #define DIT_MFMAS(buf)                                                                             \
     do {                                                                                          \
         _Pragma("unroll") for (int i = 0; i < T::TM; ++i)                                        \
             _Pragma("unroll") for (int j = 0; j < T::TN; ++j)                                    \
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bfr[buf][j], acc[i][j], 0, 0, 0); \
+                acc[i][j] = mfma32(af[buf][i], bfr[buf][j], acc[i][j]);                                \
     } while (0)
 
     wait_vmcnt<(T::NS - 1) * T::kLoads>();   // tile 0 landed
@@ -232,7 +253,30 @@ void gemm_kernel(const bf16 *__restrict__ A, const bf16 *__restrict__ W, int M, 
     wait_vmcnt<0>();      // retire the trailing (never read) loads before LDS is reused
     __syncthreads();
 
-    epi.template apply<T>(acc, m0 + wm * T::kWaveM, tn, wn, lane, M, smem);
+    if constexpr (T::ES == 2) {
+        epi.template apply<T>(acc, m0 + wm * T::kWaveM, tn, wn, lane, M, smem);
+    } else {
+        // dequantize in place: C[m, n] = acc * (a_scale[m] w_scale[n]), the int32
+        // sum converted to fp32 (rounded once)
+        const int row0 = m0 + wm * T::kWaveM;
+        float sw[T::TN];
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) sw[j] = w_scale[rowmap(tn, wn * T::kWaveN + j * 32 + lrow)];
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i) {
+            float sa[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sa[e] = a_scale[min(row0 + acc_row(i, e, lhalf), M - 1)];
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j) {
+                // whole-vector bit cast: clang mis-lowers a bit cast of one vector element
+                const intx16 iv = __builtin_bit_cast(intx16, acc[i][j]);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = (float)iv[e] * (sa[e] * sw[j]);
+            }
+        }
+        epi.template apply<T>(acc, m0 + wm * T::kWaveM, tn, wn, lane, M, smem);
+    }
 #endif
 }
 
@@ -627,6 +671,10 @@ struct EpiQkv {
 using Tile8w = Tile<256, 256, 2, 4>;
 using Tile8wTall = Tile<320, 256, 2, 4>;   // 160 x 64 per wave: ragged row counts just above a multiple of 256
 using TileNarrow = Tile<256, 128, 2, 2>;   // N = 128 outputs (the projection to latent channels)
+// the same tiles over int8 operands (128 int8 per 128-byte row)
+using Tile8wQ = Tile<256, 256, 2, 4, 128, 2, 1>;
+using Tile8wTallQ = Tile<320, 256, 2, 4, 128, 2, 1>;
+using TileNarrowQ = Tile<256, 128, 2, 2, 128, 2, 1>;
 
 // Compute units of the current device (one 256 x 256 tile runs per CU at a time).
 static int cu_count() {
@@ -652,49 +700,91 @@ static bool prefer_tall(int64_t M, int N) {
     return r320 * 320 < r256 * 256;
 }
 
+// int8 operands carry their row scales (Scales), bf16 operands none (NoScales)
+struct NoScales {
+    static constexpr bool kQ8 = false;
+    const float *a = nullptr, *w = nullptr;
+};
+struct Scales {
+    static constexpr bool kQ8 = true;
+    const float *a, *w;
+};
+
 template <class T, class RowMap, class Epi>
-static hipError_t run(const bf16 *a, const bf16 *w, int64_t M, int N_tile_cols, int K, RowMap rm, Epi epi,
-                      hipStream_t s) {
+static hipError_t run(const void *a, const void *w, int64_t M, int N_tile_cols, int K, RowMap rm, Epi epi,
+                      hipStream_t s, const float *a_scale = nullptr, const float *w_scale = nullptr) {
     const int tiles_m = (int)((M + T::BM - 1) / T::BM);
     const int tiles_n = N_tile_cols / T::BN;
     const int grid = tiles_m * tiles_n;
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL((gemm_kernel<T, RowMap, Epi>), dim3(grid), dim3(T::kThreads), 0, s, a, w, (int)M, K,
-                       N_tile_cols, tiles_m, tiles_n, rm, epi);
+                       N_tile_cols, tiles_m, tiles_n, rm, epi, a_scale, w_scale);
     return hipGetLastError();
 }
 
-template <typename TR, typename TO>
-static hipError_t residual_typed(const bf16 *a, const bf16 *w, int64_t M, int N, int K, const void *resid,
-                                 const float *gate, int gate_fn, const float *bias, void *out, hipStream_t s) {
+template <typename TR, typename TO, class SC>
+static hipError_t residual_typed(const void *a, const void *w, int64_t M, int N, int K, const void *resid,
+                                 const float *gate, int gate_fn, const float *bias, void *out, SC sc,
+                                 hipStream_t s) {
+    using TT = typename std::conditional<SC::kQ8, Tile8wTallQ, Tile8wTall>::type;
+    using TS = typename std::conditional<SC::kQ8, Tile8wQ, Tile8w>::type;
+    using TN = typename std::conditional<SC::kQ8, TileNarrowQ, TileNarrow>::type;
     EpiResidual<TR, TO> epi{(const TR *)resid, gate, bias, (TO *)out, N, gate_fn};
-    if (N % 256 == 0 && prefer_tall(M, N)) return run<Tile8wTall>(a, w, M, N, K, RowsIdentity{256}, epi, s);
-    if (N % 256 == 0) return run<Tile8w>(a, w, M, N, K, RowsIdentity{256}, epi, s);
-    return run<TileNarrow>(a, w, M, N, K, RowsIdentity{128}, epi, s);
+    if (N % 256 == 0 && prefer_tall(M, N)) return run<TT>(a, w, M, N, K, RowsIdentity{256}, epi, s, sc.a, sc.w);
+    if (N % 256 == 0) return run<TS>(a, w, M, N, K, RowsIdentity{256}, epi, s, sc.a, sc.w);
+    return run<TN>(a, w, M, N, K, RowsIdentity{128}, epi, s, sc.a, sc.w);
+}
+
+template <class SC>
+static hipError_t residual_any(const void *a, const void *w, int64_t M, int N, int K, const void *resid,
+                               int resid_f32, const float *gate, int gate_fn, const float *bias, void *out,
+                               int out_f32, SC sc, hipStream_t s) {
+    if (resid_f32) {
+        return out_f32 ? residual_typed<float, float>(a, w, M, N, K, resid, gate, gate_fn, bias, out, sc, s)
+                       : residual_typed<float, bf16>(a, w, M, N, K, resid, gate, gate_fn, bias, out, sc, s);
+    }
+    return out_f32 ? residual_typed<bf16, float>(a, w, M, N, K, resid, gate, gate_fn, bias, out, sc, s)
+                   : residual_typed<bf16, bf16>(a, w, M, N, K, resid, gate, gate_fn, bias, out, sc, s);
 }
 
 hipError_t launch_gemm_residual(const bf16 *a, const bf16 *w, int64_t M, int N, int K, const void *resid,
                                 int resid_f32, const float *gate, int gate_fn, const float *bias, void *out,
                                 int out_f32, hipStream_t s) {
-    if (resid_f32) {
-        return out_f32 ? residual_typed<float, float>(a, w, M, N, K, resid, gate, gate_fn, bias, out, s)
-                       : residual_typed<float, bf16>(a, w, M, N, K, resid, gate, gate_fn, bias, out, s);
-    }
-    return out_f32 ? residual_typed<bf16, float>(a, w, M, N, K, resid, gate, gate_fn, bias, out, s)
-                   : residual_typed<bf16, bf16>(a, w, M, N, K, resid, gate, gate_fn, bias, out, s);
+    return residual_any(a, w, M, N, K, resid, resid_f32, gate, gate_fn, bias, out, out_f32, NoScales{}, s);
+}
+
+hipError_t launch_gemm_residual_q8(const int8_t *a, const float *a_scale, const int8_t *w, const float *w_scale,
+                                   int64_t M, int N, int K, const void *resid, int resid_f32, const float *gate,
+                                   int gate_fn, const float *bias, void *out, int out_f32, hipStream_t s) {
+    return residual_any(a, w, M, N, K, resid, resid_f32, gate, gate_fn, bias, out, out_f32,
+                        Scales{a_scale, w_scale}, s);
+}
+
+template <class SC>
+static hipError_t swiglu_any(const void *a, const void *w, int64_t M, int F, int K, int act, bf16 *u, SC sc,
+                             hipStream_t s) {
+    using T = typename std::conditional<SC::kQ8, Tile8wQ, Tile8w>::type;
+    const RowsSwiglu rm{T::BN, T::kWaveN, F};
+    if (act == 1) return run<T>(a, w, M, 2 * F, K, rm, EpiSwiglu<1>{u, F}, s, sc.a, sc.w);
+    return run<T>(a, w, M, 2 * F, K, rm, EpiSwiglu<0>{u, F}, s, sc.a, sc.w);
 }
 
 hipError_t launch_gemm_swiglu(const bf16 *a, const bf16 *w, int64_t M, int F, int K, int act, bf16 *u,
                               hipStream_t s) {
-    using T = Tile8w;
-    if (act == 1) return run<T>(a, w, M, 2 * F, K, RowsSwiglu{T::BN, T::kWaveN, F}, EpiSwiglu<1>{u, F}, s);
-    return run<T>(a, w, M, 2 * F, K, RowsSwiglu{T::BN, T::kWaveN, F}, EpiSwiglu<0>{u, F}, s);
+    return swiglu_any(a, w, M, F, K, act, u, NoScales{}, s);
 }
 
-hipError_t launch_gemm_qkv(const bf16 *h, const bf16 *w, int64_t M, int N, int K, const QkvEpiArgs &e,
-                           hipStream_t s) {
-    using T = Tile8w;
-#define DIT_QKV(HD_, RMS_, RF_) run<T>(h, w, M, N, K, RowsIdentity{T::BN}, EpiQkv<HD_, RMS_, RF_>{e}, s)
+hipError_t launch_gemm_swiglu_q8(const int8_t *a, const float *a_scale, const int8_t *w, const float *w_scale,
+                                 int64_t M, int F, int K, int act, bf16 *u, hipStream_t s) {
+    return swiglu_any(a, w, M, F, K, act, u, Scales{a_scale, w_scale}, s);
+}
+
+template <class SC>
+static hipError_t qkv_any(const void *h, const void *w, int64_t M, int N, int K, const QkvEpiArgs &e, SC sc,
+                          hipStream_t s) {
+    using T = typename std::conditional<SC::kQ8, Tile8wQ, Tile8w>::type;
+#define DIT_QKV(HD_, RMS_, RF_) \
+    run<T>(h, w, M, N, K, RowsIdentity{T::BN}, EpiQkv<HD_, RMS_, RF_>{e}, s, sc.a, sc.w)
     if (e.head_dim == 128) {
         if (e.rms) return e.rope_first ? DIT_QKV(128, true, true) : DIT_QKV(128, true, false);
         return e.rope_first ? DIT_QKV(128, false, true) : DIT_QKV(128, false, false);
@@ -702,6 +792,16 @@ hipError_t launch_gemm_qkv(const bf16 *h, const bf16 *w, int64_t M, int N, int K
     if (e.rms) return e.rope_first ? DIT_QKV(64, true, true) : DIT_QKV(64, true, false);
     return e.rope_first ? DIT_QKV(64, false, true) : DIT_QKV(64, false, false);
 #undef DIT_QKV
+}
+
+hipError_t launch_gemm_qkv(const bf16 *h, const bf16 *w, int64_t M, int N, int K, const QkvEpiArgs &e,
+                           hipStream_t s) {
+    return qkv_any(h, w, M, N, K, e, NoScales{}, s);
+}
+
+hipError_t launch_gemm_qkv_q8(const int8_t *h, const float *h_scale, const int8_t *w, const float *w_scale,
+                              int64_t M, int N, int K, const QkvEpiArgs &e, hipStream_t s) {
+    return qkv_any(h, w, M, N, K, e, Scales{h_scale, w_scale}, s);
 }
 
 }  // namespace dit

@@ -22,6 +22,7 @@ DIT_ACT_SILU, DIT_ACT_GELU_TANH = 0, 1
 DIT_GATE_IDENTITY, DIT_GATE_TANH, DIT_GATE_SIGMOID = 0, 1, 2
 DIT_MOD_SHIFT_SCALE_GATE, DIT_MOD_SCALE_GATE = 0, 1
 DIT_QK_NORM_ROPE, DIT_QK_ROPE_NORM = 0, 1
+DIT_FMT_BF16, DIT_FMT_W8A8_H256 = 0, 1
 
 EXPORTED = (
     "dit_block_workspace_size", "dit_block_forward", "dit_stack_workspace_size", "dit_stack_step",
@@ -29,6 +30,8 @@ EXPORTED = (
     "dit_adaln_modulation", "dit_ln_modulate", "dit_qkv_rope", "dit_seq_pad", "dit_flash_attention",
     "dit_gemm_gated_residual", "dit_gemm_swiglu", "dit_status_string", "dit_last_error", "dit_version",
     "dit_loop_workspace_size", "dit_loop_create", "dit_loop_launch_step", "dit_loop_launch", "dit_loop_destroy",
+    "dit_quantize_h256", "dit_ln_modulate_h256q", "dit_gemm_w8a8_gated_residual", "dit_gemm_w8a8_swiglu",
+    "dit_qkv_rope_w8a8",
 )
 
 
@@ -42,11 +45,11 @@ class dit_block_desc(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("batch", "seq", "hidden", "heads", "kv_heads", "head_dim", "ffn",
                                          "cond_dim", "qk_norm", "norm", "rope")] + \
                [("eps", C.c_float), ("x_dtype", C.c_int32), ("w_dtype", C.c_int32)] + \
-               [(n, C.c_int32) for n in ("act", "gate", "mod", "qk_order")]
+               [(n, C.c_int32) for n in ("act", "gate", "mod", "qk_order", "fmt")]
 
 
 WEIGHT_FIELDS = ("w_ada", "b_ada", "ln1_g", "ln1_b", "ln2_g", "ln2_b", "w_qkv", "q_g", "q_b", "k_g", "k_b",
-                 "w_o", "w_gate_up", "w_down")
+                 "w_o", "w_gate_up", "w_down", "s_qkv", "s_o", "s_gate_up", "s_down")
 
 
 class dit_block_weights(C.Structure):
@@ -96,6 +99,12 @@ def lib():
             "dit_loop_launch_step": (C.c_int, [vp, i32, vp]),
             "dit_loop_launch": (C.c_int, [vp, vp]),
             "dit_loop_destroy": (C.c_int, [vp]),
+            "dit_quantize_h256": (C.c_int, [vp, i32, i64, i32, vp, vp, vp]),
+            "dit_ln_modulate_h256q": (C.c_int, [vp, i32, i64, i32, i32, vp, vp, i32, f32, vp, vp, vp]),
+            "dit_gemm_w8a8_gated_residual": (C.c_int, [vp, vp, vp, vp, i64, i32, i32, vp, i32, vp, i32, vp, vp,
+                                                       i32, vp]),
+            "dit_gemm_w8a8_swiglu": (C.c_int, [vp, vp, vp, vp, i64, i32, i32, i32, vp, vp]),
+            "dit_qkv_rope_w8a8": (C.c_int, [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -142,9 +151,10 @@ def _check(rc: int):
 
 def make_desc(batch, seq, hidden, heads, kv_heads, head_dim, ffn, cond_dim, qk_norm=True, rope=DIT_ROPE_INTERLEAVED,
               eps=1e-6, x_dtype=DIT_BF16, norm=DIT_LAYERNORM, w_dtype=DIT_BF16, act=DIT_ACT_SILU,
-              gate=DIT_GATE_IDENTITY, mod=DIT_MOD_SHIFT_SCALE_GATE, qk_order=DIT_QK_NORM_ROPE) -> dit_block_desc:
+              gate=DIT_GATE_IDENTITY, mod=DIT_MOD_SHIFT_SCALE_GATE, qk_order=DIT_QK_NORM_ROPE,
+              fmt=DIT_FMT_BF16) -> dit_block_desc:
     return dit_block_desc(batch, seq, hidden, heads, kv_heads, head_dim, ffn, cond_dim, int(bool(qk_norm)), norm,
-                          rope, eps, x_dtype, w_dtype, act, gate, mod, qk_order)
+                          rope, eps, x_dtype, w_dtype, act, gate, mod, qk_order, fmt)
 
 
 def make_weights(tensors: Dict[str, Any]) -> dit_block_weights:
@@ -276,6 +286,35 @@ def dit_gemm_gated_residual(a, w, M, N, K, resid, resid_dtype, gate, bias, out, 
 
 def dit_gemm_swiglu(a, w_gate_up, M, F, K, u, stream=None, act=DIT_ACT_SILU):
     _check(lib().dit_gemm_swiglu(_p(a), _p(w_gate_up), int(M), int(F), int(K), int(act), _p(u), _stream(stream)))
+
+
+def dit_quantize_h256(x, x_dtype, rows, cols, q, scale, stream=None):
+    _check(lib().dit_quantize_h256(_p(x), int(x_dtype), int(rows), int(cols), _p(q), _p(scale), _stream(stream)))
+
+
+def dit_ln_modulate_h256q(x, x_dtype, rows, dim, shift, scale, mode, eps, q, qscale, stream=None,
+                          norm=DIT_LAYERNORM):
+    _check(lib().dit_ln_modulate_h256q(_p(x), int(x_dtype), int(rows), int(dim), int(norm), _p(shift), _p(scale),
+                                       int(mode), float(eps), _p(q), _p(qscale), _stream(stream)))
+
+
+def dit_gemm_w8a8_gated_residual(a, a_scale, w, w_scale, M, N, K, resid, resid_dtype, gate, bias, out, out_dtype,
+                                 stream=None, gate_fn=DIT_GATE_IDENTITY):
+    _check(lib().dit_gemm_w8a8_gated_residual(_p(a), _p(a_scale), _p(w), _p(w_scale), int(M), int(N), int(K),
+                                              _p(resid), int(resid_dtype), _p(gate), int(gate_fn), _p(bias), _p(out),
+                                              int(out_dtype), _stream(stream)))
+
+
+def dit_gemm_w8a8_swiglu(a, a_scale, w_gate_up, w_scale, M, F, K, u, stream=None, act=DIT_ACT_SILU):
+    _check(lib().dit_gemm_w8a8_swiglu(_p(a), _p(a_scale), _p(w_gate_up), _p(w_scale), int(M), int(F), int(K),
+                                      int(act), _p(u), _stream(stream)))
+
+
+def dit_qkv_rope_w8a8(desc, h, h_scale, w_qkv, w_scale, q_g, q_b, k_g, k_b, rope_cos, rope_sin, q, k, vt,
+                      stream=None):
+    _check(lib().dit_qkv_rope_w8a8(C.byref(desc), _p(h), _p(h_scale), _p(w_qkv), _p(w_scale), _p(q_g), _p(q_b),
+                                   _p(k_g), _p(k_b), _p(rope_cos), _p(rope_sin), _p(q), _p(k), _p(vt),
+                                   _stream(stream)))
 
 
 def dit_status_string(status: int) -> str:

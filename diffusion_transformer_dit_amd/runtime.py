@@ -51,7 +51,8 @@ def desc_of(cfg: I.DiTConfig, x_dtype: Optional[str] = None) -> N.dit_block_desc
                        gate={"identity": N.DIT_GATE_IDENTITY, "tanh": N.DIT_GATE_TANH,
                              "sigmoid": N.DIT_GATE_SIGMOID}[cfg.gate],
                        mod=N.DIT_MOD_SCALE_GATE if cfg.mod == "scale_gate" else N.DIT_MOD_SHIFT_SCALE_GATE,
-                       qk_order=N.DIT_QK_ROPE_NORM if cfg.qk_order == "rope_norm" else N.DIT_QK_NORM_ROPE)
+                       qk_order=N.DIT_QK_ROPE_NORM if cfg.qk_order == "rope_norm" else N.DIT_QK_NORM_ROPE,
+                       fmt=N.DIT_FMT_W8A8_H256 if cfg.fmt == "w8a8_h256" else N.DIT_FMT_BF16)
 
 
 def rope_tables(cfg: I.DiTConfig, pos: Optional[np.ndarray] = None, device="cuda"):
@@ -81,6 +82,30 @@ class DeviceBlock:
                     tensors[k] = to_dev_f32(v, device)
         self.t = tensors
         self.c = N.make_weights(tensors)
+
+
+PROJECTIONS = {"w_qkv": "s_qkv", "w_o": "s_o", "w_gate_up": "s_gate_up", "w_down": "s_down"}
+
+
+def quantize_h256(x, stream=None):
+    """(int8 codes, fp32 row scales) of a 2-D device tensor (bf16 or fp32) by
+    the library's dit_quantize_h256."""
+    torch = _torch()
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
+    s = torch.empty(rows, dtype=torch.float32, device=x.device)
+    N.dit_quantize_h256(x, N.DIT_F32 if x.dtype == torch.float32 else N.DIT_BF16, rows, cols, q, s, stream)
+    return q, s
+
+
+def quantize_block(blk: DeviceBlock, stream=None) -> DeviceBlock:
+    """The W8A8 H256 form of a block: its four projections replaced by their
+    int8 codes and row scales, prepared once on the device; every other
+    tensor is shared with `blk`."""
+    t = dict(blk.t)
+    for k, sk in PROJECTIONS.items():
+        t[k], t[sk] = quantize_h256(blk.t[k], stream)
+    return DeviceBlock({}, tensors=t)
 
 
 def alloc_ws(nbytes: int, device="cuda"):

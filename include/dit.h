@@ -24,7 +24,8 @@
  *     DIT_ERR_NO_DEVICE (after argument validation).
  *   - Device pointers must be 16-byte aligned (DIT_ERR_ALIGNMENT otherwise).
  *   - GEMM weights are [out_features, in_features] row-major (y = x W^T),
- *     bf16.  Accumulation is fp32 everywhere.
+ *     bf16 (or int8 codes in the W8A8 H256 format).  Accumulation is fp32
+ *     everywhere (exact int32 for int8 products).
  *   - Repeated calls with the same inputs are bitwise identical (no atomics).
  *   - Calls on different streams are thread-safe when their workspaces and
  *     outputs are distinct.
@@ -68,6 +69,17 @@ typedef enum { DIT_MOD_SHIFT_SCALE_GATE = 0, DIT_MOD_SCALE_GATE = 1 } dit_mod;
 /* qk-norm before RoPE ([ZML] §VI "QKV + norm + RoPE"), or RoPE before the
  * qk-norm ([ERNIE] §IV per-layer graph draws 3D RoPE, then qk_layernorm). */
 typedef enum { DIT_QK_NORM_ROPE = 0, DIT_QK_ROPE_NORM = 1 } dit_qk_order;
+/* Numeric format of the block's four projections (QKV, out, gate/up, down):
+ * bf16 operands, or W8A8 H256 ([ZML] §VII "Precision Formats": the I8 per-row
+ * format with a 256-point Hadamard rotation on both sides, legal because
+ * (x H)(W H)^T = x W^T for orthogonal H).  In W8A8 H256 each operand row is
+ * multiplied by blockdiag(H256) along the reduction axis (H256 = the
+ * Sylvester-Hadamard matrix / 16 on every run of 256 elements) and stored as
+ * int8 codes round-half-even(v * 127 / max|v|) with the fp32 row scale
+ * max|v| / 127 (per token for activations, per output channel for weights);
+ * the int32 products are exact and are scaled back before the same fused
+ * epilogues.  Norms, attention and the residual stream are unchanged. */
+typedef enum { DIT_FMT_BF16 = 0, DIT_FMT_W8A8_H256 = 1 } dit_fmt;
 
 /* Shape and semantic switches of one block.
  *   tokens N = batch * seq; attention runs within each sequence.
@@ -88,9 +100,11 @@ typedef enum { DIT_QK_NORM_ROPE = 0, DIT_QK_ROPE_NORM = 1 } dit_qk_order;
  *   w_dtype: must be DIT_BF16.
  *   act, gate, mod, qk_order: the semantics switches above; 0 everywhere is
  *     SwiGLU, identity gate, six chunks, norm before RoPE.
+ *   fmt: dit_fmt of the four projections (0 = bf16).
  * Built shapes: head_dim in {64, 128}; hidden % 256 == 0; ffn % 128 == 0;
  * (heads + 2 kv_heads) * head_dim % 256 == 0; cond_dim % 8 == 0; any seq >= 1
- * (ragged tails handled in every kernel). */
+ * (ragged tails handled in every kernel).  W8A8 H256 also needs ffn % 256 == 0
+ * with ceil(ffn / 1024) <= 7 or a multiple of 4 (up to 32). */
 typedef struct {
     int32_t batch, seq, hidden, heads, kv_heads, head_dim, ffn, cond_dim;
     int32_t qk_norm;
@@ -103,6 +117,7 @@ typedef struct {
     int32_t gate;      /* dit_gate */
     int32_t mod;       /* dit_mod */
     int32_t qk_order;  /* dit_qk_order */
+    int32_t fmt;       /* dit_fmt */
 } dit_block_desc;
 
 /* Device pointers to one block's parameters (NULL where marked optional).
@@ -119,7 +134,11 @@ typedef struct {
  *   w_o    [hidden, heads * head_dim] bf16.
  *   w_gate_up [2 * ffn, hidden] bf16: the ffn gate rows first, then the ffn up
  *          rows (SwiGLU: SiLU(gate) * up).
- *   w_down [hidden, ffn] bf16. */
+ *   w_down [hidden, ffn] bf16.
+ * In the W8A8 H256 format w_qkv, w_o, w_gate_up and w_down hold instead the
+ * int8 codes of those matrices (same shapes, from dit_quantize_h256 of the
+ * bf16 weights) and s_qkv, s_o, s_gate_up, s_down [rows of each] fp32 their
+ * per-row scales (16-byte aligned); the scales are ignored in bf16. */
 typedef struct {
     const void *w_ada;
     const float *b_ada;
@@ -127,6 +146,7 @@ typedef struct {
     const void *w_qkv;
     const float *q_g, *q_b, *k_g, *k_b;
     const void *w_o, *w_gate_up, *w_down;
+    const float *s_qkv, *s_o, *s_gate_up, *s_down;
 } dit_block_weights;
 
 /* ------------------------------------------------------------------------ */
@@ -326,6 +346,46 @@ int dit_gemm_gated_residual(const void *a, const void *w, int64_t M, int32_t N, 
  * bf16 [M, F].  F % 128 == 0, K % 64 == 0. */
 int dit_gemm_swiglu(const void *a, const void *w_gate_up, int64_t M, int32_t F, int32_t K,
                     int32_t act, void *u, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* W8A8 H256 stage entry points ([ZML] §VII; dit_fmt above)                  */
+/* ------------------------------------------------------------------------ */
+
+/* Per-row rotation and int8 codes: for each row r, v = x[r] blockdiag(H256),
+ * scale[r] = max|v| / 127, q[r, c] = round-half-even(v_c * (127 / max|v|))
+ * in [-127, 127] (a zero row: codes 0, scale 0), decided in fp32.
+ * x device [rows, cols] of x_dtype; q device int8 [rows, cols]; scale device
+ * fp32 [rows]; no overlap between them.  cols % 256 == 0 with
+ * ceil(cols / 1024) <= 7 or a multiple of 4 (up to 32).  Prepares the weights
+ * of the W8A8 format (once) and, inside the block, the attention and GLU
+ * outputs before their projections. */
+int dit_quantize_h256(const void *x, int32_t x_dtype, int64_t rows, int32_t cols, void *q, float *scale,
+                      void *stream);
+
+/* dit_ln_modulate followed by dit_quantize_h256 of h, with h kept in fp32
+ * registers (never written): q device int8 [rows, dim], qscale device fp32
+ * [rows].  Arguments and shapes as dit_ln_modulate. */
+int dit_ln_modulate_h256q(const void *x, int32_t x_dtype, int64_t rows, int32_t dim, int32_t norm,
+                          const float *shift, const float *scale, int32_t mode, float eps, void *q, float *qscale,
+                          void *stream);
+
+/* The projections of the W8A8 format.  a: device int8 codes [M, K] with
+ * a_scale fp32 [M]; w: device int8 codes [rows, K] with w_scale fp32 [rows]
+ * (rows = N, 2F or the QKV width), all 16-byte aligned.  The product
+ * C[m, n] = a_scale[m] w_scale[n] sum_k a[m, k] w[n, k] is summed exactly in
+ * int32, converted to fp32 and fed to the epilogue of the bf16 call of the
+ * same name (dit_gemm_gated_residual, dit_gemm_swiglu, dit_qkv_rope), whose
+ * other arguments, layouts and limits it keeps; K % 128 == 0. */
+int dit_gemm_w8a8_gated_residual(const void *a, const float *a_scale, const void *w, const float *w_scale,
+                                 int64_t M, int32_t N, int32_t K, const void *resid, int32_t resid_dtype,
+                                 const float *gate, int32_t gate_fn, const float *bias, void *out,
+                                 int32_t out_dtype, void *stream);
+int dit_gemm_w8a8_swiglu(const void *a, const float *a_scale, const void *w_gate_up, const float *w_scale,
+                         int64_t M, int32_t F, int32_t K, int32_t act, void *u, void *stream);
+int dit_qkv_rope_w8a8(const dit_block_desc *desc, const void *h, const float *h_scale, const void *w_qkv,
+                      const float *w_scale, const float *q_g, const float *q_b, const float *k_g,
+                      const float *k_b, const float *rope_cos, const float *rope_sin, void *q, void *k,
+                      void *vt, void *stream);
 
 /* ------------------------------------------------------------------------ */
 const char *dit_status_string(int status);

@@ -194,10 +194,13 @@ def quantize_h256(x):
 
 
 def w8a8_matmul(qx, sx, qw, sw):
-    """y[m, n] = sx[m] sw[n] sum_k qx[m, k] qw[n, k]: the integer products are
-    summed exactly (int64), then scaled in float64."""
-    acc = np.asarray(qx, np.int64) @ np.asarray(qw, np.int64).T
-    return acc.astype(F64) * np.asarray(sx, F64)[:, None] * np.asarray(sw, F64)[None, :]
+    """y[m, n] = sx[m] sw[n] sum_k qx[m, k] qw[n, k]: the integer dot products
+    are exact (a float64 matmul of the codes: every partial sum is an integer
+    of magnitude <= K 127^2 < 2^53), then scaled in float64."""
+    K = np.shape(qx)[-1]
+    assert K * QMAX * QMAX < 2 ** 53
+    acc = np.asarray(qx, F64) @ np.asarray(qw, F64).T
+    return acc * np.asarray(sx, F64)[:, None] * np.asarray(sw, F64)[None, :]
 
 
 def w8a8_linear(x, w):

@@ -72,6 +72,9 @@ def test_desc_accepts_every_semantics_switch():
     (dict(mod=2), N.DIT_ERR_INVALID_ARG),
     (dict(qk_order=2), N.DIT_ERR_INVALID_ARG),
     (dict(w_dtype=N.DIT_F32), N.DIT_ERR_UNSUPPORTED),
+    (dict(fmt=2), N.DIT_ERR_INVALID_ARG),
+    (dict(fmt=N.DIT_FMT_W8A8_H256, ffn=640), N.DIT_ERR_UNSUPPORTED),     # W8A8: ffn % 256
+    (dict(fmt=N.DIT_FMT_W8A8_H256, ffn=9216), N.DIT_ERR_UNSUPPORTED),    # no rotation kernel for 9 rounds
 ])
 def test_desc_validation(kw, status):
     with pytest.raises(N.DitError) as e:
@@ -248,3 +251,57 @@ def test_rope_tables_validation():
         N.dit_rope_tables(np.zeros((4, 3)), N.DIT_ROPE_INTERLEAVED, (16, 24, 20), 256.0, 64)   # widths sum != hd
     with pytest.raises(N.DitError):
         N.dit_rope_tables(np.zeros((4, 3)), N.DIT_ROPE_HALF, (16, 24, 24), 256.0, 64)          # half takes 2 axes
+
+
+def test_w8a8_workspace_and_weight_scales():
+    """The W8A8 format adds int8 copies of the attention and GLU outputs and
+    three row-scale vectors to the block workspace, and needs the weights'
+    row scales."""
+    d8 = _desc(fmt=N.DIT_FMT_W8A8_H256)
+    N_, D, F = 256, 256, 768
+    assert N.dit_block_workspace_size(d8) >= N.dit_block_workspace_size(_desc()) + N_ * (D + F) + 3 * N_ * 4
+    ws_need = N.dit_block_workspace_size(d8)
+    scales = dict(s_qkv=FAKE, s_o=FAKE, s_gate_up=FAKE, s_down=FAKE)
+    for over, st in ((dict(scales, s_o=None), N.DIT_ERR_INVALID_ARG), (dict(scales, s_down=FAKE + 4), N.DIT_ERR_ALIGNMENT)):
+        with pytest.raises(N.DitError) as e:
+            N.dit_block_forward(d8, _weights(**over), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, stream=0, ws_bytes=ws_need)
+        assert e.value.status == st, (over, e.value)
+
+
+def test_w8a8_stage_entry_validation():
+    big = FAKE + (1 << 24)
+
+    def expect(st, f, *a, **kw):
+        with pytest.raises(N.DitError) as e:
+            f(*a, stream=0, **kw)
+        assert e.value.status == st, (f.__name__, a, e.value)
+
+    expect(N.DIT_ERR_UNSUPPORTED, N.dit_quantize_h256, FAKE, N.DIT_BF16, 10, 300, big, big + (1 << 20))   # cols % 256
+    expect(N.DIT_ERR_UNSUPPORTED, N.dit_quantize_h256, FAKE, N.DIT_BF16, 10, 9216, big, big + (1 << 20))
+    expect(N.DIT_ERR_INVALID_ARG, N.dit_quantize_h256, FAKE, 7, 10, 4096, big, big + (1 << 20))
+    expect(N.DIT_ERR_INVALID_ARG, N.dit_quantize_h256, FAKE, N.DIT_BF16, 10, 4096, FAKE + 1024, big)      # x overlaps q
+    expect(N.DIT_ERR_ALIGNMENT, N.dit_quantize_h256, FAKE, N.DIT_BF16, 10, 4096, big + 8, big + (1 << 20))
+    expect(N.DIT_ERR_UNSUPPORTED, N.dit_ln_modulate_h256q, FAKE, 0, 10, 8448, FAKE, FAKE, 0, 1e-6, big, big + 4096)
+    expect(N.DIT_ERR_INVALID_ARG, N.dit_ln_modulate_h256q, FAKE, 0, 10, 256, FAKE, None, 0, 1e-6, big, big + 4096)
+    expect(N.DIT_ERR_UNSUPPORTED, N.dit_gemm_w8a8_gated_residual, FAKE, FAKE, FAKE, FAKE, 256, 256, 192, None, 0,
+           None, None, big, 0)                                                                             # K % 128
+    expect(N.DIT_ERR_UNSUPPORTED, N.dit_gemm_w8a8_gated_residual, FAKE, FAKE, FAKE, FAKE, 256, 100, 256, None, 0,
+           None, None, big, 0)
+    expect(N.DIT_ERR_INVALID_ARG, N.dit_gemm_w8a8_gated_residual, FAKE, None, FAKE, FAKE, 256, 256, 256, None, 0,
+           None, None, big, 0)                                                                             # a_scale
+    expect(N.DIT_ERR_ALIGNMENT, N.dit_gemm_w8a8_swiglu, FAKE, FAKE + 4, FAKE, FAKE, 256, 128, 256, big)
+    expect(N.DIT_ERR_INVALID_ARG, N.dit_gemm_w8a8_swiglu, FAKE, FAKE, FAKE, FAKE, 256, 128, 256, big, act=5)
+    expect(N.DIT_ERR_INVALID_ARG, N.dit_qkv_rope_w8a8, _desc(fmt=N.DIT_FMT_W8A8_H256), FAKE, None, FAKE, FAKE, FAKE,
+           FAKE, FAKE, FAKE, FAKE, FAKE, big, big, big)
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd") and os.access("/dev/kfd", os.R_OK), reason="a GPU may be present")
+def test_w8a8_valid_calls_report_no_device():
+    big = FAKE + (1 << 24)
+    for f, a in ((N.dit_quantize_h256, (FAKE, N.DIT_BF16, 10, 4096, big, big + (1 << 20))),
+                 (N.dit_quantize_h256, (FAKE, N.DIT_F32, 10, 12288, big, big + (1 << 20))),
+                 (N.dit_ln_modulate_h256q, (FAKE, 0, 10, 6144, FAKE, FAKE, 0, 1e-6, big, big + (1 << 20))),
+                 (N.dit_gemm_w8a8_swiglu, (FAKE, FAKE, FAKE, FAKE, 256, 128, 256, big))):
+        with pytest.raises(N.DitError) as e:
+            f(*a, stream=0)
+        assert e.value.status == N.DIT_ERR_NO_DEVICE, f.__name__

@@ -1,0 +1,320 @@
+"""The W8A8 H256 format (zml-flow-rs page §VII: int8 codes per row with a
+256-point Hadamard rotation on both operands) on the GPU, through the C ABI,
+against the oracle.
+
+Codes are integers decided by floating point.  Both sides decide them in
+float32, but from differently rounded values (the kernels rotate with fp32
+butterflies and normalise in fp32, the oracle works in float64 and rounds the
+result), so a code may differ by one where its value lies within rounding of
+a half-integer.  Codes are compared exactly everywhere else; near such ties
+they must differ by at most one.  The GEMM stages are fed the oracle's own
+codes, so their integer sums are exact and only the fp32 dequantisation and
+the epilogue roundings remain.
+
+At block level the kernels quantize the bf16-rounded attention and GLU
+outputs (bf16 rounding points of the path), the oracle its float64 ones; the
+codes then differ wherever that rounding crosses a code boundary, which
+redraws part of the quantisation noise.  The branch delta is therefore held
+to the bf16 bar plus the format's own quantisation error (oracle W8A8 vs
+oracle float64, measured on the same inputs); `out` keeps the plain bar."""
+import numpy as np
+import pytest
+
+from diffusion_transformer_dit_amd import inputs as I
+from diffusion_transformer_dit_amd import native as N
+from diffusion_transformer_dit_amd import runtime as R
+from oracle import dit as O
+
+from gpu_helpers import SMALL, assert_parity, metrics, say
+
+pytestmark = pytest.mark.gpu
+
+TIE = 2e-3          # |code value - half-integer| below which a code may differ by one
+DELTA_EXCESS = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    R.require_gpu()
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def _dev_i8(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, np.int8)).to("cuda")
+
+
+def _host(t):
+    return t.cpu().numpy()
+
+
+def _rows(r, rows, cols):
+    """N(0,1) rows with magnitudes spread over e^{+-2}, one zero row and one
+    row dominated by a single outlier."""
+    x = r.standard_normal((rows, cols)).astype(np.float32) * np.exp(r.standard_normal((rows, 1))).astype(np.float32)
+    x[min(5, rows - 1)] = 0.0
+    if rows > 7:
+        x[7, 3] = 3.0e3
+    return x
+
+
+def _check_codes(q, s, v, what):
+    """q, s from the GPU against the oracle's I8 of the (already rotated) v."""
+    ref_q, ref_s = O.quantize_rows(v)
+    np.testing.assert_allclose(s, ref_s, rtol=2e-6, atol=0, err_msg=f"{what}: scales")
+    assert (s[ref_s == 0] == 0).all()
+    v32 = np.asarray(v, np.float32)
+    amax = np.abs(v32).max(axis=-1, keepdims=True)
+    inv = np.where(amax > 0, np.float32(127) / np.where(amax > 0, amax, 1), 0).astype(np.float32)
+    r = (v32 * inv).astype(np.float64)
+    near = np.abs(r - np.floor(r) - 0.5) < TIE
+    d = q.astype(np.int32) - ref_q.astype(np.int32)
+    bad = d != 0
+    say(f"  {what}: {int(bad.sum())} of {d.size} codes differ (all within {TIE} of a tie: "
+        f"{bool(not (bad & ~near).any())}), scale max rel {np.abs(s / np.where(ref_s == 0, 1, ref_s) - 1).max():.2e}")
+    assert np.abs(d).max() <= 1, what
+    assert not (bad & ~near).any(), what
+    assert bad.mean() < 1e-3, what
+
+
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cols", [256, 768, 1024, 3328, 4096, 6144, 12288, 16384])
+@pytest.mark.parametrize("xdt", ["bf16", "f32"])
+def test_quantize_h256_vs_oracle(cols, xdt):
+    import torch
+    rows = 37
+    say(f"quantize_h256 rows={rows} cols={cols} x={xdt}")
+    x = _rows(np.random.default_rng(cols), rows, cols)
+    if xdt == "bf16":
+        x = I.bf16_round(x)
+        xd = R.to_dev_bf16(x)
+    else:
+        xd = R.to_dev_f32(x)
+    q = torch.empty((rows, cols), dtype=torch.int8, device="cuda")
+    s = torch.empty(rows, dtype=torch.float32, device="cuda")
+    N.dit_quantize_h256(xd, N.DIT_BF16 if xdt == "bf16" else N.DIT_F32, rows, cols, q, s)
+    _sync()
+    _check_codes(_host(q), _host(s), O.rotate_h256(x.astype(np.float64)), f"quantize {cols} {xdt}")
+    assert (_host(q)[5] == 0).all() and _host(s)[5] == 0.0        # the zero row
+
+
+@pytest.mark.parametrize("dim", [256, 1024, 4096, 6144])
+@pytest.mark.parametrize("xdt,norm,mode", [("f32", "layernorm", 0), ("bf16", "layernorm", 0), ("f32", "rmsnorm", 0),
+                                           ("f32", "layernorm", 1), ("bf16", "rmsnorm", 1)])
+def test_ln_modulate_h256q_vs_oracle(dim, xdt, norm, mode):
+    import torch
+    rows = 37
+    say(f"ln_modulate_h256q rows={rows} dim={dim} x={xdt} {norm} mode={mode}")
+    r = np.random.default_rng(dim + mode)
+    x = (r.standard_normal((rows, dim)) * 2.0 + 0.5).astype(np.float32)
+    if xdt == "bf16":
+        x = I.bf16_round(x)
+    shift = (0.3 * r.standard_normal(dim)).astype(np.float32)
+    scale = (0.3 * r.standard_normal(dim)).astype(np.float32)
+    nulls = mode == 1 and norm == "rmsnorm"        # mode 1 with no affine at all
+    sh, sc = (None, None) if nulls else (shift, scale)
+    spec = I.C1.replace(norm=norm)
+    n = O.norm(x.astype(np.float64), spec)
+    if nulls:
+        h = n
+    elif mode == 0:
+        h = O.modulate(n, shift.astype(np.float64), scale.astype(np.float64))
+    else:
+        h = n * scale + shift
+    q = torch.empty((rows, dim), dtype=torch.int8, device="cuda")
+    s = torch.empty(rows, dtype=torch.float32, device="cuda")
+    N.dit_ln_modulate_h256q(R.to_dev_f32(x) if xdt == "f32" else R.to_dev_bf16(x),
+                            N.DIT_F32 if xdt == "f32" else N.DIT_BF16, rows, dim, R.to_dev_f32(sh), R.to_dev_f32(sc),
+                            mode, 1e-6, q, s, norm=N.DIT_RMSNORM if norm == "rmsnorm" else N.DIT_LAYERNORM)
+    _sync()
+    _check_codes(_host(q), _host(s), O.rotate_h256(h), f"ln_q8 {dim} {xdt} {norm} mode {mode}")
+
+
+# ---------------------------------------------------------------------------
+def _q8_operands(M, N_rows, K, seed):
+    r = np.random.default_rng(seed)
+    a = r.standard_normal((M, K)).astype(np.float32)
+    w = (r.standard_normal((N_rows, K)) * 0.02).astype(np.float32)
+    qa, sa = O.quantize_h256(a)
+    qw, sw = O.quantize_h256(w)
+    return qa, sa, qw, sw
+
+
+@pytest.mark.parametrize("M,N_,K,rdt,odt,gate_fn", [
+    (300, 256, 512, "f32", "f32", N.DIT_GATE_IDENTITY),    # 256x256 tile, ragged rows
+    (300, 384, 256, "bf16", "f32", N.DIT_GATE_TANH),      # 256x128 tile
+    (520, 512, 1024, None, "f32", N.DIT_GATE_SIGMOID),    # no residual
+    (4170, 4096, 4096, "f32", "f32", N.DIT_GATE_IDENTITY),  # the 320-row tile (joint sequence rows)
+    (1000, 768, 3072, "bf16", "bf16", N.DIT_GATE_IDENTITY),
+])
+def test_gemm_w8a8_gated_residual(M, N_, K, rdt, odt, gate_fn):
+    import torch
+    say(f"gemm_w8a8_gated_residual M={M} N={N_} K={K} resid={rdt} out={odt} gate_fn={gate_fn}")
+    qa, sa, qw, sw = _q8_operands(M, N_, K, M + K)
+    r = np.random.default_rng(7)
+    res = None if rdt is None else r.standard_normal((M, N_)).astype(np.float32)
+    if rdt == "bf16":
+        res = I.bf16_round(res)
+    g = r.standard_normal(N_).astype(np.float32)
+    b = (0.1 * r.standard_normal(N_)).astype(np.float32)
+    dres = None if res is None else (R.to_dev_f32(res) if rdt == "f32" else R.to_dev_bf16(res))
+    out = torch.empty((M, N_), dtype=torch.float32 if odt == "f32" else torch.bfloat16, device="cuda")
+    N.dit_gemm_w8a8_gated_residual(_dev_i8(qa), R.to_dev_f32(sa), _dev_i8(qw), R.to_dev_f32(sw), M, N_, K, dres,
+                                   N.DIT_F32 if rdt != "bf16" else N.DIT_BF16, R.to_dev_f32(g), R.to_dev_f32(b), out,
+                                   N.DIT_F32 if odt == "f32" else N.DIT_BF16, gate_fn=gate_fn)
+    _sync()
+    rows = np.arange(M) if M <= 1024 else np.unique(np.r_[0, 1, 255, 256, 319, 320, 2047, M - 75, M - 1,
+                                                          np.random.default_rng(1).choice(M, 40, replace=False)])
+    y = O.w8a8_matmul(qa[rows], sa[rows], qw, sw)
+    kind = {N.DIT_GATE_IDENTITY: "identity", N.DIT_GATE_TANH: "tanh", N.DIT_GATE_SIGMOID: "sigmoid"}[gate_fn]
+    ref = O.gated_residual(0.0 if res is None else res[rows], O.gate_fn(g.astype(np.float64), kind), y) + b
+    got = R.to_host_f32(out)[rows]
+    if odt == "f32":
+        assert_parity(got, ref, max_rel=1e-5, min_cos=0.9999999, what="w8a8 residual")
+    else:
+        assert_parity(got, ref, max_rel=8e-3, min_cos=0.99999, what="w8a8 residual (bf16 out)")
+
+
+@pytest.mark.parametrize("M,F,K,act", [(300, 384, 512, N.DIT_ACT_SILU), (4096, 1024, 4096, N.DIT_ACT_SILU),
+                                       (270, 256, 256, N.DIT_ACT_GELU_TANH)])
+def test_gemm_w8a8_swiglu(M, F, K, act):
+    import torch
+    say(f"gemm_w8a8_swiglu M={M} F={F} K={K} act={act}")
+    qa, sa, qw, sw = _q8_operands(M, 2 * F, K, F + K)
+    u = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    N.dit_gemm_w8a8_swiglu(_dev_i8(qa), R.to_dev_f32(sa), _dev_i8(qw), R.to_dev_f32(sw), M, F, K, u, act=act)
+    _sync()
+    ref = O.glu(O.w8a8_matmul(qa, sa, qw, sw), "gelu_tanh" if act == N.DIT_ACT_GELU_TANH else "silu")
+    assert_parity(R.to_host_f32(u), ref, max_rel=8e-3, min_cos=0.99999, what="w8a8 swiglu")
+
+
+@pytest.mark.parametrize("name", ["c1_tiny", "hd128_ragged400", "gqa3_b2_ragged300", "half_hd128_rope_first",
+                                  "c1_rms"])
+def test_qkv_rope_w8a8(name):
+    """The QKV epilogue (qk-norm, RoPE, V^T) on the dequantized int8 product."""
+    import torch
+    cfg = SMALL[name].replace(fmt="w8a8_h256")
+    say(f"qkv_rope_w8a8 {name}")
+    r = np.random.default_rng(3)
+    h = r.standard_normal((cfg.tokens, cfg.hidden))
+    w = I.block_weights(cfg, 0, affine_random=True)
+    qh, sh = O.quantize_h256(h)
+    qw, sw = O.quantize_h256(w["w_qkv"])
+    w = dict(w, w_qkv_q8=(qw, sw))
+    pos = I.positions(cfg)
+    B, S, H, Hk, hd = cfg.batch, cfg.seq, cfg.heads, cfg.kv_heads, cfg.head_dim
+    spad = N.dit_seq_pad(S)
+    q = torch.empty((B, H, S, hd), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty((B, Hk, S, hd), dtype=torch.bfloat16, device="cuda")
+    vt = torch.full((B, Hk, hd, spad), float("nan"), dtype=torch.bfloat16, device="cuda")
+    cos, sin = R.rope_tables(cfg, pos)
+    f = R.to_dev_f32
+    N.dit_qkv_rope_w8a8(R.desc_of(cfg), _dev_i8(qh), f(sh), _dev_i8(qw), f(sw), f(w["q_g"]), f(w["q_b"]),
+                        f(w["k_g"]), f(w["k_b"]), cos, sin, q, k, vt)
+    _sync()
+    qo, ko, vo = O.block_qkv(h, w, cfg, pos)      # the oracle quantizes h to the same codes
+    qg = R.to_host_f32(q).transpose(0, 2, 1, 3).reshape(B * S, H, hd)
+    kg = R.to_host_f32(k).transpose(0, 2, 1, 3).reshape(B * S, Hk, hd)
+    vtg = R.to_host_f32(vt)
+    vg = vtg[..., :S].transpose(0, 3, 1, 2).reshape(B * S, Hk, hd)
+    assert (vtg[..., S:] == 0).all()
+    for nm, g, o in (("q", qg, qo), ("k", kg, ko), ("v", vg, vo)):
+        assert_parity(g, o, max_rel=1e-2, min_cos=0.99999, what=f"{name}:{nm}")
+
+
+# ---------------------------------------------------------------------------
+def _block_w8a8(cfg, w, x, c, pos):
+    blk = R.quantize_block(R.DeviceBlock(w))
+    xd = R.to_dev_f32(x) if cfg.x_dtype == "f32" else R.to_dev_bf16(x)
+    cos, sin = R.rope_tables(cfg, pos)
+    o = R.block_forward(cfg, blk, xd, R.to_dev_f32(c) if cfg.cond_dim else None, cos, sin)
+    _sync()
+    return R.to_host_f32(o)
+
+
+def _check_block(cfg, got, ref, ref64, x):
+    """`out` to the plain bar; delta to the bf16 bar plus the format's own
+    quantisation error (oracle W8A8 against oracle float64)."""
+    x = np.asarray(x, np.float64)
+    assert_parity(got, ref, what=f"{cfg.name} out")
+    dm = metrics(got - x, ref - x)
+    qerr = metrics(ref - x, ref64 - x)["rel_rms"]
+    floor = 0.0
+    if cfg.x_dtype == "bf16":
+        floor = np.linalg.norm(I.bf16_round(np.asarray(ref, np.float32)) - ref) / np.linalg.norm(ref - x)
+    excess = np.sqrt(max(dm["rel_rms"] ** 2 - floor ** 2, 0.0))
+    gate = metrics(got - x, ref64 - x)
+    say(f"  delta {cfg.name}: vs oracle W8A8 rel_rms={dm['rel_rms']:.3e} cos={dm['cos']:.6f} "
+        f"(out-rounding floor {floor:.3e}, excess {excess:.3e}); W8A8 quantisation error {qerr:.3e}; "
+        f"GPU W8A8 vs float64 block rel_rms={gate['rel_rms']:.3e}")
+    assert excess <= DELTA_EXCESS + qerr, (dm, floor, qerr)
+
+
+@pytest.mark.parametrize("name", ["c1_tiny", "c1_ragged200", "hd128_ragged400", "gqa3_b2_ragged300", "vit_b2_f32",
+                                  "c1_f32x_t3", "tiny_joint", "qwen_like"])
+def test_block_w8a8_small_vs_oracle(name):
+    cfg = SMALL[name].replace(fmt="w8a8_h256")
+    say(f"block w8a8 {name}: N={cfg.tokens} D={cfg.hidden} F={cfg.ffn}")
+    w = I.block_weights(cfg, 0, affine_random=True)
+    x, c, pos = I.block_x(cfg), I.cond(cfg), I.positions(cfg)
+    got = _block_w8a8(cfg, w, x, c, pos)
+    ref = O.block_forward(x, c, w, cfg, pos)
+    ref64 = O.block_forward(x, c, w, cfg.replace(fmt="bf16"), pos)
+    _check_block(cfg, got, ref, ref64, x)
+
+
+def test_block_w8a8_zero_adaln_is_identity_bitwise():
+    cfg = SMALL["hd128_ragged400"].replace(fmt="w8a8_h256")
+    w = I.block_weights(cfg, 0, zero_ada=True)
+    x, c = I.block_x(cfg), I.cond(cfg)
+    np.testing.assert_array_equal(_block_w8a8(cfg, w, x, c, I.positions(cfg)), x)
+
+
+def test_block_w8a8_full_size_sampled():
+    cfg = I.C3_W8A8
+    say(f"full-size block {cfg.name}: N={cfg.tokens} D={cfg.hidden}")
+    w = I.block_weights(cfg, 0)
+    x, c, pos = I.block_x(cfg), I.cond(cfg), I.positions(cfg)
+    got = _block_w8a8(cfg, w, x, c, pos)
+    assert np.isfinite(got).all()
+    rows = np.unique(np.r_[0, 1, 31, 32, 255, 256, 2048, cfg.tokens - 257, cfg.tokens - 1,
+                           np.random.default_rng(0).choice(cfg.tokens, 12, replace=False)])
+    ref = O.block_forward(x, c, w, cfg, pos, dtype=np.float32, rows=rows)
+    ref64 = O.block_forward(x, c, w, I.C3, pos, dtype=np.float32, rows=rows)
+    _check_block(cfg, got[rows], ref, ref64, x[rows])
+
+
+def test_stack_w8a8_step_vs_oracle():
+    """A 3-layer stack (shared AdaLN linear) with every block in the W8A8
+    format: one denoising step's velocity against the oracle."""
+    import torch
+    cfg = I.C1.replace(name="stack_small_w8a8", cfg_id=20, x_dtype="f32", layers=3, latent_dim=128,
+                       grid=(1, 16, 20), fmt="w8a8_h256")
+    shared = I.shared_ada(cfg)
+    blocks = [I.stack_block_weights(cfg, l, shared) for l in range(cfg.layers)]
+    edges = I.stack_edges(cfg)
+    dev_shared = {"w_ada": R.to_dev_bf16(shared["w_ada"]), "b_ada": R.to_dev_f32(shared["b_ada"])}
+    dblocks = []
+    for w in blocks:
+        t = {k: (None if v is None else (R.to_dev_bf16(v) if k in R._BF16_KEYS else R.to_dev_f32(v)))
+             for k, v in w.items() if k not in ("w_ada", "b_ada")}
+        t.update(dev_shared)
+        dblocks.append(R.quantize_block(R.DeviceBlock(None, tensors=t)))
+    stack = R.DeviceStack(cfg, dblocks, R.upload_edges(edges))
+    pos = I.positions(cfg)
+    lat = I.latent(cfg)
+    sig = O.flowmatch_sigmas(8, 4.0)
+    cos, sin = R.rope_tables(cfg, pos)
+    cond = torch.empty(cfg.cond_dim, dtype=torch.float32, device="cuda")
+    N.dit_timestep_embedding(float(np.float32(1000.0 * sig[2])), cfg.cond_dim, cond)
+    vel = torch.empty((cfg.tokens, cfg.latent_dim), dtype=torch.float32, device="cuda")
+    stack.step(R.to_dev_f32(lat), cond, cos, sin, vel)
+    _sync()
+    ref = O.stack_step(lat, float(np.float32(sig[2])), blocks, edges, cfg, pos)
+    ref64 = O.stack_step(lat, float(np.float32(sig[2])), blocks, edges, cfg.replace(fmt="bf16"), pos)
+    say(f"  W8A8 stack velocity vs float64 stack: {metrics(R.to_host_f32(vel), ref64)}")
+    assert_parity(R.to_host_f32(vel), ref, max_rel=2e-2, min_cos=0.9995, what="w8a8 stack velocity")
