@@ -26,7 +26,23 @@ from diffusion_transformer_dit_amd import inputs as I  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 MFMA
 METRIC = "s/denoise-step (36x4096 DiT, 4096 tok) + bf16 MFMA util % of peak"
+
+
+def _event_us(fn, reps):
+    """Average device time of fn() over reps launches, HIP events on torch's current stream."""
+    import torch
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1000.0 / reps
 
 
 def block_flops(cfg) -> dict:
@@ -165,8 +181,70 @@ def time_block(cfg, blk, reps=10):
     assert torch.isfinite(out).all().item()
     us = e0.elapsed_time(e1) * 1000.0 / reps
     tf = sum(block_flops(cfg).values()) / (us * 1e-6) / 1e12
+    if cfg.fmt == "w8a8_h256":       # int8 projections (attention stays bf16): against the int8 peak
+        return {"tokens": cfg.seq, "us": round(us, 1), "achieved": round(tf, 1), "unit": "TOP/s",
+                "frac": round(tf / PEAK_INT8_TOPS, 4)}
     return {"tokens": cfg.seq, "us": round(us, 1), "achieved": round(tf, 1), "unit": "TFLOP/s",
             "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
+def time_kernels_w8a8(cfg, qblk, reps=20):
+    """The W8A8 H256 kernels at the stack's shapes (int8 codes of the block's
+    projections in qblk): the fused norm + rotation + quantize, the rotation +
+    quantize of the attention and GLU outputs, and the four int8 GEMMs."""
+    import torch
+    from diffusion_transformer_dit_amd import native as N
+    from diffusion_transformer_dit_amd import runtime as R
+    dev = "cuda"
+    Nt, D, F, hd = cfg.tokens, cfg.hidden, cfg.ffn, cfg.head_dim
+    H, Hk, S, B = cfg.heads, cfg.kv_heads, cfg.seq, cfg.batch
+    t = qblk.t
+    desc = R.desc_of(cfg, "f32")
+    bf, i8 = torch.bfloat16, torch.int8
+    g = torch.Generator(device=dev).manual_seed(7)
+    x = torch.randn((Nt, D), generator=g, device=dev)
+    m = torch.randn(6 * D, generator=g, device=dev) * 0.1
+    att = torch.randn((Nt, H * hd), generator=g, device=dev).to(bf)
+    u = torch.randn((Nt, F), generator=g, device=dev).to(bf)
+    hq, hs = torch.empty((Nt, D), dtype=i8, device=dev), torch.empty(Nt, device=dev)
+    aq, as_ = R.quantize_h256(att)
+    uq, us = R.quantize_h256(u)
+    q = torch.empty((B, H, S, hd), dtype=bf, device=dev)
+    k = torch.empty((B, Hk, S, hd), dtype=bf, device=dev)
+    vt = torch.empty((B, Hk, hd, N.dit_seq_pad(S)), dtype=bf, device=dev)
+    x1 = torch.empty((Nt, D), device=dev)
+    u2 = torch.empty((Nt, F), dtype=bf, device=dev)
+    cos, sin = R.rope_tables(cfg)
+    N.dit_ln_modulate_h256q(x, N.DIT_F32, Nt, D, m, m[D:], 0, cfg.eps, hq, hs)
+    launches = {
+        "ln_modulate_h256q": (lambda: N.dit_ln_modulate_h256q(x, N.DIT_F32, Nt, D, m, m[D:], 0, cfg.eps, hq, hs),
+                              "hbm", Nt * D * 4 + Nt * D + Nt * 4),
+        "quantize_h256_attn": (lambda: N.dit_quantize_h256(att, N.DIT_BF16, Nt, H * hd, aq, as_), "hbm",
+                               Nt * H * hd * 3 + Nt * 4),
+        "quantize_h256_glu": (lambda: N.dit_quantize_h256(u, N.DIT_BF16, Nt, F, uq, us), "hbm", Nt * F * 3 + Nt * 4),
+        "gemm_qkv": (lambda: N.dit_qkv_rope_w8a8(desc, hq, hs, t["w_qkv"], t["s_qkv"], t["q_g"], t["q_b"], t["k_g"],
+                                                 t["k_b"], cos, sin, q, k, vt), "mfma", None),
+        "gemm_out_proj": (lambda: N.dit_gemm_w8a8_gated_residual(aq, as_, t["w_o"], t["s_o"], Nt, D, H * hd, x,
+                                                                 N.DIT_F32, m[2 * D:], None, x1, N.DIT_F32),
+                          "mfma", None),
+        "gemm_swiglu": (lambda: N.dit_gemm_w8a8_swiglu(hq, hs, t["w_gate_up"], t["s_gate_up"], Nt, F, D, u2),
+                        "mfma", None),
+        "gemm_down": (lambda: N.dit_gemm_w8a8_gated_residual(uq, us, t["w_down"], t["s_down"], Nt, D, F, x1,
+                                                             N.DIT_F32, m[5 * D:], None, x, N.DIT_F32), "mfma", None),
+    }
+    fl = block_flops(cfg)
+    out = {}
+    for name, (fn, bound, nbytes) in launches.items():
+        us_ = _event_us(fn, reps)
+        if bound == "mfma":
+            tops = fl[name] / (us_ * 1e-6) / 1e12
+            out[name] = {"us": round(us_, 2), "bound": "mfma", "achieved": round(tops, 1), "unit": "TOP/s",
+                         "frac": round(tops / PEAK_INT8_TOPS, 4), "work": fl[name]}
+        else:
+            gbs = nbytes / (us_ * 1e-6) / 1e9
+            out[name] = {"us": round(us_, 2), "bound": "hbm", "achieved": round(gbs, 1), "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "work": nbytes}
+    return out
 
 
 def canary_tflops(reps=10):
@@ -345,6 +423,40 @@ def main():
     gms = gwall * 1000.0 / args.steps
     assert torch.isfinite(lat).all().item(), "non-finite latent (graph replay)"
     loop.close()
+
+    # The same stack with the four projections of every block in the W8A8 H256
+    # format (int8 codes, Hadamard-256 rotation, int8 MFMA): a separate
+    # reduced-precision measurement, never the headline value.
+    print("[bench] W8A8 H256 stack (weights quantized on the device)", file=sys.stderr, flush=True)
+    cfg8 = I.C4_W8A8
+    qblocks = [R.quantize_block(b) for b in stack.blocks]
+    stack8 = R.DeviceStack(cfg8, qblocks, stack.edges)
+    kern8 = time_kernels_w8a8(cfg8, qblocks[0])
+    blocks8 = {"latent_4096": time_block(cfg8, qblocks[0]),
+               "joint_4170": time_block(I.C3_JOINT.replace(x_dtype="f32", fmt="w8a8_h256"), qblocks[0])}
+    lat.copy_(R.to_dev_f32(I.latent(cfg)))
+
+    def one_step8(i):
+        j = i % I.STACK_STEPS
+        N.dit_timestep_embedding(1000.0 * float(sig[j]), cfg.cond_dim, cond)
+        stack8.step(lat, cond, cos, sin, vel)
+        N.euler_flowmatch_update(lat, vel, lat.numel(), float(sig[j]), float(sig[j + 1]))
+
+    for i in range(args.warmup):
+        one_step8(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step8(args.warmup + i)
+    torch.cuda.synchronize()
+    ms8 = (time.perf_counter() - t0) * 1000.0 / args.steps
+    assert torch.isfinite(lat).all().item(), "non-finite latent (W8A8)"
+    w8a8 = {"ms_per_step": round(ms8, 3), "speedup_vs_bf16": round(ms / ms8, 3),
+            "ops_util_pct_of_int8_peak": round(100.0 * step_flops(cfg) / (ms8 * 1e-3) / (PEAK_INT8_TOPS * 1e12), 2),
+            "block": blocks8, "kernels": kern8}
+    print(f"[bench] w8a8: {json.dumps({k: v for k, v in w8a8.items() if k != 'kernels'})}", file=sys.stderr,
+          flush=True)
+    del stack8, qblocks
     canary_after = canary_tflops()
 
     flops = step_flops(cfg)
@@ -382,6 +494,8 @@ def main():
         "canary_tflops": {"before": canary_before, "after": canary_after,
                           "drift_ok": abs(canary_after - canary_before) <= 0.07 * canary_before},
         "cpu_baseline": cpu,
+        # the four projections in int8 with the Hadamard-256 rotation (reduced precision: context, not value)
+        "w8a8_h256": w8a8,
     }
     print(json.dumps(line), flush=True)
 

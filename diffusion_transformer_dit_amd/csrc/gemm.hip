@@ -110,8 +110,7 @@ __device__ __forceinline__ int acc_row(int i, int e, int lhalf);
 template <class T, class RowMap, class Epi>
 __global__ __launch_bounds__(T::kThreads, 1)
 void gemm_kernel(const void *__restrict__ A, const void *__restrict__ W, int M, int K, int w_rows,
-                 int tiles_m, int tiles_n, RowMap rowmap, Epi epi, const float *__restrict__ a_scale,
-                 const float *__restrict__ w_scale) {
+                 int tiles_m, int tiles_n, RowMap rowmap, Epi epi, const float *a_scale, const float *w_scale) {
 #if defined(__HIP_DEVICE_COMPILE__)   // buffer resources exist only in the device pass
     constexpr int kMain = T::NS * T::kStageBytes;
     constexpr int kLds = Epi::template lds_bytes<T>() > kMain ? Epi::template lds_bytes<T>() : kMain;
@@ -253,7 +252,8 @@ void gemm_kernel(const void *__restrict__ A, const void *__restrict__ W, int M, 
     wait_vmcnt<0>();      // retire the trailing (never read) loads before LDS is reused
     __syncthreads();
 
-    if constexpr (T::ES == 2) {
+    if constexpr (T::ES == 2 || Epi::kDequant) {
+        // bf16, or an epilogue that dequantizes row block by row block itself
         epi.template apply<T>(acc, m0 + wm * T::kWaveM, tn, wn, lane, M, smem);
     } else {
         // dequantize in place: C[m, n] = acc * (a_scale[m] w_scale[n]), the int32
@@ -274,6 +274,9 @@ void gemm_kernel(const void *__restrict__ A, const void *__restrict__ W, int M, 
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = (float)iv[e] * (sa[e] * sw[j]);
             }
+            // compiler fence (a_scale is not restrict-qualified): the row scales of
+            // later blocks are not hoisted next to all 128 accumulators
+            asm volatile("" ::: "memory");
         }
         epi.template apply<T>(acc, m0 + wm * T::kWaveM, tn, wn, lane, M, smem);
     }
@@ -287,13 +290,19 @@ __device__ __forceinline__ int acc_row(int i, int e, int lhalf) { return i * 32 
 // ---------------------------------------------------------------------------
 // epilogue: out = resid + gate * acc + bias
 // ---------------------------------------------------------------------------
-template <typename TR, typename TO>
+// Q8: the accumulators hold int32 sums of int8 codes; each row block is
+// dequantized here with the row scales a_scale[m] w_scale[n], next to the
+// residual rows it is added to (a separate pass over all 128 accumulators
+// first makes the compiler hoist all 64 row-scale loads and spill).
+template <typename TR, typename TO, bool Q8 = false>
 struct EpiResidual {
     const TR *resid;
     const float *gate, *bias;
     TO *out;
     int N;
     int gate_fn;      // 0 identity, 1 tanh, 2 sigmoid, applied to gate[n]
+    const float *a_scale = nullptr, *w_scale = nullptr;   // Q8 only
+    static constexpr bool kDequant = Q8;
     template <class T> static constexpr int lds_bytes() { return 0; }
     template <class T>
     __device__ __forceinline__ void apply(floatx16 (&acc)[T::TM][T::TN], int row0, int tn, int wn, int lane, int M,
@@ -305,6 +314,7 @@ struct EpiResidual {
         for (int j = 0; j < T::TN; ++j) {
             const int col = col0 + j * 32 + lrow;
             g[j] = gate ? gate_f(gate[col], gate_fn) : 1.0f;
+            if constexpr (Q8) g[j] *= w_scale[col];
             bb[j] = bias ? bias[col] : 0.0f;
         }
         // out may alias resid (in-place update), but every element is read and
@@ -327,6 +337,17 @@ struct EpiResidual {
                 for (int j = 0; j < T::TN; ++j)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) r[j][e] = 0.0f;
+            }
+            if constexpr (Q8) {
+                float sa[16];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) sa[e] = a_scale[min(row0 + acc_row(i, e, lhalf), M - 1)];
+#pragma unroll
+                for (int j = 0; j < T::TN; ++j) {
+                    const intx16 iv = __builtin_bit_cast(intx16, acc[i][j]);   // whole-vector cast (see kernel)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[i][j][e] = (float)iv[e] * sa[e];
+                }
             }
             // wave-uniform: all 32 rows of block i in range -> straight-line stores
             if (row0 + i * 32 + 32 <= M) {
@@ -356,6 +377,7 @@ struct EpiResidual {
 // ---------------------------------------------------------------------------
 template <int ACT>     // 0: SiLU (SwiGLU), 1: clamped GELU-tanh
 struct EpiSwiglu {
+    static constexpr bool kDequant = false;
     bf16 *u;
     int F;
     template <class T> static constexpr int lds_bytes() { return 0; }
@@ -412,6 +434,7 @@ constexpr int kQkvStride = 260;   // floats per staged row: 256 + 4, so 16 row-p
 
 template <int HD, bool RMS, bool RF>   // qk-norm kind RMSNorm; RoPE before the qk-norm
 struct EpiQkv {
+    static constexpr bool kDequant = false;
     QkvEpiArgs e;
     static constexpr int kStageBytes = 2 * 64 * kQkvStride * 4;
     static constexpr int kHeadBlock = 64 * HD * 2;        // bf16 bytes of one head x 64 tokens
@@ -729,7 +752,7 @@ static hipError_t residual_typed(const void *a, const void *w, int64_t M, int N,
     using TT = typename std::conditional<SC::kQ8, Tile8wTallQ, Tile8wTall>::type;
     using TS = typename std::conditional<SC::kQ8, Tile8wQ, Tile8w>::type;
     using TN = typename std::conditional<SC::kQ8, TileNarrowQ, TileNarrow>::type;
-    EpiResidual<TR, TO> epi{(const TR *)resid, gate, bias, (TO *)out, N, gate_fn};
+    EpiResidual<TR, TO, SC::kQ8> epi{(const TR *)resid, gate, bias, (TO *)out, N, gate_fn, sc.a, sc.w};
     if (N % 256 == 0 && prefer_tall(M, N)) return run<TT>(a, w, M, N, K, RowsIdentity{256}, epi, s, sc.a, sc.w);
     if (N % 256 == 0) return run<TS>(a, w, M, N, K, RowsIdentity{256}, epi, s, sc.a, sc.w);
     return run<TN>(a, w, M, N, K, RowsIdentity{128}, epi, s, sc.a, sc.w);

@@ -25,22 +25,23 @@
 
 namespace dit {
 
-// v of lane (lane ^ M) inside each row of 16 lanes
+// v of lane (lane ^ M) inside each row of 16 lanes (every source lane exists,
+// so no lane keeps an old value and the move can fold into its user)
 template <int M>
 __device__ __forceinline__ float lane_xor(float v) {
     const int i = __float_as_int(v);
     int r;
     if constexpr (M == 1) {
-        r = __builtin_amdgcn_update_dpp(i, i, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
+        r = __builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, true);     // quad_perm [1,0,3,2]
     } else if constexpr (M == 2) {
-        r = __builtin_amdgcn_update_dpp(i, i, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+        r = __builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, true);     // quad_perm [2,3,0,1]
     } else if constexpr (M == 4) {
         // row_half_mirror (lane 7 - i of 8, i.e. i ^ 7), then quad_perm [3,2,1,0] (i ^ 3)
-        const int t = __builtin_amdgcn_update_dpp(i, i, 0x141, 0xF, 0xF, false);
-        r = __builtin_amdgcn_update_dpp(t, t, 0x1B, 0xF, 0xF, false);
+        const int t = __builtin_amdgcn_mov_dpp(i, 0x141, 0xF, 0xF, true);
+        r = __builtin_amdgcn_mov_dpp(t, 0x1B, 0xF, 0xF, true);
     } else {
         static_assert(M == 8, "lane_xor: 1, 2, 4 or 8");
-        r = __builtin_amdgcn_update_dpp(i, i, 0x128, 0xF, 0xF, false);   // row_ror 8: i ^ 8 of 16
+        r = __builtin_amdgcn_mov_dpp(i, 0x128, 0xF, 0xF, true);    // row_ror 8: i ^ 8 of 16
     }
     return __int_as_float(r);
 }
@@ -57,20 +58,25 @@ __device__ __forceinline__ void hadamard256(float (&v)[16], int lane) {
                 v[j] = a + b;
                 v[j | h] = a - b;
             }
-    // lanes l and l ^ m: the one with bit m clear keeps own + partner, the other
-    // partner - own (one rounding either way: the factor is +-1)
+    // lanes l and l ^ m: the pair (a, b) becomes (a + b, a - b).  Each lane computes
+    // own + sg * partner (sg = -1 on the lane with bit m set), one fused
+    // v_fmac with the partner's value read through DPP; the upper lane so holds
+    // b - a = -(a - b).  Partners carry the same sign from the earlier stages
+    // (their lane numbers differ only in bit m), so after the four stages lane l
+    // holds (-1)^popcount(l & 15) times its result, undone with the 1/16 scale.
 #define DIT_HSTAGE(M)                                                                                 \
     {                                                                                                 \
         const float sg = (lane & (M)) ? -1.0f : 1.0f;                                                 \
-        _Pragma("unroll") for (int j = 0; j < 16; ++j) v[j] = fmaf(sg, v[j], lane_xor<M>(v[j]));     \
+        _Pragma("unroll") for (int j = 0; j < 16; ++j) v[j] = fmaf(lane_xor<M>(v[j]), sg, v[j]);     \
     }
     DIT_HSTAGE(1)
     DIT_HSTAGE(2)
     DIT_HSTAGE(4)
     DIT_HSTAGE(8)
 #undef DIT_HSTAGE
+    const float fix = (__popc(lane & 15) & 1) ? -0.0625f : 0.0625f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] *= 0.0625f;
+    for (int j = 0; j < 16; ++j) v[j] *= fix;
 }
 
 // 16 codes rne(v * inv) clamped to +-127, packed little-endian into 16 bytes
