@@ -360,6 +360,8 @@ def main():
     if args.counters:
         stack, cos, sin = build_full_stack(cfg.replace(layers=1))
         kern = time_kernels(cfg, stack, reps=2)
+        kern8 = time_kernels_w8a8(I.C4_W8A8, R.quantize_block(stack.blocks[0]), reps=2)
+        kern.update({"w8a8_" + k: v for k, v in kern8.items()})
         src = torch.ones(128 * 1024 * 1024, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
