@@ -24,14 +24,28 @@
 // issued interleaved with the exponentials of tile t (VALU and the matrix
 // pipe overlap within the wave), then the PV MFMAs of tile t interleaved with
 // the row max of tile t + 1.
+//
+// Ragged tail (seq not a multiple of 256, e.g. 4096 image + 74 text tokens):
+// the last, partial q tile of every (batch, head) would otherwise be a whole
+// extra round of workgroups.  With nsplit > 1 that tile's keys are cut into
+// nsplit chunks of whole 64-key tiles, one workgroup each; a chunk writes its
+// unnormalised O, its softmax reference max and its row sum (fp32) and
+// attn_combine merges the chunks: O = sum_c 2^((m_c - M) s) O_c /
+// sum_c 2^((m_c - M) s) l_c with M = max_c m_c (the split-KV form of the same
+// online softmax).
 #include "common.h"
 
 namespace dit {
 
+// Tasks [0, n_full) are (q tile, batch * head) pairs over all keys; with
+// nsplit > 1 the tasks after them are (chunk, batch * head) pairs of the last
+// q tile (index n_full_qt), chunk c covering key tiles [c ct, (c + 1) ct).
 template <int HD>
 __global__ __launch_bounds__(512, 1)
 void flash_attn_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K, const bf16 *__restrict__ Vt,
-                       bf16 *__restrict__ O, int S, int S_pad, int H, int Hkv, int n_qt, float scale_log2) {
+                       bf16 *__restrict__ O, int S, int S_pad, int H, int Hkv, int n_full_qt, int n_full,
+                       float scale_log2, int nsplit, int ct, float *__restrict__ part_o,
+                       floatx2 *__restrict__ part_ml) {
 #if defined(__HIP_DEVICE_COMPILE__)   // buffer resources exist only in the device pass
     constexpr int NW = 8;                    // waves per workgroup
     constexpr int QW = 32;                   // queries per wave
@@ -62,9 +76,29 @@ void flash_attn_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K, c
     // Task order: with a multiple of 8 workgroups, XCD x (workgroups x, x + 8,
     // ...) runs the contiguous task range [x n/8, (x+1) n/8), so the q tiles of
     // one head share that XCD's L2 for K and V.
+    // With split chunks, XCD x runs full tasks [x F/8, (x+1) F/8) first, then its
+    // eighth of the chunks (workgroups are dispatched in index order per XCD),
+    // so every XCD gets the same mix instead of some only long, some only short
+    // tasks.
     int task = blockIdx.x;
-    if ((gridDim.x & 7) == 0) task = (task & 7) * (gridDim.x >> 3) + (task >> 3);
-    const int qt = task % n_qt, bh = task / n_qt;
+    const int G = gridDim.x;
+    if (G > n_full && (n_full & 7) == 0 && ((G - n_full) & 7) == 0) {
+        const int x = task & 7, l = task >> 3, fpx = n_full >> 3, tpx = (G - n_full) >> 3;
+        task = l < fpx ? x * fpx + l : n_full + x * tpx + (l - fpx);
+    } else if ((G & 7) == 0) {
+        task = (task & 7) * (G >> 3) + (task >> 3);
+    }
+    int qt, bh, t0 = 0, t1 = (S + BKV - 1) / BKV, chunk = -1;   // key tiles [t0, t1)
+    if (task < n_full) {
+        qt = task % n_full_qt;
+        bh = task / n_full_qt;
+    } else {
+        chunk = (task - n_full) % nsplit;
+        bh = (task - n_full) / nsplit;
+        qt = n_full_qt;
+        t0 = chunk * ct;
+        t1 = min(t1, t0 + ct);
+    }
     const int h = bh % H, b = bh / H;
     const int g = h / (H / Hkv);
     const bf16 *Qh = Q + (size_t)(b * H + h) * S * HD;
@@ -103,7 +137,6 @@ void flash_attn_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K, c
         const int d = lin >> 7, slot = (lin & 127) >> 4;
         v_off[q] = (uint32_t)d * (uint32_t)S_pad * 2u + (uint32_t)((slot ^ vswz(d)) << 4);
     }
-    const int nt = (S + BKV - 1) / BKV;
     // tail keys of K read a valid row (masked below); V^T keys in [S, S_pad) are zero
 #define DIT_ATT_ISSUE(tile, st)                                                                        \
     do {                                                                                               \
@@ -152,13 +185,13 @@ void flash_attn_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K, c
 
     // prologue: tiles 0 .. NS-2 in flight, wait for tiles 0 and 1
 #pragma unroll
-    for (int j = 0; j < NS - 1; ++j) DIT_ATT_ISSUE(min(j, nt - 1), j);
+    for (int j = 0; j < NS - 1; ++j) DIT_ATT_ISSUE(min(t0 + j, t1 - 1), (t0 + j) % NS);
     wait_vmcnt<(NS - 3) * LOADS>();
     barrier_only();
 
     floatx16 sa[2];             // scores of the tile being exponentiated
-    DIT_ATT_QK(0, sa);
-    DIT_ATT_MASK(0, sa);
+    DIT_ATT_QK(t0 % NS, sa);
+    DIT_ATT_MASK(t0 * BKV, sa);
     // running max of the raw (unscaled) scores of this lane's query; scale > 0
     // commutes with max
     float mraw;
@@ -172,13 +205,14 @@ void flash_attn_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K, c
     }
     float alpha = 1.f;          // factor taking O and l from the previous max to mraw
     float lsum = 0.f;           // this lane's partial row sum (the other 16 keys live in lane ^ 32)
+    float mref = mraw;          // the max the last exponentials were taken against (O and l refer to it)
 
     // one key tile; MASKED = 0 for the steady state (tile t + 1 holds 64 valid
     // keys), 1 for the last two tiles
 #define DIT_ATT_STEP(MASKED, T, SC, SN)                                                                       \
     do {                                                                                                      \
         /* stage (t-1) % NS was released by the barrier that closed iteration t - 1 */                        \
-        DIT_ATT_ISSUE(min((T) + NS - 1, nt - 1), ((T) + NS - 1) % NS);                                        \
+        DIT_ATT_ISSUE(min((T) + NS - 1, t1 - 1), ((T) + NS - 1) % NS);                                        \
         /* rescale only when some lane's running max grew (wave-uniform branch) */                            \
         if (__any(alpha < 1.f)) {                                                                             \
 _Pragma("unroll")                                                                                             \
@@ -191,6 +225,7 @@ _Pragma("unroll")                                                               
         /* QK^T of tile t + 1 || exponentials of tile t */                                                    \
         DIT_ATT_QK(((T) + 1) % NS, SN);                                                                       \
         const float neg = -mraw * scale_log2;                                                                 \
+        mref = mraw;                                                                                          \
         bf16x8 pf[4];                                                                                         \
 _Pragma("unroll")                                                                                             \
         for (int ks = 0; ks < 2; ++ks)                                                                        \
@@ -248,18 +283,18 @@ _Pragma("unroll")                                                               
                                                                                                               \
     } while (0)
     floatx16 sb[2];
-    int t = 0;
-    for (; t + 1 < nt - 2; t += 2) {
+    int t = t0;
+    for (; t + 1 < t1 - 2; t += 2) {
         DIT_ATT_STEP(0, t, sa, sb);
         DIT_ATT_STEP(0, t + 1, sb, sa);
     }
-    if (t < nt - 2) {
+    if (t < t1 - 2) {
         DIT_ATT_STEP(0, t, sa, sb);
         ++t;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) sa[ks] = sb[ks];
     }
-    for (; t < nt; ++t) {
+    for (; t < t1; ++t) {
         DIT_ATT_STEP(1, t, sa, sb);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) sa[ks] = sb[ks];
@@ -270,11 +305,24 @@ _Pragma("unroll")                                                               
 #undef DIT_ATT_QK
 #undef DIT_ATT_MASK
 
-    // normalise and store O[b*S + q, h*HD + d] (4 consecutive d per 8-byte store)
     const float l = lsum + __shfl_xor(lsum, 32, 64);
-    const float inv = 1.0f / l;
     const int q = q_base + lrow;
-    if (q < S) {
+    if (chunk >= 0) {
+        // a key chunk of the tail q tile: unnormalised O, reference max and row sum
+        if (q < S) {
+            const int slot = (bh * nsplit + chunk) * BQ + (q - qt * BQ);
+            float *po = part_o + (size_t)slot * HD;
+#pragma unroll
+            for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4)
+                    *(floatx4 *)(po + ds * 32 + e4 * 8 + lhalf * 4) =
+                        floatx4{oacc[ds][e4 * 4], oacc[ds][e4 * 4 + 1], oacc[ds][e4 * 4 + 2], oacc[ds][e4 * 4 + 3]};
+            if (lhalf == 0) part_ml[slot] = floatx2{mref, l};
+        }
+    } else if (q < S) {
+        // normalise and store O[b*S + q, h*HD + d] (4 consecutive d per 8-byte store)
+        const float inv = 1.0f / l;
         bf16 *orow = O + ((size_t)b * S + q) * (size_t)(H * HD) + (size_t)h * HD;
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds)
@@ -289,17 +337,106 @@ _Pragma("unroll")                                                               
 #endif
 }
 
+// Merge the key chunks of the tail q tile: one wave per (batch * head, tail
+// query), lane l owning dims l, l + 64 (HD 128) or l (HD 64).
+template <int HD>
+__global__ __launch_bounds__(256)
+void attn_combine_kernel(const float *__restrict__ part_o, const floatx2 *__restrict__ part_ml, bf16 *__restrict__ O,
+                         int S, int H, int q0, int n_tail, int n_rows, int nsplit, float scale_log2) {
+    constexpr int BQ = 256, PER = HD / 64;
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);   // bh * n_tail + tail query
+    if (row >= n_rows) return;
+    const int bh = row / n_tail, ql = row - bh * n_tail;
+    const int h = bh % H, b = bh / H;
+    float M = -INFINITY;
+    for (int c = 0; c < nsplit; ++c) M = fmaxf(M, part_ml[(bh * nsplit + c) * BQ + ql][0]);
+    float num[PER], den = 0.0f;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) num[u] = 0.0f;
+    for (int c = 0; c < nsplit; ++c) {
+        const int slot = (bh * nsplit + c) * BQ + ql;
+        const floatx2 ml = part_ml[slot];
+        const float w = __builtin_amdgcn_exp2f((ml[0] - M) * scale_log2);
+        den += w * ml[1];
+#pragma unroll
+        for (int u = 0; u < PER; ++u) num[u] += w * part_o[(size_t)slot * HD + u * 64 + lane];
+    }
+    const float inv = 1.0f / den;
+    bf16 *orow = O + ((size_t)b * S + q0 + ql) * (size_t)(H * HD) + (size_t)h * HD;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) orow[u * 64 + lane] = f2bf(num[u] * inv);
+}
+
+// Compute units of the current device (cached; 256 when it cannot be read).
+int device_cu_count() {
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            n = v;
+        else
+            n = 256;
+    }
+    return n;
+}
+
+int attention_split_count(int batch, int seq, int heads, int cus) {
+    // a tail exists and its (batch, head) tasks leave most CUs idle: spread
+    // them over the CUs, at least 2 key tiles per chunk, at most 16 chunks
+    if (seq % 256 == 0) return 1;
+    const int nt = (seq + 63) / 64, tails = batch * heads;
+    int n = cus / tails;
+    n = n < 16 ? n : 16;
+    n = n < nt / 2 ? n : nt / 2;
+    return n > 1 ? n : 1;
+}
+
+size_t attention_split_bytes(int batch, int heads, int head_dim, int nsplit) {
+    if (nsplit <= 1) return 0;
+    const size_t slots = (size_t)batch * heads * nsplit * 256;
+    return slots * head_dim * 4 + slots * 8;
+}
+
 hipError_t launch_flash_attention(const bf16 *q, const bf16 *k, const bf16 *vt, bf16 *out, int batch, int seq,
-                                  int seq_pad, int heads, int kv_heads, int head_dim, hipStream_t s) {
-    const int n_qt = (seq + 255) / 256;
-    const dim3 grid((unsigned)(n_qt * heads * batch));
+                                  int seq_pad, int heads, int kv_heads, int head_dim, int nsplit, void *part,
+                                  hipStream_t s) {
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)head_dim);
+    const int nt = (seq + 63) / 64;
+    int n_full_qt = (seq + 255) / 256, ct = nt;
+    float *part_o = nullptr;
+    floatx2 *part_ml = nullptr;
+    if (nsplit > 1 && seq % 256 != 0 && part != nullptr) {
+        n_full_qt = seq / 256;
+        ct = (nt + nsplit - 1) / nsplit;
+        nsplit = (nt + ct - 1) / ct;   // every chunk non-empty
+        part_o = (float *)part;
+        part_ml = (floatx2 *)(part_o + (size_t)batch * heads * nsplit * 256 * head_dim);
+    } else {
+        nsplit = 1;
+    }
+    const int n_full = n_full_qt * heads * batch;
+    const int tail_tasks = part_o ? nsplit * heads * batch : 0;
+    const dim3 grid((unsigned)(n_full + tail_tasks));
+#define DIT_ATT_LAUNCH(HD_)                                                                                   \
+    hipLaunchKernelGGL(flash_attn_kernel<HD_>, grid, dim3(512), 0, s, q, k, vt, out, seq, seq_pad, heads,     \
+                       kv_heads, n_full_qt, n_full, scale_log2, nsplit, ct, part_o, part_ml)
     if (head_dim == 128)
-        hipLaunchKernelGGL(flash_attn_kernel<128>, grid, dim3(512), 0, s, q, k, vt, out, seq, seq_pad, heads,
-                           kv_heads, n_qt, scale_log2);
+        DIT_ATT_LAUNCH(128);
     else
-        hipLaunchKernelGGL(flash_attn_kernel<64>, grid, dim3(512), 0, s, q, k, vt, out, seq, seq_pad, heads,
-                           kv_heads, n_qt, scale_log2);
+        DIT_ATT_LAUNCH(64);
+#undef DIT_ATT_LAUNCH
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !part_o) return e;
+    const int q0 = n_full_qt * 256, n_tail = seq - q0, n_rows = batch * heads * n_tail;
+    const dim3 cgrid((unsigned)((n_rows + 3) / 4));
+    if (head_dim == 128)
+        hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, dim3(256), 0, s, part_o, part_ml, out, seq, heads, q0,
+                           n_tail, n_rows, nsplit, scale_log2);
+    else
+        hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, dim3(256), 0, s, part_o, part_ml, out, seq, heads, q0,
+                           n_tail, n_rows, nsplit, scale_log2);
     return hipGetLastError();
 }
 

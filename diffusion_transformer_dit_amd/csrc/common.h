@@ -130,9 +130,14 @@ hipError_t launch_quantize_h256(const void *x, int x_f32, int64_t rows, int cols
 hipError_t launch_ln_modulate_q8(const void *x, int x_f32, int64_t rows, int dim, int rms, const float *shift,
                                  const float *scale, int mode, float eps, int8_t *q, float *qscale, hipStream_t s);
 
+// nsplit > 1 with part != NULL (attention_split_bytes(batch, heads, head_dim,
+// nsplit) bytes): the partial last q tile is split over nsplit key chunks
 hipError_t launch_flash_attention(const bf16 *q, const bf16 *k, const bf16 *vt, bf16 *out,
                                   int batch, int seq, int seq_pad, int heads, int kv_heads,
-                                  int head_dim, hipStream_t s);
+                                  int head_dim, int nsplit, void *part, hipStream_t s);
+int attention_split_count(int batch, int seq, int heads, int cus);
+size_t attention_split_bytes(int batch, int heads, int head_dim, int nsplit);
+int device_cu_count();
 
 hipError_t launch_adaln_gemv(const bf16 *w, const float *b, const float *c, int out_dim,
                              int in_dim, int silu_input, float *m, hipStream_t s);

@@ -67,9 +67,13 @@ int32_t seq_pad_of(int32_t s) { return (s + 63) / 64 * 64; }
 // Workspace of one block evaluation.  In the W8A8 format h holds the int8
 // codes of the normed rows (hs their scales), and the attention output and the
 // GLU output get int8 copies (aq/as, uq/us) for the projections that read them.
+// With a ragged sequence (seq % 256 != 0) it also holds the attention's
+// split-KV partials of the last q tile (up to 16 key chunks).
 struct BlockWs {
-    size_t m, h, q, k, vt, att, x1, u, hs, aq, as, uq, us, total;
+    size_t m, h, q, k, vt, att, x1, u, hs, aq, as, uq, us, part, total;
 };
+
+constexpr int kMaxAttnSplit = 16;
 
 BlockWs block_ws(const dit_block_desc &d) {
     const size_t N = (size_t)d.batch * d.seq, D = d.hidden, B = d.batch;
@@ -84,6 +88,9 @@ BlockWs block_ws(const dit_block_desc &d) {
     L.att = off; off += align256(N * H * hd * 2);
     L.x1 = off;  off += align256(N * D * 4);
     L.u = off;   off += align256(N * F * 2);
+    if (d.seq % 256) {
+        L.part = off; off += align256(attention_split_bytes(d.batch, d.heads, d.head_dim, kMaxAttnSplit));
+    }
     if (d.fmt == DIT_FMT_W8A8_H256) {
         L.hs = off; off += align256(N * 4);
         L.aq = off; off += align256(N * H * hd);
@@ -184,6 +191,10 @@ int block_body(const dit_block_desc &d, const dit_block_weights &w, const void *
     bf16 *u = (bf16 *)(ws + L.u);
     const int mode = m ? 0 : 1;
     const int rms = d.norm == DIT_RMSNORM;
+    // split-KV for the partial last q tile when the sequence is ragged
+    void *part = d.seq % 256 ? (void *)(ws + L.part) : nullptr;
+    int nsplit = attention_split_count(d.batch, d.seq, d.heads, device_cu_count());
+    nsplit = nsplit < kMaxAttnSplit ? nsplit : kMaxAttnSplit;
     // modulation chunks: (shift1, scale1, gate1, shift2, scale2, gate2) or, without
     // shift, (scale1, gate1, scale2, gate2); without AdaLN the affine LN parameters
     const float *shift1, *scale1, *gate1, *shift2, *scale2, *gate2;
@@ -205,7 +216,8 @@ int block_body(const dit_block_desc &d, const dit_block_weights &w, const void *
         DIT_TRY_HIP(launch_ln_modulate_q8(x, x_f32, N, D, rms, shift1, scale1, mode, d.eps, hq, hs, s));
         DIT_TRY_HIP(launch_vt_pad_zero(vt, d.batch * d.kv_heads * hd, d.seq, spad, s));
         DIT_TRY_HIP(launch_gemm_qkv_q8(hq, hs, (const int8_t *)w.w_qkv, w.s_qkv, N, qkv_dim, D, e, s));
-        DIT_TRY_HIP(launch_flash_attention(q, k, vt, att, d.batch, d.seq, spad, d.heads, d.kv_heads, hd, s));
+        DIT_TRY_HIP(launch_flash_attention(q, k, vt, att, d.batch, d.seq, spad, d.heads, d.kv_heads, hd, nsplit,
+                                           part, s));
         DIT_TRY_HIP(launch_quantize_h256(att, 0, N, d.heads * hd, aq, as, s));
         DIT_TRY_HIP(launch_gemm_residual_q8(aq, as, (const int8_t *)w.w_o, w.s_o, N, D, d.heads * hd, x, x_f32, gate1,
                                             d.gate, nullptr, x1, 1, s));
@@ -219,7 +231,8 @@ int block_body(const dit_block_desc &d, const dit_block_weights &w, const void *
     DIT_TRY_HIP(launch_ln_modulate(x, x_f32, N, D, rms, shift1, scale1, mode, d.eps, h, s));
     DIT_TRY_HIP(launch_vt_pad_zero(vt, d.batch * d.kv_heads * hd, d.seq, spad, s));
     DIT_TRY_HIP(launch_gemm_qkv(h, (const bf16 *)w.w_qkv, N, qkv_dim, D, e, s));
-    DIT_TRY_HIP(launch_flash_attention(q, k, vt, att, d.batch, d.seq, spad, d.heads, d.kv_heads, hd, s));
+    DIT_TRY_HIP(launch_flash_attention(q, k, vt, att, d.batch, d.seq, spad, d.heads, d.kv_heads, hd, nsplit, part,
+                                       s));
     DIT_TRY_HIP(launch_gemm_residual(att, (const bf16 *)w.w_o, N, D, d.heads * hd, x, x_f32, gate1, d.gate,
                                      nullptr, x1, 1, s));
     DIT_TRY_HIP(launch_ln_modulate(x1, 1, N, D, rms, shift2, scale2, mode, d.eps, h, s));
@@ -512,7 +525,34 @@ int dit_flash_attention(const dit_block_desc *desc, const void *q, const void *k
         return fail(DIT_ERR_ALIGNMENT, "q, k, vt, out must be 16-byte aligned");
     DIT_TRY(device_check());
     DIT_TRY_HIP(launch_flash_attention((const bf16 *)q, (const bf16 *)k, (const bf16 *)vt, (bf16 *)out, d.batch, d.seq,
-                                       seq_pad_of(d.seq), d.heads, d.kv_heads, d.head_dim, as_stream(stream)));
+                                       seq_pad_of(d.seq), d.heads, d.kv_heads, d.head_dim, 1, nullptr,
+                                       as_stream(stream)));
+    return ok();
+}
+
+int dit_attention_workspace_size(const dit_block_desc *desc, int32_t nsplit, size_t *bytes) {
+    DIT_TRY(check_desc(desc));
+    if (!bytes) return fail(DIT_ERR_INVALID_ARG, "bytes is NULL");
+    if (nsplit < 1 || nsplit > 64) return fail(DIT_ERR_INVALID_ARG, "nsplit must be in [1, 64]");
+    *bytes = attention_split_bytes(desc->batch, desc->heads, desc->head_dim, nsplit);
+    return ok();
+}
+
+int dit_flash_attention_split(const dit_block_desc *desc, const void *q, const void *k, const void *vt, void *out,
+                              int32_t nsplit, void *ws, size_t ws_bytes, void *stream) {
+    DIT_TRY(check_desc(desc));
+    const dit_block_desc &d = *desc;
+    if (!q || !k || !vt || !out) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
+    if (nsplit < 1 || nsplit > 64) return fail(DIT_ERR_INVALID_ARG, "nsplit must be in [1, 64]");
+    const size_t need = attention_split_bytes(d.batch, d.heads, d.head_dim, nsplit);
+    if (need && !ws) return fail(DIT_ERR_INVALID_ARG, "ws is required for nsplit > 1");
+    if (ws_bytes < need) return fail(DIT_ERR_WORKSPACE, "workspace %zu < required %zu bytes", ws_bytes, need);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(out) || (ws && !aligned16(ws)))
+        return fail(DIT_ERR_ALIGNMENT, "q, k, vt, out, ws must be 16-byte aligned");
+    DIT_TRY(device_check());
+    DIT_TRY_HIP(launch_flash_attention((const bf16 *)q, (const bf16 *)k, (const bf16 *)vt, (bf16 *)out, d.batch, d.seq,
+                                       seq_pad_of(d.seq), d.heads, d.kv_heads, d.head_dim, nsplit, ws,
+                                       as_stream(stream)));
     return ok();
 }
 

@@ -31,7 +31,7 @@ EXPORTED = (
     "dit_gemm_gated_residual", "dit_gemm_swiglu", "dit_status_string", "dit_last_error", "dit_version",
     "dit_loop_workspace_size", "dit_loop_create", "dit_loop_launch_step", "dit_loop_launch", "dit_loop_destroy",
     "dit_quantize_h256", "dit_ln_modulate_h256q", "dit_gemm_w8a8_gated_residual", "dit_gemm_w8a8_swiglu",
-    "dit_qkv_rope_w8a8",
+    "dit_qkv_rope_w8a8", "dit_attention_workspace_size", "dit_flash_attention_split",
 )
 
 
@@ -105,6 +105,8 @@ def lib():
                                                        i32, vp]),
             "dit_gemm_w8a8_swiglu": (C.c_int, [vp, vp, vp, vp, i64, i32, i32, i32, vp, vp]),
             "dit_qkv_rope_w8a8": (C.c_int, [pd, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+            "dit_attention_workspace_size": (C.c_int, [pd, i32, C.POINTER(sz)]),
+            "dit_flash_attention_split": (C.c_int, [pd, vp, vp, vp, vp, i32, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -276,6 +278,18 @@ def dit_qkv_rope(desc, h, w_qkv, q_g, q_b, k_g, k_b, rope_cos, rope_sin, q, k, v
 
 def dit_flash_attention(desc, q, k, vt, out, stream=None):
     _check(lib().dit_flash_attention(C.byref(desc), _p(q), _p(k), _p(vt), _p(out), _stream(stream)))
+
+
+def dit_attention_workspace_size(desc, nsplit) -> int:
+    n = C.c_size_t(0)
+    _check(lib().dit_attention_workspace_size(C.byref(desc), int(nsplit), C.byref(n)))
+    return n.value
+
+
+def dit_flash_attention_split(desc, q, k, vt, out, nsplit, ws, stream=None, ws_bytes=None):
+    nb = (_nbytes(ws) if ws is not None else 0) if ws_bytes is None else ws_bytes
+    _check(lib().dit_flash_attention_split(C.byref(desc), _p(q), _p(k), _p(vt), _p(out), int(nsplit), _p(ws), nb,
+                                           _stream(stream)))
 
 
 def dit_gemm_gated_residual(a, w, M, N, K, resid, resid_dtype, gate, bias, out, out_dtype, stream=None,

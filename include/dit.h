@@ -328,6 +328,19 @@ int32_t dit_seq_pad(int32_t seq);
 int dit_flash_attention(const dit_block_desc *desc, const void *q, const void *k,
                         const void *vt, void *out, void *stream);
 
+/* dit_flash_attention with the last, partial q tile (seq % 256 rows) of each
+ * (batch, head) split over nsplit chunks of whole 64-key tiles, each chunk
+ * one workgroup writing its unnormalised output, softmax reference max and
+ * row sum (fp32) to ws, merged by a second kernel (the split-KV form of the
+ * online softmax); dit_block_forward uses it for ragged sequences such as the
+ * joint 4096 + 74 token layout ([ERNIE] "Token Layout").  nsplit in [1, 64]
+ * (chunks hold at least one key tile; nsplit 1, or seq a multiple of 256,
+ * is dit_flash_attention).  ws: device workspace of at least
+ * dit_attention_workspace_size(desc, nsplit) bytes (may be NULL when that is 0). */
+int dit_attention_workspace_size(const dit_block_desc *desc, int32_t nsplit, size_t *bytes);
+int dit_flash_attention_split(const dit_block_desc *desc, const void *q, const void *k, const void *vt,
+                              void *out, int32_t nsplit, void *ws, size_t ws_bytes, void *stream);
+
 /* out = resid + f(gate) * (a W^T) + bias over an [M, N] output, f = the gate
  * function gate_fn (dit_gate):
  * a device bf16 [M, K]; W device bf16 [N, K]; resid device [M, N] of

@@ -305,3 +305,18 @@ def test_w8a8_valid_calls_report_no_device():
         with pytest.raises(N.DitError) as e:
             f(*a, stream=0)
         assert e.value.status == N.DIT_ERR_NO_DEVICE, f.__name__
+
+
+def test_attention_split_validation():
+    d = _desc(seq=300)
+    assert N.dit_attention_workspace_size(d, 1) == 0
+    n8 = N.dit_attention_workspace_size(d, 8)
+    assert n8 == 1 * 4 * 8 * 256 * (64 * 4 + 8)          # partial O fp32 + (max, sum) per chunk slot
+    for nsplit, ws, nb, st in ((0, FAKE, n8, N.DIT_ERR_INVALID_ARG), (65, FAKE, n8, N.DIT_ERR_INVALID_ARG),
+                               (8, None, 0, N.DIT_ERR_INVALID_ARG), (8, FAKE, n8 - 1, N.DIT_ERR_WORKSPACE),
+                               (8, FAKE + 8, n8, N.DIT_ERR_ALIGNMENT)):
+        with pytest.raises(N.DitError) as e:
+            N.dit_flash_attention_split(d, FAKE, FAKE, FAKE, FAKE + (1 << 24), nsplit, ws, stream=0, ws_bytes=nb)
+        assert e.value.status == st, (nsplit, e.value)
+    # a ragged sequence grows the block workspace by the partials of up to 16 chunks
+    assert N.dit_block_workspace_size(_desc(seq=300)) > N.dit_block_workspace_size(_desc(seq=256))

@@ -154,6 +154,53 @@ def test_flash_attention(B, S, H, Hk, hd, amp):
     assert_parity(R.to_host_f32(out), ref, max_rel=2e-2, min_cos=0.9999, what="attention")
 
 
+@pytest.mark.parametrize("B,S,H,Hk,hd,nsplit", [
+    (1, 300, 4, 2, 128, 2), (2, 1000, 4, 4, 64, 3), (1, 4170, 2, 2, 128, 8),   # joint 4096 + 74 text rows
+    (1, 100, 2, 2, 128, 2),                                                     # one partial q tile only
+    (1, 263, 4, 4, 64, 64),                                                     # more chunks than key tiles
+    (3, 130, 6, 3, 128, 16),                                                    # batch 3, GQA, 3 key tiles
+    (1, 512, 2, 2, 128, 4),                                                     # no tail: plain kernel
+])
+def test_flash_attention_split_tail(B, S, H, Hk, hd, nsplit):
+    """The partial last q tile split over key chunks and merged (split-KV)
+    against the explicit softmax; the full q tiles run unsplit in the same
+    launch."""
+    import torch
+    say(f"flash_attention_split B={B} S={S} H={H} Hkv={Hk} hd={hd} nsplit={nsplit}")
+    r = _rng(8)
+    q = I.bf16_round(r.standard_normal((B, H, S, hd), dtype=np.float32) * 1.5)
+    k = I.bf16_round(r.standard_normal((B, Hk, S, hd), dtype=np.float32) * 1.5)
+    v = I.bf16_round(r.standard_normal((B, Hk, S, hd), dtype=np.float32))
+    spad = N.dit_seq_pad(S)
+    vt = np.zeros((B, Hk, hd, spad), np.float32)
+    vt[..., :S] = v.transpose(0, 1, 3, 2)
+    cfg = I.DiTConfig("att", 0, B, (1, 1, S), H * hd, H, Hk, hd, 128, 0, False, "half2d", (hd // 2, hd // 2), 100.0)
+    desc = R.desc_of(cfg)
+    ws = R.alloc_ws(N.dit_attention_workspace_size(desc, nsplit))
+    out = torch.empty((B * S, H * hd), dtype=torch.bfloat16, device="cuda")
+    qd, kd, vd = R.to_dev_bf16(q), R.to_dev_bf16(k), R.to_dev_bf16(vt)
+    N.dit_flash_attention_split(desc, qd, kd, vd, out, nsplit, ws)
+    _sync()
+    rows = np.arange(B * S)
+    if S > 1024:                      # the oracle on the tail rows and a sample of the others
+        tail = np.arange(S // 256 * 256, S)
+        rows = np.unique(np.r_[tail, 0, 1, 255, 256, 2047, np.random.default_rng(2).choice(S, 24, replace=False)])
+    ref = np.concatenate([O.attention(q[b].transpose(1, 0, 2).astype(np.float64), k[b].transpose(1, 0, 2),
+                                      v[b].transpose(1, 0, 2), H, Hk, rows) for b in range(B)]) if B == 1 else \
+        np.concatenate([O.attention(q[b].transpose(1, 0, 2).astype(np.float64), k[b].transpose(1, 0, 2),
+                                    v[b].transpose(1, 0, 2), H, Hk) for b in range(B)])
+    got = R.to_host_f32(out)
+    got = got[rows] if B == 1 else got
+    assert_parity(got, ref, max_rel=2e-2, min_cos=0.9999, what=f"attention split {nsplit}")
+    # the same launch without the split gives the same values up to the merge's rounding
+    plain = torch.empty_like(out)
+    N.dit_flash_attention(desc, qd, kd, vd, plain)
+    _sync()
+    pm = R.to_host_f32(plain)
+    pm = pm[rows] if B == 1 else pm
+    assert_parity(got, pm, max_rel=1e-2, min_cos=0.99999, what="split vs unsplit")
+
+
 def test_flash_attention_closed_forms():
     """V == 1 gives O == 1; Q == 0 gives the mean of V over the keys."""
     import torch
