@@ -110,7 +110,8 @@ __device__ __forceinline__ int acc_row(int i, int e, int lhalf);
 template <class T, class RowMap, class Epi>
 __global__ __launch_bounds__(T::kThreads, 1)
 void gemm_kernel(const void *__restrict__ A, const void *__restrict__ W, int M, int K, int w_rows,
-                 int tiles_m, int tiles_n, RowMap rowmap, Epi epi, const float *a_scale, const float *w_scale) {
+                 int tiles_m, int tiles_n, RowMap rowmap, Epi epi, const float *a_scale, const float *w_scale,
+                 int m_base) {
 #if defined(__HIP_DEVICE_COMPILE__)   // buffer resources exist only in the device pass
     constexpr int kMain = T::NS * T::kStageBytes;
     constexpr int kLds = Epi::template lds_bytes<T>() > kMain ? Epi::template lds_bytes<T>() : kMain;
@@ -118,7 +119,7 @@ void gemm_kernel(const void *__restrict__ A, const void *__restrict__ W, int M, 
 
     int tm, tn;
     tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
-    const int m0 = tm * T::BM;
+    const int m0 = m_base + tm * T::BM;   // m_base: first row of this launch (tail launches)
 
     const int tid = threadIdx.x;
     // wave index as a scalar: the LDS destinations of the buffer->LDS loads (M0)
@@ -448,8 +449,9 @@ struct EpiQkv {
     template <class T>
     __device__ __forceinline__ void apply(floatx16 (&acc)[T::TM][T::TN], int row0, int tn, int wn, int lane, int M,
                                           uint8_t *smem) const {
-        static_assert(T::BN == 256 && T::WM == 2 && T::WN == 4 && T::kWaveM == 128 && T::kWaveN == 64,
-                      "staging assumes the 8-wave 256x256 tile");
+        static_assert(T::BN == 256 && T::WM == 2 && T::WN == 4 && (T::kWaveM == 128 || T::kWaveM == 64) &&
+                          T::kWaveN == 64,
+                      "staging assumes the 8-wave 256x256 tile or its 128-row tail variant");
         static_assert(2 * 64 * kQkvStride * 4 / 2 >= (256 / HD) * kHeadBlock, "output block fits the staging area");
         const int lrow = lane & 31, lhalf = lane >> 5;
         const int wave = threadIdx.x >> 6;
@@ -482,7 +484,7 @@ struct EpiQkv {
         // the 32 RoPE pairs of this lane: frequencies pair0 .. pair0 + 31
         const int pair0 = part * 32;
 #pragma unroll
-        for (int sp = 0; sp < 2; ++sp) {
+        for (int sp = 0; sp < T::kWaveM / 64; ++sp) {
             // the K loop, or the previous sub-pass's copy-out, is done with the LDS
             if (sp > 0) { wait_vmcnt<63, 0>(); barrier_only(); }
 #pragma unroll
@@ -698,26 +700,17 @@ using TileNarrow = Tile<256, 128, 2, 2>;   // N = 128 outputs (the projection to
 using Tile8wQ = Tile<256, 256, 2, 4, 128, 2, 1>;
 using Tile8wTallQ = Tile<320, 256, 2, 4, 128, 2, 1>;
 using TileNarrowQ = Tile<256, 128, 2, 2, 128, 2, 1>;
+// 128-row tails of the 256 x 256 tiles (8 waves of 64 x 64)
+using Tile8wHalf = Tile<128, 256, 2, 4>;
+using Tile8wHalfQ = Tile<128, 256, 2, 4, 128, 2, 1>;
 
-// Compute units of the current device (one 256 x 256 tile runs per CU at a time).
-static int cu_count() {
-    static int n = 0;
-    if (n == 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            n = v;
-        else
-            n = 256;
-    }
-    return n;
-}
 
 // Tile height for an M x N output of 256-wide column tiles: the 320-row tile
 // when it needs fewer rounds of workgroups over the CUs than the 256-row one
 // costs extra time per tile (e.g. 4170 rows x 4096 columns: 224 tiles in one
 // round instead of 272 in two).
 static bool prefer_tall(int64_t M, int N) {
-    const int64_t cus = cu_count(), tn = N / 256;
+    const int64_t cus = device_cu_count(), tn = N / 256;
     const int64_t r256 = ((M + 255) / 256 * tn + cus - 1) / cus;
     const int64_t r320 = ((M + 319) / 320 * tn + cus - 1) / cus;
     return r320 * 320 < r256 * 256;
@@ -733,16 +726,45 @@ struct Scales {
     const float *a, *w;
 };
 
+// rows [m_base, M) in tiles of T::BM
 template <class T, class RowMap, class Epi>
 static hipError_t run(const void *a, const void *w, int64_t M, int N_tile_cols, int K, RowMap rm, Epi epi,
-                      hipStream_t s, const float *a_scale = nullptr, const float *w_scale = nullptr) {
-    const int tiles_m = (int)((M + T::BM - 1) / T::BM);
+                      hipStream_t s, const float *a_scale = nullptr, const float *w_scale = nullptr,
+                      int64_t m_base = 0) {
+    const int tiles_m = (int)((M - m_base + T::BM - 1) / T::BM);
     const int tiles_n = N_tile_cols / T::BN;
     const int grid = tiles_m * tiles_n;
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL((gemm_kernel<T, RowMap, Epi>), dim3(grid), dim3(T::kThreads), 0, s, a, w, (int)M, K,
-                       N_tile_cols, tiles_m, tiles_n, rm, epi, a_scale, w_scale);
+                       N_tile_cols, tiles_m, tiles_n, rm, epi, a_scale, w_scale, (int)m_base);
     return hipGetLastError();
+}
+
+// Ragged row count (e.g. 4096 image + 74 text tokens): the last, partial row
+// of 256-row tiles costs a whole extra round of workgroups when the full rows
+// already fill whole rounds.  Then the full rows run as usual and the tail
+// rows in a second launch of 128-row tiles (TH, same columns and wave layout)
+// at about half the cost per tile.  Used for the QKV GEMM (4170 x 12288:
+// 405 instead of 427 us).
+static bool split_tail_rows(int64_t M, int N_tile_cols) {
+    if (M % 256 == 0 || M % 256 > 128 || M < 256) return false;
+    const int64_t cus = device_cu_count(), tn = N_tile_cols / 256;
+    const int64_t full = M / 256 * tn, tail = tn;
+    const double plain = (double)((full + tail + cus - 1) / cus);
+    const double split = (double)((full + cus - 1) / cus) + 0.55 * (double)((tail + cus - 1) / cus);
+    return split < plain;
+}
+
+template <class T, class TH, class RowMap, class Epi>
+static hipError_t run_tail_split(const void *a, const void *w, int64_t M, int N_tile_cols, int K, RowMap rm,
+                                 Epi epi, hipStream_t s, const float *a_scale = nullptr,
+                                 const float *w_scale = nullptr) {
+    static_assert(T::BM == 256 && TH::BM == 128 && T::BN == TH::BN, "full and tail tiles");
+    if (!split_tail_rows(M, N_tile_cols)) return run<T>(a, w, M, N_tile_cols, K, rm, epi, s, a_scale, w_scale);
+    const int64_t m_full = M / 256 * 256;
+    hipError_t e = run<T>(a, w, m_full, N_tile_cols, K, rm, epi, s, a_scale, w_scale);
+    if (e != hipSuccess) return e;
+    return run<TH>(a, w, M, N_tile_cols, K, rm, epi, s, a_scale, w_scale, m_full);
 }
 
 template <typename TR, typename TO, class SC>
@@ -786,6 +808,7 @@ hipError_t launch_gemm_residual_q8(const int8_t *a, const float *a_scale, const 
 template <class SC>
 static hipError_t swiglu_any(const void *a, const void *w, int64_t M, int F, int K, int act, bf16 *u, SC sc,
                              hipStream_t s) {
+    // (a 128-row tail launch measured no faster here: 718 vs 713 us at 4170 rows)
     using T = typename std::conditional<SC::kQ8, Tile8wQ, Tile8w>::type;
     const RowsSwiglu rm{T::BN, T::kWaveN, F};
     if (act == 1) return run<T>(a, w, M, 2 * F, K, rm, EpiSwiglu<1>{u, F}, s, sc.a, sc.w);
@@ -806,8 +829,9 @@ template <class SC>
 static hipError_t qkv_any(const void *h, const void *w, int64_t M, int N, int K, const QkvEpiArgs &e, SC sc,
                           hipStream_t s) {
     using T = typename std::conditional<SC::kQ8, Tile8wQ, Tile8w>::type;
+    using TH = typename std::conditional<SC::kQ8, Tile8wHalfQ, Tile8wHalf>::type;
 #define DIT_QKV(HD_, RMS_, RF_) \
-    run<T>(h, w, M, N, K, RowsIdentity{T::BN}, EpiQkv<HD_, RMS_, RF_>{e}, s, sc.a, sc.w)
+    run_tail_split<T, TH>(h, w, M, N, K, RowsIdentity{T::BN}, EpiQkv<HD_, RMS_, RF_>{e}, s, sc.a, sc.w)
     if (e.head_dim == 128) {
         if (e.rms) return e.rope_first ? DIT_QKV(128, true, true) : DIT_QKV(128, true, false);
         return e.rope_first ? DIT_QKV(128, false, true) : DIT_QKV(128, false, false);

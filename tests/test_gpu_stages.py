@@ -102,12 +102,18 @@ def _qkv_case(cfg, seed=3):
     return h, w
 
 
+# 4170 tokens (30 x 139 grid), 16 + 2 x 8 heads of 128: 16 full row tiles x 16 column
+# tiles fill one round of 256 CUs, so the 74-row tail runs as a 128-row tile launch
+QKV_TAIL = I.DiTConfig("qkv_tail_4170", 25, 1, (1, 30, 139), 2048, 16, 8, 128, 4096, 256, True,
+                       "interleaved3d", (32, 48, 48), 256.0, x_dtype="bf16")
+
+
 @pytest.mark.parametrize("name", ["c1_rms", "c1_rope_first", "hd128_ernie_diagram", "half_hd128_rope_first",
                                   "c1_tiny", "c1_ragged200", "hd128_ragged400", "gqa3_b2_ragged300", "vit_b2_f32",
-                                  "c1_f32x_t3"])
+                                  "c1_f32x_t3", "qkv_tail_4170"])
 def test_qkv_rope(name):
     import torch
-    cfg = SMALL[name]
+    cfg = QKV_TAIL if name == "qkv_tail_4170" else SMALL[name]
     say(f"qkv_rope {name}")
     h, w = _qkv_case(cfg)
     pos = I.positions(cfg)
@@ -290,7 +296,8 @@ def test_gemm_residual_in_place_and_identity():
     np.testing.assert_array_equal(R.to_host_f32(xd), x + a)
 
 
-@pytest.mark.parametrize("M,F,K", [(300, 384, 256), (256, 768, 256), (4097, 256, 512)])
+@pytest.mark.parametrize("M,F,K", [(300, 384, 256), (256, 768, 256), (4097, 256, 512),
+                                   (4170, 2048, 256)])   # ragged rows over one full round of tiles
 def test_gemm_swiglu(M, F, K):
     import torch
     say(f"gemm_swiglu M={M} F={F} K={K}")

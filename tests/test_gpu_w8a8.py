@@ -180,7 +180,8 @@ def test_gemm_w8a8_gated_residual(M, N_, K, rdt, odt, gate_fn):
 
 
 @pytest.mark.parametrize("M,F,K,act", [(300, 384, 512, N.DIT_ACT_SILU), (4096, 1024, 4096, N.DIT_ACT_SILU),
-                                       (270, 256, 256, N.DIT_ACT_GELU_TANH)])
+                                       (270, 256, 256, N.DIT_ACT_GELU_TANH),
+                                       (4170, 2048, 256, N.DIT_ACT_SILU)])   # ragged rows over one round
 def test_gemm_w8a8_swiglu(M, F, K, act):
     import torch
     say(f"gemm_w8a8_swiglu M={M} F={F} K={K} act={act}")
