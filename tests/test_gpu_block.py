@@ -76,6 +76,18 @@ def test_block_small_vs_oracle(name):
     _check(cfg, got, ref, x)
 
 
+@pytest.mark.parametrize("seq,batch", [(1, 1), (2, 3)])
+def test_block_degenerate_sequences(seq, batch):
+    """One- and two-token sequences (attention over a single key is the
+    identity on v), batch 3: the whole block against the oracle."""
+    cfg = I.C1.replace(name=f"c1_seq{seq}_b{batch}", seq_override=seq, batch=batch, x_dtype="f32")
+    w = I.block_weights(cfg, 0, affine_random=True)
+    x, c, pos = I.block_x(cfg), I.cond(cfg), I.positions(cfg)
+    got = _run_block(cfg, w, x, c, pos)
+    ref = O.block_forward(x, c, w, cfg, pos)
+    _check(cfg, got, ref, x)
+
+
 def test_block_zero_adaln_is_identity_bitwise():
     """AdaLN-Zero: W_ada = 0 and b_ada = 0 make every shift, scale and gate zero,
     so out == x bit for bit."""

@@ -45,7 +45,7 @@ def test_adaln_gemv(out_dim, in_dim, silu):
 
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("rows,dim,xdt,mode", [(300, 256, "f32", 0), (257, 4096, "bf16", 0), (64, 6144, "f32", 1),
-                                               (5, 1024, "bf16", 1)])
+                                               (5, 1024, "bf16", 1), (1, 4096, "f32", 0)])
 def test_ln_modulate(rows, dim, xdt, mode):
     import torch
     say(f"ln_modulate rows={rows} dim={dim} x={xdt} mode={mode}")
@@ -140,7 +140,9 @@ def test_qkv_rope(name):
 
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("B,S,H,Hk,hd,amp", [(1, 256, 4, 4, 64, 1.0), (2, 300, 4, 2, 128, 2.0), (1, 100, 2, 2, 128, 3.0),
-                                              (1, 1000, 4, 2, 64, 1.5), (3, 64, 6, 6, 128, 1.0)])
+                                              (1, 1000, 4, 2, 64, 1.5), (3, 64, 6, 6, 128, 1.0),
+                                              (1, 1, 2, 2, 128, 1.0), (2, 2, 4, 2, 64, 1.0),   # one / two tokens
+                                              (1, 65, 2, 1, 128, 2.0)])                       # one key past a tile
 def test_flash_attention(B, S, H, Hk, hd, amp):
     import torch
     say(f"flash_attention B={B} S={S} H={H} Hkv={Hk} hd={hd} amp={amp}")
@@ -166,6 +168,7 @@ def test_flash_attention(B, S, H, Hk, hd, amp):
     (1, 263, 4, 4, 64, 64),                                                     # more chunks than key tiles
     (3, 130, 6, 3, 128, 16),                                                    # batch 3, GQA, 3 key tiles
     (1, 512, 2, 2, 128, 4),                                                     # no tail: plain kernel
+    (1, 65, 2, 2, 128, 2), (1, 1, 4, 4, 64, 4),                                 # a 1-key chunk; a 1-token sequence
 ])
 def test_flash_attention_split_tail(B, S, H, Hk, hd, nsplit):
     """The partial last q tile split over key chunks and merged (split-KV)
@@ -234,6 +237,7 @@ def test_flash_attention_closed_forms():
 
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("M,Nn,K,rdt,odt,gate,bias", [
+    (1, 256, 64, "f32", "f32", True, True),           # a single row
     (300, 512, 320, "f32", "f32", True, False),
     (300, 512, 320, "bf16", "f32", True, True),
     (513, 256, 768, "f32", "bf16", False, False),
@@ -296,7 +300,7 @@ def test_gemm_residual_in_place_and_identity():
     np.testing.assert_array_equal(R.to_host_f32(xd), x + a)
 
 
-@pytest.mark.parametrize("M,F,K", [(300, 384, 256), (256, 768, 256), (4097, 256, 512),
+@pytest.mark.parametrize("M,F,K", [(300, 384, 256), (256, 768, 256), (4097, 256, 512), (1, 128, 64),
                                    (4170, 2048, 256)])   # ragged rows over one full round of tiles
 def test_gemm_swiglu(M, F, K):
     import torch

