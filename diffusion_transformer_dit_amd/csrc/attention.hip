@@ -440,4 +440,118 @@ hipError_t launch_flash_attention(const bf16 *q, const bf16 *k, const bf16 *vt, 
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// fp32 attention (the fp32 parity path): the same softmax(Q K^T / sqrt(hd)) V
+// with fp32 operands on the vector ALUs.  One workgroup = 64 queries of one
+// (batch, head); 4 lanes per query, each holding HD/4 consecutive dims of q
+// (pre-scaled by log2(e) / sqrt(hd)) and of the output.  A 64-key tile of K
+// and of V (read from V^T and transposed on the way into LDS) is staged per
+// step; the scores of the tile are partial dots reduced over the 4 lanes of a
+// query, followed by one online-softmax update of (m, l, o).
+// ---------------------------------------------------------------------------
+template <int HD>
+__global__ __launch_bounds__(256)
+void attn_f32_kernel(const float *__restrict__ Q, const float *__restrict__ K, const float *__restrict__ Vt,
+                     float *__restrict__ O, int S, int S_pad, int H, int Hkv, float scale_log2) {
+    constexpr int BKV = 64, DL = HD / 4, LD = HD + 4;
+    __shared__ float Ks[BKV * LD];
+    __shared__ float Vs[BKV * LD];
+    const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int g = h / (H / Hkv);
+    const int tid = threadIdx.x, ql = tid >> 2, sub = tid & 3;
+    const int q = qt * 64 + ql;
+    const float *Qh = Q + (size_t)(b * H + h) * S * HD;
+    const float *Kh = K + (size_t)(b * Hkv + g) * S * HD;
+    const float *Vh = Vt + (size_t)(b * Hkv + g) * HD * S_pad;
+    float qr[DL], o[DL];
+    {
+        const float *qp = Qh + (size_t)min(q, S - 1) * HD + sub * DL;
+#pragma unroll
+        for (int i = 0; i < DL; i += 4) {
+            const floatx4 v = *(const floatx4 *)(qp + i);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) { qr[i + u] = v[u] * scale_log2; o[i + u] = 0.f; }
+        }
+    }
+    float m = -INFINITY, l = 0.f;
+    const int nt = (S + BKV - 1) / BKV;
+    for (int t = 0; t < nt; ++t) {
+        const int k0 = t * BKV;
+        __syncthreads();   // the previous tile's reads are done
+        // K rows k0 .. k0 + 63 (rows past S clamped; their scores are masked)
+#pragma unroll
+        for (int it = 0; it < HD / 16; ++it) {
+            const int c = it * 256 + tid, r = c / (HD / 4), d4 = c - r * (HD / 4);
+            const floatx4 v = *(const floatx4 *)(Kh + (size_t)min(k0 + r, S - 1) * HD + d4 * 4);
+            *(floatx4 *)(Ks + r * LD + d4 * 4) = v;
+        }
+        // V^T columns k0 .. k0 + 63 (inside the padded row: S_pad is a multiple of 64)
+#pragma unroll
+        for (int it = 0; it < HD / 16; ++it) {
+            const int c = it * 256 + tid, d = c / 16, j4 = c - d * 16;
+            const floatx4 v = *(const floatx4 *)(Vh + (size_t)d * S_pad + k0 + j4 * 4);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) Vs[(j4 * 4 + u) * LD + d] = v[u];
+        }
+        __syncthreads();
+        float sc[BKV];
+        float mt = m;
+#pragma unroll
+        for (int j = 0; j < BKV; ++j) {
+            const float *kr = Ks + j * LD + sub * DL;
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < DL; i += 4) {
+                const floatx4 kv = *(const floatx4 *)(kr + i);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc += qr[i + u] * kv[u];
+            }
+            acc += __shfl_xor(acc, 1, 64);
+            acc += __shfl_xor(acc, 2, 64);
+            sc[j] = k0 + j < S ? acc : -INFINITY;
+            mt = fmaxf(mt, sc[j]);
+        }
+        const float alpha = exp2f(m - mt);
+        m = mt;
+        l *= alpha;
+#pragma unroll
+        for (int i = 0; i < DL; ++i) o[i] *= alpha;
+#pragma unroll
+        for (int j = 0; j < BKV; ++j) {
+            const float p = exp2f(sc[j] - mt);
+            l += p;
+            const float *vr = Vs + j * LD + sub * DL;
+#pragma unroll
+            for (int i = 0; i < DL; i += 4) {
+                const floatx4 vv = *(const floatx4 *)(vr + i);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) o[i + u] += p * vv[u];
+            }
+        }
+    }
+    if (q < S) {
+        const float inv = 1.0f / l;
+        float *orow = O + ((size_t)b * S + q) * (size_t)(H * HD) + (size_t)h * HD + sub * DL;
+#pragma unroll
+        for (int i = 0; i < DL; i += 4)
+            *(floatx4 *)(orow + i) = floatx4{o[i] * inv, o[i + 1] * inv, o[i + 2] * inv, o[i + 3] * inv};
+    }
+}
+
+hipError_t launch_flash_attention_f32(const float *q, const float *k, const float *vt, float *out, int batch,
+                                      int seq, int seq_pad, int heads, int kv_heads, int head_dim, hipStream_t s) {
+    if (seq_pad % 64 || seq_pad < seq) return hipErrorInvalidValue;
+    const float scale_log2 = 1.4426950408889634f / sqrtf((float)head_dim);
+    const dim3 grid((unsigned)((seq + 63) / 64), (unsigned)heads, (unsigned)batch);
+    if (head_dim == 128)
+        hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(256), 0, s, q, k, vt, out, seq, seq_pad, heads, kv_heads,
+                           scale_log2);
+    else if (head_dim == 64)
+        hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(256), 0, s, q, k, vt, out, seq, seq_pad, heads, kv_heads,
+                           scale_log2);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 }  // namespace dit

@@ -102,7 +102,7 @@ struct QkvEpiArgs {
     float eps;
     const float *q_g, *q_b, *k_g, *k_b;
     const float *cos_t, *sin_t;
-    bf16 *q, *k, *vt;
+    void *q, *k, *vt;    // bf16, or fp32 on the fp32 parity path
 };
 
 // gate_fn: 0 identity, 1 tanh, 2 sigmoid (applied to gate[n]); act: 0 SiLU, 1 clamped GELU-tanh
@@ -124,6 +124,13 @@ hipError_t launch_gemm_swiglu_q8(const int8_t *a, const float *a_scale, const in
                                  int64_t M, int F, int K, int act, bf16 *u, hipStream_t s);
 hipError_t launch_gemm_qkv_q8(const int8_t *h, const float *h_scale, const int8_t *w, const float *w_scale,
                               int64_t M, int N, int K, const QkvEpiArgs &e, hipStream_t s);
+// the fp32 parity path: fp32 operands, fp32 outputs (q, k, vt and u fp32)
+hipError_t launch_gemm_residual_f32(const float *a, const float *w, int64_t M, int N, int K, const float *resid,
+                                    const float *gate, int gate_fn, const float *bias, float *out, hipStream_t s);
+hipError_t launch_gemm_swiglu_f32(const float *a, const float *w, int64_t M, int F, int K, int act, float *u,
+                                  hipStream_t s);
+hipError_t launch_gemm_qkv_f32(const float *h, const float *w, int64_t M, int N, int K, const QkvEpiArgs &e,
+                               hipStream_t s);
 bool quantize_h256_supported(int cols);
 hipError_t launch_quantize_h256(const void *x, int x_f32, int64_t rows, int cols, int8_t *q, float *scale,
                                 hipStream_t s);
@@ -135,18 +142,23 @@ hipError_t launch_ln_modulate_q8(const void *x, int x_f32, int64_t rows, int dim
 hipError_t launch_flash_attention(const bf16 *q, const bf16 *k, const bf16 *vt, bf16 *out,
                                   int batch, int seq, int seq_pad, int heads, int kv_heads,
                                   int head_dim, int nsplit, void *part, hipStream_t s);
+// fp32 operands (the fp32 parity path); no split
+hipError_t launch_flash_attention_f32(const float *q, const float *k, const float *vt, float *out, int batch,
+                                      int seq, int seq_pad, int heads, int kv_heads, int head_dim, hipStream_t s);
 int attention_split_count(int batch, int seq, int heads, int cus);
 size_t attention_split_bytes(int batch, int heads, int head_dim, int nsplit);
 int device_cu_count();
 
-hipError_t launch_adaln_gemv(const bf16 *w, const float *b, const float *c, int out_dim,
+hipError_t launch_adaln_gemv(const void *w, int w_f32, const float *b, const float *c, int out_dim,
                              int in_dim, int silu_input, float *m, hipStream_t s);
 hipError_t launch_ln_modulate(const void *x, int x_f32, int64_t rows, int dim, int rms,
                               const float *shift, const float *scale, int mode, float eps,
                               bf16 *h, hipStream_t s);
+hipError_t launch_ln_modulate_f32(const float *x, int64_t rows, int dim, int rms, const float *shift,
+                                  const float *scale, int mode, float eps, float *h, hipStream_t s);
 hipError_t launch_euler(float *latent, const float *v, int64_t n, float dsigma, hipStream_t s);
 hipError_t launch_timestep_embedding(float t, int dim, float *out, hipStream_t s);
 hipError_t launch_f32_to_bf16(const float *x, bf16 *y, int64_t n, hipStream_t s);
-hipError_t launch_vt_pad_zero(bf16 *vt, int rows, int seq, int seq_pad, hipStream_t s);
+hipError_t launch_vt_pad_zero(void *vt, int vt_f32, int rows, int seq, int seq_pad, hipStream_t s);
 
 }  // namespace dit

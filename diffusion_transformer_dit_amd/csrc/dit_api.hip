@@ -64,7 +64,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int32_t seq_pad_of(int32_t s) { return (s + 63) / 64 * 64; }
 
-// Workspace of one block evaluation.  In the W8A8 format h holds the int8
+// Workspace of one block evaluation.  On the fp32 path (fp32 weights) the
+// intermediates h, q, k, vt, att and u are fp32.  In the W8A8 format h holds the int8
 // codes of the normed rows (hs their scales), and the attention output and the
 // GLU output get int8 copies (aq/as, uq/us) for the projections that read them.
 // With a ragged sequence (seq % 256 != 0) it also holds the attention's
@@ -78,17 +79,18 @@ constexpr int kMaxAttnSplit = 16;
 BlockWs block_ws(const dit_block_desc &d) {
     const size_t N = (size_t)d.batch * d.seq, D = d.hidden, B = d.batch;
     const size_t hd = d.head_dim, H = d.heads, Hk = d.kv_heads, F = d.ffn;
+    const size_t es = d.w_dtype == DIT_F32 ? 4 : 2;   // bytes per intermediate element
     BlockWs L{};
     size_t off = 0;
     L.m = off;   off += align256(6 * D * 4);
-    L.h = off;   off += align256(N * D * 2);
-    L.q = off;   off += align256(B * H * d.seq * hd * 2);
-    L.k = off;   off += align256(B * Hk * d.seq * hd * 2);
-    L.vt = off;  off += align256(B * Hk * hd * (size_t)seq_pad_of(d.seq) * 2);
-    L.att = off; off += align256(N * H * hd * 2);
+    L.h = off;   off += align256(N * D * es);
+    L.q = off;   off += align256(B * H * d.seq * hd * es);
+    L.k = off;   off += align256(B * Hk * d.seq * hd * es);
+    L.vt = off;  off += align256(B * Hk * hd * (size_t)seq_pad_of(d.seq) * es);
+    L.att = off; off += align256(N * H * hd * es);
     L.x1 = off;  off += align256(N * D * 4);
-    L.u = off;   off += align256(N * F * 2);
-    if (d.seq % 256) {
+    L.u = off;   off += align256(N * F * es);
+    if (d.seq % 256 && d.w_dtype != DIT_F32) {
         L.part = off; off += align256(attention_split_bytes(d.batch, d.heads, d.head_dim, kMaxAttnSplit));
     }
     if (d.fmt == DIT_FMT_W8A8_H256) {
@@ -120,7 +122,9 @@ int check_desc(const dit_block_desc *d) {
     if (d->mod != DIT_MOD_SHIFT_SCALE_GATE && d->mod != DIT_MOD_SCALE_GATE) return fail(DIT_ERR_INVALID_ARG, "bad mod");
     if (d->qk_order != DIT_QK_NORM_ROPE && d->qk_order != DIT_QK_ROPE_NORM) return fail(DIT_ERR_INVALID_ARG, "bad qk_order");
     if (d->fmt != DIT_FMT_BF16 && d->fmt != DIT_FMT_W8A8_H256) return fail(DIT_ERR_INVALID_ARG, "bad fmt");
-    if (d->w_dtype != DIT_BF16) return fail(DIT_ERR_UNSUPPORTED, "weights must be bf16");
+    if (d->w_dtype != DIT_BF16 && d->w_dtype != DIT_F32) return fail(DIT_ERR_INVALID_ARG, "bad w_dtype");
+    if (d->w_dtype == DIT_F32 && (d->x_dtype != DIT_F32 || d->fmt != DIT_FMT_BF16))
+        return fail(DIT_ERR_UNSUPPORTED, "fp32 weights (the fp32 path) need x_dtype F32 and fmt BF16");
     if (d->head_dim != 64 && d->head_dim != 128) return fail(DIT_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
     if (d->hidden % 256) return fail(DIT_ERR_UNSUPPORTED, "hidden must be a multiple of 256");
     if (d->hidden > 8192) return fail(DIT_ERR_UNSUPPORTED, "hidden must be <= 8192");
@@ -208,13 +212,30 @@ int block_body(const dit_block_desc &d, const dit_block_weights &w, const void *
 
     QkvEpiArgs e{d.batch, d.seq, spad, d.heads, d.kv_heads, hd, d.qk_norm, d.rope == DIT_ROPE_HALF, rms,
                  d.qk_order == DIT_QK_ROPE_NORM, d.eps, w.q_g, w.q_b, w.k_g, w.k_b, cosT, sinT, q, k, vt};
+    if (d.w_dtype == DIT_F32) {
+        // the fp32 path: every operand and intermediate fp32 (fp32 MFMA GEMMs,
+        // fp32 attention); x and out are the fp32 residual stream
+        float *hf = (float *)(ws + L.h), *uf = (float *)(ws + L.u), *af = (float *)(ws + L.att);
+        float *qf = (float *)(ws + L.q), *kf = (float *)(ws + L.k), *vf = (float *)(ws + L.vt);
+        DIT_TRY_HIP(launch_ln_modulate_f32((const float *)x, N, D, rms, shift1, scale1, mode, d.eps, hf, s));
+        DIT_TRY_HIP(launch_vt_pad_zero(vf, 1, d.batch * d.kv_heads * hd, d.seq, spad, s));
+        DIT_TRY_HIP(launch_gemm_qkv_f32(hf, (const float *)w.w_qkv, N, qkv_dim, D, e, s));
+        DIT_TRY_HIP(launch_flash_attention_f32(qf, kf, vf, af, d.batch, d.seq, spad, d.heads, d.kv_heads, hd, s));
+        DIT_TRY_HIP(launch_gemm_residual_f32(af, (const float *)w.w_o, N, D, d.heads * hd, (const float *)x, gate1,
+                                             d.gate, nullptr, x1, s));
+        DIT_TRY_HIP(launch_ln_modulate_f32(x1, N, D, rms, shift2, scale2, mode, d.eps, hf, s));
+        DIT_TRY_HIP(launch_gemm_swiglu_f32(hf, (const float *)w.w_gate_up, N, F, D, d.act, uf, s));
+        DIT_TRY_HIP(launch_gemm_residual_f32(uf, (const float *)w.w_down, N, D, F, x1, gate2, d.gate, nullptr,
+                                             (float *)out, s));
+        return DIT_OK;
+    }
     if (d.fmt == DIT_FMT_W8A8_H256) {
         // the four projections in int8 (zml-flow-rs page §VII W8A8 with H256 on
         // both sides); norms, attention and the residual stream as in bf16
         int8_t *hq = (int8_t *)(ws + L.h), *aq = (int8_t *)(ws + L.aq), *uq = (int8_t *)(ws + L.uq);
         float *hs = (float *)(ws + L.hs), *as = (float *)(ws + L.as), *us = (float *)(ws + L.us);
         DIT_TRY_HIP(launch_ln_modulate_q8(x, x_f32, N, D, rms, shift1, scale1, mode, d.eps, hq, hs, s));
-        DIT_TRY_HIP(launch_vt_pad_zero(vt, d.batch * d.kv_heads * hd, d.seq, spad, s));
+        DIT_TRY_HIP(launch_vt_pad_zero(vt, 0, d.batch * d.kv_heads * hd, d.seq, spad, s));
         DIT_TRY_HIP(launch_gemm_qkv_q8(hq, hs, (const int8_t *)w.w_qkv, w.s_qkv, N, qkv_dim, D, e, s));
         DIT_TRY_HIP(launch_flash_attention(q, k, vt, att, d.batch, d.seq, spad, d.heads, d.kv_heads, hd, nsplit,
                                            part, s));
@@ -229,7 +250,7 @@ int block_body(const dit_block_desc &d, const dit_block_weights &w, const void *
         return DIT_OK;
     }
     DIT_TRY_HIP(launch_ln_modulate(x, x_f32, N, D, rms, shift1, scale1, mode, d.eps, h, s));
-    DIT_TRY_HIP(launch_vt_pad_zero(vt, d.batch * d.kv_heads * hd, d.seq, spad, s));
+    DIT_TRY_HIP(launch_vt_pad_zero(vt, 0, d.batch * d.kv_heads * hd, d.seq, spad, s));
     DIT_TRY_HIP(launch_gemm_qkv(h, (const bf16 *)w.w_qkv, N, qkv_dim, D, e, s));
     DIT_TRY_HIP(launch_flash_attention(q, k, vt, att, d.batch, d.seq, spad, d.heads, d.kv_heads, hd, nsplit, part,
                                        s));
@@ -330,7 +351,8 @@ int dit_block_forward(const dit_block_desc *desc, const dit_block_weights *w, co
     float *m = nullptr;
     if (d.cond_dim > 0) {
         m = (float *)(wsb + L.m);
-        DIT_TRY_HIP(launch_adaln_gemv((const bf16 *)w->w_ada, w->b_ada, cond, ada_rows(d), d.cond_dim, 1, m, s));
+        DIT_TRY_HIP(launch_adaln_gemv(w->w_ada, d.w_dtype == DIT_F32, w->b_ada, cond, ada_rows(d), d.cond_dim, 1, m,
+                                      s));
     }
     const int xf = d.x_dtype == DIT_F32;
     DIT_TRY(block_body(d, *w, x, xf, m, rope_cos, rope_sin, out, xf, wsb, L, s));
@@ -369,9 +391,17 @@ int dit_stack_step(const dit_model *model, const float *latent, const float *con
     float *m = (float *)(wsb + L.blk.m);
     const int D = d.hidden;
 
-    // patch embedding: x = bf16(latent) W_in^T + b_in (fp32 residual stream)
-    DIT_TRY_HIP(launch_f32_to_bf16(latent, lat, N * M.latent_dim, s));
-    DIT_TRY_HIP(launch_gemm_residual(lat, (const bf16 *)M.w_in, N, D, M.latent_dim, nullptr, 1, nullptr, 0, M.b_in, x, 1, s));
+    const bool f32 = d.w_dtype == DIT_F32;
+    // patch embedding: x = bf16(latent) W_in^T + b_in (fp32 residual stream);
+    // the fp32 path takes the fp32 latent as it is
+    if (f32) {
+        DIT_TRY_HIP(launch_gemm_residual_f32(latent, (const float *)M.w_in, N, D, M.latent_dim, nullptr, nullptr, 0,
+                                             M.b_in, x, s));
+    } else {
+        DIT_TRY_HIP(launch_f32_to_bf16(latent, lat, N * M.latent_dim, s));
+        DIT_TRY_HIP(launch_gemm_residual(lat, (const bf16 *)M.w_in, N, D, M.latent_dim, nullptr, 1, nullptr, 0, M.b_in,
+                                         x, 1, s));
+    }
 
     bool shared = true;
     for (int l = 1; l < M.layers; ++l)
@@ -379,12 +409,19 @@ int dit_stack_step(const dit_model *model, const float *latent, const float *con
     for (int l = 0; l < M.layers; ++l) {
         const dit_block_weights &w = M.blocks[l];
         if (l == 0 || !shared)
-            DIT_TRY_HIP(launch_adaln_gemv((const bf16 *)w.w_ada, w.b_ada, cond, ada_rows(d), d.cond_dim, 1, m, s));
+            DIT_TRY_HIP(launch_adaln_gemv(w.w_ada, f32, w.b_ada, cond, ada_rows(d), d.cond_dim, 1, m, s));
         DIT_TRY(block_body(d, w, x, 1, m, rope_cos, rope_sin, x, 1, wsb, L.blk, s));
     }
 
     // final AdaLN-continuous norm: [scale | shift] = W_f c + b_f (no SiLU), then projection
-    DIT_TRY_HIP(launch_adaln_gemv((const bf16 *)M.w_fmod, M.b_fmod, cond, 2 * D, d.cond_dim, 0, fm, s));
+    DIT_TRY_HIP(launch_adaln_gemv(M.w_fmod, f32, M.b_fmod, cond, 2 * D, d.cond_dim, 0, fm, s));
+    if (f32) {
+        float *hf = (float *)(wsb + L.blk.h);
+        DIT_TRY_HIP(launch_ln_modulate_f32(x, N, D, d.norm == DIT_RMSNORM, fm + D, fm, 0, d.eps, hf, s));
+        DIT_TRY_HIP(launch_gemm_residual_f32(hf, (const float *)M.w_out, N, M.latent_dim, D, nullptr, nullptr, 0,
+                                             M.b_out, velocity, s));
+        return ok();
+    }
     bf16 *h = (bf16 *)(wsb + L.blk.h);
     DIT_TRY_HIP(launch_ln_modulate(x, 1, N, D, d.norm == DIT_RMSNORM, fm + D, fm, 0, d.eps, h, s));
     DIT_TRY_HIP(launch_gemm_residual(h, (const bf16 *)M.w_out, N, M.latent_dim, D, nullptr, 1, nullptr, 0, M.b_out,
@@ -473,7 +510,7 @@ int dit_adaln_modulation(const void *w, const float *b, const float *c, int32_t 
     if (!aligned16(w) || !aligned16(c) || !aligned4(m) || (b && !aligned4(b)))
         return fail(DIT_ERR_ALIGNMENT, "w and c must be 16-byte aligned");
     DIT_TRY(device_check());
-    DIT_TRY_HIP(launch_adaln_gemv((const bf16 *)w, b, c, out_dim, in_dim, silu_input, m, as_stream(stream)));
+    DIT_TRY_HIP(launch_adaln_gemv(w, 0, b, c, out_dim, in_dim, silu_input, m, as_stream(stream)));
     return ok();
 }
 
@@ -507,12 +544,17 @@ int dit_qkv_rope(const dit_block_desc *desc, const void *h, const void *w_qkv, c
     DIT_TRY(device_check());
     hipStream_t s = as_stream(stream);
     const int spad = seq_pad_of(d.seq);
-    DIT_TRY_HIP(launch_vt_pad_zero((bf16 *)vt, d.batch * d.kv_heads * d.head_dim, d.seq, spad, s));
+    const int f32 = d.w_dtype == DIT_F32;
+    DIT_TRY_HIP(launch_vt_pad_zero(vt, f32, d.batch * d.kv_heads * d.head_dim, d.seq, spad, s));
     QkvEpiArgs e{d.batch, d.seq, spad, d.heads, d.kv_heads, d.head_dim, d.qk_norm, d.rope == DIT_ROPE_HALF,
                  d.norm == DIT_RMSNORM, d.qk_order == DIT_QK_ROPE_NORM, d.eps, q_g, q_b, k_g, k_b, rope_cos, rope_sin,
-                 (bf16 *)q, (bf16 *)k, (bf16 *)vt};
-    DIT_TRY_HIP(launch_gemm_qkv((const bf16 *)h, (const bf16 *)w_qkv, (int64_t)d.batch * d.seq,
-                                (d.heads + 2 * d.kv_heads) * d.head_dim, d.hidden, e, s));
+                 q, k, vt};
+    const int64_t N = (int64_t)d.batch * d.seq;
+    const int qkv_dim = (d.heads + 2 * d.kv_heads) * d.head_dim;
+    if (f32)
+        DIT_TRY_HIP(launch_gemm_qkv_f32((const float *)h, (const float *)w_qkv, N, qkv_dim, d.hidden, e, s));
+    else
+        DIT_TRY_HIP(launch_gemm_qkv((const bf16 *)h, (const bf16 *)w_qkv, N, qkv_dim, d.hidden, e, s));
     return ok();
 }
 
@@ -524,9 +566,14 @@ int dit_flash_attention(const dit_block_desc *desc, const void *q, const void *k
     if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(out))
         return fail(DIT_ERR_ALIGNMENT, "q, k, vt, out must be 16-byte aligned");
     DIT_TRY(device_check());
-    DIT_TRY_HIP(launch_flash_attention((const bf16 *)q, (const bf16 *)k, (const bf16 *)vt, (bf16 *)out, d.batch, d.seq,
-                                       seq_pad_of(d.seq), d.heads, d.kv_heads, d.head_dim, 1, nullptr,
-                                       as_stream(stream)));
+    if (d.w_dtype == DIT_F32)
+        DIT_TRY_HIP(launch_flash_attention_f32((const float *)q, (const float *)k, (const float *)vt, (float *)out,
+                                               d.batch, d.seq, seq_pad_of(d.seq), d.heads, d.kv_heads, d.head_dim,
+                                               as_stream(stream)));
+    else
+        DIT_TRY_HIP(launch_flash_attention((const bf16 *)q, (const bf16 *)k, (const bf16 *)vt, (bf16 *)out, d.batch,
+                                           d.seq, seq_pad_of(d.seq), d.heads, d.kv_heads, d.head_dim, 1, nullptr,
+                                           as_stream(stream)));
     return ok();
 }
 
@@ -544,6 +591,7 @@ int dit_flash_attention_split(const dit_block_desc *desc, const void *q, const v
     const dit_block_desc &d = *desc;
     if (!q || !k || !vt || !out) return fail(DIT_ERR_INVALID_ARG, "NULL pointer");
     if (nsplit < 1 || nsplit > 64) return fail(DIT_ERR_INVALID_ARG, "nsplit must be in [1, 64]");
+    if (d.w_dtype == DIT_F32) return fail(DIT_ERR_UNSUPPORTED, "the fp32 path has no split-KV form");
     const size_t need = attention_split_bytes(d.batch, d.heads, d.head_dim, nsplit);
     if (need && !ws) return fail(DIT_ERR_INVALID_ARG, "ws is required for nsplit > 1");
     if (ws_bytes < need) return fail(DIT_ERR_WORKSPACE, "workspace %zu < required %zu bytes", ws_bytes, need);
@@ -700,10 +748,10 @@ int dit_qkv_rope_w8a8(const dit_block_desc *desc, const void *h, const float *h_
     DIT_TRY(device_check());
     hipStream_t s = as_stream(stream);
     const int spad = seq_pad_of(d.seq);
-    DIT_TRY_HIP(launch_vt_pad_zero((bf16 *)vt, d.batch * d.kv_heads * d.head_dim, d.seq, spad, s));
+    DIT_TRY_HIP(launch_vt_pad_zero(vt, 0, d.batch * d.kv_heads * d.head_dim, d.seq, spad, s));
     QkvEpiArgs e{d.batch, d.seq, spad, d.heads, d.kv_heads, d.head_dim, d.qk_norm, d.rope == DIT_ROPE_HALF,
                  d.norm == DIT_RMSNORM, d.qk_order == DIT_QK_ROPE_NORM, d.eps, q_g, q_b, k_g, k_b, rope_cos, rope_sin,
-                 (bf16 *)q, (bf16 *)k, (bf16 *)vt};
+                 q, k, vt};
     DIT_TRY_HIP(launch_gemm_qkv_q8((const int8_t *)h, h_scale, (const int8_t *)w_qkv, w_scale, N, qkv_dim, d.hidden,
                                    e, s));
     return ok();

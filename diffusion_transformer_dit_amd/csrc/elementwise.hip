@@ -13,26 +13,37 @@
 namespace dit {
 
 // ---------------------------------------------------------------------------
-// AdaLN GEMV: one wave per 4 output rows; each lane streams 16-byte chunks of
-// the 4 weight rows (8 bf16 each) against act(c) of the same 8 inputs, so a
-// lane keeps 8 independent 16-byte loads in flight per unrolled step.
+// AdaLN GEMV: one wave per 4 output rows; each lane streams 8-element chunks
+// of the 4 weight rows (16 bytes of bf16, or 32 bytes of fp32 weights) against
+// act(c) of the same 8 inputs, so a lane keeps 8 independent chunk loads in
+// flight per unrolled step.
 // ---------------------------------------------------------------------------
 constexpr int kGemvRows = 4;
 
+struct f32x8 {
+    floatx4 lo, hi;
+    __device__ __forceinline__ float operator[](int k) const { return k < 4 ? lo[k] : hi[k - 4]; }
+};
+__device__ __forceinline__ bf16x8 load8(const bf16 *p) { return *(const bf16x8 *)p; }
+__device__ __forceinline__ f32x8 load8(const float *p) {
+    return f32x8{*(const floatx4 *)p, *(const floatx4 *)(p + 4)};
+}
+
+template <typename TW>
 __global__ __launch_bounds__(256)
-void adaln_gemv_kernel(const bf16 *__restrict__ W, const float *__restrict__ b, const float *__restrict__ c,
+void adaln_gemv_kernel(const TW *__restrict__ W, const float *__restrict__ b, const float *__restrict__ c,
                        int out_dim, int in_dim, int silu_input, float *__restrict__ m) {
     const int lane = threadIdx.x & 63;
     const int o0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kGemvRows;
     if (o0 >= out_dim) return;
     const int nch = in_dim >> 3;   // 8-element chunks per row
     float acc[kGemvRows] = {0.f, 0.f, 0.f, 0.f};
-    const bf16 *wr[kGemvRows];
+    const TW *wr[kGemvRows];
 #pragma unroll
     for (int r = 0; r < kGemvRows; ++r) wr[r] = W + (size_t)min(o0 + r, out_dim - 1) * in_dim;
 
     for (int ch0 = lane; ch0 < nch; ch0 += 128) {
-        bf16x8 wv[2][kGemvRows];
+        decltype(load8(W)) wv[2][kGemvRows];
         floatx4 c0[2], c1[2];
         bool ok[2];
 #pragma unroll
@@ -41,7 +52,7 @@ void adaln_gemv_kernel(const bf16 *__restrict__ W, const float *__restrict__ b, 
             ok[u] = ch < nch;
             const int chs = ok[u] ? ch : ch0;
 #pragma unroll
-            for (int r = 0; r < kGemvRows; ++r) wv[u][r] = *(const bf16x8 *)(wr[r] + chs * 8);
+            for (int r = 0; r < kGemvRows; ++r) wv[u][r] = load8(wr[r] + chs * 8);
             c0[u] = *(const floatx4 *)(c + chs * 8);
             c1[u] = *(const floatx4 *)(c + chs * 8 + 4);
         }
@@ -66,11 +77,15 @@ void adaln_gemv_kernel(const bf16 *__restrict__ W, const float *__restrict__ b, 
     }
 }
 
-hipError_t launch_adaln_gemv(const bf16 *w, const float *b, const float *c, int out_dim, int in_dim,
+hipError_t launch_adaln_gemv(const void *w, int w_f32, const float *b, const float *c, int out_dim, int in_dim,
                              int silu_input, float *m, hipStream_t s) {
     const int waves = (out_dim + kGemvRows - 1) / kGemvRows;
-    hipLaunchKernelGGL(adaln_gemv_kernel, dim3((waves + 3) / 4), dim3(256), 0, s, w, b, c, out_dim, in_dim,
-                       silu_input, m);
+    if (w_f32)
+        hipLaunchKernelGGL(adaln_gemv_kernel<float>, dim3((waves + 3) / 4), dim3(256), 0, s, (const float *)w, b, c,
+                           out_dim, in_dim, silu_input, m);
+    else
+        hipLaunchKernelGGL(adaln_gemv_kernel<bf16>, dim3((waves + 3) / 4), dim3(256), 0, s, (const bf16 *)w, b, c,
+                           out_dim, in_dim, silu_input, m);
     return hipGetLastError();
 }
 
@@ -83,12 +98,25 @@ hipError_t launch_adaln_gemv(const bf16 *w, const float *b, const float *c, int 
 // then waits for every load before issuing the next).
 //   mode 0: h = n * (1 + scale) + shift      mode 1: h = n * scale + shift
 // n = (x - mean) / sqrt(var + eps) (LayerNorm) or x / sqrt(mean(x^2) + eps)
-// (RMSNorm, RMS = true: no centring).
+// (RMSNorm, RMS = true: no centring).  h is bf16, or fp32 (TH = float) on the
+// fp32 path.
 // ---------------------------------------------------------------------------
-template <typename TX, int IT, bool RMS>
+template <typename TH>
+__device__ __forceinline__ void store4(TH *p, const floatx4 &v) {
+    if constexpr (sizeof(TH) == 4) {
+        *(floatx4 *)p = v;
+    } else {
+        bf16x4 o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = f2bf(v[k]);
+        *(bf16x4 *)p = o;
+    }
+}
+
+template <typename TX, typename TH, int IT, bool RMS>
 __global__ __launch_bounds__(256)
 void ln_modulate_kernel(const TX *__restrict__ x, int64_t rows, const float *__restrict__ shift,
-                        const float *__restrict__ scale, int mode, float eps, bf16 *__restrict__ h) {
+                        const float *__restrict__ scale, int mode, float eps, TH *__restrict__ h) {
     constexpr int dim = IT * 256;
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -123,17 +151,17 @@ void ln_modulate_kernel(const TX *__restrict__ x, int64_t rows, const float *__r
         }
     const float rstd = rsqrtf(group_sum<64>(ss) * (1.0f / dim) + eps);
     const float one = mode == 0 ? 1.0f : 0.0f;
-    bf16 *hr = h + row * dim;
+    TH *hr = h + row * dim;
     if (scale && shift) {
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
             const int i = it * 256 + lane * 4;
             const floatx4 mul = *(const floatx4 *)(scale + i);
             const floatx4 add = *(const floatx4 *)(shift + i);
-            bf16x4 o;
+            floatx4 o;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) o[k] = f2bf(v[it][k] * rstd * (mul[k] + one) + add[k]);
-            *(bf16x4 *)(hr + i) = o;
+            for (int k = 0; k < 4; ++k) o[k] = v[it][k] * rstd * (mul[k] + one) + add[k];
+            store4(hr + i, o);
         }
     } else {
         // mode 1 with a null scale (taken as 1) and/or a null shift (taken as 0)
@@ -143,22 +171,22 @@ void ln_modulate_kernel(const TX *__restrict__ x, int64_t rows, const float *__r
             floatx4 mul = {1.f, 1.f, 1.f, 1.f}, add = {0.f, 0.f, 0.f, 0.f};
             if (scale) mul = *(const floatx4 *)(scale + i) + one;
             if (shift) add = *(const floatx4 *)(shift + i);
-            bf16x4 o;
+            floatx4 o;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) o[k] = f2bf(v[it][k] * rstd * mul[k] + add[k]);
-            *(bf16x4 *)(hr + i) = o;
+            for (int k = 0; k < 4; ++k) o[k] = v[it][k] * rstd * mul[k] + add[k];
+            store4(hr + i, o);
         }
     }
 }
 
-template <typename TX, bool RMS>
+template <typename TX, typename TH, bool RMS>
 static hipError_t ln_modulate_typed(const TX *x, int64_t rows, int dim, const float *shift, const float *scale,
-                                    int mode, float eps, bf16 *h, hipStream_t s) {
+                                    int mode, float eps, TH *h, hipStream_t s) {
     const dim3 grid((unsigned)((rows + 3) / 4));
     switch (dim >> 8) {
 #define DIT_LN_CASE(n)                                                                                 \
     case n:                                                                                            \
-        hipLaunchKernelGGL((ln_modulate_kernel<TX, n, RMS>), grid, dim3(256), 0, s, x, rows, shift, scale, \
+        hipLaunchKernelGGL((ln_modulate_kernel<TX, TH, n, RMS>), grid, dim3(256), 0, s, x, rows, shift, scale, \
                            mode, eps, h);                                                              \
         break;
         DIT_LN_CASE(1) DIT_LN_CASE(2) DIT_LN_CASE(3) DIT_LN_CASE(4) DIT_LN_CASE(5) DIT_LN_CASE(6)
@@ -178,10 +206,17 @@ hipError_t launch_ln_modulate(const void *x, int x_f32, int64_t rows, int dim, i
                               const float *scale, int mode, float eps, bf16 *h, hipStream_t s) {
     if (dim % 256 != 0) return hipErrorInvalidValue;
     if (x_f32)
-        return rms ? ln_modulate_typed<float, true>((const float *)x, rows, dim, shift, scale, mode, eps, h, s)
-                   : ln_modulate_typed<float, false>((const float *)x, rows, dim, shift, scale, mode, eps, h, s);
-    return rms ? ln_modulate_typed<bf16, true>((const bf16 *)x, rows, dim, shift, scale, mode, eps, h, s)
-               : ln_modulate_typed<bf16, false>((const bf16 *)x, rows, dim, shift, scale, mode, eps, h, s);
+        return rms ? ln_modulate_typed<float, bf16, true>((const float *)x, rows, dim, shift, scale, mode, eps, h, s)
+                   : ln_modulate_typed<float, bf16, false>((const float *)x, rows, dim, shift, scale, mode, eps, h, s);
+    return rms ? ln_modulate_typed<bf16, bf16, true>((const bf16 *)x, rows, dim, shift, scale, mode, eps, h, s)
+               : ln_modulate_typed<bf16, bf16, false>((const bf16 *)x, rows, dim, shift, scale, mode, eps, h, s);
+}
+
+hipError_t launch_ln_modulate_f32(const float *x, int64_t rows, int dim, int rms, const float *shift,
+                                  const float *scale, int mode, float eps, float *h, hipStream_t s) {
+    if (dim % 256 != 0) return hipErrorInvalidValue;
+    return rms ? ln_modulate_typed<float, float, true>(x, rows, dim, shift, scale, mode, eps, h, s)
+               : ln_modulate_typed<float, float, false>(x, rows, dim, shift, scale, mode, eps, h, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -246,23 +281,27 @@ hipError_t launch_f32_to_bf16(const float *x, bf16 *y, int64_t n, hipStream_t s)
 // ---------------------------------------------------------------------------
 // zero the padded key positions [seq, seq_pad) of every row of transposed V
 // ---------------------------------------------------------------------------
+template <typename TV>
 __global__ __launch_bounds__(256)
-void vt_pad_zero_kernel(bf16 *__restrict__ vt, int rows, int seq, int seq_pad) {
+void vt_pad_zero_kernel(TV *__restrict__ vt, int rows, int seq, int seq_pad) {
     const int pad = seq_pad - seq;
     const int64_t n = (int64_t)rows * pad;
     const int64_t stride = (int64_t)gridDim.x * 256;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
         const int64_t r = i / pad;
         const int c = (int)(i - r * pad);
-        vt[r * seq_pad + seq + c] = f2bf(0.f);
+        vt[r * seq_pad + seq + c] = TV(0.f);
     }
 }
 
-hipError_t launch_vt_pad_zero(bf16 *vt, int rows, int seq, int seq_pad, hipStream_t s) {
+hipError_t launch_vt_pad_zero(void *vt, int vt_f32, int rows, int seq, int seq_pad, hipStream_t s) {
     const int64_t n = (int64_t)rows * (seq_pad - seq);
     if (n <= 0) return hipSuccess;
     const int blocks = (int)std::min<int64_t>((n + 255) / 256, 4096);
-    hipLaunchKernelGGL(vt_pad_zero_kernel, dim3(blocks), dim3(256), 0, s, vt, rows, seq, seq_pad);
+    if (vt_f32)
+        hipLaunchKernelGGL(vt_pad_zero_kernel<float>, dim3(blocks), dim3(256), 0, s, (float *)vt, rows, seq, seq_pad);
+    else
+        hipLaunchKernelGGL(vt_pad_zero_kernel<bf16>, dim3(blocks), dim3(256), 0, s, (bf16 *)vt, rows, seq, seq_pad);
     return hipGetLastError();
 }
 

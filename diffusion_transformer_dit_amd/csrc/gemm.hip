@@ -103,6 +103,14 @@ __device__ __forceinline__ floatx16 mfma32(intx4 a, intx4 b, floatx16 c) {
     return __builtin_bit_cast(floatx16,
                               __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, __builtin_bit_cast(intx16, c), 0, 0, 0));
 }
+// fp32 operands (the fp32 parity path): a 16-byte fragment holds 4 k values per
+// lane, consumed by four v_mfma_f32_32x32x2_f32 (value u of both operands: the
+// same k in A and B, so every k of the 32-byte step is summed once)
+__device__ __forceinline__ floatx16 mfma32(floatx4 a, floatx4 b, floatx16 c) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[u], b[u], c, 0, 0, 0);
+    return c;
+}
 
 __device__ __forceinline__ int acc_row(int i, int e, int lhalf);
 
@@ -133,7 +141,8 @@ void gemm_kernel(const void *__restrict__ A, const void *__restrict__ W, int M, 
     // q of wave w fills tile rows kRowsPerLoad (q waves + w) ..; lane l brings
     // row + l / kChunks into physical slot l % kChunks, i.e. the logical chunk
     // (l % kChunks) ^ swz(row).
-    using Frag = typename std::conditional<T::ES == 2, bf16x8, intx4>::type;
+    using Frag = typename std::conditional<T::ES == 2, bf16x8,
+                                           typename std::conditional<T::ES == 1, intx4, floatx4>::type>::type;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)M * (uint32_t)K * (uint32_t)T::ES);
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(W, (uint32_t)w_rows * (uint32_t)K * (uint32_t)T::ES);
     const int lr = lane / T::kChunks, ls = lane % T::kChunks;
@@ -253,7 +262,7 @@ void gemm_kernel(const void *__restrict__ A, const void *__restrict__ W, int M, 
     wait_vmcnt<0>();      // retire the trailing (never read) loads before LDS is reused
     __syncthreads();
 
-    if constexpr (T::ES == 2 || Epi::kDequant) {
+    if constexpr (T::ES != 1 || Epi::kDequant) {
         // bf16, or an epilogue that dequantizes row block by row block itself
         epi.template apply<T>(acc, m0 + wm * T::kWaveM, tn, wn, lane, M, smem);
     } else {
@@ -376,10 +385,10 @@ struct EpiResidual {
 // ---------------------------------------------------------------------------
 // epilogue: u = act(gate) * up, act = SiLU or the clamped GELU-tanh
 // ---------------------------------------------------------------------------
-template <int ACT>     // 0: SiLU (SwiGLU), 1: clamped GELU-tanh
+template <int ACT, typename TU = bf16>     // ACT 0: SiLU (SwiGLU), 1: clamped GELU-tanh; TU: output type
 struct EpiSwiglu {
     static constexpr bool kDequant = false;
-    bf16 *u;
+    TU *u;
     int F;
     template <class T> static constexpr int lds_bytes() { return 0; }
     template <class T>
@@ -398,7 +407,7 @@ struct EpiSwiglu {
                     const int row = row0 + acc_row(i, e, lhalf);
                     if (row < M) {
                         const float g = ACT == 1 ? gelu_tanh_f(acc[i][j][e]) : silu_f(acc[i][j][e]);
-                        u[(size_t)row * F + f] = f2bf(g * acc[i][j + HJ][e]);
+                        u[(size_t)row * F + f] = from_f32<TU>(g * acc[i][j + HJ][e]);
                     }
                 }
         }
@@ -433,9 +442,12 @@ struct EpiSwiglu {
 // ---------------------------------------------------------------------------
 constexpr int kQkvStride = 260;   // floats per staged row: 256 + 4, so 16 row-per-lane reads hit distinct banks
 
-template <int HD, bool RMS, bool RF>   // qk-norm kind RMSNorm; RoPE before the qk-norm
+// RMS: qk-norm kind RMSNorm; RF: RoPE before the qk-norm; TQ: type of q, k, vt
+// (fp32 on the fp32 parity path: written straight from registers, no LDS copy-out)
+template <int HD, bool RMS, bool RF, typename TQ = bf16>
 struct EpiQkv {
     static constexpr bool kDequant = false;
+    static constexpr bool kF32 = sizeof(TQ) == 4;
     QkvEpiArgs e;
     static constexpr int kStageBytes = 2 * 64 * kQkvStride * 4;
     static constexpr int kHeadBlock = 64 * HD * 2;        // bf16 bytes of one head x 64 tokens
@@ -515,6 +527,17 @@ struct EpiQkv {
             // column (within the head) of this lane's 8-value chunk q, q = 0..7
             auto qcol = [&](int q) {
                 return e.rope_half ? (q < 4 ? pair0 + q * 8 : HD / 2 + pair0 + (q - 4) * 8) : part * 64 + q * 8;
+            };
+            // fp32 path: chunk q (8 values) of this lane's q/k row straight to global memory
+            auto store_f32 = [&](int q, const float (&y)[8]) {
+                const int row = rbase + rl;
+                if (row < M) {
+                    const int bi = row / S, si = row - bi * S;
+                    float *dst = (float *)(sect == 0 ? e.q : e.k) +
+                                 (((size_t)bi * (sect == 0 ? e.heads : e.kv_heads) + head) * S + si) * HD + qcol(q);
+                    *(floatx4 *)dst = floatx4{y[0], y[1], y[2], y[3]};
+                    *(floatx4 *)(dst + 4) = floatx4{y[4], y[5], y[6], y[7]};
+                }
             };
             if (sect < 2) {
                 // The row is read from LDS once per pass (mean, centred variance,
@@ -604,8 +627,12 @@ struct EpiQkv {
                         float y[8];
                         raw(q, y);
                         if (rf) { rot_il(q, y); nrm(q, y); } else { nrm(q, y); rot_il(q, y); }
+                        if constexpr (kF32) {
+                            store_f32(q, y);
+                        } else {
 #pragma unroll
-                        for (int u = 0; u < 8; ++u) o[q][u] = f2bf(y[u]);
+                            for (int u = 0; u < 8; ++u) o[q][u] = f2bf(y[u]);
+                        }
                     }
                 } else {
 #pragma unroll
@@ -622,18 +649,35 @@ struct EpiQkv {
                             nrm(q + 4, yb);
                             rot_half(q, ya, yb);
                         }
+                        if constexpr (kF32) {
+                            store_f32(q, ya);
+                            store_f32(q + 4, yb);
+                        } else {
 #pragma unroll
-                        for (int u = 0; u < 8; ++u) { o[q][u] = f2bf(ya[u]); o[q + 4][u] = f2bf(yb[u]); }
+                            for (int u = 0; u < 8; ++u) { o[q][u] = f2bf(ya[u]); o[q + 4][u] = f2bf(yb[u]); }
+                        }
                     }
                 }
             } else {
                 // v: head-dim column `within` over the 64 staged tokens
                 const float *src = red + hl * HD + within;
+                if constexpr (kF32) {
+                    for (int r = 0; r < 64; ++r) {
+                        const int row = rbase + r;
+                        if (row < M) {
+                            const int bi = row / S, si = row - bi * S;
+                            ((float *)e.vt)[(((size_t)bi * e.kv_heads + head) * HD + within) * e.seq_pad + si] =
+                                src[r * kQkvStride];
+                        }
+                    }
+                } else {
 #pragma unroll
-                for (int r8 = 0; r8 < 8; ++r8)
+                    for (int r8 = 0; r8 < 8; ++r8)
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) o[r8][u] = f2bf(src[(r8 * 8 + u) * kQkvStride]);
+                        for (int u = 0; u < 8; ++u) o[r8][u] = f2bf(src[(r8 * 8 + u) * kQkvStride]);
+                }
             }
+            if constexpr (kF32) continue;   // fp32 results are already stored
 
             // 3. results into LDS in output order (after every lane's fp32 reads)
             wait_vmcnt<63, 0>();
@@ -663,7 +707,7 @@ struct EpiQkv {
                     const int row = rbase + r;
                     if (row < M) {
                         const int bi = row / S, si = row - bi * S;
-                        bf16 *dst = (psect == 0 ? e.q : e.k) +
+                        bf16 *dst = (bf16 *)(psect == 0 ? e.q : e.k) +
                                     (((size_t)bi * (psect == 0 ? e.heads : e.kv_heads) + phead) * S + si) * HD + c * 8;
                         *(bf16x8 *)dst = *(const bf16x8 *)(ob + hs * kHeadBlock + qk_slot(r, c));
                     }
@@ -671,14 +715,14 @@ struct EpiQkv {
                     const int d = pw >> 3, c = pw & 7;
                     const bf16x8 v = *(const bf16x8 *)(ob + hs * kHeadBlock + v_slot(d, c));
                     if (v_fast) {
-                        *(bf16x8 *)(e.vt + (((size_t)b0 * e.kv_heads + phead) * HD + d) * e.seq_pad + s0 + c * 8) = v;
+                        *(bf16x8 *)((bf16 *)e.vt + (((size_t)b0 * e.kv_heads + phead) * HD + d) * e.seq_pad + s0 + c * 8) = v;
                     } else {
 #pragma unroll
                         for (int u = 0; u < 8; ++u) {
                             const int row = rbase + c * 8 + u;
                             if (row < M) {
                                 const int bi = row / S, si = row - bi * S;
-                                e.vt[(((size_t)bi * e.kv_heads + phead) * HD + d) * e.seq_pad + si] = v[u];
+                                ((bf16 *)e.vt)[(((size_t)bi * e.kv_heads + phead) * HD + d) * e.seq_pad + si] = v[u];
                             }
                         }
                     }
@@ -704,6 +748,20 @@ using TileNarrowQ = Tile<256, 128, 2, 2, 128, 2, 1>;
 using Tile8wHalf = Tile<128, 256, 2, 4>;
 using Tile8wHalfQ = Tile<128, 256, 2, 4, 128, 2, 1>;
 
+// The tile family of an operand format: 0 bf16, 1 int8 (W8A8), 2 fp32 (the
+// fp32 parity path: 32 floats of K per 128-byte LDS row, fp32 MFMA)
+template <int FMT> struct TileSet;
+template <> struct TileSet<0> {
+    using S = Tile8w; using Tall = Tile8wTall; using Nar = TileNarrow; using Half = Tile8wHalf;
+};
+template <> struct TileSet<1> {
+    using S = Tile8wQ; using Tall = Tile8wTallQ; using Nar = TileNarrowQ; using Half = Tile8wHalfQ;
+};
+template <> struct TileSet<2> {
+    using S = Tile<256, 256, 2, 4, 32, 2, 4>; using Tall = Tile<320, 256, 2, 4, 32, 2, 4>;
+    using Nar = Tile<256, 128, 2, 2, 32, 2, 4>; using Half = Tile<128, 256, 2, 4, 32, 2, 4>;
+};
+
 
 // Tile height for an M x N output of 256-wide column tiles: the 320-row tile
 // when it needs fewer rounds of workgroups over the CUs than the 256-row one
@@ -716,14 +774,22 @@ static bool prefer_tall(int64_t M, int N) {
     return r320 * 320 < r256 * 256;
 }
 
-// int8 operands carry their row scales (Scales), bf16 operands none (NoScales)
+// int8 operands carry their row scales (Scales), bf16 (NoScales) and fp32
+// (F32Ops) operands none
 struct NoScales {
     static constexpr bool kQ8 = false;
+    static constexpr int kFmt = 0;
     const float *a = nullptr, *w = nullptr;
 };
 struct Scales {
     static constexpr bool kQ8 = true;
+    static constexpr int kFmt = 1;
     const float *a, *w;
+};
+struct F32Ops {
+    static constexpr bool kQ8 = false;
+    static constexpr int kFmt = 2;
+    const float *a = nullptr, *w = nullptr;
 };
 
 // rows [m_base, M) in tiles of T::BM
@@ -771,9 +837,9 @@ template <typename TR, typename TO, class SC>
 static hipError_t residual_typed(const void *a, const void *w, int64_t M, int N, int K, const void *resid,
                                  const float *gate, int gate_fn, const float *bias, void *out, SC sc,
                                  hipStream_t s) {
-    using TT = typename std::conditional<SC::kQ8, Tile8wTallQ, Tile8wTall>::type;
-    using TS = typename std::conditional<SC::kQ8, Tile8wQ, Tile8w>::type;
-    using TN = typename std::conditional<SC::kQ8, TileNarrowQ, TileNarrow>::type;
+    using TT = typename TileSet<SC::kFmt>::Tall;
+    using TS = typename TileSet<SC::kFmt>::S;
+    using TN = typename TileSet<SC::kFmt>::Nar;
     EpiResidual<TR, TO, SC::kQ8> epi{(const TR *)resid, gate, bias, (TO *)out, N, gate_fn, sc.a, sc.w};
     if (N % 256 == 0 && prefer_tall(M, N)) return run<TT>(a, w, M, N, K, RowsIdentity{256}, epi, s, sc.a, sc.w);
     if (N % 256 == 0) return run<TS>(a, w, M, N, K, RowsIdentity{256}, epi, s, sc.a, sc.w);
@@ -784,18 +850,28 @@ template <class SC>
 static hipError_t residual_any(const void *a, const void *w, int64_t M, int N, int K, const void *resid,
                                int resid_f32, const float *gate, int gate_fn, const float *bias, void *out,
                                int out_f32, SC sc, hipStream_t s) {
-    if (resid_f32) {
-        return out_f32 ? residual_typed<float, float>(a, w, M, N, K, resid, gate, gate_fn, bias, out, sc, s)
-                       : residual_typed<float, bf16>(a, w, M, N, K, resid, gate, gate_fn, bias, out, sc, s);
+    if constexpr (SC::kFmt == 2) {   // fp32 path: fp32 residual stream only
+        if (!out_f32 || (resid && !resid_f32)) return hipErrorInvalidValue;
+        return residual_typed<float, float>(a, w, M, N, K, resid, gate, gate_fn, bias, out, sc, s);
+    } else {
+        if (resid_f32) {
+            return out_f32 ? residual_typed<float, float>(a, w, M, N, K, resid, gate, gate_fn, bias, out, sc, s)
+                           : residual_typed<float, bf16>(a, w, M, N, K, resid, gate, gate_fn, bias, out, sc, s);
+        }
+        return out_f32 ? residual_typed<bf16, float>(a, w, M, N, K, resid, gate, gate_fn, bias, out, sc, s)
+                       : residual_typed<bf16, bf16>(a, w, M, N, K, resid, gate, gate_fn, bias, out, sc, s);
     }
-    return out_f32 ? residual_typed<bf16, float>(a, w, M, N, K, resid, gate, gate_fn, bias, out, sc, s)
-                   : residual_typed<bf16, bf16>(a, w, M, N, K, resid, gate, gate_fn, bias, out, sc, s);
 }
 
 hipError_t launch_gemm_residual(const bf16 *a, const bf16 *w, int64_t M, int N, int K, const void *resid,
                                 int resid_f32, const float *gate, int gate_fn, const float *bias, void *out,
                                 int out_f32, hipStream_t s) {
     return residual_any(a, w, M, N, K, resid, resid_f32, gate, gate_fn, bias, out, out_f32, NoScales{}, s);
+}
+
+hipError_t launch_gemm_residual_f32(const float *a, const float *w, int64_t M, int N, int K, const float *resid,
+                                    const float *gate, int gate_fn, const float *bias, float *out, hipStream_t s) {
+    return residual_any(a, w, M, N, K, resid, 1, gate, gate_fn, bias, out, 1, F32Ops{}, s);
 }
 
 hipError_t launch_gemm_residual_q8(const int8_t *a, const float *a_scale, const int8_t *w, const float *w_scale,
@@ -805,19 +881,24 @@ hipError_t launch_gemm_residual_q8(const int8_t *a, const float *a_scale, const 
                         Scales{a_scale, w_scale}, s);
 }
 
-template <class SC>
-static hipError_t swiglu_any(const void *a, const void *w, int64_t M, int F, int K, int act, bf16 *u, SC sc,
+template <class SC, typename TU>
+static hipError_t swiglu_any(const void *a, const void *w, int64_t M, int F, int K, int act, TU *u, SC sc,
                              hipStream_t s) {
     // (a 128-row tail launch measured no faster here: 718 vs 713 us at 4170 rows)
-    using T = typename std::conditional<SC::kQ8, Tile8wQ, Tile8w>::type;
+    using T = typename TileSet<SC::kFmt>::S;
     const RowsSwiglu rm{T::BN, T::kWaveN, F};
-    if (act == 1) return run<T>(a, w, M, 2 * F, K, rm, EpiSwiglu<1>{u, F}, s, sc.a, sc.w);
-    return run<T>(a, w, M, 2 * F, K, rm, EpiSwiglu<0>{u, F}, s, sc.a, sc.w);
+    if (act == 1) return run<T>(a, w, M, 2 * F, K, rm, EpiSwiglu<1, TU>{u, F}, s, sc.a, sc.w);
+    return run<T>(a, w, M, 2 * F, K, rm, EpiSwiglu<0, TU>{u, F}, s, sc.a, sc.w);
 }
 
 hipError_t launch_gemm_swiglu(const bf16 *a, const bf16 *w, int64_t M, int F, int K, int act, bf16 *u,
                               hipStream_t s) {
     return swiglu_any(a, w, M, F, K, act, u, NoScales{}, s);
+}
+
+hipError_t launch_gemm_swiglu_f32(const float *a, const float *w, int64_t M, int F, int K, int act, float *u,
+                                  hipStream_t s) {
+    return swiglu_any(a, w, M, F, K, act, u, F32Ops{}, s);
 }
 
 hipError_t launch_gemm_swiglu_q8(const int8_t *a, const float *a_scale, const int8_t *w, const float *w_scale,
@@ -828,10 +909,11 @@ hipError_t launch_gemm_swiglu_q8(const int8_t *a, const float *a_scale, const in
 template <class SC>
 static hipError_t qkv_any(const void *h, const void *w, int64_t M, int N, int K, const QkvEpiArgs &e, SC sc,
                           hipStream_t s) {
-    using T = typename std::conditional<SC::kQ8, Tile8wQ, Tile8w>::type;
-    using TH = typename std::conditional<SC::kQ8, Tile8wHalfQ, Tile8wHalf>::type;
+    using T = typename TileSet<SC::kFmt>::S;
+    using TH = typename TileSet<SC::kFmt>::Half;
+    using TQ = typename std::conditional<SC::kFmt == 2, float, bf16>::type;
 #define DIT_QKV(HD_, RMS_, RF_) \
-    run_tail_split<T, TH>(h, w, M, N, K, RowsIdentity{T::BN}, EpiQkv<HD_, RMS_, RF_>{e}, s, sc.a, sc.w)
+    run_tail_split<T, TH>(h, w, M, N, K, RowsIdentity{T::BN}, EpiQkv<HD_, RMS_, RF_, TQ>{e}, s, sc.a, sc.w)
     if (e.head_dim == 128) {
         if (e.rms) return e.rope_first ? DIT_QKV(128, true, true) : DIT_QKV(128, true, false);
         return e.rope_first ? DIT_QKV(128, false, true) : DIT_QKV(128, false, false);
@@ -844,6 +926,11 @@ static hipError_t qkv_any(const void *h, const void *w, int64_t M, int N, int K,
 hipError_t launch_gemm_qkv(const bf16 *h, const bf16 *w, int64_t M, int N, int K, const QkvEpiArgs &e,
                            hipStream_t s) {
     return qkv_any(h, w, M, N, K, e, NoScales{}, s);
+}
+
+hipError_t launch_gemm_qkv_f32(const float *h, const float *w, int64_t M, int N, int K, const QkvEpiArgs &e,
+                               hipStream_t s) {
+    return qkv_any(h, w, M, N, K, e, F32Ops{}, s);
 }
 
 hipError_t launch_gemm_qkv_q8(const int8_t *h, const float *h_scale, const int8_t *w, const float *w_scale,

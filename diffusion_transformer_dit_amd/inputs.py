@@ -13,8 +13,8 @@ Workload shapes follow the pages' models:
   * Krea-2-Turbo (zml-flow-rs page, §III): a 6144-wide GQA DiT, SwiGLU 16384.
   * the resident pre-norm ViT backbone (makepad commit log): LayerNorm,
     rotate-half RoPE from precomputed tables, SwiGLU, residuals in place.
-Weights and biases are N(0, 0.02) rounded to bf16 (round-to-nearest-even),
-activations N(0, 1); every tensor has its own PCG64 stream keyed by
+Weights and biases are N(0, 0.02) rounded to bf16 (round-to-nearest-even;
+kept fp32 in the fp32 format), activations N(0, 1); every tensor has its own PCG64 stream keyed by
 (config id, block index, tensor id) under one root seed.
 """
 from __future__ import annotations
@@ -65,8 +65,9 @@ class DiTConfig:
     gate: str = "identity"           # gate function: "identity" | "tanh" | "sigmoid"
     mod: str = "shift_scale_gate"    # AdaLN chunks: "shift_scale_gate" (6D) | "scale_gate" (4D, no shift)
     qk_order: str = "norm_rope"      # "norm_rope" | "rope_norm"
-    # format of the four block projections: "bf16", or "w8a8_h256" (int8 codes
-    # of both operands after a 256-point Hadamard rotation, one scale per row)
+    # format of the four block projections: "bf16", "w8a8_h256" (int8 codes
+    # of both operands after a 256-point Hadamard rotation, one scale per row),
+    # or "f32" (the fp32 run: every weight fp32, not rounded to bf16, and x fp32)
     fmt: str = "bf16"
 
     @property
@@ -91,6 +92,10 @@ class DiTConfig:
     @property
     def qkv_dim(self) -> int:
         return (self.heads + 2 * self.kv_heads) * self.head_dim
+
+    @property
+    def bf16_weights(self) -> bool:
+        return self.fmt != "f32"
 
     def replace(self, **kw) -> "DiTConfig":
         return dataclasses.replace(self, **kw)
@@ -118,9 +123,11 @@ C1_JOINT_TF = C1_JOINT.replace(name="tiny_joint_text_first", text_first=True)
 C1_W8A8 = C1.replace(name="tiny_block_w8a8", fmt="w8a8_h256")
 C3_W8A8 = C3.replace(name="block_8b_w8a8", fmt="w8a8_h256")
 C4_W8A8 = C4.replace(name="stack_8b_w8a8", fmt="w8a8_h256")
+# the fp32 run of the tiny block (same seeds; weights not rounded to bf16)
+C1_F32 = C1.replace(name="tiny_block_f32", fmt="f32", x_dtype="f32")
 
 CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5_4096, C5_1024, C3_JOINT, C1_JOINT, C1_JOINT_TF,
-                               C1_W8A8, C3_W8A8, C4_W8A8)}
+                               C1_W8A8, C3_W8A8, C4_W8A8, C1_F32)}
 
 STACK_STEPS = 8
 STACK_SHIFT = 4.0
@@ -188,8 +195,8 @@ def block_weights(cfg: DiTConfig, block: int = 0, affine_random: bool = False,
     w: Dict[str, Optional[np.ndarray]] = {}
     if Dc > 0:
         if draw_ada:
-            w["w_ada"] = _normal(cid, block, "w_ada", (cfg.ada_rows, Dc), 0.02)
-            w["b_ada"] = _normal(cid, block, "b_ada", (cfg.ada_rows,), 0.02)
+            w["w_ada"] = _normal(cid, block, "w_ada", (cfg.ada_rows, Dc), 0.02, cfg.bf16_weights)
+            w["b_ada"] = _normal(cid, block, "b_ada", (cfg.ada_rows,), 0.02, cfg.bf16_weights)
         else:
             w["w_ada"] = w["b_ada"] = None
         if zero_ada and draw_ada:
@@ -205,10 +212,11 @@ def block_weights(cfg: DiTConfig, block: int = 0, affine_random: bool = False,
             else:
                 w[n + "_g"] = np.ones(D, np.float32)
                 w[n + "_b"] = np.zeros(D, np.float32)
-    w["w_qkv"] = _normal(cid, block, "w_qkv", (cfg.qkv_dim, D), 0.02)
-    w["w_o"] = _normal(cid, block, "w_o", (D, cfg.heads * hd), 0.02)
-    w["w_gate_up"] = _normal(cid, block, "w_gate_up", (2 * F, D), 0.02)
-    w["w_down"] = _normal(cid, block, "w_down", (D, F), 0.02)
+    bw = cfg.bf16_weights
+    w["w_qkv"] = _normal(cid, block, "w_qkv", (cfg.qkv_dim, D), 0.02, bw)
+    w["w_o"] = _normal(cid, block, "w_o", (D, cfg.heads * hd), 0.02, bw)
+    w["w_gate_up"] = _normal(cid, block, "w_gate_up", (2 * F, D), 0.02, bw)
+    w["w_down"] = _normal(cid, block, "w_down", (D, F), 0.02, bw)
     if cfg.qk_norm:
         if affine_random:
             for n in ("q", "k"):
@@ -237,14 +245,14 @@ def cond(cfg: DiTConfig) -> Optional[np.ndarray]:
 
 def stack_edges(cfg: DiTConfig) -> Dict[str, np.ndarray]:
     """Patch-embed, final modulation and output projection of the stack."""
-    D, C, Dc, cid = cfg.hidden, cfg.latent_dim, cfg.cond_dim, cfg.cfg_id
+    D, C, Dc, cid, bw = cfg.hidden, cfg.latent_dim, cfg.cond_dim, cfg.cfg_id, cfg.bf16_weights
     return {
-        "w_in": _normal(cid, 1000, "w_in", (D, C), 0.02),
-        "b_in": _normal(cid, 1000, "b_in", (D,), 0.02),
-        "w_fmod": _normal(cid, 1000, "w_fmod", (2 * D, Dc), 0.02),   # rows: scale then shift
-        "b_fmod": _normal(cid, 1000, "b_fmod", (2 * D,), 0.02),
-        "w_out": _normal(cid, 1000, "w_out", (C, D), 0.02),
-        "b_out": _normal(cid, 1000, "b_out", (C,), 0.02),
+        "w_in": _normal(cid, 1000, "w_in", (D, C), 0.02, bw),
+        "b_in": _normal(cid, 1000, "b_in", (D,), 0.02, bw),
+        "w_fmod": _normal(cid, 1000, "w_fmod", (2 * D, Dc), 0.02, bw),   # rows: scale then shift
+        "b_fmod": _normal(cid, 1000, "b_fmod", (2 * D,), 0.02, bw),
+        "w_out": _normal(cid, 1000, "w_out", (C, D), 0.02, bw),
+        "b_out": _normal(cid, 1000, "b_out", (C,), 0.02, bw),
     }
 
 
@@ -262,8 +270,8 @@ def stack_block_weights(cfg: DiTConfig, block: int, shared_ada: Dict[str, np.nda
 
 def shared_ada(cfg: DiTConfig) -> Dict[str, np.ndarray]:
     D, Dc, cid = cfg.hidden, cfg.cond_dim, cfg.cfg_id
-    return {"w_ada": _normal(cid, 999, "w_ada", (cfg.ada_rows, Dc), 0.02),
-            "b_ada": _normal(cid, 999, "b_ada", (cfg.ada_rows,), 0.02)}
+    return {"w_ada": _normal(cid, 999, "w_ada", (cfg.ada_rows, Dc), 0.02, cfg.bf16_weights),
+            "b_ada": _normal(cid, 999, "b_ada", (cfg.ada_rows,), 0.02, cfg.bf16_weights)}
 
 
 # ---------------------------------------------------------------------------

@@ -46,6 +46,7 @@ def desc_of(cfg: I.DiTConfig, x_dtype: Optional[str] = None) -> N.dit_block_desc
                        qk_norm=cfg.qk_norm,
                        rope=N.DIT_ROPE_INTERLEAVED if cfg.rope == "interleaved3d" else N.DIT_ROPE_HALF,
                        eps=cfg.eps, x_dtype=N.DIT_F32 if xd == "f32" else N.DIT_BF16,
+                       w_dtype=N.DIT_F32 if cfg.fmt == "f32" else N.DIT_BF16,
                        norm=N.DIT_RMSNORM if cfg.norm == "rmsnorm" else N.DIT_LAYERNORM,
                        act=N.DIT_ACT_GELU_TANH if cfg.act == "gelu_tanh" else N.DIT_ACT_SILU,
                        gate={"identity": N.DIT_GATE_IDENTITY, "tanh": N.DIT_GATE_TANH,
@@ -68,15 +69,16 @@ _BF16_KEYS = ("w_ada", "w_qkv", "w_o", "w_gate_up", "w_down")
 
 
 class DeviceBlock:
-    """One block's parameters resident in HBM plus the matching C struct."""
+    """One block's parameters resident in HBM plus the matching C struct
+    (matrices bf16, or fp32 with f32=True for the fp32 path)."""
 
-    def __init__(self, w: Dict[str, Optional[np.ndarray]], device="cuda", tensors=None):
+    def __init__(self, w: Dict[str, Optional[np.ndarray]], device="cuda", tensors=None, f32: bool = False):
         if tensors is None:
             tensors = {}
             for k, v in w.items():
                 if v is None:
                     tensors[k] = None
-                elif k in _BF16_KEYS:
+                elif k in _BF16_KEYS and not f32:
                     tensors[k] = to_dev_bf16(v, device)
                 else:
                     tensors[k] = to_dev_f32(v, device)
@@ -140,8 +142,9 @@ class DeviceStack:
         N.dit_stack_step(self.model, latent, cond, cos, sin, velocity, self.ws, stream)
 
 
-def upload_edges(e: Dict[str, np.ndarray], device="cuda"):
-    return {k: (to_dev_bf16(v, device) if k.startswith("w_") else to_dev_f32(v, device)) for k, v in e.items()}
+def upload_edges(e: Dict[str, np.ndarray], device="cuda", f32: bool = False):
+    return {k: (to_dev_bf16(v, device) if k.startswith("w_") and not f32 else to_dev_f32(v, device))
+            for k, v in e.items()}
 
 
 def denoise(stack: DeviceStack, latent, cos, sin, steps: int, shift: float, start: int = 0, stream=None):

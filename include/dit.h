@@ -97,7 +97,13 @@ typedef enum { DIT_FMT_BF16 = 0, DIT_FMT_W8A8_H256 = 1 } dit_fmt;
  *     optional gamma/beta are applied after either.
  *   eps: epsilon of every norm of the block.
  *   x_dtype: dtype of x and out (residual arithmetic is fp32 either way).
- *   w_dtype: must be DIT_BF16.
+ *   w_dtype: DIT_BF16, or DIT_F32 for the fp32 path (the fp32 run of the
+ *     tiny-block workload): every weight matrix fp32 (w_ada, w_qkv, w_o,
+ *     w_gate_up, w_down and, in a stack, w_in, w_fmod, w_out), x_dtype must be
+ *     DIT_F32 and fmt 0; every intermediate (h, q, k, vt, the attention
+ *     output, u) is then fp32, the GEMMs run on fp32 MFMA and attention on the
+ *     vector ALUs, with the same fused epilogues.  DIT_ERR_UNSUPPORTED for
+ *     DIT_F32 with a bf16 x or the W8A8 format.
  *   act, gate, mod, qk_order: the semantics switches above; 0 everywhere is
  *     SwiGLU, identity gate, six chunks, norm before RoPE.
  *   fmt: dit_fmt of the four projections (0 = bf16).
@@ -308,7 +314,8 @@ int dit_ln_modulate(const void *x, int32_t x_dtype, int64_t rows, int32_t dim, i
                     void *h, void *stream);
 
 /* QKV GEMM with the qk-LayerNorm and RoPE epilogue.
- * h device bf16 [batch*seq, hidden]; outputs (device bf16):
+ * h device bf16 [batch*seq, hidden]; outputs (device bf16; with
+ * desc->w_dtype == DIT_F32, h, w_qkv and the outputs are fp32):
  *   q  [batch, heads, seq, head_dim]
  *   k  [batch, kv_heads, seq, head_dim]
  *   vt [batch, kv_heads, head_dim, seq_pad], seq_pad = dit_seq_pad(seq):
@@ -324,7 +331,9 @@ int32_t dit_seq_pad(int32_t seq);
 /* Mask-free flash attention: out[b*seq + s, h*hd + d] =
  * sum_j softmax_j(q[b,h,s,:] . k[b,g,j,:] / sqrt(hd)) v[b,g,j,d], g = h/(H/Hkv)
  * ([ERNIE] §VII Decision 2 and §IX "Flash SDPA").  q, k, vt in the layouts of
- * dit_qkv_rope; out device bf16 [batch*seq, heads*head_dim]. */
+ * dit_qkv_rope; out device bf16 [batch*seq, heads*head_dim] (all fp32 with
+ * desc->w_dtype == DIT_F32).  The padded key positions of vt must hold
+ * zeros (dit_qkv_rope writes them). */
 int dit_flash_attention(const dit_block_desc *desc, const void *q, const void *k,
                         const void *vt, void *out, void *stream);
 
@@ -336,7 +345,9 @@ int dit_flash_attention(const dit_block_desc *desc, const void *q, const void *k
  * joint 4096 + 74 token layout ([ERNIE] "Token Layout").  nsplit in [1, 64]
  * (chunks hold at least one key tile; nsplit 1, or seq a multiple of 256,
  * is dit_flash_attention).  ws: device workspace of at least
- * dit_attention_workspace_size(desc, nsplit) bytes (may be NULL when that is 0). */
+ * dit_attention_workspace_size(desc, nsplit) bytes (may be NULL when that is 0).
+ * The fp32 path (desc->w_dtype == DIT_F32) has no split form:
+ * DIT_ERR_UNSUPPORTED. */
 int dit_attention_workspace_size(const dit_block_desc *desc, int32_t nsplit, size_t *bytes);
 int dit_flash_attention_split(const dit_block_desc *desc, const void *q, const void *k, const void *vt,
                               void *out, int32_t nsplit, void *ws, size_t ws_bytes, void *stream);

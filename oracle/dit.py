@@ -29,8 +29,10 @@ rope_axes, rope_theta, eps, and optionally the semantics switches the pages
 disagree on (defaults in brackets): norm ["layernorm"] | "rmsnorm"; act
 ["silu"] | "gelu_tanh"; gate ["identity"] | "tanh" | "sigmoid"; mod
 ["shift_scale_gate"] | "scale_gate"; qk_order ["norm_rope"] | "rope_norm";
-fmt ["bf16"] | "w8a8_h256" (the four block projections in int8 with a
-256-point Hadamard rotation on both operands, per-row scales).
+fmt ["bf16"] | "f32" | "w8a8_h256" (the four block projections in int8 with a
+256-point Hadamard rotation on both operands, per-row scales; "bf16" and
+"f32" differ only in the weight values the caller passes, the arithmetic here
+is the same float64 x W^T).
 
 Parity status: every function here is pinned by a closed form, an invariant,
 a special case or a brute-force loop in tests/test_oracle.py, except the

@@ -71,7 +71,9 @@ def test_desc_accepts_every_semantics_switch():
     (dict(gate=-1), N.DIT_ERR_INVALID_ARG),
     (dict(mod=2), N.DIT_ERR_INVALID_ARG),
     (dict(qk_order=2), N.DIT_ERR_INVALID_ARG),
-    (dict(w_dtype=N.DIT_F32), N.DIT_ERR_UNSUPPORTED),
+    (dict(w_dtype=N.DIT_F32), N.DIT_ERR_UNSUPPORTED),                      # fp32 weights need x fp32
+    (dict(w_dtype=N.DIT_F32, x_dtype=N.DIT_F32, fmt=N.DIT_FMT_W8A8_H256), N.DIT_ERR_UNSUPPORTED),
+    (dict(w_dtype=2), N.DIT_ERR_INVALID_ARG),
     (dict(fmt=2), N.DIT_ERR_INVALID_ARG),
     (dict(fmt=N.DIT_FMT_W8A8_H256, ffn=640), N.DIT_ERR_UNSUPPORTED),     # W8A8: ffn % 256
     (dict(fmt=N.DIT_FMT_W8A8_H256, ffn=9216), N.DIT_ERR_UNSUPPORTED),    # no rotation kernel for 9 rounds
@@ -320,3 +322,20 @@ def test_attention_split_validation():
         assert e.value.status == st, (nsplit, e.value)
     # a ragged sequence grows the block workspace by the partials of up to 16 chunks
     assert N.dit_block_workspace_size(_desc(seq=300)) > N.dit_block_workspace_size(_desc(seq=256))
+
+
+def test_f32_path_desc_and_workspace():
+    """fp32 weights select the fp32 path: fp32 intermediates, no split-KV partials."""
+    d16 = _desc(x_dtype=N.DIT_F32)
+    d32 = _desc(x_dtype=N.DIT_F32, w_dtype=N.DIT_F32)
+    n16, n32 = N.dit_block_workspace_size(d16), N.dit_block_workspace_size(d32)
+    N_, D, F = 256, 256, 768
+    # h, q, k, vt, att, x1 fp32 + u fp32 + modulation
+    assert n32 >= N_ * D * 4 * 6 + N_ * F * 4 + 6 * D * 4
+    assert n32 > n16
+    # a ragged fp32 sequence needs no split partials
+    r32 = N.dit_block_workspace_size(_desc(x_dtype=N.DIT_F32, w_dtype=N.DIT_F32, seq=300))
+    assert r32 - n32 < 300 * 4 * (5 * D + F) - 256 * 4 * (5 * D + F) + 64 * D * 4 + 8 * 256
+    with pytest.raises(N.DitError) as e:
+        N.dit_flash_attention_split(d32, FAKE, FAKE, FAKE, FAKE + (1 << 24), 4, FAKE, stream=0, ws_bytes=1 << 30)
+    assert e.value.status == N.DIT_ERR_UNSUPPORTED
