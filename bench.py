@@ -27,6 +27,7 @@ from diffusion_transformer_dit_amd import inputs as I  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 MFMA
+PEAK_FP32_TFLOPS = 157.3       # MI355X dense fp32 MFMA (and fp32 vector)
 METRIC = "s/denoise-step (36x4096 DiT, 4096 tok) + bf16 MFMA util % of peak"
 
 
@@ -190,8 +191,64 @@ def time_block(cfg, blk, reps=10):
     if cfg.fmt == "w8a8_h256":       # int8 projections (attention stays bf16): against the int8 peak
         return {"tokens": cfg.seq, "us": round(us, 1), "achieved": round(tf, 1), "unit": "TOP/s",
                 "frac": round(tf / PEAK_INT8_TOPS, 4)}
+    if cfg.fmt == "f32":             # the fp32 path: against the fp32 peak
+        return {"tokens": cfg.seq, "us": round(us, 1), "achieved": round(tf, 2), "unit": "TFLOP/s",
+                "frac": round(tf / PEAK_FP32_TFLOPS, 4)}
     return {"tokens": cfg.seq, "us": round(us, 1), "achieved": round(tf, 1), "unit": "TFLOP/s",
             "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
+def time_chain(cfgs, depth, reps=3):
+    """`depth` blocks of the shapes of cfgs[0] run back to back through
+    dit_block_forward with x updated in place (distinct GEMM weights per block,
+    N(0, 0.02) bf16 drawn on the device; one AdaLN linear shared by the blocks
+    but applied by each), for every config in cfgs (same weights, other token
+    counts).  HIP events on torch's current stream; ms per pass of the chain
+    and the algorithmic TFLOP/s against the bf16 peak."""
+    import torch
+    from diffusion_transformer_dit_amd import native as N
+    from diffusion_transformer_dit_amd import runtime as R
+    cfg = cfgs[0]
+    D, F, Dc, hd = cfg.hidden, cfg.ffn, cfg.cond_dim, cfg.head_dim
+    nb = lambda shape, blk, name: I.torch_normal_bf16(shape, 0.02, I.torch_seed(cfg.cfg_id, blk, name), "cuda")
+    shared = {}
+    if Dc > 0:
+        shared = {"w_ada": nb((cfg.ada_rows, Dc), 999, "w_ada"), "b_ada": nb((cfg.ada_rows,), 999, "b_ada").float()}
+    one = lambda n: torch.ones(n, dtype=torch.float32, device="cuda")
+    zero = lambda n: torch.zeros(n, dtype=torch.float32, device="cuda")
+    blocks = []
+    for l in range(depth):
+        t = dict(shared)
+        t.update({"w_qkv": nb((cfg.qkv_dim, D), l, "w_qkv"), "w_o": nb((D, cfg.heads * hd), l, "w_o"),
+                  "w_gate_up": nb((2 * F, D), l, "w_gate_up"), "w_down": nb((D, F), l, "w_down")})
+        if cfg.qk_norm:
+            t.update({"q_g": one(hd), "q_b": zero(hd), "k_g": one(hd), "k_b": zero(hd)})
+        if Dc == 0:
+            t.update({"ln1_g": one(D), "ln1_b": zero(D), "ln2_g": one(D), "ln2_b": zero(D)})
+        blocks.append(R.DeviceBlock(None, tensors=t))
+    out = {}
+    for c in cfgs:
+        g = torch.Generator(device="cuda").manual_seed(17)
+        x = torch.randn((c.tokens, D), generator=g, device="cuda")
+        if c.x_dtype == "bf16":
+            x = x.to(torch.bfloat16)
+        cond = torch.randn((Dc,), generator=g, device="cuda") if Dc > 0 else None
+        cos, sin = R.rope_tables(c)
+        desc = R.desc_of(c)
+        ws = R.alloc_ws(N.dit_block_workspace_size(desc))
+
+        def run():
+            for b in blocks:
+                N.dit_block_forward(desc, b.c, x, cond, cos, sin, x, ws)
+
+        us = _event_us(run, reps)
+        assert torch.isfinite(x).all().item(), f"non-finite output ({c.name})"
+        tf = depth * sum(block_flops(c).values()) / (us * 1e-6) / 1e12
+        out[f"{c.name}_x{depth}"] = {"tokens": c.tokens, "blocks": depth, "ms": round(us / 1000.0, 3),
+                                     "achieved": round(tf, 1), "unit": "TFLOP/s",
+                                     "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    del blocks
+    return out
 
 
 def time_kernels_w8a8(cfg, qblk, reps=20):
@@ -465,6 +522,26 @@ def main():
     print(f"[bench] w8a8: {json.dumps({k: v for k, v in w8a8.items() if k != 'kernels'})}", file=sys.stderr,
           flush=True)
     del stack8, qblocks
+
+    # The fp32 path (fp32 weights and intermediates, fp32 MFMA GEMMs, vector-ALU
+    # attention): the tiny block of the workload list and one 8B block.
+    print("[bench] fp32 path blocks", file=sys.stderr, flush=True)
+    c1f = I.C1_F32
+    tiny32 = R.DeviceBlock(I.block_weights(c1f, 0), f32=True)
+    b0 = stack.blocks[0].t
+    blk32 = R.DeviceBlock(None, tensors={k: (None if v is None else v.float()) for k, v in b0.items()})
+    f32 = {"tiny_256": time_block(c1f, tiny32, reps=50),
+           "latent_4096": time_block(I.C3.replace(x_dtype="f32", fmt="f32"), blk32, reps=5)}
+    print(f"[bench] f32: {json.dumps(f32)}", file=sys.stderr, flush=True)
+    del blk32, tiny32
+
+    # the other workloads of the list at their timing depths: the pre-norm ViT
+    # backbone (batch 4 x 1024 tokens, 24 blocks, fp32 x in place) and the wide
+    # GQA block stacked 28 deep at 4096 and 1024 tokens
+    print("[bench] ViT backbone and wide GQA chains", file=sys.stderr, flush=True)
+    others = time_chain([I.C2], I.C2.layers)
+    others.update(time_chain([I.C5_4096, I.C5_1024], I.C5_4096.layers))
+    print(f"[bench] other configs: {json.dumps(others)}", file=sys.stderr, flush=True)
     canary_after = canary_tflops()
 
     flops = step_flops(cfg)
@@ -504,6 +581,10 @@ def main():
         "cpu_baseline": cpu,
         # the four projections in int8 with the Hadamard-256 rotation (reduced precision: context, not value)
         "w8a8_h256": w8a8,
+        # dit_block_forward on the fp32 path (fp32 run of the tiny block; an 8B block in fp32)
+        "f32_path_block": f32,
+        # the ViT backbone forward (24 blocks) and the wide GQA block 28 deep, bf16 weights
+        "other_configs": others,
     }
     print(json.dumps(line), flush=True)
 

@@ -739,40 +739,71 @@ struct EpiQkv {
 // waits overlap the other's MFMAs.
 using Tile8w = Tile<256, 256, 2, 4>;
 using Tile8wTall = Tile<320, 256, 2, 4>;   // 160 x 64 per wave: ragged row counts just above a multiple of 256
-using TileNarrow = Tile<256, 128, 2, 2>;   // N = 128 outputs (the projection to latent channels)
+using TileNarrow = Tile<256, 128, 2, 2>;   // 4 waves of 128 x 64: 128-column outputs, few-tile shapes
+// 128-row tiles (8 waves of 64 x 64): ragged row tails, few-tile shapes
+using Tile8wHalf = Tile<128, 256, 2, 4>;
+using TileQuarter = Tile<128, 128, 2, 2>;  // 4 waves of 64 x 64: shapes with few 256 x 256 tiles
 // the same tiles over int8 operands (128 int8 per 128-byte row)
 using Tile8wQ = Tile<256, 256, 2, 4, 128, 2, 1>;
 using Tile8wTallQ = Tile<320, 256, 2, 4, 128, 2, 1>;
 using TileNarrowQ = Tile<256, 128, 2, 2, 128, 2, 1>;
-// 128-row tails of the 256 x 256 tiles (8 waves of 64 x 64)
-using Tile8wHalf = Tile<128, 256, 2, 4>;
 using Tile8wHalfQ = Tile<128, 256, 2, 4, 128, 2, 1>;
+using TileQuarterQ = Tile<128, 128, 2, 2, 128, 2, 1>;
 
 // The tile family of an operand format: 0 bf16, 1 int8 (W8A8), 2 fp32 (the
 // fp32 parity path: 32 floats of K per 128-byte LDS row, fp32 MFMA)
 template <int FMT> struct TileSet;
 template <> struct TileSet<0> {
     using S = Tile8w; using Tall = Tile8wTall; using Nar = TileNarrow; using Half = Tile8wHalf;
+    using Quar = TileQuarter;
 };
 template <> struct TileSet<1> {
     using S = Tile8wQ; using Tall = Tile8wTallQ; using Nar = TileNarrowQ; using Half = Tile8wHalfQ;
+    using Quar = TileQuarterQ;
 };
 template <> struct TileSet<2> {
     using S = Tile<256, 256, 2, 4, 32, 2, 4>; using Tall = Tile<320, 256, 2, 4, 32, 2, 4>;
     using Nar = Tile<256, 128, 2, 2, 32, 2, 4>; using Half = Tile<128, 256, 2, 4, 32, 2, 4>;
+    using Quar = Tile<128, 128, 2, 2, 32, 2, 4>;
 };
 
+// Tile choice for an M x N output.  Every tile of a launch costs about the
+// same, so the time is the number of rounds of workgroups over the CUs times
+// the cost of one tile: its area over its throughput relative to the 256 x 256
+// tile, measured at shapes that fill the chip (320 x 256: 1.0, 128 x 256:
+// 0.75, 256 x 128: 0.79, 128 x 128: 0.81; bf16, N(0, 1) x N(0, 0.02)).  E.g.
+// 4170 x 4096 takes the 320-row tile (224 tiles in one round instead of 272 in
+// two), 4096 x 1024 the 128 x 128 tile (256 tiles instead of 64), 1024 x 8192
+// the 128 x 256 tile; the 256 x 256 tile wins ties.
+enum TileKind { kTileS, kTileTall, kTileHalf, kTileNar, kTileQuar };
+struct TileCand {
+    TileKind kind;
+    int bm, bn;
+    double rate;
+};
+constexpr TileCand kTileCands[] = {{kTileS, 256, 256, 1.0},    {kTileTall, 320, 256, 1.0},
+                                   {kTileHalf, 128, 256, 0.75}, {kTileNar, 256, 128, 0.79},
+                                   {kTileQuar, 128, 128, 0.81}};
 
-// Tile height for an M x N output of 256-wide column tiles: the 320-row tile
-// when it needs fewer rounds of workgroups over the CUs than the 256-row one
-// costs extra time per tile (e.g. 4170 rows x 4096 columns: 224 tiles in one
-// round instead of 272 in two).
-static bool prefer_tall(int64_t M, int N) {
-    const int64_t cus = device_cu_count(), tn = N / 256;
-    const int64_t r256 = ((M + 255) / 256 * tn + cus - 1) / cus;
-    const int64_t r320 = ((M + 319) / 320 * tn + cus - 1) / cus;
-    return r320 * 320 < r256 * 256;
+// mask: bit k allows TileKind k
+static TileKind choose_tile(int64_t M, int N, unsigned mask) {
+    const int64_t cus = device_cu_count();
+    TileKind best = kTileS;
+    double best_cost = 0.0;
+    bool have = false;
+    for (const TileCand &c : kTileCands) {
+        if (!(mask >> c.kind & 1u) || N % c.bn) continue;
+        const int64_t tiles = (M + c.bm - 1) / c.bm * (N / c.bn);
+        const double cost = (double)((tiles + cus - 1) / cus) * c.bm * c.bn / c.rate;
+        if (!have || cost < best_cost) {
+            best = c.kind;
+            best_cost = cost;
+            have = true;
+        }
+    }
+    return best;
 }
+constexpr unsigned kAllTiles = 0x1f;
 
 // int8 operands carry their row scales (Scales), bf16 (NoScales) and fp32
 // (F32Ops) operands none
@@ -826,6 +857,9 @@ static hipError_t run_tail_split(const void *a, const void *w, int64_t M, int N_
                                  Epi epi, hipStream_t s, const float *a_scale = nullptr,
                                  const float *w_scale = nullptr) {
     static_assert(T::BM == 256 && TH::BM == 128 && T::BN == TH::BN, "full and tail tiles");
+    // few row tiles (e.g. 1024 x 8192): every row in 128-row tiles
+    if (choose_tile(M, N_tile_cols, 1u << kTileS | 1u << kTileHalf) == kTileHalf)
+        return run<TH>(a, w, M, N_tile_cols, K, rm, epi, s, a_scale, w_scale);
     if (!split_tail_rows(M, N_tile_cols)) return run<T>(a, w, M, N_tile_cols, K, rm, epi, s, a_scale, w_scale);
     const int64_t m_full = M / 256 * 256;
     hipError_t e = run<T>(a, w, m_full, N_tile_cols, K, rm, epi, s, a_scale, w_scale);
@@ -837,13 +871,15 @@ template <typename TR, typename TO, class SC>
 static hipError_t residual_typed(const void *a, const void *w, int64_t M, int N, int K, const void *resid,
                                  const float *gate, int gate_fn, const float *bias, void *out, SC sc,
                                  hipStream_t s) {
-    using TT = typename TileSet<SC::kFmt>::Tall;
-    using TS = typename TileSet<SC::kFmt>::S;
-    using TN = typename TileSet<SC::kFmt>::Nar;
+    using TSet = TileSet<SC::kFmt>;
     EpiResidual<TR, TO, SC::kQ8> epi{(const TR *)resid, gate, bias, (TO *)out, N, gate_fn, sc.a, sc.w};
-    if (N % 256 == 0 && prefer_tall(M, N)) return run<TT>(a, w, M, N, K, RowsIdentity{256}, epi, s, sc.a, sc.w);
-    if (N % 256 == 0) return run<TS>(a, w, M, N, K, RowsIdentity{256}, epi, s, sc.a, sc.w);
-    return run<TN>(a, w, M, N, K, RowsIdentity{128}, epi, s, sc.a, sc.w);
+    switch (choose_tile(M, N, kAllTiles)) {
+        case kTileTall: return run<typename TSet::Tall>(a, w, M, N, K, RowsIdentity{256}, epi, s, sc.a, sc.w);
+        case kTileHalf: return run<typename TSet::Half>(a, w, M, N, K, RowsIdentity{256}, epi, s, sc.a, sc.w);
+        case kTileNar: return run<typename TSet::Nar>(a, w, M, N, K, RowsIdentity{128}, epi, s, sc.a, sc.w);
+        case kTileQuar: return run<typename TSet::Quar>(a, w, M, N, K, RowsIdentity{128}, epi, s, sc.a, sc.w);
+        default: return run<typename TSet::S>(a, w, M, N, K, RowsIdentity{256}, epi, s, sc.a, sc.w);
+    }
 }
 
 template <class SC>
@@ -885,10 +921,21 @@ template <class SC, typename TU>
 static hipError_t swiglu_any(const void *a, const void *w, int64_t M, int F, int K, int act, TU *u, SC sc,
                              hipStream_t s) {
     // (a 128-row tail launch measured no faster here: 718 vs 713 us at 4170 rows)
-    using T = typename TileSet<SC::kFmt>::S;
-    const RowsSwiglu rm{T::BN, T::kWaveN, F};
-    if (act == 1) return run<T>(a, w, M, 2 * F, K, rm, EpiSwiglu<1, TU>{u, F}, s, sc.a, sc.w);
-    return run<T>(a, w, M, 2 * F, K, rm, EpiSwiglu<0, TU>{u, F}, s, sc.a, sc.w);
+    using TSet = TileSet<SC::kFmt>;
+    auto go = [&](auto tile, auto epi) {
+        using T = decltype(tile);
+        return run<T>(a, w, M, 2 * F, K, RowsSwiglu{T::BN, T::kWaveN, F}, epi, s, sc.a, sc.w);
+    };
+    auto with_act = [&](auto tile) {
+        return act == 1 ? go(tile, EpiSwiglu<1, TU>{u, F}) : go(tile, EpiSwiglu<0, TU>{u, F});
+    };
+    switch (choose_tile(M, 2 * F, kAllTiles)) {
+        case kTileTall: return with_act(typename TSet::Tall{});
+        case kTileHalf: return with_act(typename TSet::Half{});
+        case kTileNar: return with_act(typename TSet::Nar{});
+        case kTileQuar: return with_act(typename TSet::Quar{});
+        default: return with_act(typename TSet::S{});
+    }
 }
 
 hipError_t launch_gemm_swiglu(const bf16 *a, const bf16 *w, int64_t M, int F, int K, int act, bf16 *u,
