@@ -192,20 +192,25 @@ void flash_attn_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K, c
     floatx16 sa[2];             // scores of the tile being exponentiated
     DIT_ATT_QK(t0 % NS, sa);
     DIT_ATT_MASK(t0 * BKV, sa);
-    // running max of the raw (unscaled) scores of this lane's query; scale > 0
-    // commutes with max
-    float mraw;
+    // Reference max of the raw (unscaled) scores of this lane's query (scale > 0
+    // commutes with max): the exponentials, O and l are taken against it.  It
+    // starts at the first tile's max and moves up only when some lane of the
+    // wave sees a score more than kLazy (log2 units) above its reference, so
+    // exponentials stay <= 2^kLazy (exact in fp32 and bf16 range) while the
+    // rescale of O, which a max that creeps up would otherwise trigger on most
+    // tiles, becomes rare; O / l is the same softmax for any reference.
+    constexpr float kLazy = 8.0f;
+    float mref;
     {
         float mx = sa[0][0];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sa[ks][e]);
-        mraw = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mref = fmaxf(mx, __shfl_xor(mx, 32, 64));
     }
-    float alpha = 1.f;          // factor taking O and l from the previous max to mraw
+    float alpha = 1.f;          // factor taking O and l from the previous reference to mref
     float lsum = 0.f;           // this lane's partial row sum (the other 16 keys live in lane ^ 32)
-    float mref = mraw;          // the max the last exponentials were taken against (O and l refer to it)
 
     // one key tile; MASKED = 0 for the steady state (tile t + 1 holds 64 valid
     // keys), 1 for the last two tiles
@@ -224,17 +229,18 @@ _Pragma("unroll")                                                               
                                                                                                               \
         /* QK^T of tile t + 1 || exponentials of tile t */                                                    \
         DIT_ATT_QK(((T) + 1) % NS, SN);                                                                       \
-        const float neg = -mraw * scale_log2;                                                                 \
-        mref = mraw;                                                                                          \
+        const float neg = -mref * scale_log2;                                                                 \
         bf16x8 pf[4];                                                                                         \
+        float ps[4];                          /* four partial sums: no 32-long dependent add chain */        \
 _Pragma("unroll")                                                                                             \
         for (int ks = 0; ks < 2; ++ks)                                                                        \
 _Pragma("unroll")                                                                                             \
             for (int e = 0; e < 16; ++e) {                                                                    \
                 const float p = __builtin_amdgcn_exp2f(fmaf(SC[ks][e], scale_log2, neg));                     \
-                lsum += p;                                                                                    \
+                if (ks == 0 && e < 4) ps[e] = p; else ps[e & 3] += p;                                         \
                 pf[ks * 2 + (e >> 3)][e & 7] = f2bf(p);                                                       \
             }                                                                                                 \
+        lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);                                                            \
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                                    \
 _Pragma("unroll")                                                                                             \
         for (int i = 0; i < 2 * KK - 2; ++i) {                                                                \
@@ -264,9 +270,12 @@ _Pragma("unroll")                                                               
 _Pragma("unroll")                                                                                             \
                 for (int e = 0; e < 16; ++e) mx = fmaxf(mx, SN[ks][e]);                                       \
             mx = fmaxf(mx, __shfl_xor(mx, 32, 64));                                                           \
-            const float mnew = fmaxf(mraw, mx);                                                               \
-            alpha = __builtin_amdgcn_exp2f((mraw - mnew) * scale_log2);                                       \
-            mraw = mnew;                                                                                      \
+            alpha = 1.f;                                                                                      \
+            if (__any((mx - mref) * scale_log2 > kLazy)) {                                                    \
+                const float mnew = fmaxf(mref, mx);                                                           \
+                alpha = __builtin_amdgcn_exp2f((mref - mnew) * scale_log2);                                   \
+                mref = mnew;                                                                                  \
+            }                                                                                                 \
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                                \
 _Pragma("unroll")                                                                                             \
             for (int i = 0; i < 4 * DS - 2; ++i) {                                                            \

@@ -111,8 +111,11 @@ def test_block_in_place_and_deterministic():
 
 def test_block_joint_text_first_is_a_row_permutation():
     """On the GPU too, moving the text rows (with their positions) to the front
-    permutes the output rows (up to rounding: the row tiles differ)."""
-    cfg, cft = I.C1_JOINT, I.C1_JOINT_TF
+    permutes the output rows, up to rounding: the attention sees the keys in
+    another order and the row tiles differ.  fp32 x and out, so that the
+    comparison is not swamped by two independent bf16 roundings of out (at
+    |delta| << |x| one bf16 rounding of out alone moves delta by ~1 %)."""
+    cfg, cft = I.C1_JOINT.replace(x_dtype="f32"), I.C1_JOINT_TF.replace(x_dtype="f32")
     w = I.block_weights(cfg, 0)
     x, c = I.block_x(cfg), I.cond(cfg)
     perm = np.r_[np.arange(cfg.spatial, cfg.seq), np.arange(cfg.spatial)]
@@ -120,7 +123,7 @@ def test_block_joint_text_first_is_a_row_permutation():
     b = _run_block(cft, w, x[perm], c, I.positions(cft))
     m = metrics(b - x[perm], a[perm] - x[perm])
     say(f"  text-first vs permuted spatial-first: {m}")
-    assert m["cos"] > 0.9999
+    assert m["cos"] > 0.99999
 
 
 def test_block_rope_position_offset_invariance():
