@@ -35,7 +35,7 @@ struct Tile {
     static constexpr int kWaves = WM * WN;
     static constexpr int kThreads = kWaves * kWave;
     static constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
-    static constexpr int TM = kWaveM / 32, TN = kWaveN / 32;
+    static constexpr int TM = kWaveM / 16, TN = kWaveN / 16;    // 16 x 16 MFMA blocks per wave
     static constexpr int kRowBytes = BK * ES;                   // one tile row (BK elements) in LDS
     static constexpr int kChunks = kRowBytes / 16;              // 16-byte chunks per row
     static constexpr int kRowsPerLine = 256 / kRowBytes;        // rows sharing one 64-bank line
@@ -45,8 +45,13 @@ struct Tile {
     static constexpr int kLoads = kALoads + kBLoads;
     static constexpr int kStageBytes = (BM + BN) * kRowBytes;
     static_assert(BM % (kRowsPerLoad * kWaves) == 0 && BN % (kRowsPerLoad * kWaves) == 0, "tile vs loads");
-    static_assert(kWaveM % 32 == 0 && kWaveN % 32 == 0 && kRowBytes % 64 == 0, "wave tile");
+    static_assert(kWaveM % 16 == 0 && kWaveN % 16 == 0 && kRowBytes % 128 == 0, "wave tile");
     static_assert((NS - 2) * kLoads <= 63, "vmcnt range");
+    // Two waves per SIMD leave 256 registers per wave: when the accumulators
+    // and double-buffered A and B fragments would not fit (the 320-row tile),
+    // the A fragments are single-buffered, each reloaded right after the MFMAs
+    // of its row block.
+    static constexpr bool kSingleA = kWaves > 4 && TM * TN * 4 + 2 * (TM + TN) * 4 > 224;
     // Chunk c of tile row r lives at slot c ^ swz(r).  gfx950 LDS has 64 banks
     // (256 B per cycle) and a ds_read_b128 serves 16 lanes per cycle; the
     // fragment reads of those 16 lanes are 16 consecutive rows at one logical
@@ -93,26 +98,32 @@ struct RowsSwiglu {
     }
 };
 
-// one 32x32 MFMA block, k = 32 bytes of each operand row (16 bf16 or 32 int8).
-// The int8 form keeps its int32 accumulators in the same float registers (bit
-// patterns; 0.0f is int 0), so the dequantization below converts them in place.
-__device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+// one 16x16 MFMA block, k = 64 bytes of each operand row (32 bf16 or 64 int8):
+// lane l feeds row l % 16 with the 16 bytes of chunk l / 16 and receives
+// output rows 4 (l / 16) .. + 3 of column l % 16.  The int8 form keeps its
+// int32 accumulators in the same float registers (bit patterns; 0.0f is int
+// 0), so the dequantization below converts them in place.  16 x 16 blocks
+// rather than 32 x 32 ones: with the same bytes of LDS fragments per MFMA cycle
+// the 8-wave main loop runs 6-7 % faster (4096 x 24576 x 4096: 681 -> 638 us).
+__device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ floatx16 mfma32(intx4 a, intx4 b, floatx16 c) {
-    return __builtin_bit_cast(floatx16,
-                              __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, __builtin_bit_cast(intx16, c), 0, 0, 0));
+__device__ __forceinline__ floatx4 mfma16(intx4 a, intx4 b, floatx4 c) {
+    return __builtin_bit_cast(floatx4,
+                              __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, __builtin_bit_cast(intx4, c), 0, 0, 0));
 }
 // fp32 operands (the fp32 parity path): a 16-byte fragment holds 4 k values per
-// lane, consumed by four v_mfma_f32_32x32x2_f32 (value u of both operands: the
-// same k in A and B, so every k of the 32-byte step is summed once)
-__device__ __forceinline__ floatx16 mfma32(floatx4 a, floatx4 b, floatx16 c) {
+// lane, consumed by four v_mfma_f32_16x16x4_f32 (value u of both operands: the
+// same k in A and B, so every k of the 64-byte step is summed once)
+__device__ __forceinline__ floatx4 mfma16(floatx4 a, floatx4 b, floatx4 c) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[u], b[u], c, 0, 0, 0);
+    for (int u = 0; u < 4; ++u) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u], b[u], c, 0, 0, 0);
     return c;
 }
 
-__device__ __forceinline__ int acc_row(int i, int e, int lhalf);
+// Accumulator element (i, j, r) of a wave sits at wave-tile row i*16 +
+// (lane/16)*4 + r and wave-tile column j*16 + lane%16.
+__device__ __forceinline__ int acc_row(int i, int r, int lq) { return i * 16 + (lq << 2) + r; }
 
 // a_scale [M] / w_scale [w_rows]: the int8 operands' row scales (ES == 1 only)
 template <class T, class RowMap, class Epi>
@@ -134,7 +145,7 @@ void gemm_kernel(const void *__restrict__ A, const void *__restrict__ W, int M, 
     // are then computed on the scalar unit
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / T::WN, wn = wave % T::WN;
-    const int lrow = lane & 31, lhalf = lane >> 5;
+    const int l16 = lane & 15, lq = lane >> 4;
 
     // Global -> LDS without registers: buffer_load_dwordx4 ... lds moves 64 x 16
     // bytes of one wave into a contiguous 1 KiB of LDS (lane l at +16 l).  Load
@@ -169,39 +180,38 @@ void gemm_kernel(const void *__restrict__ A, const void *__restrict__ W, int M, 
             kb_, 0, 0);                                                                                  \
     } while (0)
 
-    floatx16 acc[T::TM][T::TN];
+    floatx4 acc[T::TM][T::TN];
 #pragma unroll
     for (int i = 0; i < T::TM; ++i)
 #pragma unroll
-        for (int j = 0; j < T::TN; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+        for (int j = 0; j < T::TN; ++j) acc[i][j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
     // NS-stage ring: stage s holds K tile kt with kt % NS == s.  Tiles past the
     // end re-load the last tile (never read) so that every iteration issues the
     // same number of loads and the vmcnt bookkeeping stays uniform.
     const int KT = K / T::BK;
-    constexpr int KS = T::kRowBytes / 32;   // MFMA k-steps per stage (even: k-step 0 always uses buffer 0)
+    constexpr int KS = T::kRowBytes / 64;   // MFMA k-steps per stage (even: k-step 0 always uses buffer 0)
     static_assert(KS % 2 == 0, "fragment double buffer");
 #pragma unroll
     for (int s0 = 0; s0 < T::NS; ++s0) DIT_ISSUE(s0, min(s0, KT - 1) * T::BK);
 
+    if constexpr (!T::kSingleA) {
     Frag af[2][T::TM], bfr[2][T::TN];
     // fragment reads in the order the MFMAs consume them: A0, B0 .. B(TN-1), A1 .. A(TM-1)
 #define DIT_LOAD_FRAGS(buf, sa_, sb_, kk)                                                           \
     do {                                                                                          \
-        const int c_ = (kk) * 2 + lhalf;                                                          \
-        af[buf][0] = *(const Frag *)((sa_) + T::off(wm * T::kWaveM + lrow, c_));                  \
+        const int c_ = (kk) * 4 + lq;                                                             \
+        af[buf][0] = *(const Frag *)((sa_) + T::off(wm * T::kWaveM + l16, c_));                   \
         _Pragma("unroll") for (int j = 0; j < T::TN; ++j)                                        \
-            bfr[buf][j] = *(const Frag *)((sb_) + T::off(wn * T::kWaveN + j * 32 + lrow, c_));    \
+            bfr[buf][j] = *(const Frag *)((sb_) + T::off(wn * T::kWaveN + j * 16 + l16, c_));     \
         _Pragma("unroll") for (int i = 1; i < T::TM; ++i)                                        \
-            af[buf][i] = *(const Frag *)((sa_) + T::off(wm * T::kWaveM + i * 32 + lrow, c_));     \
+            af[buf][i] = *(const Frag *)((sa_) + T::off(wm * T::kWaveM + i * 16 + l16, c_));      \
     } while (0)
 #define DIT_MFMAS(buf)                                                                             \
     do {                                                                                          \
         _Pragma("unroll") for (int i = 0; i < T::TM; ++i)                                        \
             _Pragma("unroll") for (int j = 0; j < T::TN; ++j)                                    \
-                acc[i][j] = mfma32(af[buf][i], bfr[buf][j], acc[i][j]);                                \
+                acc[i][j] = mfma16(af[buf][i], bfr[buf][j], acc[i][j]);                                \
     } while (0)
 
     wait_vmcnt<(T::NS - 1) * T::kLoads>();   // tile 0 landed
@@ -258,6 +268,68 @@ void gemm_kernel(const void *__restrict__ A, const void *__restrict__ W, int M, 
     }
 #undef DIT_MFMAS
 #undef DIT_LOAD_FRAGS
+    } else {
+    // single-buffered A: B fragments of the next k-step first, then per row
+    // block i its TN MFMAs followed by the reload of A fragment i
+    Frag af[T::TM], bfr[2][T::TN];
+#define DIT_LOAD_B(buf, sb_, kk)                                                                     \
+    do {                                                                                          \
+        const int c_ = (kk) * 4 + lq;                                                             \
+        _Pragma("unroll") for (int j = 0; j < T::TN; ++j)                                        \
+            bfr[buf][j] = *(const Frag *)((sb_) + T::off(wn * T::kWaveN + j * 16 + l16, c_));     \
+    } while (0)
+#define DIT_STEP_RELOAD(buf, sa_, kk)                                                              \
+    do {                                                                                          \
+        const int c_ = (kk) * 4 + lq;                                                             \
+        _Pragma("unroll") for (int i = 0; i < T::TM; ++i) {                                      \
+            _Pragma("unroll") for (int j = 0; j < T::TN; ++j)                                    \
+                acc[i][j] = mfma16(af[i], bfr[buf][j], acc[i][j]);                                 \
+            af[i] = *(const Frag *)((sa_) + T::off(wm * T::kWaveM + i * 16 + l16, c_));           \
+        }                                                                                         \
+    } while (0)
+#define DIT_SCHED_ROWS()                                                                           \
+    do {                                                                                          \
+        __builtin_amdgcn_sched_group_barrier(0x100, T::TN, 0);               /* DS read: B */     \
+        _Pragma("unroll") for (int r = 0; r < T::TM; ++r) {                                      \
+            __builtin_amdgcn_sched_group_barrier(0x008, T::TN, 0);           /* MFMA */           \
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);               /* DS read: A */     \
+        }                                                                                         \
+    } while (0)
+
+    wait_vmcnt<(T::NS - 1) * T::kLoads>();   // tile 0 landed
+    barrier_only();
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i) af[i] = *(const Frag *)(smem + T::off(wm * T::kWaveM + i * 16 + l16, lq));
+    DIT_LOAD_B(0, smem + T::BM * T::kRowBytes, 0);
+
+    for (int kt = 0; kt < KT; ++kt) {
+        const uint8_t *sa = smem + (kt % T::NS) * T::kStageBytes;
+        const uint8_t *sb = sa + T::BM * T::kRowBytes;
+#pragma unroll
+        for (int kk = 0; kk < KS - 1; ++kk) {
+            DIT_LOAD_B((kk + 1) & 1, sb, kk + 1);
+            DIT_STEP_RELOAD(kk & 1, sa, kk + 1);
+        }
+#pragma unroll
+        for (int kk = 0; kk < KS - 1; ++kk) DIT_SCHED_ROWS();
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<(T::NS - 2) * T::kLoads, 0>();
+        barrier_only();
+        {
+            // the last k-step reloads from the next stage; every LDS read of it
+            // precedes the LDS-writing tile loads, which go out at the end
+            const uint8_t *na = smem + ((kt + 1) % T::NS) * T::kStageBytes;
+            DIT_LOAD_B(0, na + T::BM * T::kRowBytes, 0);
+            DIT_STEP_RELOAD((KS - 1) & 1, na, 0);
+        }
+        DIT_SCHED_ROWS();
+        __builtin_amdgcn_sched_barrier(0);
+        DIT_ISSUE(kt % T::NS, min(kt + T::NS, KT - 1) * T::BK);
+    }
+#undef DIT_LOAD_B
+#undef DIT_STEP_RELOAD
+#undef DIT_SCHED_ROWS
+    }
 #undef DIT_ISSUE
     wait_vmcnt<0>();      // retire the trailing (never read) loads before LDS is reused
     __syncthreads();
@@ -271,18 +343,18 @@ void gemm_kernel(const void *__restrict__ A, const void *__restrict__ W, int M, 
         const int row0 = m0 + wm * T::kWaveM;
         float sw[T::TN];
 #pragma unroll
-        for (int j = 0; j < T::TN; ++j) sw[j] = w_scale[rowmap(tn, wn * T::kWaveN + j * 32 + lrow)];
+        for (int j = 0; j < T::TN; ++j) sw[j] = w_scale[rowmap(tn, wn * T::kWaveN + j * 16 + l16)];
 #pragma unroll
         for (int i = 0; i < T::TM; ++i) {
-            float sa[16];
+            float sa[4];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) sa[e] = a_scale[min(row0 + acc_row(i, e, lhalf), M - 1)];
+            for (int e = 0; e < 4; ++e) sa[e] = a_scale[min(row0 + acc_row(i, e, lq), M - 1)];
 #pragma unroll
             for (int j = 0; j < T::TN; ++j) {
                 // whole-vector bit cast: clang mis-lowers a bit cast of one vector element
-                const intx16 iv = __builtin_bit_cast(intx16, acc[i][j]);
+                const intx4 iv = __builtin_bit_cast(intx4, acc[i][j]);
 #pragma unroll
-                for (int e = 0; e < 16; ++e) acc[i][j][e] = (float)iv[e] * (sa[e] * sw[j]);
+                for (int e = 0; e < 4; ++e) acc[i][j][e] = (float)iv[e] * (sa[e] * sw[j]);
             }
             // compiler fence (a_scale is not restrict-qualified): the row scales of
             // later blocks are not hoisted next to all 128 accumulators
@@ -293,9 +365,6 @@ void gemm_kernel(const void *__restrict__ A, const void *__restrict__ W, int M, 
 #endif
 }
 
-// Accumulator element (i, j, e) of a wave sits at wave-tile row
-// i*32 + (e/4)*8 + (lane/32)*4 + e%4 and wave-tile column j*32 + lane%32.
-__device__ __forceinline__ int acc_row(int i, int e, int lhalf) { return i * 32 + ((e >> 2) << 3) + (lhalf << 2) + (e & 3); }
 
 // ---------------------------------------------------------------------------
 // epilogue: out = resid + gate * acc + bias
@@ -315,68 +384,82 @@ struct EpiResidual {
     static constexpr bool kDequant = Q8;
     template <class T> static constexpr int lds_bytes() { return 0; }
     template <class T>
-    __device__ __forceinline__ void apply(floatx16 (&acc)[T::TM][T::TN], int row0, int tn, int wn, int lane, int M,
+    __device__ __forceinline__ void apply(floatx4 (&acc)[T::TM][T::TN], int row0, int tn, int wn, int lane, int M,
                                           uint8_t *) const {
-        const int lrow = lane & 31, lhalf = lane >> 5;
+        const int l16 = lane & 15, lq = lane >> 4;
         const int col0 = tn * T::BN + wn * T::kWaveN;
         float g[T::TN], bb[T::TN];
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) {
-            const int col = col0 + j * 32 + lrow;
+            const int col = col0 + j * 16 + l16;
             g[j] = gate ? gate_f(gate[col], gate_fn) : 1.0f;
             if constexpr (Q8) g[j] *= w_scale[col];
             bb[j] = bias ? bias[col] : 0.0f;
         }
         // out may alias resid (in-place update), but every element is read and
-        // written by this lane only, so a batch of residual loads may precede the
-        // batch of stores; without the batching the compiler has to wait for each
-        // store before the next load.  Rows past M load row M - 1 and store nothing.
+        // written by this lane only, so a batch of residual loads (IB row blocks,
+        // 32 elements per lane) may precede the batch of stores; without the
+        // batching the compiler has to wait for each store before the next load.
+        // Rows past M load row M - 1 and store nothing.
+        constexpr int IB = (32 / (T::TN * 4)) > 0 ? 32 / (T::TN * 4) : 1;
+        static_assert(T::TM % IB == 0, "row blocks per batch");
 #pragma unroll
-        for (int i = 0; i < T::TM; ++i) {
-            float r[T::TN][16];
+        for (int i0 = 0; i0 < T::TM; i0 += IB) {
+            float r[IB][T::TN][4];
             if (resid) {
 #pragma unroll
-                for (int j = 0; j < T::TN; ++j)
+                for (int ib = 0; ib < IB; ++ib)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int row = min(row0 + acc_row(i, e, lhalf), M - 1);
-                        r[j][e] = to_f32<TR>(resid[(size_t)row * N + col0 + j * 32 + lrow]);
-                    }
+                    for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int row = min(row0 + acc_row(i0 + ib, e, lq), M - 1);
+                            r[ib][j][e] = to_f32<TR>(resid[(size_t)row * N + col0 + j * 16 + l16]);
+                        }
             } else {
 #pragma unroll
-                for (int j = 0; j < T::TN; ++j)
+                for (int ib = 0; ib < IB; ++ib)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) r[j][e] = 0.0f;
+                    for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) r[ib][j][e] = 0.0f;
             }
             if constexpr (Q8) {
-                float sa[16];
 #pragma unroll
-                for (int e = 0; e < 16; ++e) sa[e] = a_scale[min(row0 + acc_row(i, e, lhalf), M - 1)];
+                for (int ib = 0; ib < IB; ++ib) {
+                    float sa[4];
 #pragma unroll
-                for (int j = 0; j < T::TN; ++j) {
-                    const intx16 iv = __builtin_bit_cast(intx16, acc[i][j]);   // whole-vector cast (see kernel)
+                    for (int e = 0; e < 4; ++e) sa[e] = a_scale[min(row0 + acc_row(i0 + ib, e, lq), M - 1)];
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) acc[i][j][e] = (float)iv[e] * sa[e];
+                    for (int j = 0; j < T::TN; ++j) {
+                        const intx4 iv = __builtin_bit_cast(intx4, acc[i0 + ib][j]);   // whole-vector cast (see kernel)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[i0 + ib][j][e] = (float)iv[e] * sa[e];
+                    }
                 }
             }
-            // wave-uniform: all 32 rows of block i in range -> straight-line stores
-            if (row0 + i * 32 + 32 <= M) {
+            // wave-uniform: all rows of the batch in range -> straight-line stores
+            if (row0 + (i0 + IB) * 16 <= M) {
 #pragma unroll
-                for (int j = 0; j < T::TN; ++j)
+                for (int ib = 0; ib < IB; ++ib)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        out[(size_t)(row0 + acc_row(i, e, lhalf)) * N + col0 + j * 32 + lrow] =
-                            from_f32<TO>(fmaf(acc[i][j][e], g[j], bb[j]) + r[j][e]);
+                    for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            out[(size_t)(row0 + acc_row(i0 + ib, e, lq)) * N + col0 + j * 16 + l16] =
+                                from_f32<TO>(fmaf(acc[i0 + ib][j][e], g[j], bb[j]) + r[ib][j][e]);
             } else {
 #pragma unroll
-                for (int j = 0; j < T::TN; ++j)
+                for (int ib = 0; ib < IB; ++ib)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int row = row0 + acc_row(i, e, lhalf);
-                        if (row < M)
-                            out[(size_t)row * N + col0 + j * 32 + lrow] =
-                                from_f32<TO>(fmaf(acc[i][j][e], g[j], bb[j]) + r[j][e]);
-                    }
+                    for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int row = row0 + acc_row(i0 + ib, e, lq);
+                            if (row < M)
+                                out[(size_t)row * N + col0 + j * 16 + l16] =
+                                    from_f32<TO>(fmaf(acc[i0 + ib][j][e], g[j], bb[j]) + r[ib][j][e]);
+                        }
             }
         }
     }
@@ -392,19 +475,19 @@ struct EpiSwiglu {
     int F;
     template <class T> static constexpr int lds_bytes() { return 0; }
     template <class T>
-    __device__ __forceinline__ void apply(floatx16 (&acc)[T::TM][T::TN], int row0, int tn, int wn, int lane, int M,
+    __device__ __forceinline__ void apply(floatx4 (&acc)[T::TM][T::TN], int row0, int tn, int wn, int lane, int M,
                                           uint8_t *) const {
-        const int lrow = lane & 31, lhalf = lane >> 5;
+        const int l16 = lane & 15, lq = lane >> 4;
         constexpr int HJ = T::TN / 2;
         const int f0 = tn * (T::BN / 2) + wn * (T::kWaveN / 2);
 #pragma unroll
         for (int j = 0; j < HJ; ++j) {
-            const int f = f0 + j * 32 + lrow;
+            const int f = f0 + j * 16 + l16;
 #pragma unroll
             for (int i = 0; i < T::TM; ++i)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int row = row0 + acc_row(i, e, lhalf);
+                for (int e = 0; e < 4; ++e) {
+                    const int row = row0 + acc_row(i, e, lq);
                     if (row < M) {
                         const float g = ACT == 1 ? gelu_tanh_f(acc[i][j][e]) : silu_f(acc[i][j][e]);
                         u[(size_t)row * F + f] = from_f32<TU>(g * acc[i][j + HJ][e]);
@@ -459,13 +542,13 @@ struct EpiQkv {
     static __device__ __forceinline__ int v_slot(int d, int c) { return d * 128 + ((c ^ ((d >> 1) & 7)) << 4); }
 
     template <class T>
-    __device__ __forceinline__ void apply(floatx16 (&acc)[T::TM][T::TN], int row0, int tn, int wn, int lane, int M,
+    __device__ __forceinline__ void apply(floatx4 (&acc)[T::TM][T::TN], int row0, int tn, int wn, int lane, int M,
                                           uint8_t *smem) const {
         static_assert(T::BN == 256 && T::WM == 2 && T::WN == 4 && (T::kWaveM == 128 || T::kWaveM == 64) &&
                           T::kWaveN == 64,
                       "staging assumes the 8-wave 256x256 tile or its 128-row tail variant");
         static_assert(2 * 64 * kQkvStride * 4 / 2 >= (256 / HD) * kHeadBlock, "output block fits the staging area");
-        const int lrow = lane & 31, lhalf = lane >> 5;
+        const int l16 = lane & 15, lq = lane >> 4;
         const int wave = threadIdx.x >> 6;
         const int cl = wave >> 2;                          // cluster = wm: rows cl*128 .. +128 of the tile
         const int lc = (wave & 3) * 64 + lane;             // lane within the cluster, 0..255
@@ -500,13 +583,12 @@ struct EpiQkv {
             // the K loop, or the previous sub-pass's copy-out, is done with the LDS
             if (sp > 0) { wait_vmcnt<63, 0>(); barrier_only(); }
 #pragma unroll
-            for (int ii = 0; ii < 2; ++ii)
+            for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
                 for (int j = 0; j < T::TN; ++j)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        red[(ii * 32 + ((r >> 2) << 3) + (lhalf << 2) + (r & 3)) * kQkvStride + wn * 64 + j * 32 +
-                            lrow] = acc[sp * 2 + ii][j][r];
+                    for (int r = 0; r < 4; ++r)
+                        red[acc_row(ii, r, lq) * kQkvStride + wn * 64 + j * 16 + l16] = acc[sp * 4 + ii][j][r];
             const int rbase = row0 + sp * 64;             // token of staged row 0
             const int trow = min(rbase + rl, M - 1);
             const int sp_ = trow - (trow / S) * S;
