@@ -853,7 +853,7 @@ template <> struct TileSet<2> {
 // same, so the time is the number of rounds of workgroups over the CUs times
 // the cost of one tile: its area over its throughput relative to the 256 x 256
 // tile, measured at shapes that fill the chip (320 x 256: 1.0, 128 x 256:
-// 0.75, 256 x 128: 0.79, 128 x 128: 0.81; bf16, N(0, 1) x N(0, 0.02)).  E.g.
+// 0.69, 256 x 128: 0.69, 128 x 128: 0.775; bf16, N(0, 1) x N(0, 0.02)).  E.g.
 // 4170 x 4096 takes the 320-row tile (224 tiles in one round instead of 272 in
 // two), 4096 x 1024 the 128 x 128 tile (256 tiles instead of 64), 1024 x 8192
 // the 128 x 256 tile; the 256 x 256 tile wins ties.
@@ -864,8 +864,8 @@ struct TileCand {
     double rate;
 };
 constexpr TileCand kTileCands[] = {{kTileS, 256, 256, 1.0},    {kTileTall, 320, 256, 1.0},
-                                   {kTileHalf, 128, 256, 0.75}, {kTileNar, 256, 128, 0.79},
-                                   {kTileQuar, 128, 128, 0.81}};
+                                   {kTileHalf, 128, 256, 0.69}, {kTileNar, 256, 128, 0.69},
+                                   {kTileQuar, 128, 128, 0.775}};
 
 // mask: bit k allows TileKind k
 static TileKind choose_tile(int64_t M, int N, unsigned mask) {
