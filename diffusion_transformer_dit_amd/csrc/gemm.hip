@@ -821,10 +821,19 @@ struct EpiQkv {
 // waits overlap the other's MFMAs.
 using Tile8w = Tile<256, 256, 2, 4>;
 using Tile8wTall = Tile<320, 256, 2, 4>;   // 160 x 64 per wave: ragged row counts just above a multiple of 256
-using TileNarrow = Tile<256, 128, 2, 2>;   // 4 waves of 128 x 64: 128-column outputs, few-tile shapes
 // 128-row tiles (8 waves of 64 x 64): ragged row tails, few-tile shapes
 using Tile8wHalf = Tile<128, 256, 2, 4>;
-using TileQuarter = Tile<128, 128, 2, 2>;  // 4 waves of 64 x 64: shapes with few 256 x 256 tiles
+// Narrow and quarter tiles for shapes with few 256 x 256 tiles, also 8 waves:
+// 256 x 128 as 128 x 32 per wave over 3 LDS stages (144 KiB); 128 x 128 as
+// 32 x 64 per wave, over 2 stages (64 KiB: two workgroups fit on a CU, which
+// pays when the launch has more tiles than CUs) or over 3 stages (96 KiB: one
+// workgroup per CU, so a launch of at most one tile per CU spreads over all of
+// them instead of doubling up on some).
+using Tile8wNarrow = Tile<256, 128, 2, 4, 64, 3>;
+using Tile8wQuarter = Tile<128, 128, 4, 2>;
+using Tile8wQuarter3 = Tile<128, 128, 4, 2, 64, 3>;
+// the int8 and fp32 families keep 4-wave narrow and quarter tiles
+using TileNarrow = Tile<256, 128, 2, 2>;
 // the same tiles over int8 operands (128 int8 per 128-byte row)
 using Tile8wQ = Tile<256, 256, 2, 4, 128, 2, 1>;
 using Tile8wTallQ = Tile<320, 256, 2, 4, 128, 2, 1>;
@@ -835,28 +844,31 @@ using TileQuarterQ = Tile<128, 128, 2, 2, 128, 2, 1>;
 // The tile family of an operand format: 0 bf16, 1 int8 (W8A8), 2 fp32 (the
 // fp32 parity path: 32 floats of K per 128-byte LDS row, fp32 MFMA)
 template <int FMT> struct TileSet;
+// Quar1: the quarter tile for launches of at most one tile per CU.
 template <> struct TileSet<0> {
-    using S = Tile8w; using Tall = Tile8wTall; using Nar = TileNarrow; using Half = Tile8wHalf;
-    using Quar = TileQuarter;
+    using S = Tile8w; using Tall = Tile8wTall; using Nar = Tile8wNarrow; using Half = Tile8wHalf;
+    using Quar = Tile8wQuarter; using Quar1 = Tile8wQuarter3;
 };
 template <> struct TileSet<1> {
     using S = Tile8wQ; using Tall = Tile8wTallQ; using Nar = TileNarrowQ; using Half = Tile8wHalfQ;
-    using Quar = TileQuarterQ;
+    using Quar = TileQuarterQ; using Quar1 = TileQuarterQ;
 };
 template <> struct TileSet<2> {
     using S = Tile<256, 256, 2, 4, 32, 2, 4>; using Tall = Tile<320, 256, 2, 4, 32, 2, 4>;
     using Nar = Tile<256, 128, 2, 2, 32, 2, 4>; using Half = Tile<128, 256, 2, 4, 32, 2, 4>;
-    using Quar = Tile<128, 128, 2, 2, 32, 2, 4>;
+    using Quar = Tile<128, 128, 2, 2, 32, 2, 4>; using Quar1 = Quar;
 };
 
 // Tile choice for an M x N output.  Every tile of a launch costs about the
 // same, so the time is the number of rounds of workgroups over the CUs times
 // the cost of one tile: its area over its throughput relative to the 256 x 256
 // tile, measured at shapes that fill the chip (320 x 256: 1.0, 128 x 256:
-// 0.69, 256 x 128: 0.69, 128 x 128: 0.775; bf16, N(0, 1) x N(0, 0.02)).  E.g.
+// 0.69, 256 x 128: 0.86 for the 8-wave 3-stage bf16 tile and 0.69 for the
+// 4-wave int8 / fp32 ones, 128 x 128: 0.775; N(0, 1) x N(0, 0.02)).  E.g.
 // 4170 x 4096 takes the 320-row tile (224 tiles in one round instead of 272 in
-// two), 4096 x 1024 the 128 x 128 tile (256 tiles instead of 64), 1024 x 8192
-// the 128 x 256 tile; the 256 x 256 tile wins ties.
+// two), 4096 x 1024 the 128 x 128 tile (256 tiles instead of 64), 1024 x 6144
+// the 256 x 128 tile (192 tiles in one round), 1024 x 8192 QKV the 128 x 256
+// tile; the 256 x 256 tile wins ties.
 enum TileKind { kTileS, kTileTall, kTileHalf, kTileNar, kTileQuar };
 struct TileCand {
     TileKind kind;
@@ -867,16 +879,17 @@ constexpr TileCand kTileCands[] = {{kTileS, 256, 256, 1.0},    {kTileTall, 320, 
                                    {kTileHalf, 128, 256, 0.69}, {kTileNar, 256, 128, 0.69},
                                    {kTileQuar, 128, 128, 0.775}};
 
-// mask: bit k allows TileKind k
-static TileKind choose_tile(int64_t M, int N, unsigned mask) {
+// mask: bit k allows TileKind k; fmt: the operand format (TileSet index)
+static TileKind choose_tile(int64_t M, int N, unsigned mask, int fmt = 0) {
     const int64_t cus = device_cu_count();
     TileKind best = kTileS;
     double best_cost = 0.0;
     bool have = false;
     for (const TileCand &c : kTileCands) {
         if (!(mask >> c.kind & 1u) || N % c.bn) continue;
+        const double rate = c.kind == kTileNar && fmt == 0 ? 0.86 : c.rate;
         const int64_t tiles = (M + c.bm - 1) / c.bm * (N / c.bn);
-        const double cost = (double)((tiles + cus - 1) / cus) * c.bm * c.bn / c.rate;
+        const double cost = (double)((tiles + cus - 1) / cus) * c.bm * c.bn / rate;
         if (!have || cost < best_cost) {
             best = c.kind;
             best_cost = cost;
@@ -886,6 +899,12 @@ static TileKind choose_tile(int64_t M, int N, unsigned mask) {
     return best;
 }
 constexpr unsigned kAllTiles = 0x1f;
+
+// at most one 128 x 128 tile per CU: the quarter tile variant that keeps one
+// workgroup per CU
+static bool quarter_one_round(int64_t M, int N) {
+    return (M + 127) / 128 * (N / 128) <= (int64_t)device_cu_count();
+}
 
 // int8 operands carry their row scales (Scales), bf16 (NoScales) and fp32
 // (F32Ops) operands none
@@ -955,11 +974,14 @@ static hipError_t residual_typed(const void *a, const void *w, int64_t M, int N,
                                  hipStream_t s) {
     using TSet = TileSet<SC::kFmt>;
     EpiResidual<TR, TO, SC::kQ8> epi{(const TR *)resid, gate, bias, (TO *)out, N, gate_fn, sc.a, sc.w};
-    switch (choose_tile(M, N, kAllTiles)) {
+    switch (choose_tile(M, N, kAllTiles, SC::kFmt)) {
         case kTileTall: return run<typename TSet::Tall>(a, w, M, N, K, RowsIdentity{256}, epi, s, sc.a, sc.w);
         case kTileHalf: return run<typename TSet::Half>(a, w, M, N, K, RowsIdentity{256}, epi, s, sc.a, sc.w);
         case kTileNar: return run<typename TSet::Nar>(a, w, M, N, K, RowsIdentity{128}, epi, s, sc.a, sc.w);
-        case kTileQuar: return run<typename TSet::Quar>(a, w, M, N, K, RowsIdentity{128}, epi, s, sc.a, sc.w);
+        case kTileQuar:
+            if (quarter_one_round(M, N))
+                return run<typename TSet::Quar1>(a, w, M, N, K, RowsIdentity{128}, epi, s, sc.a, sc.w);
+            return run<typename TSet::Quar>(a, w, M, N, K, RowsIdentity{128}, epi, s, sc.a, sc.w);
         default: return run<typename TSet::S>(a, w, M, N, K, RowsIdentity{256}, epi, s, sc.a, sc.w);
     }
 }
@@ -1011,11 +1033,13 @@ static hipError_t swiglu_any(const void *a, const void *w, int64_t M, int F, int
     auto with_act = [&](auto tile) {
         return act == 1 ? go(tile, EpiSwiglu<1, TU>{u, F}) : go(tile, EpiSwiglu<0, TU>{u, F});
     };
-    switch (choose_tile(M, 2 * F, kAllTiles)) {
+    switch (choose_tile(M, 2 * F, kAllTiles, SC::kFmt)) {
         case kTileTall: return with_act(typename TSet::Tall{});
         case kTileHalf: return with_act(typename TSet::Half{});
         case kTileNar: return with_act(typename TSet::Nar{});
-        case kTileQuar: return with_act(typename TSet::Quar{});
+        case kTileQuar:
+            if (quarter_one_round(M, 2 * F)) return with_act(typename TSet::Quar1{});
+            return with_act(typename TSet::Quar{});
         default: return with_act(typename TSet::S{});
     }
 }
