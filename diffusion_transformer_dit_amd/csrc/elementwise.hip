@@ -90,7 +90,8 @@ hipError_t launch_adaln_gemv(const void *w, int w_f32, const float *b, const flo
 }
 
 // ---------------------------------------------------------------------------
-// LayerNorm (or RMSNorm) + modulation, one wave per row.  The row stays in registers
+// LayerNorm (or RMSNorm) + modulation, one wave per row, 8 rows per workgroup
+// sharing one LDS copy of the modulation vectors.  The row stays in registers
 // (IT = dim/256 float4 per lane) between the mean pass, the centred variance
 // pass and the output pass, so x is read from HBM exactly once.  IT is a
 // template parameter so that all IT loads of a lane are issued back to back
@@ -113,15 +114,22 @@ __device__ __forceinline__ void store4(TH *p, const floatx4 &v) {
     }
 }
 
+// rows (one wave each) per workgroup: they share one LDS copy of the modulation
+constexpr int kLnRows = 8;
+
 template <typename TX, typename TH, int IT, bool RMS>
-__global__ __launch_bounds__(256)
+__global__ __launch_bounds__(kLnRows * 64)
 void ln_modulate_kernel(const TX *__restrict__ x, int64_t rows, const float *__restrict__ shift,
                         const float *__restrict__ scale, int mode, float eps, TH *__restrict__ h) {
     constexpr int dim = IT * 256;
+    // multiplier (1 + scale, or scale in mode 1, or 1 without scale) and addend
+    // (shift, or 0), loaded once per workgroup instead of once per row
+    __shared__ floatx4 s_mul[IT * 64], s_add[IT * 64];
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;
-    const TX *xr = x + row * dim;
+    const int64_t row = (int64_t)blockIdx.x * kLnRows + (threadIdx.x >> 6);
+    const bool valid = row < rows;
+    const TX *xr = x + (valid ? row : 0) * dim;
+    // the row's loads go out first; the modulation fill below overlaps their latency
     floatx4 v[IT];
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
@@ -133,6 +141,16 @@ void ln_modulate_kernel(const TX *__restrict__ x, int64_t rows, const float *__r
             v[it] = floatx4{(float)t[0], (float)t[1], (float)t[2], (float)t[3]};
         }
     }
+    const float one = mode == 0 ? 1.0f : 0.0f;
+    for (int i = threadIdx.x; i < IT * 64; i += kLnRows * 64) {
+        floatx4 mul = {1.f, 1.f, 1.f, 1.f}, add = {0.f, 0.f, 0.f, 0.f};
+        if (scale) mul = *(const floatx4 *)(scale + 4 * i) + one;
+        if (shift) add = *(const floatx4 *)(shift + 4 * i);
+        s_mul[i] = mul;
+        s_add[i] = add;
+    }
+    __syncthreads();
+    if (!valid) return;
     float mean = 0.f;
     if (!RMS) {
         float s = 0.f;
@@ -150,44 +168,26 @@ void ln_modulate_kernel(const TX *__restrict__ x, int64_t rows, const float *__r
             ss += d * d;
         }
     const float rstd = rsqrtf(group_sum<64>(ss) * (1.0f / dim) + eps);
-    const float one = mode == 0 ? 1.0f : 0.0f;
     TH *hr = h + row * dim;
-    if (scale && shift) {
 #pragma unroll
-        for (int it = 0; it < IT; ++it) {
-            const int i = it * 256 + lane * 4;
-            const floatx4 mul = *(const floatx4 *)(scale + i);
-            const floatx4 add = *(const floatx4 *)(shift + i);
-            floatx4 o;
+    for (int it = 0; it < IT; ++it) {
+        const floatx4 mul = s_mul[it * 64 + lane], add = s_add[it * 64 + lane];
+        floatx4 o;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) o[k] = v[it][k] * rstd * (mul[k] + one) + add[k];
-            store4(hr + i, o);
-        }
-    } else {
-        // mode 1 with a null scale (taken as 1) and/or a null shift (taken as 0)
-#pragma unroll
-        for (int it = 0; it < IT; ++it) {
-            const int i = it * 256 + lane * 4;
-            floatx4 mul = {1.f, 1.f, 1.f, 1.f}, add = {0.f, 0.f, 0.f, 0.f};
-            if (scale) mul = *(const floatx4 *)(scale + i) + one;
-            if (shift) add = *(const floatx4 *)(shift + i);
-            floatx4 o;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) o[k] = v[it][k] * rstd * mul[k] + add[k];
-            store4(hr + i, o);
-        }
+        for (int k = 0; k < 4; ++k) o[k] = v[it][k] * rstd * mul[k] + add[k];
+        store4(hr + it * 256 + lane * 4, o);
     }
 }
 
 template <typename TX, typename TH, bool RMS>
 static hipError_t ln_modulate_typed(const TX *x, int64_t rows, int dim, const float *shift, const float *scale,
                                     int mode, float eps, TH *h, hipStream_t s) {
-    const dim3 grid((unsigned)((rows + 3) / 4));
+    const dim3 grid((unsigned)((rows + kLnRows - 1) / kLnRows));
     switch (dim >> 8) {
 #define DIT_LN_CASE(n)                                                                                 \
     case n:                                                                                            \
-        hipLaunchKernelGGL((ln_modulate_kernel<TX, TH, n, RMS>), grid, dim3(256), 0, s, x, rows, shift, scale, \
-                           mode, eps, h);                                                              \
+        hipLaunchKernelGGL((ln_modulate_kernel<TX, TH, n, RMS>), grid, dim3(kLnRows * 64), 0, s, x, rows, shift, \
+                           scale, mode, eps, h);                                                       \
         break;
         DIT_LN_CASE(1) DIT_LN_CASE(2) DIT_LN_CASE(3) DIT_LN_CASE(4) DIT_LN_CASE(5) DIT_LN_CASE(6)
         DIT_LN_CASE(7) DIT_LN_CASE(8) DIT_LN_CASE(9) DIT_LN_CASE(10) DIT_LN_CASE(11) DIT_LN_CASE(12)
