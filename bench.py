@@ -46,6 +46,34 @@ def _event_us(fn, reps):
     return e0.elapsed_time(e1) * 1000.0 / reps
 
 
+def _graph_us(fn, reps):
+    """Average device time of one fn() launch for a kernel shorter than the
+    host's per-call overhead (ctypes marshalling, ~10-20 us): the reps launches
+    are recorded once into a HIP graph and replayed between HIP events on
+    torch's current stream, so the kernels run back to back as they do inside
+    dit_stack_step.  (No stage entry point records a memset.)"""
+    import torch
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side, capture_error_mode="relaxed"):
+        for _ in range(reps):
+            fn()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del graph
+    return e0.elapsed_time(e1) * 1000.0 / reps
+
+
 def block_flops(cfg) -> dict:
     """Algorithmic flops of one block (2 per multiply-add; attention 4 S^2 hd H B)."""
     N, D, F = cfg.tokens, cfg.hidden, cfg.ffn
@@ -91,7 +119,8 @@ def build_full_stack(cfg=I.C4, device="cuda"):
 def time_kernels(cfg, stack, reps=20):
     """Average device time of each block kernel at the stack's shapes, launched
     through the stage entry points (same kernels and launch configuration as
-    inside dit_stack_step) on torch's current stream, timed with HIP events."""
+    inside dit_stack_step) on torch's current stream: reps launches in a HIP
+    graph, timed with HIP events around its replay."""
     import torch
     from diffusion_transformer_dit_amd import native as N
     from diffusion_transformer_dit_amd import runtime as R
@@ -141,16 +170,7 @@ def time_kernels(cfg, stack, reps=20):
     torch.cuda.synchronize()
     out = {}
     for name, (fn, bound, nbytes) in launches.items():
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1000.0 / reps
+        us = _graph_us(fn, reps)
         if bound == "mfma":
             tf = fl[name] / (us * 1e-6) / 1e12
             out[name] = {"us": round(us, 2), "bound": "mfma", "achieved": round(tf, 1), "unit": "TFLOP/s",
@@ -298,7 +318,7 @@ def time_kernels_w8a8(cfg, qblk, reps=20):
     fl = block_flops(cfg)
     out = {}
     for name, (fn, bound, nbytes) in launches.items():
-        us_ = _event_us(fn, reps)
+        us_ = _graph_us(fn, reps)
         if bound == "mfma":
             tops = fl[name] / (us_ * 1e-6) / 1e12
             out[name] = {"us": round(us_, 2), "bound": "mfma", "achieved": round(tops, 1), "unit": "TOP/s",
