@@ -244,6 +244,8 @@ def test_flash_attention_closed_forms():
     (100, 128, 256, None, "f32", False, True),        # narrow N tile, no residual
     (4096, 384, 128, None, "f32", False, True),       # patch-embed-like K = 128
     (4170, 4096, 256, "f32", "f32", True, True),      # ragged rows: the 320-row tile (one round of tiles)
+    (2200, 2048, 256, "f32", "f32", True, True),      # ragged rows: the 8-wave 3-stage 256 x 128 tile (144 tiles)
+    (2200, 4096, 128, "bf16", "bf16", True, False),   # ragged rows: the 8-wave 2-stage 128 x 128 tile (576 tiles)
 ])
 def test_gemm_gated_residual(M, Nn, K, rdt, odt, gate, bias):
     import torch
@@ -301,7 +303,9 @@ def test_gemm_residual_in_place_and_identity():
 
 
 @pytest.mark.parametrize("M,F,K", [(300, 384, 256), (256, 768, 256), (4097, 256, 512), (1, 128, 64),
-                                   (4170, 2048, 256)])   # ragged rows over one full round of tiles
+                                   (4170, 2048, 256),    # ragged rows over one full round of tiles
+                                   (2200, 1024, 256),    # the 256 x 128 tile
+                                   (3000, 1536, 128)])   # the 2-stage 128 x 128 tile (576 tiles)
 def test_gemm_swiglu(M, F, K):
     import torch
     say(f"gemm_swiglu M={M} F={F} K={K}")
