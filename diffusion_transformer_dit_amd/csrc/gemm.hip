@@ -1,16 +1,17 @@
-// bf16 and int8 MFMA GEMM for gfx950 with the block's fused epilogues.
+// bf16, int8 and fp32 MFMA GEMM for gfx950 with the block's fused epilogues.
 //
 // C[m, n] = sum_k A[m, k] * W[n, k]: A is [M, K] row-major (activations), W is
 // [N, K] row-major (weights as [out, in]), both K-contiguous, so both operand
 // tiles are copied to LDS row by row and read back as MFMA fragments without a
 // transpose.  One workgroup computes a BM x BN tile with WM x WN waves; each
-// wave owns a (BM/WM) x (BN/WN) sub-tile built from 32x32 MFMA blocks
-// (v_mfma_f32_32x32x16_bf16 with fp32 accumulators, or for the W8A8 H256
-// format of the zml-flow-rs page §VII v_mfma_i32_32x32x32_i8 with exact int32
-// accumulators, dequantized by the row scales of A and W before the
-// epilogue).  K advances 128 bytes of each operand row at a time (64 bf16 or
-// 128 int8) through two LDS stages: while one stage feeds the MFMAs, the next
-// tile is already in flight from global memory.
+// wave owns a (BM/WM) x (BN/WN) sub-tile built from 16x16 MFMA blocks
+// (v_mfma_f32_16x16x32_bf16 with fp32 accumulators; for the W8A8 H256 format
+// of the zml-flow-rs page §VII v_mfma_i32_16x16x64_i8 with exact int32
+// accumulators, dequantized by the row scales of A and W before the epilogue;
+// for fp32 operands four v_mfma_f32_16x16x4f32 per 16-byte fragment pair).  K
+// advances 128 bytes of each operand row at a time (64 bf16, 128 int8 or 32
+// fp32) through two or three LDS stages: while one stage feeds the MFMAs, the
+// next tiles are already in flight from global memory.
 //
 // Epilogues (run on the fp32 accumulators, no extra pass over memory):
 //   * residual : out = resid + gate[n] * acc + bias[n]   (gated residual, ERNIE
