@@ -822,8 +822,10 @@ struct EpiQkv {
 // waits overlap the other's MFMAs.
 using Tile8w = Tile<256, 256, 2, 4>;
 using Tile8wTall = Tile<320, 256, 2, 4>;   // 160 x 64 per wave: ragged row counts just above a multiple of 256
-// 128-row tiles (8 waves of 64 x 64): ragged row tails, few-tile shapes
-using Tile8wHalf = Tile<128, 256, 2, 4>;
+// 128-row tiles (8 waves of 64 x 64): ragged row tails, few-tile shapes; bf16
+// over 3 LDS stages (144 KiB: with half the MFMA work of a 256-row tile per
+// stage, loads two stages ahead are what keeps the MFMAs fed)
+using Tile8wHalf = Tile<128, 256, 2, 4, 64, 3>;
 // Narrow and quarter tiles for shapes with few 256 x 256 tiles, also 8 waves:
 // 256 x 128 as 128 x 32 per wave over 3 LDS stages (144 KiB); 128 x 128 as
 // 32 x 64 per wave, over 2 stages (64 KiB: two workgroups fit on a CU, which
@@ -863,9 +865,9 @@ template <> struct TileSet<2> {
 // Tile choice for an M x N output.  Every tile of a launch costs about the
 // same, so the time is the number of rounds of workgroups over the CUs times
 // the cost of one tile: its area over its throughput relative to the 256 x 256
-// tile, measured at shapes that fill the chip (320 x 256: 1.0, 128 x 256:
-// 0.69, 256 x 128: 0.86 for the 8-wave 3-stage bf16 tile and 0.69 for the
-// 4-wave int8 / fp32 ones, 128 x 128: 0.775; N(0, 1) x N(0, 0.02)).  E.g.
+// tile, measured at shapes that fill the chip (320 x 256: 1.0; 128 x 256 and
+// 256 x 128: 0.87 and 0.86 for the 3-stage bf16 tiles, 0.69 for the int8 /
+// fp32 ones; 128 x 128: 0.775; N(0, 1) x N(0, 0.02)).  E.g.
 // 4170 x 4096 takes the 320-row tile (224 tiles in one round instead of 272 in
 // two), 4096 x 1024 the 128 x 128 tile (256 tiles instead of 64), 1024 x 6144
 // the 256 x 128 tile (192 tiles in one round), 1024 x 8192 QKV the 128 x 256
@@ -888,7 +890,7 @@ static TileKind choose_tile(int64_t M, int N, unsigned mask, int fmt = 0) {
     bool have = false;
     for (const TileCand &c : kTileCands) {
         if (!(mask >> c.kind & 1u) || N % c.bn) continue;
-        const double rate = c.kind == kTileNar && fmt == 0 ? 0.86 : c.rate;
+        const double rate = fmt != 0 ? c.rate : c.kind == kTileNar ? 0.86 : c.kind == kTileHalf ? 0.87 : c.rate;
         const int64_t tiles = (M + c.bm - 1) / c.bm * (N / c.bn);
         const double cost = (double)((tiles + cus - 1) / cus) * c.bm * c.bn / rate;
         if (!have || cost < best_cost) {
@@ -959,8 +961,9 @@ static hipError_t run_tail_split(const void *a, const void *w, int64_t M, int N_
                                  Epi epi, hipStream_t s, const float *a_scale = nullptr,
                                  const float *w_scale = nullptr) {
     static_assert(T::BM == 256 && TH::BM == 128 && T::BN == TH::BN, "full and tail tiles");
+    constexpr int kFmt = T::ES == 2 ? 0 : (T::ES == 1 ? 1 : 2);
     // few row tiles (e.g. 1024 x 8192): every row in 128-row tiles
-    if (choose_tile(M, N_tile_cols, 1u << kTileS | 1u << kTileHalf) == kTileHalf)
+    if (choose_tile(M, N_tile_cols, 1u << kTileS | 1u << kTileHalf, kFmt) == kTileHalf)
         return run<TH>(a, w, M, N_tile_cols, K, rm, epi, s, a_scale, w_scale);
     if (!split_tail_rows(M, N_tile_cols)) return run<T>(a, w, M, N_tile_cols, K, rm, epi, s, a_scale, w_scale);
     const int64_t m_full = M / 256 * 256;
