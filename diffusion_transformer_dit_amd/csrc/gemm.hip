@@ -1028,7 +1028,6 @@ hipError_t launch_gemm_residual_q8(const int8_t *a, const float *a_scale, const 
 template <class SC, typename TU>
 static hipError_t swiglu_any(const void *a, const void *w, int64_t M, int F, int K, int act, TU *u, SC sc,
                              hipStream_t s) {
-    // (a 128-row tail launch measured no faster here: 718 vs 713 us at 4170 rows)
     using TSet = TileSet<SC::kFmt>;
     auto go = [&](auto tile, auto epi) {
         using T = decltype(tile);
@@ -1044,7 +1043,22 @@ static hipError_t swiglu_any(const void *a, const void *w, int64_t M, int F, int
         case kTileQuar:
             if (quarter_one_round(M, 2 * F)) return with_act(typename TSet::Quar1{});
             return with_act(typename TSet::Quar{});
-        default: return with_act(typename TSet::S{});
+        default:
+            if (SC::kFmt == 0 && split_tail_rows(M, 2 * F)) {
+                // full 256-row tiles, then the ragged tail rows in 3-stage 128 x 256 tiles
+                // (4170 x 24576: 7 rounds of 256-row tiles become 6 plus a short one)
+                using T = typename TSet::S;
+                using TH = typename TSet::Half;
+                const int64_t m_full = M / 256 * 256;
+                auto split = [&](auto epi) {
+                    const hipError_t e =
+                        run<T>(a, w, m_full, 2 * F, K, RowsSwiglu{T::BN, T::kWaveN, F}, epi, s, sc.a, sc.w);
+                    if (e != hipSuccess) return e;
+                    return run<TH>(a, w, M, 2 * F, K, RowsSwiglu{TH::BN, TH::kWaveN, F}, epi, s, sc.a, sc.w, m_full);
+                };
+                return act == 1 ? split(EpiSwiglu<1, TU>{u, F}) : split(EpiSwiglu<0, TU>{u, F});
+            }
+            return with_act(typename TSet::S{});
     }
 }
 
