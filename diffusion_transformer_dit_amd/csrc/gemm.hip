@@ -883,7 +883,7 @@ constexpr TileCand kTileCands[] = {{kTileS, 256, 256, 1.0},    {kTileTall, 320, 
                                    {kTileQuar, 128, 128, 0.775}};
 
 // mask: bit k allows TileKind k; fmt: the operand format (TileSet index)
-static TileKind choose_tile(int64_t M, int N, unsigned mask, int fmt = 0) {
+static TileKind choose_tile(int64_t M, int N, unsigned mask, int fmt = 0, double *cost_out = nullptr) {
     const int64_t cus = device_cu_count();
     TileKind best = kTileS;
     double best_cost = 0.0;
@@ -899,6 +899,7 @@ static TileKind choose_tile(int64_t M, int N, unsigned mask, int fmt = 0) {
             have = true;
         }
     }
+    if (cost_out) *cost_out = best_cost;
     return best;
 }
 constexpr unsigned kAllTiles = 0x1f;
@@ -972,21 +973,63 @@ static hipError_t run_tail_split(const void *a, const void *w, int64_t M, int N_
     return run<TH>(a, w, M, N_tile_cols, K, rm, epi, s, a_scale, w_scale, m_full);
 }
 
+// Column split of a bf16 residual launch whose 256 x 256 tiles fill whole
+// rounds only over part of the columns (e.g. 4096 x 6144: 384 tiles = 1.5
+// rounds): the first n0 columns in 256 x 256 tiles (whole rounds), the rest
+// by its own tile choice, as two launches over offset W rows and output
+// columns (same row stride).  4096 x 6144: one round of 256 x 256 plus one of
+// 128 x 256 instead of three rounds of 128 x 256.  Returns n0, or 0 when a
+// single launch models as fast (within 5 %).
+static int residual_column_split(int64_t M, int N) {
+    const int64_t cus = device_cu_count(), tm = (M + 255) / 256;
+    if (N % 256 || tm > cus || cus % tm) return 0;
+    const int64_t per_round = cus / tm, ct = N / 256;   // 256-column tiles per round, in all
+    const int64_t n0 = ct / per_round * per_round * 256;
+    if (n0 == 0 || n0 == N) return 0;
+    double whole = 0.0, rest = 0.0;
+    choose_tile(M, N, kAllTiles, 0, &whole);
+    choose_tile(M, (int)(N - n0), kAllTiles, 0, &rest);
+    const double split = (double)(n0 / 256 / per_round) * 65536.0 + rest;
+    return split < 0.95 * whole ? (int)n0 : 0;
+}
+
 template <typename TR, typename TO, class SC>
 static hipError_t residual_typed(const void *a, const void *w, int64_t M, int N, int K, const void *resid,
                                  const float *gate, int gate_fn, const float *bias, void *out, SC sc,
-                                 hipStream_t s) {
+                                 hipStream_t s, int n0 = 0, int n_cols = 0) {
     using TSet = TileSet<SC::kFmt>;
+    if (n_cols == 0) {   // the whole output, or its column split
+        n_cols = N;
+        if constexpr (SC::kFmt == 0) {
+            const int c0 = residual_column_split(M, N);
+            if (c0) {
+                const hipError_t e = residual_typed<TR, TO>(a, w, M, N, K, resid, gate, gate_fn, bias, out, sc, s,
+                                                            0, c0);
+                if (e != hipSuccess) return e;
+                return residual_typed<TR, TO>(a, w, M, N, K, resid, gate, gate_fn, bias, out, sc, s, c0, N - c0);
+            }
+        }
+    }
+    // columns [n0, n0 + n_cols) of the [M, N] output: W rows, output, residual,
+    // gate and bias offset by n0, the row stride stays N
+    if (n0) {
+        w = (const uint8_t *)w + (size_t)n0 * K * TSet::S::ES;
+        resid = resid ? (const void *)((const TR *)resid + n0) : nullptr;
+        out = (TO *)out + n0;
+        gate = gate ? gate + n0 : nullptr;
+        bias = bias ? bias + n0 : nullptr;
+    }
     EpiResidual<TR, TO, SC::kQ8> epi{(const TR *)resid, gate, bias, (TO *)out, N, gate_fn, sc.a, sc.w};
-    switch (choose_tile(M, N, kAllTiles, SC::kFmt)) {
-        case kTileTall: return run<typename TSet::Tall>(a, w, M, N, K, RowsIdentity{256}, epi, s, sc.a, sc.w);
-        case kTileHalf: return run<typename TSet::Half>(a, w, M, N, K, RowsIdentity{256}, epi, s, sc.a, sc.w);
-        case kTileNar: return run<typename TSet::Nar>(a, w, M, N, K, RowsIdentity{128}, epi, s, sc.a, sc.w);
+    const int Nc = n_cols;
+    switch (choose_tile(M, Nc, kAllTiles, SC::kFmt)) {
+        case kTileTall: return run<typename TSet::Tall>(a, w, M, Nc, K, RowsIdentity{256}, epi, s, sc.a, sc.w);
+        case kTileHalf: return run<typename TSet::Half>(a, w, M, Nc, K, RowsIdentity{256}, epi, s, sc.a, sc.w);
+        case kTileNar: return run<typename TSet::Nar>(a, w, M, Nc, K, RowsIdentity{128}, epi, s, sc.a, sc.w);
         case kTileQuar:
-            if (quarter_one_round(M, N))
-                return run<typename TSet::Quar1>(a, w, M, N, K, RowsIdentity{128}, epi, s, sc.a, sc.w);
-            return run<typename TSet::Quar>(a, w, M, N, K, RowsIdentity{128}, epi, s, sc.a, sc.w);
-        default: return run<typename TSet::S>(a, w, M, N, K, RowsIdentity{256}, epi, s, sc.a, sc.w);
+            if (quarter_one_round(M, Nc))
+                return run<typename TSet::Quar1>(a, w, M, Nc, K, RowsIdentity{128}, epi, s, sc.a, sc.w);
+            return run<typename TSet::Quar>(a, w, M, Nc, K, RowsIdentity{128}, epi, s, sc.a, sc.w);
+        default: return run<typename TSet::S>(a, w, M, Nc, K, RowsIdentity{256}, epi, s, sc.a, sc.w);
     }
 }
 

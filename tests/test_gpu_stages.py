@@ -246,6 +246,8 @@ def test_flash_attention_closed_forms():
     (4170, 4096, 256, "f32", "f32", True, True),      # ragged rows: the 320-row tile (one round of tiles)
     (2200, 2048, 256, "f32", "f32", True, True),      # ragged rows: the 8-wave 3-stage 256 x 128 tile (144 tiles)
     (2200, 4096, 128, "bf16", "bf16", True, False),   # ragged rows: the 8-wave 2-stage 128 x 128 tile (576 tiles)
+    (4096, 6144, 128, "f32", "f32", True, True),      # column split: 4096 columns of 256 x 256, 2048 of 128 x 256
+    (4096, 5120, 128, "bf16", "bf16", True, True),    # column split: 4096 columns of 256 x 256, 1024 of 128 x 128
 ])
 def test_gemm_gated_residual(M, Nn, K, rdt, odt, gate, bias):
     import torch
