@@ -397,6 +397,86 @@ def test_stack_loop_resume_equals_uninterrupted():
 
 
 # ---------------------------------------------------------------------------
+# the stack step's edges, from scalar loops: timestep features, patch
+# embedding with its bias, the blocks, the final (scale, shift) linear of the
+# raw conditioning (no SiLU) and the output projection with its bias
+# ---------------------------------------------------------------------------
+def _bf_temb(t, dim):
+    half = dim // 2
+    w = [10000.0 ** (-j / half) for j in range(half)]
+    return [math.cos(t * x) for x in w] + [math.sin(t * x) for x in w]
+
+
+def bf_stack_step(lat, sigma, blocks, edges, cfg, pos):
+    """ERNIE page §IV (36 layers per step) and §V Bug 4 (the final layer's
+    linear of the conditioning), zml-flow-rs page §IV (flip_sin_to_cos
+    timestep sinusoid at t = 1000 sigma), as scalar float64 loops."""
+    c = _bf_temb(1000.0 * sigma, cfg.cond_dim)
+    D, C = cfg.hidden, cfg.latent_dim
+    x = np.array([[sum(float(edges["w_in"][o][i]) * float(row[i]) for i in range(C)) + float(edges["b_in"][o])
+                   for o in range(D)] for row in lat])
+    for w in blocks:
+        x = bf_block(x, np.array(c), w, cfg, pos)
+    m = [a + float(b) for a, b in zip(_bf_matvec(edges["w_fmod"], c), edges["b_fmod"])]
+    scale, shift = m[:D], m[D:]
+    v = []
+    for row in x:
+        n = _bf_ln([float(e) for e in row], cfg.eps)
+        h = [n[i] * (1.0 + scale[i]) + shift[i] for i in range(D)]
+        v.append([a + float(b) for a, b in zip(_bf_matvec(edges["w_out"], h), edges["b_out"])])
+    return np.array(v)
+
+
+def _stack_case():
+    cfg = T0.replace(batch=1, layers=2, latent_dim=4)
+    D, Dc, C = cfg.hidden, cfg.cond_dim, cfg.latent_dim
+    r = np.random.default_rng(28)
+    blocks = [_rand_weights(cfg, seed=l) for l in range(cfg.layers)]
+    # every edge tensor nonzero and at a scale where it moves the velocity
+    edges = {"w_in": r.standard_normal((D, C)) * 0.5, "b_in": r.standard_normal(D) * 0.5,
+             "w_fmod": r.standard_normal((2 * D, Dc)) * 0.3, "b_fmod": r.standard_normal(2 * D) * 0.3,
+             "w_out": r.standard_normal((C, D)) * 0.3, "b_out": r.standard_normal(C) * 0.3}
+    lat = r.standard_normal((cfg.tokens, C))
+    return cfg, blocks, edges, lat, I.positions(cfg) + np.array([1, 2, 0])
+
+
+def test_stack_step_matches_brute_force():
+    cfg, blocks, edges, lat, pos = _stack_case()
+    sigma = 0.8
+    ref = bf_stack_step(lat, sigma, blocks, edges, cfg, pos)
+    got = O.stack_step(lat, sigma, blocks, edges, cfg, pos)
+    assert np.abs(got - ref).max() < 1e-10 * max(1.0, np.abs(ref).max())
+    assert np.abs(ref).max() > 0.5
+
+
+def test_stack_step_pin_catches_planted_edge_mistakes(monkeypatch):
+    """Three plausible misreadings of the edges, each planted in the oracle
+    (on the CPU), move the velocity far beyond the pin's tolerance: the
+    timestep fed as sigma instead of 1000 sigma, the patch-embedding bias
+    dropped, SiLU applied to the conditioning before the final linear."""
+    cfg, blocks, edges, lat, pos = _stack_case()
+    sigma = 0.8
+    ref = bf_stack_step(lat, sigma, blocks, edges, cfg, pos)
+    tol = 1e-10 * max(1.0, np.abs(ref).max())
+
+    def worst(fn):
+        return np.abs(fn() - ref).max()
+
+    temb = O.timestep_embedding
+    with monkeypatch.context() as m:
+        m.setattr(O, "timestep_embedding", lambda t, dim, dtype=O.F64: temb(t / 1000.0, dim, dtype))
+        assert worst(lambda: O.stack_step(lat, sigma, blocks, edges, cfg, pos)) > 1e3 * tol
+    no_bias = dict(edges, b_in=np.zeros_like(edges["b_in"]))     # an oracle that ignores b_in
+    assert worst(lambda: O.stack_step(lat, sigma, blocks, no_bias, cfg, pos)) > 1e3 * tol
+    final = O.final_layer
+    with monkeypatch.context() as m:
+        m.setattr(O, "final_layer", lambda x, c, e, s, dtype=O.F64: final(x, O.silu(c), e, s, dtype))
+        assert worst(lambda: O.stack_step(lat, sigma, blocks, edges, cfg, pos)) > 1e3 * tol
+    # and unplanted, the same comparison holds
+    assert worst(lambda: O.stack_step(lat, sigma, blocks, edges, cfg, pos)) < tol
+
+
+# ---------------------------------------------------------------------------
 # the oracle's own rounding floor (fp32 vs fp64) and the workload dims
 # ---------------------------------------------------------------------------
 def test_p14_fp32_vs_fp64_floor_c1():
