@@ -383,8 +383,10 @@ def measured_traffic():
 
 
 def cpu_baseline(cfg=I.C4):
-    """The float64 CPU oracle on a bounded sample of one step: one block of the
-    stack plus the stack edges, scaled by the block count to s/denoise-step."""
+    """The fp32 CPU oracle (NumPy, float32 end to end) on a bounded sample of
+    one step: one block of the stack (median of 3 runs) plus the stack edges,
+    scaled by the block count to s/denoise-step.  One float64 run of the same
+    block is reported beside it as context."""
     from oracle import dit as O
     try:
         from threadpoolctl import threadpool_info
@@ -392,6 +394,7 @@ def cpu_baseline(cfg=I.C4):
                       or [os.cpu_count() or 1])
     except Exception:
         threads = os.cpu_count() or 1
+    f32 = np.float32
     w = I.block_weights(cfg, 0)
     shared = I.shared_ada(cfg)
     w["w_ada"], w["b_ada"] = shared["w_ada"], shared["b_ada"]
@@ -399,26 +402,30 @@ def cpu_baseline(cfg=I.C4):
     lat, pos = I.latent(cfg), I.positions(cfg)
     sigma = 1.0
     t0 = time.perf_counter()
-    c = O.timestep_embedding(1000.0 * sigma, cfg.cond_dim)
-    x0 = O.linear(lat, edges["w_in"], edges["b_in"])
+    c = O.timestep_embedding(1000.0 * sigma, cfg.cond_dim, dtype=f32)
+    x0 = O.linear(lat, edges["w_in"], edges["b_in"], dtype=f32)
     t_embed = time.perf_counter()
     runs = []
     for _ in range(3):                  # the block: median of 3
         tb = time.perf_counter()
-        x = O.block_forward(x0, c, w, cfg, pos)
+        x = O.block_forward(x0, c, w, cfg, pos, dtype=f32)
         runs.append(time.perf_counter() - tb)
     t_blocks = time.perf_counter()
-    v = O.final_layer(x, c, edges, cfg)
-    _ = O.euler_update(lat, v, 1.0, 0.9)
+    v = O.final_layer(x, c, edges, cfg, dtype=f32)
+    _ = O.euler_update(lat, v, f32(1.0), f32(0.9))
     t1 = time.perf_counter()
+    tb = time.perf_counter()
+    O.block_forward(x0, c, w, cfg, pos)     # float64, one run (context only)
+    block64_s = time.perf_counter() - tb
     block_s = float(np.median(runs))
     edge_s = (t_embed - t0) + (t1 - t_blocks)
     step_s = block_s * cfg.layers + edge_s
     return {"value": round(step_s, 2), "unit": "s/denoise-step", "cores": int(threads), "kind": "oracle",
-            "host": host_info(),
-            "sample": f"1 of {cfg.layers} blocks (4096 tok, hidden 4096, float64 NumPy; median of 3 runs "
+            "host": host_info(), "float64_step_s_estimate": round(block64_s * cfg.layers + edge_s, 2),
+            "sample": f"1 of {cfg.layers} blocks (4096 tok, hidden 4096, float32 NumPy oracle; median of 3 runs "
                       f"{block_s:.2f} s) x {cfg.layers} + patch-embed + final layer + Euler ({edge_s:.2f} s); "
-                      f"{t1 - t0:.1f} s of CPU work"}
+                      f"{t1 - t0 + block64_s:.1f} s of CPU work incl. one float64 run of the block "
+                      f"({block64_s:.2f} s)"}
 
 
 def main():
@@ -470,7 +477,7 @@ def main():
 
     def one_step(i):
         j = i % I.STACK_STEPS
-        N.dit_timestep_embedding(1000.0 * float(sig[j]), cfg.cond_dim, cond)
+        N.dit_sigma_embedding(float(sig[j]), cfg.cond_dim, cond)
         stack.step(lat, cond, cos, sin, vel)
         N.euler_flowmatch_update(lat, vel, lat.numel(), float(sig[j]), float(sig[j + 1]))
 
@@ -523,7 +530,7 @@ def main():
 
     def one_step8(i):
         j = i % I.STACK_STEPS
-        N.dit_timestep_embedding(1000.0 * float(sig[j]), cfg.cond_dim, cond)
+        N.dit_sigma_embedding(float(sig[j]), cfg.cond_dim, cond)
         stack8.step(lat, cond, cos, sin, vel)
         N.euler_flowmatch_update(lat, vel, lat.numel(), float(sig[j]), float(sig[j + 1]))
 

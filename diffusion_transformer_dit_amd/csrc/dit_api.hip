@@ -134,9 +134,15 @@ int check_desc(const dit_block_desc *d) {
     if (d->cond_dim % 8) return fail(DIT_ERR_UNSUPPORTED, "cond_dim must be a multiple of 8");
     if (d->fmt == DIT_FMT_W8A8_H256 && (d->ffn % 256 || !quantize_h256_supported(d->ffn)))
         return fail(DIT_ERR_UNSUPPORTED, "W8A8 H256 needs ffn a multiple of 256 with ceil(ffn / 1024) <= 7 or a multiple of 4 up to 32");
+    // The kernels address each operand through a buffer resource whose size
+    // and offsets are 32-bit byte counts: every GEMM operand and intermediate
+    // must stay below 2^32 bytes, i.e. 2^31 bf16 elements or 2^30 fp32 ones.
     const double n = (double)d->batch * d->seq;
-    if (n * d->ffn >= 2147483648.0 || n * d->hidden >= 2147483648.0 || (double)d->ffn * 2 * d->hidden >= 2147483648.0)
-        return fail(DIT_ERR_UNSUPPORTED, "a GEMM operand exceeds 2^31 elements");
+    const double lim = d->w_dtype == DIT_F32 ? 1073741824.0 : 2147483648.0;
+    const double qkv = (double)(d->heads + 2 * d->kv_heads) * d->head_dim;
+    if (n * d->ffn >= lim || n * d->hidden >= lim || (double)d->ffn * 2 * d->hidden >= lim ||
+        qkv * d->hidden >= lim || n * qkv >= lim)
+        return fail(DIT_ERR_UNSUPPORTED, "a GEMM operand exceeds 2^32 bytes (2^31 bf16 or 2^30 fp32 elements)");
     return DIT_OK;
 }
 
@@ -450,6 +456,11 @@ int dit_timestep_embedding(float t, int32_t dim, float *cond_out, void *stream) 
     DIT_TRY(device_check());
     DIT_TRY_HIP(launch_timestep_embedding(t, dim, cond_out, as_stream(stream)));
     return ok();
+}
+
+int dit_sigma_embedding(float sigma, int32_t dim, float *cond_out, void *stream) {
+    if (!isfinite(sigma)) return fail(DIT_ERR_INVALID_ARG, "sigma must be finite");
+    return dit_timestep_embedding(1000.0f * sigma, dim, cond_out, stream);
 }
 
 int dit_flowmatch_sigmas(int32_t steps, float shift, float *out) {
@@ -823,7 +834,7 @@ int dit_loop_create(const dit_model *model, float *latent, const float *rope_cos
             rc = fail(DIT_ERR_HIP, "hipStreamBeginCapture: %s", hipGetErrorString(e));
             break;
         }
-        rc = dit_timestep_embedding(1000.0f * sig[i], M.blk.cond_dim, cond, cs);
+        rc = dit_sigma_embedding(sig[i], M.blk.cond_dim, cond, cs);
         if (rc == DIT_OK) rc = dit_stack_step(model, latent, cond, rope_cos, rope_sin, vel, wsb + L.stack, L.cond, cs);
         if (rc == DIT_OK) rc = euler_flowmatch_update(latent, vel, n, sig[i], sig[i + 1], cs);
         const std::string err = g_err;              // keep the first error across the clean-up calls

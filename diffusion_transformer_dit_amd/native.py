@@ -31,7 +31,7 @@ EXPORTED = (
     "dit_gemm_gated_residual", "dit_gemm_swiglu", "dit_status_string", "dit_last_error", "dit_version",
     "dit_loop_workspace_size", "dit_loop_create", "dit_loop_launch_step", "dit_loop_launch", "dit_loop_destroy",
     "dit_quantize_h256", "dit_ln_modulate_h256q", "dit_gemm_w8a8_gated_residual", "dit_gemm_w8a8_swiglu",
-    "dit_qkv_rope_w8a8", "dit_attention_workspace_size", "dit_flash_attention_split",
+    "dit_qkv_rope_w8a8", "dit_attention_workspace_size", "dit_flash_attention_split", "dit_sigma_embedding",
 )
 
 
@@ -82,6 +82,7 @@ def lib():
             "dit_stack_step": (C.c_int, [pm, vp, vp, vp, vp, vp, vp, sz, vp]),
             "euler_flowmatch_update": (C.c_int, [vp, vp, i64, f32, f32, vp]),
             "dit_timestep_embedding": (C.c_int, [f32, i32, vp, vp]),
+            "dit_sigma_embedding": (C.c_int, [f32, i32, vp, vp]),
             "dit_flowmatch_sigmas": (C.c_int, [i32, f32, vp]),
             "dit_rope_tables": (C.c_int, [vp, i32, i32, vp, i32, f32, i32, vp, vp]),
             "dit_adaln_modulation": (C.c_int, [vp, vp, vp, i32, i32, i32, vp, vp]),
@@ -235,6 +236,10 @@ def euler_flowmatch_update(latent, velocity, n, sigma, sigma_next, stream=None):
 
 def dit_timestep_embedding(t, dim, cond_out, stream=None):
     _check(lib().dit_timestep_embedding(float(t), int(dim), _p(cond_out), _stream(stream)))
+
+
+def dit_sigma_embedding(sigma, dim, cond_out, stream=None):
+    _check(lib().dit_sigma_embedding(float(sigma), int(dim), _p(cond_out), _stream(stream)))
 
 
 def dit_flowmatch_sigmas(steps: int, shift: float):

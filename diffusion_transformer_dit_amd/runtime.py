@@ -154,7 +154,7 @@ def denoise(stack: DeviceStack, latent, cos, sin, steps: int, shift: float, star
     cond = torch.empty(stack.cfg.cond_dim, dtype=torch.float32, device=latent.device)
     vel = torch.empty_like(latent)
     for i in range(start, steps):
-        N.dit_timestep_embedding(1000.0 * float(sig[i]), stack.cfg.cond_dim, cond, stream)
+        N.dit_sigma_embedding(float(sig[i]), stack.cfg.cond_dim, cond, stream)
         stack.step(latent, cond, cos, sin, vel, stream)
         N.euler_flowmatch_update(latent, vel, latent.numel(), float(sig[i]), float(sig[i + 1]), stream)
     return latent

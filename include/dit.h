@@ -232,12 +232,18 @@ int euler_flowmatch_update(float *latent, const float *velocity, int64_t n,
  * features ([ZML] §IV).  dim even, > 0; cond_out device fp32 [dim]. */
 int dit_timestep_embedding(float t, int32_t dim, float *cond_out, void *stream);
 
+/* The conditioning of denoising step sigma: dit_timestep_embedding at
+ * t = 1000 sigma (the scheduler's timestep scale; [ZML] §IV timestep
+ * sinusoid), with the product taken in fp32 inside the library.  sigma must
+ * be finite; dim and cond_out as dit_timestep_embedding. */
+int dit_sigma_embedding(float sigma, int32_t dim, float *cond_out, void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* Whole denoising loop, recorded once as HIP graphs                         */
 /* ------------------------------------------------------------------------ */
 
 /* The flow-match Euler loop of [ERNIE] §I (8 steps, shift 4.0, sigma grid of
- * dit_flowmatch_sigmas) with each step = dit_timestep_embedding(1000 sigma_i)
+ * dit_flowmatch_sigmas) with each step = dit_sigma_embedding(sigma_i)
  * -> dit_stack_step -> euler_flowmatch_update(sigma_i, sigma_{i+1}), recorded
  * into one HIP graph per step so that replaying a step costs one launch
  * instead of ~300 ([ZML] §XI: host round trips dominate small steps).

@@ -339,3 +339,29 @@ def test_f32_path_desc_and_workspace():
     with pytest.raises(N.DitError) as e:
         N.dit_flash_attention_split(d32, FAKE, FAKE, FAKE, FAKE + (1 << 24), 4, FAKE, stream=0, ws_bytes=1 << 30)
     assert e.value.status == N.DIT_ERR_UNSUPPORTED
+
+
+def test_f32_operands_bounded_by_bytes():
+    """Buffer resources address 32-bit byte counts: fp32 operands are held
+    below 2^30 elements (4 GiB), bf16 ones below 2^31."""
+    # 65536 tokens x hidden 4096 x ffn 16384: u is 2^30 elements
+    big = dict(seq=65536, hidden=4096, heads=32, kv_heads=32, head_dim=128, ffn=16384, cond_dim=256)
+    with pytest.raises(N.DitError) as e:
+        N.dit_block_workspace_size(_desc(x_dtype=N.DIT_F32, w_dtype=N.DIT_F32, **big))
+    assert e.value.status == N.DIT_ERR_UNSUPPORTED
+    assert N.dit_block_workspace_size(_desc(**big)) > 0                        # 2^31 bytes of bf16: fine
+    # one below the limit is accepted, fp32 too
+    ok = dict(big, seq=65535)
+    assert N.dit_block_workspace_size(_desc(x_dtype=N.DIT_F32, w_dtype=N.DIT_F32, **ok)) > 0
+    with pytest.raises(N.DitError) as e:        # bf16 at 2^31 elements
+        N.dit_block_workspace_size(_desc(**dict(big, seq=131072)))
+    assert e.value.status == N.DIT_ERR_UNSUPPORTED
+
+
+def test_sigma_embedding_validation():
+    with pytest.raises(N.DitError) as e:
+        N.dit_sigma_embedding(float("nan"), 256, FAKE)
+    assert e.value.status == N.DIT_ERR_INVALID_ARG
+    with pytest.raises(N.DitError) as e:
+        N.dit_sigma_embedding(0.5, 255, FAKE)
+    assert e.value.status == N.DIT_ERR_INVALID_ARG

@@ -148,7 +148,7 @@ def _sample_rows(n, seed=0, k=24):
     return np.unique(np.clip(np.r_[fixed, r], 0, n - 1))
 
 
-@pytest.mark.parametrize("cfg", [I.C3, I.C5_1024, I.C2, I.C3_JOINT], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [I.C3, I.C5_1024, I.C5_4096, I.C2, I.C3_JOINT], ids=lambda c: c.name)
 def test_block_full_size_sampled(cfg):
     say(f"full-size block {cfg.name}: N={cfg.tokens} D={cfg.hidden}")
     w = I.block_weights(cfg, 0)

@@ -1,9 +1,10 @@
 """dit_stack_step and the flow-match Euler loop against the oracle.
 
 A 3-layer stack of small blocks runs whole denoising loops against the
-float64 oracle; the full 36 x 4096 stack at 4096 tokens is checked by the
-properties that hold at any size (finite, bitwise deterministic, resume from
-step k equals the uninterrupted loop)."""
+float64 oracle, eagerly and as the library's recorded HIP graphs; the full
+36 x 4096 stack at 4096 tokens is checked by the properties that hold at any
+size (finite, bitwise deterministic).  Two layers at the full width are
+compared with the oracle element by element in test_gpu_full_width.py."""
 import numpy as np
 import pytest
 
@@ -54,7 +55,7 @@ def test_stack_step_vs_oracle():
     cos, sin = R.rope_tables(cfg, pos)
     for i in (0, 5):
         cond = torch.empty(cfg.cond_dim, dtype=torch.float32, device="cuda")
-        N.dit_timestep_embedding(float(np.float32(1000.0 * sig[i])), cfg.cond_dim, cond)
+        N.dit_sigma_embedding(float(np.float32(sig[i])), cfg.cond_dim, cond)
         vel = torch.empty((cfg.tokens, cfg.latent_dim), dtype=torch.float32, device="cuda")
         stack.step(R.to_dev_f32(lat), cond, cos, sin, vel)
         _sync()
@@ -84,7 +85,7 @@ def test_denoise_loop_vs_oracle_and_resume():
     cond = torch.empty(cfg.cond_dim, dtype=torch.float32, device="cuda")
     vel = torch.empty_like(lat)
     for i in range(2):
-        N.dit_timestep_embedding(1000.0 * float(sig[i]), cfg.cond_dim, cond)
+        N.dit_sigma_embedding(float(sig[i]), cfg.cond_dim, cond)
         stack.step(lat, cond, cos, sin, vel)
         N.euler_flowmatch_update(lat, vel, lat.numel(), float(sig[i]), float(sig[i + 1]))
     saved = R.to_host_f32(lat)
@@ -133,6 +134,28 @@ def test_loop_graph_replays_match_eager_loop():
         loop.close()
 
 
+def test_loop_graph_vs_oracle():
+    """dit_loop_*: the whole 8-step loop replayed from its HIP graphs against
+    the float64 oracle's loop directly (not only against the eager HIP loop)."""
+    cfg = STK
+    blocks, edges, stack = _small_stack()
+    pos = I.positions(cfg)
+    lat0 = I.latent(cfg)
+    cos, sin = R.rope_tables(cfg, pos)
+    steps = I.STACK_STEPS
+    lat = R.to_dev_f32(lat0)
+    loop = R.DeviceLoop(stack, lat, cos, sin, steps, I.STACK_SHIFT)
+    try:
+        loop.run()
+        _sync()
+        got = R.to_host_f32(lat)
+    finally:
+        loop.close()
+    ref = O.denoise(lat0, blocks, edges, cfg, pos, steps, I.STACK_SHIFT)
+    assert_parity(got, ref, max_rel=2e-2, min_cos=0.9995, what=f"graph loop latent after {steps} steps")
+    assert_parity(got - lat0, ref - lat0, max_rel=2e-2, min_cos=0.9995, what="graph loop latent change")
+
+
 def test_full_stack_step_properties():
     """The 36-block, 4096-wide stack at 4096 tokens: one denoising step is
     finite and bitwise reproducible (weights drawn on the device)."""
@@ -143,7 +166,7 @@ def test_full_stack_step_properties():
     stack, cos, sin = build_full_stack(cfg)
     lat = R.to_dev_f32(I.latent(cfg))
     cond = torch.empty(cfg.cond_dim, dtype=torch.float32, device="cuda")
-    N.dit_timestep_embedding(1000.0, cfg.cond_dim, cond)
+    N.dit_sigma_embedding(1.0, cfg.cond_dim, cond)
     v1 = torch.empty_like(lat)
     v2 = torch.empty_like(lat)
     stack.step(lat, cond, cos, sin, v1)
