@@ -334,25 +334,37 @@ int dit_block_workspace_size(const dit_block_desc *desc, size_t *bytes) {
     return ok();
 }
 
-int dit_block_forward(const dit_block_desc *desc, const dit_block_weights *w, const void *x, const float *cond,
-                      const float *rope_cos, const float *rope_sin, void *out, void *ws, size_t ws_bytes,
-                      void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the block entry points (everything but the workspace).
+int check_block_call(const dit_block_desc *desc, const dit_block_weights *w, const void *x, const float *cond,
+                     const float *rope_cos, const float *rope_sin, const void *out) {
     DIT_TRY(check_desc(desc));
     const dit_block_desc &d = *desc;
     DIT_TRY(check_weights(d, w));
-    if (!x || !out || !rope_cos || !rope_sin || !ws) return fail(DIT_ERR_INVALID_ARG, "x, out, rope tables and ws are required");
+    if (!x || !out || !rope_cos || !rope_sin) return fail(DIT_ERR_INVALID_ARG, "x, out and rope tables are required");
     if ((d.cond_dim > 0) != (cond != nullptr)) return fail(DIT_ERR_INVALID_ARG, "cond must be given iff cond_dim > 0");
-    if (!aligned16(x) || !aligned16(out) || !aligned16(ws) || !aligned4(rope_cos) || !aligned4(rope_sin) ||
-        (cond && !aligned16(cond)))
-        return fail(DIT_ERR_ALIGNMENT, "x, out, ws, cond must be 16-byte aligned (rope tables 4-byte)");
-    const BlockWs L = block_ws(d);
-    if (ws_bytes < L.total) return fail(DIT_ERR_WORKSPACE, "workspace %zu < required %zu bytes", ws_bytes, L.total);
+    if (!aligned16(x) || !aligned16(out) || !aligned4(rope_cos) || !aligned4(rope_sin) || (cond && !aligned16(cond)))
+        return fail(DIT_ERR_ALIGNMENT, "x, out, cond must be 16-byte aligned (rope tables 4-byte)");
     const size_t xbytes = (size_t)d.batch * d.seq * d.hidden * (d.x_dtype == DIT_F32 ? 4 : 2);
     if (out != x && overlaps(out, xbytes, x, xbytes)) return fail(DIT_ERR_INVALID_ARG, "out overlaps x without being equal to it");
-    if (overlaps(ws, L.total, x, xbytes) || overlaps(ws, L.total, out, xbytes))
+    return DIT_OK;
+}
+
+int check_ws_apart(const dit_block_desc &d, const void *ws, const void *x, const void *out) {
+    const size_t total = block_ws(d).total;
+    const size_t xbytes = (size_t)d.batch * d.seq * d.hidden * (d.x_dtype == DIT_F32 ? 4 : 2);
+    if (overlaps(ws, total, x, xbytes) || overlaps(ws, total, out, xbytes))
         return fail(DIT_ERR_INVALID_ARG, "workspace overlaps x or out");
-    DIT_TRY(device_check());
-    hipStream_t s = as_stream(stream);
+    return DIT_OK;
+}
+
+// The block on a validated call with a workspace of at least block_ws(d).total bytes.
+int run_block(const dit_block_desc &d, const dit_block_weights *w, const void *x, const float *cond,
+              const float *rope_cos, const float *rope_sin, void *out, void *ws, hipStream_t s) {
+    const BlockWs L = block_ws(d);
     uint8_t *wsb = (uint8_t *)ws;
     float *m = nullptr;
     if (d.cond_dim > 0) {
@@ -363,6 +375,67 @@ int dit_block_forward(const dit_block_desc *desc, const dit_block_weights *w, co
     const int xf = d.x_dtype == DIT_F32;
     DIT_TRY(block_body(d, *w, x, xf, m, rope_cos, rope_sin, out, xf, wsb, L, s));
     return ok();
+}
+
+// Scratch of the allocation-free block entry point: the block workspace in a
+// device array of the library, one copy per GPU (from the library's load on
+// that GPU until the process ends).  In host code `scratch` names a host-side
+// stand-in: its device address, per GPU, comes from hipGetSymbolAddress.
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current GPU's scratch, looked up once per GPU.
+int scratch_of_current_device(void **ptr) {
+    int dev = -1;
+    DIT_TRY_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return fail(DIT_ERR_UNSUPPORTED, "device index %d >= %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        DIT_TRY_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        if (!p) return fail(DIT_ERR_HIP, "hipGetSymbolAddress returned NULL for the scratch array");
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return DIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dit_block_forward(const dit_block_desc *desc, const dit_block_weights *w, const void *x, const float *cond,
+                      const float *rope_cos, const float *rope_sin, void *out, void *ws, size_t ws_bytes,
+                      void *stream) {
+    DIT_TRY(check_block_call(desc, w, x, cond, rope_cos, rope_sin, out));
+    if (!ws) return fail(DIT_ERR_INVALID_ARG, "ws is required");
+    if (!aligned16(ws)) return fail(DIT_ERR_ALIGNMENT, "ws must be 16-byte aligned");
+    const size_t need = block_ws(*desc).total;
+    if (ws_bytes < need) return fail(DIT_ERR_WORKSPACE, "workspace %zu < required %zu bytes", ws_bytes, need);
+    DIT_TRY(check_ws_apart(*desc, ws, x, out));
+    DIT_TRY(device_check());
+    return run_block(*desc, w, x, cond, rope_cos, rope_sin, out, ws, as_stream(stream));
+}
+
+size_t dit_block_forward_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int dit_block_forward_noalloc(const dit_block_desc *desc, const dit_block_weights *w, const void *x,
+                              const float *cond, const float *rope_cos, const float *rope_sin, void *out,
+                              void *stream) {
+    DIT_TRY(check_block_call(desc, w, x, cond, rope_cos, rope_sin, out));
+    const size_t need = block_ws(*desc).total;
+    if (need > kScratchBytes)
+        return fail(DIT_ERR_WORKSPACE, "this block needs %zu bytes of workspace; the allocation-free entry point "
+                                       "holds %zu (use dit_block_forward with a caller workspace)", need, kScratchBytes);
+    DIT_TRY(device_check());
+    void *ws = nullptr;
+    DIT_TRY(scratch_of_current_device(&ws));
+    DIT_TRY(check_ws_apart(*desc, ws, x, out));
+    return run_block(*desc, w, x, cond, rope_cos, rope_sin, out, ws, as_stream(stream));
 }
 
 int dit_stack_workspace_size(const dit_model *model, size_t *bytes) {

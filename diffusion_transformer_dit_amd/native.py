@@ -32,6 +32,7 @@ EXPORTED = (
     "dit_loop_workspace_size", "dit_loop_create", "dit_loop_launch_step", "dit_loop_launch", "dit_loop_destroy",
     "dit_quantize_h256", "dit_ln_modulate_h256q", "dit_gemm_w8a8_gated_residual", "dit_gemm_w8a8_swiglu",
     "dit_qkv_rope_w8a8", "dit_attention_workspace_size", "dit_flash_attention_split", "dit_sigma_embedding",
+    "dit_block_forward_noalloc", "dit_block_forward_noalloc_max_bytes",
 )
 
 
@@ -78,6 +79,8 @@ def lib():
         sig = {
             "dit_block_workspace_size": (C.c_int, [pd, C.POINTER(sz)]),
             "dit_block_forward": (C.c_int, [pd, pw, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "dit_block_forward_noalloc": (C.c_int, [pd, pw, vp, vp, vp, vp, vp, vp]),
+            "dit_block_forward_noalloc_max_bytes": (sz, []),
             "dit_stack_workspace_size": (C.c_int, [pm, C.POINTER(sz)]),
             "dit_stack_step": (C.c_int, [pm, vp, vp, vp, vp, vp, vp, sz, vp]),
             "euler_flowmatch_update": (C.c_int, [vp, vp, i64, f32, f32, vp]),
@@ -179,6 +182,15 @@ def dit_block_forward(desc, weights, x, cond, rope_cos, rope_sin, out, ws, strea
     nb = _nbytes(ws) if ws_bytes is None else ws_bytes
     _check(lib().dit_block_forward(C.byref(desc), C.byref(weights), _p(x), _p(cond), _p(rope_cos), _p(rope_sin),
                                    _p(out), _p(ws), nb, _stream(stream)))
+
+
+def dit_block_forward_noalloc(desc, weights, x, cond, rope_cos, rope_sin, out, stream=None):
+    _check(lib().dit_block_forward_noalloc(C.byref(desc), C.byref(weights), _p(x), _p(cond), _p(rope_cos),
+                                           _p(rope_sin), _p(out), _stream(stream)))
+
+
+def dit_block_forward_noalloc_max_bytes() -> int:
+    return int(lib().dit_block_forward_noalloc_max_bytes())
 
 
 def make_model(desc: dit_block_desc, blocks: Sequence[dit_block_weights], latent_dim: int, edges: Dict[str, Any]):

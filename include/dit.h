@@ -185,6 +185,26 @@ int dit_block_forward(const dit_block_desc *desc, const dit_block_weights *w,
                       const float *rope_cos, const float *rope_sin,
                       void *out, void *ws, size_t ws_bytes, void *stream);
 
+/* dit_block_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same kernels, with the workspace taken from a device array
+ * inside the library instead of a `ws` argument.  The array holds
+ * dit_block_forward_noalloc_max_bytes() bytes (128 MiB) on every GPU the
+ * library runs on, from the library's load on that GPU until the process
+ * ends; a block whose dit_block_workspace_size exceeds it returns
+ * DIT_ERR_WORKSPACE (nothing is launched).  The call allocates and frees
+ * nothing (its first call on a GPU looks the array's address up once).
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (each call writes every scratch slot before reading it): calls
+ * that overlap on one GPU (concurrent streams, or several host threads)
+ * race and must be serialised by the caller.  Arguments, validation and
+ * results as dit_block_forward. */
+int dit_block_forward_noalloc(const dit_block_desc *desc, const dit_block_weights *w,
+                              const void *x, const float *cond,
+                              const float *rope_cos, const float *rope_sin,
+                              void *out, void *stream);
+size_t dit_block_forward_noalloc_max_bytes(void);
+
 /* ------------------------------------------------------------------------ */
 /* Stack step and denoising loop                                             */
 /* ------------------------------------------------------------------------ */

@@ -365,3 +365,24 @@ def test_sigma_embedding_validation():
     with pytest.raises(N.DitError) as e:
         N.dit_sigma_embedding(0.5, 255, FAKE)
     assert e.value.status == N.DIT_ERR_INVALID_ARG
+
+
+def test_noalloc_block_validation_before_device():
+    """The allocation-free block entry point validates like dit_block_forward
+    and rejects a block whose workspace exceeds its scratch before any device
+    work."""
+    assert N.dit_block_forward_noalloc_max_bytes() == 128 << 20
+    far = FAKE + (1 << 40)
+    big = _desc(seq=4096, hidden=4096, heads=32, kv_heads=32, head_dim=128, ffn=12288, cond_dim=4096)
+    assert N.dit_block_workspace_size(big) > N.dit_block_forward_noalloc_max_bytes()
+    with pytest.raises(N.DitError) as e:
+        N.dit_block_forward_noalloc(big, _weights(), FAKE, FAKE, FAKE, FAKE, far)
+    assert e.value.status == N.DIT_ERR_WORKSPACE
+    d = _desc()
+    for kw, st in [(dict(w=_weights(w_qkv=None)), N.DIT_ERR_INVALID_ARG), (dict(x=FAKE + 4), N.DIT_ERR_ALIGNMENT),
+                   (dict(cond=None), N.DIT_ERR_INVALID_ARG), (dict(out=FAKE + 256), N.DIT_ERR_INVALID_ARG)]:
+        a = dict(w=_weights(), x=FAKE, cond=FAKE, out=far)
+        a.update(kw)
+        with pytest.raises(N.DitError) as e:
+            N.dit_block_forward_noalloc(d, a["w"], a["x"], a["cond"], FAKE, FAKE, a["out"])
+        assert e.value.status == st, (kw, e.value)
