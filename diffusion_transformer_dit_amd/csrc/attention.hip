@@ -25,6 +25,11 @@
 // pipe overlap within the wave), then the PV MFMAs of tile t interleaved with
 // the row max of tile t + 1.
 //
+// Softmax in log2 units: q is multiplied by log2(e) / sqrt(hd) once, when it
+// is loaded, and the QK^T MFMAs of a tile start from the accumulator
+// -reference (the query's running softmax reference), so they deliver the
+// exponent itself and every probability is one v_exp_f32 of an accumulator.
+//
 // Ragged tail (seq not a multiple of 256, e.g. 4096 image + 74 text tokens):
 // the last, partial q tile of every (batch, head) would otherwise be a whole
 // extra round of workgroups.  With nsplit > 1 that tile's keys are cut into
@@ -114,7 +119,14 @@ void flash_attn_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K, c
     {
         const int qr = min(q_base + lrow, S - 1);
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) qf[kk] = *(const bf16x8 *)(Qh + (size_t)qr * HD + kk * 16 + lhalf * 8);
+        for (int kk = 0; kk < KK; ++kk) {
+            // q pre-multiplied by log2(e) / sqrt(hd): the scores come out of the
+            // MFMA in log2 units, so the exponent needs no multiply (one more
+            // bf16 rounding of q, well inside the bf16 path's error)
+            const bf16x8 raw = *(const bf16x8 *)(Qh + (size_t)qr * HD + kk * 16 + lhalf * 8);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) qf[kk][u] = f2bf(bf2f(raw[u]) * scale_log2);
+        }
     }
 
     // Load q of this wave fills 1 KiB at (q * NW + wave) KiB of the K (V^T) tile;
@@ -149,18 +161,19 @@ void flash_attn_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K, c
             rv, (lds_void *)(base_ + KT_BYTES + (q * NW + wave) * 1024), 16, v_off[q],                 \
             (uint32_t)kv0_ * 2u, 0, 0);                                                                \
     } while (0)
-    // S^T[key, q] of the tile in stage st (64 keys x 32 queries)
-#define DIT_ATT_QK(st, acc)                                                                            \
+    // S^T[key, q] of the tile in stage st (64 keys x 32 queries), in log2
+    // units, plus the initial accumulator c0 (every element of a lane's column
+    // the same value: minus that query's softmax reference, or zero)
+#define DIT_ATT_QK(st, acc, c0)                                                                        \
     do {                                                                                               \
         const uint8_t *sk_ = smem + (st) * STAGE;                                                      \
-        _Pragma("unroll") for (int ks = 0; ks < 2; ++ks)                                               \
-            _Pragma("unroll") for (int e = 0; e < 16; ++e) acc[ks][e] = 0.f;                           \
         _Pragma("unroll") for (int kk = 0; kk < KK; ++kk) {                                            \
             const int c_ = kk * 2 + lhalf;                                                             \
             _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                         \
                 const bf16x8 kf_ =                                                                     \
                     *(const bf16x8 *)(sk_ + (ks * 32 + lrow) * KROW + ((c_ ^ kswz(lrow)) << 4));       \
-                acc[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf_, qf[kk], acc[ks], 0, 0, 0);      \
+                acc[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf_, qf[kk], kk == 0 ? (c0) : acc[ks], \
+                                                                  0, 0, 0);                            \
             }                                                                                          \
         }                                                                                              \
     } while (0)
@@ -190,15 +203,20 @@ void flash_attn_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K, c
     barrier_only();
 
     floatx16 sa[2];             // scores of the tile being exponentiated
-    DIT_ATT_QK(t0 % NS, sa);
+    floatx16 zero16;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) zero16[e] = 0.f;
+    DIT_ATT_QK(t0 % NS, sa, zero16);
     DIT_ATT_MASK(t0 * BKV, sa);
-    // Reference max of the raw (unscaled) scores of this lane's query (scale > 0
-    // commutes with max): the exponentials, O and l are taken against it.  It
-    // starts at the first tile's max and moves up only when some lane of the
-    // wave sees a score more than kLazy (log2 units) above its reference, so
-    // exponentials stay <= 2^kLazy (exact in fp32 and bf16 range) while the
-    // rescale of O, which a max that creeps up would otherwise trigger on most
-    // tiles, becomes rare; O / l is the same softmax for any reference.
+    // Softmax reference of this lane's query, in log2 units: the exponentials,
+    // O and l are taken against it.  It starts at the first tile's max and
+    // moves up only when some lane of the wave sees a score more than kLazy
+    // above its reference, so exponentials stay <= 2^kLazy (exact in fp32 and
+    // bf16 range) while the rescale of O, which a max that creeps up would
+    // otherwise trigger on most tiles, becomes rare; O / l is the same softmax
+    // for any reference.  The QK^T MFMAs of a tile start from negm = -mref, so
+    // they deliver the exponent itself; dcur is the amount the reference moved
+    // after that tile's MFMAs were issued (zero but for the rare moves).
     constexpr float kLazy = 8.0f;
     float mref;
     {
@@ -209,6 +227,10 @@ void flash_attn_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K, c
             for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sa[ks][e]);
         mref = fmaxf(mx, __shfl_xor(mx, 32, 64));
     }
+    float dcur = mref;          // the first tile was computed against 0
+    floatx16 negm;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) negm[e] = -mref;
     float alpha = 1.f;          // factor taking O and l from the previous reference to mref
     float lsum = 0.f;           // this lane's partial row sum (the other 16 keys live in lane ^ 32)
 
@@ -218,25 +240,30 @@ void flash_attn_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K, c
     do {                                                                                                      \
         /* stage (t-1) % NS was released by the barrier that closed iteration t - 1 */                        \
         DIT_ATT_ISSUE(min((T) + NS - 1, t1 - 1), ((T) + NS - 1) % NS);                                        \
-        /* rescale only when some lane's running max grew (wave-uniform branch) */                            \
+        /* rare: the reference moved (wave-uniform branches) */                                               \
         if (__any(alpha < 1.f)) {                                                                             \
 _Pragma("unroll")                                                                                             \
             for (int ds = 0; ds < DS; ++ds)                                                                   \
 _Pragma("unroll")                                                                                             \
                 for (int e = 0; e < 16; ++e) oacc[ds][e] *= alpha;                                            \
+            lsum *= alpha;                                                                                    \
         }                                                                                                     \
-        lsum *= alpha;                                                                                        \
+        if (__any(dcur != 0.f)) {                                                                             \
+_Pragma("unroll")                                                                                             \
+            for (int ks = 0; ks < 2; ++ks)                                                                    \
+_Pragma("unroll")                                                                                             \
+                for (int e = 0; e < 16; ++e) SC[ks][e] -= dcur;                                               \
+        }                                                                                                     \
                                                                                                               \
         /* QK^T of tile t + 1 || exponentials of tile t */                                                    \
-        DIT_ATT_QK(((T) + 1) % NS, SN);                                                                       \
-        const float neg = -mref * scale_log2;                                                                 \
+        DIT_ATT_QK(((T) + 1) % NS, SN, negm);                                                                 \
         bf16x8 pf[4];                                                                                         \
         float ps[4];                          /* four partial sums: no 32-long dependent add chain */        \
 _Pragma("unroll")                                                                                             \
         for (int ks = 0; ks < 2; ++ks)                                                                        \
 _Pragma("unroll")                                                                                             \
             for (int e = 0; e < 16; ++e) {                                                                    \
-                const float p = __builtin_amdgcn_exp2f(fmaf(SC[ks][e], scale_log2, neg));                     \
+                const float p = __builtin_amdgcn_exp2f(SC[ks][e]);                                            \
                 if (ks == 0 && e < 4) ps[e] = p; else ps[e & 3] += p;                                         \
                 pf[ks * 2 + (e >> 3)][e & 7] = f2bf(p);                                                       \
             }                                                                                                 \
@@ -246,7 +273,7 @@ _Pragma("unroll")                                                               
         for (int i = 0; i < 2 * KK - 2; ++i) {                                                                \
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                \
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                                \
-            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);                                                \
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);                                                \
         }                                                                                                     \
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                                    \
                                                                                                               \
@@ -264,6 +291,7 @@ _Pragma("unroll")                                                               
                     oacc[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[k2], oacc[ds], 0, 0, 0);        \
                 }                                                                                             \
             }                                                                                                 \
+            /* the largest exponent of tile t + 1 against the current reference */                            \
             float mx = SN[0][0];                                                                              \
 _Pragma("unroll")                                                                                             \
             for (int ks = 0; ks < 2; ++ks)                                                                    \
@@ -271,10 +299,13 @@ _Pragma("unroll")                                                               
                 for (int e = 0; e < 16; ++e) mx = fmaxf(mx, SN[ks][e]);                                       \
             mx = fmaxf(mx, __shfl_xor(mx, 32, 64));                                                           \
             alpha = 1.f;                                                                                      \
-            if (__any((mx - mref) * scale_log2 > kLazy)) {                                                    \
-                const float mnew = fmaxf(mref, mx);                                                           \
-                alpha = __builtin_amdgcn_exp2f((mref - mnew) * scale_log2);                                   \
-                mref = mnew;                                                                                  \
+            dcur = 0.f;                                                                                       \
+            if (__any(mx > kLazy)) {                                                                          \
+                dcur = fmaxf(mx, 0.f);                                                                        \
+                alpha = __builtin_amdgcn_exp2f(-dcur);                                                        \
+                mref += dcur;                                                                                 \
+_Pragma("unroll")                                                                                             \
+                for (int e = 0; e < 16; ++e) negm[e] = -mref;                                                 \
             }                                                                                                 \
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                                \
 _Pragma("unroll")                                                                                             \
@@ -442,10 +473,10 @@ hipError_t launch_flash_attention(const bf16 *q, const bf16 *k, const bf16 *vt, 
     const dim3 cgrid((unsigned)((n_rows + 3) / 4));
     if (head_dim == 128)
         hipLaunchKernelGGL(attn_combine_kernel<128>, cgrid, dim3(256), 0, s, part_o, part_ml, out, seq, heads, q0,
-                           n_tail, n_rows, nsplit, scale_log2);
+                           n_tail, n_rows, nsplit, 1.0f);
     else
         hipLaunchKernelGGL(attn_combine_kernel<64>, cgrid, dim3(256), 0, s, part_o, part_ml, out, seq, heads, q0,
-                           n_tail, n_rows, nsplit, scale_log2);
+                           n_tail, n_rows, nsplit, 1.0f);
     return hipGetLastError();
 }
 
