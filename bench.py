@@ -219,33 +219,34 @@ def time_block(cfg, blk, reps=10):
 
 
 def time_chain(cfgs, depth, reps=3):
-    """`depth` blocks of the shapes of cfgs[0] run back to back through
-    dit_block_forward with x updated in place (distinct GEMM weights per block,
-    N(0, 0.02) bf16 drawn on the device; one AdaLN linear shared by the blocks
-    but applied by each), for every config in cfgs (same weights, other token
-    counts).  HIP events on torch's current stream; ms per pass of the chain
-    and the algorithmic TFLOP/s against the bf16 peak."""
+    """`depth` blocks of the shapes of cfgs[0] applied in place through
+    dit_block_chain_forward (distinct N(0, 0.02) bf16 weights per block, each
+    block with its own AdaLN linear, drawn on the device), for every config in
+    cfgs (same weights, other token counts).  With AdaLN the chain runs twice:
+    with a side stream, so the next block's modulation GEMV overlaps the
+    current block ("ms"), and all on one stream ("ms_serial").  HIP events on
+    torch's current stream; ms per pass of the chain and the algorithmic
+    TFLOP/s against the bf16 peak."""
     import torch
     from diffusion_transformer_dit_amd import native as N
     from diffusion_transformer_dit_amd import runtime as R
     cfg = cfgs[0]
     D, F, Dc, hd = cfg.hidden, cfg.ffn, cfg.cond_dim, cfg.head_dim
     nb = lambda shape, blk, name: I.torch_normal_bf16(shape, 0.02, I.torch_seed(cfg.cfg_id, blk, name), "cuda")
-    shared = {}
-    if Dc > 0:
-        shared = {"w_ada": nb((cfg.ada_rows, Dc), 999, "w_ada"), "b_ada": nb((cfg.ada_rows,), 999, "b_ada").float()}
     one = lambda n: torch.ones(n, dtype=torch.float32, device="cuda")
     zero = lambda n: torch.zeros(n, dtype=torch.float32, device="cuda")
     blocks = []
     for l in range(depth):
-        t = dict(shared)
-        t.update({"w_qkv": nb((cfg.qkv_dim, D), l, "w_qkv"), "w_o": nb((D, cfg.heads * hd), l, "w_o"),
-                  "w_gate_up": nb((2 * F, D), l, "w_gate_up"), "w_down": nb((D, F), l, "w_down")})
+        t = {"w_qkv": nb((cfg.qkv_dim, D), l, "w_qkv"), "w_o": nb((D, cfg.heads * hd), l, "w_o"),
+             "w_gate_up": nb((2 * F, D), l, "w_gate_up"), "w_down": nb((D, F), l, "w_down")}
+        if Dc > 0:
+            t.update({"w_ada": nb((cfg.ada_rows, Dc), l, "w_ada"), "b_ada": nb((cfg.ada_rows,), l, "b_ada").float()})
         if cfg.qk_norm:
             t.update({"q_g": one(hd), "q_b": zero(hd), "k_g": one(hd), "k_b": zero(hd)})
         if Dc == 0:
             t.update({"ln1_g": one(D), "ln1_b": zero(D), "ln2_g": one(D), "ln2_b": zero(D)})
         blocks.append(R.DeviceBlock(None, tensors=t))
+    side = torch.cuda.Stream()
     out = {}
     for c in cfgs:
         g = torch.Generator(device="cuda").manual_seed(17)
@@ -255,16 +256,18 @@ def time_chain(cfgs, depth, reps=3):
         cond = torch.randn((Dc,), generator=g, device="cuda") if Dc > 0 else None
         cos, sin = R.rope_tables(c)
         desc = R.desc_of(c)
-        ws = R.alloc_ws(N.dit_block_workspace_size(desc))
+        ws = R.alloc_ws(N.dit_block_chain_workspace_size(desc))
+        wc = [b.c for b in blocks]
 
-        def run():
-            for b in blocks:
-                N.dit_block_forward(desc, b.c, x, cond, cos, sin, x, ws)
+        def run(side_stream):
+            return lambda: N.dit_block_chain_forward(desc, wc, x, cond, cos, sin, ws, side_stream=side_stream)
 
-        us = _event_us(run, reps)
+        us = _event_us(run(side if Dc > 0 else None), reps)
+        us_serial = _event_us(run(None), reps) if Dc > 0 else us
         assert torch.isfinite(x).all().item(), f"non-finite output ({c.name})"
         tf = depth * sum(block_flops(c).values()) / (us * 1e-6) / 1e12
         out[f"{c.name}_x{depth}"] = {"tokens": c.tokens, "blocks": depth, "ms": round(us / 1000.0, 3),
+                                     "ms_serial": round(us_serial / 1000.0, 3),
                                      "achieved": round(tf, 1), "unit": "TFLOP/s",
                                      "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
     del blocks

@@ -438,6 +438,92 @@ int dit_block_forward_noalloc(const dit_block_desc *desc, const dit_block_weight
     return run_block(*desc, w, x, cond, rope_cos, rope_sin, out, ws, as_stream(stream));
 }
 
+// ---------------------------------------------------------------------------
+// chain of blocks in place, with the next block's modulation GEMV pipelined
+// ---------------------------------------------------------------------------
+namespace {
+size_t chain_ws_bytes(const dit_block_desc &d) {
+    return block_ws(d).total + align256((size_t)ada_rows(d) * 4);
+}
+
+struct EventPair {
+    hipEvent_t ready = nullptr, freed = nullptr;
+    ~EventPair() {
+        if (ready) (void)hipEventDestroy(ready);
+        if (freed) (void)hipEventDestroy(freed);
+    }
+};
+}  // namespace
+
+int dit_block_chain_workspace_size(const dit_block_desc *desc, size_t *bytes) {
+    DIT_TRY(check_desc(desc));
+    if (!bytes) return fail(DIT_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = chain_ws_bytes(*desc);
+    return ok();
+}
+
+int dit_block_chain_forward(const dit_block_desc *desc, const dit_block_weights *blocks, int32_t n_blocks, void *x,
+                            const float *cond, const float *rope_cos, const float *rope_sin, void *ws,
+                            size_t ws_bytes, void *stream, void *side_stream) {
+    if (n_blocks < 1 || !blocks) return fail(DIT_ERR_INVALID_ARG, "n_blocks must be >= 1 and blocks non-NULL");
+    for (int l = 0; l < n_blocks; ++l) DIT_TRY(check_block_call(desc, &blocks[l], x, cond, rope_cos, rope_sin, x));
+    const dit_block_desc &d = *desc;
+    if (!ws) return fail(DIT_ERR_INVALID_ARG, "ws is required");
+    if (!aligned16(ws)) return fail(DIT_ERR_ALIGNMENT, "ws must be 16-byte aligned");
+    const size_t need = chain_ws_bytes(d);
+    if (ws_bytes < need) return fail(DIT_ERR_WORKSPACE, "workspace %zu < required %zu bytes", ws_bytes, need);
+    const size_t xbytes = (size_t)d.batch * d.seq * d.hidden * (d.x_dtype == DIT_F32 ? 4 : 2);
+    if (overlaps(ws, need, x, xbytes)) return fail(DIT_ERR_INVALID_ARG, "workspace overlaps x");
+    DIT_TRY(device_check());
+    hipStream_t s = as_stream(stream), side = as_stream(side_stream);
+    const BlockWs L = block_ws(d);
+    uint8_t *wsb = (uint8_t *)ws;
+    const int xf = d.x_dtype == DIT_F32, wf = d.w_dtype == DIT_F32;
+    if (d.cond_dim == 0) {
+        for (int l = 0; l < n_blocks; ++l)
+            DIT_TRY(block_body(d, blocks[l], x, xf, nullptr, rope_cos, rope_sin, x, xf, wsb, L, s));
+        return ok();
+    }
+    // two modulation buffers: the block's own slot and one behind the block workspace
+    float *mbuf[2] = {(float *)(wsb + L.m), (float *)(wsb + L.total)};
+    bool shared = true;
+    for (int l = 1; l < n_blocks; ++l)
+        shared = shared && blocks[l].w_ada == blocks[0].w_ada && blocks[l].b_ada == blocks[0].b_ada;
+    const int rows = ada_rows(d);
+    DIT_TRY_HIP(launch_adaln_gemv(blocks[0].w_ada, wf, blocks[0].b_ada, cond, rows, d.cond_dim, 1, mbuf[0], s));
+    if (shared || n_blocks == 1 || !side_stream || side == s) {
+        for (int l = 0; l < n_blocks; ++l) {
+            float *m = mbuf[0];
+            if (l > 0 && !shared)
+                DIT_TRY_HIP(launch_adaln_gemv(blocks[l].w_ada, wf, blocks[l].b_ada, cond, rows, d.cond_dim, 1, m, s));
+            DIT_TRY(block_body(d, blocks[l], x, xf, m, rope_cos, rope_sin, x, xf, wsb, L, s));
+        }
+        return ok();
+    }
+    // Layer pipelining: the modulation GEMV of block l + 1 (HBM-bound) runs on
+    // the side stream while block l's GEMMs (MFMA-bound) run on the main
+    // stream.  `freed` marks the end of the block that last read a buffer,
+    // `ready` the end of the GEMV that refills it.
+    EventPair ev;
+    DIT_TRY_HIP(hipEventCreateWithFlags(&ev.ready, hipEventDisableTiming));
+    DIT_TRY_HIP(hipEventCreateWithFlags(&ev.freed, hipEventDisableTiming));
+    DIT_TRY_HIP(hipEventRecord(ev.freed, s));   // cond and every earlier write on the main stream
+    for (int l = 0; l < n_blocks; ++l) {
+        if (l + 1 < n_blocks) {
+            DIT_TRY_HIP(hipStreamWaitEvent(side, ev.freed, 0));
+            DIT_TRY_HIP(launch_adaln_gemv(blocks[l + 1].w_ada, wf, blocks[l + 1].b_ada, cond, rows, d.cond_dim, 1,
+                                          mbuf[(l + 1) & 1], side));
+            DIT_TRY_HIP(hipEventRecord(ev.ready, side));
+        }
+        DIT_TRY(block_body(d, blocks[l], x, xf, mbuf[l & 1], rope_cos, rope_sin, x, xf, wsb, L, s));
+        if (l + 1 < n_blocks) {
+            DIT_TRY_HIP(hipEventRecord(ev.freed, s));
+            DIT_TRY_HIP(hipStreamWaitEvent(s, ev.ready, 0));
+        }
+    }
+    return ok();
+}
+
 int dit_stack_workspace_size(const dit_model *model, size_t *bytes) {
     DIT_TRY(check_model(model));
     if (!bytes) return fail(DIT_ERR_INVALID_ARG, "bytes is NULL");

@@ -32,7 +32,8 @@ EXPORTED = (
     "dit_loop_workspace_size", "dit_loop_create", "dit_loop_launch_step", "dit_loop_launch", "dit_loop_destroy",
     "dit_quantize_h256", "dit_ln_modulate_h256q", "dit_gemm_w8a8_gated_residual", "dit_gemm_w8a8_swiglu",
     "dit_qkv_rope_w8a8", "dit_attention_workspace_size", "dit_flash_attention_split", "dit_sigma_embedding",
-    "dit_block_forward_noalloc", "dit_block_forward_noalloc_max_bytes",
+    "dit_block_forward_noalloc", "dit_block_forward_noalloc_max_bytes", "dit_block_chain_workspace_size",
+    "dit_block_chain_forward",
 )
 
 
@@ -81,6 +82,8 @@ def lib():
             "dit_block_forward": (C.c_int, [pd, pw, vp, vp, vp, vp, vp, vp, sz, vp]),
             "dit_block_forward_noalloc": (C.c_int, [pd, pw, vp, vp, vp, vp, vp, vp]),
             "dit_block_forward_noalloc_max_bytes": (sz, []),
+            "dit_block_chain_workspace_size": (C.c_int, [pd, C.POINTER(sz)]),
+            "dit_block_chain_forward": (C.c_int, [pd, pw, i32, vp, vp, vp, vp, vp, sz, vp, vp]),
             "dit_stack_workspace_size": (C.c_int, [pm, C.POINTER(sz)]),
             "dit_stack_step": (C.c_int, [pm, vp, vp, vp, vp, vp, vp, sz, vp]),
             "euler_flowmatch_update": (C.c_int, [vp, vp, i64, f32, f32, vp]),
@@ -191,6 +194,21 @@ def dit_block_forward_noalloc(desc, weights, x, cond, rope_cos, rope_sin, out, s
 
 def dit_block_forward_noalloc_max_bytes() -> int:
     return int(lib().dit_block_forward_noalloc_max_bytes())
+
+
+def dit_block_chain_workspace_size(desc: dit_block_desc) -> int:
+    n = C.c_size_t(0)
+    _check(lib().dit_block_chain_workspace_size(C.byref(desc), C.byref(n)))
+    return n.value
+
+
+def dit_block_chain_forward(desc, blocks: Sequence[dit_block_weights], x, cond, rope_cos, rope_sin, ws,
+                            stream=None, side_stream=None, ws_bytes=None):
+    arr = (dit_block_weights * len(blocks))(*blocks)
+    nb = _nbytes(ws) if ws_bytes is None else ws_bytes
+    _check(lib().dit_block_chain_forward(C.byref(desc), arr, len(blocks), _p(x), _p(cond), _p(rope_cos),
+                                         _p(rope_sin), _p(ws), nb, _stream(stream),
+                                         None if side_stream is None else _stream(side_stream)))
 
 
 def make_model(desc: dit_block_desc, blocks: Sequence[dit_block_weights], latent_dim: int, edges: Dict[str, Any]):

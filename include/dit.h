@@ -205,6 +205,28 @@ int dit_block_forward_noalloc(const dit_block_desc *desc, const dit_block_weight
                               void *out, void *stream);
 size_t dit_block_forward_noalloc_max_bytes(void);
 
+/* A chain of n_blocks blocks of one shape applied in place to x, all with the
+ * same conditioning cond: x <- block_{n-1}(... block_0(x, cond) ..., cond)
+ * ([ERNIE] §IV: the layers of one denoising step; blocks[l] is a HOST array of
+ * weight sets).  When the blocks carry their own AdaLN linear (w_ada / b_ada
+ * differ between blocks) and side_stream is a second stream, the modulation
+ * GEMV of block l + 1, which is bound by HBM bandwidth, is issued on
+ * side_stream while block l runs on `stream` ("layer pipelining", [ERNIE] §IX
+ * headroom item 4); events order the two streams (side_stream first waits for
+ * the work already on `stream`, and `stream` waits for each GEMV before the
+ * block that reads it), so on return every write of the call is ordered on
+ * `stream`.  With one shared AdaLN linear the modulation is computed once;
+ * side_stream NULL (or equal to stream) runs everything on `stream`.
+ * x: device [batch*seq, hidden] of desc->x_dtype; cond, rope tables as
+ * dit_block_forward; ws: at least dit_block_chain_workspace_size bytes (the
+ * block workspace plus a second modulation buffer).  Results are bitwise
+ * those of n_blocks dit_block_forward calls with out == x.  The call creates
+ * two HIP events (host-side objects) and destroys them before returning. */
+int dit_block_chain_workspace_size(const dit_block_desc *desc, size_t *bytes);
+int dit_block_chain_forward(const dit_block_desc *desc, const dit_block_weights *blocks, int32_t n_blocks,
+                            void *x, const float *cond, const float *rope_cos, const float *rope_sin,
+                            void *ws, size_t ws_bytes, void *stream, void *side_stream);
+
 /* ------------------------------------------------------------------------ */
 /* Stack step and denoising loop                                             */
 /* ------------------------------------------------------------------------ */

@@ -386,3 +386,27 @@ def test_noalloc_block_validation_before_device():
         with pytest.raises(N.DitError) as e:
             N.dit_block_forward_noalloc(d, a["w"], a["x"], a["cond"], FAKE, FAKE, a["out"])
         assert e.value.status == st, (kw, e.value)
+
+
+def test_block_chain_validation_before_device():
+    d = _desc()
+    need = N.dit_block_chain_workspace_size(d)
+    assert need > N.dit_block_workspace_size(d)            # plus a second modulation buffer
+    w = [_weights(), _weights(w_ada=FAKE + (1 << 22))]
+    far = 1 << 40
+    with pytest.raises(N.DitError) as e:
+        N.dit_block_chain_forward(d, [], FAKE, FAKE, FAKE, FAKE, far, stream=0, ws_bytes=need)
+    assert e.value.status == N.DIT_ERR_INVALID_ARG
+    with pytest.raises(N.DitError) as e:
+        N.dit_block_chain_forward(d, w, FAKE, FAKE, FAKE, FAKE, far, stream=0, ws_bytes=need - 1)
+    assert e.value.status == N.DIT_ERR_WORKSPACE
+    with pytest.raises(N.DitError) as e:
+        N.dit_block_chain_forward(d, [w[0], _weights(w_o=None)], FAKE, FAKE, FAKE, FAKE, far, stream=0, ws_bytes=need)
+    assert e.value.status == N.DIT_ERR_INVALID_ARG
+    with pytest.raises(N.DitError) as e:
+        N.dit_block_chain_forward(d, w, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0, ws_bytes=need)   # ws overlaps x
+    assert e.value.status == N.DIT_ERR_INVALID_ARG
+    if not (os.path.exists("/dev/kfd") and os.access("/dev/kfd", os.R_OK)):
+        with pytest.raises(N.DitError) as e:
+            N.dit_block_chain_forward(d, w, FAKE, FAKE, FAKE, FAKE, far, stream=0, side_stream=8, ws_bytes=need)
+        assert e.value.status == N.DIT_ERR_NO_DEVICE
