@@ -352,6 +352,59 @@ def canary_tflops(reps=10):
     return round(2 * 4096 ** 3 / (e0.elapsed_time(e1) * 1e-3 / reps) / 1e12, 1)
 
 
+class ClockSampler:
+    """Samples the GPU's shader clock (MHz) with rocm-smi every `period` s in a
+    background thread while the timed region runs (a child process, the GPU
+    itself is not touched): MFMA-heavy steps run below the 2.4 GHz the peak
+    assumes, and the sample separates the part's power limit from kernel
+    quality."""
+
+    def __init__(self, period=0.25):
+        import threading
+        self.period, self.samples, self.error = period, [], None
+        self._stop = threading.Event()
+        self._t = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def read_mhz():
+        import re
+        import subprocess
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=10)
+        d = json.loads(r.stdout)
+        for card in d.values():
+            if isinstance(card, dict):
+                for k, v in card.items():
+                    if "sclk" in k.lower():
+                        m = re.search(r"(\d+)\s*Mhz", str(v), re.I)
+                        if m:
+                            return int(m.group(1))
+        raise RuntimeError("no sclk field in rocm-smi output")
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self.read_mhz())
+            except Exception as e:          # tool missing or output changed: report, never fail the bench
+                self.error = f"{type(e).__name__}: {e}"[:200]
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._t.join(timeout=15)
+
+    def summary(self):
+        if not self.samples:
+            return {"samples": 0, "error": self.error}
+        v = sorted(self.samples)
+        return {"samples": len(v), "median_mhz": v[len(v) // 2], "min_mhz": v[0], "max_mhz": v[-1],
+                "source": "rocm-smi --showclocks (sclk), sampled during the timed steps"}
+
+
 def host_info():
     model = "unknown"
     try:
@@ -437,6 +490,8 @@ def main():
     ap.add_argument("--steps", type=int, default=8)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--trace", default=None,
+                    help="also write the library's Chrome trace of one extra (untimed) denoising step to this path")
     ap.add_argument("--counters", action="store_true",
                     help="one block's weights; each block kernel a few times plus a 512 MiB copy (for rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -490,16 +545,37 @@ def main():
     torch.cuda.synchronize()
     per = []
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    t0 = time.perf_counter()
-    ev[0].record()
-    for i in range(args.steps):
-        one_step(args.warmup + i)
-        ev[i + 1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler() as clocks:
+        t0 = time.perf_counter()
+        ev[0].record()
+        for i in range(args.steps):
+            one_step(args.warmup + i)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
     ms = wall * 1000.0 / args.steps
     assert torch.isfinite(lat).all().item(), "non-finite latent"
+
+    # one more (untimed) step under the library's tracer: the per-operation
+    # breakdown of a step from device events around every launch
+    import tempfile
+    trace_path = args.trace or os.path.join(tempfile.mkdtemp(prefix="dit_trace_"), "step.json")
+    N.dit_trace_begin(1 << 12)
+    try:
+        one_step(args.warmup + args.steps)
+    finally:
+        N.dit_trace_end(trace_path)
+    breakdown = {}
+    for e in json.load(open(trace_path))["traceEvents"]:
+        b = breakdown.setdefault(e["name"], {"launches": 0, "us": 0.0})
+        b["launches"] += 1
+        b["us"] += e["dur"]
+    traced_ms = sum(b["us"] for b in breakdown.values()) / 1000.0
+    breakdown = {k: {"launches": v["launches"], "us": round(v["us"], 1), "pct": round(v["us"] / (10.0 * traced_ms), 2)}
+                 for k, v in sorted(breakdown.items(), key=lambda kv: -kv[1]["us"])}
+    print(f"[bench] traced step: {traced_ms:.3f} ms in {sum(v['launches'] for v in breakdown.values())} launches",
+          file=sys.stderr, flush=True)
 
     # the same steps replayed from the library's per-step HIP graphs (dit_loop_*)
     loop = R.DeviceLoop(stack, lat, cos, sin, I.STACK_STEPS, I.STACK_SHIFT)
@@ -594,6 +670,7 @@ def main():
                    "head_dim": cfg.head_dim, "ffn": cfg.ffn, "steps_per_loop": I.STACK_STEPS},
         "mfma_util_pct": round(100.0 * util, 2),
         "step_tflop": round(flops / 1e12, 3),
+        "sclk_during_steps": clocks.summary(),
         "step_ms_events": {"median": round(float(np.median(per)), 3), "min": round(min(per), 3),
                            "max": round(max(per), 3)},
         # the loop executor: each step replayed as one HIP graph (timestep embedding + 36 blocks + Euler)
@@ -601,6 +678,8 @@ def main():
         "graph_step_ms_events": {"median": round(float(np.median(gper)), 3), "min": round(min(gper), 3),
                                  "max": round(max(gper), 3)},
         "roofline": roof,
+        # one step through the library's tracer (DIT_TRACE): device time per operation
+        "step_breakdown": {"traced_ms": round(traced_ms, 3), "ops": breakdown},
         "kernels": kern,
         # dit_block_forward at 4096 tokens and on the joint text + image sequence (4096 + 74 tokens)
         "block": blocks,

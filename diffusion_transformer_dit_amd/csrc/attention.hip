@@ -39,6 +39,7 @@
 // sum_c 2^((m_c - M) s) l_c with M = max_c m_c (the split-KV form of the same
 // online softmax).
 #include "common.h"
+#include "trace.h"
 
 namespace dit {
 
@@ -442,6 +443,8 @@ size_t attention_split_bytes(int batch, int heads, int head_dim, int nsplit) {
 hipError_t launch_flash_attention(const bf16 *q, const bf16 *k, const bf16 *vt, bf16 *out, int batch, int seq,
                                   int seq_pad, int heads, int kv_heads, int head_dim, int nsplit, void *part,
                                   hipStream_t s) {
+    TraceScope trace_(s, "flash_attention");
+    if (trace_.on()) trace_.args("B=%d S=%d H=%d Hkv=%d hd=%d nsplit=%d", batch, seq, heads, kv_heads, head_dim, nsplit);
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)head_dim);
     const int nt = (seq + 63) / 64;
     int n_full_qt = (seq + 255) / 256, ct = nt;
@@ -580,6 +583,8 @@ void attn_f32_kernel(const float *__restrict__ Q, const float *__restrict__ K, c
 
 hipError_t launch_flash_attention_f32(const float *q, const float *k, const float *vt, float *out, int batch,
                                       int seq, int seq_pad, int heads, int kv_heads, int head_dim, hipStream_t s) {
+    TraceScope trace_(s, "attn_f32");
+    if (trace_.on()) trace_.args("B=%d S=%d H=%d Hkv=%d hd=%d", batch, seq, heads, kv_heads, head_dim);
     if (seq_pad % 64 || seq_pad < seq) return hipErrorInvalidValue;
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)head_dim);
     const dim3 grid((unsigned)((seq + 63) / 64), (unsigned)heads, (unsigned)batch);

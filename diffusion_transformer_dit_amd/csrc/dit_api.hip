@@ -109,8 +109,10 @@ int check_desc(const dit_block_desc *d) {
     if (d->batch <= 0 || d->seq <= 0 || d->hidden <= 0 || d->heads <= 0 || d->kv_heads <= 0 ||
         d->head_dim <= 0 || d->ffn <= 0 || d->cond_dim < 0)
         return fail(DIT_ERR_INVALID_ARG, "dimensions must be positive (cond_dim >= 0)");
-    if (d->heads * d->head_dim != d->hidden)
-        return fail(DIT_ERR_INVALID_ARG, "heads * head_dim (%d) != hidden (%d)", d->heads * d->head_dim, d->hidden);
+    // products in 64 bits: any of the fields may be near INT32_MAX here
+    if ((int64_t)d->heads * d->head_dim != d->hidden)
+        return fail(DIT_ERR_INVALID_ARG, "heads * head_dim (%lld) != hidden (%d)",
+                    (long long)d->heads * d->head_dim, d->hidden);
     if (d->heads % d->kv_heads != 0)
         return fail(DIT_ERR_INVALID_ARG, "heads (%d) not a multiple of kv_heads (%d)", d->heads, d->kv_heads);
     if (!(d->eps > 0.f) || !isfinite(d->eps)) return fail(DIT_ERR_INVALID_ARG, "eps must be positive and finite");
@@ -129,7 +131,7 @@ int check_desc(const dit_block_desc *d) {
     if (d->hidden % 256) return fail(DIT_ERR_UNSUPPORTED, "hidden must be a multiple of 256");
     if (d->hidden > 8192) return fail(DIT_ERR_UNSUPPORTED, "hidden must be <= 8192");
     if (d->ffn % 128) return fail(DIT_ERR_UNSUPPORTED, "ffn must be a multiple of 128");
-    if (((d->heads + 2 * d->kv_heads) * d->head_dim) % 256)
+    if ((((int64_t)d->heads + 2 * (int64_t)d->kv_heads) * d->head_dim) % 256)
         return fail(DIT_ERR_UNSUPPORTED, "(heads + 2 kv_heads) * head_dim must be a multiple of 256");
     if (d->cond_dim % 8) return fail(DIT_ERR_UNSUPPORTED, "cond_dim must be a multiple of 8");
     if (d->fmt == DIT_FMT_W8A8_H256 && (d->ffn % 256 || !quantize_h256_supported(d->ffn)))

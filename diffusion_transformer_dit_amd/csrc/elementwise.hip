@@ -9,6 +9,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "trace.h"
 
 namespace dit {
 
@@ -79,6 +80,8 @@ void adaln_gemv_kernel(const TW *__restrict__ W, const float *__restrict__ b, co
 
 hipError_t launch_adaln_gemv(const void *w, int w_f32, const float *b, const float *c, int out_dim, int in_dim,
                              int silu_input, float *m, hipStream_t s) {
+    TraceScope trace_(s, "adaln_gemv");
+    if (trace_.on()) trace_.args("out=%d in=%d silu=%d", out_dim, in_dim, silu_input);
     const int waves = (out_dim + kGemvRows - 1) / kGemvRows;
     if (w_f32)
         hipLaunchKernelGGL(adaln_gemv_kernel<float>, dim3((waves + 3) / 4), dim3(256), 0, s, (const float *)w, b, c,
@@ -204,6 +207,8 @@ static hipError_t ln_modulate_typed(const TX *x, int64_t rows, int dim, const fl
 
 hipError_t launch_ln_modulate(const void *x, int x_f32, int64_t rows, int dim, int rms, const float *shift,
                               const float *scale, int mode, float eps, bf16 *h, hipStream_t s) {
+    TraceScope trace_(s, "ln_modulate");
+    if (trace_.on()) trace_.args("rows=%lld dim=%d x_f32=%d", (long long)rows, dim, x_f32);
     if (dim % 256 != 0) return hipErrorInvalidValue;
     if (x_f32)
         return rms ? ln_modulate_typed<float, bf16, true>((const float *)x, rows, dim, shift, scale, mode, eps, h, s)
@@ -214,6 +219,8 @@ hipError_t launch_ln_modulate(const void *x, int x_f32, int64_t rows, int dim, i
 
 hipError_t launch_ln_modulate_f32(const float *x, int64_t rows, int dim, int rms, const float *shift,
                                   const float *scale, int mode, float eps, float *h, hipStream_t s) {
+    TraceScope trace_(s, "ln_modulate_f32");
+    if (trace_.on()) trace_.args("rows=%lld dim=%d", (long long)rows, dim);
     if (dim % 256 != 0) return hipErrorInvalidValue;
     return rms ? ln_modulate_typed<float, float, true>(x, rows, dim, shift, scale, mode, eps, h, s)
                : ln_modulate_typed<float, float, false>(x, rows, dim, shift, scale, mode, eps, h, s);
@@ -239,6 +246,8 @@ void euler_kernel(float *__restrict__ lat, const float *__restrict__ v, int64_t 
 }
 
 hipError_t launch_euler(float *latent, const float *v, int64_t n, float dsigma, hipStream_t s) {
+    TraceScope trace_(s, "euler_update");
+    if (trace_.on()) trace_.args("n=%lld", (long long)n);
     const int64_t n4 = (n >> 2) + 1;
     const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 4096);
     hipLaunchKernelGGL(euler_kernel, dim3(blocks), dim3(256), 0, s, latent, v, n, dsigma);
@@ -258,6 +267,8 @@ __global__ void timestep_embedding_kernel(float t, int half, float *__restrict__
 }
 
 hipError_t launch_timestep_embedding(float t, int dim, float *out, hipStream_t s) {
+    TraceScope trace_(s, "timestep_embedding");
+    if (trace_.on()) trace_.args("dim=%d", dim);
     const int half = dim / 2;
     hipLaunchKernelGGL(timestep_embedding_kernel, dim3((half + 255) / 256), dim3(256), 0, s, t, half, out);
     return hipGetLastError();
@@ -273,6 +284,8 @@ void f32_to_bf16_kernel(const float *__restrict__ x, bf16 *__restrict__ y, int64
 }
 
 hipError_t launch_f32_to_bf16(const float *x, bf16 *y, int64_t n, hipStream_t s) {
+    TraceScope trace_(s, "f32_to_bf16");
+    if (trace_.on()) trace_.args("n=%lld", (long long)n);
     const int blocks = (int)std::min<int64_t>((n + 255) / 256, 8192);
     hipLaunchKernelGGL(f32_to_bf16_kernel, dim3(blocks), dim3(256), 0, s, x, y, n);
     return hipGetLastError();
@@ -295,6 +308,8 @@ void vt_pad_zero_kernel(TV *__restrict__ vt, int rows, int seq, int seq_pad) {
 }
 
 hipError_t launch_vt_pad_zero(void *vt, int vt_f32, int rows, int seq, int seq_pad, hipStream_t s) {
+    TraceScope trace_(s, "vt_pad_zero");
+    if (trace_.on()) trace_.args("rows=%d seq=%d pad=%d", rows, seq, seq_pad);
     const int64_t n = (int64_t)rows * (seq_pad - seq);
     if (n <= 0) return hipSuccess;
     const int blocks = (int)std::min<int64_t>((n + 255) / 256, 4096);

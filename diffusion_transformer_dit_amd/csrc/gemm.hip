@@ -25,6 +25,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "trace.h"
 
 namespace dit {
 
@@ -1053,17 +1054,23 @@ static hipError_t residual_any(const void *a, const void *w, int64_t M, int N, i
 hipError_t launch_gemm_residual(const bf16 *a, const bf16 *w, int64_t M, int N, int K, const void *resid,
                                 int resid_f32, const float *gate, int gate_fn, const float *bias, void *out,
                                 int out_f32, hipStream_t s) {
+    TraceScope trace_(s, "gemm_gated_residual");
+    if (trace_.on()) trace_.args("M=%lld N=%d K=%d", (long long)M, N, K);
     return residual_any(a, w, M, N, K, resid, resid_f32, gate, gate_fn, bias, out, out_f32, NoScales{}, s);
 }
 
 hipError_t launch_gemm_residual_f32(const float *a, const float *w, int64_t M, int N, int K, const float *resid,
                                     const float *gate, int gate_fn, const float *bias, float *out, hipStream_t s) {
+    TraceScope trace_(s, "gemm_gated_residual_f32");
+    if (trace_.on()) trace_.args("M=%lld N=%d K=%d", (long long)M, N, K);
     return residual_any(a, w, M, N, K, resid, 1, gate, gate_fn, bias, out, 1, F32Ops{}, s);
 }
 
 hipError_t launch_gemm_residual_q8(const int8_t *a, const float *a_scale, const int8_t *w, const float *w_scale,
                                    int64_t M, int N, int K, const void *resid, int resid_f32, const float *gate,
                                    int gate_fn, const float *bias, void *out, int out_f32, hipStream_t s) {
+    TraceScope trace_(s, "gemm_gated_residual_w8a8");
+    if (trace_.on()) trace_.args("M=%lld N=%d K=%d", (long long)M, N, K);
     return residual_any(a, w, M, N, K, resid, resid_f32, gate, gate_fn, bias, out, out_f32,
                         Scales{a_scale, w_scale}, s);
 }
@@ -1107,16 +1114,22 @@ static hipError_t swiglu_any(const void *a, const void *w, int64_t M, int F, int
 
 hipError_t launch_gemm_swiglu(const bf16 *a, const bf16 *w, int64_t M, int F, int K, int act, bf16 *u,
                               hipStream_t s) {
+    TraceScope trace_(s, "gemm_swiglu");
+    if (trace_.on()) trace_.args("M=%lld F=%d K=%d", (long long)M, F, K);
     return swiglu_any(a, w, M, F, K, act, u, NoScales{}, s);
 }
 
 hipError_t launch_gemm_swiglu_f32(const float *a, const float *w, int64_t M, int F, int K, int act, float *u,
                                   hipStream_t s) {
+    TraceScope trace_(s, "gemm_swiglu_f32");
+    if (trace_.on()) trace_.args("M=%lld F=%d K=%d", (long long)M, F, K);
     return swiglu_any(a, w, M, F, K, act, u, F32Ops{}, s);
 }
 
 hipError_t launch_gemm_swiglu_q8(const int8_t *a, const float *a_scale, const int8_t *w, const float *w_scale,
                                  int64_t M, int F, int K, int act, bf16 *u, hipStream_t s) {
+    TraceScope trace_(s, "gemm_swiglu_w8a8");
+    if (trace_.on()) trace_.args("M=%lld F=%d K=%d", (long long)M, F, K);
     return swiglu_any(a, w, M, F, K, act, u, Scales{a_scale, w_scale}, s);
 }
 
@@ -1139,16 +1152,22 @@ static hipError_t qkv_any(const void *h, const void *w, int64_t M, int N, int K,
 
 hipError_t launch_gemm_qkv(const bf16 *h, const bf16 *w, int64_t M, int N, int K, const QkvEpiArgs &e,
                            hipStream_t s) {
+    TraceScope trace_(s, "gemm_qkv");
+    if (trace_.on()) trace_.args("M=%lld N=%d K=%d", (long long)M, N, K);
     return qkv_any(h, w, M, N, K, e, NoScales{}, s);
 }
 
 hipError_t launch_gemm_qkv_f32(const float *h, const float *w, int64_t M, int N, int K, const QkvEpiArgs &e,
                                hipStream_t s) {
+    TraceScope trace_(s, "gemm_qkv_f32");
+    if (trace_.on()) trace_.args("M=%lld N=%d K=%d", (long long)M, N, K);
     return qkv_any(h, w, M, N, K, e, F32Ops{}, s);
 }
 
 hipError_t launch_gemm_qkv_q8(const int8_t *h, const float *h_scale, const int8_t *w, const float *w_scale,
                               int64_t M, int N, int K, const QkvEpiArgs &e, hipStream_t s) {
+    TraceScope trace_(s, "gemm_qkv_w8a8");
+    if (trace_.on()) trace_.args("M=%lld N=%d K=%d", (long long)M, N, K);
     return qkv_any(h, w, M, N, K, e, Scales{h_scale, w_scale}, s);
 }
 

@@ -22,6 +22,7 @@
 // moves reach without LDS.  A row length that is not a multiple of 1024 leaves
 // whole 16-lane groups idle (holding zeros) in its last round.
 #include "common.h"
+#include "trace.h"
 
 namespace dit {
 
@@ -210,6 +211,8 @@ bool quantize_h256_supported(int cols) {
 
 hipError_t launch_quantize_h256(const void *x, int x_f32, int64_t rows, int cols, int8_t *q, float *scale,
                                 hipStream_t s) {
+    TraceScope trace_(s, "quantize_h256");
+    if (trace_.on()) trace_.args("rows=%lld cols=%d", (long long)rows, cols);
     if (rows <= 0) return hipSuccess;
     return x_f32 ? quantize_typed((const float *)x, rows, cols, q, scale, s)
                  : quantize_typed((const bf16 *)x, rows, cols, q, scale, s);
@@ -324,6 +327,8 @@ static hipError_t ln_q8_typed(const TX *x, int64_t rows, int dim, const float *s
 
 hipError_t launch_ln_modulate_q8(const void *x, int x_f32, int64_t rows, int dim, int rms, const float *shift,
                                  const float *scale, int mode, float eps, int8_t *q, float *qscale, hipStream_t s) {
+    TraceScope trace_(s, "ln_modulate_h256q");
+    if (trace_.on()) trace_.args("rows=%lld dim=%d", (long long)rows, dim);
     if (rows <= 0) return hipSuccess;
     if (x_f32)
         return rms ? ln_q8_typed<float, true>((const float *)x, rows, dim, shift, scale, mode, eps, q, qscale, s)

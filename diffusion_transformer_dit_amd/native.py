@@ -33,7 +33,7 @@ EXPORTED = (
     "dit_quantize_h256", "dit_ln_modulate_h256q", "dit_gemm_w8a8_gated_residual", "dit_gemm_w8a8_swiglu",
     "dit_qkv_rope_w8a8", "dit_attention_workspace_size", "dit_flash_attention_split", "dit_sigma_embedding",
     "dit_block_forward_noalloc", "dit_block_forward_noalloc_max_bytes", "dit_block_chain_workspace_size",
-    "dit_block_chain_forward",
+    "dit_block_chain_forward", "dit_trace_begin", "dit_trace_end",
 )
 
 
@@ -84,6 +84,8 @@ def lib():
             "dit_block_forward_noalloc_max_bytes": (sz, []),
             "dit_block_chain_workspace_size": (C.c_int, [pd, C.POINTER(sz)]),
             "dit_block_chain_forward": (C.c_int, [pd, pw, i32, vp, vp, vp, vp, vp, sz, vp, vp]),
+            "dit_trace_begin": (C.c_int, [i32]),
+            "dit_trace_end": (C.c_int, [C.c_char_p]),
             "dit_stack_workspace_size": (C.c_int, [pm, C.POINTER(sz)]),
             "dit_stack_step": (C.c_int, [pm, vp, vp, vp, vp, vp, vp, sz, vp]),
             "euler_flowmatch_update": (C.c_int, [vp, vp, i64, f32, f32, vp]),
@@ -119,6 +121,11 @@ def lib():
             f = getattr(L, name)
             f.restype, f.argtypes = res, args
         _lib = L
+        if os.environ.get("DIT_TRACE", "0") not in ("", "0"):
+            # write the trace the library records under DIT_TRACE before the
+            # HIP runtime is torn down (Python's exit handlers run first)
+            import atexit
+            atexit.register(lambda: L.dit_trace_end(None))
     return _lib
 
 
@@ -364,6 +371,14 @@ def dit_qkv_rope_w8a8(desc, h, h_scale, w_qkv, w_scale, q_g, q_b, k_g, k_b, rope
     _check(lib().dit_qkv_rope_w8a8(C.byref(desc), _p(h), _p(h_scale), _p(w_qkv), _p(w_scale), _p(q_g), _p(q_b),
                                    _p(k_g), _p(k_b), _p(rope_cos), _p(rope_sin), _p(q), _p(k), _p(vt),
                                    _stream(stream)))
+
+
+def dit_trace_begin(capacity: int = 1 << 16):
+    _check(lib().dit_trace_begin(int(capacity)))
+
+
+def dit_trace_end(path: Optional[str] = None):
+    _check(lib().dit_trace_end(None if path is None else os.fsencode(path)))
 
 
 def dit_status_string(status: int) -> str:

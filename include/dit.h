@@ -460,6 +460,30 @@ int dit_qkv_rope_w8a8(const dit_block_desc *desc, const void *h, const float *h_
                       void *vt, void *stream);
 
 /* ------------------------------------------------------------------------ */
+/* Tracing                                                                   */
+/* ------------------------------------------------------------------------ */
+
+/* Per-launch GPU times, the per-operation breakdown of a step ([ERNIE] §IX
+ * "Per-Step Latency Breakdown", produced there by a Chrome-trace tracer).
+ * While tracing is on, every kernel launch of the library records a HIP event
+ * on its stream before and after its kernels, with the operation's name and
+ * shape; nothing synchronises while recording, and launches into a stream
+ * that is being captured into a HIP graph are not recorded.
+ * dit_trace_begin: discards earlier records and starts recording at most
+ * `capacity` launches (1 .. 2^24; further launches are counted as dropped).
+ * dit_trace_end: waits for the recorded launches, writes Chrome trace JSON
+ * (one complete "X" event per launch, "tid" = the stream, "ts"/"dur" in
+ * microseconds from dit_trace_begin) to `path` (NULL: the path DIT_TRACE
+ * named), releases the records and stops recording.  DIT_ERR_INVALID_ARG
+ * when not tracing or the file cannot be written.
+ * Environment: DIT_TRACE=<path> (or 1 for ./dit_trace.json) starts tracing at
+ * the library's first launch; DIT_DEBUG_SYNC=1 synchronises the stream after
+ * every launch and prints the first failing operation (debugging only).
+ * Tracing is process-wide; calls from several threads are serialised. */
+int dit_trace_begin(int32_t capacity);
+int dit_trace_end(const char *path);
+
+/* ------------------------------------------------------------------------ */
 const char *dit_status_string(int status);
 const char *dit_last_error(void);
 /* Library version string. */

@@ -410,3 +410,16 @@ def test_block_chain_validation_before_device():
         with pytest.raises(N.DitError) as e:
             N.dit_block_chain_forward(d, w, FAKE, FAKE, FAKE, FAKE, far, stream=0, side_stream=8, ws_bytes=need)
         assert e.value.status == N.DIT_ERR_NO_DEVICE
+
+
+def test_trace_validation():
+    with pytest.raises(N.DitError) as e:
+        N.dit_trace_end("/tmp/never.json")            # not tracing
+    assert e.value.status == N.DIT_ERR_INVALID_ARG
+    with pytest.raises(N.DitError) as e:
+        N.dit_trace_begin(0)
+    assert e.value.status == N.DIT_ERR_INVALID_ARG
+    if not (os.path.exists("/dev/kfd") and os.access("/dev/kfd", os.R_OK)):
+        with pytest.raises(N.DitError) as e:
+            N.dit_trace_begin(16)
+        assert e.value.status == N.DIT_ERR_NO_DEVICE
