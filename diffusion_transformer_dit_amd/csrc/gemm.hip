@@ -369,6 +369,217 @@ void gemm_kernel(const void *__restrict__ A, const void *__restrict__ W, int M, 
 
 
 // ---------------------------------------------------------------------------
+// 4-wave 256 x 256 bf16 tile for the gated-residual and SwiGLU GEMMs: one wave
+// per SIMD with a 128 x 128 wave tile (8 x 8 MFMA blocks of 16 x 16).  Every
+// K fragment read from LDS then feeds 8 MFMAs, so the LDS read traffic per
+// MFMA is two thirds of the 8-wave tile's (0.25 instead of 0.375 fragment
+// reads per MFMA), which is what bounds the 8-wave loop.  The 256 fp32
+// accumulators of a wave fill its AGPRs.  With a single wave per SIMD nothing
+// else hides a gap in its MFMA stream, so the K loop is written as inline
+// assembly blocks of 16 MFMAs (one pair of A row blocks against the 8 B column
+// blocks), each with its share of the other work between the MFMAs:
+//   k-step 0 of a stage   : the LDS reads of four fragments of k-step 1;
+//   k-step 1, first block : 8 MFMAs, then the wait for the next stage's
+//                           copies and the workgroup barrier (the matrix pipe
+//                           still busy), then the next stage's fragment reads
+//                           and four buffer->LDS copies of the stage after it;
+//   k-step 1, other blocks: four reads and four copies, one of each per four
+//                           MFMAs (issued together the copies slow the loop).
+// Every block waits for its own LDS reads before it ends, so no load that
+// writes a register is in flight outside a block; the buffer->LDS copies
+// write no register and are counted by the vmcnt wait before the barrier.
+// The accumulators stay in AGPRs: the compiler never moves them, since every
+// block takes them as tied operands.
+// ---------------------------------------------------------------------------
+using Tile4w = Tile<256, 256, 2, 2>;   // BK 64, 2 LDS stages of 64 KiB
+
+#define DIT_MF(c, a, b) "v_mfma_f32_16x16x32_bf16 %[" #c "], %[" #a "], %[" #b "], %[" #c "]\n\t"
+#define DIT_RD(dst, base, off) "ds_read_b128 %[" #dst "], %[" #base "] offset:%[" #off "]\n\t"
+// copy j of a block: M0 = LDS destination (the add also sets SCC, declared clobbered)
+#define DIT_CP(j) "s_add_u32 m0, %[lb], %[d" #j "]\n\t"
+#define DIT_LD(j) "buffer_load_dwordx4 %[v" #j "], %[rs], %[so] offen lds\n\t"
+// operands: accumulators of A row blocks i0, i0 + 1; the next k-step's
+// fragments written by the block (A i0, i0 + 1 and B i0, i0 + 1); the current
+// fragments; the LDS addresses of the next fragments (fragment r at r * 2048)
+#define DIT_K4_OPERANDS(acc_, fa_, fb_, na_, nb_, i0, adA, adB)                                            \
+    [c00] "+a"(acc_[i0][0]), [c01] "+a"(acc_[i0][1]), [c02] "+a"(acc_[i0][2]), [c03] "+a"(acc_[i0][3]),    \
+        [c04] "+a"(acc_[i0][4]), [c05] "+a"(acc_[i0][5]), [c06] "+a"(acc_[i0][6]),                         \
+        [c07] "+a"(acc_[i0][7]), [c10] "+a"(acc_[i0 + 1][0]), [c11] "+a"(acc_[i0 + 1][1]),                 \
+        [c12] "+a"(acc_[i0 + 1][2]), [c13] "+a"(acc_[i0 + 1][3]), [c14] "+a"(acc_[i0 + 1][4]),             \
+        [c15] "+a"(acc_[i0 + 1][5]), [c16] "+a"(acc_[i0 + 1][6]), [c17] "+a"(acc_[i0 + 1][7]),             \
+        [na0] "=&v"(na_[i0]), [na1] "=&v"(na_[i0 + 1]), [nb0] "=&v"(nb_[i0]), [nb1] "=&v"(nb_[i0 + 1])     \
+        : [a0] "v"(fa_[i0]), [a1] "v"(fa_[i0 + 1]), [b0] "v"(fb_[0]), [b1] "v"(fb_[1]), [b2] "v"(fb_[2]),  \
+          [b3] "v"(fb_[3]), [b4] "v"(fb_[4]), [b5] "v"(fb_[5]), [b6] "v"(fb_[6]), [b7] "v"(fb_[7]),         \
+          [pa] "v"(adA), [pb] "v"(adB), [oa0] "i"((i0) * 2048), [oa1] "i"((i0 + 1) * 2048)
+// copies: buffer resource, LDS base (SGPR), K byte offset (SGPR), the four
+// per-lane global offsets and the first LDS offset (then + 4 KiB each)
+#define DIT_K4_COPIES(rsrc_, ldsb_, soff_, vo_, doff_)                                                     \
+    , [rs] "s"(rsrc_), [lb] "s"(ldsb_), [so] "s"(soff_), [v0] "v"(vo_[0]), [v1] "v"(vo_[1]),                \
+        [v2] "v"(vo_[2]), [v3] "v"(vo_[3]), [d0] "i"(doff_), [d1] "i"((doff_) + 4096),                     \
+        [d2] "i"((doff_) + 8192), [d3] "i"((doff_) + 12288)
+
+// k-step 0 block: 16 MFMAs with four fragment reads
+#define DIT_K4_STEP(acc_, fa_, fb_, na_, nb_, i0, adA, adB)                                                \
+    asm volatile(DIT_RD(na0, pa, oa0) DIT_MF(c00, a0, b0) DIT_RD(na1, pa, oa1) DIT_MF(c01, a0, b1)         \
+                 DIT_RD(nb0, pb, oa0) DIT_MF(c02, a0, b2) DIT_RD(nb1, pb, oa1) DIT_MF(c03, a0, b3)         \
+                 DIT_MF(c04, a0, b4) DIT_MF(c05, a0, b5) DIT_MF(c06, a0, b6) DIT_MF(c07, a0, b7)           \
+                 DIT_MF(c10, a1, b0) DIT_MF(c11, a1, b1) DIT_MF(c12, a1, b2) DIT_MF(c13, a1, b3)           \
+                 DIT_MF(c14, a1, b4) DIT_MF(c15, a1, b5) DIT_MF(c16, a1, b6) DIT_MF(c17, a1, b7)           \
+                 "s_waitcnt lgkmcnt(0)"                                                                    \
+                 : DIT_K4_OPERANDS(acc_, fa_, fb_, na_, nb_, i0, adA, adB)                                 \
+                 : "memory")
+// first k-step 1 block: 8 MFMAs, the next stage's wait and the barrier, then
+// 8 MFMAs with four reads and four copies
+#define DIT_K4_STEP_BARRIER(acc_, fa_, fb_, na_, nb_, i0, adA, adB, rsrc_, ldsb_, soff_, vo_, doff_)       \
+    asm volatile(DIT_MF(c00, a0, b0) DIT_MF(c01, a0, b1) DIT_MF(c02, a0, b2) DIT_MF(c03, a0, b3)           \
+                 DIT_MF(c04, a0, b4) DIT_MF(c05, a0, b5) DIT_MF(c06, a0, b6) DIT_MF(c07, a0, b7)           \
+                 "s_waitcnt vmcnt(0)\n\ts_barrier\n\t"                                                     \
+                 DIT_RD(na0, pa, oa0) DIT_CP(0) DIT_MF(c10, a1, b0) DIT_LD(0) DIT_MF(c11, a1, b1)          \
+                 DIT_RD(na1, pa, oa1) DIT_CP(1) DIT_MF(c12, a1, b2) DIT_LD(1) DIT_MF(c13, a1, b3)          \
+                 DIT_RD(nb0, pb, oa0) DIT_CP(2) DIT_MF(c14, a1, b4) DIT_LD(2) DIT_MF(c15, a1, b5)          \
+                 DIT_RD(nb1, pb, oa1) DIT_CP(3) DIT_MF(c16, a1, b6) DIT_LD(3) DIT_MF(c17, a1, b7)          \
+                 "s_waitcnt lgkmcnt(0)"                                                                    \
+                 : DIT_K4_OPERANDS(acc_, fa_, fb_, na_, nb_, i0, adA, adB)                                 \
+                     DIT_K4_COPIES(rsrc_, ldsb_, soff_, vo_, doff_)                                        \
+                 : "memory", "m0", "scc")
+// other k-step 1 blocks: one read and one copy per four MFMAs
+#define DIT_K4_STEP_COPY(acc_, fa_, fb_, na_, nb_, i0, adA, adB, rsrc_, ldsb_, soff_, vo_, doff_)          \
+    asm volatile(DIT_MF(c00, a0, b0) DIT_RD(na0, pa, oa0) DIT_MF(c01, a0, b1) DIT_CP(0)                    \
+                 DIT_MF(c02, a0, b2) DIT_LD(0) DIT_MF(c03, a0, b3)                                         \
+                 DIT_MF(c04, a0, b4) DIT_RD(na1, pa, oa1) DIT_MF(c05, a0, b5) DIT_CP(1)                    \
+                 DIT_MF(c06, a0, b6) DIT_LD(1) DIT_MF(c07, a0, b7)                                         \
+                 DIT_MF(c10, a1, b0) DIT_RD(nb0, pb, oa0) DIT_MF(c11, a1, b1) DIT_CP(2)                    \
+                 DIT_MF(c12, a1, b2) DIT_LD(2) DIT_MF(c13, a1, b3)                                         \
+                 DIT_MF(c14, a1, b4) DIT_RD(nb1, pb, oa1) DIT_MF(c15, a1, b5) DIT_CP(3)                    \
+                 DIT_MF(c16, a1, b6) DIT_LD(3) DIT_MF(c17, a1, b7)                                         \
+                 "s_waitcnt lgkmcnt(0)"                                                                    \
+                 : DIT_K4_OPERANDS(acc_, fa_, fb_, na_, nb_, i0, adA, adB)                                 \
+                     DIT_K4_COPIES(rsrc_, ldsb_, soff_, vo_, doff_)                                        \
+                 : "memory", "m0", "scc")
+
+template <class T, class RowMap, class Epi>
+__global__ __launch_bounds__(256, 1)
+void gemm4_kernel(const void *__restrict__ A, const void *__restrict__ W, int M, int K, int w_rows, int tiles_m,
+                  int tiles_n, RowMap rowmap, Epi epi, int m_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    static_assert(T::kWaves == 4 && T::TM == 8 && T::TN == 8 && T::ES == 2 && T::NS == 2 && T::BK == 64 &&
+                  T::kALoads == 8 && T::kBLoads == 8 && T::kStageBytes == 65536, "the 4-wave 256 x 256 bf16 tile");
+    static_assert(Epi::template lds_bytes<T>() <= T::NS * T::kStageBytes, "epilogue LDS");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[T::NS * T::kStageBytes];
+
+    int tm, tn;
+    tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = m_base + tm * T::BM;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / T::WN, wn = wave % T::WN;
+    const int l16 = lane & 15, lq = lane >> 4;
+
+    // Copies as in gemm_kernel: copy q (0-7: A rows, 8-15: W rows) of wave w
+    // moves tile rows 8 (4 q + w) .. + 7 into 1 KiB of its stage.
+    const uint32_t a_bytes = (uint32_t)M * (uint32_t)K * 2u, w_bytes = (uint32_t)w_rows * (uint32_t)K * 2u;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, a_bytes);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(W, w_bytes);
+    const int lr = lane / T::kChunks, ls = lane % T::kChunks;
+    uint32_t a_off[8], b_off[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int r = (q * 4 + wave) * T::kRowsPerLoad + lr;
+        a_off[q] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)K * 2u + (uint32_t)((ls ^ T::swz(r)) << 4);
+        b_off[q] = (uint32_t)rowmap(tn, r) * (uint32_t)K * 2u + (uint32_t)((ls ^ T::swz(r)) << 4);
+    }
+    // the same two buffer resources as plain dwords for the copies inside the
+    // asm blocks: base address (48 bits), no stride, size in bytes, format word
+    typedef int int4v __attribute__((ext_vector_type(4)));
+    const uint64_t pa64 = (uint64_t)(uintptr_t)A, pw64 = (uint64_t)(uintptr_t)W;
+    const int4v ra4 = {(int)(uint32_t)pa64, (int)((pa64 >> 32) & 0xffff), (int)a_bytes, 0x00020000};
+    const int4v rw4 = {(int)(uint32_t)pw64, (int)((pw64 >> 32) & 0xffff), (int)w_bytes, 0x00020000};
+    const uint32_t va[2][4] = {{a_off[0], a_off[1], a_off[2], a_off[3]}, {a_off[4], a_off[5], a_off[6], a_off[7]}};
+    const uint32_t vb[2][4] = {{b_off[0], b_off[1], b_off[2], b_off[3]}, {b_off[4], b_off[5], b_off[6], b_off[7]}};
+
+    floatx4 acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // LDS byte addresses of this lane's fragments: stage s, k-step kk (chunk
+    // kk * 4 + lq of the 128-byte row), fragment r at + r * 2048 (16 rows on);
+    // the swizzle of rows base + 16 r + l16 depends on l16 only
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
+    const int swl = (l16 >> 1) & 7;
+    uint32_t adA[2][2], adB[2][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const uint32_t col = (uint32_t)(((kk * 4 + lq) ^ swl) << 4);
+            adA[s][kk] = lds0 + s * T::kStageBytes + (uint32_t)(wm * 128 + l16) * 128u + col;
+            adB[s][kk] = lds0 + s * T::kStageBytes + T::BM * 128u + (uint32_t)(wn * 128 + l16) * 128u + col;
+        }
+
+    const int KT = K / T::BK;
+    // prologue (compiled copies): K tiles 0 and 1 in flight, tile 0 landed, its
+    // k-step 0 fragments read
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        uint8_t *base = smem + t * T::kStageBytes;
+        const uint32_t kb = (uint32_t)(min(t, KT - 1) * T::BK) * 2u;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(base + (q * 4 + wave) * 1024), 16, a_off[q], kb,
+                                                     0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rw, (lds_void *)(base + T::BM * T::kRowBytes + (q * 4 + wave) * 1024), 16, b_off[q], kb, 0, 0);
+        }
+    }
+    wait_vmcnt<16>();
+    barrier_only();
+    bf16x8 fa[8], fb[8], na[8], nb[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        fa[r] = *(const bf16x8 *)(smem + adA[0][0] - lds0 + r * 2048);
+        fb[r] = *(const bf16x8 *)(smem + adB[0][0] - lds0 + r * 2048);
+    }
+
+    for (int kt = 0; kt < KT; ++kt) {
+        const int cur = kt & 1, nxt = cur ^ 1;
+        // k-step 0 of tile kt (fa, fb) || reads of its k-step 1
+        DIT_K4_STEP(acc, fa, fb, na, nb, 0, adA[cur][1], adB[cur][1]);
+        DIT_K4_STEP(acc, fa, fb, na, nb, 2, adA[cur][1], adB[cur][1]);
+        DIT_K4_STEP(acc, fa, fb, na, nb, 4, adA[cur][1], adB[cur][1]);
+        DIT_K4_STEP(acc, fa, fb, na, nb, 6, adA[cur][1], adB[cur][1]);
+        // k-step 1 of tile kt (na, nb) || after the barrier (tile kt + 1 has
+        // landed in stage nxt and every wave is done with stage cur): reads of
+        // k-step 0 of tile kt + 1, copies of tile kt + 2 into stage cur
+        const uint32_t lb = (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds0 + cur * T::kStageBytes + wave * 1024));
+        const uint32_t kb = (uint32_t)__builtin_amdgcn_readfirstlane(min(kt + 2, KT - 1) * T::BK * 2);
+        DIT_K4_STEP_BARRIER(acc, na, nb, fa, fb, 0, adA[nxt][0], adB[nxt][0], ra4, lb, kb, va[0], 0);
+        DIT_K4_STEP_COPY(acc, na, nb, fa, fb, 2, adA[nxt][0], adB[nxt][0], ra4, lb, kb, va[1], 16384);
+        DIT_K4_STEP_COPY(acc, na, nb, fa, fb, 4, adA[nxt][0], adB[nxt][0], rw4, lb, kb, vb[0], 32768);
+        DIT_K4_STEP_COPY(acc, na, nb, fa, fb, 6, adA[nxt][0], adB[nxt][0], rw4, lb, kb, vb[1], 49152);
+    }
+    wait_vmcnt<0>();      // retire the trailing (never read) copies before LDS is reused
+    __syncthreads();
+    // the last MFMAs' results are written back before anything reads the AGPRs
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    epi.template apply<T>(acc, m0 + wm * T::kWaveM, tn, wn, lane, M, smem);
+#endif
+}
+#undef DIT_K4_STEP_COPY
+#undef DIT_K4_STEP_BARRIER
+#undef DIT_K4_STEP
+#undef DIT_K4_COPIES
+#undef DIT_K4_OPERANDS
+#undef DIT_LD
+#undef DIT_CP
+#undef DIT_RD
+#undef DIT_MF
+
+#undef DIT_Q4_MFMA
+
+
+// ---------------------------------------------------------------------------
 // epilogue: out = resid + gate * acc + bias
 // ---------------------------------------------------------------------------
 // Q8: the accumulators hold int32 sums of int8 codes; each row block is
@@ -943,6 +1154,19 @@ static hipError_t run(const void *a, const void *w, int64_t M, int N_tile_cols, 
     return hipGetLastError();
 }
 
+template <class RowMap, class Epi>
+static hipError_t run4(const void *a, const void *w, int64_t M, int N_tile_cols, int K, RowMap rm, Epi epi,
+                       hipStream_t s, int64_t m_base = 0) {
+    using T = Tile4w;
+    const int tiles_m = (int)((M - m_base + T::BM - 1) / T::BM);
+    const int tiles_n = N_tile_cols / T::BN;
+    const int grid = tiles_m * tiles_n;
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL((gemm4_kernel<T, RowMap, Epi>), dim3(grid), dim3(T::kThreads), 0, s, a, w, (int)M, K,
+                       N_tile_cols, tiles_m, tiles_n, rm, epi, (int)m_base);
+    return hipGetLastError();
+}
+
 // Ragged row count (e.g. 4096 image + 74 text tokens): the last, partial row
 // of 256-row tiles costs a whole extra round of workgroups when the full rows
 // already fill whole rounds.  Then the full rows run as usual and the tail
@@ -1030,7 +1254,9 @@ static hipError_t residual_typed(const void *a, const void *w, int64_t M, int N,
             if (quarter_one_round(M, Nc))
                 return run<typename TSet::Quar1>(a, w, M, Nc, K, RowsIdentity{128}, epi, s, sc.a, sc.w);
             return run<typename TSet::Quar>(a, w, M, Nc, K, RowsIdentity{128}, epi, s, sc.a, sc.w);
-        default: return run<typename TSet::S>(a, w, M, Nc, K, RowsIdentity{256}, epi, s, sc.a, sc.w);
+        default:
+            if constexpr (SC::kFmt == 0) return run4(a, w, M, Nc, K, RowsIdentity{256}, epi, s);
+            return run<typename TSet::S>(a, w, M, Nc, K, RowsIdentity{256}, epi, s, sc.a, sc.w);
     }
 }
 
@@ -1094,19 +1320,21 @@ static hipError_t swiglu_any(const void *a, const void *w, int64_t M, int F, int
             if (quarter_one_round(M, 2 * F)) return with_act(typename TSet::Quar1{});
             return with_act(typename TSet::Quar{});
         default:
-            if (SC::kFmt == 0 && split_tail_rows(M, 2 * F)) {
-                // full 256-row tiles, then the ragged tail rows in 3-stage 128 x 256 tiles
-                // (4170 x 24576: 7 rounds of 256-row tiles become 6 plus a short one)
-                using T = typename TSet::S;
+            if constexpr (SC::kFmt == 0) {
+                // bf16: the 4-wave tile; a ragged tail that would cost a whole round
+                // of 256-row tiles runs as a second launch of 3-stage 128 x 256
+                // tiles (4170 x 24576: 7 rounds of 256-row tiles become 6 plus a
+                // short one)
                 using TH = typename TSet::Half;
-                const int64_t m_full = M / 256 * 256;
-                auto split = [&](auto epi) {
+                const bool split = split_tail_rows(M, 2 * F);
+                const int64_t m_full = split ? M / 256 * 256 : M;
+                auto launch = [&](auto epi) {
                     const hipError_t e =
-                        run<T>(a, w, m_full, 2 * F, K, RowsSwiglu{T::BN, T::kWaveN, F}, epi, s, sc.a, sc.w);
-                    if (e != hipSuccess) return e;
+                        run4(a, w, m_full, 2 * F, K, RowsSwiglu{Tile4w::BN, Tile4w::kWaveN, F}, epi, s);
+                    if (e != hipSuccess || !split) return e;
                     return run<TH>(a, w, M, 2 * F, K, RowsSwiglu{TH::BN, TH::kWaveN, F}, epi, s, sc.a, sc.w, m_full);
                 };
-                return act == 1 ? split(EpiSwiglu<1, TU>{u, F}) : split(EpiSwiglu<0, TU>{u, F});
+                return act == 1 ? launch(EpiSwiglu<1, TU>{u, F}) : launch(EpiSwiglu<0, TU>{u, F});
             }
             return with_act(typename TSet::S{});
     }
