@@ -6,12 +6,12 @@
 //
 // Work split: one workgroup = 8 waves = 256 queries of one (batch, head); each
 // wave owns 32 queries, two waves share a SIMD.  Keys stream through LDS in
-// tiles of 64 (the K tile and the transposed V tile) over a 4-stage ring that
-// is filled by register-free buffer->LDS loads, two tiles ahead of use.
+// tiles of 64, the K tile and the transposed V tile each over a ring of 4
+// slots, filled by register-free buffer->LDS loads three steps ahead of use.
 //
 // The scores are computed transposed, S^T = K Q^T (MFMA A = K rows, B = Q rows),
-// so an accumulator lane owns one query column and 16 keys: the running row
-// max and row sum are in-lane reductions plus one exchange with lane ^ 32.
+// so an accumulator lane owns one query column and 16 keys: row maxima and
+// row sums are in-lane reductions plus one exchange with lane ^ 32.
 // P^T is then already the B operand of O^T += V^T P^T provided the 16 keys a
 // lane holds per MFMA k-step are the 8 consecutive keys its half of the wave
 // feeds to that k-step.  The accumulator puts rows {0-3, 8-11} of each
@@ -20,15 +20,22 @@
 // key r with bits 2 and 3 exchanged.  V^T then stays in natural key order and
 // every V^T fragment is one 16-byte LDS read.
 //
-// Software pipeline per wave and key tile t: the QK^T MFMAs of tile t + 1 are
-// issued interleaved with the exponentials of tile t (VALU and the matrix
-// pipe overlap within the wave), then the PV MFMAs of tile t interleaved with
-// the row max of tile t + 1.
+// Three-stage software pipeline per wave: step t runs the QK^T MFMAs of key
+// tile t + 2, the PV MFMAs of tile t and the exponentials of tile t + 1, none
+// of which waits for another, so the matrix pipe and the VALU of the two waves
+// on a SIMD always have independent work; one barrier per step releases the
+// ring slots.  Every fragment read is a per-lane base register plus a
+// constant offset (the step loop is unrolled over the 4 ring slots), and the
+// K loads are bounded by their buffer resource, so a step spends no VALU on
+// addresses.
 //
 // Softmax in log2 units: q is multiplied by log2(e) / sqrt(hd) once, when it
 // is loaded, and the QK^T MFMAs of a tile start from the accumulator
-// -reference (the query's running softmax reference), so they deliver the
-// exponent itself and every probability is one v_exp_f32 of an accumulator.
+// -reference (the query's softmax reference), so they deliver the exponent
+// itself and every probability is one v_exp_f32 of an accumulator.  Row sums
+// are taken over the bf16 probabilities the PV MFMAs use, by v_dot2 with
+// (1, 1); there is no per-tile row max (the reference moves only when a
+// tile's probabilities sum past a bound).
 //
 // Ragged tail (seq not a multiple of 256, e.g. 4096 image + 74 text tokens):
 // the last, partial q tile of every (batch, head) would otherwise be a whole
@@ -39,9 +46,12 @@
 // sum_c 2^((m_c - M) s) l_c with M = max_c m_c (the split-KV form of the same
 // online softmax).
 #include "common.h"
+
+#include <type_traits>
 #include "trace.h"
 
 namespace dit {
+template <int N> using IC = std::integral_constant<int, N>;
 
 // Tasks [0, n_full) are (q tile, batch * head) pairs over all keys; with
 // nsplit > 1 the tasks after them are (chunk, batch * head) pairs of the last
@@ -57,18 +67,22 @@ void flash_attn_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K, c
     constexpr int QW = 32;                   // queries per wave
     constexpr int BQ = NW * QW;              // queries per workgroup
     constexpr int BKV = 64;                  // keys per tile
-    constexpr int NS = 4;                    // LDS ring stages
+    constexpr int NS = 4;                    // slots of the K ring and of the V^T ring
     constexpr int KROW = HD * 2;             // bytes per K row
     constexpr int KT_BYTES = BKV * KROW;     // K tile  [64 keys][HD]
     constexpr int VT_BYTES = HD * BKV * 2;   // V^T tile [HD][64 keys]
-    constexpr int STAGE = KT_BYTES + VT_BYTES;
+    constexpr int V_BASE = NS * KT_BYTES;    // the V^T ring follows the K ring
     constexpr int KL = KT_BYTES / (1024 * NW);   // 1 KiB K loads per wave per tile
     constexpr int VL = VT_BYTES / (1024 * NW);   // 1 KiB V^T loads per wave per tile
     constexpr int LOADS = KL + VL;
     constexpr int KK = HD / 16;              // MFMA k-steps over head_dim
     constexpr int DS = HD / 32;              // 32-row blocks of O^T
     static_assert(KL >= 1 && VL >= 1 && KT_BYTES % (1024 * NW) == 0, "tile vs waves");
-    __shared__ __attribute__((aligned(16))) uint8_t smem[NS * STAGE];
+    // every fragment read is a per-lane base register plus a constant that
+    // fits the 16-bit LDS offset field
+    static_assert((NS - 1) * KT_BYTES + 32 * KROW < 65536, "K offsets");
+    static_assert((NS - 1) * VT_BYTES + (DS - 1) * 32 * 128 < 65536, "V offsets");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[NS * (KT_BYTES + VT_BYTES)];
 
     // LDS layouts (gfx950: 64 banks, 256 B per cycle; a ds_read_b128 serves 16
     // lanes per cycle).
@@ -111,7 +125,8 @@ void flash_attn_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K, c
     const bf16 *Kh = K + (size_t)(b * Hkv + g) * S * HD;
     const bf16 *Vh = Vt + (size_t)(b * Hkv + g) * HD * S_pad;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lrow = lane & 31, lhalf = lane >> 5;
     const int q_base = qt * BQ + wave * QW;
 
@@ -130,19 +145,20 @@ void flash_attn_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K, c
         }
     }
 
-    // Load q of this wave fills 1 KiB at (q * NW + wave) KiB of the K (V^T) tile;
+    // Load q of this wave fills 1 KiB at (q * NW + wave) KiB of a K (V^T) tile;
     // lane l lands at +16 l, i.e. in row lin / rowbytes, slot (lin % rowbytes) / 16.
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh, (uint32_t)S * (uint32_t)KROW);
+    // K rows are read through a buffer resource based at the tile's first key
+    // and bounded at S, so rows past the end read as zeros (their scores are
+    // masked); V^T keys in [S, S_pad) are zero in memory.
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh, (uint32_t)HD * (uint32_t)S_pad * 2u);
-    int k_key[KL];            // key within the tile (bits 2 and 3 of the row swapped)
-    uint32_t k_col[KL];       // byte offset of the logical chunk within the row
+    uint32_t k_off[KL];       // byte offset within the tile (key bits 2 and 3 swapped, swizzled chunk)
     uint32_t v_off[VL];
 #pragma unroll
     for (int q = 0; q < KL; ++q) {
         const int lin = (q * NW + wave) * 1024 + lane * 16;
         const int r = lin / KROW, slot = (lin % KROW) >> 4;
-        k_key[q] = (r & ~15) | (((r >> 2) & 1) << 3) | (((r >> 3) & 1) << 2) | (r & 3);
-        k_col[q] = (uint32_t)((slot ^ kswz(r)) << 4);
+        const int key = (r & ~15) | (((r >> 2) & 1) << 3) | (((r >> 3) & 1) << 2) | (r & 3);
+        k_off[q] = (uint32_t)(key * KROW + ((slot ^ kswz(r)) << 4));
     }
 #pragma unroll
     for (int q = 0; q < VL; ++q) {
@@ -150,201 +166,212 @@ void flash_attn_kernel(const bf16 *__restrict__ Q, const bf16 *__restrict__ K, c
         const int d = lin >> 7, slot = (lin & 127) >> 4;
         v_off[q] = (uint32_t)d * (uint32_t)S_pad * 2u + (uint32_t)((slot ^ vswz(d)) << 4);
     }
-    // tail keys of K read a valid row (masked below); V^T keys in [S, S_pad) are zero
-#define DIT_ATT_ISSUE(tile, st)                                                                        \
-    do {                                                                                               \
-        const int kv0_ = (tile) * BKV;                                                                 \
-        uint8_t *base_ = smem + (st) * STAGE;                                                          \
-        _Pragma("unroll") for (int q = 0; q < KL; ++q) __builtin_amdgcn_raw_ptr_buffer_load_lds(      \
-            rk, (lds_void *)(base_ + (q * NW + wave) * 1024), 16,                                      \
-            (uint32_t)min(kv0_ + k_key[q], S - 1) * (uint32_t)KROW + k_col[q], 0, 0, 0);               \
-        _Pragma("unroll") for (int q = 0; q < VL; ++q) __builtin_amdgcn_raw_ptr_buffer_load_lds(      \
-            rv, (lds_void *)(base_ + KT_BYTES + (q * NW + wave) * 1024), 16, v_off[q],                 \
-            (uint32_t)kv0_ * 2u, 0, 0);                                                                \
-    } while (0)
-    // S^T[key, q] of the tile in stage st (64 keys x 32 queries), in log2
-    // units, plus the initial accumulator c0 (every element of a lane's column
-    // the same value: minus that query's softmax reference, or zero)
-#define DIT_ATT_QK(st, acc, c0)                                                                        \
-    do {                                                                                               \
-        const uint8_t *sk_ = smem + (st) * STAGE;                                                      \
-        _Pragma("unroll") for (int kk = 0; kk < KK; ++kk) {                                            \
-            const int c_ = kk * 2 + lhalf;                                                             \
-            _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                         \
-                const bf16x8 kf_ =                                                                     \
-                    *(const bf16x8 *)(sk_ + (ks * 32 + lrow) * KROW + ((c_ ^ kswz(lrow)) << 4));       \
-                acc[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf_, qf[kk], kk == 0 ? (c0) : acc[ks], \
-                                                                  0, 0, 0);                            \
-            }                                                                                          \
-        }                                                                                              \
-    } while (0)
-    // keys >= S (tail tile, or the never-used tile past the end) -> -inf; element
-    // e of acc[ks] in lane half h is key kv0 + 32 ks + 16 (e / 8) + 8 h + e % 8
-#define DIT_ATT_MASK(kv0, acc)                                                                         \
-    do {                                                                                               \
-        if ((kv0) + BKV > S) {                                                                         \
-            _Pragma("unroll") for (int ks = 0; ks < 2; ++ks)                                           \
-                _Pragma("unroll") for (int e = 0; e < 16; ++e) {                                       \
-                    const int key_ = (kv0) + ks * 32 + ((e >> 3) << 4) + (lhalf << 3) + (e & 7);       \
-                    if (key_ >= S) acc[ks][e] = -INFINITY;                                             \
-                }                                                                                      \
-        }                                                                                              \
-    } while (0)
-
-    floatx16 oacc[DS];
+    auto issue_k = [&](int tile, auto SLOT) __attribute__((always_inline)) {
+        const int kv0 = tile * BKV;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)kv0 * HD, (uint32_t)(S - kv0) * (uint32_t)KROW);
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds)
+        for (int q = 0; q < KL; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rk, (lds_void *)(smem + decltype(SLOT)::value * KT_BYTES + (q * NW + wave) * 1024), 16, k_off[q], 0,
+                0, 0);
+    };
+    auto issue_v = [&](int tile, auto SLOT) __attribute__((always_inline)) {
+        const int kv0 = tile * BKV;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[ds][e] = 0.f;
+        for (int q = 0; q < VL; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rv, (lds_void *)(smem + V_BASE + decltype(SLOT)::value * VT_BYTES + (q * NW + wave) * 1024), 16,
+                v_off[q], (uint32_t)kv0 * 2u, 0, 0);
+    };
 
-    // prologue: tiles 0 .. NS-2 in flight, wait for tiles 0 and 1
+    // per-lane fragment bases: K chunk of k-step kk in row lrow; V^T chunk of
+    // key group k2 in row lrow of the V ring
+    int kb[KK], vb[4];
 #pragma unroll
-    for (int j = 0; j < NS - 1; ++j) DIT_ATT_ISSUE(min(t0 + j, t1 - 1), (t0 + j) % NS);
-    wait_vmcnt<(NS - 3) * LOADS>();
-    barrier_only();
+    for (int kk = 0; kk < KK; ++kk) kb[kk] = lrow * KROW + (((kk * 2 + lhalf) ^ kswz(lrow)) << 4);
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) vb[k2] = V_BASE + lrow * 128 + (((k2 * 2 + lhalf) ^ vswz(lrow)) << 4);
+    // opaque to the compiler, so the V_BASE part stays in the register and the
+    // constant part of every read (slot, row block) goes to the offset field
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) asm volatile("" : "+v"(vb[k2]));
 
-    floatx16 sa[2];             // scores of the tile being exponentiated
     floatx16 zero16;
 #pragma unroll
     for (int e = 0; e < 16; ++e) zero16[e] = 0.f;
-    DIT_ATT_QK(t0 % NS, sa, zero16);
-    DIT_ATT_MASK(t0 * BKV, sa);
-    // Softmax reference of this lane's query, in log2 units: the exponentials,
-    // O and l are taken against it.  It starts at the first tile's max and
-    // moves up only when some lane of the wave sees a score more than kLazy
-    // above its reference, so exponentials stay <= 2^kLazy (exact in fp32 and
-    // bf16 range) while the rescale of O, which a max that creeps up would
-    // otherwise trigger on most tiles, becomes rare; O / l is the same softmax
-    // for any reference.  The QK^T MFMAs of a tile start from negm = -mref, so
-    // they deliver the exponent itself; dcur is the amount the reference moved
-    // after that tile's MFMAs were issued (zero but for the rare moves).
-    constexpr float kLazy = 8.0f;
-    float mref;
-    {
-        float mx = sa[0][0];
+    floatx16 oacc[DS];
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) oacc[ds] = zero16;
+    floatx16 sc[2][2];   // S^T of two key tiles (64 keys x 32 queries each), log2 units
+    bf16x8 pf[2][4];     // P^T of two key tiles, bf16, as B operands of the PV MFMAs
+
+    // S^T[key, q] = K Q^T of the tile in K slot SLOT, plus the start value c0
+    // (in every element of a lane's column the same: minus the query's softmax
+    // reference, or zero)
+    auto qk = [&](floatx16(&acc)[2], auto SLOT, const floatx16 &c0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const bf16x8 kf =
+                    *(const bf16x8 *)(smem + kb[kk] + (decltype(SLOT)::value * KT_BYTES + ks * 32 * KROW));
+                acc[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], kk == 0 ? c0 : acc[ks], 0, 0, 0);
+            }
+    };
+    // O^T[d, q] += V^T[d, keys] P^T[keys, q] of the tile in V slot SLOT
+    auto pv = [&](const bf16x8(&p)[4], auto SLOT) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2)
+#pragma unroll
+            for (int ds = 0; ds < DS; ++ds) {
+                const bf16x8 vf =
+                    *(const bf16x8 *)(smem + vb[k2] + (decltype(SLOT)::value * VT_BYTES + ds * 32 * 128));
+                oacc[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p[k2], oacc[ds], 0, 0, 0);
+            }
+    };
+    // keys >= S (the last, partial tile) -> -inf; element e of acc[ks] in lane
+    // half h is key kv0 + 32 ks + 16 (e / 8) + 8 h + e % 8
+    auto mask = [&](floatx16(&acc)[2], int kv0) __attribute__((always_inline)) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sa[ks][e]);
-        mref = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    }
-    float dcur = mref;          // the first tile was computed against 0
+            for (int e = 0; e < 16; ++e) {
+                const int key = kv0 + ks * 32 + ((e >> 3) << 4) + (lhalf << 3) + (e & 7);
+                if (key >= S) acc[ks][e] = -INFINITY;
+            }
+    };
+
+    // Softmax reference of this lane's query, in log2 units: the exponentials,
+    // O and l are taken against it; the QK^T MFMAs start from negm = -mref, so
+    // they deliver the exponent itself.  It starts at the first tile's max and
+    // moves only when a tile's probabilities against it sum to more than
+    // 2^kLazy in some lane of the wave (which every probability above 2^kLazy,
+    // an overflow included, implies): then it moves up to that tile's max, O
+    // and l are rescaled and the tile's probabilities recomputed.  So every
+    // probability that reaches O and l is <= 2^kLazy (exact in fp32 and bf16
+    // range), with no per-tile max, and O / l is the same softmax for any
+    // reference.
+    constexpr float kLazyMax = 256.0f;   // 2^kLazy, kLazy = 8
+    float mref;
     floatx16 negm;
+    // P = 2^S in bf16 (S already relative to the reference); returns this lane's sum of the bf16 values (the
+    // very numbers the PV MFMAs multiply), by dot products with (1, 1)
+    auto expo = [&](const floatx16(&s)[2], bf16x8(&p)[4]) __attribute__((always_inline)) -> float {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                p[ks * 2 + (e >> 3)][e & 7] = f2bf(__builtin_amdgcn_exp2f(s[ks][e]));
+        const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+        float a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bf16x2 pr = {p[k2][2 * i], p[k2][2 * i + 1]};
+                a[i] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, a[i], false);
+            }
+        return (a[0] + a[1]) + (a[2] + a[3]);
+    };
+    auto tile_max = [&](const floatx16(&s)[2]) __attribute__((always_inline)) {
+        float mx = s[0][0];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[ks][e]);
+        return fmaxf(mx, __shfl_xor(mx, 32, 64));
+    };
+
+    // Pipeline: key tile j has its K in K slot (j - t0) % NS and its V^T in V
+    // slot (j - t0) % NS; S^T and P^T of tile j live in buffer (j - t0) % 2.
+    // Step t runs, with no dependence among the three, the QK^T MFMAs of tile
+    // t + 2, the PV MFMAs of tile t and the exponentials of tile t + 1; it
+    // issues the loads of K(t + 5) and V(t + 3) (three steps ahead of use) and
+    // ends with tiles K(t + 3), V(t + 1) landed and a barrier.
+    // prologue: K(t0 .. t0+2), V(t0) in one group, then K(t0+3), V(t0+1)
+    issue_k(t0, IC<0>{});
+    issue_k(min(t0 + 1, t1 - 1), IC<1>{});
+    issue_k(min(t0 + 2, t1 - 1), IC<2>{});
+    issue_v(t0, IC<0>{});
+    issue_k(min(t0 + 3, t1 - 1), IC<3>{});
+    issue_v(min(t0 + 1, t1 - 1), IC<1>{});
+    wait_vmcnt<LOADS>();
+    barrier_only();
+    qk(sc[0], IC<0>{}, zero16);
+    qk(sc[1], IC<1>{}, zero16);
+    if ((t0 + 1) * BKV > S) mask(sc[0], t0 * BKV);
+    mref = tile_max(sc[0]);
 #pragma unroll
     for (int e = 0; e < 16; ++e) negm[e] = -mref;
-    float alpha = 1.f;          // factor taking O and l from the previous reference to mref
-    float lsum = 0.f;           // this lane's partial row sum (the other 16 keys live in lane ^ 32)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        sc[0][ks] += negm;
+        sc[1][ks] += negm;
+    }
+    float lsum = expo(sc[0], pf[0]);   // this lane's partial row sum (the other 32 keys live in lane ^ 32)
+    barrier_only();                    // K slot 0 (tile t0) is read by every wave before K(t0 + 4) replaces it
+    issue_k(min(t0 + 4, t1 - 1), IC<0>{});
+    issue_v(min(t0 + 2, t1 - 1), IC<2>{});
 
-    // one key tile; MASKED = 0 for the steady state (tile t + 1 holds 64 valid
-    // keys), 1 for the last two tiles
-#define DIT_ATT_STEP(MASKED, T, SC, SN)                                                                       \
-    do {                                                                                                      \
-        /* stage (t-1) % NS was released by the barrier that closed iteration t - 1 */                        \
-        DIT_ATT_ISSUE(min((T) + NS - 1, t1 - 1), ((T) + NS - 1) % NS);                                        \
-        /* rare: the reference moved (wave-uniform branches) */                                               \
-        if (__any(alpha < 1.f)) {                                                                             \
-_Pragma("unroll")                                                                                             \
-            for (int ds = 0; ds < DS; ++ds)                                                                   \
-_Pragma("unroll")                                                                                             \
-                for (int e = 0; e < 16; ++e) oacc[ds][e] *= alpha;                                            \
-            lsum *= alpha;                                                                                    \
-        }                                                                                                     \
-        if (__any(dcur != 0.f)) {                                                                             \
-_Pragma("unroll")                                                                                             \
-            for (int ks = 0; ks < 2; ++ks)                                                                    \
-_Pragma("unroll")                                                                                             \
-                for (int e = 0; e < 16; ++e) SC[ks][e] -= dcur;                                               \
-        }                                                                                                     \
-                                                                                                              \
-        /* QK^T of tile t + 1 || exponentials of tile t */                                                    \
-        DIT_ATT_QK(((T) + 1) % NS, SN, negm);                                                                 \
-        bf16x8 pf[4];                                                                                         \
-        float ps[4];                          /* four partial sums: no 32-long dependent add chain */        \
-_Pragma("unroll")                                                                                             \
-        for (int ks = 0; ks < 2; ++ks)                                                                        \
-_Pragma("unroll")                                                                                             \
-            for (int e = 0; e < 16; ++e) {                                                                    \
-                const float p = __builtin_amdgcn_exp2f(SC[ks][e]);                                            \
-                if (ks == 0 && e < 4) ps[e] = p; else ps[e & 3] += p;                                         \
-                pf[ks * 2 + (e >> 3)][e & 7] = f2bf(p);                                                       \
-            }                                                                                                 \
-        lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);                                                            \
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                                    \
-_Pragma("unroll")                                                                                             \
-        for (int i = 0; i < 2 * KK - 2; ++i) {                                                                \
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                \
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                                \
-            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);                                                \
-        }                                                                                                     \
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                                    \
-                                                                                                              \
-        if (MASKED) DIT_ATT_MASK(((T) + 1) * BKV, SN);                                                        \
-                                                                                                              \
-        /* O^T[d, q] += V^T[d, keys] P^T[keys, q] of tile t || row max of tile t + 1 */                       \
-        {                                                                                                     \
-            const uint8_t *sv = smem + ((T) % NS) * STAGE + KT_BYTES;                                         \
-_Pragma("unroll")                                                                                             \
-            for (int k2 = 0; k2 < 4; ++k2) {                                                                  \
-_Pragma("unroll")                                                                                             \
-                for (int ds = 0; ds < DS; ++ds) {                                                             \
-                    const int d = ds * 32 + lrow;                                                             \
-                    const bf16x8 vf = *(const bf16x8 *)(sv + d * 128 + (((k2 * 2 + lhalf) ^ vswz(d)) << 4));  \
-                    oacc[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[k2], oacc[ds], 0, 0, 0);        \
-                }                                                                                             \
-            }                                                                                                 \
-            /* the largest exponent of tile t + 1 against the current reference */                            \
-            float mx = SN[0][0];                                                                              \
-_Pragma("unroll")                                                                                             \
-            for (int ks = 0; ks < 2; ++ks)                                                                    \
-_Pragma("unroll")                                                                                             \
-                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, SN[ks][e]);                                       \
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));                                                           \
-            alpha = 1.f;                                                                                      \
-            dcur = 0.f;                                                                                       \
-            if (__any(mx > kLazy)) {                                                                          \
-                dcur = fmaxf(mx, 0.f);                                                                        \
-                alpha = __builtin_amdgcn_exp2f(-dcur);                                                        \
-                mref += dcur;                                                                                 \
-_Pragma("unroll")                                                                                             \
-                for (int e = 0; e < 16; ++e) negm[e] = -mref;                                                 \
-            }                                                                                                 \
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                                \
-_Pragma("unroll")                                                                                             \
-            for (int i = 0; i < 4 * DS - 2; ++i) {                                                            \
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                            \
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                            \
-                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);                                            \
-            }                                                                                                 \
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                                \
-        }                                                                                                     \
-                                                                                                              \
-        /* tile t + 2 landed (tiles t+3 .. t+NS-1 may still be in flight) */                                  \
-        wait_vmcnt<(NS - 3) * LOADS>();                                                                       \
-        barrier_only();                                                                                       \
-                                                                                                              \
-    } while (0)
-    floatx16 sb[2];
-    int t = t0;
-    for (; t + 1 < t1 - 2; t += 2) {
-        DIT_ATT_STEP(0, t, sa, sb);
-        DIT_ATT_STEP(0, t + 1, sb, sa);
-    }
-    if (t < t1 - 2) {
-        DIT_ATT_STEP(0, t, sa, sb);
-        ++t;
+    auto step = [&](int t, auto R_) __attribute__((always_inline)) {
+        constexpr int R = decltype(R_)::value;   // (t - t0) % NS
+        constexpr int CUR = R % 2, NXT = (R + 1) % 2;
+        issue_k(min(t + 5, t1 - 1), IC<(R + 1) % NS>{});
+        issue_v(min(t + 3, t1 - 1), IC<(R + 3) % NS>{});
+        if (t + 1 < t1 && (t + 2) * BKV > S) mask(sc[NXT], (t + 1) * BKV);
+        // tiles past t1 - 1 are computed on a repeated tile and never used
+        qk(sc[CUR], IC<(R + 2) % NS>{}, negm);
+        pv(pf[CUR], IC<R % NS>{});
+        float psum = expo(sc[NXT], pf[NXT]);
+        // interleave: per MFMA one fragment read and three VALU instructions
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) sa[ks] = sb[ks];
-    }
-    for (; t < t1; ++t) {
-        DIT_ATT_STEP(1, t, sa, sb);
+        for (int i = 0; i < 4 * KK - 2; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        if (t + 1 < t1) {
+            if (__any(psum > kLazyMax)) {
+                // rare: move the reference up to this tile's max; the scores of
+                // this tile and of tile t + 2 were taken against the old one
+                const float dcur = fmaxf(tile_max(sc[NXT]), 0.f);
+                const float alpha = __builtin_amdgcn_exp2f(-dcur);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) sa[ks] = sb[ks];
+                for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) oacc[ds][e] *= alpha;
+                lsum *= alpha;
+                mref += dcur;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) negm[e] = -mref;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        sc[NXT][ks][e] -= dcur;
+                        sc[CUR][ks][e] -= dcur;
+                    }
+                psum = expo(sc[NXT], pf[NXT]);
+            }
+            lsum += psum;
+        }
+        // K(t + 3) and V(t + 1) landed (the loads of the last two steps may be in flight)
+        wait_vmcnt<2 * LOADS, 0>();
+        barrier_only();
+    };
+    for (int t = t0;;) {
+        step(t, IC<0>{});
+        if (++t >= t1) break;
+        step(t, IC<1>{});
+        if (++t >= t1) break;
+        step(t, IC<2>{});
+        if (++t >= t1) break;
+        step(t, IC<3>{});
+        if (++t >= t1) break;
     }
-#undef DIT_ATT_STEP
     wait_vmcnt<0>();      // retire the trailing (never read) loads before the workgroup's LDS is released
-#undef DIT_ATT_ISSUE
-#undef DIT_ATT_QK
-#undef DIT_ATT_MASK
 
     const float l = lsum + __shfl_xor(lsum, 32, 64);
     const int q = q_base + lrow;
