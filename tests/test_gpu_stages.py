@@ -210,6 +210,48 @@ def test_flash_attention_split_tail(B, S, H, Hk, hd, nsplit):
     assert_parity(got, pm, max_rel=1e-2, min_cos=0.99999, what="split vs unsplit")
 
 
+@pytest.mark.parametrize("kind,S,hd,nsplit", [("ramp", 1000, 128, 1), ("ramp", 1000, 64, 1), ("ramp", 700, 128, 4),
+                                               ("late_spike", 900, 128, 1), ("late_spike", 333, 64, 3)])
+def test_flash_attention_reference_moves(kind, S, hd, nsplit):
+    """Scores that keep growing along the keys move the softmax reference many
+    times (ramp: key norms grow 4x from the first key to the last); one late
+    key whose score tops every earlier one by far more than the exponent range
+    (late_spike: every query leans on one direction u, that key is 40 u) must
+    be caught before its probability overflows.  Both against the explicit
+    softmax."""
+    import torch
+    say(f"flash_attention reference moves kind={kind} S={S} hd={hd} nsplit={nsplit}")
+    B, H, Hk = 1, 4, 2
+    r = _rng(12)
+    if kind == "ramp":
+        q = r.standard_normal((B, H, S, hd), dtype=np.float32)
+        k = r.standard_normal((B, Hk, S, hd), dtype=np.float32) * np.linspace(0.5, 2.0, S, dtype=np.float32)[:, None]
+    else:
+        u = r.standard_normal(hd, dtype=np.float32)
+        q = u + 0.5 * r.standard_normal((B, H, S, hd), dtype=np.float32)
+        k = r.standard_normal((B, Hk, S, hd), dtype=np.float32)
+        k[:, :, S - 10] = 40.0 * u
+    q, k = I.bf16_round(q), I.bf16_round(k)
+    v = I.bf16_round(r.standard_normal((B, Hk, S, hd), dtype=np.float32))
+    spad = N.dit_seq_pad(S)
+    vt = np.zeros((B, Hk, hd, spad), np.float32)
+    vt[..., :S] = v.transpose(0, 1, 3, 2)
+    cfg = I.DiTConfig("att", 0, B, (1, 1, S), H * hd, H, Hk, hd, 128, 0, False, "half2d", (hd // 2, hd // 2), 100.0)
+    desc = R.desc_of(cfg)
+    out = torch.empty((B * S, H * hd), dtype=torch.bfloat16, device="cuda")
+    if nsplit > 1:
+        ws = R.alloc_ws(N.dit_attention_workspace_size(desc, nsplit))
+        N.dit_flash_attention_split(desc, R.to_dev_bf16(q), R.to_dev_bf16(k), R.to_dev_bf16(vt), out, nsplit, ws)
+    else:
+        N.dit_flash_attention(desc, R.to_dev_bf16(q), R.to_dev_bf16(k), R.to_dev_bf16(vt), out)
+    _sync()
+    ref = O.attention(q[0].transpose(1, 0, 2).astype(np.float64), k[0].transpose(1, 0, 2), v[0].transpose(1, 0, 2),
+                      H, Hk)
+    got = R.to_host_f32(out)
+    assert np.isfinite(got).all()
+    assert_parity(got, ref, max_rel=2e-2, min_cos=0.9999, what=f"attention {kind}")
+
+
 def test_flash_attention_closed_forms():
     """V == 1 gives O == 1; Q == 0 gives the mean of V over the keys."""
     import torch
