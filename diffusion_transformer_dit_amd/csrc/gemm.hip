@@ -693,20 +693,22 @@ struct EpiSwiglu {
         const int l16 = lane & 15, lq = lane >> 4;
         constexpr int HJ = T::TN / 2;
         const int f0 = tn * (T::BN / 2) + wn * (T::kWaveN / 2);
+        // the HJ column blocks of one output row are stored back to back, so
+        // each 16 HJ-feature row segment reaches L2 whole instead of in pieces
+        // far apart in time (which cost partial-line write-backs)
 #pragma unroll
-        for (int j = 0; j < HJ; ++j) {
-            const int f = f0 + j * 16 + l16;
+        for (int i = 0; i < T::TM; ++i)
 #pragma unroll
-            for (int i = 0; i < T::TM; ++i)
+            for (int e = 0; e < 4; ++e) {
+                const int row = row0 + acc_row(i, e, lq);
+                if (row < M) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int row = row0 + acc_row(i, e, lq);
-                    if (row < M) {
+                    for (int j = 0; j < HJ; ++j) {
                         const float g = ACT == 1 ? gelu_tanh_f(acc[i][j][e]) : silu_f(acc[i][j][e]);
-                        u[(size_t)row * F + f] = from_f32<TU>(g * acc[i][j + HJ][e]);
+                        u[(size_t)row * F + f0 + j * 16 + l16] = from_f32<TU>(g * acc[i][j + HJ][e]);
                     }
                 }
-        }
+            }
     }
 };
 
