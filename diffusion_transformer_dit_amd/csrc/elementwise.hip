@@ -308,10 +308,10 @@ void vt_pad_zero_kernel(TV *__restrict__ vt, int rows, int seq, int seq_pad) {
 }
 
 hipError_t launch_vt_pad_zero(void *vt, int vt_f32, int rows, int seq, int seq_pad, hipStream_t s) {
+    const int64_t n = (int64_t)rows * (seq_pad - seq);
+    if (n <= 0) return hipSuccess;   // nothing to zero: no launch, and no trace record
     TraceScope trace_(s, "vt_pad_zero");
     if (trace_.on()) trace_.args("rows=%d seq=%d pad=%d", rows, seq, seq_pad);
-    const int64_t n = (int64_t)rows * (seq_pad - seq);
-    if (n <= 0) return hipSuccess;
     const int blocks = (int)std::min<int64_t>((n + 255) / 256, 4096);
     if (vt_f32)
         hipLaunchKernelGGL(vt_pad_zero_kernel<float>, dim3(blocks), dim3(256), 0, s, (float *)vt, rows, seq, seq_pad);

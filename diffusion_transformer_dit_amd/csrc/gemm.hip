@@ -740,9 +740,10 @@ struct EpiSwiglu {
 // ---------------------------------------------------------------------------
 constexpr int kQkvStride = 260;   // floats per staged row: 256 + 4, so 16 row-per-lane reads hit distinct banks
 
-// RMS: qk-norm kind RMSNorm; RF: RoPE before the qk-norm; TQ: type of q, k, vt
-// (fp32 on the fp32 parity path: written straight from registers, no LDS copy-out)
-template <int HD, bool RMS, bool RF, typename TQ = bf16>
+// RMS: qk-norm kind RMSNorm; RF: RoPE before the qk-norm; RH: rotate-half RoPE
+// pairs (else interleaved); TQ: type of q, k, vt (fp32 on the fp32 parity path:
+// written straight from registers, no LDS copy-out)
+template <int HD, bool RMS, bool RF, bool RH, typename TQ = bf16>
 struct EpiQkv {
     static constexpr bool kDequant = false;
     static constexpr bool kF32 = sizeof(TQ) == 4;
@@ -791,7 +792,10 @@ struct EpiQkv {
         }
         constexpr int PARTS = HD / 64;                     // lanes per q/k head row
         const int rl = within / PARTS, part = within % PARTS;
-        // the 32 RoPE pairs of this lane: frequencies pair0 .. pair0 + 31
+        // the 32 RoPE pairs of this lane: rotate-half pairs pair0 .. pair0 + 31;
+        // interleaved pairs in 4-pair runs, run q at 4 (PARTS q + part), so the
+        // two lanes of a head row read chunks 32 bytes apart from the staged
+        // row (distinct banks) rather than 256 bytes apart (the same banks)
         const int pair0 = part * 32;
 #pragma unroll
         for (int sp = 0; sp < T::kWaveM / 64; ++sp) {
@@ -813,8 +817,9 @@ struct EpiQkv {
             if (sect < 2) {
 #pragma unroll
                 for (int m4 = 0; m4 < 8; ++m4) {
-                    cpre[m4] = *(const floatx4 *)(ct + pair0 + m4 * 4);
-                    spre[m4] = *(const floatx4 *)(st + pair0 + m4 * 4);
+                    const int p4 = RH ? pair0 + m4 * 4 : (PARTS * m4 + part) * 4;
+                    cpre[m4] = *(const floatx4 *)(ct + p4);
+                    spre[m4] = *(const floatx4 *)(st + p4);
                 }
             }
             wait_vmcnt<63, 0>();   // this wave's LDS writes done; global loads stay in flight
@@ -823,7 +828,7 @@ struct EpiQkv {
             bf16x8 o[8];           // this lane's 64 bf16 results, 8 at a time
             // column (within the head) of this lane's 8-value chunk q, q = 0..7
             auto qcol = [&](int q) {
-                return e.rope_half ? (q < 4 ? pair0 + q * 8 : HD / 2 + pair0 + (q - 4) * 8) : part * 64 + q * 8;
+                return RH ? (q < 4 ? pair0 + q * 8 : HD / 2 + pair0 + (q - 4) * 8) : (PARTS * q + part) * 8;
             };
             // fp32 path: chunk q (8 values) of this lane's q/k row straight to global memory
             auto store_f32 = [&](int q, const float (&y)[8]) {
@@ -880,7 +885,7 @@ struct EpiQkv {
 #pragma unroll
                             for (int u = 0; u < 8; ++u) acc_ += pass == 0 ? y[u] : (y[u] - mean) * (y[u] - mean);
                         };
-                        if (!e.rope_half) {
+                        if constexpr (!RH) {
 #pragma unroll
                             for (int q = 0; q < 8; ++q) {
                                 float y[8];
@@ -918,7 +923,7 @@ struct EpiQkv {
                         }
                     }
                 };
-                if (!e.rope_half) {
+                if constexpr (!RH) {
 #pragma unroll
                     for (int q = 0; q < 8; ++q) {
                         float y[8];
@@ -1369,8 +1374,10 @@ static hipError_t qkv_any(const void *h, const void *w, int64_t M, int N, int K,
     using T = typename TileSet<SC::kFmt>::S;
     using TH = typename TileSet<SC::kFmt>::Half;
     using TQ = typename std::conditional<SC::kFmt == 2, float, bf16>::type;
+#define DIT_QKV_RH(HD_, RMS_, RF_, RH_) \
+    run_tail_split<T, TH>(h, w, M, N, K, RowsIdentity{T::BN}, EpiQkv<HD_, RMS_, RF_, RH_, TQ>{e}, s, sc.a, sc.w)
 #define DIT_QKV(HD_, RMS_, RF_) \
-    run_tail_split<T, TH>(h, w, M, N, K, RowsIdentity{T::BN}, EpiQkv<HD_, RMS_, RF_, TQ>{e}, s, sc.a, sc.w)
+    (e.rope_half ? DIT_QKV_RH(HD_, RMS_, RF_, true) : DIT_QKV_RH(HD_, RMS_, RF_, false))
     if (e.head_dim == 128) {
         if (e.rms) return e.rope_first ? DIT_QKV(128, true, true) : DIT_QKV(128, true, false);
         return e.rope_first ? DIT_QKV(128, false, true) : DIT_QKV(128, false, false);
@@ -1378,6 +1385,7 @@ static hipError_t qkv_any(const void *h, const void *w, int64_t M, int N, int K,
     if (e.rms) return e.rope_first ? DIT_QKV(64, true, true) : DIT_QKV(64, true, false);
     return e.rope_first ? DIT_QKV(64, false, true) : DIT_QKV(64, false, false);
 #undef DIT_QKV
+#undef DIT_QKV_RH
 }
 
 hipError_t launch_gemm_qkv(const bf16 *h, const bf16 *w, int64_t M, int N, int K, const QkvEpiArgs &e,

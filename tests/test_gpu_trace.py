@@ -53,3 +53,22 @@ def test_trace_of_block_forward(tmp_path):
     R.block_forward(cfg, blk, xd, cd, cos, sin)
     with pytest.raises(N.DitError):
         N.dit_trace_end(path)
+
+
+def test_trace_records_only_real_launches(tmp_path):
+    """At a sequence length that is a multiple of 64 the transposed V has no
+    padded key columns, so the pad kernel is not launched and leaves no record."""
+    cfg = I.C1.replace(name="trace_block_256", x_dtype="f32", seq_override=256)
+    w = I.block_weights(cfg, 0)
+    x, c, pos = I.block_x(cfg), I.cond(cfg), I.positions(cfg)
+    blk = R.DeviceBlock(w)
+    cos, sin = R.rope_tables(cfg, pos)
+    xd, cd = R.to_dev_f32(x), R.to_dev_f32(c)
+    path = str(tmp_path / "trace256.json")
+    N.dit_trace_begin(64)
+    try:
+        R.block_forward(cfg, blk, xd, cd, cos, sin)
+    finally:
+        N.dit_trace_end(path)
+    names = [e["name"] for e in json.load(open(path))["traceEvents"]]
+    assert names == [n for n in BLOCK_ORDER if n != "vt_pad_zero"]
