@@ -425,13 +425,16 @@ def host_info():
 
 def measured_traffic():
     """HBM bytes per launch of the SwiGLU GEMM from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE summary, or None when gemm.hip changed since."""
+    FETCH_SIZE / WRITE_SIZE summary, or None when a source file the kernel is
+    compiled from (the profile lists them) changed since."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "gemm_swiglu_stack_8b_hbm_counters.md")
     try:
         kv = dict(l.strip().split(": ", 1) for l in open(path) if l.startswith("    ") and ": " in l)
-        src = open(os.path.join(ROOT, kv["source"]), "rb").read()
-        if hashlib.sha256(src).hexdigest()[:16] != kv["source_sha256_16"]:
+        h = hashlib.sha256()
+        for f in kv["sources"].split():
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if h.hexdigest()[:16] != kv["sources_sha256_16"]:
             return None
         return int(kv["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
