@@ -542,22 +542,37 @@ def main():
         stack.step(lat, cond, cos, sin, vel)
         N.euler_flowmatch_update(lat, vel, lat.numel(), float(sig[j]), float(sig[j + 1]))
 
-    canary_before = canary_tflops()
-    for i in range(args.warmup):
-        one_step(i)
-    torch.cuda.synchronize()
-    per = []
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    with ClockSampler() as clocks:
-        t0 = time.perf_counter()
-        ev[0].record()
-        for i in range(args.steps):
-            one_step(args.warmup + i)
-            ev[i + 1].record()
+    # Guarded timing: W warm-up steps, the canary, exactly K timed steps, the
+    # canary again.  A canary drift above 7 % marks the round as disturbed
+    # (clock or contention change during the timed steps); then the round is
+    # repeated, at most three rounds in all.  The first undisturbed round is
+    # reported; if all three are disturbed, the median one.
+    def timed_round():
+        for i in range(args.warmup):
+            one_step(i)
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
-    ms = wall * 1000.0 / args.steps
+        before = canary_tflops()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        with ClockSampler() as clk:
+            t0 = time.perf_counter()
+            ev[0].record()
+            for i in range(args.steps):
+                one_step(args.warmup + i)
+                ev[i + 1].record()
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+        after = canary_tflops()
+        return {"ms": wall * 1000.0 / args.steps, "per": [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)],
+                "clocks": clk.summary(), "before": before, "after": after,
+                "drift_ok": abs(after - before) <= 0.07 * before}
+
+    rounds = [timed_round()]
+    while not rounds[-1]["drift_ok"] and len(rounds) < 3:
+        rounds.append(timed_round())
+    ok = [r for r in rounds if r["drift_ok"]]
+    chosen = ok[0] if ok else sorted(rounds, key=lambda r: r["ms"])[len(rounds) // 2]
+    ms, per = chosen["ms"], chosen["per"]
+    canary_before, canary_after = chosen["before"], chosen["after"]
     assert torch.isfinite(lat).all().item(), "non-finite latent"
 
     # one more (untimed) step under the library's tracer: the per-operation
@@ -651,8 +666,6 @@ def main():
     others = time_chain([I.C2], I.C2.layers)
     others.update(time_chain([I.C5_4096, I.C5_1024], I.C5_4096.layers))
     print(f"[bench] other configs: {json.dumps(others)}", file=sys.stderr, flush=True)
-    canary_after = canary_tflops()
-
     flops = step_flops(cfg)
     util = flops / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
     # The dominant kernel's average launch duration: HIP events on the launch
@@ -684,7 +697,7 @@ def main():
                    "head_dim": cfg.head_dim, "ffn": cfg.ffn, "steps_per_loop": I.STACK_STEPS},
         "mfma_util_pct": round(100.0 * util, 2),
         "step_tflop": round(flops / 1e12, 3),
-        "sclk_during_steps": clocks.summary(),
+        "sclk_during_steps": chosen["clocks"],
         "step_ms_events": {"median": round(float(np.median(per)), 3), "min": round(min(per), 3),
                            "max": round(max(per), 3)},
         # the loop executor: each step replayed as one HIP graph (timestep embedding + 36 blocks + Euler)
@@ -697,10 +710,14 @@ def main():
         "kernels": kern,
         # dit_block_forward at 4096 tokens and on the joint text + image sequence (4096 + 74 tokens)
         "block": blocks,
-        # hipBLASLt bf16 4096^3 before / after the timed steps: a drift of more than 7 %
-        # marks a clock or contention change during the run
+        # hipBLASLt bf16 4096^3 right before / after the timed steps of the reported
+        # round: a drift of more than 7 % marks a clock or contention change
         "canary_tflops": {"before": canary_before, "after": canary_after,
                           "drift_ok": abs(canary_after - canary_before) <= 0.07 * canary_before},
+        # every timed round (a disturbed round is repeated, at most 3 rounds; the
+        # first undisturbed one is reported, else the median)
+        "timed_rounds": [{"ms_per_step": round(r["ms"], 3), "canary_before": r["before"],
+                          "canary_after": r["after"], "drift_ok": r["drift_ok"]} for r in rounds],
         "cpu_baseline": cpu,
         # the four projections in int8 with the Hadamard-256 rotation (reduced precision: context, not value)
         "w8a8_h256": w8a8,
