@@ -389,7 +389,11 @@ void gemm_kernel(const void *__restrict__ A, const void *__restrict__ W, int M, 
 // writes a register is in flight outside a block; the buffer->LDS copies
 // write no register and are counted by the vmcnt wait before the barrier.
 // The accumulators stay in AGPRs: the compiler never moves them, since every
-// block takes them as tied operands.
+// block takes them as tied operands; a tile's first k-step starts them from an
+// inline zero.  The workgroups are persistent (one per CU): after a tile's K
+// loop the first two K stages of its next tile are copied into LDS, then the
+// epilogue runs (reading each accumulator from its AGPR where it is used), so
+// the copies' latency and the workgroup launch are off the critical path.
 // ---------------------------------------------------------------------------
 using Tile4w = Tile<256, 256, 2, 2>;   // BK 64, 2 LDS stages of 64 KiB
 
@@ -401,12 +405,12 @@ using Tile4w = Tile<256, 256, 2, 2>;   // BK 64, 2 LDS stages of 64 KiB
 // operands: accumulators of A row blocks i0, i0 + 1; the next k-step's
 // fragments written by the block (A i0, i0 + 1 and B i0, i0 + 1); the current
 // fragments; the LDS addresses of the next fragments (fragment r at r * 2048)
-#define DIT_K4_OPERANDS(acc_, fa_, fb_, na_, nb_, i0, adA, adB)                                            \
-    [c00] "+a"(acc_[i0][0]), [c01] "+a"(acc_[i0][1]), [c02] "+a"(acc_[i0][2]), [c03] "+a"(acc_[i0][3]),    \
-        [c04] "+a"(acc_[i0][4]), [c05] "+a"(acc_[i0][5]), [c06] "+a"(acc_[i0][6]),                         \
-        [c07] "+a"(acc_[i0][7]), [c10] "+a"(acc_[i0 + 1][0]), [c11] "+a"(acc_[i0 + 1][1]),                 \
-        [c12] "+a"(acc_[i0 + 1][2]), [c13] "+a"(acc_[i0 + 1][3]), [c14] "+a"(acc_[i0 + 1][4]),             \
-        [c15] "+a"(acc_[i0 + 1][5]), [c16] "+a"(acc_[i0 + 1][6]), [c17] "+a"(acc_[i0 + 1][7]),             \
+#define DIT_K4_OPERANDS(ac_, acc_, fa_, fb_, na_, nb_, i0, adA, adB)                                            \
+    [c00] ac_(acc_[i0][0]), [c01] ac_(acc_[i0][1]), [c02] ac_(acc_[i0][2]), [c03] ac_(acc_[i0][3]),    \
+        [c04] ac_(acc_[i0][4]), [c05] ac_(acc_[i0][5]), [c06] ac_(acc_[i0][6]),                         \
+        [c07] ac_(acc_[i0][7]), [c10] ac_(acc_[i0 + 1][0]), [c11] ac_(acc_[i0 + 1][1]),                 \
+        [c12] ac_(acc_[i0 + 1][2]), [c13] ac_(acc_[i0 + 1][3]), [c14] ac_(acc_[i0 + 1][4]),             \
+        [c15] ac_(acc_[i0 + 1][5]), [c16] ac_(acc_[i0 + 1][6]), [c17] ac_(acc_[i0 + 1][7]),             \
         [na0] "=&v"(na_[i0]), [na1] "=&v"(na_[i0 + 1]), [nb0] "=&v"(nb_[i0]), [nb1] "=&v"(nb_[i0 + 1])     \
         : [a0] "v"(fa_[i0]), [a1] "v"(fa_[i0 + 1]), [b0] "v"(fb_[0]), [b1] "v"(fb_[1]), [b2] "v"(fb_[2]),  \
           [b3] "v"(fb_[3]), [b4] "v"(fb_[4]), [b5] "v"(fb_[5]), [b6] "v"(fb_[6]), [b7] "v"(fb_[7]),         \
@@ -426,7 +430,19 @@ using Tile4w = Tile<256, 256, 2, 2>;   // BK 64, 2 LDS stages of 64 KiB
                  DIT_MF(c10, a1, b0) DIT_MF(c11, a1, b1) DIT_MF(c12, a1, b2) DIT_MF(c13, a1, b3)           \
                  DIT_MF(c14, a1, b4) DIT_MF(c15, a1, b5) DIT_MF(c16, a1, b6) DIT_MF(c17, a1, b7)           \
                  "s_waitcnt lgkmcnt(0)"                                                                    \
-                 : DIT_K4_OPERANDS(acc_, fa_, fb_, na_, nb_, i0, adA, adB)                                 \
+                 : DIT_K4_OPERANDS("+a", acc_, fa_, fb_, na_, nb_, i0, adA, adB)                                 \
+                 : "memory")
+// the same block for k-step 0 of a tile's first K stage: each MFMA starts its
+// sum from an inline zero, so no accumulator is cleared beforehand
+#define DIT_MZ(c, a, b) "v_mfma_f32_16x16x32_bf16 %[" #c "], %[" #a "], %[" #b "], 0\n\t"
+#define DIT_K4_STEP_Z(acc_, fa_, fb_, na_, nb_, i0, adA, adB)                                              \
+    asm volatile(DIT_RD(na0, pa, oa0) DIT_MZ(c00, a0, b0) DIT_RD(na1, pa, oa1) DIT_MZ(c01, a0, b1)         \
+                 DIT_RD(nb0, pb, oa0) DIT_MZ(c02, a0, b2) DIT_RD(nb1, pb, oa1) DIT_MZ(c03, a0, b3)         \
+                 DIT_MZ(c04, a0, b4) DIT_MZ(c05, a0, b5) DIT_MZ(c06, a0, b6) DIT_MZ(c07, a0, b7)           \
+                 DIT_MZ(c10, a1, b0) DIT_MZ(c11, a1, b1) DIT_MZ(c12, a1, b2) DIT_MZ(c13, a1, b3)           \
+                 DIT_MZ(c14, a1, b4) DIT_MZ(c15, a1, b5) DIT_MZ(c16, a1, b6) DIT_MZ(c17, a1, b7)           \
+                 "s_waitcnt lgkmcnt(0)"                                                                    \
+                 : DIT_K4_OPERANDS("=a", acc_, fa_, fb_, na_, nb_, i0, adA, adB)                           \
                  : "memory")
 // first k-step 1 block: 8 MFMAs, the next stage's wait and the barrier, then
 // 8 MFMAs with four reads and four copies
@@ -439,7 +455,7 @@ using Tile4w = Tile<256, 256, 2, 2>;   // BK 64, 2 LDS stages of 64 KiB
                  DIT_RD(nb0, pb, oa0) DIT_CP(2) DIT_MF(c14, a1, b4) DIT_LD(2) DIT_MF(c15, a1, b5)          \
                  DIT_RD(nb1, pb, oa1) DIT_CP(3) DIT_MF(c16, a1, b6) DIT_LD(3) DIT_MF(c17, a1, b7)          \
                  "s_waitcnt lgkmcnt(0)"                                                                    \
-                 : DIT_K4_OPERANDS(acc_, fa_, fb_, na_, nb_, i0, adA, adB)                                 \
+                 : DIT_K4_OPERANDS("+a", acc_, fa_, fb_, na_, nb_, i0, adA, adB)                                 \
                      DIT_K4_COPIES(rsrc_, ldsb_, soff_, vo_, doff_)                                        \
                  : "memory", "m0", "scc")
 // other k-step 1 blocks: one read and one copy per four MFMAs
@@ -453,9 +469,18 @@ using Tile4w = Tile<256, 256, 2, 2>;   // BK 64, 2 LDS stages of 64 KiB
                  DIT_MF(c14, a1, b4) DIT_RD(nb1, pb, oa1) DIT_MF(c15, a1, b5) DIT_CP(3)                    \
                  DIT_MF(c16, a1, b6) DIT_LD(3) DIT_MF(c17, a1, b7)                                         \
                  "s_waitcnt lgkmcnt(0)"                                                                    \
-                 : DIT_K4_OPERANDS(acc_, fa_, fb_, na_, nb_, i0, adA, adB)                                 \
+                 : DIT_K4_OPERANDS("+a", acc_, fa_, fb_, na_, nb_, i0, adA, adB)                                 \
                      DIT_K4_COPIES(rsrc_, ldsb_, soff_, vo_, doff_)                                        \
                  : "memory", "m0", "scc")
+
+// The lane index, computed afresh by each call: a value the compiler can not
+// hoist and keep live (the persistent 4-wave kernel has no register to hold
+// lane-derived addresses across its K loop).
+__device__ __forceinline__ int lane_now() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
 
 template <class T, class RowMap, class Epi>
 __global__ __launch_bounds__(256, 1)
@@ -464,111 +489,156 @@ void gemm4_kernel(const void *__restrict__ A, const void *__restrict__ W, int M,
 #if defined(__HIP_DEVICE_COMPILE__)
     static_assert(T::kWaves == 4 && T::TM == 8 && T::TN == 8 && T::ES == 2 && T::NS == 2 && T::BK == 64 &&
                   T::kALoads == 8 && T::kBLoads == 8 && T::kStageBytes == 65536, "the 4-wave 256 x 256 bf16 tile");
-    static_assert(Epi::template lds_bytes<T>() <= T::NS * T::kStageBytes, "epilogue LDS");
+    // the next tile's first two K stages are copied into LDS while the
+    // epilogue of the current one runs, so the epilogue may not use LDS
+    static_assert(Epi::template lds_bytes<T>() == 0, "epilogue LDS");
     __shared__ __attribute__((aligned(16))) uint8_t smem[T::NS * T::kStageBytes];
 
-    int tm, tn;
-    tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
-    const int m0 = m_base + tm * T::BM;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ntiles = tiles_m * tiles_n;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int wm = wave / T::WN, wn = wave % T::WN;
-    const int l16 = lane & 15, lq = lane >> 4;
 
     // Copies as in gemm_kernel: copy q (0-7: A rows, 8-15: W rows) of wave w
     // moves tile rows 8 (4 q + w) .. + 7 into 1 KiB of its stage.
     const uint32_t a_bytes = (uint32_t)M * (uint32_t)K * 2u, w_bytes = (uint32_t)w_rows * (uint32_t)K * 2u;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, a_bytes);
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(W, w_bytes);
-    const int lr = lane / T::kChunks, ls = lane % T::kChunks;
     uint32_t a_off[8], b_off[8];
+    auto tile_offsets = [&](int tm_, int tn_) {
+        const int m0_ = m_base + tm_ * T::BM;
+        // the lane terms are recomputed for each tile, not held in registers
+        // across the K loop (where there are none to spare)
+        const int ln = lane_now(), lr_ = ln / T::kChunks, ls_ = ln % T::kChunks;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int r = (q * 4 + wave) * T::kRowsPerLoad + lr;
-        a_off[q] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)K * 2u + (uint32_t)((ls ^ T::swz(r)) << 4);
-        b_off[q] = (uint32_t)rowmap(tn, r) * (uint32_t)K * 2u + (uint32_t)((ls ^ T::swz(r)) << 4);
-    }
+        for (int q = 0; q < 8; ++q) {
+            const int r = (q * 4 + wave) * T::kRowsPerLoad + lr_;
+            a_off[q] = (uint32_t)min(m0_ + r, M - 1) * (uint32_t)K * 2u + (uint32_t)((ls_ ^ T::swz(r)) << 4);
+            b_off[q] = (uint32_t)rowmap(tn_, r) * (uint32_t)K * 2u + (uint32_t)((ls_ ^ T::swz(r)) << 4);
+        }
+    };
     // the same two buffer resources as plain dwords for the copies inside the
     // asm blocks: base address (48 bits), no stride, size in bytes, format word
     typedef int int4v __attribute__((ext_vector_type(4)));
     const uint64_t pa64 = (uint64_t)(uintptr_t)A, pw64 = (uint64_t)(uintptr_t)W;
     const int4v ra4 = {(int)(uint32_t)pa64, (int)((pa64 >> 32) & 0xffff), (int)a_bytes, 0x00020000};
     const int4v rw4 = {(int)(uint32_t)pw64, (int)((pw64 >> 32) & 0xffff), (int)w_bytes, 0x00020000};
-    const uint32_t va[2][4] = {{a_off[0], a_off[1], a_off[2], a_off[3]}, {a_off[4], a_off[5], a_off[6], a_off[7]}};
-    const uint32_t vb[2][4] = {{b_off[0], b_off[1], b_off[2], b_off[3]}, {b_off[4], b_off[5], b_off[6], b_off[7]}};
 
-    floatx4 acc[8][8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-
-    // LDS byte addresses of this lane's fragments: stage s, k-step kk (chunk
-    // kk * 4 + lq of the 128-byte row), fragment r at + r * 2048 (16 rows on);
-    // the swizzle of rows base + 16 r + l16 depends on l16 only
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
-    const int swl = (l16 >> 1) & 7;
-    uint32_t adA[2][2], adB[2][2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const uint32_t col = (uint32_t)(((kk * 4 + lq) ^ swl) << 4);
-            adA[s][kk] = lds0 + s * T::kStageBytes + (uint32_t)(wm * 128 + l16) * 128u + col;
-            adB[s][kk] = lds0 + s * T::kStageBytes + T::BM * 128u + (uint32_t)(wn * 128 + l16) * 128u + col;
-        }
 
     const int KT = K / T::BK;
-    // prologue (compiled copies): K tiles 0 and 1 in flight, tile 0 landed, its
-    // k-step 0 fragments read
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        uint8_t *base = smem + t * T::kStageBytes;
-        const uint32_t kb = (uint32_t)(min(t, KT - 1) * T::BK) * 2u;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(base + (q * 4 + wave) * 1024), 16, a_off[q], kb,
-                                                     0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rw, (lds_void *)(base + T::BM * T::kRowBytes + (q * 4 + wave) * 1024), 16, b_off[q], kb, 0, 0);
-        }
-    }
-    wait_vmcnt<16>();
-    barrier_only();
-    bf16x8 fa[8], fb[8], na[8], nb[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        fa[r] = *(const bf16x8 *)(smem + adA[0][0] - lds0 + r * 2048);
-        fb[r] = *(const bf16x8 *)(smem + adB[0][0] - lds0 + r * 2048);
-    }
+    // K tiles 0 and 1 of a tile into the two stages: copy q of A rows and of W
+    // rows to + q * 4 KiB of the stage's A and W halves (as in the K loop, M0
+    // holds the LDS destination); stage 0 goes out first
+    const uint32_t lbw = lds0 + wave * 1024, kb1 = (uint32_t)(min(1, KT - 1) * T::BK * 2);
+#define DIT_PCP(m0off, vo, rs, kb) \
+    "s_add_u32 m0, %[lb], " #m0off "\n\tbuffer_load_dwordx4 %[" #vo "], %[" #rs "], %[" #kb "] offen lds\n\t"
+    auto issue_first_stages = [&]() {
+        asm volatile(
+            // stage 0
+            DIT_PCP(0, a0, ra, k0) DIT_PCP(32768, b0, rw, k0) DIT_PCP(4096, a1, ra, k0) DIT_PCP(36864, b1, rw, k0)
+            DIT_PCP(8192, a2, ra, k0) DIT_PCP(40960, b2, rw, k0) DIT_PCP(12288, a3, ra, k0) DIT_PCP(45056, b3, rw, k0)
+            DIT_PCP(16384, a4, ra, k0) DIT_PCP(49152, b4, rw, k0) DIT_PCP(20480, a5, ra, k0) DIT_PCP(53248, b5, rw, k0)
+            DIT_PCP(24576, a6, ra, k0) DIT_PCP(57344, b6, rw, k0) DIT_PCP(28672, a7, ra, k0) DIT_PCP(61440, b7, rw, k0)
+            // stage 1
+            DIT_PCP(65536, a0, ra, k1) DIT_PCP(98304, b0, rw, k1) DIT_PCP(69632, a1, ra, k1) DIT_PCP(102400, b1, rw, k1)
+            DIT_PCP(73728, a2, ra, k1) DIT_PCP(106496, b2, rw, k1) DIT_PCP(77824, a3, ra, k1) DIT_PCP(110592, b3, rw, k1)
+            DIT_PCP(81920, a4, ra, k1) DIT_PCP(114688, b4, rw, k1) DIT_PCP(86016, a5, ra, k1) DIT_PCP(118784, b5, rw, k1)
+            DIT_PCP(90112, a6, ra, k1) DIT_PCP(122880, b6, rw, k1) DIT_PCP(94208, a7, ra, k1) DIT_PCP(126976, b7, rw, k1)
+            : : [lb] "s"(lbw), [ra] "s"(ra4), [rw] "s"(rw4), [k0] "s"(0u), [k1] "s"(kb1),
+              [a0] "v"(a_off[0]), [a1] "v"(a_off[1]), [a2] "v"(a_off[2]), [a3] "v"(a_off[3]),
+              [a4] "v"(a_off[4]), [a5] "v"(a_off[5]), [a6] "v"(a_off[6]), [a7] "v"(a_off[7]),
+              [b0] "v"(b_off[0]), [b1] "v"(b_off[1]), [b2] "v"(b_off[2]), [b3] "v"(b_off[3]),
+              [b4] "v"(b_off[4]), [b5] "v"(b_off[5]), [b6] "v"(b_off[6]), [b7] "v"(b_off[7])
+            : "memory", "m0", "scc");
+    };
+#undef DIT_PCP
 
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1, nxt = cur ^ 1;
-        // k-step 0 of tile kt (fa, fb) || reads of its k-step 1
-        DIT_K4_STEP(acc, fa, fb, na, nb, 0, adA[cur][1], adB[cur][1]);
-        DIT_K4_STEP(acc, fa, fb, na, nb, 2, adA[cur][1], adB[cur][1]);
-        DIT_K4_STEP(acc, fa, fb, na, nb, 4, adA[cur][1], adB[cur][1]);
-        DIT_K4_STEP(acc, fa, fb, na, nb, 6, adA[cur][1], adB[cur][1]);
-        // k-step 1 of tile kt (na, nb) || after the barrier (tile kt + 1 has
-        // landed in stage nxt and every wave is done with stage cur): reads of
-        // k-step 0 of tile kt + 1, copies of tile kt + 2 into stage cur
-        const uint32_t lb = (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds0 + cur * T::kStageBytes + wave * 1024));
-        const uint32_t kb = (uint32_t)__builtin_amdgcn_readfirstlane(min(kt + 2, KT - 1) * T::BK * 2);
-        DIT_K4_STEP_BARRIER(acc, na, nb, fa, fb, 0, adA[nxt][0], adB[nxt][0], ra4, lb, kb, va[0], 0);
-        DIT_K4_STEP_COPY(acc, na, nb, fa, fb, 2, adA[nxt][0], adB[nxt][0], ra4, lb, kb, va[1], 16384);
-        DIT_K4_STEP_COPY(acc, na, nb, fa, fb, 4, adA[nxt][0], adB[nxt][0], rw4, lb, kb, vb[0], 32768);
-        DIT_K4_STEP_COPY(acc, na, nb, fa, fb, 6, adA[nxt][0], adB[nxt][0], rw4, lb, kb, vb[1], 49152);
+    // Persistent: workgroup b takes tiles b, b + grid, ... in the order of
+    // tile_coords, so the tiles resident together on one XCD are the same as
+    // with one workgroup per tile.
+    int pid = blockIdx.x, tm, tn;
+    tile_coords(pid, ntiles, tiles_m, tiles_n, tm, tn);
+    tile_offsets(tm, tn);
+    issue_first_stages();
+    floatx4 acc[8][8];
+    bf16x8 fa[8], fb[8], na[8], nb[8];
+    for (bool first = true;; first = false) {
+        // LDS byte addresses of this lane's fragments: stage s, k-step kk (chunk
+        // kk * 4 + lq of the 128-byte row), fragment r at + r * 2048 (16 rows
+        // on); the swizzle of rows base + 16 r + l16 depends on l16 only.  Like
+        // the copy offsets they are rebuilt for each tile, so that nothing but
+        // the accumulators is live across the epilogue.
+        uint32_t adA[2][2], adB[2][2];
+        {
+            const int ln = lane_now(), l16_ = ln & 15, lq_ = ln >> 4, swl = (l16_ >> 1) & 7;
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const uint32_t col = (uint32_t)(((kk * 4 + lq_) ^ swl) << 4);
+                    adA[s][kk] = lds0 + s * T::kStageBytes + (uint32_t)(wm * 128 + l16_) * 128u + col;
+                    adB[s][kk] = lds0 + s * T::kStageBytes + T::BM * 128u + (uint32_t)(wn * 128 + l16_) * 128u + col;
+                }
+        }
+        if (!first) tile_offsets(tm, tn);
+        const uint32_t va[2][4] = {{a_off[0], a_off[1], a_off[2], a_off[3]}, {a_off[4], a_off[5], a_off[6], a_off[7]}};
+        const uint32_t vb[2][4] = {{b_off[0], b_off[1], b_off[2], b_off[3]}, {b_off[4], b_off[5], b_off[6], b_off[7]}};
+        // K tile 0 landed.  The first tile's K tile 1 may still be in flight; a
+        // later tile's copies went out before the previous epilogue, whose
+        // stores count in the same counter, so there everything is waited for.
+        if (first) wait_vmcnt<16>();
+        else wait_vmcnt<0>();
+        barrier_only();
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            fa[r] = *(const bf16x8 *)(smem + adA[0][0] - lds0 + r * 2048);
+            fb[r] = *(const bf16x8 *)(smem + adB[0][0] - lds0 + r * 2048);
+        }
+
+        // one K tile: k-step 0 (fa, fb) || reads of its k-step 1; then k-step 1
+        // (na, nb) || after the barrier (tile kt + 1 has landed in stage nxt and
+        // every wave is done with stage cur): reads of k-step 0 of tile kt + 1,
+        // copies of tile kt + 2 into stage cur.  STEP0 is the k-step 0 block:
+        // the zero-start one in the tile's first K tile.
+#define DIT_K4_TILE(kt, STEP0)                                                                                     \
+    do {                                                                                                           \
+        const int cur = (kt) & 1, nxt = cur ^ 1;                                                                   \
+        STEP0(acc, fa, fb, na, nb, 0, adA[cur][1], adB[cur][1]);                                                   \
+        STEP0(acc, fa, fb, na, nb, 2, adA[cur][1], adB[cur][1]);                                                   \
+        STEP0(acc, fa, fb, na, nb, 4, adA[cur][1], adB[cur][1]);                                                   \
+        STEP0(acc, fa, fb, na, nb, 6, adA[cur][1], adB[cur][1]);                                                   \
+        const uint32_t lb =                                                                                        \
+            (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds0 + cur * T::kStageBytes + wave * 1024));            \
+        const uint32_t kb = (uint32_t)__builtin_amdgcn_readfirstlane(min((kt) + 2, KT - 1) * T::BK * 2);          \
+        DIT_K4_STEP_BARRIER(acc, na, nb, fa, fb, 0, adA[nxt][0], adB[nxt][0], ra4, lb, kb, va[0], 0);              \
+        DIT_K4_STEP_COPY(acc, na, nb, fa, fb, 2, adA[nxt][0], adB[nxt][0], ra4, lb, kb, va[1], 16384);             \
+        DIT_K4_STEP_COPY(acc, na, nb, fa, fb, 4, adA[nxt][0], adB[nxt][0], rw4, lb, kb, vb[0], 32768);             \
+        DIT_K4_STEP_COPY(acc, na, nb, fa, fb, 6, adA[nxt][0], adB[nxt][0], rw4, lb, kb, vb[1], 49152);             \
+    } while (0)
+        DIT_K4_TILE(0, DIT_K4_STEP_Z);
+        for (int kt = 1; kt < KT; ++kt) DIT_K4_TILE(kt, DIT_K4_STEP);
+#undef DIT_K4_TILE
+        wait_vmcnt<0>();      // retire the trailing (never read) copies before LDS is reused
+        __syncthreads();
+        // the last MFMAs' results are written back before anything reads the AGPRs
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+        const int row0 = m_base + tm * T::BM + wm * T::kWaveM, tn_cur = tn;
+        pid += gridDim.x;
+        const bool more = pid < ntiles;
+        if (more) {
+            // every wave is past its last LDS read of this tile (the barrier above)
+            tile_coords(pid, ntiles, tiles_m, tiles_n, tm, tn);
+            tile_offsets(tm, tn);
+            issue_first_stages();
+        }
+        epi.template apply<T>(acc, row0, tn_cur, wn, lane_now(), M, smem);
+        if (!more) break;
     }
-    wait_vmcnt<0>();      // retire the trailing (never read) copies before LDS is reused
-    __syncthreads();
-    // the last MFMAs' results are written back before anything reads the AGPRs
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-    epi.template apply<T>(acc, m0 + wm * T::kWaveM, tn, wn, lane, M, smem);
 #endif
 }
 #undef DIT_K4_STEP_COPY
 #undef DIT_K4_STEP_BARRIER
+#undef DIT_K4_STEP_Z
 #undef DIT_K4_STEP
+#undef DIT_MZ
 #undef DIT_K4_COPIES
 #undef DIT_K4_OPERANDS
 #undef DIT_LD
@@ -578,6 +648,21 @@ void gemm4_kernel(const void *__restrict__ A, const void *__restrict__ W, int M,
 
 #undef DIT_Q4_MFMA
 
+
+// An accumulator element read by an epilogue.  The 4-wave tile keeps its
+// accumulators in AGPRs; there each element is read into a VGPR where it is
+// used (with plain reads the compiler copies all 256 out right after the K
+// loop, which takes every VGPR and spills what the persistent loop keeps).
+template <class T>
+__device__ __forceinline__ float acc_get(const floatx4 &a, int e) {
+    if constexpr (T::kWaves == 4) {
+        float x;
+        asm("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(a[e]));
+        return x;
+    } else {
+        return a[e];
+    }
+}
 
 // ---------------------------------------------------------------------------
 // epilogue: out = resid + gate * acc + bias
@@ -660,7 +745,7 @@ struct EpiResidual {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             out[(size_t)(row0 + acc_row(i0 + ib, e, lq)) * N + col0 + j * 16 + l16] =
-                                from_f32<TO>(fmaf(acc[i0 + ib][j][e], g[j], bb[j]) + r[ib][j][e]);
+                                from_f32<TO>(fmaf(acc_get<T>(acc[i0 + ib][j], e), g[j], bb[j]) + r[ib][j][e]);
             } else {
 #pragma unroll
                 for (int ib = 0; ib < IB; ++ib)
@@ -671,7 +756,7 @@ struct EpiResidual {
                             const int row = row0 + acc_row(i0 + ib, e, lq);
                             if (row < M)
                                 out[(size_t)row * N + col0 + j * 16 + l16] =
-                                    from_f32<TO>(fmaf(acc[i0 + ib][j][e], g[j], bb[j]) + r[ib][j][e]);
+                                    from_f32<TO>(fmaf(acc_get<T>(acc[i0 + ib][j], e), g[j], bb[j]) + r[ib][j][e]);
                         }
             }
         }
@@ -696,19 +781,28 @@ struct EpiSwiglu {
         // the HJ column blocks of one output row are stored back to back, so
         // each 16 HJ-feature row segment reaches L2 whole instead of in pieces
         // far apart in time (which cost partial-line write-backs)
-#pragma unroll
-        for (int i = 0; i < T::TM; ++i)
+        auto row_block = [&](int i, bool check) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int row = row0 + acc_row(i, e, lq);
-                if (row < M) {
+                if (!check || row < M) {
 #pragma unroll
                     for (int j = 0; j < HJ; ++j) {
-                        const float g = ACT == 1 ? gelu_tanh_f(acc[i][j][e]) : silu_f(acc[i][j][e]);
-                        u[(size_t)row * F + f0 + j * 16 + l16] = from_f32<TU>(g * acc[i][j + HJ][e]);
+                        const float z = acc_get<T>(acc[i][j], e);
+                        const float g = ACT == 1 ? gelu_tanh_f(z) : silu_f(z);
+                        u[(size_t)row * F + f0 + j * 16 + l16] = from_f32<TU>(g * acc_get<T>(acc[i][j + HJ], e));
                     }
                 }
             }
+        };
+        // wave-uniform: all the wave's rows in range -> no per-row branches
+        const bool full = row0 + T::kWaveM <= M;
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i) {
+            if (full) row_block(i, false);
+            else row_block(i, true);
+            if constexpr (T::kWaves == 4) __builtin_amdgcn_sched_barrier(0);
+        }
     }
 };
 
@@ -1167,8 +1261,11 @@ static hipError_t run4(const void *a, const void *w, int64_t M, int N_tile_cols,
     using T = Tile4w;
     const int tiles_m = (int)((M - m_base + T::BM - 1) / T::BM);
     const int tiles_n = N_tile_cols / T::BN;
-    const int grid = tiles_m * tiles_n;
-    if (grid == 0) return hipSuccess;
+    const int ntiles = tiles_m * tiles_n;
+    if (ntiles == 0) return hipSuccess;
+    // persistent workgroups, one per CU (a multiple of 8, one per XCD in turn)
+    int grid = (int)std::min<int64_t>(ntiles, device_cu_count());
+    if (grid < ntiles && grid >= 8) grid -= grid % 8;
     hipLaunchKernelGGL((gemm4_kernel<T, RowMap, Epi>), dim3(grid), dim3(T::kThreads), 0, s, a, w, (int)M, K,
                        N_tile_cols, tiles_m, tiles_n, rm, epi, (int)m_base);
     return hipGetLastError();

@@ -290,6 +290,7 @@ def test_flash_attention_closed_forms():
     (2200, 4096, 128, "bf16", "bf16", True, False),   # ragged rows: the 8-wave 2-stage 128 x 128 tile (576 tiles)
     (4096, 6144, 128, "f32", "f32", True, True),      # column split: 4096 columns of 256 x 256, 2048 of 128 x 256
     (4096, 5120, 128, "bf16", "bf16", True, True),    # column split: 4096 columns of 256 x 256, 1024 of 128 x 128
+    (4096, 8192, 128, "f32", "f32", True, True),      # 512 tiles of 256 x 256: two per persistent workgroup
 ])
 def test_gemm_gated_residual(M, Nn, K, rdt, odt, gate, bias):
     import torch
@@ -349,7 +350,9 @@ def test_gemm_residual_in_place_and_identity():
 @pytest.mark.parametrize("M,F,K", [(300, 384, 256), (256, 768, 256), (4097, 256, 512), (1, 128, 64),
                                    (4170, 2048, 256),    # ragged rows over one full round of tiles
                                    (2200, 1024, 256),    # the 256 x 128 tile
-                                   (3000, 1536, 128)])   # the 2-stage 128 x 128 tile (576 tiles)
+                                   (3000, 1536, 128),    # the 2-stage 128 x 128 tile (576 tiles)
+                                   (4096, 4096, 128),    # 512 tiles of 256 x 256: two per persistent workgroup
+                                   (3840, 3456, 64)])    # 405 tiles (not a multiple of 8), a single K tile
 def test_gemm_swiglu(M, F, K):
     import torch
     say(f"gemm_swiglu M={M} F={F} K={K}")
