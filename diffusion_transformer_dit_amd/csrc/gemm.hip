@@ -83,19 +83,22 @@ __device__ __forceinline__ void tile_coords(int pid, int num, int tiles_m, int t
     tn = in / gm;
 }
 
+// Tile widths are template parameters, so the per-tile row arithmetic (done
+// for every tile a persistent workgroup takes) has no run-time division.
+template <int BN>
 struct RowsIdentity {
-    int bn;
-    __device__ __forceinline__ int operator()(int tile_n, int t) const { return tile_n * bn + t; }
+    __device__ __forceinline__ int operator()(int tile_n, int t) const { return tile_n * BN + t; }
 };
 
-// SwiGLU tile rows: each wave's kWaveN columns are kWaveN/2 gate rows followed by
+// SwiGLU tile rows: each wave's WAVE_N columns are WAVE_N/2 gate rows followed by
 // the up rows (offset F) of the same features.
+template <int BN, int WAVE_N>
 struct RowsSwiglu {
-    int bn, wave_n, F;
+    int F;
     __device__ __forceinline__ int operator()(int tile_n, int t) const {
-        const int half = wave_n >> 1;
-        const int w = t / wave_n, within = t - w * wave_n;
-        const int feat = tile_n * (bn >> 1) + w * half + (within % half);
+        constexpr int half = WAVE_N / 2;
+        const int w = t / WAVE_N, within = t - w * WAVE_N;
+        const int feat = tile_n * (BN / 2) + w * half + (within % half);
         return within >= half ? feat + F : feat;
     }
 };
@@ -797,6 +800,41 @@ struct EpiSwiglu {
         };
         // wave-uniform: all the wave's rows in range -> no per-row branches
         const bool full = row0 + T::kWaveM <= M;
+        if constexpr (T::kWaves == 4 && std::is_same<TU, bf16>::value) {
+            if (full) {
+                // stores at a wave-uniform row-block base plus a per-lane 32-bit
+                // byte offset (no per-row address arithmetic); the results of
+                // rows 4 lq + e and + e + 1 share one bf16 conversion
+                uint32_t off[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) off[e] = (uint32_t)((lq * 4 + e) * F + l16) * 2u;
+#pragma unroll
+                for (int i = 0; i < T::TM; ++i) {
+                    uint8_t *base = (uint8_t *)(u + (size_t)(row0 + i * 16) * F + f0);
+                    // the row block's 16 outputs as independent chains (the
+                    // exponentials and reciprocals of one hide the others' latency)
+                    float y[4][HJ];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int j = 0; j < HJ; ++j) {
+                            const float z = acc_get<T>(acc[i][j], e);
+                            y[e][j] = (ACT == 1 ? gelu_tanh_f(z) : silu_f(z)) * acc_get<T>(acc[i][j + HJ], e);
+                        }
+#pragma unroll
+                    for (int e = 0; e < 4; e += 2)
+#pragma unroll
+                        for (int j = 0; j < HJ; ++j) {
+                            uint32_t pk;   // both rounded to nearest even (the plain conversion's rounding)
+                            asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(pk) : "v"(y[e][j]), "v"(y[e + 1][j]));
+                            *(uint16_t *)(base + off[e] + j * 32) = (uint16_t)pk;
+                            *(uint16_t *)(base + off[e + 1] + j * 32) = (uint16_t)(pk >> 16);
+                        }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                return;
+            }
+        }
 #pragma unroll
         for (int i = 0; i < T::TM; ++i) {
             if (full) row_block(i, false);
@@ -1351,16 +1389,16 @@ static hipError_t residual_typed(const void *a, const void *w, int64_t M, int N,
     EpiResidual<TR, TO, SC::kQ8> epi{(const TR *)resid, gate, bias, (TO *)out, N, gate_fn, sc.a, sc.w};
     const int Nc = n_cols;
     switch (choose_tile(M, Nc, kAllTiles, SC::kFmt)) {
-        case kTileTall: return run<typename TSet::Tall>(a, w, M, Nc, K, RowsIdentity{256}, epi, s, sc.a, sc.w);
-        case kTileHalf: return run<typename TSet::Half>(a, w, M, Nc, K, RowsIdentity{256}, epi, s, sc.a, sc.w);
-        case kTileNar: return run<typename TSet::Nar>(a, w, M, Nc, K, RowsIdentity{128}, epi, s, sc.a, sc.w);
+        case kTileTall: return run<typename TSet::Tall>(a, w, M, Nc, K, RowsIdentity<256>{}, epi, s, sc.a, sc.w);
+        case kTileHalf: return run<typename TSet::Half>(a, w, M, Nc, K, RowsIdentity<256>{}, epi, s, sc.a, sc.w);
+        case kTileNar: return run<typename TSet::Nar>(a, w, M, Nc, K, RowsIdentity<128>{}, epi, s, sc.a, sc.w);
         case kTileQuar:
             if (quarter_one_round(M, Nc))
-                return run<typename TSet::Quar1>(a, w, M, Nc, K, RowsIdentity{128}, epi, s, sc.a, sc.w);
-            return run<typename TSet::Quar>(a, w, M, Nc, K, RowsIdentity{128}, epi, s, sc.a, sc.w);
+                return run<typename TSet::Quar1>(a, w, M, Nc, K, RowsIdentity<128>{}, epi, s, sc.a, sc.w);
+            return run<typename TSet::Quar>(a, w, M, Nc, K, RowsIdentity<128>{}, epi, s, sc.a, sc.w);
         default:
-            if constexpr (SC::kFmt == 0) return run4(a, w, M, Nc, K, RowsIdentity{256}, epi, s);
-            return run<typename TSet::S>(a, w, M, Nc, K, RowsIdentity{256}, epi, s, sc.a, sc.w);
+            if constexpr (SC::kFmt == 0) return run4(a, w, M, Nc, K, RowsIdentity<256>{}, epi, s);
+            return run<typename TSet::S>(a, w, M, Nc, K, RowsIdentity<256>{}, epi, s, sc.a, sc.w);
     }
 }
 
@@ -1411,7 +1449,7 @@ static hipError_t swiglu_any(const void *a, const void *w, int64_t M, int F, int
     using TSet = TileSet<SC::kFmt>;
     auto go = [&](auto tile, auto epi) {
         using T = decltype(tile);
-        return run<T>(a, w, M, 2 * F, K, RowsSwiglu{T::BN, T::kWaveN, F}, epi, s, sc.a, sc.w);
+        return run<T>(a, w, M, 2 * F, K, RowsSwiglu<T::BN, T::kWaveN>{F}, epi, s, sc.a, sc.w);
     };
     auto with_act = [&](auto tile) {
         return act == 1 ? go(tile, EpiSwiglu<1, TU>{u, F}) : go(tile, EpiSwiglu<0, TU>{u, F});
@@ -1434,9 +1472,9 @@ static hipError_t swiglu_any(const void *a, const void *w, int64_t M, int F, int
                 const int64_t m_full = split ? M / 256 * 256 : M;
                 auto launch = [&](auto epi) {
                     const hipError_t e =
-                        run4(a, w, m_full, 2 * F, K, RowsSwiglu{Tile4w::BN, Tile4w::kWaveN, F}, epi, s);
+                        run4(a, w, m_full, 2 * F, K, RowsSwiglu<Tile4w::BN, Tile4w::kWaveN>{F}, epi, s);
                     if (e != hipSuccess || !split) return e;
-                    return run<TH>(a, w, M, 2 * F, K, RowsSwiglu{TH::BN, TH::kWaveN, F}, epi, s, sc.a, sc.w, m_full);
+                    return run<TH>(a, w, M, 2 * F, K, RowsSwiglu<TH::BN, TH::kWaveN>{F}, epi, s, sc.a, sc.w, m_full);
                 };
                 return act == 1 ? launch(EpiSwiglu<1, TU>{u, F}) : launch(EpiSwiglu<0, TU>{u, F});
             }
@@ -1472,7 +1510,7 @@ static hipError_t qkv_any(const void *h, const void *w, int64_t M, int N, int K,
     using TH = typename TileSet<SC::kFmt>::Half;
     using TQ = typename std::conditional<SC::kFmt == 2, float, bf16>::type;
 #define DIT_QKV_RH(HD_, RMS_, RF_, RH_) \
-    run_tail_split<T, TH>(h, w, M, N, K, RowsIdentity{T::BN}, EpiQkv<HD_, RMS_, RF_, RH_, TQ>{e}, s, sc.a, sc.w)
+    run_tail_split<T, TH>(h, w, M, N, K, RowsIdentity<T::BN>{}, EpiQkv<HD_, RMS_, RF_, RH_, TQ>{e}, s, sc.a, sc.w)
 #define DIT_QKV(HD_, RMS_, RF_) \
     (e.rope_half ? DIT_QKV_RH(HD_, RMS_, RF_, true) : DIT_QKV_RH(HD_, RMS_, RF_, false))
     if (e.head_dim == 128) {
