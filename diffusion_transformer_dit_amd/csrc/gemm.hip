@@ -941,8 +941,23 @@ struct EpiQkv {
                     for (int r = 0; r < 4; ++r)
                         red[acc_row(ii, r, lq) * kQkvStride + wn * 64 + j * 16 + l16] = acc[sp * 4 + ii][j][r];
             const int rbase = row0 + sp * 64;             // token of staged row 0
-            const int trow = min(rbase + rl, M - 1);
-            const int sp_ = trow - (trow / S) * S;
+            // (batch, position) of staged row r: one wave-uniform division per
+            // sub-pass; with S >= 64 the 64-row window crosses at most one
+            // batch boundary, so each row's position follows by a compare
+            const int rb = min(rbase, M - 1);
+            const int b0 = rb / S, s0 = rb - b0 * S;
+            auto tok = [&](int r, int &bi, int &si) {
+                if (S >= 64) {
+                    si = s0 + r;
+                    bi = b0;
+                    if (si >= S) { si -= S; ++bi; }
+                } else {
+                    bi = (rb + r) / S;
+                    si = rb + r - bi * S;
+                }
+            };
+            int tb_, sp_;
+            tok(min(rbase + rl, M - 1) - rb, tb_, sp_);
             const float *ct = e.cos_t + (size_t)sp_ * (HD / 2);
             const float *st = e.sin_t + (size_t)sp_ * (HD / 2);
             floatx4 cpre[8], spre[8];    // cos/sin of this lane's 32 pairs, loaded before the barrier
@@ -1128,7 +1143,6 @@ struct EpiQkv {
 
             // copy-out: 16-byte piece pc of the cluster's (256 / HD) head blocks;
             // one wave's 64 pieces always lie in one head block
-            const int b0 = min(rbase, M - 1) / S, s0 = min(rbase, M - 1) - b0 * S;
             const bool v_fast = (rbase + 63 < M) && (s0 + 63 < S) && ((s0 & 7) == 0);
 #pragma unroll
             for (int it = 0; it < 8; ++it) {
@@ -1140,7 +1154,8 @@ struct EpiQkv {
                     const int r = pw / kRowChunks, c = pw - r * kRowChunks;
                     const int row = rbase + r;
                     if (row < M) {
-                        const int bi = row / S, si = row - bi * S;
+                        int bi, si;
+                        tok(r, bi, si);
                         bf16 *dst = (bf16 *)(psect == 0 ? e.q : e.k) +
                                     (((size_t)bi * (psect == 0 ? e.heads : e.kv_heads) + phead) * S + si) * HD + c * 8;
                         *(bf16x8 *)dst = *(const bf16x8 *)(ob + hs * kHeadBlock + qk_slot(r, c));
@@ -1155,7 +1170,8 @@ struct EpiQkv {
                         for (int u = 0; u < 8; ++u) {
                             const int row = rbase + c * 8 + u;
                             if (row < M) {
-                                const int bi = row / S, si = row - bi * S;
+                                int bi, si;
+                                tok(c * 8 + u, bi, si);
                                 ((bf16 *)e.vt)[(((size_t)bi * e.kv_heads + phead) * HD + d) * e.seq_pad + si] = v[u];
                             }
                         }
@@ -1165,6 +1181,198 @@ struct EpiQkv {
         }
     }
 };
+
+// ---------------------------------------------------------------------------
+// Split QKV (bf16, 4-wave tile): the GEMM epilogue only rounds and scatters,
+// q and k to [B, H, S, hd] and v to v^T [B, Hk, hd, seq_pad]; qk_norm_rope_kernel
+// then applies the qk-norm and RoPE to the q and k rows in place.  Each wave's
+// 128 columns hold 128 / hd whole heads; a lane stores rows 4 lq + e of column
+// l16 of each 16 x 16 block, from a wave-uniform base plus lane offsets: q / k
+// with one 2-byte store per value (row pairs share one conversion), v^T with
+// one 8-byte store of four consecutive tokens.
+// ---------------------------------------------------------------------------
+template <int HD>
+struct EpiQkvRaw {
+    static constexpr bool kDequant = false;
+    QkvEpiArgs e;
+    template <class T> static constexpr int lds_bytes() { return 0; }
+    // Taken only when the sequence length is a multiple of 16: a 16-row block
+    // then never crosses a sequence boundary (and M, a multiple of it, never
+    // cuts one), and v^T's 4-token groups are 8-byte aligned.
+    template <class T>
+    __device__ __forceinline__ void apply(floatx4 (&acc)[T::TM][T::TN], int row0, int tn, int wn, int lane, int M,
+                                          uint8_t *) const {
+        static_assert(T::kWaves == 4 && T::TN == 8 && T::kWaveN % HD == 0, "the 4-wave tile, whole heads per wave");
+        const int l16 = lane & 15, lq = lane >> 4;
+        const int S = e.seq, spad = e.seq_pad;
+        const int qcols = e.heads * HD, kcols = e.kv_heads * HD;
+        // per column block: section (0 q, 1 k, 2 v) and the byte address of its
+        // first column at sequence 0, position 0 (wave-uniform)
+        int sect[T::TN];
+        uint8_t *cbase[T::TN];
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) {
+            const int c0 = tn * T::BN + wn * T::kWaveN + j * 16;
+            sect[j] = c0 < qcols ? 0 : (c0 < qcols + kcols ? 1 : 2);
+            const int cs = c0 - (sect[j] == 0 ? 0 : (sect[j] == 1 ? qcols : qcols + kcols));
+            const int head = cs / HD, d0 = cs - head * HD;
+            cbase[j] = sect[j] == 2 ? (uint8_t *)((bf16 *)e.vt + ((size_t)head * HD + d0) * spad)
+                                    : (uint8_t *)((bf16 *)(sect[j] == 0 ? e.q : e.k) + ((size_t)head * S * HD + d0));
+        }
+        // lane byte offsets: q / k rows 4 lq + e are HD apart; a v^T row holds
+        // one column's tokens, the lane's four adjacent
+        uint32_t qo[4];
+#pragma unroll
+        for (int e_ = 0; e_ < 4; ++e_) qo[e_] = (uint32_t)((lq * 4 + e_) * HD + l16) * 2u;
+        const uint32_t vo = ((uint32_t)l16 * (uint32_t)spad + (uint32_t)lq * 4u) * 2u;
+        // SEC: the section of every block of the wave (0 q, 1 k, 2 v), or -1 for a
+        // wave whose columns cross a section boundary (hd 64 only)
+        auto store = [&](auto sec_c) {
+            constexpr int SEC = decltype(sec_c)::value;
+#pragma unroll
+            for (int i = 0; i < T::TM; ++i) {
+                const int t0 = row0 + i * 16;                 // token of the block's first row
+                if (t0 < M) {
+                    const int b0 = t0 / S, s0 = t0 - b0 * S;
+                    // byte offsets of (b0, s0) in q, k and v^T
+                    const size_t oq = ((size_t)b0 * e.heads * S + s0) * HD * 2;
+                    const size_t ok = ((size_t)b0 * e.kv_heads * S + s0) * HD * 2;
+                    const size_t ov = ((size_t)b0 * e.kv_heads * HD * spad + s0) * 2;
+#pragma unroll
+                    for (int j = 0; j < T::TN; ++j) {
+                        float z[4];
+#pragma unroll
+                        for (int e_ = 0; e_ < 4; ++e_) z[e_] = acc_get<T>(acc[i][j], e_);
+                        const int sj = SEC >= 0 ? SEC : sect[j];
+                        if (sj < 2) {
+                            uint8_t *base = cbase[j] + (sj == 0 ? oq : ok);
+#pragma unroll
+                            for (int e_ = 0; e_ < 4; e_ += 2) {
+                                uint32_t pk;   // both rounded to nearest even (the plain conversion's rounding)
+                                asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(pk) : "v"(z[e_]), "v"(z[e_ + 1]));
+                                *(uint16_t *)(base + qo[e_]) = (uint16_t)pk;
+                                *(uint16_t *)(base + qo[e_ + 1]) = (uint16_t)(pk >> 16);
+                            }
+                        } else {
+                            uint32_t p0, p1;
+                            asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(p0) : "v"(z[0]), "v"(z[1]));
+                            asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(p1) : "v"(z[2]), "v"(z[3]));
+                            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                            *(u32x2 *)(cbase[j] + ov + vo) = u32x2{p0, p1};
+                        }
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        if (sect[0] != sect[T::TN - 1]) store(std::integral_constant<int, -1>{});
+        else if (sect[0] == 0) store(std::integral_constant<int, 0>{});
+        else if (sect[0] == 1) store(std::integral_constant<int, 1>{});
+        else store(std::integral_constant<int, 2>{});
+    }
+};
+
+// In-place qk-norm and RoPE over the q and k rows of tokens [0, m_end) that the
+// split QKV projection wrote (same arithmetic as the fused QKV epilogue, on the
+// bf16-rounded projection).  A row of HD values is HD / 8 lanes of 8 values
+// (one 16-byte chunk each); statistics by butterflies over those lanes.
+// Interleaved RoPE pairs (2m, 2m + 1) lie in one lane; rotate-half pairs
+// (m, m + HD / 2) in lanes HD / 16 apart.  A workgroup takes 256 / (HD / 8)
+// consecutive tokens (one per lane group) and kGroup of the q and k heads
+// (q heads first): a lane group loads its token's cos / sin and both norms'
+// gamma / beta once, then its kGroup rows, all loads in flight together.
+constexpr int kQkNormGroup = 8;
+template <int HD, bool RMS, bool RF, bool RH>
+__global__ __launch_bounds__(256)
+void qk_norm_rope_kernel(QkvEpiArgs e, int m_end) {
+    constexpr int LPR = HD / 8;                  // lanes per row
+    constexpr int TPB = 256 / LPR;               // tokens per workgroup
+    const int li = threadIdx.x % LPR;
+    const int t = blockIdx.x * TPB + threadIdx.x / LPR;    // token, < m_end <= 2^31
+    if (t >= m_end) return;                      // whole lane groups leave together
+    const int S = e.seq;
+    const int b = t / S, si = t - b * S;
+    const int h0 = blockIdx.y * kQkNormGroup, nh = e.heads + e.kv_heads;
+    bf16 *ptr[kQkNormGroup];
+    bf16x8 raw[kQkNormGroup];
+#pragma unroll
+    for (int g = 0; g < kQkNormGroup; ++g) {
+        const int hh = min(h0 + g, nh - 1);       // (a short last group repeats its last head, not stored twice)
+        ptr[g] = hh < e.heads ? (bf16 *)e.q + (((size_t)b * e.heads + hh) * S + si) * HD + li * 8
+                              : (bf16 *)e.k + (((size_t)b * e.kv_heads + (hh - e.heads)) * S + si) * HD + li * 8;
+        raw[g] = *(const bf16x8 *)ptr[g];
+    }
+    // this lane's RoPE coefficients: 4 interleaved pairs or 8 rotate-half pairs
+    const float *ct = e.cos_t + (size_t)si * (HD / 2), *st = e.sin_t + (size_t)si * (HD / 2);
+    constexpr int H2 = LPR / 2;                  // lanes per half row (rotate-half)
+    const bool lo = li < H2;
+    const int m0 = RH ? (lo ? li : li - H2) * 8 : li * 4;
+    const floatx4 c0 = *(const floatx4 *)(ct + m0), s0 = *(const floatx4 *)(st + m0);
+    floatx4 c1 = c0, s1 = s0;
+    if constexpr (RH) {
+        c1 = *(const floatx4 *)(ct + m0 + 4);
+        s1 = *(const floatx4 *)(st + m0 + 4);
+    }
+    floatx4 gq0 = {}, gq1 = {}, bq0 = {}, bq1 = {}, gk0 = {}, gk1 = {}, bk0 = {}, bk1 = {};
+    if (e.qk_norm) {
+        gq0 = *(const floatx4 *)(e.q_g + li * 8), gq1 = *(const floatx4 *)(e.q_g + li * 8 + 4);
+        bq0 = *(const floatx4 *)(e.q_b + li * 8), bq1 = *(const floatx4 *)(e.q_b + li * 8 + 4);
+        gk0 = *(const floatx4 *)(e.k_g + li * 8), gk1 = *(const floatx4 *)(e.k_g + li * 8 + 4);
+        bk0 = *(const floatx4 *)(e.k_b + li * 8), bk1 = *(const floatx4 *)(e.k_b + li * 8 + 4);
+    }
+#pragma unroll
+    for (int g = 0; g < kQkNormGroup; ++g) {
+        const int hh = h0 + g;
+        if (hh >= nh) break;
+        const bool isq = hh < e.heads;
+        float y[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) y[u] = (float)raw[g][u];
+        auto rope = [&]() {
+            if constexpr (!RH) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float a0 = y[2 * u], a1 = y[2 * u + 1];
+                    y[2 * u] = a0 * c0[u] - a1 * s0[u];
+                    y[2 * u + 1] = a0 * s0[u] + a1 * c0[u];
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float other = __shfl_xor(y[u], H2, 64);
+                    const float cs = u < 4 ? c0[u] : c1[u - 4], sn = u < 4 ? s0[u] : s1[u - 4];
+                    // first half: a0 = own, a1 = partner; second half: a0 = partner, a1 = own
+                    y[u] = lo ? y[u] * cs - other * sn : other * sn + y[u] * cs;
+                }
+            }
+        };
+        if (RF) rope();
+        if (e.qk_norm) {
+            float mean = 0.f;
+            if constexpr (!RMS) {
+                float a = 0.f;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) a += y[u];
+                mean = group_sum<LPR>(a) * (1.0f / HD);
+            }
+            float v = 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v += (y[u] - mean) * (y[u] - mean);
+            const float rstd = rsqrtf(group_sum<LPR>(v) * (1.0f / HD) + e.eps);
+            const floatx4 g0 = isq ? gq0 : gk0, g1 = isq ? gq1 : gk1, b0 = isq ? bq0 : bk0, b1 = isq ? bq1 : bk1;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                y[u] = (y[u] - mean) * rstd * g0[u] + b0[u];
+                y[u + 4] = (y[u + 4] - mean) * rstd * g1[u] + b1[u];
+            }
+        }
+        if (!RF) rope();
+        bf16x8 o;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) o[u] = f2bf(y[u]);
+        *(bf16x8 *)ptr[g] = o;
+    }
+}
 
 // ---------------------------------------------------------------------------
 // launchers
@@ -1503,12 +1711,65 @@ hipError_t launch_gemm_swiglu_q8(const int8_t *a, const float *a_scale, const in
     return swiglu_any(a, w, M, F, K, act, u, Scales{a_scale, w_scale}, s);
 }
 
+// Rows of a bf16 QKV projection that take the split form: those the tile
+// choice puts in 256 x 256 tiles (all rows, or the full row tiles when a short
+// tail runs in 128-row tiles); 0 when it picks 128-row tiles throughout, when
+// the sequence length is not a multiple of 16 (the split epilogue's condition)
+// and for 64-wide heads (measured slower split: their norm pass moves the same
+// bytes for half the GEMM work).
+static int64_t qkv_split_rows(int64_t M, int N, int seq, int head_dim) {
+    if (head_dim != 128 || seq % 16 || choose_tile(M, N, 1u << kTileS | 1u << kTileHalf, 0) == kTileHalf) return 0;
+    return split_tail_rows(M, N) ? M / 256 * 256 : M;
+}
+
+static hipError_t launch_qk_norm_rope(const QkvEpiArgs &e, int64_t m_end, hipStream_t s) {
+    if (m_end <= 0) return hipSuccess;
+    if (m_end >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    const int tpb = 256 / (e.head_dim / 8);
+    const dim3 grid((unsigned)((m_end + tpb - 1) / tpb), (unsigned)((e.heads + e.kv_heads + kQkNormGroup - 1) / kQkNormGroup));
+#define DIT_QNR(HD_, RMS_, RF_, RH_) \
+    hipLaunchKernelGGL((qk_norm_rope_kernel<HD_, RMS_, RF_, RH_>), grid, dim3(256), 0, s, e, (int)m_end)
+#define DIT_QNR2(HD_, RMS_, RF_) \
+    do { if (e.rope_half) DIT_QNR(HD_, RMS_, RF_, true); else DIT_QNR(HD_, RMS_, RF_, false); } while (0)
+#define DIT_QNR3(HD_) \
+    do { \
+        if (e.rms) { if (e.rope_first) DIT_QNR2(HD_, true, true); else DIT_QNR2(HD_, true, false); } \
+        else { if (e.rope_first) DIT_QNR2(HD_, false, true); else DIT_QNR2(HD_, false, false); } \
+    } while (0)
+    DIT_QNR3(128);
+#undef DIT_QNR3
+#undef DIT_QNR2
+#undef DIT_QNR
+    return hipGetLastError();
+}
+
 template <class SC>
 static hipError_t qkv_any(const void *h, const void *w, int64_t M, int N, int K, const QkvEpiArgs &e, SC sc,
                           hipStream_t s) {
     using T = typename TileSet<SC::kFmt>::S;
     using TH = typename TileSet<SC::kFmt>::Half;
     using TQ = typename std::conditional<SC::kFmt == 2, float, bf16>::type;
+    if constexpr (SC::kFmt == 0) {
+        // bf16 rows in 256 x 256 tiles: the split form (4-wave GEMM with a plain
+        // epilogue, then the in-place qk-norm + RoPE pass); a 128-row tail keeps
+        // the fused 8-wave epilogue, whose rows the pass skips
+        const int64_t m4 = qkv_split_rows(M, N, e.seq, e.head_dim);
+        if (m4 > 0) {
+            hipError_t err = run4(h, w, m4, N, K, RowsIdentity<256>{}, EpiQkvRaw<128>{e}, s);
+            if (err != hipSuccess) return err;
+            if (m4 < M) {
+#define DIT_QKV_TAIL(HD_, RMS_, RF_, RH_) \
+    run<TH>(h, w, M, N, K, RowsIdentity<TH::BN>{}, EpiQkv<HD_, RMS_, RF_, RH_, TQ>{e}, s, sc.a, sc.w, m4)
+#define DIT_QKV_TAIL2(HD_, RMS_, RF_) (e.rope_half ? DIT_QKV_TAIL(HD_, RMS_, RF_, true) : DIT_QKV_TAIL(HD_, RMS_, RF_, false))
+                err = e.rms ? (e.rope_first ? DIT_QKV_TAIL2(128, true, true) : DIT_QKV_TAIL2(128, true, false))
+                            : (e.rope_first ? DIT_QKV_TAIL2(128, false, true) : DIT_QKV_TAIL2(128, false, false));
+#undef DIT_QKV_TAIL2
+#undef DIT_QKV_TAIL
+                if (err != hipSuccess) return err;
+            }
+            return launch_qk_norm_rope(e, m4, s);
+        }
+    }
 #define DIT_QKV_RH(HD_, RMS_, RF_, RH_) \
     run_tail_split<T, TH>(h, w, M, N, K, RowsIdentity<T::BN>{}, EpiQkv<HD_, RMS_, RF_, RH_, TQ>{e}, s, sc.a, sc.w)
 #define DIT_QKV(HD_, RMS_, RF_) \
