@@ -367,7 +367,11 @@ int dit_ln_modulate(const void *x, int32_t x_dtype, int64_t rows, int32_t dim, i
  *   q  [batch, heads, seq, head_dim]
  *   k  [batch, kv_heads, seq, head_dim]
  *   vt [batch, kv_heads, head_dim, seq_pad], seq_pad = dit_seq_pad(seq):
- *      V transposed; positions [seq, seq_pad) are written with zeros. */
+ *      V transposed; positions [seq, seq_pad) are written with zeros.
+ * The bf16 path normalises q and k either from the fp32 projection or, for
+ * 128-wide heads and seq % 16 == 0 when the GEMM fills whole rounds of
+ * 256 x 256 tiles, from the projection rounded to bf16 (written to q / k,
+ * then normalised in place by a second kernel on the same stream). */
 int dit_qkv_rope(const dit_block_desc *desc, const void *h, const void *w_qkv,
                  const float *q_g, const float *q_b, const float *k_g, const float *k_b,
                  const float *rope_cos, const float *rope_sin,
