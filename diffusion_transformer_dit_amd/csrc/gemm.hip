@@ -1282,6 +1282,21 @@ struct EpiQkvRaw {
 // (q heads first): a lane group loads its token's cos / sin and both norms'
 // gamma / beta once, then its kGroup rows, all loads in flight together.
 constexpr int kQkNormGroup = 8;
+// v from lane (lane ^ 1), (lane ^ 2), the mirror in its 8 / 16 lanes, lane ^ 8 (DPP)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+// sum over aligned groups of W = 8 or 16 lanes, the same value in every lane
+template <int W>
+__device__ __forceinline__ float dpp_group_sum(float v) {
+    static_assert(W == 8 || W == 16, "lane group");
+    v += dpp_f32<0xB1>(v);          // quad_perm [1,0,3,2]
+    v += dpp_f32<0x4E>(v);          // quad_perm [2,3,0,1]
+    v += dpp_f32<0x141>(v);         // row_half_mirror: the other quad of the 8
+    if constexpr (W == 16) v += dpp_f32<0x140>(v);   // row_mirror: the other 8 of the 16
+    return v;
+}
 template <int HD, bool RMS, bool RF, bool RH>
 __global__ __launch_bounds__(256)
 void qk_norm_rope_kernel(QkvEpiArgs e, int m_end) {
@@ -1307,71 +1322,79 @@ void qk_norm_rope_kernel(QkvEpiArgs e, int m_end) {
     constexpr int H2 = LPR / 2;                  // lanes per half row (rotate-half)
     const bool lo = li < H2;
     const int m0 = RH ? (lo ? li : li - H2) * 8 : li * 4;
-    const floatx4 c0 = *(const floatx4 *)(ct + m0), s0 = *(const floatx4 *)(st + m0);
+    const floatx4 c0 = *(const floatx4 *)(ct + m0);
+    floatx4 s0 = *(const floatx4 *)(st + m0);
     floatx4 c1 = c0, s1 = s0;
     if constexpr (RH) {
+        // rotate-half: the first half takes own cos - partner sin, the second
+        // partner sin + own cos, i.e. own cos + partner (-+ sin)
         c1 = *(const floatx4 *)(ct + m0 + 4);
         s1 = *(const floatx4 *)(st + m0 + 4);
+        if (lo) { s0 = -s0; s1 = -s1; }
     }
-    floatx4 gq0 = {}, gq1 = {}, bq0 = {}, bq1 = {}, gk0 = {}, gk1 = {}, bk0 = {}, bk1 = {};
-    if (e.qk_norm) {
-        gq0 = *(const floatx4 *)(e.q_g + li * 8), gq1 = *(const floatx4 *)(e.q_g + li * 8 + 4);
-        bq0 = *(const floatx4 *)(e.q_b + li * 8), bq1 = *(const floatx4 *)(e.q_b + li * 8 + 4);
-        gk0 = *(const floatx4 *)(e.k_g + li * 8), gk1 = *(const floatx4 *)(e.k_g + li * 8 + 4);
-        bk0 = *(const floatx4 *)(e.k_b + li * 8), bk1 = *(const floatx4 *)(e.k_b + li * 8 + 4);
-    }
+    // rows g0 .. g1 - 1 of the group, all q rows (Q = 1) or all k rows (Q = 0)
+    auto rows = [&](int g0, int g1, auto q_c) {
+        constexpr bool Q = decltype(q_c)::value;
+        floatx4 ga = {}, gb = {}, ba = {}, bb = {};
+        if (e.qk_norm) {
+            const float *g = Q ? e.q_g : e.k_g, *be = Q ? e.q_b : e.k_b;
+            ga = *(const floatx4 *)(g + li * 8), gb = *(const floatx4 *)(g + li * 8 + 4);
+            ba = *(const floatx4 *)(be + li * 8), bb = *(const floatx4 *)(be + li * 8 + 4);
+        }
 #pragma unroll
-    for (int g = 0; g < kQkNormGroup; ++g) {
-        const int hh = h0 + g;
-        if (hh >= nh) break;
-        const bool isq = hh < e.heads;
-        float y[8];
+        for (int g = 0; g < kQkNormGroup; ++g) {
+            if (g < g0 || g >= g1) continue;
+            float y[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) y[u] = (float)raw[g][u];
-        auto rope = [&]() {
-            if constexpr (!RH) {
+            for (int u = 0; u < 8; ++u) y[u] = (float)raw[g][u];
+            auto rope = [&]() {
+                if constexpr (!RH) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const float a0 = y[2 * u], a1 = y[2 * u + 1];
+                        y[2 * u] = a0 * c0[u] - a1 * s0[u];
+                        y[2 * u + 1] = a0 * s0[u] + a1 * c0[u];
+                    }
+                } else {
+                    static_assert(H2 == 8, "rotate-half partner lane ^ 8");
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const float other = dpp_f32<0x128>(y[u]);   // row_ror 8: lane ^ 8 of 16
+                        const float cs = u < 4 ? c0[u] : c1[u - 4], sn = u < 4 ? s0[u] : s1[u - 4];
+                        y[u] = y[u] * cs + other * sn;
+                    }
+                }
+            };
+            if (RF) rope();
+            if (e.qk_norm) {
+                float mean = 0.f;
+                if constexpr (!RMS) {
+                    float a = 0.f;
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) a += y[u];
+                    mean = dpp_group_sum<LPR>(a) * (1.0f / HD);
+                }
+                float v = 0.f;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v += (y[u] - mean) * (y[u] - mean);
+                const float rstd = rsqrtf(dpp_group_sum<LPR>(v) * (1.0f / HD) + e.eps);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const float a0 = y[2 * u], a1 = y[2 * u + 1];
-                    y[2 * u] = a0 * c0[u] - a1 * s0[u];
-                    y[2 * u + 1] = a0 * s0[u] + a1 * c0[u];
-                }
-            } else {
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const float other = __shfl_xor(y[u], H2, 64);
-                    const float cs = u < 4 ? c0[u] : c1[u - 4], sn = u < 4 ? s0[u] : s1[u - 4];
-                    // first half: a0 = own, a1 = partner; second half: a0 = partner, a1 = own
-                    y[u] = lo ? y[u] * cs - other * sn : other * sn + y[u] * cs;
+                    y[u] = (y[u] - mean) * rstd * ga[u] + ba[u];
+                    y[u + 4] = (y[u + 4] - mean) * rstd * gb[u] + bb[u];
                 }
             }
-        };
-        if (RF) rope();
-        if (e.qk_norm) {
-            float mean = 0.f;
-            if constexpr (!RMS) {
-                float a = 0.f;
+            if (!RF) rope();
+            bf16x8 o;
 #pragma unroll
-                for (int u = 0; u < 8; ++u) a += y[u];
-                mean = group_sum<LPR>(a) * (1.0f / HD);
-            }
-            float v = 0.f;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) v += (y[u] - mean) * (y[u] - mean);
-            const float rstd = rsqrtf(group_sum<LPR>(v) * (1.0f / HD) + e.eps);
-            const floatx4 g0 = isq ? gq0 : gk0, g1 = isq ? gq1 : gk1, b0 = isq ? bq0 : bk0, b1 = isq ? bq1 : bk1;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                y[u] = (y[u] - mean) * rstd * g0[u] + b0[u];
-                y[u + 4] = (y[u + 4] - mean) * rstd * g1[u] + b1[u];
-            }
+            for (int u = 0; u < 8; ++u) o[u] = f2bf(y[u]);
+            *(bf16x8 *)ptr[g] = o;
         }
-        if (!RF) rope();
-        bf16x8 o;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) o[u] = f2bf(y[u]);
-        *(bf16x8 *)ptr[g] = o;
-    }
+    };
+    // q rows: heads h0 .. min(heads, h0 + group); k rows after them (group-uniform)
+    const int nq = min(max(e.heads - h0, 0), kQkNormGroup), nall = min(nh - h0, kQkNormGroup);
+    if (nq > 0) rows(0, nq, std::true_type{});
+    if (nall > nq) rows(nq, nall, std::false_type{});
 }
 
 // ---------------------------------------------------------------------------
