@@ -1226,43 +1226,95 @@ struct EpiQkvRaw {
         for (int e_ = 0; e_ < 4; ++e_) qo[e_] = (uint32_t)((lq * 4 + e_) * HD + l16) * 2u;
         const uint32_t vo = ((uint32_t)l16 * (uint32_t)spad + (uint32_t)lq * 4u) * 2u;
         // SEC: the section of every block of the wave (0 q, 1 k, 2 v), or -1 for a
-        // wave whose columns cross a section boundary (hd 64 only)
+        // wave whose columns cross a section boundary (hd 64 only).  Stores are
+        // ordered so that each 128-byte line is written by consecutive stores
+        // (whole lines reach L2 together, no partial-line write-backs): a q / k
+        // row's column blocks back to back, a v^T row's 16-token pieces back to
+        // back (the row blocks innermost).
+        auto offsets = [&](int i, size_t &oq, size_t &ok, size_t &ov) {
+            const int t0 = row0 + i * 16;
+            const int b0 = t0 / S, s0 = t0 - b0 * S;
+            oq = ((size_t)b0 * e.heads * S + s0) * HD * 2;
+            ok = ((size_t)b0 * e.kv_heads * S + s0) * HD * 2;
+            ov = ((size_t)b0 * e.kv_heads * HD * spad + s0) * 2;
+        };
         auto store = [&](auto sec_c) {
             constexpr int SEC = decltype(sec_c)::value;
+            if constexpr (SEC == 2) {
+                size_t ov[T::TM];
 #pragma unroll
-            for (int i = 0; i < T::TM; ++i) {
-                const int t0 = row0 + i * 16;                 // token of the block's first row
-                if (t0 < M) {
-                    const int b0 = t0 / S, s0 = t0 - b0 * S;
-                    // byte offsets of (b0, s0) in q, k and v^T
-                    const size_t oq = ((size_t)b0 * e.heads * S + s0) * HD * 2;
-                    const size_t ok = ((size_t)b0 * e.kv_heads * S + s0) * HD * 2;
-                    const size_t ov = ((size_t)b0 * e.kv_heads * HD * spad + s0) * 2;
+                for (int i = 0; i < T::TM; ++i) {
+                    size_t oq_, ok_;
+                    offsets(min(i, (M - 1 - row0) / 16), oq_, ok_, ov[i]);   // (rows past M: not stored)
+                }
 #pragma unroll
-                    for (int j = 0; j < T::TN; ++j) {
-                        float z[4];
+                for (int j = 0; j < T::TN; ++j) {
 #pragma unroll
-                        for (int e_ = 0; e_ < 4; ++e_) z[e_] = acc_get<T>(acc[i][j], e_);
-                        const int sj = SEC >= 0 ? SEC : sect[j];
-                        if (sj < 2) {
-                            uint8_t *base = cbase[j] + (sj == 0 ? oq : ok);
-#pragma unroll
-                            for (int e_ = 0; e_ < 4; e_ += 2) {
-                                uint32_t pk;   // both rounded to nearest even (the plain conversion's rounding)
-                                asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(pk) : "v"(z[e_]), "v"(z[e_ + 1]));
-                                *(uint16_t *)(base + qo[e_]) = (uint16_t)pk;
-                                *(uint16_t *)(base + qo[e_ + 1]) = (uint16_t)(pk >> 16);
-                            }
-                        } else {
+                    for (int i = 0; i < T::TM; ++i) {
+                        if (row0 + i * 16 < M) {
                             uint32_t p0, p1;
-                            asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(p0) : "v"(z[0]), "v"(z[1]));
-                            asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(p1) : "v"(z[2]), "v"(z[3]));
+                            asm("v_cvt_pk_bf16_f32 %0, %1, %2"
+                                : "=v"(p0) : "v"(acc_get<T>(acc[i][j], 0)), "v"(acc_get<T>(acc[i][j], 1)));
+                            asm("v_cvt_pk_bf16_f32 %0, %1, %2"
+                                : "=v"(p1) : "v"(acc_get<T>(acc[i][j], 2)), "v"(acc_get<T>(acc[i][j], 3)));
                             typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-                            *(u32x2 *)(cbase[j] + ov + vo) = u32x2{p0, p1};
+                            *(u32x2 *)(cbase[j] + ov[i] + vo) = u32x2{p0, p1};
                         }
                     }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                __builtin_amdgcn_sched_barrier(0);
+            } else {
+#pragma unroll
+                for (int i = 0; i < T::TM; ++i) {
+                    if (row0 + i * 16 < M) {
+                        size_t oq, ok, ov;
+                        offsets(i, oq, ok, ov);
+                        if constexpr (SEC >= 0) {
+                            // rows 4 lq + e (pairs share a conversion), each row's
+                            // column blocks stored back to back
+                            uint32_t pk[T::TN][2];
+#pragma unroll
+                            for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+                                for (int h = 0; h < 2; ++h)
+                                    asm("v_cvt_pk_bf16_f32 %0, %1, %2"
+                                        : "=v"(pk[j][h])
+                                        : "v"(acc_get<T>(acc[i][j], 2 * h)), "v"(acc_get<T>(acc[i][j], 2 * h + 1)));
+#pragma unroll
+                            for (int e_ = 0; e_ < 4; ++e_)
+#pragma unroll
+                                for (int j = 0; j < T::TN; ++j) {
+                                    uint8_t *base = cbase[j] + (SEC == 0 ? oq : ok);
+                                    const uint32_t w = pk[j][e_ >> 1];
+                                    *(uint16_t *)(base + qo[e_]) = (uint16_t)((e_ & 1) ? (w >> 16) : w);
+                                }
+                        } else {
+#pragma unroll
+                            for (int j = 0; j < T::TN; ++j) {
+                                float z[4];
+#pragma unroll
+                                for (int e_ = 0; e_ < 4; ++e_) z[e_] = acc_get<T>(acc[i][j], e_);
+                                if (sect[j] < 2) {
+                                    uint8_t *base = cbase[j] + (sect[j] == 0 ? oq : ok);
+#pragma unroll
+                                    for (int e_ = 0; e_ < 4; e_ += 2) {
+                                        uint32_t pk;
+                                        asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(pk) : "v"(z[e_]), "v"(z[e_ + 1]));
+                                        *(uint16_t *)(base + qo[e_]) = (uint16_t)pk;
+                                        *(uint16_t *)(base + qo[e_ + 1]) = (uint16_t)(pk >> 16);
+                                    }
+                                } else {
+                                    uint32_t p0, p1;
+                                    asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(p0) : "v"(z[0]), "v"(z[1]));
+                                    asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(p1) : "v"(z[2]), "v"(z[3]));
+                                    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                                    *(u32x2 *)(cbase[j] + ov + vo) = u32x2{p0, p1};
+                                }
+                            }
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         };
         if (sect[0] != sect[T::TN - 1]) store(std::integral_constant<int, -1>{});
