@@ -1196,9 +1196,10 @@ struct EpiQkvRaw {
     static constexpr bool kDequant = false;
     QkvEpiArgs e;
     template <class T> static constexpr int lds_bytes() { return 0; }
-    // Taken only when the sequence length is a multiple of 16: a 16-row block
-    // then never crosses a sequence boundary (and M, a multiple of it, never
-    // cuts one), and v^T's 4-token groups are 8-byte aligned.
+    // Taken only when every 16-row block lies in one sequence and below M (a
+    // single sequence, or a sequence length that is a multiple of 16, and M a
+    // multiple of 16); a block's first position is then a multiple of 4, so
+    // v^T's 4-token groups are 8-byte aligned.
     template <class T>
     __device__ __forceinline__ void apply(floatx4 (&acc)[T::TM][T::TN], int row0, int tn, int wn, int lane, int M,
                                           uint8_t *) const {
@@ -1788,13 +1789,17 @@ hipError_t launch_gemm_swiglu_q8(const int8_t *a, const float *a_scale, const in
 
 // Rows of a bf16 QKV projection that take the split form: those the tile
 // choice puts in 256 x 256 tiles (all rows, or the full row tiles when a short
-// tail runs in 128-row tiles); 0 when it picks 128-row tiles throughout, when
-// the sequence length is not a multiple of 16 (the split epilogue's condition)
-// and for 64-wide heads (measured slower split: their norm pass moves the same
-// bytes for half the GEMM work).
-static int64_t qkv_split_rows(int64_t M, int N, int seq, int head_dim) {
-    if (head_dim != 128 || seq % 16 || choose_tile(M, N, 1u << kTileS | 1u << kTileHalf, 0) == kTileHalf) return 0;
-    return split_tail_rows(M, N) ? M / 256 * 256 : M;
+// tail runs in 128-row tiles).  0 (the fused epilogue throughout) when it picks
+// 128-row tiles, for 64-wide heads (measured slower split: their norm pass
+// moves the same bytes for half the GEMM work), and unless every 16-row block
+// of the split rows lies in one sequence and below the row count (the split
+// epilogue's condition): a row count that is a multiple of 16 and one
+// sequence or a sequence length that is a multiple of 16.
+static int64_t qkv_split_rows(int64_t M, int N, int batch, int seq, int head_dim) {
+    if (head_dim != 128 || choose_tile(M, N, 1u << kTileS | 1u << kTileHalf, 0) == kTileHalf) return 0;
+    const int64_t m4 = split_tail_rows(M, N) ? M / 256 * 256 : M;
+    if (m4 % 16 || (batch > 1 && seq % 16)) return 0;
+    return m4;
 }
 
 static hipError_t launch_qk_norm_rope(const QkvEpiArgs &e, int64_t m_end, hipStream_t s) {
@@ -1828,7 +1833,7 @@ static hipError_t qkv_any(const void *h, const void *w, int64_t M, int N, int K,
         // bf16 rows in 256 x 256 tiles: the split form (4-wave GEMM with a plain
         // epilogue, then the in-place qk-norm + RoPE pass); a 128-row tail keeps
         // the fused 8-wave epilogue, whose rows the pass skips
-        const int64_t m4 = qkv_split_rows(M, N, e.seq, e.head_dim);
+        const int64_t m4 = qkv_split_rows(M, N, e.batch, e.seq, e.head_dim);
         if (m4 > 0) {
             hipError_t err = run4(h, w, m4, N, K, RowsIdentity<256>{}, EpiQkvRaw<128>{e}, s);
             if (err != hipSuccess) return err;

@@ -112,7 +112,7 @@ QKV_TAIL = I.DiTConfig("qkv_tail_4170", 25, 1, (1, 30, 139), 2048, 16, 8, 128, 4
 # sequence length that is a multiple of 16 the projection takes the split form
 # (plain-epilogue 4-wave GEMM, then the in-place qk-norm + RoPE pass).  Two
 # sequences of 1008 tokens, GQA 32 / 16 heads, a ragged last row tile; 1904
-# tokens, GQA 32 / 8, rotate-half RoPE before an RMS qk-norm.  The third keeps
+# tokens, GQA 32 / 8, rotate-half RoPE before an RMS qk-norm.  The last keeps
 # the fused epilogue (64-wide heads, 1899 tokens) at a similar size.
 QKV_SPLIT = {
     "qkv_split_b2_1008": I.DiTConfig("qkv_split_b2_1008", 26, 2, (1, 28, 36), 4096, 32, 16, 128, 256, 256, True,
@@ -120,6 +120,10 @@ QKV_SPLIT = {
     "qkv_split_half_1904": I.DiTConfig("qkv_split_half_1904", 41, 1, (1, 28, 68), 4096, 32, 8, 128, 256, 256, True,
                                        "half2d", (64, 64), 100.0, x_dtype="bf16", norm="rmsnorm",
                                        qk_order="rope_norm"),
+    # one sequence of 4170 tokens (not a multiple of 16): the 4096 rows of full
+    # 256-row tiles split, the 74-row tail in the fused 128-row launch
+    "qkv_split_joint_4170": I.DiTConfig("qkv_split_joint_4170", 42, 1, (1, 30, 139), 4096, 32, 32, 128, 256, 256, True,
+                                        "interleaved3d", (32, 48, 48), 256.0, x_dtype="bf16"),
     "qkv_fused_hd64_1899": I.DiTConfig("qkv_fused_hd64_1899", 27, 1, (1, 9, 211), 4096, 64, 32, 64, 256, 256, True,
                                        "half2d", (32, 32), 100.0, x_dtype="bf16", norm="rmsnorm",
                                        qk_order="rope_norm"),
@@ -129,7 +133,7 @@ QKV_SPLIT = {
 @pytest.mark.parametrize("name", ["c1_rms", "c1_rope_first", "hd128_ernie_diagram", "half_hd128_rope_first",
                                   "c1_tiny", "c1_ragged200", "hd128_ragged400", "gqa3_b2_ragged300", "vit_b2_f32",
                                   "c1_f32x_t3", "qkv_tail_4170", "qkv_split_b2_1008", "qkv_split_half_1904",
-                                  "qkv_fused_hd64_1899"])
+                                  "qkv_split_joint_4170", "qkv_fused_hd64_1899"])
 def test_qkv_rope(name):
     import torch
     cfg = QKV_TAIL if name == "qkv_tail_4170" else QKV_SPLIT.get(name) or SMALL[name]
