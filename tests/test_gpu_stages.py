@@ -124,6 +124,13 @@ QKV_SPLIT = {
     # 256-row tiles split, the 74-row tail in the fused 128-row launch
     "qkv_split_joint_4170": I.DiTConfig("qkv_split_joint_4170", 42, 1, (1, 30, 139), 4096, 32, 32, 128, 256, 256, True,
                                         "interleaved3d", (32, 48, 48), 256.0, x_dtype="bf16"),
+    # 34 q heads and 2 k heads: the qk-norm pass's last group of 8 heads holds
+    # both q and k rows
+    "qkv_split_mixed_group_3072": I.DiTConfig("qkv_split_mixed_group_3072", 43, 1, (1, 48, 64), 4352, 34, 2, 128, 256,
+                                              256, True, "interleaved3d", (32, 48, 48), 256.0, x_dtype="bf16"),
+    # no qk-norm: the pass applies RoPE only
+    "qkv_split_no_qknorm_b2_1008": I.DiTConfig("qkv_split_no_qknorm_b2_1008", 44, 2, (1, 28, 36), 4096, 32, 16, 128,
+                                               256, 256, False, "interleaved3d", (32, 48, 48), 256.0, x_dtype="bf16"),
     "qkv_fused_hd64_1899": I.DiTConfig("qkv_fused_hd64_1899", 27, 1, (1, 9, 211), 4096, 64, 32, 64, 256, 256, True,
                                        "half2d", (32, 32), 100.0, x_dtype="bf16", norm="rmsnorm",
                                        qk_order="rope_norm"),
@@ -133,7 +140,8 @@ QKV_SPLIT = {
 @pytest.mark.parametrize("name", ["c1_rms", "c1_rope_first", "hd128_ernie_diagram", "half_hd128_rope_first",
                                   "c1_tiny", "c1_ragged200", "hd128_ragged400", "gqa3_b2_ragged300", "vit_b2_f32",
                                   "c1_f32x_t3", "qkv_tail_4170", "qkv_split_b2_1008", "qkv_split_half_1904",
-                                  "qkv_split_joint_4170", "qkv_fused_hd64_1899"])
+                                  "qkv_split_joint_4170", "qkv_split_mixed_group_3072", "qkv_split_no_qknorm_b2_1008",
+                                  "qkv_fused_hd64_1899"])
 def test_qkv_rope(name):
     import torch
     cfg = QKV_TAIL if name == "qkv_tail_4170" else QKV_SPLIT.get(name) or SMALL[name]
