@@ -35,6 +35,7 @@ template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64, int NS_ = 2, int ES_
 struct Tile {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_, ES = ES_;
     static constexpr int kWaves = WM * WN;
+    static constexpr bool kAgpr = false;   // accumulators in AGPRs (the persistent 4-wave kernel's tiles)
     static constexpr int kThreads = kWaves * kWave;
     static constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
     static constexpr int TM = kWaveM / 16, TN = kWaveN / 16;    // 16 x 16 MFMA blocks per wave
@@ -398,9 +399,16 @@ void gemm_kernel(const void *__restrict__ A, const void *__restrict__ W, int M, 
 // epilogue runs (reading each accumulator from its AGPR where it is used), so
 // the copies' latency and the workgroup launch are off the critical path.
 // ---------------------------------------------------------------------------
-using Tile4w = Tile<256, 256, 2, 2>;   // BK 64, 2 LDS stages of 64 KiB
+// its tiles: bf16 (BK 64, 2 LDS stages of 64 KiB) and int8 operands (BK 128,
+// int32 sums in the accumulators, dequantized by the epilogue where read)
+struct Tile4w : Tile<256, 256, 2, 2> { static constexpr bool kAgpr = true; };
+struct Tile4wQ : Tile<256, 256, 2, 2, 128, 2, 1> { static constexpr bool kAgpr = true; };
 
-#define DIT_MF(c, a, b) "v_mfma_f32_16x16x32_bf16 %[" #c "], %[" #a "], %[" #b "], %[" #c "]\n\t"
+// INS: the MFMA instruction, v_mfma_f32_16x16x32_bf16 (bf16 operands) or
+// v_mfma_i32_16x16x64_i8 (int8 operands: int32 sums in the accumulators)
+#define DIT_INS_BF16 "v_mfma_f32_16x16x32_bf16"
+#define DIT_INS_I8 "v_mfma_i32_16x16x64_i8"
+#define DIT_MF(INS, c, a, b) INS " %[" #c "], %[" #a "], %[" #b "], %[" #c "]\n\t"
 #define DIT_RD(dst, base, off) "ds_read_b128 %[" #dst "], %[" #base "] offset:%[" #off "]\n\t"
 // copy j of a block: M0 = LDS destination (the add also sets SCC, declared clobbered)
 #define DIT_CP(j) "s_add_u32 m0, %[lb], %[d" #j "]\n\t"
@@ -426,51 +434,51 @@ using Tile4w = Tile<256, 256, 2, 2>;   // BK 64, 2 LDS stages of 64 KiB
         [d2] "i"((doff_) + 8192), [d3] "i"((doff_) + 12288)
 
 // k-step 0 block: 16 MFMAs with four fragment reads
-#define DIT_K4_STEP(acc_, fa_, fb_, na_, nb_, i0, adA, adB)                                                \
-    asm volatile(DIT_RD(na0, pa, oa0) DIT_MF(c00, a0, b0) DIT_RD(na1, pa, oa1) DIT_MF(c01, a0, b1)         \
-                 DIT_RD(nb0, pb, oa0) DIT_MF(c02, a0, b2) DIT_RD(nb1, pb, oa1) DIT_MF(c03, a0, b3)         \
-                 DIT_MF(c04, a0, b4) DIT_MF(c05, a0, b5) DIT_MF(c06, a0, b6) DIT_MF(c07, a0, b7)           \
-                 DIT_MF(c10, a1, b0) DIT_MF(c11, a1, b1) DIT_MF(c12, a1, b2) DIT_MF(c13, a1, b3)           \
-                 DIT_MF(c14, a1, b4) DIT_MF(c15, a1, b5) DIT_MF(c16, a1, b6) DIT_MF(c17, a1, b7)           \
+#define DIT_K4_STEP(INS, acc_, fa_, fb_, na_, nb_, i0, adA, adB)                                                \
+    asm volatile(DIT_RD(na0, pa, oa0) DIT_MF(INS, c00, a0, b0) DIT_RD(na1, pa, oa1) DIT_MF(INS, c01, a0, b1)         \
+                 DIT_RD(nb0, pb, oa0) DIT_MF(INS, c02, a0, b2) DIT_RD(nb1, pb, oa1) DIT_MF(INS, c03, a0, b3)         \
+                 DIT_MF(INS, c04, a0, b4) DIT_MF(INS, c05, a0, b5) DIT_MF(INS, c06, a0, b6) DIT_MF(INS, c07, a0, b7)           \
+                 DIT_MF(INS, c10, a1, b0) DIT_MF(INS, c11, a1, b1) DIT_MF(INS, c12, a1, b2) DIT_MF(INS, c13, a1, b3)           \
+                 DIT_MF(INS, c14, a1, b4) DIT_MF(INS, c15, a1, b5) DIT_MF(INS, c16, a1, b6) DIT_MF(INS, c17, a1, b7)           \
                  "s_waitcnt lgkmcnt(0)"                                                                    \
                  : DIT_K4_OPERANDS("+a", acc_, fa_, fb_, na_, nb_, i0, adA, adB)                                 \
                  : "memory")
 // the same block for k-step 0 of a tile's first K stage: each MFMA starts its
 // sum from an inline zero, so no accumulator is cleared beforehand
-#define DIT_MZ(c, a, b) "v_mfma_f32_16x16x32_bf16 %[" #c "], %[" #a "], %[" #b "], 0\n\t"
-#define DIT_K4_STEP_Z(acc_, fa_, fb_, na_, nb_, i0, adA, adB)                                              \
-    asm volatile(DIT_RD(na0, pa, oa0) DIT_MZ(c00, a0, b0) DIT_RD(na1, pa, oa1) DIT_MZ(c01, a0, b1)         \
-                 DIT_RD(nb0, pb, oa0) DIT_MZ(c02, a0, b2) DIT_RD(nb1, pb, oa1) DIT_MZ(c03, a0, b3)         \
-                 DIT_MZ(c04, a0, b4) DIT_MZ(c05, a0, b5) DIT_MZ(c06, a0, b6) DIT_MZ(c07, a0, b7)           \
-                 DIT_MZ(c10, a1, b0) DIT_MZ(c11, a1, b1) DIT_MZ(c12, a1, b2) DIT_MZ(c13, a1, b3)           \
-                 DIT_MZ(c14, a1, b4) DIT_MZ(c15, a1, b5) DIT_MZ(c16, a1, b6) DIT_MZ(c17, a1, b7)           \
+#define DIT_MZ(INS, c, a, b) INS " %[" #c "], %[" #a "], %[" #b "], 0\n\t"
+#define DIT_K4_STEP_Z(INS, acc_, fa_, fb_, na_, nb_, i0, adA, adB)                                              \
+    asm volatile(DIT_RD(na0, pa, oa0) DIT_MZ(INS, c00, a0, b0) DIT_RD(na1, pa, oa1) DIT_MZ(INS, c01, a0, b1)         \
+                 DIT_RD(nb0, pb, oa0) DIT_MZ(INS, c02, a0, b2) DIT_RD(nb1, pb, oa1) DIT_MZ(INS, c03, a0, b3)         \
+                 DIT_MZ(INS, c04, a0, b4) DIT_MZ(INS, c05, a0, b5) DIT_MZ(INS, c06, a0, b6) DIT_MZ(INS, c07, a0, b7)           \
+                 DIT_MZ(INS, c10, a1, b0) DIT_MZ(INS, c11, a1, b1) DIT_MZ(INS, c12, a1, b2) DIT_MZ(INS, c13, a1, b3)           \
+                 DIT_MZ(INS, c14, a1, b4) DIT_MZ(INS, c15, a1, b5) DIT_MZ(INS, c16, a1, b6) DIT_MZ(INS, c17, a1, b7)           \
                  "s_waitcnt lgkmcnt(0)"                                                                    \
                  : DIT_K4_OPERANDS("=a", acc_, fa_, fb_, na_, nb_, i0, adA, adB)                           \
                  : "memory")
 // first k-step 1 block: 8 MFMAs, the next stage's wait and the barrier, then
 // 8 MFMAs with four reads and four copies
-#define DIT_K4_STEP_BARRIER(acc_, fa_, fb_, na_, nb_, i0, adA, adB, rsrc_, ldsb_, soff_, vo_, doff_)       \
-    asm volatile(DIT_MF(c00, a0, b0) DIT_MF(c01, a0, b1) DIT_MF(c02, a0, b2) DIT_MF(c03, a0, b3)           \
-                 DIT_MF(c04, a0, b4) DIT_MF(c05, a0, b5) DIT_MF(c06, a0, b6) DIT_MF(c07, a0, b7)           \
+#define DIT_K4_STEP_BARRIER(INS, acc_, fa_, fb_, na_, nb_, i0, adA, adB, rsrc_, ldsb_, soff_, vo_, doff_)       \
+    asm volatile(DIT_MF(INS, c00, a0, b0) DIT_MF(INS, c01, a0, b1) DIT_MF(INS, c02, a0, b2) DIT_MF(INS, c03, a0, b3)           \
+                 DIT_MF(INS, c04, a0, b4) DIT_MF(INS, c05, a0, b5) DIT_MF(INS, c06, a0, b6) DIT_MF(INS, c07, a0, b7)           \
                  "s_waitcnt vmcnt(0)\n\ts_barrier\n\t"                                                     \
-                 DIT_RD(na0, pa, oa0) DIT_CP(0) DIT_MF(c10, a1, b0) DIT_LD(0) DIT_MF(c11, a1, b1)          \
-                 DIT_RD(na1, pa, oa1) DIT_CP(1) DIT_MF(c12, a1, b2) DIT_LD(1) DIT_MF(c13, a1, b3)          \
-                 DIT_RD(nb0, pb, oa0) DIT_CP(2) DIT_MF(c14, a1, b4) DIT_LD(2) DIT_MF(c15, a1, b5)          \
-                 DIT_RD(nb1, pb, oa1) DIT_CP(3) DIT_MF(c16, a1, b6) DIT_LD(3) DIT_MF(c17, a1, b7)          \
+                 DIT_RD(na0, pa, oa0) DIT_CP(0) DIT_MF(INS, c10, a1, b0) DIT_LD(0) DIT_MF(INS, c11, a1, b1)          \
+                 DIT_RD(na1, pa, oa1) DIT_CP(1) DIT_MF(INS, c12, a1, b2) DIT_LD(1) DIT_MF(INS, c13, a1, b3)          \
+                 DIT_RD(nb0, pb, oa0) DIT_CP(2) DIT_MF(INS, c14, a1, b4) DIT_LD(2) DIT_MF(INS, c15, a1, b5)          \
+                 DIT_RD(nb1, pb, oa1) DIT_CP(3) DIT_MF(INS, c16, a1, b6) DIT_LD(3) DIT_MF(INS, c17, a1, b7)          \
                  "s_waitcnt lgkmcnt(0)"                                                                    \
                  : DIT_K4_OPERANDS("+a", acc_, fa_, fb_, na_, nb_, i0, adA, adB)                                 \
                      DIT_K4_COPIES(rsrc_, ldsb_, soff_, vo_, doff_)                                        \
                  : "memory", "m0", "scc")
 // other k-step 1 blocks: one read and one copy per four MFMAs
-#define DIT_K4_STEP_COPY(acc_, fa_, fb_, na_, nb_, i0, adA, adB, rsrc_, ldsb_, soff_, vo_, doff_)          \
-    asm volatile(DIT_MF(c00, a0, b0) DIT_RD(na0, pa, oa0) DIT_MF(c01, a0, b1) DIT_CP(0)                    \
-                 DIT_MF(c02, a0, b2) DIT_LD(0) DIT_MF(c03, a0, b3)                                         \
-                 DIT_MF(c04, a0, b4) DIT_RD(na1, pa, oa1) DIT_MF(c05, a0, b5) DIT_CP(1)                    \
-                 DIT_MF(c06, a0, b6) DIT_LD(1) DIT_MF(c07, a0, b7)                                         \
-                 DIT_MF(c10, a1, b0) DIT_RD(nb0, pb, oa0) DIT_MF(c11, a1, b1) DIT_CP(2)                    \
-                 DIT_MF(c12, a1, b2) DIT_LD(2) DIT_MF(c13, a1, b3)                                         \
-                 DIT_MF(c14, a1, b4) DIT_RD(nb1, pb, oa1) DIT_MF(c15, a1, b5) DIT_CP(3)                    \
-                 DIT_MF(c16, a1, b6) DIT_LD(3) DIT_MF(c17, a1, b7)                                         \
+#define DIT_K4_STEP_COPY(INS, acc_, fa_, fb_, na_, nb_, i0, adA, adB, rsrc_, ldsb_, soff_, vo_, doff_)          \
+    asm volatile(DIT_MF(INS, c00, a0, b0) DIT_RD(na0, pa, oa0) DIT_MF(INS, c01, a0, b1) DIT_CP(0)                    \
+                 DIT_MF(INS, c02, a0, b2) DIT_LD(0) DIT_MF(INS, c03, a0, b3)                                         \
+                 DIT_MF(INS, c04, a0, b4) DIT_RD(na1, pa, oa1) DIT_MF(INS, c05, a0, b5) DIT_CP(1)                    \
+                 DIT_MF(INS, c06, a0, b6) DIT_LD(1) DIT_MF(INS, c07, a0, b7)                                         \
+                 DIT_MF(INS, c10, a1, b0) DIT_RD(nb0, pb, oa0) DIT_MF(INS, c11, a1, b1) DIT_CP(2)                    \
+                 DIT_MF(INS, c12, a1, b2) DIT_LD(2) DIT_MF(INS, c13, a1, b3)                                         \
+                 DIT_MF(INS, c14, a1, b4) DIT_RD(nb1, pb, oa1) DIT_MF(INS, c15, a1, b5) DIT_CP(3)                    \
+                 DIT_MF(INS, c16, a1, b6) DIT_LD(3) DIT_MF(INS, c17, a1, b7)                                         \
                  "s_waitcnt lgkmcnt(0)"                                                                    \
                  : DIT_K4_OPERANDS("+a", acc_, fa_, fb_, na_, nb_, i0, adA, adB)                                 \
                      DIT_K4_COPIES(rsrc_, ldsb_, soff_, vo_, doff_)                                        \
@@ -490,8 +498,10 @@ __global__ __launch_bounds__(256, 1)
 void gemm4_kernel(const void *__restrict__ A, const void *__restrict__ W, int M, int K, int w_rows, int tiles_m,
                   int tiles_n, RowMap rowmap, Epi epi, int m_base) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    static_assert(T::kWaves == 4 && T::TM == 8 && T::TN == 8 && T::ES == 2 && T::NS == 2 && T::BK == 64 &&
-                  T::kALoads == 8 && T::kBLoads == 8 && T::kStageBytes == 65536, "the 4-wave 256 x 256 bf16 tile");
+    static_assert(T::kAgpr && T::kWaves == 4 && T::TM == 8 && T::TN == 8 && (T::ES == 2 || T::ES == 1) &&
+                      T::NS == 2 && T::kRowBytes == 128 && T::kALoads == 8 && T::kBLoads == 8 &&
+                      T::kStageBytes == 65536,
+                  "the 4-wave 256 x 256 tile: bf16 (64-deep K tiles) or int8 (128-deep)");
     // the next tile's first two K stages are copied into LDS while the
     // epilogue of the current one runs, so the epilogue may not use LDS
     static_assert(Epi::template lds_bytes<T>() == 0, "epilogue LDS");
@@ -503,7 +513,8 @@ void gemm4_kernel(const void *__restrict__ A, const void *__restrict__ W, int M,
 
     // Copies as in gemm_kernel: copy q (0-7: A rows, 8-15: W rows) of wave w
     // moves tile rows 8 (4 q + w) .. + 7 into 1 KiB of its stage.
-    const uint32_t a_bytes = (uint32_t)M * (uint32_t)K * 2u, w_bytes = (uint32_t)w_rows * (uint32_t)K * 2u;
+    constexpr uint32_t ES = T::ES;
+    const uint32_t a_bytes = (uint32_t)M * (uint32_t)K * ES, w_bytes = (uint32_t)w_rows * (uint32_t)K * ES;
     uint32_t a_off[8], b_off[8];
     auto tile_offsets = [&](int tm_, int tn_) {
         const int m0_ = m_base + tm_ * T::BM;
@@ -513,8 +524,8 @@ void gemm4_kernel(const void *__restrict__ A, const void *__restrict__ W, int M,
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const int r = (q * 4 + wave) * T::kRowsPerLoad + lr_;
-            a_off[q] = (uint32_t)min(m0_ + r, M - 1) * (uint32_t)K * 2u + (uint32_t)((ls_ ^ T::swz(r)) << 4);
-            b_off[q] = (uint32_t)rowmap(tn_, r) * (uint32_t)K * 2u + (uint32_t)((ls_ ^ T::swz(r)) << 4);
+            a_off[q] = (uint32_t)min(m0_ + r, M - 1) * (uint32_t)K * ES + (uint32_t)((ls_ ^ T::swz(r)) << 4);
+            b_off[q] = (uint32_t)rowmap(tn_, r) * (uint32_t)K * ES + (uint32_t)((ls_ ^ T::swz(r)) << 4);
         }
     };
     // the same two buffer resources as plain dwords for the copies inside the
@@ -530,7 +541,7 @@ void gemm4_kernel(const void *__restrict__ A, const void *__restrict__ W, int M,
     // K tiles 0 and 1 of a tile into the two stages: copy q of A rows and of W
     // rows to + q * 4 KiB of the stage's A and W halves (as in the K loop, M0
     // holds the LDS destination); stage 0 goes out first
-    const uint32_t lbw = lds0 + wave * 1024, kb1 = (uint32_t)(min(1, KT - 1) * T::BK * 2);
+    const uint32_t lbw = lds0 + wave * 1024, kb1 = (uint32_t)(min(1, KT - 1) * T::kRowBytes);
 #define DIT_PCP(m0off, vo, rs, kb) \
     "s_add_u32 m0, %[lb], " #m0off "\n\tbuffer_load_dwordx4 %[" #vo "], %[" #rs "], %[" #kb "] offen lds\n\t"
     auto issue_first_stages = [&]() {
@@ -601,23 +612,28 @@ void gemm4_kernel(const void *__restrict__ A, const void *__restrict__ W, int M,
         // every wave is done with stage cur): reads of k-step 0 of tile kt + 1,
         // copies of tile kt + 2 into stage cur.  STEP0 is the k-step 0 block:
         // the zero-start one in the tile's first K tile.
-#define DIT_K4_TILE(kt, STEP0)                                                                                     \
+#define DIT_K4_TILE(INS, kt, STEP0)                                                                                     \
     do {                                                                                                           \
         const int cur = (kt) & 1, nxt = cur ^ 1;                                                                   \
-        STEP0(acc, fa, fb, na, nb, 0, adA[cur][1], adB[cur][1]);                                                   \
-        STEP0(acc, fa, fb, na, nb, 2, adA[cur][1], adB[cur][1]);                                                   \
-        STEP0(acc, fa, fb, na, nb, 4, adA[cur][1], adB[cur][1]);                                                   \
-        STEP0(acc, fa, fb, na, nb, 6, adA[cur][1], adB[cur][1]);                                                   \
+        STEP0(INS, acc, fa, fb, na, nb, 0, adA[cur][1], adB[cur][1]);                                                   \
+        STEP0(INS, acc, fa, fb, na, nb, 2, adA[cur][1], adB[cur][1]);                                                   \
+        STEP0(INS, acc, fa, fb, na, nb, 4, adA[cur][1], adB[cur][1]);                                                   \
+        STEP0(INS, acc, fa, fb, na, nb, 6, adA[cur][1], adB[cur][1]);                                                   \
         const uint32_t lb =                                                                                        \
             (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds0 + cur * T::kStageBytes + wave * 1024));            \
-        const uint32_t kb = (uint32_t)__builtin_amdgcn_readfirstlane(min((kt) + 2, KT - 1) * T::BK * 2);          \
-        DIT_K4_STEP_BARRIER(acc, na, nb, fa, fb, 0, adA[nxt][0], adB[nxt][0], ra4, lb, kb, va[0], 0);              \
-        DIT_K4_STEP_COPY(acc, na, nb, fa, fb, 2, adA[nxt][0], adB[nxt][0], ra4, lb, kb, va[1], 16384);             \
-        DIT_K4_STEP_COPY(acc, na, nb, fa, fb, 4, adA[nxt][0], adB[nxt][0], rw4, lb, kb, vb[0], 32768);             \
-        DIT_K4_STEP_COPY(acc, na, nb, fa, fb, 6, adA[nxt][0], adB[nxt][0], rw4, lb, kb, vb[1], 49152);             \
+        const uint32_t kb = (uint32_t)__builtin_amdgcn_readfirstlane(min((kt) + 2, KT - 1) * T::kRowBytes);          \
+        DIT_K4_STEP_BARRIER(INS, acc, na, nb, fa, fb, 0, adA[nxt][0], adB[nxt][0], ra4, lb, kb, va[0], 0);              \
+        DIT_K4_STEP_COPY(INS, acc, na, nb, fa, fb, 2, adA[nxt][0], adB[nxt][0], ra4, lb, kb, va[1], 16384);             \
+        DIT_K4_STEP_COPY(INS, acc, na, nb, fa, fb, 4, adA[nxt][0], adB[nxt][0], rw4, lb, kb, vb[0], 32768);             \
+        DIT_K4_STEP_COPY(INS, acc, na, nb, fa, fb, 6, adA[nxt][0], adB[nxt][0], rw4, lb, kb, vb[1], 49152);             \
     } while (0)
-        DIT_K4_TILE(0, DIT_K4_STEP_Z);
-        for (int kt = 1; kt < KT; ++kt) DIT_K4_TILE(kt, DIT_K4_STEP);
+        if constexpr (T::ES == 2) {
+            DIT_K4_TILE(DIT_INS_BF16, 0, DIT_K4_STEP_Z);
+            for (int kt = 1; kt < KT; ++kt) DIT_K4_TILE(DIT_INS_BF16, kt, DIT_K4_STEP);
+        } else {
+            DIT_K4_TILE(DIT_INS_I8, 0, DIT_K4_STEP_Z);
+            for (int kt = 1; kt < KT; ++kt) DIT_K4_TILE(DIT_INS_I8, kt, DIT_K4_STEP);
+        }
 #undef DIT_K4_TILE
         wait_vmcnt<0>();      // retire the trailing (never read) copies before LDS is reused
         __syncthreads();
@@ -642,6 +658,8 @@ void gemm4_kernel(const void *__restrict__ A, const void *__restrict__ W, int M,
 #undef DIT_K4_STEP_Z
 #undef DIT_K4_STEP
 #undef DIT_MZ
+#undef DIT_INS_BF16
+#undef DIT_INS_I8
 #undef DIT_K4_COPIES
 #undef DIT_K4_OPERANDS
 #undef DIT_LD
@@ -652,13 +670,14 @@ void gemm4_kernel(const void *__restrict__ A, const void *__restrict__ W, int M,
 #undef DIT_Q4_MFMA
 
 
-// An accumulator element read by an epilogue.  The 4-wave tile keeps its
-// accumulators in AGPRs; there each element is read into a VGPR where it is
-// used (with plain reads the compiler copies all 256 out right after the K
-// loop, which takes every VGPR and spills what the persistent loop keeps).
+// An accumulator element read by an epilogue.  The persistent 4-wave kernel
+// keeps its accumulators in AGPRs; there each element is read into a VGPR
+// where it is used (with plain reads the compiler copies all 256 out right
+// after the K loop, which takes every VGPR and spills what the persistent loop
+// keeps).
 template <class T>
 __device__ __forceinline__ float acc_get(const floatx4 &a, int e) {
-    if constexpr (T::kWaves == 4) {
+    if constexpr (T::kAgpr) {
         float x;
         asm("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(a[e]));
         return x;
@@ -725,20 +744,31 @@ struct EpiResidual {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) r[ib][j][e] = 0.0f;
             }
+            float sa[IB][4];   // Q8: row scales of the batch
             if constexpr (Q8) {
 #pragma unroll
                 for (int ib = 0; ib < IB; ++ib) {
-                    float sa[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) sa[e] = a_scale[min(row0 + acc_row(i0 + ib, e, lq), M - 1)];
+                    for (int e = 0; e < 4; ++e) sa[ib][e] = a_scale[min(row0 + acc_row(i0 + ib, e, lq), M - 1)];
+                    if constexpr (!T::kAgpr) {
 #pragma unroll
-                    for (int j = 0; j < T::TN; ++j) {
-                        const intx4 iv = __builtin_bit_cast(intx4, acc[i0 + ib][j]);   // whole-vector cast (see kernel)
+                        for (int j = 0; j < T::TN; ++j) {
+                            const intx4 iv = __builtin_bit_cast(intx4, acc[i0 + ib][j]);   // whole-vector cast (see kernel)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) acc[i0 + ib][j][e] = (float)iv[e] * sa[e];
+                            for (int e = 0; e < 4; ++e) acc[i0 + ib][j][e] = (float)iv[e] * sa[ib][e];
+                        }
                     }
                 }
             }
+            // the product of a row and a column: the persistent 4-wave tile
+            // dequantizes its AGPR-held int32 sums here, where each is read (the
+            // other tiles above)
+            auto val = [&](int ib, int j, int e) -> float {
+                if constexpr (Q8 && T::kAgpr)
+                    return (float)__builtin_bit_cast(int, acc_get<T>(acc[i0 + ib][j], e)) * sa[ib][e];
+                else
+                    return acc_get<T>(acc[i0 + ib][j], e);
+            };
             // wave-uniform: all rows of the batch in range -> straight-line stores
             if (row0 + (i0 + IB) * 16 <= M) {
 #pragma unroll
@@ -748,7 +778,7 @@ struct EpiResidual {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             out[(size_t)(row0 + acc_row(i0 + ib, e, lq)) * N + col0 + j * 16 + l16] =
-                                from_f32<TO>(fmaf(acc_get<T>(acc[i0 + ib][j], e), g[j], bb[j]) + r[ib][j][e]);
+                                from_f32<TO>(fmaf(val(ib, j, e), g[j], bb[j]) + r[ib][j][e]);
             } else {
 #pragma unroll
                 for (int ib = 0; ib < IB; ++ib)
@@ -759,7 +789,7 @@ struct EpiResidual {
                             const int row = row0 + acc_row(i0 + ib, e, lq);
                             if (row < M)
                                 out[(size_t)row * N + col0 + j * 16 + l16] =
-                                    from_f32<TO>(fmaf(acc_get<T>(acc[i0 + ib][j], e), g[j], bb[j]) + r[ib][j][e]);
+                                    from_f32<TO>(fmaf(val(ib, j, e), g[j], bb[j]) + r[ib][j][e]);
                         }
             }
         }
@@ -774,6 +804,9 @@ struct EpiSwiglu {
     static constexpr bool kDequant = false;
     TU *u;
     int F;
+    // int8 operands on the 4-wave tile: row and W-row scales, applied here (the
+    // 8-wave kernels dequantize before the epilogue)
+    const float *a_scale = nullptr, *w_scale = nullptr;
     template <class T> static constexpr int lds_bytes() { return 0; }
     template <class T>
     __device__ __forceinline__ void apply(floatx4 (&acc)[T::TM][T::TN], int row0, int tn, int wn, int lane, int M,
@@ -781,19 +814,42 @@ struct EpiSwiglu {
         const int l16 = lane & 15, lq = lane >> 4;
         constexpr int HJ = T::TN / 2;
         const int f0 = tn * (T::BN / 2) + wn * (T::kWaveN / 2);
+        // int32 sums in the accumulators (the 4-wave int8 tile): C[m, n] =
+        // sum * (a_scale[m] w_scale[n]); column block j < HJ holds gate features
+        // f0 + 16 j + l16 (W rows of the same index), j >= HJ their up rows (+ F)
+        constexpr bool kQ = T::ES == 1 && T::kAgpr;
+        float sw[kQ ? T::TN : 1];
+        if constexpr (kQ) {
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j) sw[j] = w_scale[(j < HJ ? 0 : F) + f0 + (j % HJ) * 16 + l16];
+        }
+        auto row_scales = [&](int i, float (&sa)[4]) {
+            if constexpr (kQ) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sa[e] = a_scale[min(row0 + acc_row(i, e, lq), M - 1)];
+            }
+        };
+        auto val = [&](int i, int j, int e, const float (&sa)[4]) -> float {
+            if constexpr (kQ)
+                return (float)__builtin_bit_cast(int, acc_get<T>(acc[i][j], e)) * (sa[e] * sw[j]);
+            else
+                return acc_get<T>(acc[i][j], e);
+        };
         // the HJ column blocks of one output row are stored back to back, so
         // each 16 HJ-feature row segment reaches L2 whole instead of in pieces
         // far apart in time (which cost partial-line write-backs)
         auto row_block = [&](int i, bool check) {
+            float sa[4];
+            row_scales(i, sa);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int row = row0 + acc_row(i, e, lq);
                 if (!check || row < M) {
 #pragma unroll
                     for (int j = 0; j < HJ; ++j) {
-                        const float z = acc_get<T>(acc[i][j], e);
+                        const float z = val(i, j, e, sa);
                         const float g = ACT == 1 ? gelu_tanh_f(z) : silu_f(z);
-                        u[(size_t)row * F + f0 + j * 16 + l16] = from_f32<TU>(g * acc_get<T>(acc[i][j + HJ], e));
+                        u[(size_t)row * F + f0 + j * 16 + l16] = from_f32<TU>(g * val(i, j + HJ, e, sa));
                     }
                 }
             }
@@ -813,13 +869,14 @@ struct EpiSwiglu {
                     uint8_t *base = (uint8_t *)(u + (size_t)(row0 + i * 16) * F + f0);
                     // the row block's 16 outputs as independent chains (the
                     // exponentials and reciprocals of one hide the others' latency)
-                    float y[4][HJ];
+                    float y[4][HJ], sa[4];
+                    row_scales(i, sa);
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
 #pragma unroll
                         for (int j = 0; j < HJ; ++j) {
-                            const float z = acc_get<T>(acc[i][j], e);
-                            y[e][j] = (ACT == 1 ? gelu_tanh_f(z) : silu_f(z)) * acc_get<T>(acc[i][j + HJ], e);
+                            const float z = val(i, j, e, sa);
+                            y[e][j] = (ACT == 1 ? gelu_tanh_f(z) : silu_f(z)) * val(i, j + HJ, e, sa);
                         }
 #pragma unroll
                     for (int e = 0; e < 4; e += 2)
@@ -1203,7 +1260,7 @@ struct EpiQkvRaw {
     template <class T>
     __device__ __forceinline__ void apply(floatx4 (&acc)[T::TM][T::TN], int row0, int tn, int wn, int lane, int M,
                                           uint8_t *) const {
-        static_assert(T::kWaves == 4 && T::TN == 8 && T::kWaveN % HD == 0, "the 4-wave tile, whole heads per wave");
+        static_assert(T::kAgpr && T::TN == 8 && T::kWaveN % HD == 0, "the 4-wave tile, whole heads per wave");
         const int l16 = lane & 15, lq = lane >> 4;
         const int S = e.seq, spad = e.seq_pad;
         const int qcols = e.heads * HD, kcols = e.kv_heads * HD;
@@ -1577,10 +1634,9 @@ static hipError_t run(const void *a, const void *w, int64_t M, int N_tile_cols, 
     return hipGetLastError();
 }
 
-template <class RowMap, class Epi>
+template <class T, class RowMap, class Epi>
 static hipError_t run4(const void *a, const void *w, int64_t M, int N_tile_cols, int K, RowMap rm, Epi epi,
                        hipStream_t s, int64_t m_base = 0) {
-    using T = Tile4w;
     const int tiles_m = (int)((M - m_base + T::BM - 1) / T::BM);
     const int tiles_n = N_tile_cols / T::BN;
     const int ntiles = tiles_m * tiles_n;
@@ -1681,7 +1737,8 @@ static hipError_t residual_typed(const void *a, const void *w, int64_t M, int N,
                 return run<typename TSet::Quar1>(a, w, M, Nc, K, RowsIdentity<128>{}, epi, s, sc.a, sc.w);
             return run<typename TSet::Quar>(a, w, M, Nc, K, RowsIdentity<128>{}, epi, s, sc.a, sc.w);
         default:
-            if constexpr (SC::kFmt == 0) return run4(a, w, M, Nc, K, RowsIdentity<256>{}, epi, s);
+            if constexpr (SC::kFmt == 0) return run4<Tile4w>(a, w, M, Nc, K, RowsIdentity<256>{}, epi, s);
+            if constexpr (SC::kFmt == 1) return run4<Tile4wQ>(a, w, M, Nc, K, RowsIdentity<256>{}, epi, s);
             return run<typename TSet::S>(a, w, M, Nc, K, RowsIdentity<256>{}, epi, s, sc.a, sc.w);
     }
 }
@@ -1746,21 +1803,23 @@ static hipError_t swiglu_any(const void *a, const void *w, int64_t M, int F, int
             if (quarter_one_round(M, 2 * F)) return with_act(typename TSet::Quar1{});
             return with_act(typename TSet::Quar{});
         default:
-            if constexpr (SC::kFmt == 0) {
-                // bf16: the 4-wave tile; a ragged tail that would cost a whole round
-                // of 256-row tiles runs as a second launch of 3-stage 128 x 256
+            if constexpr (SC::kFmt != 2) {
+                // bf16 and int8: the 4-wave tile; a ragged tail that would cost a
+                // whole round of 256-row tiles runs as a second launch of 128 x 256
                 // tiles (4170 x 24576: 7 rounds of 256-row tiles become 6 plus a
                 // short one)
+                using T4 = std::conditional_t<SC::kFmt == 0, Tile4w, Tile4wQ>;
                 using TH = typename TSet::Half;
                 const bool split = split_tail_rows(M, 2 * F);
                 const int64_t m_full = split ? M / 256 * 256 : M;
                 auto launch = [&](auto epi) {
                     const hipError_t e =
-                        run4(a, w, m_full, 2 * F, K, RowsSwiglu<Tile4w::BN, Tile4w::kWaveN>{F}, epi, s);
+                        run4<T4>(a, w, m_full, 2 * F, K, RowsSwiglu<T4::BN, T4::kWaveN>{F}, epi, s);
                     if (e != hipSuccess || !split) return e;
                     return run<TH>(a, w, M, 2 * F, K, RowsSwiglu<TH::BN, TH::kWaveN>{F}, epi, s, sc.a, sc.w, m_full);
                 };
-                return act == 1 ? launch(EpiSwiglu<1, TU>{u, F}) : launch(EpiSwiglu<0, TU>{u, F});
+                return act == 1 ? launch(EpiSwiglu<1, TU>{u, F, sc.a, sc.w})
+                                : launch(EpiSwiglu<0, TU>{u, F, sc.a, sc.w});
             }
             return with_act(typename TSet::S{});
     }
@@ -1835,7 +1894,7 @@ static hipError_t qkv_any(const void *h, const void *w, int64_t M, int N, int K,
         // the fused 8-wave epilogue, whose rows the pass skips
         const int64_t m4 = qkv_split_rows(M, N, e.batch, e.seq, e.head_dim);
         if (m4 > 0) {
-            hipError_t err = run4(h, w, m4, N, K, RowsIdentity<256>{}, EpiQkvRaw<128>{e}, s);
+            hipError_t err = run4<Tile4w>(h, w, m4, N, K, RowsIdentity<256>{}, EpiQkvRaw<128>{e}, s);
             if (err != hipSuccess) return err;
             if (m4 < M) {
 #define DIT_QKV_TAIL(HD_, RMS_, RF_, RH_) \

@@ -152,6 +152,11 @@ def _q8_operands(M, N_rows, K, seed):
     (520, 512, 1024, None, "f32", N.DIT_GATE_SIGMOID),    # no residual
     (4170, 4096, 4096, "f32", "f32", N.DIT_GATE_IDENTITY),  # the 320-row tile (joint sequence rows)
     (1000, 768, 3072, "bf16", "bf16", N.DIT_GATE_IDENTITY),
+    # 256 x 256 tiles (the persistent 4-wave kernel): one full round, a ragged
+    # last row of tiles, no residual
+    (4096, 4096, 1024, "f32", "f32", N.DIT_GATE_IDENTITY),
+    (3900, 4096, 512, "bf16", "bf16", N.DIT_GATE_TANH),
+    (4096, 4096, 256, None, "f32", N.DIT_GATE_SIGMOID),
 ])
 def test_gemm_w8a8_gated_residual(M, N_, K, rdt, odt, gate_fn):
     import torch
@@ -183,7 +188,12 @@ def test_gemm_w8a8_gated_residual(M, N_, K, rdt, odt, gate_fn):
 
 @pytest.mark.parametrize("M,F,K,act", [(300, 384, 512, N.DIT_ACT_SILU), (4096, 1024, 4096, N.DIT_ACT_SILU),
                                        (270, 256, 256, N.DIT_ACT_GELU_TANH),
-                                       (4170, 2048, 256, N.DIT_ACT_SILU)])   # ragged rows over one round
+                                       (4170, 2048, 256, N.DIT_ACT_SILU),   # ragged rows over one round
+                                       # 256 x 256 tiles (the persistent 4-wave kernel): full, ragged,
+                                       # and full rows plus a 74-row tail launch of 128-row tiles
+                                       (4096, 4096, 512, N.DIT_ACT_SILU),
+                                       (3900, 4096, 256, N.DIT_ACT_GELU_TANH),
+                                       (4170, 12288, 256, N.DIT_ACT_SILU)])
 def test_gemm_w8a8_swiglu(M, F, K, act):
     import torch
     say(f"gemm_w8a8_swiglu M={M} F={F} K={K} act={act}")
@@ -191,8 +201,10 @@ def test_gemm_w8a8_swiglu(M, F, K, act):
     u = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
     N.dit_gemm_w8a8_swiglu(_dev_i8(qa), R.to_dev_f32(sa), _dev_i8(qw), R.to_dev_f32(sw), M, F, K, u, act=act)
     _sync()
-    ref = O.glu(O.w8a8_matmul(qa, sa, qw, sw), "gelu_tanh" if act == N.DIT_ACT_GELU_TANH else "silu")
-    assert_parity(R.to_host_f32(u), ref, max_rel=8e-3, min_cos=0.99999, what="w8a8 swiglu")
+    rows = np.arange(M) if M <= 1024 else np.unique(np.r_[0, 1, 127, 128, 255, 256, 2047, M - 75, M - 74, M - 1,
+                                                          np.random.default_rng(2).choice(M, 40, replace=False)])
+    ref = O.glu(O.w8a8_matmul(qa[rows], sa[rows], qw, sw), "gelu_tanh" if act == N.DIT_ACT_GELU_TANH else "silu")
+    assert_parity(R.to_host_f32(u)[rows], ref, max_rel=8e-3, min_cos=0.99999, what="w8a8 swiglu")
 
 
 @pytest.mark.parametrize("name", ["c1_tiny", "hd128_ragged400", "gqa3_b2_ragged300", "half_hd128_rope_first",
