@@ -1252,6 +1252,8 @@ template <int HD>
 struct EpiQkvRaw {
     static constexpr bool kDequant = false;
     QkvEpiArgs e;
+    // int8 operands: row and W-row scales of the int32 sums (Tile4wQ)
+    const float *a_scale = nullptr, *w_scale = nullptr;
     template <class T> static constexpr int lds_bytes() { return 0; }
     // Taken only when every 16-row block lies in one sequence and below M (a
     // single sequence, or a sequence length that is a multiple of 16, and M a
@@ -1268,9 +1270,14 @@ struct EpiQkvRaw {
         // first column at sequence 0, position 0 (wave-uniform)
         int sect[T::TN];
         uint8_t *cbase[T::TN];
+        // int8 operands: C[m, n] = sum * (a_scale[m] w_scale[n]), converted and
+        // scaled where each sum is read (the same products as the 8-wave kernel)
+        constexpr bool kQ = T::ES == 1;
+        float sw[kQ ? T::TN : 1];
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) {
             const int c0 = tn * T::BN + wn * T::kWaveN + j * 16;
+            if constexpr (kQ) sw[j] = w_scale[c0 + l16];
             sect[j] = c0 < qcols ? 0 : (c0 < qcols + kcols ? 1 : 2);
             const int cs = c0 - (sect[j] == 0 ? 0 : (sect[j] == 1 ? qcols : qcols + kcols));
             const int head = cs / HD, d0 = cs - head * HD;
@@ -1283,6 +1290,18 @@ struct EpiQkvRaw {
 #pragma unroll
         for (int e_ = 0; e_ < 4; ++e_) qo[e_] = (uint32_t)((lq * 4 + e_) * HD + l16) * 2u;
         const uint32_t vo = ((uint32_t)l16 * (uint32_t)spad + (uint32_t)lq * 4u) * 2u;
+        auto row_scales = [&](int i, float (&sa)[4]) {
+            if constexpr (kQ) {
+#pragma unroll
+                for (int e_ = 0; e_ < 4; ++e_) sa[e_] = a_scale[min(row0 + acc_row(i, e_, lq), M - 1)];
+            }
+        };
+        auto val = [&](int i, int j, int e_, const float (&sa)[4]) -> float {
+            if constexpr (kQ)
+                return (float)__builtin_bit_cast(int, acc_get<T>(acc[i][j], e_)) * (sa[e_] * sw[j]);
+            else
+                return acc_get<T>(acc[i][j], e_);
+        };
         // SEC: the section of every block of the wave (0 q, 1 k, 2 v), or -1 for a
         // wave whose columns cross a section boundary (hd 64 only).  Stores are
         // ordered so that each 128-byte line is written by consecutive stores
@@ -1300,10 +1319,12 @@ struct EpiQkvRaw {
             constexpr int SEC = decltype(sec_c)::value;
             if constexpr (SEC == 2) {
                 size_t ov[T::TM];
+                float sa[T::TM][4];
 #pragma unroll
                 for (int i = 0; i < T::TM; ++i) {
                     size_t oq_, ok_;
                     offsets(min(i, (M - 1 - row0) / 16), oq_, ok_, ov[i]);   // (rows past M: not stored)
+                    row_scales(i, sa[i]);
                 }
 #pragma unroll
                 for (int j = 0; j < T::TN; ++j) {
@@ -1312,9 +1333,9 @@ struct EpiQkvRaw {
                         if (row0 + i * 16 < M) {
                             uint32_t p0, p1;
                             asm("v_cvt_pk_bf16_f32 %0, %1, %2"
-                                : "=v"(p0) : "v"(acc_get<T>(acc[i][j], 0)), "v"(acc_get<T>(acc[i][j], 1)));
+                                : "=v"(p0) : "v"(val(i, j, 0, sa[i])), "v"(val(i, j, 1, sa[i])));
                             asm("v_cvt_pk_bf16_f32 %0, %1, %2"
-                                : "=v"(p1) : "v"(acc_get<T>(acc[i][j], 2)), "v"(acc_get<T>(acc[i][j], 3)));
+                                : "=v"(p1) : "v"(val(i, j, 2, sa[i])), "v"(val(i, j, 3, sa[i])));
                             typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
                             *(u32x2 *)(cbase[j] + ov[i] + vo) = u32x2{p0, p1};
                         }
@@ -1327,6 +1348,8 @@ struct EpiQkvRaw {
                     if (row0 + i * 16 < M) {
                         size_t oq, ok, ov;
                         offsets(i, oq, ok, ov);
+                        float sa[4];
+                        row_scales(i, sa);
                         if constexpr (SEC >= 0) {
                             // rows 4 lq + e (pairs share a conversion), each row's
                             // column blocks stored back to back
@@ -1337,7 +1360,7 @@ struct EpiQkvRaw {
                                 for (int h = 0; h < 2; ++h)
                                     asm("v_cvt_pk_bf16_f32 %0, %1, %2"
                                         : "=v"(pk[j][h])
-                                        : "v"(acc_get<T>(acc[i][j], 2 * h)), "v"(acc_get<T>(acc[i][j], 2 * h + 1)));
+                                        : "v"(val(i, j, 2 * h, sa)), "v"(val(i, j, 2 * h + 1, sa)));
 #pragma unroll
                             for (int e_ = 0; e_ < 4; ++e_)
 #pragma unroll
@@ -1351,7 +1374,7 @@ struct EpiQkvRaw {
                             for (int j = 0; j < T::TN; ++j) {
                                 float z[4];
 #pragma unroll
-                                for (int e_ = 0; e_ < 4; ++e_) z[e_] = acc_get<T>(acc[i][j], e_);
+                                for (int e_ = 0; e_ < 4; ++e_) z[e_] = val(i, j, e_, sa);
                                 if (sect[j] < 2) {
                                     uint8_t *base = cbase[j] + (sect[j] == 0 ? oq : ok);
 #pragma unroll
@@ -1846,16 +1869,16 @@ hipError_t launch_gemm_swiglu_q8(const int8_t *a, const float *a_scale, const in
     return swiglu_any(a, w, M, F, K, act, u, Scales{a_scale, w_scale}, s);
 }
 
-// Rows of a bf16 QKV projection that take the split form: those the tile
-// choice puts in 256 x 256 tiles (all rows, or the full row tiles when a short
+// Rows of a bf16 or int8 (fmt 0 / 1) QKV projection that take the split form:
+// those the tile choice puts in 256 x 256 tiles (all rows, or the full row tiles when a short
 // tail runs in 128-row tiles).  0 (the fused epilogue throughout) when it picks
 // 128-row tiles, for 64-wide heads (measured slower split: their norm pass
 // moves the same bytes for half the GEMM work), and unless every 16-row block
 // of the split rows lies in one sequence and below the row count (the split
 // epilogue's condition): a row count that is a multiple of 16 and one
 // sequence or a sequence length that is a multiple of 16.
-static int64_t qkv_split_rows(int64_t M, int N, int batch, int seq, int head_dim) {
-    if (head_dim != 128 || choose_tile(M, N, 1u << kTileS | 1u << kTileHalf, 0) == kTileHalf) return 0;
+static int64_t qkv_split_rows(int64_t M, int N, int batch, int seq, int head_dim, int fmt) {
+    if (head_dim != 128 || choose_tile(M, N, 1u << kTileS | 1u << kTileHalf, fmt) == kTileHalf) return 0;
     const int64_t m4 = split_tail_rows(M, N) ? M / 256 * 256 : M;
     if (m4 % 16 || (batch > 1 && seq % 16)) return 0;
     return m4;
@@ -1888,13 +1911,15 @@ static hipError_t qkv_any(const void *h, const void *w, int64_t M, int N, int K,
     using T = typename TileSet<SC::kFmt>::S;
     using TH = typename TileSet<SC::kFmt>::Half;
     using TQ = typename std::conditional<SC::kFmt == 2, float, bf16>::type;
-    if constexpr (SC::kFmt == 0) {
-        // bf16 rows in 256 x 256 tiles: the split form (4-wave GEMM with a plain
-        // epilogue, then the in-place qk-norm + RoPE pass); a 128-row tail keeps
-        // the fused 8-wave epilogue, whose rows the pass skips
-        const int64_t m4 = qkv_split_rows(M, N, e.batch, e.seq, e.head_dim);
+    if constexpr (SC::kFmt != 2) {
+        // bf16 and int8 rows in 256 x 256 tiles: the split form (persistent
+        // 4-wave GEMM with a plain epilogue, then the in-place qk-norm + RoPE
+        // pass); a 128-row tail keeps the fused 8-wave epilogue, whose rows the
+        // pass skips
+        using T4 = std::conditional_t<SC::kFmt == 0, Tile4w, Tile4wQ>;
+        const int64_t m4 = qkv_split_rows(M, N, e.batch, e.seq, e.head_dim, SC::kFmt);
         if (m4 > 0) {
-            hipError_t err = run4<Tile4w>(h, w, m4, N, K, RowsIdentity<256>{}, EpiQkvRaw<128>{e}, s);
+            hipError_t err = run4<T4>(h, w, m4, N, K, RowsIdentity<256>{}, EpiQkvRaw<128>{e, sc.a, sc.w}, s);
             if (err != hipSuccess) return err;
             if (m4 < M) {
 #define DIT_QKV_TAIL(HD_, RMS_, RF_, RH_) \

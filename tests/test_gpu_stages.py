@@ -8,7 +8,7 @@ from diffusion_transformer_dit_amd import native as N
 from diffusion_transformer_dit_amd import runtime as R
 from oracle import dit as O
 
-from gpu_helpers import SMALL, assert_parity, say
+from gpu_helpers import QKV_SPLIT, QKV_TAIL, SMALL, assert_parity, say
 
 pytestmark = pytest.mark.gpu
 
@@ -100,41 +100,6 @@ def _qkv_case(cfg, seed=3):
     h = I.bf16_round(r.standard_normal((cfg.tokens, cfg.hidden), dtype=np.float32))
     w = I.block_weights(cfg, 0, affine_random=True)
     return h, w
-
-
-# 4170 tokens (30 x 139 grid), 16 + 2 x 8 heads of 128: 16 full row tiles x 16 column
-# tiles fill one round of 256 CUs, so the 74-row tail runs as a 128-row tile launch
-QKV_TAIL = I.DiTConfig("qkv_tail_4170", 25, 1, (1, 30, 139), 2048, 16, 8, 128, 4096, 256, True,
-                       "interleaved3d", (32, 48, 48), 256.0, x_dtype="bf16")
-
-
-# bf16 shapes whose 256 x 256 tile count fills a round: with 128-wide heads and a
-# sequence length that is a multiple of 16 the projection takes the split form
-# (plain-epilogue 4-wave GEMM, then the in-place qk-norm + RoPE pass).  Two
-# sequences of 1008 tokens, GQA 32 / 16 heads, a ragged last row tile; 1904
-# tokens, GQA 32 / 8, rotate-half RoPE before an RMS qk-norm.  The last keeps
-# the fused epilogue (64-wide heads, 1899 tokens) at a similar size.
-QKV_SPLIT = {
-    "qkv_split_b2_1008": I.DiTConfig("qkv_split_b2_1008", 26, 2, (1, 28, 36), 4096, 32, 16, 128, 256, 256, True,
-                                     "interleaved3d", (32, 48, 48), 256.0, x_dtype="bf16"),
-    "qkv_split_half_1904": I.DiTConfig("qkv_split_half_1904", 41, 1, (1, 28, 68), 4096, 32, 8, 128, 256, 256, True,
-                                       "half2d", (64, 64), 100.0, x_dtype="bf16", norm="rmsnorm",
-                                       qk_order="rope_norm"),
-    # one sequence of 4170 tokens (not a multiple of 16): the 4096 rows of full
-    # 256-row tiles split, the 74-row tail in the fused 128-row launch
-    "qkv_split_joint_4170": I.DiTConfig("qkv_split_joint_4170", 42, 1, (1, 30, 139), 4096, 32, 32, 128, 256, 256, True,
-                                        "interleaved3d", (32, 48, 48), 256.0, x_dtype="bf16"),
-    # 34 q heads and 2 k heads: the qk-norm pass's last group of 8 heads holds
-    # both q and k rows
-    "qkv_split_mixed_group_3072": I.DiTConfig("qkv_split_mixed_group_3072", 43, 1, (1, 48, 64), 4352, 34, 2, 128, 256,
-                                              256, True, "interleaved3d", (32, 48, 48), 256.0, x_dtype="bf16"),
-    # no qk-norm: the pass applies RoPE only
-    "qkv_split_no_qknorm_b2_1008": I.DiTConfig("qkv_split_no_qknorm_b2_1008", 44, 2, (1, 28, 36), 4096, 32, 16, 128,
-                                               256, 256, False, "interleaved3d", (32, 48, 48), 256.0, x_dtype="bf16"),
-    "qkv_fused_hd64_1899": I.DiTConfig("qkv_fused_hd64_1899", 27, 1, (1, 9, 211), 4096, 64, 32, 64, 256, 256, True,
-                                       "half2d", (32, 32), 100.0, x_dtype="bf16", norm="rmsnorm",
-                                       qk_order="rope_norm"),
-}
 
 
 @pytest.mark.parametrize("name", ["c1_rms", "c1_rope_first", "hd128_ernie_diagram", "half_hd128_rope_first",

@@ -25,7 +25,7 @@ from diffusion_transformer_dit_amd import native as N
 from diffusion_transformer_dit_amd import runtime as R
 from oracle import dit as O
 
-from gpu_helpers import SMALL, assert_parity, metrics, say
+from gpu_helpers import QKV_SPLIT, QKV_TAIL, SMALL, assert_parity, metrics, say
 
 pytestmark = pytest.mark.gpu
 
@@ -207,12 +207,16 @@ def test_gemm_w8a8_swiglu(M, F, K, act):
     assert_parity(R.to_host_f32(u)[rows], ref, max_rel=8e-3, min_cos=0.99999, what="w8a8 swiglu")
 
 
+# the small shapes (8-wave int8 tiles, fused epilogue) and those whose 256 x
+# 256 tiles take the split form (persistent 4-wave int8 GEMM writing q, k, v,
+# then the qk-norm + RoPE pass; with a 74-row fused tail at 4170 tokens)
 @pytest.mark.parametrize("name", ["c1_tiny", "hd128_ragged400", "gqa3_b2_ragged300", "half_hd128_rope_first",
-                                  "c1_rms"])
+                                  "c1_rms", "qkv_tail_4170", "qkv_split_b2_1008", "qkv_split_half_1904",
+                                  "qkv_split_joint_4170", "qkv_split_mixed_group_3072", "qkv_split_no_qknorm_b2_1008"])
 def test_qkv_rope_w8a8(name):
     """The QKV epilogue (qk-norm, RoPE, V^T) on the dequantized int8 product."""
     import torch
-    cfg = SMALL[name].replace(fmt="w8a8_h256")
+    cfg = (QKV_TAIL if name == "qkv_tail_4170" else QKV_SPLIT.get(name) or SMALL[name]).replace(fmt="w8a8_h256")
     say(f"qkv_rope_w8a8 {name}")
     r = np.random.default_rng(3)
     h = r.standard_normal((cfg.tokens, cfg.hidden))
