@@ -373,12 +373,14 @@ void gemm_kernel(const void *__restrict__ A, const void *__restrict__ W, int M, 
 
 
 // ---------------------------------------------------------------------------
-// 4-wave 256 x 256 bf16 tile for the gated-residual and SwiGLU GEMMs: one wave
-// per SIMD with a 128 x 128 wave tile (8 x 8 MFMA blocks of 16 x 16).  Every
+// 4-wave 256 x 256 tile for the gated-residual, SwiGLU and split-form QKV
+// GEMMs, over bf16 or int8 operands: one wave per SIMD with a 128 x 128 wave
+// tile (8 x 8 MFMA blocks of 16 x 16; an int8 block is the same 16 x 16 output
+// over 64 instead of 32 k, with int32 sums in the accumulators).  Every
 // K fragment read from LDS then feeds 8 MFMAs, so the LDS read traffic per
 // MFMA is two thirds of the 8-wave tile's (0.25 instead of 0.375 fragment
-// reads per MFMA), which is what bounds the 8-wave loop.  The 256 fp32
-// accumulators of a wave fill its AGPRs.  With a single wave per SIMD nothing
+// reads per MFMA), which is what bounds the 8-wave loop.  The 256 fp32 (or
+// int32) accumulators of a wave fill its AGPRs.  With a single wave per SIMD nothing
 // else hides a gap in its MFMA stream, so the K loop is written as inline
 // assembly blocks of 16 MFMAs (one pair of A row blocks against the 8 B column
 // blocks), each with its share of the other work between the MFMAs:

@@ -451,7 +451,9 @@ int dit_ln_modulate_h256q(const void *x, int32_t x_dtype, int64_t rows, int32_t 
  * C[m, n] = a_scale[m] w_scale[n] sum_k a[m, k] w[n, k] is summed exactly in
  * int32, converted to fp32 and fed to the epilogue of the bf16 call of the
  * same name (dit_gemm_gated_residual, dit_gemm_swiglu, dit_qkv_rope), whose
- * other arguments, layouts and limits it keeps; K % 128 == 0. */
+ * other arguments, layouts and limits it keeps (for the QKV projection also
+ * its choice between the fp32 and the bf16-rounded product as the input of the
+ * qk-norm); K % 128 == 0. */
 int dit_gemm_w8a8_gated_residual(const void *a, const float *a_scale, const void *w, const float *w_scale,
                                  int64_t M, int32_t N, int32_t K, const void *resid, int32_t resid_dtype,
                                  const float *gate, int32_t gate_fn, const float *bias, void *out,
