@@ -423,18 +423,29 @@ def host_info():
     return {"cpu": model, "nproc": os.cpu_count(), "blas": blas}
 
 
+def code_digest(paths):
+    """First 16 hex digits of the sha256 of the C/HIP sources' code: comments
+    removed and every run of white space collapsed, so that an edit of a
+    comment leaves it unchanged and any change of the code changes it."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in paths:
+        text = open(os.path.join(ROOT, f), encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic():
     """HBM bytes per launch of the SwiGLU GEMM from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE summary, or None when a source file the kernel is
-    compiled from (the profile lists them) changed since."""
-    import hashlib
+    FETCH_SIZE / WRITE_SIZE summary, or None when the code of a source file the
+    kernel is compiled from (the profile lists them) changed since."""
     path = os.path.join(ROOT, "profiles", "gemm_swiglu_stack_8b_hbm_counters.md")
     try:
         kv = dict(l.strip().split(": ", 1) for l in open(path) if l.startswith("    ") and ": " in l)
-        h = hashlib.sha256()
-        for f in kv["sources"].split():
-            h.update(open(os.path.join(ROOT, f), "rb").read())
-        if h.hexdigest()[:16] != kv["sources_sha256_16"]:
+        if code_digest(kv["sources"].split()) != kv["code_sha256_16"]:
             return None
         return int(kv["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
