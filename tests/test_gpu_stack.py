@@ -1,9 +1,10 @@
 """dit_stack_step and the flow-match Euler loop against the oracle.
 
 A 3-layer stack of small blocks runs whole denoising loops against the
-float64 oracle, eagerly and as the library's recorded HIP graphs; the full
-36 x 4096 stack at 4096 tokens is checked by the properties that hold at any
-size (finite, bitwise deterministic).  Two layers at the full width are
+float64 oracle, eagerly and as the library's recorded HIP graphs; two layers
+at the full width replay the recorded loop (bf16 and W8A8) bitwise equal to
+the eager one; the full 36 x 4096 stack at 4096 tokens is checked by the
+properties that hold at any size (finite, bitwise deterministic).  Two layers at the full width are
 compared with the oracle element by element in test_gpu_full_width.py."""
 import numpy as np
 import pytest
@@ -130,6 +131,41 @@ def test_loop_graph_replays_match_eager_loop():
         with pytest.raises(N.DitError) as err:
             loop.step(steps)
         assert err.value.status == N.DIT_ERR_INVALID_ARG
+    finally:
+        loop.close()
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "w8a8_h256"])
+def test_loop_graph_replays_match_eager_full_width(fmt):
+    """The recorded loop at the 8B stack's widths (hidden 4096, 32 x 128 heads,
+    SwiGLU 12288, 4096 tokens; 2 layers, 2 steps), where the projections run on
+    the persistent 4-wave GEMM (bf16 or int8 operands) and the QKV projection
+    in its split form with the separate qk-norm + RoPE pass: every replay
+    bitwise equal to the eager loop, with eager work between the replays."""
+    import bench
+    cfg = I.C4.replace(name="stack_8b_graph", layers=2)
+    say(f"loop graph at hidden {cfg.hidden}, {cfg.tokens} tokens, {cfg.layers} layers, {fmt}")
+    stack, cos, sin = bench.build_full_stack(cfg)
+    if fmt == "w8a8_h256":
+        cfg = cfg.replace(fmt=fmt)
+        stack = R.DeviceStack(cfg, [R.quantize_block(b) for b in stack.blocks], stack.edges)
+    lat0 = I.latent(cfg)
+    steps = 2
+    eager = R.to_host_f32(R.denoise(stack, R.to_dev_f32(lat0), cos, sin, steps, I.STACK_SHIFT))
+    assert np.isfinite(eager).all()
+    lat = R.to_dev_f32(lat0)
+    loop = R.DeviceLoop(stack, lat, cos, sin, steps, I.STACK_SHIFT)
+    try:
+        other = R.to_dev_f32(lat0)
+        for rep in range(3):
+            lat.copy_(R.to_dev_f32(lat0))
+            loop.run()
+            _sync()
+            got = R.to_host_f32(lat)
+            say(f"  replay {rep}: max |graph - eager| = {np.abs(got - eager).max():.3e}")
+            np.testing.assert_array_equal(got, eager)
+            R.denoise(stack, other, cos, sin, 1, I.STACK_SHIFT)     # eager work between replays
+            _sync()
     finally:
         loop.close()
 
