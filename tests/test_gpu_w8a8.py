@@ -138,7 +138,17 @@ def test_ln_modulate_h256q_vs_oracle(dim, xdt, norm, mode):
 
 # ---------------------------------------------------------------------------
 def _q8_operands(M, N_rows, K, seed):
+    """int8 codes and row scales: the oracle's H256 quantization of N(0, 1) rows
+    and N(0, 0.02) weight rows, or, for a reduction length the rotation does not
+    take (K % 256 != 0, which the GEMM entry points accept), uniform codes in
+    [-127, 127] with positive scales of the same magnitudes."""
     r = np.random.default_rng(seed)
+    if K % 256:
+        qa = r.integers(-127, 128, (M, K)).astype(np.int8)
+        qw = r.integers(-127, 128, (N_rows, K)).astype(np.int8)
+        sa = (r.uniform(0.5, 1.5, M) * 3.0 / 127).astype(np.float32)
+        sw = (r.uniform(0.5, 1.5, N_rows) * 0.06 / 127).astype(np.float32)
+        return qa, sa, qw, sw
     a = r.standard_normal((M, K)).astype(np.float32)
     w = (r.standard_normal((N_rows, K)) * 0.02).astype(np.float32)
     qa, sa = O.quantize_h256(a)
@@ -157,6 +167,7 @@ def _q8_operands(M, N_rows, K, seed):
     (4096, 4096, 1024, "f32", "f32", N.DIT_GATE_IDENTITY),
     (3900, 4096, 512, "bf16", "bf16", N.DIT_GATE_TANH),
     (4096, 4096, 256, None, "f32", N.DIT_GATE_SIGMOID),
+    (4096, 4096, 128, "f32", "f32", N.DIT_GATE_IDENTITY),   # a single 128-deep K tile
 ])
 def test_gemm_w8a8_gated_residual(M, N_, K, rdt, odt, gate_fn):
     import torch
@@ -193,7 +204,9 @@ def test_gemm_w8a8_gated_residual(M, N_, K, rdt, odt, gate_fn):
                                        # and full rows plus a 74-row tail launch of 128-row tiles
                                        (4096, 4096, 512, N.DIT_ACT_SILU),
                                        (3900, 4096, 256, N.DIT_ACT_GELU_TANH),
-                                       (4170, 12288, 256, N.DIT_ACT_SILU)])
+                                       (4170, 12288, 256, N.DIT_ACT_SILU),
+                                       # 405 tiles (not a multiple of 8), a single K tile
+                                       (3840, 3456, 128, N.DIT_ACT_SILU)])
 def test_gemm_w8a8_swiglu(M, F, K, act):
     import torch
     say(f"gemm_w8a8_swiglu M={M} F={F} K={K} act={act}")
