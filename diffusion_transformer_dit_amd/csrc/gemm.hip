@@ -614,9 +614,9 @@ void gemm4_kernel(const void *__restrict__ A, const void *__restrict__ W, int M,
         // every wave is done with stage cur): reads of k-step 0 of tile kt + 1,
         // copies of tile kt + 2 into stage cur.  STEP0 is the k-step 0 block:
         // the zero-start one in the tile's first K tile.
-#define DIT_K4_TILE(INS, kt, STEP0)                                                                                     \
+#define DIT_K4_TILE(INS, kt, CUR, STEP0)                                                                                \
     do {                                                                                                           \
-        const int cur = (kt) & 1, nxt = cur ^ 1;                                                                   \
+        constexpr int cur = (CUR), nxt = cur ^ 1;                                                                   \
         STEP0(INS, acc, fa, fb, na, nb, 0, adA[cur][1], adB[cur][1]);                                                   \
         STEP0(INS, acc, fa, fb, na, nb, 2, adA[cur][1], adB[cur][1]);                                                   \
         STEP0(INS, acc, fa, fb, na, nb, 4, adA[cur][1], adB[cur][1]);                                                   \
@@ -629,12 +629,26 @@ void gemm4_kernel(const void *__restrict__ A, const void *__restrict__ W, int M,
         DIT_K4_STEP_COPY(INS, acc, na, nb, fa, fb, 4, adA[nxt][0], adB[nxt][0], rw4, lb, kb, vb[0], 32768);             \
         DIT_K4_STEP_COPY(INS, acc, na, nb, fa, fb, 6, adA[nxt][0], adB[nxt][0], rw4, lb, kb, vb[1], 49152);             \
     } while (0)
+        // K tile kt uses stage kt & 1: the loop is unrolled by two so that the
+        // stage, and with it every LDS address of a block, is a constant (a
+        // run-time stage index costs selects of the fragment addresses in
+        // front of every block)
         if constexpr (T::ES == 2) {
-            DIT_K4_TILE(DIT_INS_BF16, 0, DIT_K4_STEP_Z);
-            for (int kt = 1; kt < KT; ++kt) DIT_K4_TILE(DIT_INS_BF16, kt, DIT_K4_STEP);
+            DIT_K4_TILE(DIT_INS_BF16, 0, 0, DIT_K4_STEP_Z);
+            int kt = 1;
+            for (; kt + 1 < KT; kt += 2) {
+                DIT_K4_TILE(DIT_INS_BF16, kt, 1, DIT_K4_STEP);
+                DIT_K4_TILE(DIT_INS_BF16, kt + 1, 0, DIT_K4_STEP);
+            }
+            if (kt < KT) DIT_K4_TILE(DIT_INS_BF16, kt, 1, DIT_K4_STEP);
         } else {
-            DIT_K4_TILE(DIT_INS_I8, 0, DIT_K4_STEP_Z);
-            for (int kt = 1; kt < KT; ++kt) DIT_K4_TILE(DIT_INS_I8, kt, DIT_K4_STEP);
+            DIT_K4_TILE(DIT_INS_I8, 0, 0, DIT_K4_STEP_Z);
+            int kt = 1;
+            for (; kt + 1 < KT; kt += 2) {
+                DIT_K4_TILE(DIT_INS_I8, kt, 1, DIT_K4_STEP);
+                DIT_K4_TILE(DIT_INS_I8, kt + 1, 0, DIT_K4_STEP);
+            }
+            if (kt < KT) DIT_K4_TILE(DIT_INS_I8, kt, 1, DIT_K4_STEP);
         }
 #undef DIT_K4_TILE
         wait_vmcnt<0>();      // retire the trailing (never read) copies before LDS is reused
