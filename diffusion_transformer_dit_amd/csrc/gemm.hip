@@ -196,6 +196,11 @@ void gemm_kernel(const void *__restrict__ A, const void *__restrict__ W, int M, 
     // end re-load the last tile (never read) so that every iteration issues the
     // same number of loads and the vmcnt bookkeeping stays uniform.
     const int KT = K / T::BK;
+    static_assert(T::NS == 2 || T::NS == 3, "the K loop is unrolled over 2 or 3 stages");
+    // the unrolled loop keeps more addresses live: only where two waves per
+    // SIMD still leave room (at most 16 accumulator blocks per wave), or with
+    // one wave per SIMD; the larger 8-wave tiles spill with it
+    constexpr bool kUnrollStages = T::kWaves == 4 || T::TM * T::TN <= 16;
     constexpr int KS = T::kRowBytes / 64;   // MFMA k-steps per stage (even: k-step 0 always uses buffer 0)
     static_assert(KS % 2 == 0, "fragment double buffer");
 #pragma unroll
@@ -228,8 +233,11 @@ void gemm_kernel(const void *__restrict__ A, const void *__restrict__ W, int M, 
     // MFMAs run after it, from fragments already in registers, and cover the
     // barrier, the loads of a later tile and the first fragment reads of the
     // next stage, so the matrix pipe does not drain at every K tile.
-    for (int kt = 0; kt < KT; ++kt) {
-        const uint8_t *sa = smem + (kt % T::NS) * T::kStageBytes;
+    // K tile kt uses stage ST = kt % NS.  Where the registers allow (see
+    // kUnrollStages) the loop is unrolled over the NS stages, so that ST, and
+    // every LDS address of the tile, is a constant
+    auto k_tile = [&](int kt, int ST) __attribute__((always_inline)) {
+        const uint8_t *sa = smem + ST * T::kStageBytes;
         const uint8_t *sb = sa + T::BM * T::kRowBytes;
 #pragma unroll
         for (int kk = 0; kk < KS - 1; ++kk) {
@@ -256,10 +264,10 @@ void gemm_kernel(const void *__restrict__ A, const void *__restrict__ W, int M, 
         {
             // next stage's first fragments (before the loads: LDS reads are not
             // reordered across the LDS-writing loads)
-            const uint8_t *na = smem + ((kt + 1) % T::NS) * T::kStageBytes;
+            const uint8_t *na = smem + ((ST + 1) % T::NS) * T::kStageBytes;
             DIT_LOAD_FRAGS(0, na, na + T::BM * T::kRowBytes, 0);
         }
-        DIT_ISSUE(kt % T::NS, min(kt + T::NS, KT - 1) * T::BK);
+        DIT_ISSUE(ST, min(kt + T::NS, KT - 1) * T::BK);
         DIT_MFMAS((KS - 1) & 1);
         // after the barrier: fragment reads, then the tile loads spread between
         // the MFMAs of the last k-step
@@ -271,6 +279,20 @@ void gemm_kernel(const void *__restrict__ A, const void *__restrict__ W, int M, 
             __builtin_amdgcn_sched_group_barrier(0x020, kPer, 0);            // VMEM
         }
         __builtin_amdgcn_sched_barrier(0);
+    };
+    if constexpr (kUnrollStages) {
+        for (int kt = 0;;) {
+            k_tile(kt, 0);
+            if (++kt >= KT) break;
+            k_tile(kt, 1 % T::NS);
+            if (++kt >= KT) break;
+            if constexpr (T::NS == 3) {
+                k_tile(kt, 2);
+                if (++kt >= KT) break;
+            }
+        }
+    } else {
+        for (int kt = 0; kt < KT; ++kt) k_tile(kt, kt % T::NS);
     }
 #undef DIT_MFMAS
 #undef DIT_LOAD_FRAGS
@@ -308,8 +330,8 @@ void gemm_kernel(const void *__restrict__ A, const void *__restrict__ W, int M, 
     for (int i = 0; i < T::TM; ++i) af[i] = *(const Frag *)(smem + T::off(wm * T::kWaveM + i * 16 + l16, lq));
     DIT_LOAD_B(0, smem + T::BM * T::kRowBytes, 0);
 
-    for (int kt = 0; kt < KT; ++kt) {
-        const uint8_t *sa = smem + (kt % T::NS) * T::kStageBytes;
+    auto k_tile = [&](int kt, int ST) __attribute__((always_inline)) {   // ST = kt % NS (see above)
+        const uint8_t *sa = smem + ST * T::kStageBytes;
         const uint8_t *sb = sa + T::BM * T::kRowBytes;
 #pragma unroll
         for (int kk = 0; kk < KS - 1; ++kk) {
@@ -324,13 +346,27 @@ void gemm_kernel(const void *__restrict__ A, const void *__restrict__ W, int M, 
         {
             // the last k-step reloads from the next stage; every LDS read of it
             // precedes the LDS-writing tile loads, which go out at the end
-            const uint8_t *na = smem + ((kt + 1) % T::NS) * T::kStageBytes;
+            const uint8_t *na = smem + ((ST + 1) % T::NS) * T::kStageBytes;
             DIT_LOAD_B(0, na + T::BM * T::kRowBytes, 0);
             DIT_STEP_RELOAD((KS - 1) & 1, na, 0);
         }
         DIT_SCHED_ROWS();
         __builtin_amdgcn_sched_barrier(0);
-        DIT_ISSUE(kt % T::NS, min(kt + T::NS, KT - 1) * T::BK);
+        DIT_ISSUE(ST, min(kt + T::NS, KT - 1) * T::BK);
+    };
+    if constexpr (kUnrollStages) {
+        for (int kt = 0;;) {
+            k_tile(kt, 0);
+            if (++kt >= KT) break;
+            k_tile(kt, 1 % T::NS);
+            if (++kt >= KT) break;
+            if constexpr (T::NS == 3) {
+                k_tile(kt, 2);
+                if (++kt >= KT) break;
+            }
+        }
+    } else {
+        for (int kt = 0; kt < KT; ++kt) k_tile(kt, kt % T::NS);
     }
 #undef DIT_LOAD_B
 #undef DIT_STEP_RELOAD
