@@ -420,25 +420,32 @@ void gemm_kernel(const void *__restrict__ A, const void *__restrict__ W, int M, 
 // else hides a gap in its MFMA stream, so the K loop is written as inline
 // assembly blocks of 16 MFMAs (one pair of A row blocks against the 8 B column
 // blocks), each with its share of the other work between the MFMAs:
-//   k-step 0 of a stage   : the LDS reads of four fragments of k-step 1;
-//   k-step 1, first block : 8 MFMAs, then the wait for the next stage's
+//   k-step 0 of a K tile  : the LDS reads of four fragments of k-step 1;
+//   k-step 1, first block : 8 MFMAs, then the wait for the next K tile's
 //                           copies and the workgroup barrier (the matrix pipe
-//                           still busy), then the next stage's fragment reads
-//                           and four buffer->LDS copies of the stage after it;
+//                           still busy), then the next K tile's fragment reads
+//                           and four buffer->LDS copies;
 //   k-step 1, other blocks: four reads and four copies, one of each per four
 //                           MFMAs (issued together the copies slow the loop).
+// LDS holds the A tiles of two K tiles and the W tiles of three (5 x 32 KiB):
+// after the barrier of K tile kt the A tile of K tile kt + 2 and the W tile
+// of K tile kt + 3 are copied (into the slots of tile kt), so the W copies,
+// which more often come from memory than the A rows an XCD's CUs share in L2,
+// have two K tiles to land and the barrier waits only for the others.
 // Every block waits for its own LDS reads before it ends, so no load that
 // writes a register is in flight outside a block; the buffer->LDS copies
 // write no register and are counted by the vmcnt wait before the barrier.
 // The accumulators stay in AGPRs: the compiler never moves them, since every
 // block takes them as tied operands; a tile's first k-step starts them from an
 // inline zero.  The workgroups are persistent (one per CU): after a tile's K
-// loop the first two K stages of its next tile are copied into LDS, then the
+// loop the first K tiles of its next tile (A and W of K tiles 0 and 1, W of
+// K tile 2) are copied into LDS, then the
 // epilogue runs (reading each accumulator from its AGPR where it is used), so
 // the copies' latency and the workgroup launch are off the critical path.
 // ---------------------------------------------------------------------------
-// its tiles: bf16 (BK 64, 2 LDS stages of 64 KiB) and int8 operands (BK 128,
-// int32 sums in the accumulators, dequantized by the epilogue where read)
+// its tiles: bf16 (BK 64: a K tile's A and W rows are 32 KiB each) and int8
+// operands (BK 128, int32 sums in the accumulators, dequantized by the
+// epilogue where read)
 struct Tile4w : Tile<256, 256, 2, 2> { static constexpr bool kAgpr = true; };
 struct Tile4wQ : Tile<256, 256, 2, 2, 128, 2, 1> { static constexpr bool kAgpr = true; };
 
@@ -493,12 +500,13 @@ struct Tile4wQ : Tile<256, 256, 2, 2, 128, 2, 1> { static constexpr bool kAgpr =
                  "s_waitcnt lgkmcnt(0)"                                                                    \
                  : DIT_K4_OPERANDS("=a", acc_, fa_, fb_, na_, nb_, i0, adA, adB)                           \
                  : "memory")
-// first k-step 1 block: 8 MFMAs, the next stage's wait and the barrier, then
-// 8 MFMAs with four reads and four copies
+// first k-step 1 block: 8 MFMAs, the wait for all copies but the last eight
+// (the W copies of the K tile after next) and the barrier, then 8 MFMAs with
+// four reads and four copies
 #define DIT_K4_STEP_BARRIER(INS, acc_, fa_, fb_, na_, nb_, i0, adA, adB, rsrc_, ldsb_, soff_, vo_, doff_)       \
     asm volatile(DIT_MF(INS, c00, a0, b0) DIT_MF(INS, c01, a0, b1) DIT_MF(INS, c02, a0, b2) DIT_MF(INS, c03, a0, b3)           \
                  DIT_MF(INS, c04, a0, b4) DIT_MF(INS, c05, a0, b5) DIT_MF(INS, c06, a0, b6) DIT_MF(INS, c07, a0, b7)           \
-                 "s_waitcnt vmcnt(0)\n\ts_barrier\n\t"                                                     \
+                 "s_waitcnt vmcnt(8)\n\ts_barrier\n\t"                                                     \
                  DIT_RD(na0, pa, oa0) DIT_CP(0) DIT_MF(INS, c10, a1, b0) DIT_LD(0) DIT_MF(INS, c11, a1, b1)          \
                  DIT_RD(na1, pa, oa1) DIT_CP(1) DIT_MF(INS, c12, a1, b2) DIT_LD(1) DIT_MF(INS, c13, a1, b3)          \
                  DIT_RD(nb0, pb, oa0) DIT_CP(2) DIT_MF(INS, c14, a1, b4) DIT_LD(2) DIT_MF(INS, c15, a1, b5)          \
@@ -540,10 +548,13 @@ void gemm4_kernel(const void *__restrict__ A, const void *__restrict__ W, int M,
                       T::NS == 2 && T::kRowBytes == 128 && T::kALoads == 8 && T::kBLoads == 8 &&
                       T::kStageBytes == 65536,
                   "the 4-wave 256 x 256 tile: bf16 (64-deep K tiles) or int8 (128-deep)");
-    // the next tile's first two K stages are copied into LDS while the
-    // epilogue of the current one runs, so the epilogue may not use LDS
+    // the next tile's first K tiles are copied into LDS while the epilogue of
+    // the current one runs, so the epilogue may not use LDS
     static_assert(Epi::template lds_bytes<T>() == 0, "epilogue LDS");
-    __shared__ __attribute__((aligned(16))) uint8_t smem[T::NS * T::kStageBytes];
+    // two 32 KiB A slots (K tiles kt % 2) and three W slots (kt % 3): the W tile
+    // of K tile kt + 3 is copied while tile kt + 1 is in use, two K tiles ahead
+    constexpr uint32_t kA0 = 0, kW0 = 65536, kSlot = 32768;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kSlot + 3 * kSlot];
 
     const int ntiles = tiles_m * tiles_n;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -576,25 +587,27 @@ void gemm4_kernel(const void *__restrict__ A, const void *__restrict__ W, int M,
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)smem;
 
     const int KT = K / T::BK;
-    // K tiles 0 and 1 of a tile into the two stages: copy q of A rows and of W
-    // rows to + q * 4 KiB of the stage's A and W halves (as in the K loop, M0
-    // holds the LDS destination); stage 0 goes out first
-    const uint32_t lbw = lds0 + wave * 1024, kb1 = (uint32_t)(min(1, KT - 1) * T::kRowBytes);
+    // A and W of K tiles 0 and 1 and W of K tile 2 into their slots: copy q of
+    // A rows and of W rows to + q * 4 KiB of the slot (as in the K loop, M0
+    // holds the LDS destination)
+    const uint32_t lbw = lds0 + wave * 1024, kb1 = (uint32_t)(min(1, KT - 1) * T::kRowBytes),
+                   kb2 = (uint32_t)(min(2, KT - 1) * T::kRowBytes);
 #define DIT_PCP(m0off, vo, rs, kb) \
     "s_add_u32 m0, %[lb], " #m0off "\n\tbuffer_load_dwordx4 %[" #vo "], %[" #rs "], %[" #kb "] offen lds\n\t"
     auto issue_first_stages = [&]() {
         asm volatile(
-            // stage 0
-            DIT_PCP(0, a0, ra, k0) DIT_PCP(32768, b0, rw, k0) DIT_PCP(4096, a1, ra, k0) DIT_PCP(36864, b1, rw, k0)
-            DIT_PCP(8192, a2, ra, k0) DIT_PCP(40960, b2, rw, k0) DIT_PCP(12288, a3, ra, k0) DIT_PCP(45056, b3, rw, k0)
-            DIT_PCP(16384, a4, ra, k0) DIT_PCP(49152, b4, rw, k0) DIT_PCP(20480, a5, ra, k0) DIT_PCP(53248, b5, rw, k0)
-            DIT_PCP(24576, a6, ra, k0) DIT_PCP(57344, b6, rw, k0) DIT_PCP(28672, a7, ra, k0) DIT_PCP(61440, b7, rw, k0)
-            // stage 1
-            DIT_PCP(65536, a0, ra, k1) DIT_PCP(98304, b0, rw, k1) DIT_PCP(69632, a1, ra, k1) DIT_PCP(102400, b1, rw, k1)
-            DIT_PCP(73728, a2, ra, k1) DIT_PCP(106496, b2, rw, k1) DIT_PCP(77824, a3, ra, k1) DIT_PCP(110592, b3, rw, k1)
-            DIT_PCP(81920, a4, ra, k1) DIT_PCP(114688, b4, rw, k1) DIT_PCP(86016, a5, ra, k1) DIT_PCP(118784, b5, rw, k1)
-            DIT_PCP(90112, a6, ra, k1) DIT_PCP(122880, b6, rw, k1) DIT_PCP(94208, a7, ra, k1) DIT_PCP(126976, b7, rw, k1)
-            : : [lb] "s"(lbw), [ra] "s"(ra4), [rw] "s"(rw4), [k0] "s"(0u), [k1] "s"(kb1),
+            // A0, W0 (K tile 0), A1, W1 (K tile 1), W2 (K tile 2), in this order
+            DIT_PCP(0, a0, ra, k0) DIT_PCP(4096, a1, ra, k0) DIT_PCP(8192, a2, ra, k0) DIT_PCP(12288, a3, ra, k0)
+            DIT_PCP(16384, a4, ra, k0) DIT_PCP(20480, a5, ra, k0) DIT_PCP(24576, a6, ra, k0) DIT_PCP(28672, a7, ra, k0)
+            DIT_PCP(65536, b0, rw, k0) DIT_PCP(69632, b1, rw, k0) DIT_PCP(73728, b2, rw, k0) DIT_PCP(77824, b3, rw, k0)
+            DIT_PCP(81920, b4, rw, k0) DIT_PCP(86016, b5, rw, k0) DIT_PCP(90112, b6, rw, k0) DIT_PCP(94208, b7, rw, k0)
+            DIT_PCP(32768, a0, ra, k1) DIT_PCP(36864, a1, ra, k1) DIT_PCP(40960, a2, ra, k1) DIT_PCP(45056, a3, ra, k1)
+            DIT_PCP(49152, a4, ra, k1) DIT_PCP(53248, a5, ra, k1) DIT_PCP(57344, a6, ra, k1) DIT_PCP(61440, a7, ra, k1)
+            DIT_PCP(98304, b0, rw, k1) DIT_PCP(102400, b1, rw, k1) DIT_PCP(106496, b2, rw, k1) DIT_PCP(110592, b3, rw, k1)
+            DIT_PCP(114688, b4, rw, k1) DIT_PCP(118784, b5, rw, k1) DIT_PCP(122880, b6, rw, k1) DIT_PCP(126976, b7, rw, k1)
+            DIT_PCP(131072, b0, rw, k2) DIT_PCP(135168, b1, rw, k2) DIT_PCP(139264, b2, rw, k2) DIT_PCP(143360, b3, rw, k2)
+            DIT_PCP(147456, b4, rw, k2) DIT_PCP(151552, b5, rw, k2) DIT_PCP(155648, b6, rw, k2) DIT_PCP(159744, b7, rw, k2)
+            : : [lb] "s"(lbw), [ra] "s"(ra4), [rw] "s"(rw4), [k0] "s"(0u), [k1] "s"(kb1), [k2] "s"(kb2),
               [a0] "v"(a_off[0]), [a1] "v"(a_off[1]), [a2] "v"(a_off[2]), [a3] "v"(a_off[3]),
               [a4] "v"(a_off[4]), [a5] "v"(a_off[5]), [a6] "v"(a_off[6]), [a7] "v"(a_off[7]),
               [b0] "v"(b_off[0]), [b1] "v"(b_off[1]), [b2] "v"(b_off[2]), [b3] "v"(b_off[3]),
@@ -618,25 +631,26 @@ void gemm4_kernel(const void *__restrict__ A, const void *__restrict__ W, int M,
         // on); the swizzle of rows base + 16 r + l16 depends on l16 only.  Like
         // the copy offsets they are rebuilt for each tile, so that nothing but
         // the accumulators is live across the epilogue.
-        uint32_t adA[2][2], adB[2][2];
+        uint32_t adA[2][2], adB[3][2];
         {
             const int ln = lane_now(), l16_ = ln & 15, lq_ = ln >> 4, swl = (l16_ >> 1) & 7;
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
+            for (int kk = 0; kk < 2; ++kk) {
+                const uint32_t col = (uint32_t)(((kk * 4 + lq_) ^ swl) << 4);
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const uint32_t col = (uint32_t)(((kk * 4 + lq_) ^ swl) << 4);
-                    adA[s][kk] = lds0 + s * T::kStageBytes + (uint32_t)(wm * 128 + l16_) * 128u + col;
-                    adB[s][kk] = lds0 + s * T::kStageBytes + T::BM * 128u + (uint32_t)(wn * 128 + l16_) * 128u + col;
-                }
+                for (int s = 0; s < 2; ++s) adA[s][kk] = lds0 + kA0 + s * kSlot + (uint32_t)(wm * 128 + l16_) * 128u + col;
+#pragma unroll
+                for (int s = 0; s < 3; ++s) adB[s][kk] = lds0 + kW0 + s * kSlot + (uint32_t)(wn * 128 + l16_) * 128u + col;
+            }
         }
         if (!first) tile_offsets(tm, tn);
         const uint32_t va[2][4] = {{a_off[0], a_off[1], a_off[2], a_off[3]}, {a_off[4], a_off[5], a_off[6], a_off[7]}};
         const uint32_t vb[2][4] = {{b_off[0], b_off[1], b_off[2], b_off[3]}, {b_off[4], b_off[5], b_off[6], b_off[7]}};
-        // K tile 0 landed.  The first tile's K tile 1 may still be in flight; a
-        // later tile's copies went out before the previous epilogue, whose
-        // stores count in the same counter, so there everything is waited for.
-        if (first) wait_vmcnt<16>();
+        // K tile 0 landed.  The first tile's later copies may still be in
+        // flight; a later tile's copies went out before the previous epilogue,
+        // whose stores count in the same counter, so there everything is
+        // waited for.
+        if (first) wait_vmcnt<24>();   // A0, W0 landed; A1, W1, W2 may be in flight
         else wait_vmcnt<0>();
         barrier_only();
 #pragma unroll
@@ -646,46 +660,44 @@ void gemm4_kernel(const void *__restrict__ A, const void *__restrict__ W, int M,
         }
 
         // one K tile: k-step 0 (fa, fb) || reads of its k-step 1; then k-step 1
-        // (na, nb) || after the barrier (tile kt + 1 has landed in stage nxt and
-        // every wave is done with stage cur): reads of k-step 0 of tile kt + 1,
-        // copies of tile kt + 2 into stage cur.  STEP0 is the k-step 0 block:
-        // the zero-start one in the tile's first K tile.
-#define DIT_K4_TILE(INS, kt, CUR, STEP0)                                                                                \
+        // (na, nb) || after the barrier (K tile kt + 1 has landed and every
+        // wave is done with the slots of K tile kt): reads of k-step 0 of K tile
+        // kt + 1, copies of A(kt + 2) and W(kt + 3) into the slots of K tile kt
+        // (A slot SA = kt % 2, W slot SW = kt % 3).  STEP0 is the k-step 0
+        // block: the zero-start one in the tile's first K tile.
+#define DIT_K4_TILE(INS, kt, SA, SW, STEP0)                                                                          \
     do {                                                                                                           \
-        constexpr int cur = (CUR), nxt = cur ^ 1;                                                                   \
-        STEP0(INS, acc, fa, fb, na, nb, 0, adA[cur][1], adB[cur][1]);                                                   \
-        STEP0(INS, acc, fa, fb, na, nb, 2, adA[cur][1], adB[cur][1]);                                                   \
-        STEP0(INS, acc, fa, fb, na, nb, 4, adA[cur][1], adB[cur][1]);                                                   \
-        STEP0(INS, acc, fa, fb, na, nb, 6, adA[cur][1], adB[cur][1]);                                                   \
-        const uint32_t lb =                                                                                        \
-            (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds0 + cur * T::kStageBytes + wave * 1024));            \
-        const uint32_t kb = (uint32_t)__builtin_amdgcn_readfirstlane(min((kt) + 2, KT - 1) * T::kRowBytes);          \
-        DIT_K4_STEP_BARRIER(INS, acc, na, nb, fa, fb, 0, adA[nxt][0], adB[nxt][0], ra4, lb, kb, va[0], 0);              \
-        DIT_K4_STEP_COPY(INS, acc, na, nb, fa, fb, 2, adA[nxt][0], adB[nxt][0], ra4, lb, kb, va[1], 16384);             \
-        DIT_K4_STEP_COPY(INS, acc, na, nb, fa, fb, 4, adA[nxt][0], adB[nxt][0], rw4, lb, kb, vb[0], 32768);             \
-        DIT_K4_STEP_COPY(INS, acc, na, nb, fa, fb, 6, adA[nxt][0], adB[nxt][0], rw4, lb, kb, vb[1], 49152);             \
+        constexpr int sa_ = (SA), sw_ = (SW), na_ = sa_ ^ 1, nw_ = (sw_ + 1) % 3;                                   \
+        STEP0(INS, acc, fa, fb, na, nb, 0, adA[sa_][1], adB[sw_][1]);                                              \
+        STEP0(INS, acc, fa, fb, na, nb, 2, adA[sa_][1], adB[sw_][1]);                                              \
+        STEP0(INS, acc, fa, fb, na, nb, 4, adA[sa_][1], adB[sw_][1]);                                              \
+        STEP0(INS, acc, fa, fb, na, nb, 6, adA[sa_][1], adB[sw_][1]);                                              \
+        const uint32_t lbA = (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds0 + kA0 + sa_ * kSlot + wave * 1024)); \
+        const uint32_t lbW = (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds0 + kW0 + sw_ * kSlot + wave * 1024)); \
+        const uint32_t kbA = (uint32_t)__builtin_amdgcn_readfirstlane(min((kt) + 2, KT - 1) * T::kRowBytes);       \
+        const uint32_t kbW = (uint32_t)__builtin_amdgcn_readfirstlane(min((kt) + 3, KT - 1) * T::kRowBytes);       \
+        DIT_K4_STEP_BARRIER(INS, acc, na, nb, fa, fb, 0, adA[na_][0], adB[nw_][0], ra4, lbA, kbA, va[0], 0);        \
+        DIT_K4_STEP_COPY(INS, acc, na, nb, fa, fb, 2, adA[na_][0], adB[nw_][0], ra4, lbA, kbA, va[1], 16384);       \
+        DIT_K4_STEP_COPY(INS, acc, na, nb, fa, fb, 4, adA[na_][0], adB[nw_][0], rw4, lbW, kbW, vb[0], 0);           \
+        DIT_K4_STEP_COPY(INS, acc, na, nb, fa, fb, 6, adA[na_][0], adB[nw_][0], rw4, lbW, kbW, vb[1], 16384);       \
     } while (0)
-        // K tile kt uses stage kt & 1: the loop is unrolled by two so that the
-        // stage, and with it every LDS address of a block, is a constant (a
-        // run-time stage index costs selects of the fragment addresses in
-        // front of every block)
-        if constexpr (T::ES == 2) {
-            DIT_K4_TILE(DIT_INS_BF16, 0, 0, DIT_K4_STEP_Z);
-            int kt = 1;
-            for (; kt + 1 < KT; kt += 2) {
-                DIT_K4_TILE(DIT_INS_BF16, kt, 1, DIT_K4_STEP);
-                DIT_K4_TILE(DIT_INS_BF16, kt + 1, 0, DIT_K4_STEP);
-            }
-            if (kt < KT) DIT_K4_TILE(DIT_INS_BF16, kt, 1, DIT_K4_STEP);
-        } else {
-            DIT_K4_TILE(DIT_INS_I8, 0, 0, DIT_K4_STEP_Z);
-            int kt = 1;
-            for (; kt + 1 < KT; kt += 2) {
-                DIT_K4_TILE(DIT_INS_I8, kt, 1, DIT_K4_STEP);
-                DIT_K4_TILE(DIT_INS_I8, kt + 1, 0, DIT_K4_STEP);
-            }
-            if (kt < KT) DIT_K4_TILE(DIT_INS_I8, kt, 1, DIT_K4_STEP);
-        }
+        // K tile kt uses A slot kt % 2 and W slot kt % 3: the loop is unrolled over
+        // the 6 combinations so that every LDS address of a block is a constant
+#define DIT_K4_LOOP(INS)                                                                                          \
+    do {                                                                                                           \
+        DIT_K4_TILE(INS, 0, 0, 0, DIT_K4_STEP_Z);                                                                  \
+        for (int kt = 1; kt < KT;) {                                                                               \
+            DIT_K4_TILE(INS, kt, 1, 1, DIT_K4_STEP); if (++kt >= KT) break;                                        \
+            DIT_K4_TILE(INS, kt, 0, 2, DIT_K4_STEP); if (++kt >= KT) break;                                        \
+            DIT_K4_TILE(INS, kt, 1, 0, DIT_K4_STEP); if (++kt >= KT) break;                                        \
+            DIT_K4_TILE(INS, kt, 0, 1, DIT_K4_STEP); if (++kt >= KT) break;                                        \
+            DIT_K4_TILE(INS, kt, 1, 2, DIT_K4_STEP); if (++kt >= KT) break;                                        \
+            DIT_K4_TILE(INS, kt, 0, 0, DIT_K4_STEP); ++kt;                                                         \
+        }                                                                                                          \
+    } while (0)
+        if constexpr (T::ES == 2) DIT_K4_LOOP(DIT_INS_BF16);
+        else DIT_K4_LOOP(DIT_INS_I8);
+#undef DIT_K4_LOOP
 #undef DIT_K4_TILE
         wait_vmcnt<0>();      // retire the trailing (never read) copies before LDS is reused
         __syncthreads();
